@@ -1,0 +1,520 @@
+// Host runtime of libtq: the C ABI, argument validation, the handle's constants
+// (seeded Gaussians, Householder QR, Lloyd-Max codebooks) and the device upload.
+// Compiled with -ffp-contract=off so that its float64 arithmetic is plain IEEE.
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "tq_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+tq_status fail(tq_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+tq_status ok() {
+  g_last_error.clear();
+  return TQ_OK;
+}
+
+tq_status device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(TQ_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------------------------------
+// SplitMix64 (Steele, Lea, Flood, OOPSLA 2014): word i of stream `seed` is
+// mix(seed + (i + 1) * 0x9E3779B97F4A7C15), a counter-based generator.
+// ---------------------------------------------------------------------------------------
+uint64_t splitmix_word(uint64_t seed, uint64_t i) {
+  uint64_t z = seed + (i + 1) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// n standard normals: Box-Muller (Box & Muller 1958) on word pairs (2k, 2k+1).
+std::vector<double> normals(uint64_t seed, size_t n) {
+  std::vector<double> out(n);
+  const double two_pi = 6.283185307179586;
+  const double inv53 = 1.0 / 9007199254740992.0;  // 2^-53
+  for (size_t k = 0; 2 * k < n; ++k) {
+    const double u1 = (double)((splitmix_word(seed, 2 * k) >> 11) + 1) * inv53;
+    const double u2 = (double)(splitmix_word(seed, 2 * k + 1) >> 11) * inv53;
+    const double rad = std::sqrt(-2.0 * std::log(u1));
+    const double ang = two_pi * u2;
+    out[2 * k] = rad * std::cos(ang);
+    if (2 * k + 1 < n) out[2 * k + 1] = rad * std::sin(ang);
+  }
+  return out;
+}
+
+// Random rotation: Q of the Householder QR of the row-major d x d Gaussian G, with
+// column j of Q negated when R_jj < 0 (so R = Q^T G has a positive diagonal).
+std::vector<float> make_rotation(uint64_t seed, int d) {
+  std::vector<double> A = normals(seed, (size_t)d * d);  // overwritten by R
+  std::vector<double> V((size_t)d * d, 0.0);              // Householder vectors, column k
+  std::vector<double> rdiag(d, 0.0);
+  for (int k = 0; k < d; ++k) {
+    double norm2 = 0.0;
+    for (int i = k; i < d; ++i) norm2 += A[(size_t)i * d + k] * A[(size_t)i * d + k];
+    const double norm = std::sqrt(norm2);
+    if (norm == 0.0) { rdiag[k] = 0.0; continue; }
+    const double x0 = A[(size_t)k * d + k];
+    const double alpha = x0 >= 0.0 ? -norm : norm;       // avoids cancellation in v0
+    double vn2 = 0.0;
+    for (int i = k; i < d; ++i) {
+      const double vi = A[(size_t)i * d + k] - (i == k ? alpha : 0.0);
+      V[(size_t)i * d + k] = vi;
+      vn2 += vi * vi;
+    }
+    const double vn = std::sqrt(vn2);
+    for (int i = k; i < d; ++i) V[(size_t)i * d + k] /= vn;
+    for (int j = k; j < d; ++j) {          // A[k:, j] -= 2 v (v . A[k:, j])
+      double dot = 0.0;
+      for (int i = k; i < d; ++i) dot += V[(size_t)i * d + k] * A[(size_t)i * d + j];
+      for (int i = k; i < d; ++i) A[(size_t)i * d + j] -= 2.0 * dot * V[(size_t)i * d + k];
+    }
+    rdiag[k] = alpha;
+  }
+  // Q = H_0 H_1 ... H_{d-1} I, applied from the right-most reflection outwards.
+  std::vector<double> Q((size_t)d * d, 0.0);
+  for (int i = 0; i < d; ++i) Q[(size_t)i * d + i] = 1.0;
+  for (int k = d - 1; k >= 0; --k) {
+    if (rdiag[k] == 0.0 && k < d) {
+      bool zero = true;
+      for (int i = k; i < d; ++i) zero &= V[(size_t)i * d + k] == 0.0;
+      if (zero) continue;
+    }
+    for (int j = 0; j < d; ++j) {
+      double dot = 0.0;
+      for (int i = k; i < d; ++i) dot += V[(size_t)i * d + k] * Q[(size_t)i * d + j];
+      for (int i = k; i < d; ++i) Q[(size_t)i * d + j] -= 2.0 * dot * V[(size_t)i * d + k];
+    }
+  }
+  std::vector<float> pi((size_t)d * d);
+  for (int j = 0; j < d; ++j) {
+    const double sgn = rdiag[j] < 0.0 ? -1.0 : 1.0;
+    for (int i = 0; i < d; ++i) pi[(size_t)i * d + j] = (float)(sgn * Q[(size_t)i * d + j]);
+  }
+  return pi;
+}
+
+std::vector<float> make_qjl(uint64_t seed, int m, int d) {
+  std::vector<double> g = normals(seed, (size_t)m * d);
+  std::vector<float> s(g.size());
+  for (size_t i = 0; i < g.size(); ++i) s[i] = (float)g[i];
+  return s;
+}
+
+// Standard normal: mass and first moment of the cell (lo, hi).  The upper tail uses erfc
+// directly so that small tail masses keep their relative accuracy.
+void cell(double lo, double hi, double* mass, double* moment) {
+  const double r2 = 0.7071067811865476;  // 1/sqrt(2)
+  auto upper = [&](double t) {           // P(X > t)
+    if (std::isinf(t)) return t > 0 ? 0.0 : 1.0;
+    return 0.5 * std::erfc(t * r2);
+  };
+  auto dens = [](double t) {
+    if (std::isinf(t)) return 0.0;
+    return std::exp(-0.5 * t * t) * 0.3989422804014327;  // 1/sqrt(2 pi)
+  };
+  *mass = upper(lo) - upper(hi);
+  *moment = dens(lo) - dens(hi);
+}
+
+// Lloyd-Max quantizer for N(0,1): alternate midpoint boundaries and conditional-mean
+// levels in float64 until the levels move less than 1e-14, keeping the levels exactly
+// antisymmetric (the density is symmetric).  Start: levels evenly spaced on [-2, 2].
+void lloyd_max(int bits, std::vector<double>* levels, std::vector<double>* bounds) {
+  const int L = 1 << bits;
+  std::vector<double> lev(L), nxt(L);
+  for (int i = 0; i < L; ++i) lev[i] = -2.0 + 4.0 * (i + 0.5) / L;
+  for (int i = 0; i < L / 2; ++i) { lev[L - 1 - i] = 0.5 * (lev[L - 1 - i] - lev[i]); lev[i] = -lev[L - 1 - i]; }
+  for (int it = 0; it < 20000; ++it) {
+    for (int i = 0; i < L; ++i) {
+      const double lo = i == 0 ? -INFINITY : 0.5 * (lev[i - 1] + lev[i]);
+      const double hi = i == L - 1 ? INFINITY : 0.5 * (lev[i] + lev[i + 1]);
+      double mass, mom;
+      cell(lo, hi, &mass, &mom);
+      nxt[i] = mom / mass;
+    }
+    double delta = 0.0;
+    for (int i = 0; i < L / 2; ++i) {
+      const double a = 0.5 * (nxt[L - 1 - i] - nxt[i]);
+      delta = std::fmax(delta, std::fabs(a - lev[L - 1 - i]));
+      lev[L - 1 - i] = a;
+      lev[i] = -a;
+    }
+    if (delta < 1e-14) break;
+  }
+  levels->assign(lev.begin(), lev.end());
+  bounds->resize(L - 1);
+  for (int i = 0; i + 1 < L; ++i) (*bounds)[i] = 0.5 * (lev[i] + lev[i + 1]);
+}
+
+tq_status check_config(const tq_config* cfg) {
+  if (!cfg) return fail(TQ_ERR_INVALID_ARGUMENT, "config is NULL");
+  if (cfg->head_dim <= 0 || cfg->key_bits <= 0 || cfg->value_bits <= 0 || cfg->qjl_dim < 0)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "head_dim, key_bits, value_bits must be > 0, qjl_dim >= 0");
+  if (cfg->key_bits > 4 || cfg->value_bits > 4)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "key_bits and value_bits must be in 1..4");
+  if (cfg->qjl_dim % 32 != 0 || cfg->qjl_dim > 256)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "qjl_dim must be 0 or a multiple of 32 up to 256");
+  if (cfg->head_dim != 64 && cfg->head_dim != 128)
+    return fail(TQ_ERR_UNSUPPORTED, "head_dim %d not built (64 or 128)", cfg->head_dim);
+  if (cfg->key_bits < 2 || cfg->value_bits < 2)
+    return fail(TQ_ERR_UNSUPPORTED, "1-bit stage-1 codes are not built (key/value bits 2..4)");
+  return TQ_OK;
+}
+
+void fill_consts(const tq_config* cfg, tq::Consts* c) {
+  std::memset(c, 0, sizeof *c);
+  c->d = cfg->head_dim;
+  c->kb = cfg->key_bits;
+  c->m = cfg->qjl_dim;
+  c->vb = cfg->value_bits;
+  c->kbytes = c->d * c->kb / 8;
+  c->sbytes = c->m / 8;
+  c->vbytes = c->d * c->vb / 8;
+  c->norm_off = c->kbytes + c->sbytes + c->vbytes;
+  c->rec_bytes = (c->norm_off + 12 + 15) / 16 * 16;
+  c->sqrt_d = std::sqrt((double)c->d);
+  c->inv_sqrt_d = (float)(1.0 / c->sqrt_d);
+  c->qjl_coef = c->m ? (float)(std::sqrt(3.141592653589793 / 2.0) / c->m) : 0.0f;
+  for (int i = 0; i < tq::kMaxLevels; ++i) c->key_bounds[i] = c->val_bounds[i] = INFINITY;
+  std::vector<double> lv, bd;
+  lloyd_max(c->kb, &lv, &bd);
+  for (size_t i = 0; i < lv.size(); ++i) c->key_levels[i] = (float)lv[i];
+  for (size_t i = 0; i < bd.size(); ++i) c->key_bounds[i] = (float)bd[i];
+  lloyd_max(c->vb, &lv, &bd);
+  for (size_t i = 0; i < lv.size(); ++i) c->val_levels[i] = (float)lv[i];
+  for (size_t i = 0; i < bd.size(); ++i) c->val_bounds[i] = (float)bd[i];
+}
+
+// MFMA A-operand order used by the compress kernel: entry ((ct * (d/4) + s) * 64 + l)
+// holds M[row(ct, l % 16)][(d/4) * (l / 16) + s] with row(ct, i) = (rows/4)(i % 4) + 4 ct + i/4.
+std::vector<float> mfma_order(const std::vector<float>& M, int rows, int d) {
+  std::vector<float> out((size_t)rows * d);
+  const int q = d / 4, rq = rows / 4;
+  for (int ct = 0; ct < rows / 16; ++ct)
+    for (int s = 0; s < q; ++s)
+      for (int l = 0; l < 64; ++l) {
+        const int i = l % 16;
+        const int row = rq * (i % 4) + 4 * ct + i / 4;
+        const int col = q * (l / 16) + s;
+        out[((size_t)ct * q + s) * 64 + l] = M[(size_t)row * d + col];
+      }
+  return out;
+}
+
+bool elem_size(tq_dtype dt, size_t* sz) {
+  switch (dt) {
+    case TQ_F32: *sz = 4; return true;
+    case TQ_F16: case TQ_BF16: *sz = 2; return true;
+  }
+  return false;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+struct tq_handle {
+  tq_config cfg;
+  tq::Consts c;
+  tq::DevConsts dc;
+  void* dev_block;
+  int device;
+};
+
+extern "C" {
+
+const char* tq_last_error(void) { return g_last_error.c_str(); }
+
+tq_status tq_host_constants(const tq_config* cfg, float* pi, float* s, float* key_levels,
+                            float* key_bounds, float* value_levels, float* value_bounds) {
+  tq_status st = check_config(cfg);
+  if (st != TQ_OK) return st;
+  tq::Consts c;
+  fill_consts(cfg, &c);
+  if (pi) {
+    std::vector<float> p = make_rotation(cfg->rotation_seed, c.d);
+    std::memcpy(pi, p.data(), p.size() * sizeof(float));
+  }
+  if (s && c.m) {
+    std::vector<float> q = make_qjl(cfg->qjl_seed, c.m, c.d);
+    std::memcpy(s, q.data(), q.size() * sizeof(float));
+  }
+  if (key_levels) std::memcpy(key_levels, c.key_levels, sizeof(float) << c.kb);
+  if (key_bounds) std::memcpy(key_bounds, c.key_bounds, sizeof(float) * ((1 << c.kb) - 1));
+  if (value_levels) std::memcpy(value_levels, c.val_levels, sizeof(float) << c.vb);
+  if (value_bounds) std::memcpy(value_bounds, c.val_bounds, sizeof(float) * ((1 << c.vb) - 1));
+  return ok();
+}
+
+tq_status tq_create(const tq_config* cfg, tq_handle** out) {
+  if (!out) return fail(TQ_ERR_INVALID_ARGUMENT, "out is NULL");
+  *out = nullptr;
+  tq_status st = check_config(cfg);
+  if (st != TQ_OK) return st;
+  tq_handle* h = new (std::nothrow) tq_handle();
+  if (!h) return fail(TQ_ERR_OUT_OF_MEMORY, "host allocation failed");
+  h->cfg = *cfg;
+  fill_consts(cfg, &h->c);
+  const int d = h->c.d, m = h->c.m;
+  std::vector<float> pi = make_rotation(cfg->rotation_seed, d);
+  std::vector<float> s = m ? make_qjl(cfg->qjl_seed, m, d) : std::vector<float>();
+  std::vector<float> pi_m = mfma_order(pi, d, d);
+  std::vector<float> s_m = m ? mfma_order(s, m, d) : std::vector<float>();
+  const size_t n_pi = (size_t)d * d, n_s = (size_t)m * d;
+  const size_t total = (2 * n_pi + 2 * n_s) * sizeof(float);
+  if (hipGetDevice(&h->device) != hipSuccess) { delete h; return fail(TQ_ERR_DEVICE, "no HIP device"); }
+  if (hipMalloc(&h->dev_block, total) != hipSuccess) {
+    delete h;
+    return fail(TQ_ERR_OUT_OF_MEMORY, "hipMalloc of %zu bytes failed", total);
+  }
+  float* base = (float*)h->dev_block;
+  std::vector<float> host;
+  host.reserve(total / sizeof(float));
+  host.insert(host.end(), pi.begin(), pi.end());
+  host.insert(host.end(), pi_m.begin(), pi_m.end());
+  host.insert(host.end(), s.begin(), s.end());
+  host.insert(host.end(), s_m.begin(), s_m.end());
+  hipError_t e = hipMemcpy(base, host.data(), total, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(h->dev_block);
+    delete h;
+    return device_status(e, "upload of handle constants");
+  }
+  h->dc.pi = base;
+  h->dc.pi_mfma = base + n_pi;
+  h->dc.s = m ? base + 2 * n_pi : nullptr;
+  h->dc.s_mfma = m ? base + 2 * n_pi + n_s : nullptr;
+  *out = h;
+  return ok();
+}
+
+tq_status tq_destroy(tq_handle* h) {
+  if (!h) return fail(TQ_ERR_INVALID_ARGUMENT, "handle is NULL");
+  hipError_t e = hipFree(h->dev_block);
+  delete h;
+  return device_status(e, "hipFree");
+}
+
+tq_status tq_record_bytes(const tq_handle* h, size_t* record_bytes, size_t* index_record_bytes) {
+  if (!h) return fail(TQ_ERR_INVALID_ARGUMENT, "handle is NULL");
+  if (record_bytes) *record_bytes = (size_t)h->c.rec_bytes;
+  if (index_record_bytes) *index_record_bytes = (size_t)h->c.d / 8;
+  return ok();
+}
+
+static tq_status check_kv_addressing(const tq_handle* h, const void* k, tq_dtype dt, int32_t batch,
+                                     int64_t n_tokens, int32_t heads, int64_t seq_stride,
+                                     int64_t tok_stride, int64_t head_stride, int64_t capacity,
+                                     int64_t first_slot) {
+  size_t es;
+  if (!elem_size(dt, &es)) return fail(TQ_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dt);
+  if (batch < 0 || n_tokens < 0 || heads <= 0) return fail(TQ_ERR_INVALID_ARGUMENT, "bad batch/tokens/heads");
+  if (capacity < 0 || first_slot < 0 || first_slot + n_tokens > capacity)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "first_slot + n_tokens (%lld) exceeds capacity (%lld)",
+                (long long)(first_slot + n_tokens), (long long)capacity);
+  if (seq_stride < 0 || tok_stride < 0 || head_stride < 0)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "negative stride");
+  if (batch * n_tokens == 0) return TQ_OK;
+  if (!k) return fail(TQ_ERR_INVALID_ARGUMENT, "key/value pointer is NULL");
+  const size_t a = 16;
+  if (!aligned(k, a) || (seq_stride * es) % a || (tok_stride * es) % a || (head_stride * es) % a)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "key/value base and strides must be 16-byte aligned");
+  (void)h;
+  return TQ_OK;
+}
+
+tq_status tq_compress_kv(const tq_handle* h, const void* k, const void* v, tq_dtype dt,
+                         int32_t batch, int64_t n_tokens, int32_t kv_heads, int64_t seq_stride,
+                         int64_t tok_stride, int64_t head_stride, void* records,
+                         int64_t capacity, int64_t first_slot, hipStream_t stream) {
+  if (!h) return fail(TQ_ERR_INVALID_ARGUMENT, "handle is NULL");
+  tq_status st = check_kv_addressing(h, k, dt, batch, n_tokens, kv_heads, seq_stride, tok_stride,
+                                     head_stride, capacity, first_slot);
+  if (st != TQ_OK) return st;
+  if ((int64_t)batch * n_tokens == 0) return ok();
+  st = check_kv_addressing(h, v, dt, batch, n_tokens, kv_heads, seq_stride, tok_stride,
+                           head_stride, capacity, first_slot);
+  if (st != TQ_OK) return st;
+  if (!records || !aligned(records, 16)) return fail(TQ_ERR_INVALID_ARGUMENT, "records NULL or not 16-byte aligned");
+  return device_status(tq::launch_compress(h->c, h->dc, k, v, dt, batch, n_tokens, kv_heads,
+                                           seq_stride, tok_stride, head_stride, records,
+                                           capacity, first_slot, stream),
+                       "compress launch");
+}
+
+tq_status tq_debug_quantize(const tq_handle* h, const float* z_k, const float* p,
+                            const float* r_k, const float* rho, const float* z_v,
+                            const float* r_v, int64_t n, void* records, hipStream_t stream) {
+  if (!h) return fail(TQ_ERR_INVALID_ARGUMENT, "handle is NULL");
+  if (n < 0) return fail(TQ_ERR_INVALID_ARGUMENT, "n < 0");
+  if (n == 0) return ok();
+  if (!z_k || !r_k || !rho || !z_v || !r_v || !records || (h->c.m && !p))
+    return fail(TQ_ERR_INVALID_ARGUMENT, "NULL input");
+  if (!aligned(records, 16)) return fail(TQ_ERR_INVALID_ARGUMENT, "records not 16-byte aligned");
+  return device_status(tq::launch_debug_quantize(h->c, z_k, p, r_k, rho, z_v, r_v, n, records, stream),
+                       "debug quantize launch");
+}
+
+tq_status tq_decode_workspace_size(const tq_handle* h, int32_t batch, int32_t q_heads,
+                                   int32_t kv_heads, int64_t capacity, int32_t k_sel,
+                                   size_t* bytes) {
+  if (!h || !bytes) return fail(TQ_ERR_INVALID_ARGUMENT, "NULL handle or output");
+  if (batch < 0 || q_heads <= 0 || kv_heads <= 0 || q_heads % kv_heads || capacity < 0 || k_sel < 0)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "bad decode shape");
+  tq::DecodePlan plan;
+  if (!tq::plan_decode(h->c, batch, q_heads, kv_heads, k_sel > 0 ? k_sel : capacity, &plan))
+    return fail(TQ_ERR_UNSUPPORTED, "group size %d not supported", q_heads / kv_heads);
+  *bytes = plan.ws_total;
+  return ok();
+}
+
+tq_status tq_decode_attention(const tq_handle* h, const void* q, tq_dtype q_dt, int32_t batch,
+                              int32_t q_heads, int32_t kv_heads, const void* records,
+                              int64_t capacity, const int32_t* seq_lens, const void* hot_k,
+                              const void* hot_v, tq_dtype hot_dt, const int32_t* hot_lens,
+                              int64_t hot_capacity, const int32_t* sel_idx, int32_t k_sel,
+                              float scale, float* out, float* lse, float* logits,
+                              void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!h) return fail(TQ_ERR_INVALID_ARGUMENT, "handle is NULL");
+  size_t es;
+  if (!elem_size(q_dt, &es)) return fail(TQ_ERR_INVALID_ARGUMENT, "unknown query dtype");
+  if (batch < 0 || q_heads <= 0 || kv_heads <= 0 || q_heads % kv_heads)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "q_heads must be a positive multiple of kv_heads");
+  if (capacity < 0 || k_sel < 0) return fail(TQ_ERR_INVALID_ARGUMENT, "negative capacity or k_sel");
+  if (!(scale >= 0.0f) || std::isinf(scale)) return fail(TQ_ERR_INVALID_ARGUMENT, "scale must be finite and >= 0");
+  if (batch == 0) return ok();
+  if (!q || !out || !seq_lens) return fail(TQ_ERR_INVALID_ARGUMENT, "q, out and seq_lens are required");
+  if (capacity > 0 && !records) return fail(TQ_ERR_INVALID_ARGUMENT, "records is NULL");
+  if (records && !aligned(records, 16)) return fail(TQ_ERR_INVALID_ARGUMENT, "records not 16-byte aligned");
+  if (sel_idx && k_sel == 0) return fail(TQ_ERR_INVALID_ARGUMENT, "gather mode needs k_sel > 0");
+  if (hot_lens) {
+    size_t hs;
+    if (!elem_size(hot_dt, &hs)) return fail(TQ_ERR_INVALID_ARGUMENT, "unknown hot dtype");
+    if (hot_capacity <= 0 || !hot_k || !hot_v)
+      return fail(TQ_ERR_INVALID_ARGUMENT, "exact segment needs hot_k, hot_v and hot_capacity > 0");
+  }
+  tq::DecodePlan plan;
+  if (!tq::plan_decode(h->c, batch, q_heads, kv_heads, sel_idx ? k_sel : capacity, &plan))
+    return fail(TQ_ERR_UNSUPPORTED, "group size %d not supported", q_heads / kv_heads);
+  if (!workspace || ws_bytes < plan.ws_total || !aligned(workspace, 256))
+    return fail(TQ_ERR_WORKSPACE_TOO_SMALL, "decode needs %zu bytes of 256-byte aligned workspace",
+                plan.ws_total);
+  return device_status(tq::launch_decode(h->c, h->dc, plan, q, q_dt, batch, q_heads, kv_heads,
+                                         records, capacity, seq_lens, hot_k, hot_v, hot_dt,
+                                         hot_lens, hot_capacity, sel_idx, k_sel, scale, out, lse,
+                                         logits, workspace, stream),
+                       "decode launch");
+}
+
+tq_status tq_index_workspace_size(const tq_handle* h, int32_t batch, int32_t kv_heads,
+                                  size_t* bytes) {
+  if (!h || !bytes) return fail(TQ_ERR_INVALID_ARGUMENT, "NULL handle or output");
+  if (batch < 0 || kv_heads <= 0) return fail(TQ_ERR_INVALID_ARGUMENT, "bad shape");
+  // worst case over n_tokens: the plan caps the number of chunks
+  *bytes = tq::plan_index(h->c, batch, kv_heads, (int64_t)1 << 40).ws_total;
+  return ok();
+}
+
+tq_status tq_build_sign_index(const tq_handle* h, const void* k, tq_dtype dt, int32_t batch,
+                              int64_t n_tokens, int32_t kv_heads, int64_t seq_stride,
+                              int64_t tok_stride, int64_t head_stride, void* index,
+                              float* codebook, float* mean, int64_t capacity,
+                              int64_t first_slot, void* workspace, size_t ws_bytes,
+                              hipStream_t stream) {
+  if (!h) return fail(TQ_ERR_INVALID_ARGUMENT, "handle is NULL");
+  tq_status st = check_kv_addressing(h, k, dt, batch, n_tokens, kv_heads, seq_stride, tok_stride,
+                                     head_stride, capacity, first_slot);
+  if (st != TQ_OK) return st;
+  if (batch == 0) return ok();
+  if (!index || !codebook) return fail(TQ_ERR_INVALID_ARGUMENT, "index and codebook are required");
+  tq::IndexPlan plan = tq::plan_index(h->c, batch, kv_heads, n_tokens);
+  if (!workspace || ws_bytes < plan.ws_total || !aligned(workspace, 256))
+    return fail(TQ_ERR_WORKSPACE_TOO_SMALL, "sign index needs %zu bytes of workspace", plan.ws_total);
+  return device_status(tq::launch_sign_index(h->c, plan, k, dt, batch, n_tokens, kv_heads,
+                                             seq_stride, tok_stride, head_stride, index, codebook,
+                                             mean, capacity, first_slot, workspace, stream),
+                       "sign index launch");
+}
+
+tq_status tq_select_workspace_size(const tq_handle* h, int32_t batch, int32_t kv_heads,
+                                   int64_t capacity, size_t* bytes) {
+  if (!h || !bytes) return fail(TQ_ERR_INVALID_ARGUMENT, "NULL handle or output");
+  if (batch < 0 || kv_heads <= 0 || capacity < 0) return fail(TQ_ERR_INVALID_ARGUMENT, "bad shape");
+  *bytes = tq::plan_select(h->c, batch, kv_heads, capacity).ws_total;
+  return ok();
+}
+
+tq_status tq_select_topk(const tq_handle* h, const void* q, tq_dtype q_dt, int32_t batch,
+                         int32_t q_heads, int32_t kv_heads, const void* index,
+                         const float* codebook, int64_t capacity, const int32_t* seq_lens,
+                         int32_t k, int32_t* out_idx, int32_t* out_count, int32_t* out_scores,
+                         void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!h) return fail(TQ_ERR_INVALID_ARGUMENT, "handle is NULL");
+  size_t es;
+  if (!elem_size(q_dt, &es)) return fail(TQ_ERR_INVALID_ARGUMENT, "unknown query dtype");
+  if (batch < 0 || q_heads <= 0 || kv_heads <= 0 || q_heads % kv_heads || capacity < 0 || k < 0)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "bad select shape");
+  if (q_heads / kv_heads > 16) return fail(TQ_ERR_UNSUPPORTED, "group size above 16");
+  if (batch == 0) return ok();
+  if (!q || !seq_lens || !out_count || (k > 0 && !out_idx) || (capacity > 0 && (!index || !codebook)))
+    return fail(TQ_ERR_INVALID_ARGUMENT, "NULL input or output");
+  tq::SelectPlan plan = tq::plan_select(h->c, batch, kv_heads, capacity);
+  if (!workspace || ws_bytes < plan.ws_total || !aligned(workspace, 256))
+    return fail(TQ_ERR_WORKSPACE_TOO_SMALL, "select needs %zu bytes of workspace", plan.ws_total);
+  return device_status(tq::launch_select(h->c, plan, q, q_dt, batch, q_heads, kv_heads, index,
+                                         codebook, capacity, seq_lens, k, out_idx, out_count,
+                                         out_scores, workspace, stream),
+                       "select launch");
+}
+
+tq_status tq_scan_workspace_size(const tq_handle* h, int32_t batch, int32_t kv_heads,
+                                 int32_t n_queries, size_t* bytes) {
+  if (!h || !bytes) return fail(TQ_ERR_INVALID_ARGUMENT, "NULL handle or output");
+  if (batch < 0 || kv_heads <= 0 || n_queries < 0) return fail(TQ_ERR_INVALID_ARGUMENT, "bad shape");
+  *bytes = tq::plan_scan(h->c, batch, kv_heads, n_queries).ws_total;
+  return ok();
+}
+
+tq_status tq_score_scan(const tq_handle* h, const void* q, tq_dtype q_dt, int32_t batch,
+                        int32_t kv_heads, int32_t n_queries, const void* records,
+                        int64_t capacity, int64_t n_tokens, float* scores, void* workspace,
+                        size_t ws_bytes, hipStream_t stream) {
+  if (!h) return fail(TQ_ERR_INVALID_ARGUMENT, "handle is NULL");
+  size_t es;
+  if (!elem_size(q_dt, &es)) return fail(TQ_ERR_INVALID_ARGUMENT, "unknown query dtype");
+  if (batch < 0 || kv_heads <= 0 || n_queries < 0 || n_tokens < 0 || n_tokens > capacity)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "bad scan shape (n_tokens must be <= capacity)");
+  if ((int64_t)batch * n_queries * n_tokens == 0) return ok();
+  if (2 * 64 * (h->c.d + h->c.m + 4) * 4 > 160 * 1024)
+    return fail(TQ_ERR_UNSUPPORTED, "scan tile does not fit in LDS for head_dim %d, qjl_dim %d", h->c.d, h->c.m);
+  if (!q || !records || !scores) return fail(TQ_ERR_INVALID_ARGUMENT, "NULL input or output");
+  if (!aligned(records, 16)) return fail(TQ_ERR_INVALID_ARGUMENT, "records not 16-byte aligned");
+  tq::ScanPlan plan = tq::plan_scan(h->c, batch, kv_heads, n_queries);
+  if (!workspace || ws_bytes < plan.ws_total || !aligned(workspace, 256))
+    return fail(TQ_ERR_WORKSPACE_TOO_SMALL, "scan needs %zu bytes of workspace", plan.ws_total);
+  return device_status(tq::launch_scan(h->c, h->dc, plan, q, q_dt, batch, kv_heads, n_queries,
+                                       records, capacity, n_tokens, scores, workspace, stream),
+                       "scan launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,104 @@
+// Internal declarations shared by the host runtime (tq_host.cpp) and the gfx950 kernels
+// (tq_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/tq.h"
+
+namespace tq {
+
+constexpr int kMaxLevels = 16;   // 2^4: key/value codes have at most 4 bits
+constexpr int kWave = 64;
+
+// Per-handle constants passed by value to every kernel.
+struct Consts {
+  float key_levels[kMaxLevels];
+  float key_bounds[kMaxLevels];   // 2^kb - 1 used
+  float val_levels[kMaxLevels];
+  float val_bounds[kMaxLevels];   // 2^vb - 1 used
+  int d, kb, m, vb;
+  int kbytes, sbytes, vbytes;     // code / sign field sizes in bytes
+  int rec_bytes;                  // record stride in bytes (multiple of 16)
+  int norm_off;                   // byte offset of r_k (then rho, r_v)
+  float inv_sqrt_d;               // 1/sqrt(d) rounded to float32
+  double sqrt_d;                  // sqrt(d) in float64
+  float qjl_coef;                 // sqrt(pi/2)/m rounded to float32 (0 when m = 0)
+};
+
+// Device buffers a handle owns.
+struct DevConsts {
+  const float* pi;        // [d][d] row-major (x = Pi k)
+  const float* s;         // [m][d] row-major
+  const float* pi_mfma;   // Pi in the order the compress kernel's MFMA A operand reads it
+  const float* s_mfma;    // S in the same order
+};
+
+// ---- launchers (tq_kernels.hip) ----------------------------------------------------------
+hipError_t launch_compress(const Consts& c, const DevConsts& dc, const void* k, const void* v,
+                           tq_dtype dt, int batch, int64_t n_tokens, int heads,
+                           int64_t seq_stride, int64_t tok_stride, int64_t head_stride,
+                           void* records, int64_t capacity, int64_t first_slot,
+                           hipStream_t stream);
+
+hipError_t launch_debug_quantize(const Consts& c, const float* z_k, const float* p,
+                                 const float* r_k, const float* rho, const float* z_v,
+                                 const float* r_v, int64_t n, void* records,
+                                 hipStream_t stream);
+
+struct DecodePlan {
+  int chunk;        // tokens per split-K chunk
+  int n_chunks;
+  int group;        // q_heads / kv_heads
+  int hpl;          // heads per lane (1 or 4)
+  bool key_pairs;   // key LUT indexed by pairs of codes (else single codes)
+  bool sign_bytes;  // QJL LUT indexed by bytes (else nibbles)
+  size_t lds_bytes;
+  size_t ws_qx, ws_qs, ws_part, ws_total;   // workspace offsets / size
+};
+
+bool plan_decode(const Consts& c, int batch, int q_heads, int kv_heads, int64_t n_max,
+                 DecodePlan* plan);
+
+hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan& plan,
+                         const void* q, tq_dtype q_dt, int batch, int q_heads, int kv_heads,
+                         const void* records, int64_t capacity, const int32_t* seq_lens,
+                         const void* hot_k, const void* hot_v, tq_dtype hot_dt,
+                         const int32_t* hot_lens, int64_t hot_capacity,
+                         const int32_t* sel_idx, int k_sel, float scale, float* out, float* lse,
+                         float* logits, void* workspace, hipStream_t stream);
+
+struct IndexPlan {
+  int chunk, n_chunks;
+  size_t ws_mean, ws_csum, ws_ccnt, ws_total;
+};
+IndexPlan plan_index(const Consts& c, int batch, int heads, int64_t n_tokens);
+hipError_t launch_sign_index(const Consts& c, const IndexPlan& plan, const void* k, tq_dtype dt,
+                             int batch, int64_t n_tokens, int heads, int64_t seq_stride,
+                             int64_t tok_stride, int64_t head_stride, void* index,
+                             float* codebook, float* mean, int64_t capacity, int64_t first_slot,
+                             void* workspace, hipStream_t stream);
+
+struct SelectPlan {
+  size_t ws_lut, ws_scores, ws_total;
+};
+SelectPlan plan_select(const Consts& c, int batch, int heads, int64_t capacity);
+hipError_t launch_select(const Consts& c, const SelectPlan& plan, const void* q, tq_dtype q_dt,
+                         int batch, int q_heads, int kv_heads, const void* index,
+                         const float* codebook, int64_t capacity, const int32_t* seq_lens,
+                         int k, int32_t* out_idx, int32_t* out_count, int32_t* out_scores,
+                         void* workspace, hipStream_t stream);
+
+struct ScanPlan {
+  size_t ws_q, ws_total;
+};
+ScanPlan plan_scan(const Consts& c, int batch, int heads, int n_queries);
+hipError_t launch_scan(const Consts& c, const DevConsts& dc, const ScanPlan& plan, const void* q,
+                       tq_dtype q_dt, int batch, int heads, int n_queries, const void* records,
+                       int64_t capacity, int64_t n_tokens, float* scores, void* workspace,
+                       hipStream_t stream);
+
+}  // namespace tq

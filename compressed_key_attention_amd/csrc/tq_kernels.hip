@@ -1,0 +1,1495 @@
+// gfx950 (MI355X) kernels of libtq.
+//
+//  compress_kernel       rotation and QJL projection as float64 MFMA products
+//                        (v_mfma_f64_16x16x4f64), quantize/pack epilogue, one record per token
+//  debug_quantize_kernel records from given rotated coordinates (same packing code)
+//  query_prep_kernel     q_x = Pi q, q_s = S q_x (float64 accumulate)
+//  decode_scan_kernel    split-K scan over packed records: LUT-GEMV key scores, online softmax,
+//                        rotated-domain value aggregation; one partial (m, l, o_x) per chunk
+//  decode_merge_kernel   log-sum-exp merge of the partials + exact segment + un-rotation
+//  index_* kernels       Self-Indexing sign index (channel mean, patterns, centroids)
+//  select_* kernels      integer LUT-GEMV scores, radix select, ordered compaction
+//  scan_* kernels        bulk multi-query score scan
+//
+// Method sources are cited at each kernel; the arithmetic each performs is stated there.
+
+#include <algorithm>
+#include <cfloat>
+#include <cmath>
+
+#include "tq_internal.h"
+
+namespace tq {
+
+namespace {
+
+constexpr float kNegInf = -INFINITY;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+
+// Load n (multiple of 8 for 16-bit types, of 4 for f32) consecutive elements starting at a
+// 16-byte aligned address, converting to float32 (exact for bf16/f16/f32).
+template <int N>
+__device__ __forceinline__ void load_row(const void* base, tq_dtype dt, int64_t elem_off, bool valid,
+                                         float (&out)[N]) {
+  if (!valid) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) out[i] = 0.0f;
+    return;
+  }
+  if (dt == TQ_F32) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + elem_off);
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      uint4 u = p[i];
+      out[4 * i + 0] = __uint_as_float(u.x);
+      out[4 * i + 1] = __uint_as_float(u.y);
+      out[4 * i + 2] = __uint_as_float(u.z);
+      out[4 * i + 3] = __uint_as_float(u.w);
+    }
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem_off);
+#pragma unroll
+    for (int i = 0; i < N / 8; ++i) {
+      uint4 u = p[i];
+      uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (dt == TQ_BF16) {
+          out[8 * i + 2 * j] = bf16_bits_to_f32(w[j] & 0xFFFFu);
+          out[8 * i + 2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
+        } else {
+          out[8 * i + 2 * j] = f16_bits_to_f32(w[j] & 0xFFFFu);
+          out[8 * i + 2 * j + 1] = f16_bits_to_f32(w[j] >> 16);
+        }
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ float load_elem(const void* base, tq_dtype dt, int64_t off) {
+  if (dt == TQ_F32) return static_cast<const float*>(base)[off];
+  const uint32_t b = static_cast<const uint16_t*>(base)[off];
+  return dt == TQ_BF16 ? bf16_bits_to_f32(b) : f16_bits_to_f32(b);
+}
+
+// Code of a float32 coordinate: number of boundaries it reaches, c = #{j : z >= tau_j}.
+// Unused boundary slots hold +inf.
+__device__ __forceinline__ uint32_t quantize_code(float z, const float* bounds) {
+  uint32_t c = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxLevels - 1; ++j) c += (z >= bounds[j]) ? 1u : 0u;
+  return c;
+}
+
+// Append `nbits` low bits of `v` to a little-endian bit writer that flushes whole bytes.
+struct ByteWriter {
+  uint8_t* dst;
+  uint64_t acc;
+  int n;
+  __device__ __forceinline__ void put(uint32_t v, int nbits) {
+    acc |= (uint64_t)v << n;
+    n += nbits;
+    while (n >= 8) {
+      *dst++ = (uint8_t)acc;
+      acc >>= 8;
+      n -= 8;
+    }
+  }
+};
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+int num_cus() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0;
+    hipDeviceProp_t p;
+    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&p, dev) == hipSuccess)
+      n = p.multiProcessorCount;
+    if (n <= 0) n = 256;
+  }
+  return n;
+}
+
+inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Kernels that take more than 64 KB of dynamic LDS declare it once per kernel.
+template <typename K>
+void allow_lds(K kernel, size_t bytes) {
+  if (bytes > 64 * 1024)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+}  // namespace
+
+// =========================================================================================
+// Compression.  TurboQuant page (de.news.hada.io/topic?id=27867), "Funktionsweise von
+// TurboQuant": step 1 rotates the vector at random and applies a fixed per-coordinate
+// quantizer; step 2 adds a 1-bit QJL sketch of the residual ("QJL: Eine 1-Bit-Methode ohne
+// Overhead").  Per token-head: r = |k|, x = Pi k, z = x * (sqrt(d)/r) rounded to float32,
+// c = #{j : z >= tau_j}, e = x - (r32/sqrt(d)) gamma[c], rho = |e|, bit_j = [(S e)_j >= 0];
+// values: codes and r_v only.  All of x, e, S e are float64 (MFMA f64), so the integer
+// decisions match a float64 evaluation up to summation order.
+//
+// Wave tile = 16 token-heads.  MFMA 16x16x4 f64: lane l supplies A[l%16][l/16] and
+// B[l/16][l%16]; accumulator register r of lane l holds C[l/16 + 4r][l%16].  A = rows of Pi
+// (or S), permuted on the host so that lane group g = l/16, register r of output tile ct
+// holds coordinate (d/4) g + 4 ct + r; B = the token's input at contraction index
+// (d/4) g + s for k-step s.  Hence each lane ends up with d/4 consecutive rotated
+// coordinates of one token, and the residual needed as the B operand of the projection at
+// k-step s is the lane's own register (tile s/4, register s%4).
+// =========================================================================================
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+struct CompressArgs {
+  Consts c;
+  const float* pi_m;
+  const float* s_m;
+  const void* k;
+  const void* v;
+  tq_dtype dt;
+  int heads;
+  int64_t n_tokens, seq_stride, tok_stride, head_stride;
+  uint8_t* records;
+  int64_t capacity, first_slot;
+  int64_t tiles_per_bh, n_tiles;
+  int s_in_lds;
+};
+
+template <int D>
+__device__ __forceinline__ void rotate_tile(const float* lds_pi, const float (&in)[D / 4], int lane,
+                                            f64x4 (&acc)[D / 16]) {
+  constexpr int Q = D / 4, CT = D / 16;
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) acc[ct] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int s = 0; s < Q; ++s) {
+    const double b = (double)in[s];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const double a = (double)lds_pi[(ct * Q + s) * 64 + lane];
+      acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[ct], 0, 0, 0);
+    }
+  }
+}
+
+// Epilogue for one rotated vector held as acc[ct][r] = x[(d/4) g + 4 ct + r]:
+// z, codes packed into `dst` (bit offset 0 = the lane's first coordinate).  Returns via
+// `acc` the residual e = x - a*gamma[c] when want_residual.
+template <int D>
+__device__ __forceinline__ void quantize_rotated(f64x4 (&acc)[D / 16], double zscale, double a,
+                                                 const float* levels, const float* bounds, int bits,
+                                                 uint8_t* dst, bool want_residual) {
+  constexpr int CT = D / 16;
+  ByteWriter w{dst, 0, 0};
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float z = (float)(acc[ct][r] * zscale);
+      const uint32_t code = quantize_code(z, bounds);
+      w.put(code, bits);
+      if (want_residual) acc[ct][r] = acc[ct][r] - a * (double)levels[code];
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void compress_kernel(CompressArgs A) {
+  constexpr int Q = D / 4, CT = D / 16;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const Consts& c = A.c;
+  float* lds_pi = reinterpret_cast<float*>(smem);
+  float* lds_s = lds_pi + D * D;
+  float* lds_tab = lds_s + (A.s_in_lds ? c.m * D : 0);   // 4 x 16 floats
+  uint8_t* stage_all = reinterpret_cast<uint8_t*>(lds_tab + 4 * kMaxLevels);
+
+  // constants to LDS
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(A.pi_m);
+    uint4* dst = reinterpret_cast<uint4*>(lds_pi);
+    for (int i = threadIdx.x; i < D * D / 4; i += blockDim.x) dst[i] = src[i];
+    if (A.s_in_lds) {
+      const uint4* s2 = reinterpret_cast<const uint4*>(A.s_m);
+      uint4* d2 = reinterpret_cast<uint4*>(lds_s);
+      for (int i = threadIdx.x; i < c.m * D / 4; i += blockDim.x) d2[i] = s2[i];
+    }
+    if (threadIdx.x < kMaxLevels) {
+      lds_tab[threadIdx.x] = c.key_levels[threadIdx.x];
+      lds_tab[kMaxLevels + threadIdx.x] = c.key_bounds[threadIdx.x];
+      lds_tab[2 * kMaxLevels + threadIdx.x] = c.val_levels[threadIdx.x];
+      lds_tab[3 * kMaxLevels + threadIdx.x] = c.val_bounds[threadIdx.x];
+    }
+  }
+  __syncthreads();
+  const float* s_src = A.s_in_lds ? lds_s : A.s_m;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  const int tok = lane & 15, g = lane >> 4;
+  uint8_t* stage = stage_all + (size_t)wave * 16 * c.rec_bytes;
+  const int mtiles = c.m / 16;
+
+  for (int64_t tile = (int64_t)blockIdx.x * nwaves + wave; tile < A.n_tiles;
+       tile += (int64_t)gridDim.x * nwaves) {
+    const int64_t bh = tile / A.tiles_per_bh;
+    const int64_t t0 = (tile % A.tiles_per_bh) * 16;
+    const int64_t b = bh / A.heads;
+    const int h = (int)(bh % A.heads);
+    const int64_t t = t0 + tok;
+    const bool valid = t < A.n_tokens;
+    const int64_t row = b * A.seq_stride + t * A.tok_stride + h * A.head_stride + (int64_t)Q * g;
+    uint8_t* rec = stage + tok * c.rec_bytes;
+
+    // ---------------- keys ----------------
+    float in[Q];
+    load_row<Q>(A.k, A.dt, row, valid, in);
+    double n2 = 0.0;
+#pragma unroll
+    for (int s = 0; s < Q; ++s) n2 += (double)in[s] * (double)in[s];
+    n2 += __shfl_xor(n2, 16);
+    n2 += __shfl_xor(n2, 32);
+    const double r = sqrt(n2);
+    const float r32 = (float)r;
+    f64x4 x[CT];
+    rotate_tile<D>(lds_pi, in, lane, x);
+    const double zs = r > 0.0 ? c.sqrt_d / r : 0.0;
+    const double a = (double)r32 / c.sqrt_d;
+    quantize_rotated<D>(x, zs, a, lds_tab, lds_tab + kMaxLevels, c.kb, rec + (Q * g * c.kb) / 8,
+                        true);
+    double e2 = 0.0;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) e2 += x[ct][rr] * x[ct][rr];
+    e2 += __shfl_xor(e2, 16);
+    e2 += __shfl_xor(e2, 32);
+    const float rho32 = (float)sqrt(e2);
+
+    // ---------------- QJL sketch of the residual ----------------
+    for (int pass = 0; pass * 8 < mtiles; ++pass) {
+      f64x4 p[8];
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) p[ct] = f64x4{0.0, 0.0, 0.0, 0.0};
+      const int nt = min(8, mtiles - pass * 8);
+#pragma unroll
+      for (int s = 0; s < Q; ++s) {
+        const double bop = x[s / 4][s % 4];
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+          if (ct < nt) {
+            const double aop = (double)s_src[((pass * 8 + ct) * Q + s) * 64 + lane];
+            p[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(aop, bop, p[ct], 0, 0, 0);
+          }
+        }
+      }
+      // lane group g holds p_j for j = (m/4) g + 32 pass + 4 ct + rr
+      ByteWriter w{rec + c.kbytes + (c.m / 4) * g / 8 + 4 * pass, 0, 0};
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct)
+        if (ct < nt)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) w.put(((float)p[ct][rr] >= 0.0f) ? 1u : 0u, 1);
+    }
+
+    // ---------------- values ----------------
+    load_row<Q>(A.v, A.dt, row, valid, in);
+    double v2 = 0.0;
+#pragma unroll
+    for (int s = 0; s < Q; ++s) v2 += (double)in[s] * (double)in[s];
+    v2 += __shfl_xor(v2, 16);
+    v2 += __shfl_xor(v2, 32);
+    const double rv = sqrt(v2);
+    rotate_tile<D>(lds_pi, in, lane, x);
+    const double zsv = rv > 0.0 ? c.sqrt_d / rv : 0.0;
+    quantize_rotated<D>(x, zsv, 0.0, lds_tab + 2 * kMaxLevels, lds_tab + 3 * kMaxLevels, c.vb,
+                        rec + c.kbytes + c.sbytes + (Q * g * c.vb) / 8, false);
+
+    if (g == 0) {
+      float* nrm = reinterpret_cast<float*>(rec + c.norm_off);
+      nrm[0] = r32;
+      nrm[1] = rho32;
+      nrm[2] = (float)rv;
+    } else if (g == 1) {
+      for (int i = c.norm_off + 12; i < c.rec_bytes; ++i) rec[i] = 0;
+    }
+    wave_lds_sync();
+    // copy the staged records (16 consecutive slots of one (b, h)) to global memory
+    const int64_t nvalid = min((int64_t)16, A.n_tokens - t0);
+    const int n16 = (int)(nvalid * c.rec_bytes / 16);
+    uint4* gdst = reinterpret_cast<uint4*>(A.records + ((bh * A.capacity) + A.first_slot + t0) * c.rec_bytes);
+    const uint4* lsrc = reinterpret_cast<const uint4*>(stage);
+    for (int i = lane; i < n16; i += 64) gdst[i] = lsrc[i];
+    wave_lds_sync();
+  }
+}
+
+hipError_t launch_compress(const Consts& c, const DevConsts& dc, const void* k, const void* v,
+                           tq_dtype dt, int batch, int64_t n_tokens, int heads, int64_t seq_stride,
+                           int64_t tok_stride, int64_t head_stride, void* records,
+                           int64_t capacity, int64_t first_slot, hipStream_t stream) {
+  CompressArgs A;
+  A.c = c;
+  A.pi_m = dc.pi_mfma;
+  A.s_m = dc.s_mfma;
+  A.k = k;
+  A.v = v;
+  A.dt = dt;
+  A.heads = heads;
+  A.n_tokens = n_tokens;
+  A.seq_stride = seq_stride;
+  A.tok_stride = tok_stride;
+  A.head_stride = head_stride;
+  A.records = static_cast<uint8_t*>(records);
+  A.capacity = capacity;
+  A.first_slot = first_slot;
+  A.tiles_per_bh = (n_tokens + 15) / 16;
+  A.n_tiles = A.tiles_per_bh * batch * heads;
+  const int threads = 256, nwaves = threads / 64;
+  const size_t base = (size_t)c.d * c.d * 4 + 4 * kMaxLevels * 4 + (size_t)nwaves * 16 * c.rec_bytes;
+  const size_t with_s = base + (size_t)c.m * c.d * 4;
+  A.s_in_lds = with_s <= 160 * 1024 ? 1 : 0;
+  const size_t lds = A.s_in_lds ? with_s : base;
+  int64_t blocks = (A.n_tiles + nwaves - 1) / nwaves;
+  blocks = std::min<int64_t>(blocks, (int64_t)num_cus());
+  if (c.d == 128) {
+    allow_lds(compress_kernel<128>, lds);
+    hipLaunchKernelGGL(compress_kernel<128>, dim3((unsigned)blocks), dim3(threads), lds, stream, A);
+  } else {
+    allow_lds(compress_kernel<64>, lds);
+    hipLaunchKernelGGL(compress_kernel<64>, dim3((unsigned)blocks), dim3(threads), lds, stream, A);
+  }
+  return hipGetLastError();
+}
+
+// Records from given float32 rotated inputs (the quantize + pack stage alone).
+__global__ void debug_quantize_kernel(Consts c, const float* z_k, const float* p, const float* r_k,
+                                      const float* rho, const float* z_v, const float* r_v,
+                                      int64_t n, uint8_t* records) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n) return;
+  uint8_t* rec = records + t * c.rec_bytes;
+  ByteWriter w{rec, 0, 0};
+  for (int i = 0; i < c.d; ++i) w.put(quantize_code(z_k[t * c.d + i], c.key_bounds), c.kb);
+  ByteWriter ws{rec + c.kbytes, 0, 0};
+  for (int j = 0; j < c.m; ++j) ws.put(p[t * c.m + j] >= 0.0f ? 1u : 0u, 1);
+  ByteWriter wv{rec + c.kbytes + c.sbytes, 0, 0};
+  for (int i = 0; i < c.d; ++i) wv.put(quantize_code(z_v[t * c.d + i], c.val_bounds), c.vb);
+  float* nrm = reinterpret_cast<float*>(rec + c.norm_off);
+  nrm[0] = r_k[t];
+  nrm[1] = rho[t];
+  nrm[2] = r_v[t];
+  for (int i = c.norm_off + 12; i < c.rec_bytes; ++i) rec[i] = 0;
+}
+
+hipError_t launch_debug_quantize(const Consts& c, const float* z_k, const float* p, const float* r_k,
+                                 const float* rho, const float* z_v, const float* r_v, int64_t n,
+                                 void* records, hipStream_t stream) {
+  const int threads = 128;
+  hipLaunchKernelGGL(debug_quantize_kernel, dim3((unsigned)((n + threads - 1) / threads)), dim3(threads),
+                     0, stream, c, z_k, p, r_k, rho, z_v, r_v, n, static_cast<uint8_t*>(records));
+  return hipGetLastError();
+}
+
+// =========================================================================================
+// Decode attention.  Query prep: q_x = Pi q, q_s = S q_x in float64 (one block per query).
+// =========================================================================================
+__global__ void query_prep_kernel(const float* __restrict__ pi, const float* __restrict__ s, int d,
+                                  int m, const void* q, tq_dtype q_dt, float* qx_out,
+                                  float* qs_out) {
+  __shared__ double qv[256];
+  __shared__ double xv[256];
+  const int64_t row = blockIdx.x;  // flattened (b, h)
+  for (int i = threadIdx.x; i < d; i += blockDim.x) qv[i] = (double)load_elem(q, q_dt, row * d + i);
+  __syncthreads();
+  for (int i = threadIdx.x; i < d; i += blockDim.x) {
+    double acc = 0.0;
+    for (int j = 0; j < d; ++j) acc += (double)pi[i * d + j] * qv[j];
+    xv[i] = acc;
+    qx_out[row * d + i] = (float)acc;
+  }
+  __syncthreads();
+  for (int k = threadIdx.x; k < m; k += blockDim.x) {
+    double acc = 0.0;
+    for (int i = 0; i < d; ++i) acc += (double)s[k * d + i] * xv[i];
+    qs_out[row * m + k] = (float)acc;
+  }
+}
+
+// -----------------------------------------------------------------------------------------
+// Decode scan.  For the G query heads of one (sequence, KV head) and one chunk of tokens:
+//   s_t = (r_k/sqrt(d)) sum_i q_x,i gamma_k[c_t,i] + sqrt(pi/2)/m rho_t sum_j q_s,j (2 bit_t,j - 1)
+// (TurboQuant page, "QJL": the asymmetric estimator, full-precision query against 1-bit
+// data), logit = scale * s_t, running softmax, o_x += p_t (r_v,t/sqrt(d)) gamma_v[c^v_t].
+// Key sums are LUT-GEMV lookups (as the Self-Indexing page, "Methodologie" 3, does for its
+// selector): a table of sum_{i in pair} q_x,i gamma[c_i] for every pair of codes, and a table
+// of sum_{j in byte} q_s,j (+-1) for every byte of sign bits, both in LDS, each entry holding
+// the HPL heads of one head group.
+// Lane layout: LPT = (d/32) * (G/HPL) lanes per token; lane (cq, hg) handles coordinates
+// [32 cq, 32 cq + 32) and heads [HPL hg, HPL hg + HPL).  Lanes keep private running maxima
+// (raised lazily, only when a logit exceeds the max by kLazy) and private accumulators that
+// are merged across lanes and waves at the end of the chunk.
+// -----------------------------------------------------------------------------------------
+constexpr float kLazy = 8.0f;
+constexpr int kDecodeThreads = 512;
+
+struct DecodeArgs {
+  const float* qx;
+  const float* qs;
+  const uint8_t* records;
+  const int32_t* seq_lens;
+  const int32_t* sel_idx;
+  float* part;
+  float* logits;
+  int64_t capacity, logit_stride;
+  int d, m, kbytes, sbytes, rec_bytes, norm_off;
+  int G, q_heads, kv_heads, k_sel, chunk, n_chunks, sign_bytes;
+  float scale, inv_sqrt_d, qjl_coef;
+  float key_levels[kMaxLevels];
+  float val_levels[kMaxLevels];
+};
+
+template <int NW>
+__device__ __forceinline__ uint32_t field(const uint32_t (&w)[NW], int pos, int nbits) {
+  const int wi = pos >> 5, sh = pos & 31;
+  uint32_t v = w[wi] >> sh;
+  if (sh + nbits > 32 && wi + 1 < NW) v |= w[wi + 1] << (32 - sh);
+  return v & ((1u << nbits) - 1u);
+}
+
+template <int HPL, int BK, int BV>
+__global__ __launch_bounds__(kDecodeThreads) void decode_scan_kernel(DecodeArgs A) {
+  constexpr bool kPairs = BK <= 3;
+  constexpr int kEnt = kPairs ? (1 << (2 * BK)) : (1 << BK);   // entries per key table
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  const int d = A.d, G = A.G, NHG = G / HPL, LPTc = d / 32, LPT = LPTc * NHG, TPW = 64 / LPT;
+  const int b = blockIdx.z, hkv = blockIdx.y, chunk = blockIdx.x;
+  const int nkt = kPairs ? d / 2 : d;                          // key tables per head group
+  const int sgrp = A.sign_bytes ? A.m / 8 : A.m / 4;            // sign tables per head group
+  const int sent = A.sign_bytes ? 256 : 16;
+  float* lut_k = lds;                                           // [NHG][nkt][kEnt][HPL]
+  float* lut_s = lut_k + NHG * nkt * kEnt * HPL;                // [NHG][sgrp][sent][HPL]
+  float* gam_v = lut_s + NHG * sgrp * sent * HPL;               // [16]
+
+  const int64_t qrow0 = ((int64_t)b * A.q_heads + (int64_t)hkv * G);  // first query head row
+  // ---- LUT build ----
+  {
+    const float* qx = A.qx + qrow0 * d;
+    const int nk = NHG * nkt * kEnt * HPL;
+    for (int e = threadIdx.x; e < nk; e += blockDim.x) {
+      const int j = e % HPL;
+      const int ent = (e / HPL) % kEnt;
+      const int tbl = (e / HPL / kEnt) % nkt;
+      const int hg = e / HPL / kEnt / nkt;
+      const float* qh = qx + (int64_t)(hg * HPL + j) * d;
+      float val;
+      if (kPairs) {
+        const int c0 = ent & ((1 << BK) - 1), c1 = ent >> BK;
+        val = fmaf(qh[2 * tbl + 1], A.key_levels[c1], qh[2 * tbl] * A.key_levels[c0]);
+      } else {
+        val = qh[tbl] * A.key_levels[ent];
+      }
+      lut_k[e] = val;
+    }
+    const float* qs = A.qs + qrow0 * A.m;
+    const int ns = NHG * sgrp * sent * HPL;
+    const int per = A.sign_bytes ? 8 : 4;
+    for (int e = threadIdx.x; e < ns; e += blockDim.x) {
+      const int j = e % HPL;
+      const int ent = (e / HPL) % sent;
+      const int grp = (e / HPL / sent) % sgrp;
+      const int hg = e / HPL / sent / sgrp;
+      const float* qh = qs + (int64_t)(hg * HPL + j) * A.m + grp * per;
+      float val = 0.0f;
+      for (int k = 0; k < per; ++k) val += ((ent >> k) & 1) ? qh[k] : -qh[k];
+      lut_s[e] = val;
+    }
+    if (threadIdx.x < kMaxLevels) gam_v[threadIdx.x] = A.val_levels[threadIdx.x];
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  const int lt = lane % LPT, cq = lt % LPTc, hg = lt / LPTc, slot = lane / LPT;
+  const bool gather = A.sel_idx != nullptr;
+  int n = gather ? A.k_sel : min((int64_t)A.seq_lens[b], A.capacity);
+  const int c0 = chunk * A.chunk, c1 = min(n, c0 + A.chunk);
+  const uint8_t* recs = A.records + ((int64_t)b * A.kv_heads + hkv) * A.capacity * A.rec_bytes;
+  const int32_t* sel = gather ? A.sel_idx + ((int64_t)b * A.kv_heads + hkv) * A.k_sel : nullptr;
+
+  float mrun[HPL], lsum[HPL], acc[HPL][32];
+#pragma unroll
+  for (int j = 0; j < HPL; ++j) {
+    mrun[j] = kNegInf;
+    lsum[j] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc[j][i] = 0.0f;
+  }
+  const float* lk = lut_k + (hg * nkt + (kPairs ? 16 : 32) * cq) * kEnt * HPL;
+  const int nsw = A.m / 32;   // sign dwords per token
+
+  for (int base = c0 + wave * TPW; base < c1; base += nwaves * TPW) {
+    const int pos = base + slot;
+    int64_t t = pos;
+    bool valid = pos < c1;
+    if (gather && valid) t = sel[pos];
+    valid = valid && t >= 0 && t < A.capacity;
+    const uint8_t* rec = recs + (valid ? t : 0) * A.rec_bytes;
+    uint32_t kw[BK], vw[BV];
+#pragma unroll
+    for (int i = 0; i < BK; ++i) kw[i] = valid ? reinterpret_cast<const uint32_t*>(rec + cq * 4 * BK)[i] : 0u;
+#pragma unroll
+    for (int i = 0; i < BV; ++i)
+      vw[i] = valid ? reinterpret_cast<const uint32_t*>(rec + A.kbytes + A.sbytes + cq * 4 * BV)[i] : 0u;
+    const float* nrm = reinterpret_cast<const float*>(rec + A.norm_off);
+    const float rk = valid ? nrm[0] : 0.0f, rho = valid ? nrm[1] : 0.0f, rv = valid ? nrm[2] : 0.0f;
+
+    // key code part: sum over this lane's 32 coordinates
+    float cs[HPL];
+#pragma unroll
+    for (int j = 0; j < HPL; ++j) cs[j] = 0.0f;
+    if (kPairs) {
+#pragma unroll
+      for (int p = 0; p < 16; ++p) {
+        const uint32_t idx = field<BK>(kw, 2 * p * BK, 2 * BK);
+        const float* e = lk + (p * kEnt + idx) * HPL;
+        if (HPL == 4) {
+          const float4 v = *reinterpret_cast<const float4*>(e);
+          cs[0] += v.x; cs[HPL > 1 ? 1 : 0] += v.y; cs[HPL > 2 ? 2 : 0] += v.z; cs[HPL > 3 ? 3 : 0] += v.w;
+        } else {
+#pragma unroll
+          for (int j = 0; j < HPL; ++j) cs[j] += e[j];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const uint32_t idx = field<BK>(kw, i * BK, BK);
+        const float* e = lk + (i * kEnt + idx) * HPL;
+        if (HPL == 4) {
+          const float4 v = *reinterpret_cast<const float4*>(e);
+          cs[0] += v.x; cs[HPL > 1 ? 1 : 0] += v.y; cs[HPL > 2 ? 2 : 0] += v.z; cs[HPL > 3 ? 3 : 0] += v.w;
+        } else {
+#pragma unroll
+          for (int j = 0; j < HPL; ++j) cs[j] += e[j];
+        }
+        // keep at most 8 table reads in flight (register pressure next to 4 x 32 accumulators)
+        if (HPL == 4 && (i % 8) == 7) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // QJL part: this lane's sign dwords
+    float qsum[HPL];
+#pragma unroll
+    for (int j = 0; j < HPL; ++j) qsum[j] = 0.0f;
+    for (int jw = cq; jw < nsw; jw += LPTc) {
+      const uint32_t sw = valid ? reinterpret_cast<const uint32_t*>(rec + A.kbytes)[jw] : 0u;
+      if (A.sign_bytes) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float* e = lut_s + ((hg * sgrp + jw * 4 + q4) * 256 + ((sw >> (8 * q4)) & 255u)) * HPL;
+#pragma unroll
+          for (int j = 0; j < HPL; ++j) qsum[j] += e[j];
+        }
+      } else {
+#pragma unroll
+        for (int q8 = 0; q8 < 8; ++q8) {
+          const float* e = lut_s + ((hg * sgrp + jw * 8 + q8) * 16 + ((sw >> (4 * q8)) & 15u)) * HPL;
+#pragma unroll
+          for (int j = 0; j < HPL; ++j) qsum[j] += e[j];
+        }
+      }
+    }
+    float logit[HPL];
+    const float ak = rk * A.inv_sqrt_d, aq = A.qjl_coef * rho;
+#pragma unroll
+    for (int j = 0; j < HPL; ++j) {
+      float sj = fmaf(aq, qsum[j], ak * cs[j]);
+      for (int msk = 1; msk < LPTc; msk <<= 1) sj += __shfl_xor(sj, msk);
+      logit[j] = A.scale * sj;
+    }
+    if (A.logits && valid && cq == 0) {
+#pragma unroll
+      for (int j = 0; j < HPL; ++j)
+        A.logits[(qrow0 + hg * HPL + j) * A.logit_stride + pos] = logit[j];
+    }
+    // lazy online softmax
+    float w[HPL];
+#pragma unroll
+    for (int j = 0; j < HPL; ++j) {
+      if (valid && logit[j] > mrun[j] + kLazy) {
+        const float f = mrun[j] == kNegInf ? 0.0f : __expf(mrun[j] - logit[j]);
+        lsum[j] *= f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) acc[j][i] *= f;
+        mrun[j] = logit[j];
+      }
+      const float p = valid ? __expf(logit[j] - mrun[j]) : 0.0f;
+      lsum[j] += p;
+      w[j] = p * rv * A.inv_sqrt_d;
+    }
+    // values
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float gv = gam_v[field<BV>(vw, i * BV, BV)];
+#pragma unroll
+      for (int j = 0; j < HPL; ++j) acc[j][i] = fmaf(w[j], gv, acc[j][i]);
+    }
+  }
+
+  // ---- merge all (wave, token slot) partials of the block through LDS, one head at a time --
+  __syncthreads();   // the LUTs are no longer needed
+  const int nthr = blockDim.x;
+  float* pacc = lds;                     // [nthr][33]  accumulators of head j (+1 pad)
+  float* pf = pacc + nthr * 33;          // [nthr]      per-lane scale exp(m - M)
+  float* pl = pf + nthr;                 // [nthr]      per-lane l
+  float* pm = pl + nthr;                 // [NHG]       block maximum per head group
+  const int stride = d + 2;
+  for (int j = 0; j < HPL; ++j) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) pacc[threadIdx.x * 33 + i] = acc[j][i];
+    pf[threadIdx.x] = mrun[j];
+    pl[threadIdx.x] = lsum[j];
+    __syncthreads();
+    // block maximum of head (hg, j) over the lanes that own it (cq = 0 lanes carry m and l)
+    for (int hh = threadIdx.x; hh < NHG; hh += nthr) {
+      float mx = kNegInf;
+      for (int t2 = hh * LPTc; t2 < nthr; t2 += LPT) mx = fmaxf(mx, pf[t2]);
+      pm[hh] = mx;
+    }
+    __syncthreads();
+    {
+      const int hh = (threadIdx.x % LPT) / LPTc;
+      const float mt = pf[threadIdx.x], mx = pm[hh];
+      const float f = mt == kNegInf ? 0.0f : __expf(mt - mx);
+      __syncthreads();
+      pf[threadIdx.x] = f;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < NHG * stride; e += nthr) {
+      const int hh = e / stride, col = e % stride;
+      float v;
+      if (col == 0) {
+        v = pm[hh];
+      } else if (col == 1) {
+        v = 0.0f;
+        for (int t2 = hh * LPTc; t2 < nthr; t2 += LPT) v += pl[t2] * pf[t2];
+      } else {
+        const int i = col - 2, cqo = i / 32, io = i % 32;
+        v = 0.0f;
+        for (int t2 = hh * LPTc + cqo; t2 < nthr; t2 += LPT) v += pacc[t2 * 33 + io] * pf[t2];
+      }
+      A.part[((qrow0 + hh * HPL + j) * A.n_chunks + chunk) * stride + col] = v;
+    }
+    __syncthreads();
+  }
+}
+
+// Merge: log-sum-exp of the chunk partials, the exact (hot) segment in the same softmax
+// (Monarch v3 page, "Wie es funktioniert"), and o = Pi^T o_x + o_hot, divided by the sum.
+struct MergeArgs {
+  const float* pi;
+  const float* part;
+  const void* q;
+  tq_dtype q_dt;
+  const void* hot_k;
+  const void* hot_v;
+  tq_dtype hot_dt;
+  const int32_t* hot_lens;
+  int64_t hot_capacity, logit_hot_off, logit_stride;
+  float* out;
+  float* lse;
+  float* logits;
+  int d, G, q_heads, kv_heads, n_chunks;
+  float scale;
+};
+
+constexpr int kMergeThreads = 256;
+
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs A) {
+  __shared__ float qv[256];
+  __shared__ float ox[256];
+  __shared__ float oh[256];
+  __shared__ float hl[kMergeThreads];
+  __shared__ float red[kMergeThreads];
+  __shared__ float s_stat[2];
+  const int hq = blockIdx.x, b = blockIdx.y, d = A.d, hkv = hq / A.G;
+  const int64_t row = (int64_t)b * A.q_heads + hq;
+  const int stride = d + 2;
+  const float* pr = A.part + row * A.n_chunks * stride;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) {
+    qv[i] = load_elem(A.q, A.q_dt, row * d + i);
+    oh[i] = 0.0f;
+  }
+  // global max over chunk partials and hot logits
+  float mx = kNegInf;
+  for (int c = threadIdx.x; c < A.n_chunks; c += blockDim.x) mx = fmaxf(mx, pr[(int64_t)c * stride]);
+  const int nh = A.hot_lens ? (int)min((int64_t)A.hot_lens[b], A.hot_capacity) : 0;
+  const int64_t hbase = ((int64_t)b * A.kv_heads + hkv) * A.hot_capacity * d;
+  __syncthreads();
+  for (int t = threadIdx.x; t < nh; t += blockDim.x) {
+    float dot = 0.0f;
+    for (int i = 0; i < d; ++i) dot = fmaf(qv[i], load_elem(A.hot_k, A.hot_dt, hbase + (int64_t)t * d + i), dot);
+    const float lg = A.scale * dot;
+    mx = fmaxf(mx, lg);
+    if (A.logits) A.logits[row * A.logit_stride + A.logit_hot_off + t] = lg;
+  }
+  red[threadIdx.x] = mx;
+  __syncthreads();
+  for (int s = blockDim.x / 2; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  __syncthreads();
+  // sum of weights
+  float l = 0.0f;
+  if (M != kNegInf) {
+    for (int c = threadIdx.x; c < A.n_chunks; c += blockDim.x) {
+      const float mc = pr[(int64_t)c * stride];
+      if (mc != kNegInf) l += pr[(int64_t)c * stride + 1] * __expf(mc - M);
+    }
+  }
+  // cold rotated-domain output
+  for (int i = threadIdx.x; i < d; i += blockDim.x) {
+    float acc = 0.0f;
+    if (M != kNegInf)
+      for (int c = 0; c < A.n_chunks; ++c) {
+        const float mc = pr[(int64_t)c * stride];
+        if (mc != kNegInf) acc += pr[(int64_t)c * stride + 2 + i] * __expf(mc - M);
+      }
+    ox[i] = acc;
+  }
+  // hot tokens, in tiles of blockDim: weights, then value sums
+  for (int t0 = 0; t0 < nh; t0 += blockDim.x) {
+    const int t = t0 + threadIdx.x;
+    float p = 0.0f;
+    if (t < nh) {
+      float dot = 0.0f;
+      for (int i = 0; i < d; ++i) dot = fmaf(qv[i], load_elem(A.hot_k, A.hot_dt, hbase + (int64_t)t * d + i), dot);
+      p = __expf(A.scale * dot - M);
+    }
+    l += p;
+    __syncthreads();
+    hl[threadIdx.x] = p;
+    __syncthreads();
+    const int nt = min((int)blockDim.x, nh - t0);
+    for (int i = threadIdx.x; i < d; i += blockDim.x) {
+      float acc = oh[i];
+      for (int u = 0; u < nt; ++u)
+        acc = fmaf(hl[u], load_elem(A.hot_v, A.hot_dt, hbase + (int64_t)(t0 + u) * d + i), acc);
+      oh[i] = acc;
+    }
+  }
+  red[threadIdx.x] = l;
+  __syncthreads();
+  for (int s = blockDim.x / 2; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    s_stat[0] = red[0];
+    s_stat[1] = M;
+  }
+  __syncthreads();
+  const float L = s_stat[0];
+  for (int i = threadIdx.x; i < d; i += blockDim.x) {
+    float o = 0.0f;
+    if (L > 0.0f) {
+      for (int k = 0; k < d; ++k) o = fmaf(A.pi[(int64_t)k * d + i], ox[k], o);
+      o = (o + oh[i]) / L;
+    }
+    A.out[row * d + i] = o;
+  }
+  if (threadIdx.x == 0 && A.lse) A.lse[row] = L > 0.0f ? s_stat[1] + logf(L) : kNegInf;
+}
+
+bool plan_decode(const Consts& c, int batch, int q_heads, int kv_heads, int64_t n_max,
+                 DecodePlan* plan) {
+  const int G = q_heads / kv_heads;
+  const int hpl = (G % 4 == 0) ? 4 : 1;
+  const int lpt = (c.d / 32) * (G / hpl);
+  if (lpt > 64 || (lpt & (lpt - 1)) != 0) return false;
+  plan->group = G;
+  plan->hpl = hpl;
+  plan->key_pairs = c.kb <= 3;
+  const size_t key_tab = (size_t)G * (plan->key_pairs ? (c.d / 2) * (1 << (2 * c.kb)) : c.d * (1 << c.kb));
+  const size_t sign_bytes_tab = (size_t)G * (c.m / 8) * 256;
+  const size_t sign_nib_tab = (size_t)G * (c.m / 4) * 16;
+  const size_t budget = 150 * 1024 / 4;
+  plan->sign_bytes = key_tab + sign_bytes_tab + kMaxLevels <= budget;
+  const size_t lut = key_tab + (plan->sign_bytes ? sign_bytes_tab : sign_nib_tab) + kMaxLevels;
+  const size_t red = (size_t)kDecodeThreads * 36 + 64;
+  const size_t floats = std::max(lut, red);
+  if (floats > 160 * 1024 / 4) return false;
+  plan->lds_bytes = floats * 4;
+  // split-K: aim at ~2 blocks per CU (one resident at a time when the LUTs are large)
+  const int64_t units = (int64_t)std::max(batch, 1) * kv_heads;
+  const int64_t target_blocks = 2 * (int64_t)num_cus();
+  int64_t chunk = (n_max * units + target_blocks - 1) / std::max<int64_t>(target_blocks, 1);
+  chunk = std::max<int64_t>(chunk, 256);
+  chunk = std::min<int64_t>(chunk, 16384);
+  chunk = (chunk + 255) / 256 * 256;
+  plan->chunk = (int)chunk;
+  plan->n_chunks = (int)std::max<int64_t>(1, (n_max + chunk - 1) / chunk);
+  const size_t rows = (size_t)std::max(batch, 1) * q_heads;
+  plan->ws_qx = 0;
+  plan->ws_qs = align256(rows * c.d * 4);
+  plan->ws_part = plan->ws_qs + align256(rows * std::max(c.m, 1) * 4);
+  plan->ws_total = plan->ws_part + align256(rows * plan->n_chunks * (c.d + 2) * 4);
+  return true;
+}
+
+template <int HPL>
+static void launch_scan_hpl(const DecodeArgs& a, int kb, int vb, dim3 grid, size_t lds, hipStream_t st) {
+#define TQ_DEC(BK_, BV_)                                                                         \
+  if (kb == BK_ && vb == BV_) {                                                                  \
+    allow_lds(decode_scan_kernel<HPL, BK_, BV_>, lds);                                            \
+    hipLaunchKernelGGL((decode_scan_kernel<HPL, BK_, BV_>), grid, dim3(kDecodeThreads), lds, st, a); \
+    return;                                                                                      \
+  }
+  TQ_DEC(2, 2) TQ_DEC(2, 3) TQ_DEC(2, 4) TQ_DEC(3, 2) TQ_DEC(3, 3) TQ_DEC(3, 4)
+  TQ_DEC(4, 2) TQ_DEC(4, 3) TQ_DEC(4, 4)
+#undef TQ_DEC
+}
+
+hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan& plan, const void* q,
+                         tq_dtype q_dt, int batch, int q_heads, int kv_heads, const void* records,
+                         int64_t capacity, const int32_t* seq_lens, const void* hot_k,
+                         const void* hot_v, tq_dtype hot_dt, const int32_t* hot_lens,
+                         int64_t hot_capacity, const int32_t* sel_idx, int k_sel, float scale,
+                         float* out, float* lse, float* logits, void* workspace,
+                         hipStream_t stream) {
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* qx = reinterpret_cast<float*>(ws + plan.ws_qx);
+  float* qs = reinterpret_cast<float*>(ws + plan.ws_qs);
+  float* part = reinterpret_cast<float*>(ws + plan.ws_part);
+  const float sc = scale > 0.0f ? scale : c.inv_sqrt_d;
+  const int rows = batch * q_heads;
+  hipLaunchKernelGGL(query_prep_kernel, dim3(rows), dim3(128), 0, stream, dc.pi, dc.s, c.d, c.m, q,
+                     q_dt, qx, qs);
+  const int64_t n_cold = sel_idx ? k_sel : capacity;
+  const int64_t lstride = n_cold + (hot_lens ? hot_capacity : 0);
+  DecodeArgs a;
+  a.qx = qx;
+  a.qs = qs;
+  a.records = static_cast<const uint8_t*>(records);
+  a.seq_lens = seq_lens;
+  a.sel_idx = sel_idx;
+  a.part = part;
+  a.logits = logits;
+  a.capacity = capacity;
+  a.logit_stride = lstride;
+  a.d = c.d;
+  a.m = c.m;
+  a.kbytes = c.kbytes;
+  a.sbytes = c.sbytes;
+  a.rec_bytes = c.rec_bytes;
+  a.norm_off = c.norm_off;
+  a.G = plan.group;
+  a.q_heads = q_heads;
+  a.kv_heads = kv_heads;
+  a.k_sel = k_sel;
+  a.chunk = plan.chunk;
+  a.n_chunks = plan.n_chunks;
+  a.sign_bytes = plan.sign_bytes ? 1 : 0;
+  a.scale = sc;
+  a.inv_sqrt_d = c.inv_sqrt_d;
+  a.qjl_coef = c.qjl_coef;
+  for (int i = 0; i < kMaxLevels; ++i) {
+    a.key_levels[i] = c.key_levels[i];
+    a.val_levels[i] = c.val_levels[i];
+  }
+  dim3 grid(plan.n_chunks, kv_heads, batch);
+  if (plan.hpl == 4)
+    launch_scan_hpl<4>(a, c.kb, c.vb, grid, plan.lds_bytes, stream);
+  else
+    launch_scan_hpl<1>(a, c.kb, c.vb, grid, plan.lds_bytes, stream);
+  MergeArgs mg;
+  mg.pi = dc.pi;
+  mg.part = part;
+  mg.q = q;
+  mg.q_dt = q_dt;
+  mg.hot_k = hot_k;
+  mg.hot_v = hot_v;
+  mg.hot_dt = hot_dt;
+  mg.hot_lens = hot_lens;
+  mg.hot_capacity = hot_capacity;
+  mg.logit_hot_off = n_cold;
+  mg.logit_stride = lstride;
+  mg.out = out;
+  mg.lse = lse;
+  mg.logits = logits;
+  mg.d = c.d;
+  mg.G = plan.group;
+  mg.q_heads = q_heads;
+  mg.kv_heads = kv_heads;
+  mg.n_chunks = plan.n_chunks;
+  mg.scale = sc;
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(q_heads, batch), dim3(kMergeThreads), 0, stream, mg);
+  return hipGetLastError();
+}
+
+// =========================================================================================
+// Self-Indexing sign index (Self-Indexing KVCache page, "Methodologie" 1-2): per (sequence,
+// KV head) the channel mean mu over the tokens indexed, bit = [k >= mu] (float32), one 4-bit
+// pattern per 4-channel group, and 16 centroids per group = mean of the members' (k - mu)
+// sub-vectors (0 for a pattern without members).  Sums are float64 and taken in a fixed
+// order (per-chunk partial sums, then chunks in order), so the result is deterministic.
+// =========================================================================================
+constexpr int kIndexSub = 128;   // tokens staged per sub-tile in the centroid pass
+
+IndexPlan plan_index(const Consts& c, int batch, int heads, int64_t n_tokens) {
+  IndexPlan p;
+  int64_t chunk = 4096;
+  const int64_t max_chunks = 64;
+  if (n_tokens > chunk * max_chunks) chunk = (n_tokens + max_chunks - 1) / max_chunks;
+  chunk = (chunk + kIndexSub - 1) / kIndexSub * kIndexSub;
+  p.chunk = (int)chunk;
+  p.n_chunks = (int)std::max<int64_t>(1, (n_tokens + chunk - 1) / chunk);
+  const size_t units = (size_t)std::max(batch, 1) * heads;
+  const int ng = c.d / 4;
+  p.ws_mean = 0;                                                         // f64 [units][chunks][d], then f32 mu [units][d]
+  const size_t mean_bytes = align256(units * p.n_chunks * c.d * 8) + align256(units * c.d * 4);
+  p.ws_csum = mean_bytes;                                                // f64 [units][chunks][ng][16][4]
+  p.ws_ccnt = p.ws_csum + align256(units * p.n_chunks * ng * 16 * 4 * 8);  // i32 [units][chunks][ng][16]
+  p.ws_total = p.ws_ccnt + align256(units * p.n_chunks * ng * 16 * 4);
+  return p;
+}
+
+struct IndexArgs {
+  const void* k;
+  tq_dtype dt;
+  int d, heads, chunk, n_chunks;
+  int64_t n_tokens, seq_stride, tok_stride, head_stride, capacity, first_slot;
+  double* mean_part;
+  float* mu;
+  double* csum;
+  int32_t* ccnt;
+  uint8_t* index;
+  float* codebook;
+  float* mean_out;
+};
+
+__global__ __launch_bounds__(256) void index_mean_kernel(IndexArgs A) {
+  __shared__ double part[256];
+  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z, d = A.d;
+  const int lanes_per_ch = blockDim.x / d;  // token lanes
+  const int ch = threadIdx.x % d, tl = threadIdx.x / d;
+  const int64_t t0 = (int64_t)chunk * A.chunk, t1 = min(A.n_tokens, t0 + A.chunk);
+  double s = 0.0;
+  for (int64_t t = t0 + tl; t < t1; t += lanes_per_ch)
+    s += (double)load_elem(A.k, A.dt, b * A.seq_stride + t * A.tok_stride + h * A.head_stride + ch);
+  part[threadIdx.x] = s;
+  __syncthreads();
+  if (tl == 0) {
+    double tot = 0.0;
+    for (int u = 0; u < lanes_per_ch; ++u) tot += part[u * d + ch];
+    A.mean_part[(((int64_t)b * A.heads + h) * A.n_chunks + chunk) * d + ch] = tot;
+  }
+}
+
+__global__ void index_mean_final_kernel(IndexArgs A) {
+  const int h = blockIdx.x, b = blockIdx.y, d = A.d;
+  const int64_t unit = (int64_t)b * A.heads + h;
+  for (int ch = threadIdx.x; ch < d; ch += blockDim.x) {
+    double s = 0.0;
+    for (int c = 0; c < A.n_chunks; ++c) s += A.mean_part[(unit * A.n_chunks + c) * d + ch];
+    const float mu = (float)(s / (double)A.n_tokens);
+    A.mu[unit * d + ch] = mu;
+    if (A.mean_out) A.mean_out[unit * d + ch] = mu;
+  }
+}
+
+// Patterns of a chunk of tokens (index records) and per-chunk centroid sums.
+__global__ __launch_bounds__(256) void index_pattern_kernel(IndexArgs A) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z, d = A.d, ng = d / 4;
+  const int64_t unit = (int64_t)b * A.heads + h;
+  float* mu = reinterpret_cast<float*>(smem);                       // [d]
+  float* kt = mu + d;                                               // [kIndexSub][d] (k - mu as float64 later)
+  uint8_t* pat = reinterpret_cast<uint8_t*>(kt + kIndexSub * d);    // [kIndexSub][ng]
+  double* acc = reinterpret_cast<double*>(pat + ((kIndexSub * ng + 7) / 8) * 8);  // [d][16]
+  int32_t* cnt = reinterpret_cast<int32_t*>(acc + d * 16);          // [ng][16]
+  for (int i = threadIdx.x; i < d; i += blockDim.x) mu[i] = A.mu[unit * d + i];
+  for (int i = threadIdx.x; i < d * 16; i += blockDim.x) acc[i] = 0.0;
+  for (int i = threadIdx.x; i < ng * 16; i += blockDim.x) cnt[i] = 0;
+  __syncthreads();
+  const int64_t t0 = (int64_t)chunk * A.chunk, t1 = min(A.n_tokens, t0 + A.chunk);
+  for (int64_t s0 = t0; s0 < t1; s0 += kIndexSub) {
+    const int ns = (int)min((int64_t)kIndexSub, t1 - s0);
+    for (int e = threadIdx.x; e < ns * d; e += blockDim.x) {
+      const int tt = e / d, ch = e % d;
+      kt[e] = load_elem(A.k, A.dt, b * A.seq_stride + (s0 + tt) * A.tok_stride + h * A.head_stride + ch);
+    }
+    __syncthreads();
+    // one thread per token: pattern bits, index record
+    for (int tt = threadIdx.x; tt < ns; tt += blockDim.x) {
+      uint8_t* rec = A.index + (unit * A.capacity + A.first_slot + s0 + tt) * (d / 8);
+      for (int g2 = 0; g2 < ng; g2 += 2) {
+        uint32_t byte = 0;
+        for (int u = 0; u < 2; ++u) {
+          uint32_t p = 0;
+          for (int j = 0; j < 4; ++j) p |= (kt[tt * d + 4 * (g2 + u) + j] >= mu[4 * (g2 + u) + j] ? 1u : 0u) << j;
+          pat[tt * ng + g2 + u] = (uint8_t)p;
+          byte |= p << (4 * u);
+        }
+        rec[g2 / 2] = (uint8_t)byte;
+      }
+    }
+    __syncthreads();
+    // one thread per channel: members' (k - mu) summed in token order
+    for (int ch = threadIdx.x; ch < d; ch += blockDim.x) {
+      const int g = ch / 4;
+      for (int tt = 0; tt < ns; ++tt) {
+        const int p = pat[tt * ng + g];
+        acc[ch * 16 + p] += (double)kt[tt * d + ch] - (double)mu[ch];
+        if ((ch & 3) == 0) cnt[g * 16 + p] += 1;
+      }
+    }
+    __syncthreads();
+  }
+  for (int e = threadIdx.x; e < ng * 16 * 4; e += blockDim.x) {
+    const int g = e / 64, p = (e / 4) % 16, j = e % 4;
+    A.csum[((unit * A.n_chunks + chunk) * ng + g) * 64 + p * 4 + j] = acc[(4 * g + j) * 16 + p];
+  }
+  for (int e = threadIdx.x; e < ng * 16; e += blockDim.x)
+    A.ccnt[(unit * A.n_chunks + chunk) * ng * 16 + e] = cnt[e];
+}
+
+__global__ void index_centroid_final_kernel(IndexArgs A) {
+  const int h = blockIdx.x, b = blockIdx.y, ng = A.d / 4;
+  const int64_t unit = (int64_t)b * A.heads + h;
+  for (int e = threadIdx.x; e < ng * 64; e += blockDim.x) {
+    const int g = e / 64, p = (e / 4) % 16;
+    double s = 0.0;
+    int64_t n = 0;
+    for (int c = 0; c < A.n_chunks; ++c) {
+      s += A.csum[((unit * A.n_chunks + c) * ng + g) * 64 + (e % 64)];
+      n += A.ccnt[(unit * A.n_chunks + c) * ng * 16 + g * 16 + p];
+    }
+    A.codebook[unit * ng * 64 + e] = n > 0 ? (float)(s / (double)n) : 0.0f;
+  }
+}
+
+hipError_t launch_sign_index(const Consts& c, const IndexPlan& plan, const void* k, tq_dtype dt,
+                             int batch, int64_t n_tokens, int heads, int64_t seq_stride,
+                             int64_t tok_stride, int64_t head_stride, void* index, float* codebook,
+                             float* mean, int64_t capacity, int64_t first_slot, void* workspace,
+                             hipStream_t stream) {
+  if (n_tokens == 0) return hipSuccess;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const size_t units = (size_t)batch * heads;
+  IndexArgs A;
+  A.k = k;
+  A.dt = dt;
+  A.d = c.d;
+  A.heads = heads;
+  A.chunk = plan.chunk;
+  A.n_chunks = plan.n_chunks;
+  A.n_tokens = n_tokens;
+  A.seq_stride = seq_stride;
+  A.tok_stride = tok_stride;
+  A.head_stride = head_stride;
+  A.capacity = capacity;
+  A.first_slot = first_slot;
+  A.mean_part = reinterpret_cast<double*>(ws + plan.ws_mean);
+  A.mu = reinterpret_cast<float*>(ws + plan.ws_mean + align256(units * plan.n_chunks * c.d * 8));
+  A.csum = reinterpret_cast<double*>(ws + plan.ws_csum);
+  A.ccnt = reinterpret_cast<int32_t*>(ws + plan.ws_ccnt);
+  A.index = static_cast<uint8_t*>(index);
+  A.codebook = codebook;
+  A.mean_out = mean;
+  dim3 grid(plan.n_chunks, heads, batch);
+  hipLaunchKernelGGL(index_mean_kernel, grid, dim3(256), 0, stream, A);
+  hipLaunchKernelGGL(index_mean_final_kernel, dim3(heads, batch), dim3(128), 0, stream, A);
+  const int ng = c.d / 4;
+  const size_t lds = c.d * 4 + (size_t)kIndexSub * c.d * 4 + ((kIndexSub * ng + 7) / 8) * 8 +
+                     (size_t)c.d * 16 * 8 + (size_t)ng * 16 * 4;
+  allow_lds(index_pattern_kernel, lds);
+  hipLaunchKernelGGL(index_pattern_kernel, grid, dim3(256), lds, stream, A);
+  hipLaunchKernelGGL(index_centroid_final_kernel, dim3(heads, batch), dim3(256), 0, stream, A);
+  return hipGetLastError();
+}
+
+// =========================================================================================
+// Top-k selection from the sign index (Self-Indexing page, "Methodologie" 3, LUT-GEMV).
+// LUT[h][g][p] = ((q0 c0 + q1 c1) + q2 c2) + q3 c3 in float64 (no fused multiply-add, so the
+// rounding is fixed), s = largest integer with G (d/4) max|LUT| 2^s <= 2^30, entries
+// rint(LUT 2^s) (half to even) summed over the group's heads: integer scores, exact and
+// independent of summation order.  Ranking: score descending, then token index ascending.
+// =========================================================================================
+SelectPlan plan_select(const Consts& c, int batch, int heads, int64_t capacity) {
+  SelectPlan p;
+  const size_t units = (size_t)std::max(batch, 1) * heads;
+  p.ws_lut = 0;                                                 // i32 [units][d/8][256]
+  p.ws_scores = align256(units * (c.d / 8) * 256 * 4);          // i32 [units][capacity]
+  p.ws_total = p.ws_scores + align256(units * std::max<int64_t>(capacity, 1) * 4);
+  return p;
+}
+
+__device__ __forceinline__ double lut_entry(double q0, double q1, double q2, double q3, const float* cen) {
+#pragma clang fp contract(off)
+  double t = q0 * (double)cen[0];
+  t = t + q1 * (double)cen[1];
+  t = t + q2 * (double)cen[2];
+  t = t + q3 * (double)cen[3];
+  return t;
+}
+
+__global__ __launch_bounds__(256) void select_lut_kernel(const void* q, tq_dtype q_dt, const float* codebook,
+                                                         int d, int G, int q_heads, int heads,
+                                                         int32_t* lut_out) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int h = blockIdx.x, b = blockIdx.y, ng = d / 4;
+  const int64_t unit = (int64_t)b * heads + h;
+  double* lut = reinterpret_cast<double*>(smem);           // [G][ng][16]
+  int32_t* comb = reinterpret_cast<int32_t*>(lut + G * ng * 16);  // [ng][16]
+  __shared__ double mx[256];
+  const float* cb = codebook + unit * ng * 64;
+  double m = 0.0;
+  for (int e = threadIdx.x; e < G * ng * 16; e += blockDim.x) {
+    const int j = e / (ng * 16), g = (e / 16) % ng, p = e % 16;
+    const int64_t qrow = ((int64_t)b * q_heads + (int64_t)h * G + j) * d + 4 * g;
+    const double v = lut_entry((double)load_elem(q, q_dt, qrow), (double)load_elem(q, q_dt, qrow + 1),
+                               (double)load_elem(q, q_dt, qrow + 2), (double)load_elem(q, q_dt, qrow + 3),
+                               cb + g * 64 + p * 4);
+    lut[e] = v;
+    m = fmax(m, fabs(v));
+  }
+  mx[threadIdx.x] = m;
+  __syncthreads();
+  for (int s = blockDim.x / 2; s > 0; s >>= 1) {
+    if (threadIdx.x < s) mx[threadIdx.x] = fmax(mx[threadIdx.x], mx[threadIdx.x + s]);
+    __syncthreads();
+  }
+  const double a = (double)(G * ng) * mx[0];
+  int sexp = 0;
+  if (a != 0.0) {
+    int e;
+    const double f = frexp(a, &e);
+    sexp = 30 - e + (f == 0.5 ? 1 : 0);
+  }
+  for (int e = threadIdx.x; e < ng * 16; e += blockDim.x) {
+    int64_t s = 0;
+    for (int j = 0; j < G; ++j) s += (int64_t)rint(ldexp(lut[j * ng * 16 + e], sexp));
+    comb[e] = (int32_t)s;
+  }
+  __syncthreads();
+  // byte table: two groups per index byte (low nibble = even group)
+  for (int e = threadIdx.x; e < (ng / 2) * 256; e += blockDim.x) {
+    const int pg = e / 256, byte = e % 256;
+    lut_out[unit * (ng / 2) * 256 + e] = comb[(2 * pg) * 16 + (byte & 15)] + comb[(2 * pg + 1) * 16 + (byte >> 4)];
+  }
+}
+
+__global__ __launch_bounds__(256) void select_score_kernel(const uint8_t* index, const int32_t* lut_all,
+                                                           const int32_t* seq_lens, int d, int heads,
+                                                           int64_t capacity, int32_t* scores) {
+  __shared__ int32_t lut[16 * 256];
+  const int h = blockIdx.y, b = blockIdx.z, nb = d / 8;
+  const int64_t unit = (int64_t)b * heads + h;
+  for (int e = threadIdx.x; e < nb * 256; e += blockDim.x) lut[e] = lut_all[unit * nb * 256 + e];
+  __syncthreads();
+  const int64_t n = min((int64_t)seq_lens[b], capacity);
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n) return;
+  const uint8_t* rec = index + (unit * capacity + t) * nb;
+  int32_t s = 0;
+  if (nb == 16) {
+    const uint4 u = *reinterpret_cast<const uint4*>(rec);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += lut[i * 256 + ((w[i / 4] >> (8 * (i % 4))) & 255u)];
+  } else {
+    for (int i = 0; i < nb; ++i) s += lut[i * 256 + rec[i]];
+  }
+  scores[unit * capacity + t] = s;
+}
+
+constexpr int kSelThreads = 1024;
+
+__device__ __forceinline__ uint32_t order_key(int32_t s) { return (uint32_t)s ^ 0x80000000u; }
+
+// Block-wide exclusive prefix sum of 0/1 flags; returns the prefix, *total the block total.
+__device__ __forceinline__ int block_flag_scan(bool f, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const uint64_t bal = __ballot(f);
+  const int in_wave = __popcll(bal & ((1ull << lane) - 1ull));
+  __syncthreads();
+  if (lane == 0) wsum[wave] = __popcll(bal);
+  __syncthreads();
+  int off = 0, tot = 0;
+  for (int w = 0; w < nw; ++w) {
+    if (w < wave) off += wsum[w];
+    tot += wsum[w];
+  }
+  *total = tot;
+  return off + in_wave;
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const int32_t* scores, const int32_t* seq_lens,
+                                                                  int heads, int64_t capacity, int k,
+                                                                  int32_t* out_idx, int32_t* out_count,
+                                                                  int32_t* out_scores) {
+  __shared__ int hist[256];
+  __shared__ int wsum[kSelThreads / 64];
+  __shared__ uint32_t s_prefix, s_remaining;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int64_t unit = (int64_t)b * heads + h;
+  const int n = (int)min((int64_t)seq_lens[b], capacity);
+  const int kk = min(k, n);
+  const int32_t* sc = scores + unit * capacity;
+  int32_t* oi = out_idx ? out_idx + unit * k : nullptr;
+  int32_t* os = out_scores ? out_scores + unit * k : nullptr;
+  if (threadIdx.x == 0) out_count[unit] = kk;
+  for (int i = kk + threadIdx.x; i < k; i += blockDim.x) {
+    oi[i] = -1;
+    if (os) os[i] = 0;
+  }
+  if (kk == 0) return;
+  uint32_t prefix = 0, mask = 0;
+  uint32_t remaining = (uint32_t)kk;
+  bool take_all = kk == n;
+  if (!take_all) {
+    for (int pass = 3; pass >= 0; --pass) {
+      for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0;
+      __syncthreads();
+      const int sh = 8 * pass;
+      for (int t = threadIdx.x; t < n; t += blockDim.x) {
+        const uint32_t u = order_key(sc[t]);
+        if ((u & mask) == prefix) atomicAdd(&hist[(u >> sh) & 255u], 1);
+      }
+      __syncthreads();
+      if (threadIdx.x < 64) {
+        // lane l owns digits [4l, 4l+4); suffix sums from the top digit down
+        const int l = threadIdx.x;
+        int own = 0;
+        for (int j = 0; j < 4; ++j) own += hist[4 * l + j];
+        // inclusive suffix scan of `own` over lanes (higher lanes hold higher digits)
+        int suf = own;
+        for (int o = 1; o < 64; o <<= 1) {
+          const int v = __shfl_down(suf, o);
+          if (l + o < 64) suf += v;
+        }
+        const int above = suf - own;   // elements whose digit is above 4l+3
+        if (above < (int)remaining && suf >= (int)remaining) {
+          int cum = above;
+          for (int j = 3; j >= 0; --j) {
+            const int hv = hist[4 * l + j];
+            if (cum + hv >= (int)remaining) {
+              s_prefix = prefix | ((uint32_t)(4 * l + j) << sh);
+              s_remaining = remaining - (uint32_t)cum;
+              break;
+            }
+            cum += hv;
+          }
+        }
+      }
+      __syncthreads();
+      prefix = s_prefix;
+      remaining = s_remaining;
+      mask |= 255u << sh;
+      __syncthreads();
+    }
+  }
+  // ordered compaction: all keys > T, then the first `remaining` keys == T in index order
+  const uint32_t T = prefix;
+  int out_base = 0, eq_base = 0;
+  for (int t0 = 0; t0 < n; t0 += blockDim.x) {
+    const int t = t0 + threadIdx.x;
+    uint32_t u = 0;
+    if (t < n) u = order_key(sc[t]);
+    const bool in = t < n;
+    const bool eq = in && !take_all && u == T;
+    int eq_tot;
+    const int eq_before = eq_base + block_flag_scan(eq, wsum, &eq_tot);
+    const bool take = in && (take_all || u > T || (eq && eq_before < (int)remaining));
+    int tk_tot;
+    const int pos = out_base + block_flag_scan(take, wsum, &tk_tot);
+    if (take) {
+      oi[pos] = t;
+      if (os) os[pos] = sc[t];
+    }
+    out_base += tk_tot;
+    eq_base += eq_tot;
+  }
+}
+
+hipError_t launch_select(const Consts& c, const SelectPlan& plan, const void* q, tq_dtype q_dt, int batch,
+                         int q_heads, int kv_heads, const void* index, const float* codebook,
+                         int64_t capacity, const int32_t* seq_lens, int k, int32_t* out_idx,
+                         int32_t* out_count, int32_t* out_scores, void* workspace, hipStream_t stream) {
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int32_t* lut = reinterpret_cast<int32_t*>(ws + plan.ws_lut);
+  int32_t* scores = reinterpret_cast<int32_t*>(ws + plan.ws_scores);
+  const int G = q_heads / kv_heads, ng = c.d / 4;
+  if (capacity > 0) {
+    const size_t lds = (size_t)G * ng * 16 * 8 + (size_t)ng * 16 * 4;
+    hipLaunchKernelGGL(select_lut_kernel, dim3(kv_heads, batch), dim3(256), lds, stream, q, q_dt, codebook,
+                       c.d, G, q_heads, kv_heads, lut);
+    hipLaunchKernelGGL(select_score_kernel, dim3((unsigned)((capacity + 255) / 256), kv_heads, batch), dim3(256),
+                       0, stream, static_cast<const uint8_t*>(index), lut, seq_lens, c.d, kv_heads, capacity,
+                       scores);
+  }
+  hipLaunchKernelGGL(select_topk_kernel, dim3(kv_heads, batch), dim3(kSelThreads), 0, stream, scores, seq_lens,
+                     kv_heads, capacity, k, out_idx, out_count, out_scores);
+  return hipGetLastError();
+}
+
+// =========================================================================================
+// Bulk scan (TurboQuant page, "Leistung bei der Vektorsuche"): every query of a KV head
+// against every record, s = <[q_x ; q_s], [(r_k/sqrt(d)) gamma[c] ; sqrt(pi/2)/m rho (2 bit - 1)]>.
+// A block dequantizes 64 records and stages 64 prepared queries in LDS, then each thread
+// computes a 4 x 4 tile of scores.
+// =========================================================================================
+ScanPlan plan_scan(const Consts& c, int batch, int heads, int n_queries) {
+  ScanPlan p;
+  p.ws_q = 0;
+  p.ws_total = align256((size_t)std::max(batch, 1) * heads * std::max(n_queries, 1) * (c.d + c.m) * 4);
+  return p;
+}
+
+__global__ void scan_prep_kernel(const float* __restrict__ pi, const float* __restrict__ s, int d, int m,
+                                 const void* q, tq_dtype q_dt, float* out) {
+  __shared__ double qv[256];
+  __shared__ double xv[256];
+  const int64_t row = blockIdx.x;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) qv[i] = (double)load_elem(q, q_dt, row * d + i);
+  __syncthreads();
+  float* o = out + row * (d + m);
+  for (int i = threadIdx.x; i < d; i += blockDim.x) {
+    double acc = 0.0;
+    for (int j = 0; j < d; ++j) acc += (double)pi[i * d + j] * qv[j];
+    xv[i] = acc;
+    o[i] = (float)acc;
+  }
+  __syncthreads();
+  for (int k = threadIdx.x; k < m; k += blockDim.x) {
+    double acc = 0.0;
+    for (int i = 0; i < d; ++i) acc += (double)s[k * d + i] * xv[i];
+    o[d + k] = (float)acc;
+  }
+}
+
+constexpr int kScanTile = 64;
+
+struct ScanArgs {
+  const float* qprep;
+  const uint8_t* records;
+  float* scores;
+  int64_t capacity, n_tokens;
+  int d, m, kb, kbytes, rec_bytes, norm_off, heads, n_queries;
+  float inv_sqrt_d, qjl_coef;
+  float key_levels[kMaxLevels];
+};
+
+__global__ __launch_bounds__(256) void scan_kernel(ScanArgs A) {
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  const int K = A.d + A.m, KP = K + 4;   // padded row
+  float* qt = lds;                        // [64][KP]
+  float* kt = lds + kScanTile * KP;       // [64][KP]
+  const int unit = blockIdx.z;
+  const int64_t tok0 = (int64_t)blockIdx.x * kScanTile;
+  const int q0 = blockIdx.y * kScanTile;
+  const uint8_t* recs = A.records + (int64_t)unit * A.capacity * A.rec_bytes;
+  // stage queries
+  for (int e = threadIdx.x; e < kScanTile * K; e += blockDim.x) {
+    const int qi = e / K, kk = e % K;
+    qt[qi * KP + kk] = (q0 + qi < A.n_queries) ? A.qprep[((int64_t)unit * A.n_queries + q0 + qi) * K + kk] : 0.0f;
+  }
+  // dequantize records: 4 threads per token
+  {
+    const int tt = threadIdx.x / 4, part = threadIdx.x % 4;
+    const int64_t t = tok0 + tt;
+    const bool valid = t < A.n_tokens;
+    const uint8_t* rec = recs + (valid ? t : 0) * A.rec_bytes;
+    const float* nrm = reinterpret_cast<const float*>(rec + A.norm_off);
+    const float ak = valid ? nrm[0] * A.inv_sqrt_d : 0.0f;
+    const float aq = valid ? A.qjl_coef * nrm[1] : 0.0f;
+    const uint32_t* kw = reinterpret_cast<const uint32_t*>(rec);
+    for (int i = part; i < A.d; i += 4) {
+      const int pos = i * A.kb, wi = pos >> 5, sh = pos & 31;
+      uint32_t v = kw[wi] >> sh;
+      if (sh + A.kb > 32) v |= kw[wi + 1] << (32 - sh);
+      v &= (1u << A.kb) - 1u;
+      kt[tt * KP + i] = ak * A.key_levels[v];
+    }
+    const uint32_t* sw = reinterpret_cast<const uint32_t*>(rec + A.kbytes);
+    for (int j = part; j < A.m; j += 4) {
+      const uint32_t bit = (sw[j >> 5] >> (j & 31)) & 1u;
+      kt[tt * KP + A.d + j] = bit ? aq : -aq;
+    }
+  }
+  __syncthreads();
+  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;   // tokens tx + 16 j, queries 4 ty + i
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+  for (int kk = 0; kk < K; kk += 4) {
+    float4 qa[4], ka[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qa[i] = *reinterpret_cast<const float4*>(qt + (4 * ty + i) * KP + kk);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ka[j] = *reinterpret_cast<const float4*>(kt + (tx + 16 * j) * KP + kk);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[i][j] = fmaf(qa[i].x, ka[j].x, acc[i][j]);
+        acc[i][j] = fmaf(qa[i].y, ka[j].y, acc[i][j]);
+        acc[i][j] = fmaf(qa[i].z, ka[j].z, acc[i][j]);
+        acc[i][j] = fmaf(qa[i].w, ka[j].w, acc[i][j]);
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int qi = q0 + 4 * ty + i;
+    if (qi >= A.n_queries) continue;
+    float* o = A.scores + ((int64_t)unit * A.n_queries + qi) * A.n_tokens + tok0 + tx;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (tok0 + tx + 16 * j < A.n_tokens) o[16 * j] = acc[i][j];
+  }
+}
+
+hipError_t launch_scan(const Consts& c, const DevConsts& dc, const ScanPlan& plan, const void* q, tq_dtype q_dt,
+                       int batch, int heads, int n_queries, const void* records, int64_t capacity,
+                       int64_t n_tokens, float* scores, void* workspace, hipStream_t stream) {
+  float* qprep = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + plan.ws_q);
+  const int rows = batch * heads * n_queries;
+  hipLaunchKernelGGL(scan_prep_kernel, dim3(rows), dim3(128), 0, stream, dc.pi, dc.s, c.d, c.m, q, q_dt, qprep);
+  ScanArgs a;
+  a.qprep = qprep;
+  a.records = static_cast<const uint8_t*>(records);
+  a.scores = scores;
+  a.capacity = capacity;
+  a.n_tokens = n_tokens;
+  a.d = c.d;
+  a.m = c.m;
+  a.kb = c.kb;
+  a.kbytes = c.kbytes;
+  a.rec_bytes = c.rec_bytes;
+  a.norm_off = c.norm_off;
+  a.heads = heads;
+  a.n_queries = n_queries;
+  a.inv_sqrt_d = c.inv_sqrt_d;
+  a.qjl_coef = c.qjl_coef;
+  for (int i = 0; i < kMaxLevels; ++i) a.key_levels[i] = c.key_levels[i];
+  const size_t lds = (size_t)2 * kScanTile * (c.d + c.m + 4) * 4;
+  dim3 grid((unsigned)((n_tokens + kScanTile - 1) / kScanTile), (unsigned)((n_queries + kScanTile - 1) / kScanTile),
+            (unsigned)(batch * heads));
+  allow_lds(scan_kernel, lds);
+  hipLaunchKernelGGL(scan_kernel, grid, dim3(256), lds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace tq

@@ -1,0 +1,209 @@
+/*
+ * tq.h - C ABI of libtq: TurboQuant-style KV-cache compression and decode attention
+ * computed directly over the compressed cache, for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (sources are the public web pages on the method):
+ *  - Compression (TurboQuant page, de.news.hada.io/topic?id=27867, "Funktionsweise von
+ *    TurboQuant", steps 1 and 2; TurboQuant explainer, chatgpz.de, "Stufe 1" and
+ *    "Stufe 2"): a seeded random rotation Pi, a fixed Lloyd-Max code for N(0,1) applied to
+ *    every rotated coordinate z = (Pi k) * sqrt(d) / |k| (Hacker News comments on the
+ *    TurboQuant page), and a 1-bit QJL sign sketch of the key residual
+ *    ("QJL: Eine 1-Bit-Methode ohne Overhead").  Values get codes only.
+ *  - Decode attention over the compressed cache: inner products estimated from the codes
+ *    and signs, softmax, value aggregation in the rotated basis, optional exact ("hot")
+ *    tokens in the same softmax (Monarch v3 page, "Wie es funktioniert").
+ *  - Self-Indexing top-k (Self-Indexing KVCache page, gist.science 2603.14224,
+ *    "Methodologie" 1-3): 1-bit sign patterns of 4-dim groups after channel-mean
+ *    centring, 16 centroids per group, LUT-GEMV scores, top-k.
+ *  - Bulk scan: estimates for many queries against a whole compressed cache
+ *    (TurboQuant page, "Leistung bei der Vektorsuche").
+ *
+ * Conventions
+ *  - Every entry point returns tq_status.  TQ_OK = 0.  On any other status nothing was
+ *    enqueued and no output was written; tq_last_error() gives a thread-local message.
+ *    Shapes, dtypes, bit widths, alignment and null pointers are validated on the host
+ *    before any launch.  A failing launch returns TQ_ERR_DEVICE.  Faults during
+ *    asynchronous execution surface at the caller's next stream synchronisation.
+ *  - Tensors are caller-owned DEVICE pointers unless a parameter says "host".  Work is
+ *    enqueued on the caller's hipStream_t (NULL = the default stream); the library never
+ *    synchronises the host and never allocates or frees device memory outside
+ *    tq_create/tq_destroy.  Calls that take a workspace need
+ *    tq_*_workspace_size() bytes of device memory, 256-byte aligned.
+ *  - A handle is immutable after tq_create, so concurrent calls on different streams
+ *    are allowed.  Calls that share a workspace or output buffer must be ordered.
+ *  - Inputs must be finite.  Non-finite inputs give unspecified codes and outputs but
+ *    never an out-of-bounds access.
+ *
+ * Record layout (one contiguous record per token per KV head, little-endian):
+ *    [ key codes  : head_dim * key_bits / 8 bytes                      ]
+ *    [ QJL signs  : qjl_dim / 8 bytes  (bit j = 1 iff (S e)_j >= 0)     ]
+ *    [ value codes: head_dim * value_bits / 8 bytes                    ]
+ *    [ r_k float32 | rho float32 | r_v float32 ] [ zero pad to 16 B ]
+ *  A code stream is a little-endian bitstream over 32-bit words: code i occupies stream
+ *  bits [b*i, b*i + b) and may straddle two words.  A cache is an array
+ *  records[batch][kv_heads][capacity][record_bytes].
+ *  Sign index: one record of head_dim/8 bytes per token per KV head; the 4-bit pattern of
+ *  channel group g (channels 4g..4g+3, bit j = channel 4g+j) sits at stream bits
+ *  [4g, 4g+4).  Index array: index[batch][kv_heads][capacity][head_dim/8];
+ *  codebook[batch][kv_heads][head_dim/4][16][4] float32; mean[batch][kv_heads][head_dim].
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tq_status {
+  TQ_OK = 0,
+  TQ_ERR_INVALID_ARGUMENT = 1,   /* bad pointer, shape, stride, dtype or value        */
+  TQ_ERR_UNSUPPORTED = 2,        /* valid but not built (e.g. head_dim not 64 or 128) */
+  TQ_ERR_WORKSPACE_TOO_SMALL = 3,
+  TQ_ERR_OUT_OF_MEMORY = 4,      /* tq_create only                                   */
+  TQ_ERR_DEVICE = 5              /* a HIP call or kernel launch failed               */
+} tq_status;
+
+typedef enum tq_dtype { TQ_F32 = 0, TQ_F16 = 1, TQ_BF16 = 2 } tq_dtype;
+
+typedef struct tq_config {
+  int32_t head_dim;       /* d: 64 or 128                                              */
+  int32_t key_bits;       /* b_k: 1..4 bits per rotated key coordinate                 */
+  int32_t qjl_dim;        /* m: 0 (no QJL sketch) or a multiple of 32, at most 256     */
+  int32_t value_bits;     /* b_v: 1..4                                                 */
+  uint64_t rotation_seed; /* seed of the Gaussian matrix whose QR factor is Pi         */
+  uint64_t qjl_seed;      /* seed of the QJL projection S                              */
+} tq_config;
+
+typedef struct tq_handle tq_handle;
+
+/* Message of the last failing call on this thread ("" if none).  Never NULL. */
+const char* tq_last_error(void);
+
+/* Build the handle's constants on the host and upload them to the current device.
+ *  - Pi (d x d): Q factor of a d x d Gaussian matrix G drawn from rotation_seed, with the
+ *    signs of Q's columns chosen so that R = Q^T G has a positive diagonal, rounded to
+ *    float32 (TurboQuant page, "Funktionsweise", step 1: random rotation).
+ *  - S (m x d): i.i.d. N(0,1) from qjl_seed, float32 (TurboQuant page, "QJL").
+ *  - Lloyd-Max levels/boundaries for N(0,1) at key_bits and value_bits, iterated in
+ *    float64 and rounded to float32 (Hacker News comments on the TurboQuant page).
+ *  Gaussians: SplitMix64 (Steele, Lea, Flood 2014) word i of a seed is
+ *  mix(seed + (i+1) * 0x9E3779B97F4A7C15); pair k of normals is Box-Muller of words 2k,
+ *  2k+1 with u1 = ((w>>11)+1)*2^-53, u2 = (w>>11)*2^-53.  Matrices are filled row-major.
+ *  The only call that allocates device memory.  *out receives the handle. */
+tq_status tq_create(const tq_config* cfg, tq_handle** out);
+tq_status tq_destroy(tq_handle* h);
+
+/* Host-only: the constants tq_create would build, written to HOST arrays (any may be
+ * NULL): pi[d*d], s[m*d], key_levels[2^kb], key_bounds[2^kb - 1], value_levels[2^vb],
+ * value_bounds[2^vb - 1].  Needs no GPU. */
+tq_status tq_host_constants(const tq_config* cfg, float* pi, float* s, float* key_levels,
+                            float* key_bounds, float* value_levels, float* value_bounds);
+
+/* Bytes of one cache record and of one sign-index record (host pointers). */
+tq_status tq_record_bytes(const tq_handle* h, size_t* record_bytes, size_t* index_record_bytes);
+
+/* Compress keys and values into records (TurboQuant page, "Funktionsweise", steps 1-2).
+ *  k, v: element (b, t, h, i) at k[b*seq_stride + t*tok_stride + h*head_stride + i] in
+ *  dtype dt (strides in elements; the innermost dimension is contiguous).
+ *  Writes records[b][h][first_slot + t] for t < n_tokens, b < batch, h < kv_heads;
+ *  requires first_slot + n_tokens <= capacity.  Per token-head: r = |k|;
+ *  x = Pi k, z = x * sqrt(d) / r (z = 0 when r = 0), code c_i = #{j : z_i >= tau_j}
+ *  (float32 comparison); residual e = x - (r/sqrt(d)) gamma[c]; rho = |e|; QJL bit j =
+ *  [(S e)_j >= 0].  Values: codes and r_v only.  The rotation and projection run as
+ *  float64 matrix-core (MFMA) products, so codes equal a float64 reference except where
+ *  a rotated coordinate lies within rounding of a boundary. */
+tq_status tq_compress_kv(const tq_handle* h, const void* k, const void* v, tq_dtype dt,
+                         int32_t batch, int64_t n_tokens, int32_t kv_heads,
+                         int64_t seq_stride, int64_t tok_stride, int64_t head_stride,
+                         void* records, int64_t capacity, int64_t first_slot,
+                         hipStream_t stream);
+
+/* Test entry: records from given rotated inputs (device float32 arrays):
+ *  z_k[n][d], z_v[n][d] (already scaled by sqrt(d)/r), p[n][m] (S e), r_k[n], rho[n],
+ *  r_v[n].  Codes are c = #{j : z >= tau_j}, bits [p >= 0].  Writes records[n]. */
+tq_status tq_debug_quantize(const tq_handle* h, const float* z_k, const float* p,
+                            const float* r_k, const float* rho, const float* z_v,
+                            const float* r_v, int64_t n, void* records, hipStream_t stream);
+
+/* Decode attention over the compressed cache.
+ *  q[b][hq][d] (dtype q_dt); KV head of query head hq is hq / (q_heads / kv_heads).
+ *  Cold tokens of sequence b: slots [0, seq_lens[b]) of records[b][h] (seq_lens: device
+ *  int32[batch], each <= capacity), or, in gather mode (sel_idx != NULL), the slots
+ *  sel_idx[b][h][0..k_sel) that are >= 0 (device int32; -1 entries are skipped; each
+ *  slot < capacity).  Cold logit = scale * s_t with
+ *    s_t = (r_k/sqrt(d)) <Pi q, gamma_k[c_t]> + sqrt(pi/2)/m rho_t <S Pi q, 2 bit_t - 1>
+ *  (the QJL estimator; the second term is absent when m = 0).
+ *  Exact segment (optional, hot_lens != NULL): hot_k/hot_v[b][h][hot_capacity][d] in
+ *  hot_dt, tokens [0, hot_lens[b]); logit = scale * <q, k>; one softmax over cold+hot
+ *  (Monarch v3 page, "Wie es funktioniert").  scale = 0 selects 1/sqrt(d).
+ *  out[b][hq][d] float32 = (Pi^T sum_cold p_t vhat_t + sum_hot p_t v_t) / sum_t p_t,
+ *  vhat_t = (r_v/sqrt(d)) gamma_v[c^v_t]; zero when no token is attended.
+ *  lse[b][hq] (optional) = log sum_t exp(logit_t) (-inf when empty).
+ *  logits (optional, for tests) float32 [b][hq][n_cold_max + hot_capacity], n_cold_max =
+ *  capacity (or k_sel in gather mode); cold logits first, then hot; unattended entries are
+ *  not written.  workspace: tq_decode_workspace_size bytes. */
+tq_status tq_decode_workspace_size(const tq_handle* h, int32_t batch, int32_t q_heads,
+                                   int32_t kv_heads, int64_t capacity, int32_t k_sel,
+                                   size_t* bytes);
+tq_status tq_decode_attention(const tq_handle* h, const void* q, tq_dtype q_dt, int32_t batch,
+                              int32_t q_heads, int32_t kv_heads, const void* records,
+                              int64_t capacity, const int32_t* seq_lens,
+                              const void* hot_k, const void* hot_v, tq_dtype hot_dt,
+                              const int32_t* hot_lens, int64_t hot_capacity,
+                              const int32_t* sel_idx, int32_t k_sel, float scale, float* out,
+                              float* lse, float* logits, void* workspace, size_t ws_bytes,
+                              hipStream_t stream);
+
+/* Self-Indexing sign index of keys over slots [first_slot, first_slot + n_tokens)
+ * (Self-Indexing page, "Methodologie" 1-2).  k addressed as in tq_compress_kv.
+ * mean[b][h][i] = float32(mean_t k), bit = [k >= mean] (float32), pattern per 4-channel
+ * group, codebook[b][h][g][p][0..3] = float32 mean of (k - mean) over members (0 if none).
+ * The mean and centroids use only the tokens of this call.  workspace:
+ * tq_index_workspace_size bytes. */
+tq_status tq_index_workspace_size(const tq_handle* h, int32_t batch, int32_t kv_heads,
+                                  size_t* bytes);
+tq_status tq_build_sign_index(const tq_handle* h, const void* k, tq_dtype dt, int32_t batch,
+                              int64_t n_tokens, int32_t kv_heads, int64_t seq_stride,
+                              int64_t tok_stride, int64_t head_stride, void* index,
+                              float* codebook, float* mean, int64_t capacity,
+                              int64_t first_slot, void* workspace, size_t ws_bytes,
+                              hipStream_t stream);
+
+/* Top-k tokens per (sequence, KV head) from the sign index (Self-Indexing page,
+ * "Methodologie" 3: LUT-GEMV).  Table LUT[g][p] = ((q0 c0 + q1 c1) + q2 c2) + q3 c3 in
+ * float64 for each query head of the group; s = largest integer with
+ * G * (d/4) * max|LUT| * 2^s <= 2^30 (s = 0 if max|LUT| = 0); entries rounded half to
+ * even to integers; score_t = sum over heads and groups (int32, exact).  Ranking: score
+ * descending, then token index ascending.  out_idx[b][h][k] = the min(k, n) chosen slots
+ * in ascending order, -1 padded; out_count[b][h] = min(k, n); out_scores (optional)
+ * [b][h][k] = their scores (0 padded).  n = seq_lens[b] (device int32).  k >= 0.
+ * workspace: tq_select_workspace_size bytes. */
+tq_status tq_select_workspace_size(const tq_handle* h, int32_t batch, int32_t kv_heads,
+                                   int64_t capacity, size_t* bytes);
+tq_status tq_select_topk(const tq_handle* h, const void* q, tq_dtype q_dt, int32_t batch,
+                         int32_t q_heads, int32_t kv_heads, const void* index,
+                         const float* codebook, int64_t capacity, const int32_t* seq_lens,
+                         int32_t k, int32_t* out_idx, int32_t* out_count, int32_t* out_scores,
+                         void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Bulk scan (TurboQuant page, "Leistung bei der Vektorsuche"): for q[b][h][i][d]
+ * (i < n_queries) and every slot t < n_tokens of records[b][h], scores[b][h][i][t] =
+ * s_t as in tq_decode_attention (unscaled estimate, no softmax).  float32 output.
+ * workspace: tq_scan_workspace_size bytes. */
+tq_status tq_scan_workspace_size(const tq_handle* h, int32_t batch, int32_t kv_heads,
+                                 int32_t n_queries, size_t* bytes);
+tq_status tq_score_scan(const tq_handle* h, const void* q, tq_dtype q_dt, int32_t batch,
+                        int32_t kv_heads, int32_t n_queries, const void* records,
+                        int64_t capacity, int64_t n_tokens, float* scores, void* workspace,
+                        size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H_ */

@@ -1,0 +1,87 @@
+"""CPU checks of the C ABI: the library loads, exports what include/tq.h declares, builds the
+same constants as the oracle from independent code, and rejects bad arguments on the host."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tq.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:tq_status|const char\*)\s+(tq_\w+)\s*\(", txt, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    import compressed_key_attention_amd as tq
+    names = _declared()
+    assert len(names) >= 15
+    lib = ctypes.CDLL(tq.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(tq.EXPORTED) == names
+
+
+@pytest.mark.parametrize("cfg", [(128, 3, 128, 4, 303, 304), (64, 3, 64, 4, 1, 2),
+                                 (128, 4, 0, 4, 7, 8), (64, 2, 32, 2, 11, 12), (128, 2, 256, 3, 5, 6)])
+def test_host_constants_equal_oracle(cfg):
+    """Library (C++ SplitMix64 + Box-Muller + Householder QR + Lloyd-Max) and oracle
+    (Python generator + LAPACK QR + scipy Lloyd-Max) are independent implementations of one
+    definition; their float32 constants must agree bit for bit (one ulp tolerated in Pi)."""
+    import compressed_key_attention_amd as tq
+    from oracle import tq_oracle as O
+    d, kb, m, vb, rs, qs = cfg
+    lib = tq.host_constants(d, kb, m, vb, rs, qs)
+    ref = O.Codec(d, kb, m, vb, rs, qs)
+    ulp = np.abs(lib["pi"].view(np.int32).astype(np.int64) - ref.Pi.view(np.int32).astype(np.int64))
+    assert ulp.max() <= 1, ulp.max()
+    assert np.array_equal(lib["s"], ref.S)
+    assert np.array_equal(lib["key_levels"], ref.key_levels)
+    assert np.array_equal(lib["key_bounds"], ref.key_bounds)
+    assert np.array_equal(lib["val_levels"], ref.val_levels)
+    assert np.array_equal(lib["val_bounds"], ref.val_bounds)
+
+
+def _cfg(**kw):
+    import compressed_key_attention_amd as tq
+    base = dict(head_dim=128, key_bits=3, qjl_dim=128, value_bits=4, rotation_seed=1, qjl_seed=2)
+    base.update(kw)
+    return tq.TqConfig(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), 2), (dict(head_dim=0), 1), (dict(key_bits=5), 1), (dict(value_bits=0), 1),
+    (dict(qjl_dim=48), 1), (dict(qjl_dim=512), 1), (dict(key_bits=1), 2), (dict(qjl_dim=-32), 1)])
+def test_config_validation_on_host(kw, status):
+    import compressed_key_attention_amd as tq
+    cfg = _cfg(**kw)
+    assert tq._host_constants(ctypes.byref(cfg), None, None, None, None, None, None) == status
+    assert tq.last_error() != ""
+    h = ctypes.c_void_p()
+    assert tq._create(ctypes.byref(cfg), ctypes.byref(h)) == status
+    assert not h.value
+
+
+def test_null_handle_is_rejected_everywhere():
+    import compressed_key_attention_amd as tq
+    n = ctypes.c_size_t()
+    assert tq._destroy(None) == 1
+    assert tq._record_bytes(None, ctypes.byref(n), None) == 1
+    assert tq._decode_ws(None, 1, 1, 1, 1, 0, ctypes.byref(n)) == 1
+    assert tq._compress(None, None, None, 0, 1, 1, 1, 0, 0, 0, None, 1, 0, None) == 1
+    assert tq._decode(None, None, 0, 1, 1, 1, None, 1, None, None, None, 0, None, 0, None, 0, 0.0,
+                      None, None, None, None, 0, None) == 1
+    assert tq._select(None, None, 0, 1, 1, 1, None, None, 1, None, 1, None, None, None, None, 0, None) == 1
+    assert tq._scan(None, None, 0, 1, 1, 1, None, 1, 1, None, None, 0, None) == 1
+    assert "NULL" in tq.last_error()
+
+
+def test_record_size_formula_matches_oracle():
+    from oracle import tq_oracle as O
+    for d, kb, m, vb in [(128, 3, 128, 4), (64, 3, 64, 4), (128, 4, 0, 4), (64, 2, 32, 2)]:
+        payload = d * kb // 8 + m // 8 + d * vb // 8 + 12
+        assert O.Codec(d, kb, m, vb, 1, 2).record_bytes == (payload + 15) // 16 * 16

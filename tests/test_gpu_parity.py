@@ -1,0 +1,429 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle on identical seeded inputs.
+
+Rules (checked element by element):
+* packing from given rotated inputs: records bytewise equal;
+* compress end to end: norms within 1e-6 relative; a key/value code may differ only where
+  the oracle's rotated coordinate lies within 1e-6 of a boundary; a QJL bit may differ only
+  where |p/rho| <= 1e-6, with p recomputed from the GPU's own codes;
+* decode on identical records: logits and outputs within 1e-4 + 1e-3 |oracle|;
+* sign index: patterns equal except where a key equals its channel mean to rounding;
+  centroids within float32 rounding; top-k sets, counts and scores bit-exact given the same
+  index and codebook;
+* determinism: two runs give identical bytes.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from compressed_key_attention_amd import workloads as W
+from oracle import tq_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL = 1e-4, 1e-3
+
+
+def _tq():
+    import compressed_key_attention_amd as tq
+    return tq
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy() if t.dtype in (torch.bfloat16, torch.float16) else t.detach().cpu().numpy()
+
+
+def _close(gpu, ref, what):
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    bad = np.abs(gpu - ref) > ATOL + RTOL * np.abs(ref)
+    assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} outside tolerance; worst "
+                           f"{np.max(np.abs(gpu - ref) - RTOL * np.abs(ref)):.3e}")
+
+
+_CODECS = {}
+
+
+def _codec(h):
+    key = (h.head_dim, h.key_bits, h.qjl_dim, h.value_bits, h.rotation_seed, h.qjl_seed)
+    if key not in _CODECS:
+        _CODECS[key] = O.Codec(*key)
+    return _CODECS[key]
+
+
+def _handle(w: W.Workload):
+    return _tq().Handle(w.head_dim, w.key_bits, w.qjl_dim, w.value_bits, w.seed * 3 + 1, w.seed * 3 + 2)
+
+
+def check_compress(codec, K, V, rec_gpu):
+    """End-to-end compress rule on one set of tokens: K, V [n, d] float, rec_gpu [n, R] u8."""
+    d = codec.head_dim
+    fg = O.unpack_records(codec, rec_gpu)
+    ref = O.compress(codec, K, V)
+    for key in ("r_k", "r_v"):
+        assert np.allclose(fg[key], ref[key], rtol=1e-6, atol=0), key
+    assert np.all(rec_gpu[:, codec.kbytes + codec.sbytes + codec.vbytes + 12:] == 0)   # zero pad
+    stats = {}
+    for which, X, bounds in (("kc", K, codec.key_bounds), ("vc", V, codec.val_bounds)):
+        _, _, z32, _ = O._rotate_and_code(codec, X, bounds)
+        mism = fg[which] != ref[which]
+        if mism.any():
+            dist = np.min(np.abs(z32[..., None].astype(np.float64) - bounds.astype(np.float64)), axis=-1)
+            assert np.all(dist[mism] <= 1e-6), f"{which}: code mismatch away from a boundary"
+        stats[which] = int(mism.sum())
+    # residual sketch, recomputed from the GPU's codes
+    if codec.qjl_dim:
+        k64 = K.astype(np.float64)
+        x = k64 @ codec.Pi64.T
+        xhat = (fg["r_k"].astype(np.float64) / math.sqrt(d))[:, None] * codec.key_levels.astype(np.float64)[fg["kc"]]
+        e = x - xhat
+        rho = np.sqrt(np.sum(e * e, -1))
+        assert np.allclose(fg["rho"], rho.astype(np.float32), rtol=2e-6, atol=1e-30)
+        p = e @ codec.S64.T
+        want = (p.astype(np.float32) >= 0)
+        mism = (fg["bits"] == 1) != want
+        if mism.any():
+            rel = np.abs(p) / np.maximum(rho, 1e-300)[:, None]
+            assert np.all(rel[mism] <= 1e-6), "QJL bit mismatch away from zero"
+        stats["bits"] = int(mism.sum())
+    return stats
+
+
+def _compress(w, h, K, V, capacity=None, first_slot=0):
+    B, T, H, d = K.shape
+    cap = T + first_slot if capacity is None else capacity
+    rec = torch.full((B, H, cap, h.record_bytes), 0xAB, dtype=torch.uint8, device="cuda")
+    h.compress_kv(K, V, rec, first_slot=first_slot)
+    torch.cuda.synchronize()
+    return rec
+
+
+# ------------------------------------------------------------------ packing -------------
+@pytest.mark.parametrize("cfg", [(128, 3, 128, 4), (64, 3, 64, 4), (128, 4, 0, 4), (128, 2, 256, 3),
+                                 (64, 4, 32, 2), (128, 3, 64, 2)])
+def test_debug_quantize_is_bit_exact(cfg):
+    tq = _tq()
+    d, kb, m, vb = cfg
+    h = tq.Handle(d, kb, m, vb, 5, 6)
+    codec = _codec(h)
+    n = 333
+    rng = np.random.default_rng(sum(cfg))
+    zk = rng.standard_normal((n, d)).astype(np.float32) * 1.5
+    zv = rng.standard_normal((n, d)).astype(np.float32) * 1.5
+    # exact boundaries, their neighbours, signed zeros and far tails
+    zk[0, : len(codec.key_bounds)] = codec.key_bounds
+    zk[1, : len(codec.key_bounds)] = np.nextafter(codec.key_bounds, np.float32(-np.inf))
+    zk[2, :4] = [0.0, -0.0, 1e30, -1e30]
+    zv[0, : len(codec.val_bounds)] = codec.val_bounds
+    p = rng.standard_normal((n, max(m, 1))).astype(np.float32)[:, :m]
+    if m:
+        p[0, :3] = [0.0, -0.0, -1e-40]
+    rk, rho, rv = (rng.random(n).astype(np.float32) + 0.1 for _ in range(3))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    rec = torch.full((n, h.record_bytes), 0xCD, dtype=torch.uint8, device="cuda")
+    h.debug_quantize(dev(zk), dev(p) if m else dev(np.zeros((n, 1), np.float32)), dev(rk), dev(rho), dev(zv),
+                     dev(rv), rec)
+    torch.cuda.synchronize()
+    ref = O.quantize_from_rotated(codec, zk, p, rk, rho, zv, rv)
+    assert np.array_equal(rec.cpu().numpy(), ref)
+
+
+# ------------------------------------------------------------------ compress ------------
+@pytest.mark.parametrize("name,tokens,batch", [("single_head_1k", 1024, 1), ("tinyllama_layer", 1024, 1),
+                                               ("llama8b_decode_32k", 1000, 2), ("sparse_128k_top2048", 777, 1),
+                                               ("bulk_64k_scan", 2000, 1)])
+def test_compress_end_to_end(name, tokens, batch):
+    w = W.small(W.WORKLOADS[name], tokens=tokens, batch=batch)
+    h = _handle(w)
+    codec = _codec(h)
+    K, V = W.make_kv(w, "cpu")
+    K[0, 5] = 0          # a zero key/value vector (codes at the middle cell, rho = 0)
+    V[0, 5] = 0
+    Kc, Vc = K.cuda(), V.cuda()
+    rec = _compress(w, h, Kc, Vc)
+    rec2 = _compress(w, h, Kc, Vc)
+    assert torch.equal(rec, rec2), "compress is not deterministic"
+    r = rec.cpu().numpy()
+    Kn, Vn = _np(K), _np(V)
+    total = {}
+    for b in range(w.batch):
+        for hh in range(w.kv_heads):
+            st = check_compress(codec, Kn[b, :, hh], Vn[b, :, hh], r[b, hh])
+            for k2, v2 in st.items():
+                total[k2] = total.get(k2, 0) + v2
+    f = O.unpack_records(codec, r[0, 0, 5:6])
+    assert np.all(f["kc"] == 1 << (w.key_bits - 1)) and f["rho"][0] == 0
+    if w.qjl_dim:
+        assert np.all(f["bits"] == 1)
+    print(name, "exempt mismatches", total)
+
+
+def test_compress_strided_layout_offset_slots_and_ragged_tail():
+    w = W.small(W.WORKLOADS["llama8b_decode_32k"], tokens=203, batch=2)
+    h = _handle(w)
+    codec = _codec(h)
+    K, V = W.make_kv(w, "cpu")
+    # [B, H, T, d] storage viewed as [B, T, H, d]
+    Kh = K.permute(0, 2, 1, 3).contiguous().cuda().permute(0, 2, 1, 3)
+    Vh = V.permute(0, 2, 1, 3).contiguous().cuda().permute(0, 2, 1, 3)
+    rec = _compress(w, h, Kh, Vh, capacity=300, first_slot=50)
+    ref = _compress(w, h, K.cuda(), V.cuda())
+    r = rec.cpu().numpy()
+    assert np.array_equal(r[:, :, 50:253], ref.cpu().numpy())
+    assert np.all(r[:, :, :50] == 0xAB) and np.all(r[:, :, 253:] == 0xAB)   # untouched slots
+    check_compress(codec, _np(K)[1, :, 3], _np(V)[1, :, 3], r[1, 3, 50:253])
+
+
+def test_compress_rejects_bad_arguments():
+    tq = _tq()
+    h = tq.Handle(128, 3, 128, 4, 1, 2)
+    K = torch.zeros((1, 8, 1, 128), dtype=torch.bfloat16, device="cuda")
+    rec = torch.zeros((1, 1, 8, h.record_bytes), dtype=torch.uint8, device="cuda")
+    with pytest.raises(tq.TqError) as e:
+        h.compress_kv(K, K, rec, first_slot=1)        # exceeds capacity
+    assert e.value.status == tq.TQ_ERR_INVALID_ARGUMENT
+    Kodd = torch.zeros((1, 8, 1, 130), dtype=torch.bfloat16, device="cuda")[..., 1:129]
+    with pytest.raises(tq.TqError):
+        h.compress_kv(Kodd, Kodd, rec)                # misaligned rows
+
+
+# ------------------------------------------------------------------ decode --------------
+def _decode_case(w, seq_lens, hot_lens=None, scale=0.0, sel=None, heads_to_check=None):
+    h = _handle(w)
+    codec = _codec(h)
+    K, V = W.make_kv(w, "cuda")
+    rec = _compress(w, h, K, V)
+    q = W.make_queries(w, "cuda")
+    B = w.batch
+    sl = torch.tensor(seq_lens, dtype=torch.int32, device="cuda")
+    hk = hv = hl = None
+    if hot_lens is not None:
+        hk, hv = W.make_hot(w, "cuda")
+        hl = torch.tensor(hot_lens, dtype=torch.int32, device="cuda")
+    k_sel = 0 if sel is None else sel.shape[-1]
+    ncold = k_sel if sel is not None else rec.shape[2]
+    lw = ncold + (0 if hk is None else hk.shape[2])
+    out = torch.full((B, w.q_heads, w.head_dim), float("nan"), device="cuda")
+    lse = torch.full((B, w.q_heads), float("nan"), device="cuda")
+    logits = torch.full((B, w.q_heads, lw), float("nan"), device="cuda")
+    h.decode_attention(q, rec, sl, hot_k=hk, hot_v=hv, hot_lens=hl, sel_idx=sel, scale=scale,
+                       out=out, lse=lse, logits=logits)
+    out2 = h.decode_attention(q, rec, sl, hot_k=hk, hot_v=hv, hot_lens=hl, sel_idx=sel, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2), "decode is not deterministic"
+    r = rec.cpu().numpy()
+    qn = _np(q)
+    ref_out, ref_lse, ref_lg = O.decode_attention(
+        codec, qn, r, seq_lens, None if hk is None else _np(hk), None if hv is None else _np(hv),
+        hot_lens, None if sel is None else sel.cpu().numpy(), scale, heads=heads_to_check)
+    o, L, lg = out.cpu().numpy(), lse.cpu().numpy(), logits.cpu().numpy()
+    for (b, hq), (lc, lh) in ref_lg.items():
+        _close(o[b, hq], ref_out[b, hq], f"out[{b},{hq}]")
+        if np.isinf(ref_lse[b, hq]):
+            assert np.isneginf(L[b, hq]) and np.all(o[b, hq] == 0)
+        else:
+            _close(L[b, hq], ref_lse[b, hq], f"lse[{b},{hq}]")
+        if sel is None:
+            _close(lg[b, hq, : len(lc)], lc, f"cold logits[{b},{hq}]")
+        else:
+            idx = sel.cpu().numpy()[b, hq // w.group]
+            pos = np.nonzero(idx >= 0)[0]
+            _close(lg[b, hq, pos], lc, f"gathered logits[{b},{hq}]")
+        if len(lh):
+            _close(lg[b, hq, ncold: ncold + len(lh)], lh, f"hot logits[{b},{hq}]")
+    return out
+
+
+def test_decode_single_head_1k_full_size():
+    w = W.WORKLOADS["single_head_1k"]
+    _decode_case(w, [1024])
+
+
+def test_decode_tinyllama_layer_full_size_with_exact_segment():
+    w = W.WORKLOADS["tinyllama_layer"]
+    _decode_case(w, [1024], hot_lens=[512])
+
+
+def test_decode_llama8b_shape_reduced_ragged():
+    w = W.small(W.WORKLOADS["llama8b_decode_32k"], tokens=3000, batch=3)
+    _decode_case(w, [3000, 1, 2049])
+
+
+def test_decode_group_sizes_and_empty_sequences():
+    base = W.small(W.WORKLOADS["llama8b_decode_32k"], tokens=700, batch=2)
+    for hq in (8, 16, 64):           # G = 1, 2, 8
+        w = W.Workload(**{**base.__dict__, "q_heads": hq, "name": "llama8b_decode_32k"})
+        _decode_case(w, [700, 0])
+    w2 = W.small(W.WORKLOADS["tinyllama_layer"], tokens=300, batch=2, hot_tokens=40)
+    _decode_case(w2, [0, 299], hot_lens=[17, 0], scale=0.3)
+
+
+def test_decode_gather_mode():
+    w = W.small(W.WORKLOADS["sparse_128k_top2048"], tokens=4000, batch=2)
+    rng = np.random.default_rng(1)
+    sel = np.full((2, w.kv_heads, 300), -1, np.int32)
+    for b in range(2):
+        for hh in range(w.kv_heads):
+            k = rng.integers(1, 300)
+            sel[b, hh, :k] = np.sort(rng.choice(4000, size=k, replace=False))
+    _decode_case(w, [4000, 4000], sel=torch.from_numpy(sel).cuda())
+
+
+def test_decode_rejects_small_workspace():
+    tq = _tq()
+    h = tq.Handle(128, 3, 128, 4, 1, 2)
+    q = torch.zeros((1, 4, 128), dtype=torch.bfloat16, device="cuda")
+    rec = torch.zeros((1, 1, 64, h.record_bytes), dtype=torch.uint8, device="cuda")
+    sl = torch.tensor([64], dtype=torch.int32, device="cuda")
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(tq.TqError) as e:
+        h.decode_attention(q, rec, sl, workspace=ws)
+    assert e.value.status == tq.TQ_ERR_WORKSPACE_TOO_SMALL
+
+
+# ------------------------------------------------------------------ sign index + top-k ---
+def _index_case(w, seq_lens, k, q_heads=None):
+    h = _handle(w)
+    codec = _codec(h)
+    K, _ = W.make_kv(w, "cuda")
+    B, T, H, d = K.shape
+    index = torch.full((B, H, T, d // 8), 0xEE, dtype=torch.uint8, device="cuda")
+    book = torch.full((B, H, d // 4, 16, 4), float("nan"), device="cuda")
+    mean = torch.empty((B, H, d), device="cuda")
+    h.build_sign_index(K, index, book, mean)
+    torch.cuda.synchronize()
+    Kn = _np(K)
+    ref_idx, ref_book, ref_mu = O.build_sign_index(codec, Kn, T)
+    mu = mean.cpu().numpy()
+    assert np.allclose(mu, ref_mu, rtol=1e-6, atol=1e-7)
+    gi, gb = index.cpu().numpy(), book.cpu().numpy()
+    if np.array_equal(mu, ref_mu):
+        assert np.array_equal(gi, ref_idx)
+        assert np.allclose(gb, ref_book, rtol=1e-5, atol=1e-6)
+    # selection: GPU vs oracle on the GPU-built index and codebook -> bit-exact
+    Hq = q_heads or w.q_heads
+    q = W.make_queries(W.Workload(**{**w.__dict__, "q_heads": Hq}), "cuda")
+    sl = torch.tensor(seq_lens, dtype=torch.int32, device="cuda")
+    out_idx = torch.full((B, H, k), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((B, H), -7, dtype=torch.int32, device="cuda")
+    scs = torch.full((B, H, k), -7, dtype=torch.int32, device="cuda")
+    h.select_topk(q, index, book, sl, k, out_idx=out_idx, out_count=cnt, out_scores=scs)
+    torch.cuda.synchronize()
+    ri, rc, rs = O.select_topk(codec, _np(q), gi, gb, seq_lens, k)
+    assert np.array_equal(cnt.cpu().numpy(), rc)
+    assert np.array_equal(out_idx.cpu().numpy(), ri)
+    assert np.array_equal(scs.cpu().numpy(), rs)
+    return h, K, q, index, book, out_idx
+
+
+def test_sign_index_and_topk_reduced():
+    w = W.small(W.WORKLOADS["sparse_128k_top2048"], tokens=9000, batch=2)
+    _index_case(w, [9000, 4097], 512)
+
+
+@pytest.mark.parametrize("k,lens", [(0, [100, 100]), (100, [100, 37]), (1, [100, 1]), (300, [300, 0])])
+def test_topk_edge_cases(k, lens):
+    w = W.small(W.WORKLOADS["sparse_128k_top2048"], tokens=300, batch=2)
+    _index_case(w, lens, k)
+
+
+def test_topk_with_ties_and_grouped_heads():
+    w = W.small(W.WORKLOADS["sparse_128k_top2048"], tokens=2048, batch=1)
+    _index_case(w, [2048], 333, q_heads=32)       # G = 4: one selection per KV head
+
+
+def test_select_then_gather_attention():
+    w = W.small(W.WORKLOADS["sparse_128k_top2048"], tokens=6000, batch=2, top_k=256)
+    h, K, q, index, book, sel = _index_case(w, [6000, 6000], 256)
+    codec = _codec(h)
+    _, V = W.make_kv(w, "cuda")
+    rec = _compress(w, h, K, V)
+    sl = torch.tensor([6000, 6000], dtype=torch.int32, device="cuda")
+    out = h.decode_attention(q, rec, sl, sel_idx=sel)
+    torch.cuda.synchronize()
+    ref, _, _ = O.decode_attention(codec, _np(q), rec.cpu().numpy(), [6000, 6000], sel_idx=sel.cpu().numpy())
+    _close(out.cpu().numpy(), ref, "gather attention")
+
+
+# ------------------------------------------------------------------ bulk scan -----------
+def test_score_scan_reduced():
+    w = W.small(W.WORKLOADS["bulk_64k_scan"], tokens=1000, scan_queries=70)
+    h = _handle(w)
+    codec = _codec(h)
+    K, V = W.make_kv(w, "cuda")
+    rec = _compress(w, h, K, V)
+    q = W.make_queries(w, "cuda")
+    sc = torch.full((1, w.kv_heads, 70, 1000), float("nan"), device="cuda")
+    h.score_scan(q, rec, 1000, scores=sc)
+    torch.cuda.synchronize()
+    ref = O.score_scan(codec, _np(q), rec.cpu().numpy(), 1000)
+    _close(sc.cpu().numpy(), ref, "scan scores")
+
+
+# ------------------------------------------------------------------ full sizes, sampled --
+def test_llama8b_decode_full_size_sampled():
+    w = W.WORKLOADS["llama8b_decode_32k"]
+    h = _handle(w)
+    codec = _codec(h)
+    K, V = W.make_kv(w, "cuda")
+    rec = _compress(w, h, K, V)
+    # compress: sampled tokens of sampled (b, h)
+    r = rec[[0, 15]][:, [0, 7]].cpu().numpy()
+    for bi, b in enumerate([0, 15]):
+        for hi, hh in enumerate([0, 7]):
+            toks = np.r_[0:64, 32700:32768]
+            check_compress(codec, _np(K[b, toks, hh]), _np(V[b, toks, hh]), r[bi, hi, toks])
+    q = W.make_queries(w, "cuda")
+    sl = torch.full((w.batch,), w.tokens, dtype=torch.int32, device="cuda")
+    lse = torch.empty((w.batch, w.q_heads), device="cuda")
+    out = h.decode_attention(q, rec, sl, lse=lse)
+    torch.cuda.synchronize()
+    for b, hq in [(0, 0), (7, 13), (15, 31)]:
+        ref, ref_lse, _ = O.decode_attention(codec, _np(q[b:b + 1]), rec[b:b + 1].cpu().numpy(), [w.tokens],
+                                             heads=[hq])
+        _close(out[b, hq].cpu().numpy(), ref[0, hq], f"out[{b},{hq}]")
+        _close(lse[b, hq].item(), ref_lse[0, hq], f"lse[{b},{hq}]")
+
+
+def test_sparse_128k_full_size_sampled():
+    w = W.WORKLOADS["sparse_128k_top2048"]
+    h = _handle(w)
+    codec = _codec(h)
+    K, V = W.make_kv(w, "cuda")
+    B, T, H, d = K.shape
+    index = torch.empty((B, H, T, d // 8), dtype=torch.uint8, device="cuda")
+    book = torch.empty((B, H, d // 4, 16, 4), device="cuda")
+    h.build_sign_index(K, index, book)
+    q = W.make_queries(w, "cuda")
+    sl = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    sel, cnt = h.select_topk(q, index, book, sl, w.top_k)
+    rec = _compress(w, h, K, V)
+    out = h.decode_attention(q, rec, sl, sel_idx=sel)
+    torch.cuda.synchronize()
+    gi, gb = index.cpu().numpy(), book.cpu().numpy()
+    qn = _np(q)
+    for b, hh in [(0, 0), (3, 5)]:
+        ri, rc, _ = O.select_topk(codec, qn[b:b + 1, hh:hh + 1], gi[b:b + 1, hh:hh + 1], gb[b:b + 1, hh:hh + 1], [T],
+                                  w.top_k)
+        assert np.array_equal(sel[b, hh].cpu().numpy(), ri[0, 0]) and cnt[b, hh].item() == w.top_k
+        ref, _, _ = O.decode_attention(codec, qn[b:b + 1, hh:hh + 1], rec[b:b + 1, hh:hh + 1].cpu().numpy(), [T],
+                                       sel_idx=ri)
+        _close(out[b, hh].cpu().numpy(), ref[0, 0], f"sparse out[{b},{hh}]")
+
+
+def test_bulk_scan_full_size_sampled():
+    w = W.WORKLOADS["bulk_64k_scan"]
+    h = _handle(w)
+    codec = _codec(h)
+    K, V = W.make_kv(w, "cuda")
+    rec = _compress(w, h, K, V)
+    q = W.make_queries(w, "cuda")
+    sc = h.score_scan(q, rec, w.tokens)
+    torch.cuda.synchronize()
+    for hh, qi in [(0, 0), (4, 200), (7, 255)]:
+        ref = O.score_scan(codec, _np(q[:, hh:hh + 1, qi:qi + 1]), rec[:, hh:hh + 1].cpu().numpy(), w.tokens)
+        _close(sc[0, hh, qi].cpu().numpy(), ref[0, 0, 0], f"scan[{hh},{qi}]")
+    r = rec[0, 2].cpu().numpy()
+    toks = np.r_[0:100, 65000:65536]
+    check_compress(codec, _np(K[0, toks, 2]), _np(V[0, toks, 2]), r[toks])
