@@ -14,6 +14,14 @@
 namespace {
 
 thread_local std::string g_last_error;
+thread_local tq::ProfileEvents g_events;
+
+// The events armed by tq_set_profile_events, handed to one call and then cleared.
+tq::ProfileEvents take_events() {
+  tq::ProfileEvents e = g_events;
+  g_events = tq::ProfileEvents();
+  return e;
+}
 
 tq_status fail(tq_status st, const char* fmt, ...) {
   char buf[512];
@@ -245,6 +253,14 @@ extern "C" {
 
 const char* tq_last_error(void) { return g_last_error.c_str(); }
 
+tq_status tq_set_profile_events(hipEvent_t start, hipEvent_t stop) {
+  if ((start == nullptr) != (stop == nullptr))
+    return fail(TQ_ERR_INVALID_ARGUMENT, "start and stop must both be set or both be NULL");
+  g_events.start = start;
+  g_events.stop = stop;
+  return ok();
+}
+
 tq_status tq_host_constants(const tq_config* cfg, float* pi, float* s, float* key_levels,
                             float* key_bounds, float* value_levels, float* value_bounds) {
   tq_status st = check_config(cfg);
@@ -358,7 +374,7 @@ tq_status tq_compress_kv(const tq_handle* h, const void* k, const void* v, tq_dt
   if (!records || !aligned(records, 16)) return fail(TQ_ERR_INVALID_ARGUMENT, "records NULL or not 16-byte aligned");
   return device_status(tq::launch_compress(h->c, h->dc, k, v, dt, batch, n_tokens, kv_heads,
                                            seq_stride, tok_stride, head_stride, records,
-                                           capacity, first_slot, stream),
+                                           capacity, first_slot, stream, take_events()),
                        "compress launch");
 }
 
@@ -422,7 +438,7 @@ tq_status tq_decode_attention(const tq_handle* h, const void* q, tq_dtype q_dt, 
   return device_status(tq::launch_decode(h->c, h->dc, plan, q, q_dt, batch, q_heads, kv_heads,
                                          records, capacity, seq_lens, hot_k, hot_v, hot_dt,
                                          hot_lens, hot_capacity, sel_idx, k_sel, scale, out, lse,
-                                         logits, workspace, stream),
+                                         logits, workspace, stream, take_events()),
                        "decode launch");
 }
 
@@ -483,7 +499,7 @@ tq_status tq_select_topk(const tq_handle* h, const void* q, tq_dtype q_dt, int32
     return fail(TQ_ERR_WORKSPACE_TOO_SMALL, "select needs %zu bytes of workspace", plan.ws_total);
   return device_status(tq::launch_select(h->c, plan, q, q_dt, batch, q_heads, kv_heads, index,
                                          codebook, capacity, seq_lens, k, out_idx, out_count,
-                                         out_scores, workspace, stream),
+                                         out_scores, workspace, stream, take_events()),
                        "select launch");
 }
 
@@ -513,7 +529,8 @@ tq_status tq_score_scan(const tq_handle* h, const void* q, tq_dtype q_dt, int32_
   if (!workspace || ws_bytes < plan.ws_total || !aligned(workspace, 256))
     return fail(TQ_ERR_WORKSPACE_TOO_SMALL, "scan needs %zu bytes of workspace", plan.ws_total);
   return device_status(tq::launch_scan(h->c, h->dc, plan, q, q_dt, batch, kv_heads, n_queries,
-                                       records, capacity, n_tokens, scores, workspace, stream),
+                                       records, capacity, n_tokens, scores, workspace, stream,
+                                       take_events()),
                        "scan launch");
 }
 

@@ -12,6 +12,13 @@
 namespace tq {
 
 constexpr int kMaxLevels = 16;   // 2^4: key/value codes have at most 4 bits
+
+// Optional events recorded around the main kernel of one call (measurement only).
+struct ProfileEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+  void before(hipStream_t s) const { if (start) (void)hipEventRecord(start, s); }
+  void after(hipStream_t s) const { if (stop) (void)hipEventRecord(stop, s); }
+};
 constexpr int kWave = 64;
 
 // Per-handle constants passed by value to every kernel.
@@ -42,7 +49,7 @@ hipError_t launch_compress(const Consts& c, const DevConsts& dc, const void* k, 
                            tq_dtype dt, int batch, int64_t n_tokens, int heads,
                            int64_t seq_stride, int64_t tok_stride, int64_t head_stride,
                            void* records, int64_t capacity, int64_t first_slot,
-                           hipStream_t stream);
+                           hipStream_t stream, const ProfileEvents& ev);
 
 hipError_t launch_debug_quantize(const Consts& c, const float* z_k, const float* p,
                                  const float* r_k, const float* rho, const float* z_v,
@@ -69,7 +76,8 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
                          const void* hot_k, const void* hot_v, tq_dtype hot_dt,
                          const int32_t* hot_lens, int64_t hot_capacity,
                          const int32_t* sel_idx, int k_sel, float scale, float* out, float* lse,
-                         float* logits, void* workspace, hipStream_t stream);
+                         float* logits, void* workspace, hipStream_t stream,
+                         const ProfileEvents& ev);
 
 struct IndexPlan {
   int chunk, n_chunks;
@@ -90,7 +98,7 @@ hipError_t launch_select(const Consts& c, const SelectPlan& plan, const void* q,
                          int batch, int q_heads, int kv_heads, const void* index,
                          const float* codebook, int64_t capacity, const int32_t* seq_lens,
                          int k, int32_t* out_idx, int32_t* out_count, int32_t* out_scores,
-                         void* workspace, hipStream_t stream);
+                         void* workspace, hipStream_t stream, const ProfileEvents& ev);
 
 struct ScanPlan {
   size_t ws_q, ws_total;
@@ -99,6 +107,6 @@ ScanPlan plan_scan(const Consts& c, int batch, int heads, int n_queries);
 hipError_t launch_scan(const Consts& c, const DevConsts& dc, const ScanPlan& plan, const void* q,
                        tq_dtype q_dt, int batch, int heads, int n_queries, const void* records,
                        int64_t capacity, int64_t n_tokens, float* scores, void* workspace,
-                       hipStream_t stream);
+                       hipStream_t stream, const ProfileEvents& ev);
 
 }  // namespace tq

@@ -335,7 +335,8 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs A) {
 hipError_t launch_compress(const Consts& c, const DevConsts& dc, const void* k, const void* v,
                            tq_dtype dt, int batch, int64_t n_tokens, int heads, int64_t seq_stride,
                            int64_t tok_stride, int64_t head_stride, void* records,
-                           int64_t capacity, int64_t first_slot, hipStream_t stream) {
+                           int64_t capacity, int64_t first_slot, hipStream_t stream,
+                           const ProfileEvents& ev) {
   CompressArgs A;
   A.c = c;
   A.pi_m = dc.pi_mfma;
@@ -360,6 +361,7 @@ hipError_t launch_compress(const Consts& c, const DevConsts& dc, const void* k, 
   const size_t lds = A.s_in_lds ? with_s : base;
   int64_t blocks = (A.n_tiles + nwaves - 1) / nwaves;
   blocks = std::min<int64_t>(blocks, (int64_t)num_cus());
+  ev.before(stream);
   if (c.d == 128) {
     allow_lds(compress_kernel<128>, lds);
     hipLaunchKernelGGL(compress_kernel<128>, dim3((unsigned)blocks), dim3(threads), lds, stream, A);
@@ -367,6 +369,7 @@ hipError_t launch_compress(const Consts& c, const DevConsts& dc, const void* k, 
     allow_lds(compress_kernel<64>, lds);
     hipLaunchKernelGGL(compress_kernel<64>, dim3((unsigned)blocks), dim3(threads), lds, stream, A);
   }
+  ev.after(stream);
   return hipGetLastError();
 }
 
@@ -865,7 +868,7 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
                          const void* hot_v, tq_dtype hot_dt, const int32_t* hot_lens,
                          int64_t hot_capacity, const int32_t* sel_idx, int k_sel, float scale,
                          float* out, float* lse, float* logits, void* workspace,
-                         hipStream_t stream) {
+                         hipStream_t stream, const ProfileEvents& ev) {
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   float* qx = reinterpret_cast<float*>(ws + plan.ws_qx);
   float* qs = reinterpret_cast<float*>(ws + plan.ws_qs);
@@ -907,10 +910,12 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
     a.val_levels[i] = c.val_levels[i];
   }
   dim3 grid(plan.n_chunks, kv_heads, batch);
+  ev.before(stream);
   if (plan.hpl == 4)
     launch_scan_hpl<4>(a, c.kb, c.vb, grid, plan.lds_bytes, stream);
   else
     launch_scan_hpl<1>(a, c.kb, c.vb, grid, plan.lds_bytes, stream);
+  ev.after(stream);
   MergeArgs mg;
   mg.pi = dc.pi;
   mg.part = part;
@@ -1325,7 +1330,8 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const int32_t*
 hipError_t launch_select(const Consts& c, const SelectPlan& plan, const void* q, tq_dtype q_dt, int batch,
                          int q_heads, int kv_heads, const void* index, const float* codebook,
                          int64_t capacity, const int32_t* seq_lens, int k, int32_t* out_idx,
-                         int32_t* out_count, int32_t* out_scores, void* workspace, hipStream_t stream) {
+                         int32_t* out_count, int32_t* out_scores, void* workspace, hipStream_t stream,
+                         const ProfileEvents& ev) {
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   int32_t* lut = reinterpret_cast<int32_t*>(ws + plan.ws_lut);
   int32_t* scores = reinterpret_cast<int32_t*>(ws + plan.ws_scores);
@@ -1334,9 +1340,11 @@ hipError_t launch_select(const Consts& c, const SelectPlan& plan, const void* q,
     const size_t lds = (size_t)G * ng * 16 * 8 + (size_t)ng * 16 * 4;
     hipLaunchKernelGGL(select_lut_kernel, dim3(kv_heads, batch), dim3(256), lds, stream, q, q_dt, codebook,
                        c.d, G, q_heads, kv_heads, lut);
+    ev.before(stream);
     hipLaunchKernelGGL(select_score_kernel, dim3((unsigned)((capacity + 255) / 256), kv_heads, batch), dim3(256),
                        0, stream, static_cast<const uint8_t*>(index), lut, seq_lens, c.d, kv_heads, capacity,
                        scores);
+    ev.after(stream);
   }
   hipLaunchKernelGGL(select_topk_kernel, dim3(kv_heads, batch), dim3(kSelThreads), 0, stream, scores, seq_lens,
                      kv_heads, capacity, k, out_idx, out_count, out_scores);
@@ -1463,7 +1471,8 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs A) {
 
 hipError_t launch_scan(const Consts& c, const DevConsts& dc, const ScanPlan& plan, const void* q, tq_dtype q_dt,
                        int batch, int heads, int n_queries, const void* records, int64_t capacity,
-                       int64_t n_tokens, float* scores, void* workspace, hipStream_t stream) {
+                       int64_t n_tokens, float* scores, void* workspace, hipStream_t stream,
+                       const ProfileEvents& ev) {
   float* qprep = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + plan.ws_q);
   const int rows = batch * heads * n_queries;
   hipLaunchKernelGGL(scan_prep_kernel, dim3(rows), dim3(128), 0, stream, dc.pi, dc.s, c.d, c.m, q, q_dt, qprep);
@@ -1488,7 +1497,9 @@ hipError_t launch_scan(const Consts& c, const DevConsts& dc, const ScanPlan& pla
   dim3 grid((unsigned)((n_tokens + kScanTile - 1) / kScanTile), (unsigned)((n_queries + kScanTile - 1) / kScanTile),
             (unsigned)(batch * heads));
   allow_lds(scan_kernel, lds);
+  ev.before(stream);
   hipLaunchKernelGGL(scan_kernel, grid, dim3(256), lds, stream, a);
+  ev.after(stream);
   return hipGetLastError();
 }
 

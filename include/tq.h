@@ -202,6 +202,13 @@ tq_status tq_score_scan(const tq_handle* h, const void* q, tq_dtype q_dt, int32_
                         int64_t capacity, int64_t n_tokens, float* scores, void* workspace,
                         size_t ws_bytes, hipStream_t stream);
 
+/* Measurement support: on this thread, the next tq_decode_attention, tq_compress_kv,
+ * tq_select_topk or tq_score_scan call records `start` on its stream just before its main
+ * kernel (decode: the split-K scan; compress: the compress kernel; select: the sign-index
+ * score kernel; scan: the score kernel) and `stop` just after it, then forgets both.
+ * Events are caller-created (hipEventCreate) and caller-owned; NULL, NULL clears. */
+tq_status tq_set_profile_events(hipEvent_t start, hipEvent_t stop);
+
 #ifdef __cplusplus
 }
 #endif
