@@ -104,7 +104,18 @@ def main():
     ap.add_argument("--workload", default="llama8b_decode_32k",
                     choices=["llama8b_decode_32k", "tinyllama_layer", "single_head_1k"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 5 device-to-device copies of 1 GiB (HBM counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": src.numel(), "copies": 5}))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; --gpus above 1 is not "
                                    "supported (the decode shards with no exchange, see the design notes)"}))

@@ -63,6 +63,7 @@ struct DecodePlan {
   int hpl;          // heads per lane (1 or 4)
   bool key_pairs;   // key LUT indexed by pairs of codes (else single codes)
   bool sign_bytes;  // QJL LUT indexed by bytes (else nibbles)
+  bool mfma;        // matrix-core scan (head_dim 128, 4 query heads per KV head)
   size_t lds_bytes;
   size_t ws_qx, ws_qs, ws_part, ws_total;   // workspace offsets / size
 };

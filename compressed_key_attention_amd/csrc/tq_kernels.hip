@@ -694,6 +694,239 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_scan_kernel(DecodeArgs 
   }
 }
 
+// -----------------------------------------------------------------------------------------
+// Matrix-core decode scan for head_dim 128 and 4 query heads per KV head (2- or 3-bit keys,
+// 4-bit values).  Same arithmetic as decode_scan_kernel, laid out for gfx950:
+//  * key scores on v_mfma_f32_16x16x32_bf16: rows = 16 tokens, columns = (head, code part /
+//    QJL part, query high / low bf16 half).  The K dimension runs over (coordinate, codebook
+//    level high / low bf16 half) and over QJL sign bits (+-1, exact in bf16).  Splitting both
+//    operands into two bf16 halves keeps ~16 significant bits per factor with float32
+//    accumulation.  Codebook halves are looked up in registers with v_perm_b32 (no LDS).
+//  * the 16 x 16 score tile goes through 1 KB of LDS to a lane-per-(token, head) layout where
+//    each lane runs one online softmax (raised lazily) and forms w = p r_v / sqrt(d);
+//  * value aggregation on v_mfma_f32_4x4x1f32: block = token slot, row = coordinate group,
+//    column = head, one instruction per coordinate offset; accumulators hold, per lane,
+//    o[head][32 r + k] partials; value levels come from an LDS table of level pairs per byte.
+// -----------------------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t bf16_rn_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ float bf16_bits_f(uint32_t h) { return __uint_as_float(h << 16); }
+// high (sp = 0) or low (sp = 1) bf16 half of x: x ~= hi + lo with ~16 significant bits
+__device__ __forceinline__ uint32_t bf16_half(float x, int sp) {
+  const uint32_t hi = bf16_rn_bits(x);
+  return sp == 0 ? hi : bf16_rn_bits(x - bf16_bits_f(hi));
+}
+
+// Spread four FW-bit fields (low 4*FW bits of x) into the four bytes of the result.
+template <int FW>
+__device__ __forceinline__ uint32_t spread4(uint32_t x) {
+  constexpr uint32_t m1 = (1u << (2 * FW)) - 1u;
+  constexpr uint32_t m2 = ((1u << FW) - 1u) * 0x00010001u;
+  const uint32_t y = (x & m1) | ((x & (m1 << (2 * FW))) << (16 - 2 * FW));
+  return (y & m2) | ((y & (m2 << FW)) << (8 - FW));
+}
+
+constexpr int kMfmaThreads = 256;
+
+template <int BK, bool QJL>
+__global__ __launch_bounds__(kMfmaThreads, 2) void decode_mfma_kernel(DecodeArgs A) {
+  constexpr int D = 128, G = 4, NW = kMfmaThreads / 64;
+  __shared__ float2 vtab[256];              // byte of value codes -> (level[lo nibble], level[hi nibble])
+  __shared__ __attribute__((aligned(16))) float stile[NW][16 * 16];   // per-wave score tile
+  __shared__ float red[NW][G][D + 2];       // cross-wave merge
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b = blockIdx.z, hkv = blockIdx.y, chunk = blockIdx.x;
+  const int64_t qrow0 = (int64_t)b * A.q_heads + (int64_t)hkv * G;
+
+  for (int e = threadIdx.x; e < 256; e += blockDim.x) vtab[e] = make_float2(A.val_levels[e & 15], A.val_levels[e >> 4]);
+
+  // codebook halves as byte tables for v_perm: byte c of each pair = code c
+  uint32_t thl[2] = {0, 0}, thh[2] = {0, 0}, tll[2] = {0, 0}, tlh[2] = {0, 0};
+#pragma unroll
+  for (int c = 0; c < (1 << BK); ++c) {
+    const float g = A.key_levels[c];
+    const uint32_t h = bf16_rn_bits(g), l = bf16_rn_bits(g - bf16_bits_f(h));
+    thl[c >> 2] |= (h & 0xFFu) << (8 * (c & 3));
+    thh[c >> 2] |= (h >> 8) << (8 * (c & 3));
+    tll[c >> 2] |= (l & 0xFFu) << (8 * (c & 3));
+    tlh[c >> 2] |= (l >> 8) << (8 * (c & 3));
+  }
+
+  // query operand (B): lane column n = (head, part, half), K slice kg
+  const int n = lane & 15, kg = lane >> 4;
+  const int hB = n >> 2, part = (n >> 1) & 1, sp = n & 1;
+  bf16x8 Bc[8], Bq[4];
+  {
+    const float* qx = A.qx + (qrow0 + hB) * D;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t v = part == 0 ? bf16_half(qx[32 * kg + 4 * j + (e & 3)], sp) : 0u;
+        Bc[j][e] = __builtin_bit_cast(__bf16, (uint16_t)v);
+      }
+    const float* qs = A.qs + (qrow0 + hB) * A.m;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t v = (QJL && part == 1) ? bf16_half(qs[32 * kg + 8 * j + e], sp) : 0u;
+        Bq[j][e] = __builtin_bit_cast(__bf16, (uint16_t)v);
+      }
+  }
+  __syncthreads();
+
+  const bool gather = A.sel_idx != nullptr;
+  const int n_tok = gather ? A.k_sel : (int)min((int64_t)A.seq_lens[b], A.capacity);
+  const int c0 = chunk * A.chunk, c1 = min(n_tok, c0 + A.chunk);
+  const uint8_t* recs = A.records + ((int64_t)b * A.kv_heads + hkv) * A.capacity * A.rec_bytes;
+  const int32_t* sel = gather ? A.sel_idx + ((int64_t)b * A.kv_heads + hkv) * A.k_sel : nullptr;
+  const int vslot = lane >> 2, vj = lane & 3;        // value layout: token slot, head / coordinate group
+  float* tile = stile[wave];
+
+  f32x4 acc[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) acc[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float mrun = kNegInf, lsum = 0.0f;
+
+  for (int base = c0 + wave * 16; base < c1; base += NW * 16) {
+    // ---- key-layout loads: token base + n, coordinates [32 kg, 32 kg + 32) ----
+    int pk = min(base + n, c1 - 1);
+    int64_t tk = gather ? sel[pk] : pk;
+    if (tk < 0 || tk >= A.capacity) tk = 0;
+    const uint8_t* rk = recs + tk * A.rec_bytes;
+    uint32_t kw[BK];
+#pragma unroll
+    for (int i = 0; i < BK; ++i) kw[i] = reinterpret_cast<const uint32_t*>(rk + kg * 4 * BK)[i];
+    const uint32_t sw = QJL ? reinterpret_cast<const uint32_t*>(rk + A.kbytes)[kg] : 0u;
+    // ---- value-layout loads: token base + vslot, coordinates [32 vj, 32 vj + 32) ----
+    const int pv = base + vslot;
+    bool valid = pv < c1;
+    int64_t tv = gather ? sel[min(pv, c1 - 1)] : min(pv, c1 - 1);
+    valid = valid && tv >= 0 && tv < A.capacity;
+    if (!valid) tv = 0;
+    const uint8_t* rv = recs + tv * A.rec_bytes;
+    const u32x4 vw = *reinterpret_cast<const u32x4*>(rv + A.kbytes + A.sbytes + 16 * vj);
+    const float* nrm = reinterpret_cast<const float*>(rv + A.norm_off);
+    const float nk = nrm[0], nrho = nrm[1], nv = nrm[2];
+
+    // ---- key scores on the matrix cores ----
+    f32x4 C0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f}, C1 = C0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t x = field<BK>(kw, 4 * BK * j, 4 * BK);
+      const uint32_t S = spread4<BK>(x);
+      const uint32_t bl = __builtin_amdgcn_perm(thl[1], thl[0], S);
+      const uint32_t bh = __builtin_amdgcn_perm(thh[1], thh[0], S);
+      const uint32_t ll = __builtin_amdgcn_perm(tll[1], tll[0], S);
+      const uint32_t lh = __builtin_amdgcn_perm(tlh[1], tlh[0], S);
+      const u32x4 a = u32x4{__builtin_amdgcn_perm(bh, bl, 0x05010400u), __builtin_amdgcn_perm(bh, bl, 0x07030602u),
+                            __builtin_amdgcn_perm(lh, ll, 0x05010400u), __builtin_amdgcn_perm(lh, ll, 0x07030602u)};
+      const bf16x8 av = __builtin_bit_cast(bf16x8, a);
+      if (j & 1)
+        C1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, Bc[j], C1, 0, 0, 0);
+      else
+        C0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, Bc[j], C0, 0, 0, 0);
+    }
+    if (QJL) {
+      const uint32_t nsw = ~sw;   // bit set -> negative sign
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x4 a;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint32_t t2 = (nsw >> (8 * j + 2 * v)) & 3u;
+          a[v] = ((t2 * 0x40008000u) & 0x80008000u) | 0x3F803F80u;
+        }
+        const bf16x8 av = __builtin_bit_cast(bf16x8, a);
+        if (j & 1)
+          C1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, Bq[j], C1, 0, 0, 0);
+        else
+          C0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, Bq[j], C0, 0, 0, 0);
+      }
+    }
+    // ---- score tile -> lane per (token slot, head) ----
+#pragma unroll
+    for (int r = 0; r < 4; ++r) tile[(4 * kg + r) * 16 + n] = C0[r] + C1[r];
+    wave_lds_sync();
+    const f32x4 s4 = *reinterpret_cast<const f32x4*>(tile + vslot * 16 + 4 * vj);
+    wave_lds_sync();
+    const float shat = fmaf(A.qjl_coef * nrho, s4[2] + s4[3], nk * A.inv_sqrt_d * (s4[0] + s4[1]));
+    const float logit = A.scale * shat;
+    if (A.logits && valid) A.logits[(qrow0 + vj) * A.logit_stride + pv] = logit;
+    // ---- lazy online softmax (per lane: one token slot, one head) ----
+    if (valid && logit > mrun + kLazy) {
+      const float f = mrun == kNegInf ? 0.0f : __expf(mrun - logit);
+      lsum *= f;
+#pragma unroll
+      for (int k = 0; k < 32; ++k) acc[k] *= f;
+      mrun = logit;
+    }
+    const float p = valid ? __expf(logit - mrun) : 0.0f;
+    lsum += p;
+    const float wv = p * nv * A.inv_sqrt_d;
+    // ---- values on the matrix cores ----
+#pragma unroll
+    for (int mb = 0; mb < 16; ++mb) {
+      const uint32_t byte = (vw[mb >> 2] >> (8 * (mb & 3))) & 0xFFu;
+      const float2 g = vtab[byte];
+      acc[2 * mb] = __builtin_amdgcn_mfma_f32_4x4x1f32(g.x, wv, acc[2 * mb], 0, 0, 0);
+      acc[2 * mb + 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(g.y, wv, acc[2 * mb + 1], 0, 0, 0);
+    }
+  }
+
+  // ---- merge the 16 token slots of the wave (lane bits 2..5), then the waves ----
+#pragma unroll
+  for (int msk = 4; msk < 64; msk <<= 1) {
+    const float mo = __shfl_xor(mrun, msk);
+    const float lo = __shfl_xor(lsum, msk);
+    const float mx = fmaxf(mrun, mo);
+    const float fs = mrun == kNegInf ? 0.0f : __expf(mrun - mx);
+    const float fo = mo == kNegInf ? 0.0f : __expf(mo - mx);
+    lsum = lsum * fs + lo * fo;
+#pragma unroll
+    for (int k = 0; k < 32; ++k)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float ao = __shfl_xor(acc[k][r], msk);
+        acc[k][r] = acc[k][r] * fs + ao * fo;
+      }
+    mrun = mx;
+  }
+  if (vslot == 0) {
+    float* rr = red[wave][vj];
+    rr[0] = mrun;
+    rr[1] = lsum;
+#pragma unroll
+    for (int k = 0; k < 32; ++k)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rr[2 + 32 * r + k] = acc[k][r];
+  }
+  __syncthreads();
+  const int stride = D + 2;
+  for (int e = threadIdx.x; e < G * stride; e += blockDim.x) {
+    const int hh = e / stride, col = e % stride;
+    float mx = kNegInf;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) mx = fmaxf(mx, red[w2][hh][0]);
+    float v = mx;
+    if (col > 0) {
+      v = 0.0f;
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2)
+        if (red[w2][hh][0] != kNegInf) v += red[w2][hh][col] * __expf(red[w2][hh][0] - mx);
+    }
+    A.part[((qrow0 + hh) * A.n_chunks + chunk) * stride + col] = v;
+  }
+}
+
 // Merge: log-sum-exp of the chunk partials, the exact (hot) segment in the same softmax
 // (Monarch v3 page, "Wie es funktioniert"), and o = Pi^T o_x + o_hot, divided by the sum.
 struct MergeArgs {
@@ -813,9 +1046,14 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs A
   if (threadIdx.x == 0 && A.lse) A.lse[row] = L > 0.0f ? s_stat[1] + logf(L) : kNegInf;
 }
 
+static bool mfma_path(const Consts& c, int G) {
+  return c.d == 128 && G == 4 && c.vb == 4 && (c.kb == 2 || c.kb == 3) && (c.m == 0 || c.m == 128);
+}
+
 bool plan_decode(const Consts& c, int batch, int q_heads, int kv_heads, int64_t n_max,
                  DecodePlan* plan) {
   const int G = q_heads / kv_heads;
+  plan->mfma = mfma_path(c, G);
   const int hpl = (G % 4 == 0) ? 4 : 1;
   const int lpt = (c.d / 32) * (G / hpl);
   if (lpt > 64 || (lpt & (lpt - 1)) != 0) return false;
@@ -832,7 +1070,7 @@ bool plan_decode(const Consts& c, int batch, int q_heads, int kv_heads, int64_t 
   const size_t floats = std::max(lut, red);
   if (floats > 160 * 1024 / 4) return false;
   plan->lds_bytes = floats * 4;
-  // split-K: aim at ~2 blocks per CU (one resident at a time when the LUTs are large)
+  // split-K: aim at ~2 blocks per CU
   const int64_t units = (int64_t)std::max(batch, 1) * kv_heads;
   const int64_t target_blocks = 2 * (int64_t)num_cus();
   int64_t chunk = (n_max * units + target_blocks - 1) / std::max<int64_t>(target_blocks, 1);
@@ -911,10 +1149,20 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
   }
   dim3 grid(plan.n_chunks, kv_heads, batch);
   ev.before(stream);
-  if (plan.hpl == 4)
+  if (plan.mfma) {
+    if (c.kb == 3 && c.m)
+      hipLaunchKernelGGL((decode_mfma_kernel<3, true>), grid, dim3(kMfmaThreads), 0, stream, a);
+    else if (c.kb == 3)
+      hipLaunchKernelGGL((decode_mfma_kernel<3, false>), grid, dim3(kMfmaThreads), 0, stream, a);
+    else if (c.m)
+      hipLaunchKernelGGL((decode_mfma_kernel<2, true>), grid, dim3(kMfmaThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_mfma_kernel<2, false>), grid, dim3(kMfmaThreads), 0, stream, a);
+  } else if (plan.hpl == 4) {
     launch_scan_hpl<4>(a, c.kb, c.vb, grid, plan.lds_bytes, stream);
-  else
+  } else {
     launch_scan_hpl<1>(a, c.kb, c.vb, grid, plan.lds_bytes, stream);
+  }
   ev.after(stream);
   MergeArgs mg;
   mg.pi = dc.pi;

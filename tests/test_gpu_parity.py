@@ -270,6 +270,22 @@ def test_decode_gather_mode():
     _decode_case(w, [4000, 4000], sel=torch.from_numpy(sel).cuda())
 
 
+@pytest.mark.parametrize("kb,m", [(3, 128), (2, 128), (3, 0), (2, 0)])
+def test_decode_matrix_core_path_variants(kb, m):
+    """head_dim 128 with 4 query heads per KV head and 4-bit values runs the matrix-core scan;
+    cover each of its key widths with and without the QJL sketch, ragged lengths, gather."""
+    base = W.small(W.WORKLOADS["llama8b_decode_32k"], tokens=1500, batch=2)
+    w = W.Workload(**{**base.__dict__, "key_bits": kb, "qjl_dim": m})
+    _decode_case(w, [1500, 777])
+    rng = np.random.default_rng(kb + m)
+    sel = np.full((2, w.kv_heads, 200), -1, np.int32)
+    for b in range(2):
+        for hh in range(w.kv_heads):
+            k = rng.integers(1, 200)
+            sel[b, hh, :k] = np.sort(rng.choice(1500, size=k, replace=False))
+    _decode_case(w, [1500, 1500], sel=torch.from_numpy(sel).cuda())
+
+
 def test_decode_rejects_small_workspace():
     tq = _tq()
     h = tq.Handle(128, 3, 128, 4, 1, 2)
