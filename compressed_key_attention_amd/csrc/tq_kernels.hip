@@ -696,21 +696,23 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_scan_kernel(DecodeArgs 
 
 // -----------------------------------------------------------------------------------------
 // Matrix-core decode scan for head_dim 128 and 4 query heads per KV head (2- or 3-bit keys,
-// 4-bit values).  Same arithmetic as decode_scan_kernel, laid out for gfx950:
-//  * key scores on v_mfma_f32_16x16x32_bf16: rows = 16 tokens, columns = (head, code part /
-//    QJL part, query high / low bf16 half).  The K dimension runs over (coordinate, codebook
-//    level high / low bf16 half) and over QJL sign bits (+-1, exact in bf16).  Splitting both
-//    operands into two bf16 halves keeps ~16 significant bits per factor with float32
-//    accumulation.  Codebook halves are looked up in registers with v_perm_b32 (no LDS).
-//  * the 16 x 16 score tile goes through 1 KB of LDS to a lane-per-(token, head) layout where
-//    each lane runs one online softmax (raised lazily) and forms w = p r_v / sqrt(d);
-//  * value aggregation on v_mfma_f32_4x4x1f32: block = token slot, row = coordinate group,
-//    column = head, one instruction per coordinate offset; accumulators hold, per lane,
-//    o[head][32 r + k] partials; value levels come from an LDS table of level pairs per byte.
+// 4-bit values).  Same arithmetic as decode_scan_kernel, laid out for gfx950.  Each wave
+// takes 16 tokens per step:
+//  * key scores on v_mfma_f32_16x16x32_bf16: rows = tokens, columns = (head, code part / QJL
+//    part, query high / low bf16 half); K runs over (coordinate, codebook level high / low
+//    bf16 half) and over QJL sign bits (+-1, exact in bf16).  Two bf16 halves per factor keep
+//    ~16 significant bits with float32 accumulation.  Key levels are looked up in registers
+//    (v_perm_b32); sign patterns come from a 256-entry LDS table of +-1 bf16 octets.
+//  * the score tile goes through LDS to a lane-per-(token, head) layout; the running maximum of
+//    each head is shared by the wave (raised lazily), p and w = p r_v / sqrt(d) per lane;
+//  * value aggregation on the same bf16 MFMA: rows = coordinates, K = (token, level half),
+//    columns = (head, w half); the 16 tokens' value codes are transposed through 1 KB of LDS
+//    and their level halves read as pairs from a 256-entry LDS table.
 // -----------------------------------------------------------------------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t bf16_rn_bits(float x) {
   uint32_t u = __float_as_uint(x);
@@ -722,6 +724,10 @@ __device__ __forceinline__ float bf16_bits_f(uint32_t h) { return __uint_as_floa
 __device__ __forceinline__ uint32_t bf16_half(float x, int sp) {
   const uint32_t hi = bf16_rn_bits(x);
   return sp == 0 ? hi : bf16_rn_bits(x - bf16_bits_f(hi));
+}
+__device__ __forceinline__ uint32_t bf16_pair(float x) {      // hi | lo << 16
+  const uint32_t hi = bf16_rn_bits(x);
+  return hi | (bf16_rn_bits(x - bf16_bits_f(hi)) << 16);
 }
 
 // Spread four FW-bit fields (low 4*FW bits of x) into the four bytes of the result.
@@ -735,19 +741,29 @@ __device__ __forceinline__ uint32_t spread4(uint32_t x) {
 
 constexpr int kMfmaThreads = 256;
 
-template <int BK, bool QJL>
-__global__ __launch_bounds__(kMfmaThreads, 2) void decode_mfma_kernel(DecodeArgs A) {
+template <int BK, bool QJL, bool GATHER, bool LOGITS>
+__global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs A) {
   constexpr int D = 128, G = 4, NW = kMfmaThreads / 64;
-  __shared__ float2 vtab[256];              // byte of value codes -> (level[lo nibble], level[hi nibble])
-  __shared__ __attribute__((aligned(16))) float stile[NW][16 * 16];   // per-wave score tile
+  __shared__ u32x2 vtab[256];               // byte of value codes -> (level pair of lo nibble, of hi nibble)
+  __shared__ u32x4 stab[256];               // byte of QJL bits -> 8 bf16 (+1 for a set bit, -1 otherwise)
+  __shared__ __attribute__((aligned(16))) float stile[NW][16 * 16];    // score tile
+  __shared__ __attribute__((aligned(16))) uint32_t vstage[NW][16 * 16]; // [coord octet][token] value codes
+  __shared__ __attribute__((aligned(16))) float wstage[NW][4 * 16];    // [head][token] weights
   __shared__ float red[NW][G][D + 2];       // cross-wave merge
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = blockIdx.z, hkv = blockIdx.y, chunk = blockIdx.x;
   const int64_t qrow0 = (int64_t)b * A.q_heads + (int64_t)hkv * G;
 
-  for (int e = threadIdx.x; e < 256; e += blockDim.x) vtab[e] = make_float2(A.val_levels[e & 15], A.val_levels[e >> 4]);
+  for (int e = threadIdx.x; e < 256; e += blockDim.x) {
+    vtab[e] = u32x2{bf16_pair(A.val_levels[e & 15]), bf16_pair(A.val_levels[e >> 4])};
+    u32x4 sp;
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      sp[v] = (((e >> (2 * v)) & 1) ? 0x3F80u : 0xBF80u) | ((((e >> (2 * v + 1)) & 1) ? 0x3F80u : 0xBF80u) << 16);
+    stab[e] = sp;
+  }
 
-  // codebook halves as byte tables for v_perm: byte c of each pair = code c
+  // key codebook halves as byte tables for v_perm: byte c of each pair = code c
   uint32_t thl[2] = {0, 0}, thh[2] = {0, 0}, tll[2] = {0, 0}, tlh[2] = {0, 0};
 #pragma unroll
   for (int c = 0; c < (1 << BK); ++c) {
@@ -759,155 +775,191 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void decode_mfma_kernel(DecodeArgs
     tlh[c >> 2] |= (l >> 8) << (8 * (c & 3));
   }
 
-  // query operand (B): lane column n = (head, part, half), K slice kg
+  // query operand (B) of the key product: lane column n = (head, part, half), K slice kg.
+  // Code MFMA j takes slots e <-> (coordinate 32 kg + 4 j + e % 4, level half e / 4).
   const int n = lane & 15, kg = lane >> 4;
-  const int hB = n >> 2, part = (n >> 1) & 1, sp = n & 1;
   bf16x8 Bc[8], Bq[4];
   {
-    const float* qx = A.qx + (qrow0 + hB) * D;
+    const int hB = n >> 2, part = (n >> 1) & 1, sp = n & 1;
+    const f32x4* qx4 = reinterpret_cast<const f32x4*>(A.qx + (qrow0 + hB) * D + 32 * kg);
+    const f32x4* qs4 = reinterpret_cast<const f32x4*>(A.qs + (qrow0 + hB) * (QJL ? A.m : 0) + (QJL ? 32 * kg : 0));
+    f32x4 xv[8], sv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      xv[i] = qx4[i];
+      sv[i] = QJL ? qs4[i] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    const bool use_x = part == 0, use_s = QJL && part == 1;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t v = part == 0 ? bf16_half(qx[32 * kg + 4 * j + (e & 3)], sp) : 0u;
-        Bc[j][e] = __builtin_bit_cast(__bf16, (uint16_t)v);
+        const uint32_t vx = bf16_half(xv[j][e & 3], sp);
+        Bc[j][e] = __builtin_bit_cast(__bf16, (uint16_t)(use_x ? vx : 0u));
       }
-    const float* qs = A.qs + (qrow0 + hB) * A.m;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t v = (QJL && part == 1) ? bf16_half(qs[32 * kg + 8 * j + e], sp) : 0u;
-        Bq[j][e] = __builtin_bit_cast(__bf16, (uint16_t)v);
+        const uint32_t vs = bf16_half(sv[(8 * j + e) >> 2][e & 3], sp);
+        Bq[j][e] = __builtin_bit_cast(__bf16, (uint16_t)(use_s ? vs : 0u));
       }
   }
   __syncthreads();
 
-  const bool gather = A.sel_idx != nullptr;
-  const int n_tok = gather ? A.k_sel : (int)min((int64_t)A.seq_lens[b], A.capacity);
+  const int n_tok = GATHER ? A.k_sel : (int)min((int64_t)A.seq_lens[b], A.capacity);
   const int c0 = chunk * A.chunk, c1 = min(n_tok, c0 + A.chunk);
   const uint8_t* recs = A.records + ((int64_t)b * A.kv_heads + hkv) * A.capacity * A.rec_bytes;
-  const int32_t* sel = gather ? A.sel_idx + ((int64_t)b * A.kv_heads + hkv) * A.k_sel : nullptr;
-  const int vslot = lane >> 2, vj = lane & 3;        // value layout: token slot, head / coordinate group
+  const int32_t* sel = GATHER ? A.sel_idx + ((int64_t)b * A.kv_heads + hkv) * A.k_sel : nullptr;
+  const int vslot = lane >> 2, vj = lane & 3;   // softmax layout: token slot, head (also coordinate quarter)
   float* tile = stile[wave];
+  uint32_t* vst = vstage[wave];
+  float* wst = wstage[wave];
 
-  f32x4 acc[32];
+  // value accumulators: lane (column n = 2 h + w half, K slice kg) holds rows 4 kg + r of
+  // coordinate tile mt, i.e. o[h][8 (4 kg + r) + mt] for its w half (columns 8..15 unused)
+  f32x4 acc[8];
 #pragma unroll
-  for (int k = 0; k < 32; ++k) acc[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float mrun = kNegInf, lsum = 0.0f;
+  for (int mt = 0; mt < 8; ++mt) acc[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float mrun = kNegInf;    // running maximum of head vj (uniform across the wave for each head)
+  float lsum = 0.0f;       // this lane's share of sum_t p_t for head vj
+  const int vh = n >> 1;   // head of this lane's value column (n < 8)
 
-  for (int base = c0 + wave * 16; base < c1; base += NW * 16) {
-    // ---- key-layout loads: token base + n, coordinates [32 kg, 32 kg + 32) ----
-    int pk = min(base + n, c1 - 1);
-    int64_t tk = gather ? sel[pk] : pk;
-    if (tk < 0 || tk >= A.capacity) tk = 0;
-    const uint8_t* rk = recs + tk * A.rec_bytes;
+  struct Fields {
     uint32_t kw[BK];
+    uint32_t sw;
+    u32x4 vw;
+    float nk, nrho, nv;
+    bool valid;
+  };
+  // Addresses are always clamped to a record of this (sequence, head), so every load is
+  // unconditional (no memory operation under a branch in the loop).
+  auto fetch = [&](int base, Fields& f) {
+    const int pk = min(base + n, c1 - 1);
+    int64_t tk = pk;
+    if (GATHER) {
+      tk = sel[pk];
+      tk = (tk < 0 || tk >= A.capacity) ? 0 : tk;
+    }
+    const uint8_t* rk = recs + tk * A.rec_bytes;
 #pragma unroll
-    for (int i = 0; i < BK; ++i) kw[i] = reinterpret_cast<const uint32_t*>(rk + kg * 4 * BK)[i];
-    const uint32_t sw = QJL ? reinterpret_cast<const uint32_t*>(rk + A.kbytes)[kg] : 0u;
-    // ---- value-layout loads: token base + vslot, coordinates [32 vj, 32 vj + 32) ----
+    for (int i = 0; i < BK; ++i) f.kw[i] = reinterpret_cast<const uint32_t*>(rk + kg * 4 * BK)[i];
+    f.sw = QJL ? reinterpret_cast<const uint32_t*>(rk + A.kbytes)[kg] : 0u;
     const int pv = base + vslot;
-    bool valid = pv < c1;
-    int64_t tv = gather ? sel[min(pv, c1 - 1)] : min(pv, c1 - 1);
-    valid = valid && tv >= 0 && tv < A.capacity;
-    if (!valid) tv = 0;
+    int64_t tv = min(pv, c1 - 1);
+    if (GATHER) tv = sel[tv];
+    f.valid = pv < c1 && tv >= 0 && tv < A.capacity;
+    tv = f.valid ? tv : 0;
     const uint8_t* rv = recs + tv * A.rec_bytes;
-    const u32x4 vw = *reinterpret_cast<const u32x4*>(rv + A.kbytes + A.sbytes + 16 * vj);
+    f.vw = *reinterpret_cast<const u32x4*>(rv + A.kbytes + A.sbytes + 16 * vj);
     const float* nrm = reinterpret_cast<const float*>(rv + A.norm_off);
-    const float nk = nrm[0], nrho = nrm[1], nv = nrm[2];
+    f.nk = nrm[0];
+    f.nrho = nrm[1];
+    f.nv = nrm[2];
+  };
 
-    // ---- key scores on the matrix cores ----
+  Fields cur;
+  int base = c0 + wave * 16;
+  if (base < c1) fetch(base, cur);
+  for (; base < c1; base += NW * 16) {
+    Fields nxt;
+    fetch(base + NW * 16, nxt);      // prefetch the next step's record fields (clamped)
+
+    // ---- key scores ----
     f32x4 C0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f}, C1 = C0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t x = field<BK>(kw, 4 * BK * j, 4 * BK);
+      const uint32_t x = field<BK>(cur.kw, 4 * BK * j, 4 * BK);
       const uint32_t S = spread4<BK>(x);
-      const uint32_t bl = __builtin_amdgcn_perm(thl[1], thl[0], S);
-      const uint32_t bh = __builtin_amdgcn_perm(thh[1], thh[0], S);
-      const uint32_t ll = __builtin_amdgcn_perm(tll[1], tll[0], S);
-      const uint32_t lh = __builtin_amdgcn_perm(tlh[1], tlh[0], S);
+      const uint32_t bl = __builtin_amdgcn_perm(thl[1], thl[0], S), bh = __builtin_amdgcn_perm(thh[1], thh[0], S);
+      const uint32_t ll = __builtin_amdgcn_perm(tll[1], tll[0], S), lh = __builtin_amdgcn_perm(tlh[1], tlh[0], S);
       const u32x4 a = u32x4{__builtin_amdgcn_perm(bh, bl, 0x05010400u), __builtin_amdgcn_perm(bh, bl, 0x07030602u),
                             __builtin_amdgcn_perm(lh, ll, 0x05010400u), __builtin_amdgcn_perm(lh, ll, 0x07030602u)};
-      const bf16x8 av = __builtin_bit_cast(bf16x8, a);
       if (j & 1)
-        C1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, Bc[j], C1, 0, 0, 0);
+        C1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), Bc[j], C1, 0, 0, 0);
       else
-        C0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, Bc[j], C0, 0, 0, 0);
+        C0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), Bc[j], C0, 0, 0, 0);
     }
     if (QJL) {
-      const uint32_t nsw = ~sw;   // bit set -> negative sign
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        u32x4 a;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const uint32_t t2 = (nsw >> (8 * j + 2 * v)) & 3u;
-          a[v] = ((t2 * 0x40008000u) & 0x80008000u) | 0x3F803F80u;
-        }
-        const bf16x8 av = __builtin_bit_cast(bf16x8, a);
+        const u32x4 a = stab[(cur.sw >> (8 * j)) & 0xFFu];
         if (j & 1)
-          C1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, Bq[j], C1, 0, 0, 0);
+          C1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), Bq[j], C1, 0, 0, 0);
         else
-          C0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, Bq[j], C0, 0, 0, 0);
+          C0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), Bq[j], C0, 0, 0, 0);
       }
     }
-    // ---- score tile -> lane per (token slot, head) ----
+    // ---- score tile -> lane per (token slot, head); stage value codes by coordinate octet ----
 #pragma unroll
     for (int r = 0; r < 4; ++r) tile[(4 * kg + r) * 16 + n] = C0[r] + C1[r];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vst[(4 * vj + r) * 16 + vslot] = cur.vw[r];
     wave_lds_sync();
     const f32x4 s4 = *reinterpret_cast<const f32x4*>(tile + vslot * 16 + 4 * vj);
-    wave_lds_sync();
-    const float shat = fmaf(A.qjl_coef * nrho, s4[2] + s4[3], nk * A.inv_sqrt_d * (s4[0] + s4[1]));
-    const float logit = A.scale * shat;
-    if (A.logits && valid) A.logits[(qrow0 + vj) * A.logit_stride + pv] = logit;
-    // ---- lazy online softmax (per lane: one token slot, one head) ----
-    if (valid && logit > mrun + kLazy) {
-      const float f = mrun == kNegInf ? 0.0f : __expf(mrun - logit);
-      lsum *= f;
+    const float shat = fmaf(A.qjl_coef * cur.nrho, s4[2] + s4[3], cur.nk * A.inv_sqrt_d * (s4[0] + s4[1]));
+    const float logit = cur.valid ? A.scale * shat : kNegInf;
+    if (LOGITS && cur.valid) A.logits[(qrow0 + vj) * A.logit_stride + base + vslot] = logit;
+    // ---- running maximum per head, shared by the wave, raised lazily ----
+    float tmax = logit;
 #pragma unroll
-      for (int k = 0; k < 32; ++k) acc[k] *= f;
-      mrun = logit;
+    for (int msk = 4; msk < 64; msk <<= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, msk));
+    const bool raise = tmax > mrun + kLazy;           // uniform within each head
+    if (__ballot(raise) != 0ull) {
+      const float fct = raise ? (mrun == kNegInf ? 0.0f : __expf(mrun - tmax)) : 1.0f;
+      lsum *= fct;
+      mrun = raise ? tmax : mrun;
+      // rescale the value accumulators of head vh by that head's factor
+      const float fv = __shfl(fct, vh);               // lane vh (slot 0) holds head vh's factor
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) acc[mt] *= fv;
     }
-    const float p = valid ? __expf(logit - mrun) : 0.0f;
+    const float p = cur.valid ? __expf(logit - mrun) : 0.0f;
     lsum += p;
-    const float wv = p * nv * A.inv_sqrt_d;
-    // ---- values on the matrix cores ----
+    wst[vj * 16 + vslot] = p * cur.nv * A.inv_sqrt_d;
+    wave_lds_sync();
+    // ---- values: B = w halves of (head vh) for tokens 4 kg .. 4 kg + 3, A = level halves ----
+    const f32x4 w4 = *reinterpret_cast<const f32x4*>(wst + (vh & 3) * 16 + 4 * kg);
+    const u32x4 codes = *reinterpret_cast<const u32x4*>(vst + n * 16 + 4 * kg);   // row n = coordinate octet
+    wave_lds_sync();
+    u32x4 bw;
 #pragma unroll
-    for (int mb = 0; mb < 16; ++mb) {
-      const uint32_t byte = (vw[mb >> 2] >> (8 * (mb & 3))) & 0xFFu;
-      const float2 g = vtab[byte];
-      acc[2 * mb] = __builtin_amdgcn_mfma_f32_4x4x1f32(g.x, wv, acc[2 * mb], 0, 0, 0);
-      acc[2 * mb + 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(g.y, wv, acc[2 * mb + 1], 0, 0, 0);
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t h = bf16_half(w4[d], n & 1);
+      bw[d] = n < 8 ? (h | (h << 16)) : 0u;
     }
+    const bf16x8 Bv = __builtin_bit_cast(bf16x8, bw);
+#pragma unroll
+    for (int pr = 0; pr < 4; ++pr) {                  // coordinate tiles 2 pr, 2 pr + 1
+      u32x4 a0, a1;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const u32x2 pv = vtab[(codes[d] >> (8 * pr)) & 0xFFu];
+        a0[d] = pv[0];
+        a1[d] = pv[1];
+      }
+      acc[2 * pr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), Bv, acc[2 * pr], 0, 0, 0);
+      acc[2 * pr + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), Bv, acc[2 * pr + 1], 0, 0, 0);
+    }
+    cur = nxt;
   }
 
-  // ---- merge the 16 token slots of the wave (lane bits 2..5), then the waves ----
+  // ---- merge: sum the two w halves (columns 2h, 2h+1), the slots' l, then the waves ----
 #pragma unroll
-  for (int msk = 4; msk < 64; msk <<= 1) {
-    const float mo = __shfl_xor(mrun, msk);
-    const float lo = __shfl_xor(lsum, msk);
-    const float mx = fmaxf(mrun, mo);
-    const float fs = mrun == kNegInf ? 0.0f : __expf(mrun - mx);
-    const float fo = mo == kNegInf ? 0.0f : __expf(mo - mx);
-    lsum = lsum * fs + lo * fo;
+  for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-    for (int k = 0; k < 32; ++k)
+    for (int r = 0; r < 4; ++r) acc[mt][r] += __shfl_xor(acc[mt][r], 1);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float ao = __shfl_xor(acc[k][r], msk);
-        acc[k][r] = acc[k][r] * fs + ao * fo;
-      }
-    mrun = mx;
+  for (int msk = 4; msk < 64; msk <<= 1) lsum += __shfl_xor(lsum, msk);
+  if (lane < 4) {               // slot 0 lanes: head vj's m and l
+    red[wave][vj][0] = mrun;
+    red[wave][vj][1] = lsum;
   }
-  if (vslot == 0) {
-    float* rr = red[wave][vj];
-    rr[0] = mrun;
-    rr[1] = lsum;
+  if (n < 8 && (n & 1) == 0) {  // column (h, hi half) lanes: o[h][8 (4 kg + r) + mt]
 #pragma unroll
-    for (int k = 0; k < 32; ++k)
+    for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) rr[2 + 32 * r + k] = acc[k][r];
+      for (int r = 0; r < 4; ++r) red[wave][vh][2 + 8 * (4 * kg + r) + mt] = acc[mt][r];
   }
   __syncthreads();
   const int stride = D + 2;
@@ -1087,6 +1139,26 @@ bool plan_decode(const Consts& c, int batch, int q_heads, int kv_heads, int64_t 
   return true;
 }
 
+template <int BK, bool QJL>
+static void launch_mfma_bk(const DecodeArgs& a, bool gather, bool logits, dim3 grid, hipStream_t st) {
+  if (gather && logits)
+    hipLaunchKernelGGL((decode_mfma_kernel<BK, QJL, true, true>), grid, dim3(kMfmaThreads), 0, st, a);
+  else if (gather)
+    hipLaunchKernelGGL((decode_mfma_kernel<BK, QJL, true, false>), grid, dim3(kMfmaThreads), 0, st, a);
+  else if (logits)
+    hipLaunchKernelGGL((decode_mfma_kernel<BK, QJL, false, true>), grid, dim3(kMfmaThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<BK, QJL, false, false>), grid, dim3(kMfmaThreads), 0, st, a);
+}
+
+static void launch_mfma_scan(const DecodeArgs& a, int kb, bool qjl, bool gather, bool logits, dim3 grid,
+                             hipStream_t st) {
+  if (kb == 3 && qjl) launch_mfma_bk<3, true>(a, gather, logits, grid, st);
+  else if (kb == 3) launch_mfma_bk<3, false>(a, gather, logits, grid, st);
+  else if (qjl) launch_mfma_bk<2, true>(a, gather, logits, grid, st);
+  else launch_mfma_bk<2, false>(a, gather, logits, grid, st);
+}
+
 template <int HPL>
 static void launch_scan_hpl(const DecodeArgs& a, int kb, int vb, dim3 grid, size_t lds, hipStream_t st) {
 #define TQ_DEC(BK_, BV_)                                                                         \
@@ -1150,14 +1222,7 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
   dim3 grid(plan.n_chunks, kv_heads, batch);
   ev.before(stream);
   if (plan.mfma) {
-    if (c.kb == 3 && c.m)
-      hipLaunchKernelGGL((decode_mfma_kernel<3, true>), grid, dim3(kMfmaThreads), 0, stream, a);
-    else if (c.kb == 3)
-      hipLaunchKernelGGL((decode_mfma_kernel<3, false>), grid, dim3(kMfmaThreads), 0, stream, a);
-    else if (c.m)
-      hipLaunchKernelGGL((decode_mfma_kernel<2, true>), grid, dim3(kMfmaThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL((decode_mfma_kernel<2, false>), grid, dim3(kMfmaThreads), 0, stream, a);
+    launch_mfma_scan(a, c.kb, c.m > 0, sel_idx != nullptr, logits != nullptr, grid, stream);
   } else if (plan.hpl == 4) {
     launch_scan_hpl<4>(a, c.kb, c.vb, grid, plan.lds_bytes, stream);
   } else {
