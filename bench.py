@@ -2,9 +2,9 @@
 """Benchmark of the compressed-KV decode path on one MI355X.
 
 A step is one decode pass of the hot path over the resident compressed cache: query
-preparation (q_x = Pi q, q_s = S q_x), the split-K scan over every packed record (LUT-GEMV
-score estimates, online softmax, rotated-domain value aggregation) and the merge
-(log-sum-exp combine, un-rotation).  The cache is compressed once before the timed region
+preparation (q_x = Pi q, q_s = S q_x), the split-K scan over every packed record (score
+estimates from the codes, online softmax, rotated-domain value aggregation) and the merge
+(log-sum-exp combine, exact segment, un-rotation).  The cache is compressed once before the timed region
 (that compress is timed separately and reported beside the step).  The default workload is
 the Llama-3-8B-shaped 32K-context decode (batch 16, 32 query heads, 8 KV heads, head_dim
 128, 3-bit keys + 128-bit QJL sketch, 4-bit values, Student-t(4) K/V in bf16).
@@ -72,6 +72,14 @@ def traffic_from_profile(workload: str, launches_bytes: float):
     if s.get("kernel_source_sha256_16") != kernel_source_hash() or s.get("workload") != workload:
         return None
     return s.get("hbm_bytes_per_launch")
+
+
+def scan_kernel_name(w) -> str:
+    """The scan kernel the library picks for this shape (matrix-core path for head_dim 128,
+    4 query heads per KV head, 2/3-bit keys, 4-bit values, m in {0, 128})."""
+    mfma = (w.head_dim == 128 and w.q_heads == 4 * w.kv_heads and w.value_bits == 4
+            and w.key_bits in (2, 3) and w.qjl_dim in (0, 128))
+    return "decode_mfma_kernel" if mfma else "decode_scan_kernel"
 
 
 def cpu_baseline(w, h, q, records, budget_s: float = 12.0):
@@ -195,7 +203,7 @@ def main():
                    "key_bits": w.key_bits, "qjl_dim": w.qjl_dim, "value_bits": w.value_bits,
                    "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype, "record_bytes": h.record_bytes,
                    "seed": w.seed},
-        "roofline": {"bound": "hbm", "kernel": "decode_scan_kernel", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": scan_kernel_name(w), "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic_from_profile(w.name, alg_bytes),
                      "algorithmic_bytes_per_launch": alg_bytes, "scan_ms": scan_ms},
