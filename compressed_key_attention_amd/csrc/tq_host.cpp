@@ -2,6 +2,7 @@
 // (seeded Gaussians, Householder QR, Lloyd-Max codebooks) and the device upload.
 // Compiled with -ffp-contract=off so that its float64 arithmetic is plain IEEE.
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -174,6 +175,31 @@ void lloyd_max(int bits, std::vector<double>* levels, std::vector<double>* bound
   for (int i = 0; i + 1 < L; ++i) (*bounds)[i] = 0.5 * (lev[i] + lev[i + 1]);
 }
 
+// Scale F for two-limb fixed-point key levels (level ~= round(level * F) / F, |round| <= 32512):
+// among F in [F_max / 2, F_max] the one whose products with the float32 levels lie closest
+// to integers (worst case over the levels), so integer score products lose the least.
+float key_fixed_point_scale(const float* levels, int n) {
+  double gmax = 0.0;
+  for (int i = 0; i < n; ++i) gmax = std::max(gmax, std::fabs((double)levels[i]));
+  if (gmax == 0.0) return 1.0f;
+  const double f_max = 32512.0 / gmax;
+  const int steps = 1 << 18;
+  double best_f = f_max, best_err = INFINITY;
+  for (int s = 0; s <= steps; ++s) {
+    const double f = (float)(f_max * (0.5 + 0.5 * s / steps));   // candidates exact in float32
+    double err = 0.0;
+    for (int i = 0; i < n; ++i) {
+      const double v = (double)levels[i] * f;
+      err = std::max(err, std::fabs(v - std::nearbyint(v)) / f);
+    }
+    if (err < best_err) {
+      best_err = err;
+      best_f = f;
+    }
+  }
+  return (float)best_f;
+}
+
 tq_status check_config(const tq_config* cfg) {
   if (!cfg) return fail(TQ_ERR_INVALID_ARGUMENT, "config is NULL");
   if (cfg->head_dim <= 0 || cfg->key_bits <= 0 || cfg->value_bits <= 0 || cfg->qjl_dim < 0)
@@ -208,6 +234,7 @@ void fill_consts(const tq_config* cfg, tq::Consts* c) {
   lloyd_max(c->kb, &lv, &bd);
   for (size_t i = 0; i < lv.size(); ++i) c->key_levels[i] = (float)lv[i];
   for (size_t i = 0; i < bd.size(); ++i) c->key_bounds[i] = (float)bd[i];
+  c->key_fix = key_fixed_point_scale(c->key_levels, 1 << c->kb);
   lloyd_max(c->vb, &lv, &bd);
   for (size_t i = 0; i < lv.size(); ++i) c->val_levels[i] = (float)lv[i];
   for (size_t i = 0; i < bd.size(); ++i) c->val_bounds[i] = (float)bd[i];

@@ -34,6 +34,8 @@ struct Consts {
   float inv_sqrt_d;               // 1/sqrt(d) rounded to float32
   double sqrt_d;                  // sqrt(d) in float64
   float qjl_coef;                 // sqrt(pi/2)/m rounded to float32 (0 when m = 0)
+  float key_fix;                  // fixed-point scale of the key levels for integer products:
+                                  // |level| * key_fix <= 32512, levels * key_fix near integers
 };
 
 // Device buffers a handle owns.

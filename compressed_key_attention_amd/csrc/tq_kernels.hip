@@ -455,7 +455,7 @@ struct DecodeArgs {
   int64_t capacity, logit_stride;
   int d, m, kbytes, sbytes, rec_bytes, norm_off;
   int G, q_heads, kv_heads, k_sel, chunk, n_chunks, sign_bytes;
-  float scale, inv_sqrt_d, qjl_coef;
+  float scale, inv_sqrt_d, qjl_coef, key_fix;
   float key_levels[kMaxLevels];
   float val_levels[kMaxLevels];
 };
@@ -698,21 +698,45 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_scan_kernel(DecodeArgs 
 // Matrix-core decode scan for head_dim 128 and 4 query heads per KV head (2- or 3-bit keys,
 // 4-bit values).  Same arithmetic as decode_scan_kernel, laid out for gfx950.  Each wave
 // takes 16 tokens per step:
-//  * key scores on v_mfma_f32_16x16x32_bf16: rows = tokens, columns = (head, code part / QJL
-//    part, query high / low bf16 half); K runs over (coordinate, codebook level high / low
-//    bf16 half) and over QJL sign bits (+-1, exact in bf16).  Two bf16 halves per factor keep
-//    ~16 significant bits with float32 accumulation.  Key levels are looked up in registers
-//    (v_perm_b32); sign patterns come from a 256-entry LDS table of +-1 bf16 octets.
+//  * key scores on v_mfma_i32_16x16x64_i8, exact in int32: rows = tokens, columns = (head,
+//    part).  Key levels are two-limb fixed point (level ~= (256 hi + lo) / F with int8 limbs,
+//    F chosen on the host so the levels sit near integers); queries and query sketches are
+//    three-limb fixed point (24 bits against the head's largest entry).  The code product
+//    keeps the limb products of weight 2^24, 2^16 and 2^8 (three columns per head) and drops
+//    only low x low (2^-24 relative); the QJL product has its own accumulator with one column
+//    per sketch limb.  Level limbs come from registers (v_perm_b32, 4 codes per
+//    instruction); QJL bits enter as 0/1 bytes and the sketch sum is subtracted afterwards.
 //  * the score tile goes through LDS to a lane-per-(token, head) layout; the running maximum of
 //    each head is shared by the wave (raised lazily), p and w = p r_v / sqrt(d) per lane;
-//  * value aggregation on the same bf16 MFMA: rows = coordinates, K = (token, level half),
-//    columns = (head, w half); the 16 tokens' value codes are transposed through 1 KB of LDS
-//    and their level halves read as pairs from a 256-entry LDS table.
+//  * value aggregation on v_mfma_f32_16x16x32_bf16: rows = coordinates, K = (token, level
+//    half), columns = (head, w half); the 16 tokens' value codes are transposed through 1 KB
+//    of LDS and their level halves read as pairs from a 256-entry LDS table.
 // -----------------------------------------------------------------------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Two int8 limbs of a fixed-point integer v (|v| <= 32639): v = 256 hi + lo, lo in [-128, 127].
+__device__ __forceinline__ void int8_limbs(int v, int& hi, int& lo) {
+  hi = (v + 128) >> 8;
+  lo = v - 256 * hi;
+}
+// Three int8 limbs (|v| <= 127 * 65536 + 32767): v = 65536 l2 + 256 l1 + l0, l0, l1 in [-128, 127].
+__device__ __forceinline__ void int8_limbs3(int v, int& l2, int& l1, int& l0) {
+  int rest;
+  int8_limbs(v, rest, l0);
+  int8_limbs(rest, l2, l1);
+}
+
+// Coordinate (within a lane's 32-coordinate slice) of byte k of key selector s.  3-bit codes:
+// selector s holds codes 4s .. 4s+3 (spread from the bitstream); 2-bit codes: selector
+// 4w + t holds the codes at bits 2t of every byte of word w, i.e. 16w + 4k + t.
+template <int BK>
+__device__ constexpr int sel_coord(int s, int k) {
+  return BK == 3 ? 4 * s + k : 16 * (s >> 2) + 4 * k + (s & 3);
+}
 
 __device__ __forceinline__ uint32_t bf16_rn_bits(float x) {
   uint32_t u = __float_as_uint(x);
@@ -745,8 +769,7 @@ template <int BK, bool QJL, bool GATHER, bool LOGITS>
 __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs A) {
   constexpr int D = 128, G = 4, NW = kMfmaThreads / 64;
   __shared__ u32x2 vtab[256];               // byte of value codes -> (level pair of lo nibble, of hi nibble)
-  __shared__ u32x4 stab[256];               // byte of QJL bits -> 8 bf16 (+1 for a set bit, -1 otherwise)
-  __shared__ __attribute__((aligned(16))) float stile[NW][16 * 16];    // score tile
+  __shared__ __attribute__((aligned(16))) float stile[NW][2 * 16 * 16]; // score tiles (code, QJL)
   __shared__ __attribute__((aligned(16))) uint32_t vstage[NW][16 * 16]; // [coord octet][token] value codes
   __shared__ __attribute__((aligned(16))) float wstage[NW][4 * 16];    // [head][token] weights
   __shared__ float red[NW][G][D + 2];       // cross-wave merge
@@ -754,33 +777,32 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
   const int b = blockIdx.z, hkv = blockIdx.y, chunk = blockIdx.x;
   const int64_t qrow0 = (int64_t)b * A.q_heads + (int64_t)hkv * G;
 
-  for (int e = threadIdx.x; e < 256; e += blockDim.x) {
+  for (int e = threadIdx.x; e < 256; e += blockDim.x)
     vtab[e] = u32x2{bf16_pair(A.val_levels[e & 15]), bf16_pair(A.val_levels[e >> 4])};
-    u32x4 sp;
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-      sp[v] = (((e >> (2 * v)) & 1) ? 0x3F80u : 0xBF80u) | ((((e >> (2 * v + 1)) & 1) ? 0x3F80u : 0xBF80u) << 16);
-    stab[e] = sp;
-  }
 
-  // key codebook halves as byte tables for v_perm: byte c of each pair = code c
-  uint32_t thl[2] = {0, 0}, thh[2] = {0, 0}, tll[2] = {0, 0}, tlh[2] = {0, 0};
+  // key levels as int8 limbs: gamma ~= (256 hi + lo) / F, byte c of each table word = code c
+  const float fk = A.key_fix;
+  uint32_t th[2] = {0, 0}, tl[2] = {0, 0};
 #pragma unroll
   for (int c = 0; c < (1 << BK); ++c) {
-    const float g = A.key_levels[c];
-    const uint32_t h = bf16_rn_bits(g), l = bf16_rn_bits(g - bf16_bits_f(h));
-    thl[c >> 2] |= (h & 0xFFu) << (8 * (c & 3));
-    thh[c >> 2] |= (h >> 8) << (8 * (c & 3));
-    tll[c >> 2] |= (l & 0xFFu) << (8 * (c & 3));
-    tlh[c >> 2] |= (l >> 8) << (8 * (c & 3));
+    int hi, lo;
+    int8_limbs((int)rintf(A.key_levels[c] * fk), hi, lo);
+    th[c >> 2] |= (uint32_t)(hi & 0xFF) << (8 * (c & 3));
+    tl[c >> 2] |= (uint32_t)(lo & 0xFF) << (8 * (c & 3));
   }
 
-  // query operand (B) of the key product: lane column n = (head, part, half), K slice kg.
-  // Code MFMA j takes slots e <-> (coordinate 32 kg + 4 j + e % 4, level half e / 4).
+  // query operands (B): lane column n = (head n / 4, part n % 4), K slice kg holding the
+  // lane's coordinates 32 kg .. 32 kg + 31 (sketch coordinates likewise).
+  //  code MFMA j: elements 0..7 <-> high level limb of selectors 2j, 2j+1, 8..15 <-> low limb;
+  //    part 0 (weight 2^24): hi x q2; part 1 (2^16): hi x q1 + lo x q2; part 2 (2^8):
+  //    hi x q0 + lo x q1; part 3 unused.
+  //  QJL MFMA j: element 4w + k <-> sketch coordinate 32 kg + 8k + 4j + w; part p < 3 holds
+  //    sketch limb 2 - p (weight 2^(8 (2 - p))); part 3 unused.
   const int n = lane & 15, kg = lane >> 4;
-  bf16x8 Bc[8], Bq[4];
+  i32x4 Bc[4], Bq[2];
+  float colscale_k, colscale_q, coloff_q;
   {
-    const int hB = n >> 2, part = (n >> 1) & 1, sp = n & 1;
+    const int hB = n >> 2, part = n & 3;
     const f32x4* qx4 = reinterpret_cast<const f32x4*>(A.qx + (qrow0 + hB) * D + 32 * kg);
     const f32x4* qs4 = reinterpret_cast<const f32x4*>(A.qs + (qrow0 + hB) * (QJL ? A.m : 0) + (QJL ? 32 * kg : 0));
     f32x4 xv[8], sv[8];
@@ -789,21 +811,63 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
       xv[i] = qx4[i];
       sv[i] = QJL ? qs4[i] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
-    const bool use_x = part == 0, use_s = QJL && part == 1;
+    float mx = 0.0f, ms = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t vx = bf16_half(xv[j][e & 3], sp);
-        Bc[j][e] = __builtin_bit_cast(__bf16, (uint16_t)(use_x ? vx : 0u));
+      for (int e = 0; e < 4; ++e) {
+        mx = fmaxf(mx, fabsf(xv[i][e]));
+        ms = fmaxf(ms, fabsf(sv[i][e]));
       }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    ms = fmaxf(ms, __shfl_xor(ms, 16));
+    ms = fmaxf(ms, __shfl_xor(ms, 32));
+    constexpr float kFix3 = 8323072.0f;   // 127 * 65536: the three-limb range
+    const float fq = mx > 0.0f ? kFix3 / mx : 1.0f, fs = ms > 0.0f ? kFix3 / ms : 1.0f;
+    int ssum = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ssum += (int)rintf(sv[i][e] * fs);
+    ssum += __shfl_xor(ssum, 16);
+    ssum += __shfl_xor(ssum, 32);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t vs = bf16_half(sv[(8 * j + e) >> 2][e & 3], sp);
-        Bq[j][e] = __builtin_bit_cast(__bf16, (uint16_t)(use_s ? vs : 0u));
+      for (int w = 0; w < 4; ++w) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int coord = sel_coord<BK>(2 * j + (w & 1), k);
+          int l2, l1, l0;
+          int8_limbs3((int)rintf(xv[coord >> 2][coord & 3] * fq), l2, l1, l0);
+          const bool hi_slot = w < 2;
+          const int v = part == 0 ? (hi_slot ? l2 : 0) : part == 1 ? (hi_slot ? l1 : l2)
+                      : part == 2 ? (hi_slot ? l0 : l1) : 0;
+          word |= (uint32_t)(v & 0xFF) << (8 * k);
+        }
+        Bc[j][w] = (int)word;
       }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int coord = 8 * k + 4 * j + w;
+          int l2, l1, l0;
+          int8_limbs3((int)rintf(sv[coord >> 2][coord & 3] * fs), l2, l1, l0);
+          const int v = part == 0 ? l2 : part == 1 ? l1 : part == 2 ? l0 : 0;
+          word |= (uint32_t)(v & 0xFF) << (8 * k);
+        }
+        Bq[j][w] = (int)word;
+      }
+    const float wpart = part == 0 ? 16777216.0f : part == 1 ? 65536.0f : part == 2 ? 256.0f : 0.0f;
+    colscale_k = wpart / (fq * fk);
+    colscale_q = QJL ? 2.0f * (wpart / 256.0f) / fs : 0.0f;
+    coloff_q = (QJL && part == 0) ? -(float)ssum / fs : 0.0f;
   }
   __syncthreads();
 
@@ -865,39 +929,48 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
     Fields nxt;
     fetch(base + NW * 16, nxt);      // prefetch the next step's record fields (clamped)
 
-    // ---- key scores ----
-    f32x4 C0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f}, C1 = C0;
+    // ---- key scores (exact int32) ----
+    uint32_t sel[8];
+    if constexpr (BK == 3) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t x = field<BK>(cur.kw, 4 * BK * j, 4 * BK);
-      const uint32_t S = spread4<BK>(x);
-      const uint32_t bl = __builtin_amdgcn_perm(thl[1], thl[0], S), bh = __builtin_amdgcn_perm(thh[1], thh[0], S);
-      const uint32_t ll = __builtin_amdgcn_perm(tll[1], tll[0], S), lh = __builtin_amdgcn_perm(tlh[1], tlh[0], S);
-      const u32x4 a = u32x4{__builtin_amdgcn_perm(bh, bl, 0x05010400u), __builtin_amdgcn_perm(bh, bl, 0x07030602u),
-                            __builtin_amdgcn_perm(lh, ll, 0x05010400u), __builtin_amdgcn_perm(lh, ll, 0x07030602u)};
-      if (j & 1)
-        C1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), Bc[j], C1, 0, 0, 0);
-      else
-        C0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), Bc[j], C0, 0, 0, 0);
+      for (int t = 0; t < 8; ++t) sel[t] = spread4<3>(field<BK>(cur.kw, 12 * t, 12));
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) sel[t] = (cur.kw[t >> 2] >> (2 * (t & 3))) & 0x03030303u;
     }
-    if (QJL) {
+    i32x4 C0 = i32x4{0, 0, 0, 0}, C1 = C0, Cq = C0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u32x4 a = stab[(cur.sw >> (8 * j)) & 0xFFu];
-        if (j & 1)
-          C1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), Bq[j], C1, 0, 0, 0);
-        else
-          C0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), Bq[j], C0, 0, 0, 0);
+    for (int j = 0; j < 4; ++j) {
+      const i32x4 a = i32x4{(int)__builtin_amdgcn_perm(th[1], th[0], sel[2 * j]),
+                            (int)__builtin_amdgcn_perm(th[1], th[0], sel[2 * j + 1]),
+                            (int)__builtin_amdgcn_perm(tl[1], tl[0], sel[2 * j]),
+                            (int)__builtin_amdgcn_perm(tl[1], tl[0], sel[2 * j + 1])};
+      if (j & 1)
+        C1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, Bc[j], C1, 0, 0, 0);
+      else
+        C0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, Bc[j], C0, 0, 0, 0);
+      if (QJL && (j & 1)) {
+        i32x4 q;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) q[w] = (int)((cur.sw >> (2 * (j & 2) + w)) & 0x01010101u);
+        Cq = __builtin_amdgcn_mfma_i32_16x16x64_i8(q, Bq[j >> 1], Cq, 0, 0, 0);
       }
     }
     // ---- score tile -> lane per (token slot, head); stage value codes by coordinate octet ----
 #pragma unroll
-    for (int r = 0; r < 4; ++r) tile[(4 * kg + r) * 16 + n] = C0[r] + C1[r];
+    for (int r = 0; r < 4; ++r) {
+      tile[(4 * kg + r) * 16 + n] = (float)(C0[r] + C1[r]) * colscale_k;
+      if (QJL) tile[256 + (4 * kg + r) * 16 + n] = fmaf((float)Cq[r], colscale_q, coloff_q);
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) vst[(4 * vj + r) * 16 + vslot] = cur.vw[r];
     wave_lds_sync();
-    const f32x4 s4 = *reinterpret_cast<const f32x4*>(tile + vslot * 16 + 4 * vj);
-    const float shat = fmaf(A.qjl_coef * cur.nrho, s4[2] + s4[3], cur.nk * A.inv_sqrt_d * (s4[0] + s4[1]));
+    const f32x4 sk = *reinterpret_cast<const f32x4*>(tile + vslot * 16 + 4 * vj);
+    float shat = cur.nk * A.inv_sqrt_d * ((sk[0] + sk[1]) + sk[2]);
+    if (QJL) {
+      const f32x4 sq = *reinterpret_cast<const f32x4*>(tile + 256 + vslot * 16 + 4 * vj);
+      shat = fmaf(A.qjl_coef * cur.nrho, (sq[0] + sq[1]) + sq[2], shat);
+    }
     const float logit = cur.valid ? A.scale * shat : kNegInf;
     if (LOGITS && cur.valid) A.logits[(qrow0 + vj) * A.logit_stride + base + vslot] = logit;
     // ---- running maximum per head, shared by the wave, raised lazily ----
@@ -1215,6 +1288,7 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
   a.scale = sc;
   a.inv_sqrt_d = c.inv_sqrt_d;
   a.qjl_coef = c.qjl_coef;
+  a.key_fix = c.key_fix;
   for (int i = 0; i < kMaxLevels; ++i) {
     a.key_levels[i] = c.key_levels[i];
     a.val_levels[i] = c.val_levels[i];
