@@ -771,7 +771,8 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
   __shared__ u32x2 vtab[256];               // byte of value codes -> (level pair of lo nibble, of hi nibble)
   __shared__ __attribute__((aligned(16))) float stile[NW][2 * 16 * 16]; // score tiles (code, QJL)
   __shared__ __attribute__((aligned(16))) uint32_t vstage[NW][16 * 16]; // [coord octet][token] value codes
-  __shared__ __attribute__((aligned(16))) float wstage[NW][4 * 16];    // [head][token] weights
+  __shared__ __attribute__((aligned(16))) uint32_t wstage[NW][2][4 * 16];  // [w half][head][token] bf16 in high 16 bits
+  __shared__ __attribute__((aligned(16))) uint32_t wzero[4];              // B rows of the unused value columns
   __shared__ float red[NW][G][D + 2];       // cross-wave merge
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = blockIdx.z, hkv = blockIdx.y, chunk = blockIdx.x;
@@ -779,6 +780,7 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
 
   for (int e = threadIdx.x; e < 256; e += blockDim.x)
     vtab[e] = u32x2{bf16_pair(A.val_levels[e & 15]), bf16_pair(A.val_levels[e >> 4])};
+  if (threadIdx.x < 4) wzero[threadIdx.x] = 0u;
 
   // key levels as int8 limbs: gamma ~= (256 hi + lo) / F, byte c of each table word = code c
   const float fk = A.key_fix;
@@ -878,7 +880,7 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
   const int vslot = lane >> 2, vj = lane & 3;   // softmax layout: token slot, head (also coordinate quarter)
   float* tile = stile[wave];
   uint32_t* vst = vstage[wave];
-  float* wst = wstage[wave];
+  uint32_t* wst = wstage[wave][0];
 
   // value accumulators: lane (column n = 2 h + w half, K slice kg) holds rows 4 kg + r of
   // coordinate tile mt, i.e. o[h][8 (4 kg + r) + mt] for its w half (columns 8..15 unused)
@@ -888,6 +890,8 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
   float mrun = kNegInf;    // running maximum of head vj (uniform across the wave for each head)
   float lsum = 0.0f;       // this lane's share of sum_t p_t for head vj
   const int vh = n >> 1;   // head of this lane's value column (n < 8)
+  // B rows of the value product: the w half (n & 1) of head vh for tokens 4 kg .. 4 kg + 3
+  const uint32_t* wsrc = n < 8 ? wstage[wave][n & 1] + (vh & 3) * 16 + 4 * kg : wzero;
 
   struct Fields {
     uint32_t kw[BK];
@@ -897,26 +901,42 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
     bool valid;
   };
   // Addresses are always clamped to a record of this (sequence, head), so every load is
-  // unconditional (no memory operation under a branch in the loop).
+  // unconditional (no memory operation under a branch in the loop).  Byte offsets within the
+  // (sequence, head) run fit in 32 bits (the host routes larger caches to the generic kernel).
+  const uint32_t rb = (uint32_t)A.rec_bytes;
+  const uint32_t kofs = (uint32_t)(kg * 4 * BK), sofs = (uint32_t)(A.kbytes + 4 * kg);
+  const uint32_t vofs = (uint32_t)(A.kbytes + A.sbytes + 16 * vj), nofs = (uint32_t)A.norm_off;
   auto fetch = [&](int base, Fields& f) {
     const int pk = min(base + n, c1 - 1);
-    int64_t tk = pk;
+    uint32_t tk = (uint32_t)pk;
     if (GATHER) {
-      tk = sel[pk];
-      tk = (tk < 0 || tk >= A.capacity) ? 0 : tk;
+      const int t = sel[pk];
+      tk = (t < 0 || (int64_t)t >= A.capacity) ? 0u : (uint32_t)t;
     }
-    const uint8_t* rk = recs + tk * A.rec_bytes;
-#pragma unroll
-    for (int i = 0; i < BK; ++i) f.kw[i] = reinterpret_cast<const uint32_t*>(rk + kg * 4 * BK)[i];
-    f.sw = QJL ? reinterpret_cast<const uint32_t*>(rk + A.kbytes)[kg] : 0u;
+    const uint32_t ok = (uint32_t)__umul24(tk, rb);
+    if constexpr (BK == 3) {
+      typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+      const u32x3 w = *reinterpret_cast<const u32x3*>(recs + (size_t)(ok + kofs));
+      f.kw[0] = w[0];
+      f.kw[1] = w[1];
+      f.kw[2] = w[2];
+    } else {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(recs + (size_t)(ok + kofs));
+      f.kw[0] = w[0];
+      f.kw[1] = w[1];
+    }
+    f.sw = QJL ? *reinterpret_cast<const uint32_t*>(recs + (size_t)(ok + sofs)) : 0u;
     const int pv = base + vslot;
-    int64_t tv = min(pv, c1 - 1);
-    if (GATHER) tv = sel[tv];
-    f.valid = pv < c1 && tv >= 0 && tv < A.capacity;
-    tv = f.valid ? tv : 0;
-    const uint8_t* rv = recs + tv * A.rec_bytes;
-    f.vw = *reinterpret_cast<const u32x4*>(rv + A.kbytes + A.sbytes + 16 * vj);
-    const float* nrm = reinterpret_cast<const float*>(rv + A.norm_off);
+    uint32_t tv = (uint32_t)min(pv, c1 - 1);
+    f.valid = pv < c1;
+    if (GATHER) {
+      const int t = sel[tv];
+      f.valid = f.valid && t >= 0 && (int64_t)t < A.capacity;
+      tv = f.valid ? (uint32_t)t : 0u;
+    }
+    const uint32_t ov = (uint32_t)__umul24(tv, rb);
+    f.vw = *reinterpret_cast<const u32x4*>(recs + (size_t)(ov + vofs));
+    const float* nrm = reinterpret_cast<const float*>(recs + (size_t)(ov + nofs));
     f.nk = nrm[0];
     f.nrho = nrm[1];
     f.nv = nrm[2];
@@ -973,12 +993,12 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
     }
     const float logit = cur.valid ? A.scale * shat : kNegInf;
     if (LOGITS && cur.valid) A.logits[(qrow0 + vj) * A.logit_stride + base + vslot] = logit;
-    // ---- running maximum per head, shared by the wave, raised lazily ----
-    float tmax = logit;
+    // ---- running maximum per head, shared by the wave, raised lazily (rare branch) ----
+    if (__ballot(logit > mrun + kLazy) != 0ull) {
+      float tmax = logit;
 #pragma unroll
-    for (int msk = 4; msk < 64; msk <<= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, msk));
-    const bool raise = tmax > mrun + kLazy;           // uniform within each head
-    if (__ballot(raise) != 0ull) {
+      for (int msk = 4; msk < 64; msk <<= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, msk));
+      const bool raise = tmax > mrun + kLazy;         // uniform within each head
       const float fct = raise ? (mrun == kNegInf ? 0.0f : __expf(mrun - tmax)) : 1.0f;
       lsum *= fct;
       mrun = raise ? tmax : mrun;
@@ -989,18 +1009,22 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
     }
     const float p = cur.valid ? __expf(logit - mrun) : 0.0f;
     lsum += p;
-    wst[vj * 16 + vslot] = p * cur.nv * A.inv_sqrt_d;
+    {
+      // w = hi + lo: hi rounded to bf16, lo the remainder truncated to bf16 (2^-17 relative)
+      const uint32_t wb = __float_as_uint(p * cur.nv * A.inv_sqrt_d);
+      const uint32_t hi = (wb + 0x7FFFu + ((wb >> 16) & 1u)) & 0xFFFF0000u;
+      const uint32_t lo = __float_as_uint(__uint_as_float(wb) - __uint_as_float(hi)) & 0xFFFF0000u;
+      wst[vj * 16 + vslot] = hi;
+      wst[64 + vj * 16 + vslot] = lo;
+    }
     wave_lds_sync();
     // ---- values: B = w halves of (head vh) for tokens 4 kg .. 4 kg + 3, A = level halves ----
-    const f32x4 w4 = *reinterpret_cast<const f32x4*>(wst + (vh & 3) * 16 + 4 * kg);
+    const u32x4 w4 = *reinterpret_cast<const u32x4*>(wsrc);
     const u32x4 codes = *reinterpret_cast<const u32x4*>(vst + n * 16 + 4 * kg);   // row n = coordinate octet
     wave_lds_sync();
     u32x4 bw;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const uint32_t h = bf16_half(w4[d], n & 1);
-      bw[d] = n < 8 ? (h | (h << 16)) : 0u;
-    }
+    for (int d = 0; d < 4; ++d) bw[d] = __builtin_amdgcn_perm(w4[d], w4[d], 0x03020302u);
     const bf16x8 Bv = __builtin_bit_cast(bf16x8, bw);
 #pragma unroll
     for (int pr = 0; pr < 4; ++pr) {                  // coordinate tiles 2 pr, 2 pr + 1
@@ -1295,7 +1319,10 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
   }
   dim3 grid(plan.n_chunks, kv_heads, batch);
   ev.before(stream);
-  if (plan.mfma) {
+  // the matrix-core kernel addresses a (sequence, head) run with 32-bit byte offsets
+  const bool mfma = plan.mfma && capacity < (int64_t(1) << 24) &&
+                    capacity * (int64_t)c.rec_bytes < (int64_t(1) << 31);
+  if (mfma) {
     launch_mfma_scan(a, c.kb, c.m > 0, sel_idx != nullptr, logits != nullptr, grid, stream);
   } else if (plan.hpl == 4) {
     launch_scan_hpl<4>(a, c.kb, c.vb, grid, plan.lds_bytes, stream);

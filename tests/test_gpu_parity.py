@@ -37,7 +37,10 @@ def _np(t):
 def _close(gpu, ref, what):
     gpu = np.asarray(gpu, np.float64)
     ref = np.asarray(ref, np.float64)
-    bad = np.abs(gpu - ref) > ATOL + RTOL * np.abs(ref)
+    tol = ATOL + RTOL * np.abs(ref)
+    bad = np.abs(gpu - ref) > tol
+    if gpu.size:
+        print(f"[tolerance] {what}: worst |gpu - ref| / tol = {np.max(np.abs(gpu - ref) / tol):.3f}", flush=True)
     assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} outside tolerance; worst "
                            f"{np.max(np.abs(gpu - ref) - RTOL * np.abs(ref)):.3e}")
 
