@@ -101,6 +101,36 @@ struct ByteWriter {
   }
 };
 
+// 3-bit code fields are stored in groups of 32 codes, 12 bytes read as little-endian words
+// W0, W1, W2.  Code j < 24 sits at bits 8 (j % 4) + 3 ((j % 8) / 4) of W_(j / 8); code 24 + r
+// (r = 0..7) is bits 3 (r / 4) .. +2 of the 6-bit value T_k of byte lane k = r % 4, bit t of T_k
+// being bit 8k + 6 + (t % 2) of W_(t / 2).  Masking a word (or its shift by 3) with 0x07070707
+// then yields four codes, one per byte: ready-made v_perm selectors.
+__device__ __forceinline__ uint32_t group3_top(uint32_t w0, uint32_t w1, uint32_t w2) {
+  return ((w0 >> 6) & 0x03030303u) | ((w1 >> 4) & 0x0C0C0C0Cu) | ((w2 >> 2) & 0x30303030u);
+}
+__device__ __forceinline__ uint32_t group3_code(uint32_t w0, uint32_t w1, uint32_t w2, int j) {
+  if (j < 24) {
+    const uint32_t w = j < 8 ? w0 : (j < 16 ? w1 : w2);
+    return (w >> (8 * (j & 3) + 3 * ((j >> 2) & 1))) & 7u;
+  }
+  const int r = j - 24;
+  return (group3_top(w0, w1, w2) >> (8 * (r & 3) + 3 * (r >> 2))) & 7u;
+}
+// Place code j of a group (j a compile-time constant after unrolling).
+__device__ __forceinline__ void group3_put(uint32_t (&w)[3], int j, uint32_t code) {
+  if (j < 24) {
+    w[j >> 3] |= code << (8 * (j & 3) + 3 * ((j >> 2) & 1));
+    return;
+  }
+  const int r = j - 24, k = r & 3;
+#pragma unroll
+  for (int b = 0; b < 3; ++b) {
+    const int t = 3 * (r >> 2) + b;
+    w[t >> 1] |= ((code >> b) & 1u) << (8 * k + 6 + (t & 1));
+  }
+}
+
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -182,24 +212,61 @@ __device__ __forceinline__ void rotate_tile(const float* lds_pi, const float (&i
   }
 }
 
-// Epilogue for one rotated vector held as acc[ct][r] = x[(d/4) g + 4 ct + r]:
-// z, codes packed into `dst` (bit offset 0 = the lane's first coordinate).  Returns via
-// `acc` the residual e = x - a*gamma[c] when want_residual.
+// Epilogue for one rotated vector held as acc[ct][r] = x[(d/4) g + 4 ct + r] (lane group g):
+// z, codes packed into the code field starting at `field`.  Returns via `acc` the residual
+// e = x - a*gamma[c] when want_residual.  3-bit fields use the 32-code group layout; at
+// d = 64 two lane groups (g, g ^ 1: lanes l and l ^ 16) share a group and combine it with a
+// shuffle, so every lane must call this.
 template <int D>
 __device__ __forceinline__ void quantize_rotated(f64x4 (&acc)[D / 16], double zscale, double a,
                                                  const float* levels, const float* bounds, int bits,
-                                                 uint8_t* dst, bool want_residual) {
-  constexpr int CT = D / 16;
-  ByteWriter w{dst, 0, 0};
+                                                 uint8_t* field, int g, bool want_residual) {
+  constexpr int CT = D / 16, Q = D / 4;
+  uint32_t codes[CT][4];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float z = (float)(acc[ct][r] * zscale);
       const uint32_t code = quantize_code(z, bounds);
-      w.put(code, bits);
+      codes[ct][r] = code;
       if (want_residual) acc[ct][r] = acc[ct][r] - a * (double)levels[code];
     }
+  }
+  if (bits == 3) {
+    uint32_t w[3] = {0u, 0u, 0u};
+    if (Q == 32) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) group3_put(w, 4 * ct + r, codes[ct][r]);
+    } else {   // Q == 16: this lane group holds codes 16 (g & 1) .. + 15 of group g / 2
+      uint32_t w1[3] = {0u, 0u, 0u};
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          group3_put(w, 4 * ct + r, codes[ct][r]);
+          group3_put(w1, 16 + 4 * ct + r, codes[ct][r]);
+        }
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        w[i] = (g & 1) ? w1[i] : w[i];
+        w[i] |= __shfl_xor(w[i], 16);
+      }
+    }
+    if (Q == 32 || (g & 1) == 0) {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(field + 12 * (Q == 32 ? g : g >> 1));
+      dst[0] = w[0];
+      dst[1] = w[1];
+      dst[2] = w[2];
+    }
+  } else {
+    ByteWriter w{field + (Q * g * bits) / 8, 0, 0};
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w.put(codes[ct][r], bits);
   }
 }
 
@@ -263,8 +330,7 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs A) {
     rotate_tile<D>(lds_pi, in, lane, x);
     const double zs = r > 0.0 ? c.sqrt_d / r : 0.0;
     const double a = (double)r32 / c.sqrt_d;
-    quantize_rotated<D>(x, zs, a, lds_tab, lds_tab + kMaxLevels, c.kb, rec + (Q * g * c.kb) / 8,
-                        true);
+    quantize_rotated<D>(x, zs, a, lds_tab, lds_tab + kMaxLevels, c.kb, rec, g, true);
     double e2 = 0.0;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
@@ -311,7 +377,7 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs A) {
     rotate_tile<D>(lds_pi, in, lane, x);
     const double zsv = rv > 0.0 ? c.sqrt_d / rv : 0.0;
     quantize_rotated<D>(x, zsv, 0.0, lds_tab + 2 * kMaxLevels, lds_tab + 3 * kMaxLevels, c.vb,
-                        rec + c.kbytes + c.sbytes + (Q * g * c.vb) / 8, false);
+                        rec + c.kbytes + c.sbytes, g, false);
 
     if (g == 0) {
       float* nrm = reinterpret_cast<float*>(rec + c.norm_off);
@@ -380,12 +446,26 @@ __global__ void debug_quantize_kernel(Consts c, const float* z_k, const float* p
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= n) return;
   uint8_t* rec = records + t * c.rec_bytes;
-  ByteWriter w{rec, 0, 0};
-  for (int i = 0; i < c.d; ++i) w.put(quantize_code(z_k[t * c.d + i], c.key_bounds), c.kb);
+  auto put_codes = [&](uint8_t* field, const float* z, const float* bounds, int bits) {
+    if (bits == 3) {
+      for (int gi = 0; gi < c.d / 32; ++gi) {
+        uint32_t w[3] = {0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 32; ++j) group3_put(w, j, quantize_code(z[32 * gi + j], bounds));
+        uint32_t* dst = reinterpret_cast<uint32_t*>(field + 12 * gi);
+        dst[0] = w[0];
+        dst[1] = w[1];
+        dst[2] = w[2];
+      }
+    } else {
+      ByteWriter w{field, 0, 0};
+      for (int i = 0; i < c.d; ++i) w.put(quantize_code(z[i], bounds), bits);
+    }
+  };
+  put_codes(rec, z_k + t * c.d, c.key_bounds, c.kb);
   ByteWriter ws{rec + c.kbytes, 0, 0};
   for (int j = 0; j < c.m; ++j) ws.put(p[t * c.m + j] >= 0.0f ? 1u : 0u, 1);
-  ByteWriter wv{rec + c.kbytes + c.sbytes, 0, 0};
-  for (int i = 0; i < c.d; ++i) wv.put(quantize_code(z_v[t * c.d + i], c.val_bounds), c.vb);
+  put_codes(rec + c.kbytes + c.sbytes, z_v + t * c.d, c.val_bounds, c.vb);
   float* nrm = reinterpret_cast<float*>(rec + c.norm_off);
   nrm[0] = r_k[t];
   nrm[1] = rho[t];
@@ -495,8 +575,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_scan_kernel(DecodeArgs 
       const float* qh = qx + (int64_t)(hg * HPL + j) * d;
       float val;
       if (kPairs) {
+        // pair p of a 32-coordinate group: 2-bit codes (2p, 2p+1), adjacent in the bitstream;
+        // 3-bit codes (8 (p / 4) + p % 4, that + 4), one 6-bit byte field of the group layout
         const int c0 = ent & ((1 << BK) - 1), c1 = ent >> BK;
-        val = fmaf(qh[2 * tbl + 1], A.key_levels[c1], qh[2 * tbl] * A.key_levels[c0]);
+        const int pp = tbl & 15, g32 = 32 * (tbl >> 4);
+        const int i0 = BK == 3 ? g32 + 8 * (pp >> 2) + (pp & 3) : 2 * tbl;
+        const int i1 = BK == 3 ? i0 + 4 : 2 * tbl + 1;
+        val = fmaf(qh[i1], A.key_levels[c1], qh[i0] * A.key_levels[c0]);
       } else {
         val = qh[tbl] * A.key_levels[ent];
       }
@@ -559,9 +644,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_scan_kernel(DecodeArgs 
 #pragma unroll
     for (int j = 0; j < HPL; ++j) cs[j] = 0.0f;
     if (kPairs) {
+      const uint32_t top = BK == 3 ? group3_top(kw[0], kw[BK > 1 ? 1 : 0], kw[BK > 2 ? 2 : 0]) : 0u;
 #pragma unroll
       for (int p = 0; p < 16; ++p) {
-        const uint32_t idx = field<BK>(kw, 2 * p * BK, 2 * BK);
+        const uint32_t idx = BK == 3 ? ((p < 12 ? kw[(p >> 2) < BK ? (p >> 2) : 0] : top) >> (8 * (p & 3))) & 63u
+                                     : field<BK>(kw, 2 * p * BK, 2 * BK);
         const float* e = lk + (p * kEnt + idx) * HPL;
         if (HPL == 4) {
           const float4 v = *reinterpret_cast<const float4*>(e);
@@ -640,7 +727,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_scan_kernel(DecodeArgs 
     // values
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      const float gv = gam_v[field<BV>(vw, i * BV, BV)];
+      const uint32_t vc = BV == 3 ? group3_code(vw[0], vw[BV > 1 ? 1 : 0], vw[BV > 2 ? 2 : 0], i)
+                                  : field<BV>(vw, i * BV, BV);
+      const float gv = gam_v[vc];
 #pragma unroll
       for (int j = 0; j < HPL; ++j) acc[j][i] = fmaf(w[j], gv, acc[j][i]);
     }
@@ -731,8 +820,8 @@ __device__ __forceinline__ void int8_limbs3(int v, int& l2, int& l1, int& l0) {
 }
 
 // Coordinate (within a lane's 32-coordinate slice) of byte k of key selector s.  3-bit codes:
-// selector s holds codes 4s .. 4s+3 (spread from the bitstream); 2-bit codes: selector
-// 4w + t holds the codes at bits 2t of every byte of word w, i.e. 16w + 4k + t.
+// selector s holds codes 4s .. 4s+3 (a masked word of the 32-code group layout); 2-bit codes:
+// selector 4w + t holds the codes at bits 2t of every byte of word w, i.e. 16w + 4k + t.
 template <int BK>
 __device__ constexpr int sel_coord(int s, int k) {
   return BK == 3 ? 4 * s + k : 16 * (s >> 2) + 4 * k + (s & 3);
@@ -754,26 +843,25 @@ __device__ __forceinline__ uint32_t bf16_pair(float x) {      // hi | lo << 16
   return hi | (bf16_rn_bits(x - bf16_bits_f(hi)) << 16);
 }
 
-// Spread four FW-bit fields (low 4*FW bits of x) into the four bytes of the result.
-template <int FW>
-__device__ __forceinline__ uint32_t spread4(uint32_t x) {
-  constexpr uint32_t m1 = (1u << (2 * FW)) - 1u;
-  constexpr uint32_t m2 = ((1u << FW) - 1u) * 0x00010001u;
-  const uint32_t y = (x & m1) | ((x & (m1 << (2 * FW))) << (16 - 2 * FW));
-  return (y & m2) | ((y & (m2 << FW)) << (8 - FW));
-}
-
 constexpr int kMfmaThreads = 256;
 
 template <int BK, bool QJL, bool GATHER, bool LOGITS>
 __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs A) {
   constexpr int D = 128, G = 4, NW = kMfmaThreads / 64;
   __shared__ u32x2 vtab[256];               // byte of value codes -> (level pair of lo nibble, of hi nibble)
-  __shared__ __attribute__((aligned(16))) float stile[NW][2 * 16 * 16]; // score tiles (code, QJL)
-  __shared__ __attribute__((aligned(16))) uint32_t vstage[NW][16 * 16]; // [coord octet][token] value codes
+  // Staging tiles, rows padded to TS words so that the four K-slices of a write (and the 16
+  // rows of a 16-byte read) fall on distinct LDS banks.  The cross-wave merge reuses them.
+  constexpr int TS = 20;
+  struct Stage {
+    float tile[NW][2][16 * TS];      // score tiles (code, QJL): [token][column]
+    uint32_t vst[NW][16 * TS];       // value codes: [coordinate octet][token]
+  };
+  __shared__ __attribute__((aligned(16))) union {
+    Stage st;
+    float red[NW][G][D + 2];         // cross-wave merge
+  } sh;
   __shared__ __attribute__((aligned(16))) uint32_t wstage[NW][2][4 * 16];  // [w half][head][token] bf16 in high 16 bits
   __shared__ __attribute__((aligned(16))) uint32_t wzero[4];              // B rows of the unused value columns
-  __shared__ float red[NW][G][D + 2];       // cross-wave merge
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = blockIdx.z, hkv = blockIdx.y, chunk = blockIdx.x;
   const int64_t qrow0 = (int64_t)b * A.q_heads + (int64_t)hkv * G;
@@ -878,8 +966,8 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
   const uint8_t* recs = A.records + ((int64_t)b * A.kv_heads + hkv) * A.capacity * A.rec_bytes;
   const int32_t* sel = GATHER ? A.sel_idx + ((int64_t)b * A.kv_heads + hkv) * A.k_sel : nullptr;
   const int vslot = lane >> 2, vj = lane & 3;   // softmax layout: token slot, head (also coordinate quarter)
-  float* tile = stile[wave];
-  uint32_t* vst = vstage[wave];
+  float* tile = sh.st.tile[wave][0];
+  uint32_t* vst = sh.st.vst[wave];
   uint32_t* wst = wstage[wave][0];
 
   // value accumulators: lane (column n = 2 h + w half, K slice kg) holds rows 4 kg + r of
@@ -952,8 +1040,14 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
     // ---- key scores (exact int32) ----
     uint32_t sel[8];
     if constexpr (BK == 3) {
+      const uint32_t top = group3_top(cur.kw[0], cur.kw[1], cur.kw[2]);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) sel[t] = spread4<3>(field<BK>(cur.kw, 12 * t, 12));
+      for (int t = 0; t < 3; ++t) {
+        sel[2 * t] = cur.kw[t] & 0x07070707u;
+        sel[2 * t + 1] = (cur.kw[t] >> 3) & 0x07070707u;
+      }
+      sel[6] = top & 0x07070707u;
+      sel[7] = (top >> 3) & 0x07070707u;
     } else {
 #pragma unroll
       for (int t = 0; t < 8; ++t) sel[t] = (cur.kw[t >> 2] >> (2 * (t & 3))) & 0x03030303u;
@@ -979,16 +1073,16 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
     // ---- score tile -> lane per (token slot, head); stage value codes by coordinate octet ----
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      tile[(4 * kg + r) * 16 + n] = (float)(C0[r] + C1[r]) * colscale_k;
-      if (QJL) tile[256 + (4 * kg + r) * 16 + n] = fmaf((float)Cq[r], colscale_q, coloff_q);
+      tile[(4 * kg + r) * TS + n] = (float)(C0[r] + C1[r]) * colscale_k;
+      if (QJL) tile[16 * TS + (4 * kg + r) * TS + n] = fmaf((float)Cq[r], colscale_q, coloff_q);
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) vst[(4 * vj + r) * 16 + vslot] = cur.vw[r];
+    for (int r = 0; r < 4; ++r) vst[(4 * vj + r) * TS + vslot] = cur.vw[r];
     wave_lds_sync();
-    const f32x4 sk = *reinterpret_cast<const f32x4*>(tile + vslot * 16 + 4 * vj);
+    const f32x4 sk = *reinterpret_cast<const f32x4*>(tile + vslot * TS + 4 * vj);
     float shat = cur.nk * A.inv_sqrt_d * ((sk[0] + sk[1]) + sk[2]);
     if (QJL) {
-      const f32x4 sq = *reinterpret_cast<const f32x4*>(tile + 256 + vslot * 16 + 4 * vj);
+      const f32x4 sq = *reinterpret_cast<const f32x4*>(tile + 16 * TS + vslot * TS + 4 * vj);
       shat = fmaf(A.qjl_coef * cur.nrho, (sq[0] + sq[1]) + sq[2], shat);
     }
     const float logit = cur.valid ? A.scale * shat : kNegInf;
@@ -1020,7 +1114,7 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
     wave_lds_sync();
     // ---- values: B = w halves of (head vh) for tokens 4 kg .. 4 kg + 3, A = level halves ----
     const u32x4 w4 = *reinterpret_cast<const u32x4*>(wsrc);
-    const u32x4 codes = *reinterpret_cast<const u32x4*>(vst + n * 16 + 4 * kg);   // row n = coordinate octet
+    const u32x4 codes = *reinterpret_cast<const u32x4*>(vst + n * TS + 4 * kg);   // row n = coordinate octet
     wave_lds_sync();
     u32x4 bw;
 #pragma unroll
@@ -1048,6 +1142,8 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
     for (int r = 0; r < 4; ++r) acc[mt][r] += __shfl_xor(acc[mt][r], 1);
 #pragma unroll
   for (int msk = 4; msk < 64; msk <<= 1) lsum += __shfl_xor(lsum, msk);
+  __syncthreads();              // every wave is done with the staging tiles the merge reuses
+  float (*red)[G][D + 2] = sh.red;
   if (lane < 4) {               // slot 0 lanes: head vj's m and l
     red[wave][vj][0] = mrun;
     red[wave][vj][1] = lsum;
@@ -1219,7 +1315,8 @@ bool plan_decode(const Consts& c, int batch, int q_heads, int kv_heads, int64_t 
   const size_t floats = std::max(lut, red);
   if (floats > 160 * 1024 / 4) return false;
   plan->lds_bytes = floats * 4;
-  // split-K: aim at ~2 blocks per CU
+  // split-K: aim at ~2 blocks per CU (3 on the matrix-core path, whose 256-thread blocks fit
+  // three to a CU)
   const int64_t units = (int64_t)std::max(batch, 1) * kv_heads;
   const int64_t target_blocks = 2 * (int64_t)num_cus();
   int64_t chunk = (n_max * units + target_blocks - 1) / std::max<int64_t>(target_blocks, 1);
@@ -1837,10 +1934,16 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs A) {
     const float aq = valid ? A.qjl_coef * nrm[1] : 0.0f;
     const uint32_t* kw = reinterpret_cast<const uint32_t*>(rec);
     for (int i = part; i < A.d; i += 4) {
-      const int pos = i * A.kb, wi = pos >> 5, sh = pos & 31;
-      uint32_t v = kw[wi] >> sh;
-      if (sh + A.kb > 32) v |= kw[wi + 1] << (32 - sh);
-      v &= (1u << A.kb) - 1u;
+      uint32_t v;
+      if (A.kb == 3) {
+        const uint32_t* gw = kw + 3 * (i >> 5);
+        v = group3_code(gw[0], gw[1], gw[2], i & 31);
+      } else {
+        const int pos = i * A.kb, wi = pos >> 5, sh = pos & 31;
+        v = kw[wi] >> sh;
+        if (sh + A.kb > 32) v |= kw[wi + 1] << (32 - sh);
+        v &= (1u << A.kb) - 1u;
+      }
       kt[tt * KP + i] = ak * A.key_levels[v];
     }
     const uint32_t* sw = reinterpret_cast<const uint32_t*>(rec + A.kbytes);

@@ -255,21 +255,86 @@ def compress(codec: Codec, k: np.ndarray, v: np.ndarray):
 
 
 def _pack_stream(codes: np.ndarray, b: int) -> np.ndarray:
-    """Little-endian bitstream: code i occupies stream bits [b*i, b*i + b); stream bit n is
-    bit n % 8 of byte n // 8 (the same as bit n % 32 of little-endian word n // 32)."""
+    """Pack a field of b-bit codes (last axis) into bytes.
+
+    b = 1, 2, 4: little-endian bitstream - code i occupies stream bits [b*i, b*i + b), stream
+    bit n being bit n % 8 of byte n // 8.
+    b = 3: groups of 32 codes, each 12 bytes read as little-endian 32-bit words W0, W1, W2.
+    Code j < 24 occupies bits [8*(j % 4) + 3*((j % 8) // 4), +3) of W_(j // 8).  Code
+    24 + r (r = 0..7) occupies the 6-bit value T_k of byte lane k = r % 4 (bits [3*(r // 4), +3)),
+    where bit t of T_k is bit 8k + 6 + (t % 2) of W_(t // 2).  (Four codes of one selector
+    byte-lane pattern then come out of a word with one shift and one mask.)  A trailing
+    partial group - only fields shorter than a multiple of 32 codes, which no head_dim the
+    library builds has - is a plain bitstream as for the other widths.
+    """
     if codes.shape[-1] == 0:
         return np.zeros(codes.shape[:-1] + (0,), dtype=np.uint8)
+    if b == 3:
+        return _pack_groups3(codes)
+    return _pack_plain(codes, b)
+
+
+def _group3_bit_positions() -> np.ndarray:
+    """pos[j, t] = bit index within the 96-bit group (32 * word + bit) of bit t of code j."""
+    pos = np.zeros((32, 3), dtype=np.int64)
+    for j in range(32):
+        for t in range(3):
+            if j < 24:
+                word, bit = j // 8, 8 * (j % 4) + 3 * ((j % 8) // 4) + t
+            else:
+                r = j - 24
+                k, tt = r % 4, 3 * (r // 4) + t          # bit tt of T_k
+                word, bit = tt // 2, 8 * k + 6 + tt % 2
+            pos[j, t] = 32 * word + bit
+    return pos
+
+
+def _pack_plain(codes: np.ndarray, b: int) -> np.ndarray:
     bitarr = ((codes[..., :, None] >> np.arange(b)) & 1).astype(np.uint8)
     bitarr = bitarr.reshape(codes.shape[:-1] + (codes.shape[-1] * b,))
     return np.packbits(bitarr, axis=-1, bitorder="little")
 
 
-def _unpack_stream(buf: np.ndarray, n: int, b: int) -> np.ndarray:
-    if n == 0:
-        return np.zeros(buf.shape[:-1] + (0,), dtype=np.int64)
+def _unpack_plain(buf: np.ndarray, n: int, b: int) -> np.ndarray:
     bitarr = np.unpackbits(buf, axis=-1, bitorder="little")[..., : n * b]
     bitarr = bitarr.reshape(buf.shape[:-1] + (n, b)).astype(np.int64)
     return np.sum(bitarr << np.arange(b), axis=-1)
+
+
+def _pack_groups3(codes: np.ndarray) -> np.ndarray:
+    n = codes.shape[-1]
+    ng = n // 32
+    pos = _group3_bit_positions()
+    g = codes[..., : 32 * ng].reshape(codes.shape[:-1] + (ng, 32))
+    bits = np.zeros(g.shape[:-1] + (96,), dtype=np.uint8)
+    for j in range(32):
+        for t in range(3):
+            bits[..., pos[j, t]] = (g[..., j] >> t) & 1
+    out = np.packbits(bits, axis=-1, bitorder="little")      # word w bit i = stream bit 32w + i
+    out = out.reshape(codes.shape[:-1] + (ng * 12,))
+    if n % 32:
+        out = np.concatenate([out, _pack_plain(codes[..., 32 * ng:], 3)], axis=-1)
+    return out
+
+
+def _unpack_stream(buf: np.ndarray, n: int, b: int) -> np.ndarray:
+    if n == 0:
+        return np.zeros(buf.shape[:-1] + (0,), dtype=np.int64)
+    if b == 3:
+        ng = n // 32
+        pos = _group3_bit_positions()
+        bits = np.unpackbits(buf[..., : ng * 12], axis=-1, bitorder="little")
+        bits = bits.reshape(buf.shape[:-1] + (ng, 96)).astype(np.int64)
+        codes = np.zeros(buf.shape[:-1] + (ng, 32), dtype=np.int64)
+        for j in range(32):
+            for t in range(3):
+                codes[..., j] |= bits[..., pos[j, t]] << t
+        codes = codes.reshape(buf.shape[:-1] + (32 * ng,))
+        if n % 32:
+            tail = _unpack_plain(buf[..., ng * 12:], n - 32 * ng, 3)
+            codes = np.concatenate([codes, tail], axis=-1)
+        return codes
+    return _unpack_plain(buf, n, b)
 
 
 def pack_records(codec: Codec, f: dict) -> np.ndarray:

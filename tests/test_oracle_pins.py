@@ -144,6 +144,30 @@ def test_pack_unpack_roundtrip(bits):
     assert np.array_equal(O._unpack_stream(O._pack_stream(c, bits), 128, bits), c)
 
 
+@pytest.mark.parametrize("n", [8, 16, 72])
+def test_pack_unpack_roundtrip_partial_3bit_group(n):
+    c = np.random.default_rng(n).integers(0, 8, size=(5, n))
+    buf = O._pack_stream(c, 3)
+    assert buf.shape[-1] == 3 * n // 8
+    assert np.array_equal(O._unpack_stream(buf, n, 3), c)
+
+
+def test_3bit_group_bytes_are_selectors():
+    """The property the 3-bit grouped layout exists for: read as words, (W_p >> 3s) masked by
+    0x07070707 holds codes 8p + 4s + k in byte k, and the top two bits of the three words
+    assemble codes 24..31 the same way."""
+    c = np.random.default_rng(7).integers(0, 8, size=(32,))
+    w = O._pack_stream(c[None], 3)[0].view("<u4").astype(np.int64)
+    def bytes_of(x):
+        return [(x >> (8 * k)) & 0xFF for k in range(4)]
+    for p in range(3):
+        for s in range(2):
+            assert bytes_of((w[p] >> (3 * s)) & 0x07070707) == list(c[8 * p + 4 * s: 8 * p + 4 * s + 4])
+    t = ((w[0] >> 6) & 0x03030303) | ((w[1] >> 4) & 0x0C0C0C0C) | ((w[2] >> 2) & 0x30303030)
+    assert bytes_of(t & 0x07070707) == list(c[24:28])
+    assert bytes_of((t >> 3) & 0x07070707) == list(c[28:32])
+
+
 @pytest.mark.parametrize("cfg,size", [((128, 3, 128, 4), 144), ((64, 3, 64, 4), 80),
                                       ((128, 4, 0, 4), 144), ((128, 2, 128, 2), 96)])
 def test_record_layout(cfg, size):
