@@ -848,7 +848,9 @@ constexpr int kMfmaThreads = 256;
 template <int BK, bool QJL, bool GATHER, bool LOGITS>
 __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs A) {
   constexpr int D = 128, G = 4, NW = kMfmaThreads / 64;
-  __shared__ u32x2 vtab[256];               // byte of value codes -> (level pair of lo nibble, of hi nibble)
+  // value code -> bf16 (hi, lo) pair of its level: 16 words in 16 distinct banks, so lookups
+  // never conflict (equal codes are broadcast)
+  __shared__ uint32_t vtab[16];
   // Staging tiles, rows padded to TS words so that the four K-slices of a write (and the 16
   // rows of a 16-byte read) fall on distinct LDS banks.  The cross-wave merge reuses them.
   constexpr int TS = 20;
@@ -866,8 +868,7 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
   const int b = blockIdx.z, hkv = blockIdx.y, chunk = blockIdx.x;
   const int64_t qrow0 = (int64_t)b * A.q_heads + (int64_t)hkv * G;
 
-  for (int e = threadIdx.x; e < 256; e += blockDim.x)
-    vtab[e] = u32x2{bf16_pair(A.val_levels[e & 15]), bf16_pair(A.val_levels[e >> 4])};
+  if (threadIdx.x < 16) vtab[threadIdx.x] = bf16_pair(A.val_levels[threadIdx.x]);
   if (threadIdx.x < 4) wzero[threadIdx.x] = 0u;
 
   // key levels as int8 limbs: gamma ~= (256 hi + lo) / F, byte c of each table word = code c
@@ -1120,14 +1121,19 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
 #pragma unroll
     for (int d = 0; d < 4; ++d) bw[d] = __builtin_amdgcn_perm(w4[d], w4[d], 0x03020302u);
     const bf16x8 Bv = __builtin_bit_cast(bf16x8, bw);
+    u32x4 nib[2];                                     // low / high nibbles of the code bytes
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      nib[0][d] = codes[d] & 0x0F0F0F0Fu;
+      nib[1][d] = (codes[d] >> 4) & 0x0F0F0F0Fu;
+    }
 #pragma unroll
     for (int pr = 0; pr < 4; ++pr) {                  // coordinate tiles 2 pr, 2 pr + 1
       u32x4 a0, a1;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const u32x2 pv = vtab[(codes[d] >> (8 * pr)) & 0xFFu];
-        a0[d] = pv[0];
-        a1[d] = pv[1];
+        a0[d] = vtab[(nib[0][d] >> (8 * pr)) & 0xFFu];
+        a1[d] = vtab[(nib[1][d] >> (8 * pr)) & 0xFFu];
       }
       acc[2 * pr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), Bv, acc[2 * pr], 0, 0, 0);
       acc[2 * pr + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), Bv, acc[2 * pr + 1], 0, 0, 0);
