@@ -1031,12 +1031,8 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
     f.nv = nrm[2];
   };
 
-  Fields cur;
-  int base = c0 + wave * 16;
-  if (base < c1) fetch(base, cur);
-  for (; base < c1; base += NW * 16) {
-    Fields nxt;
-    fetch(base + NW * 16, nxt);      // prefetch the next step's record fields (clamped)
+  // one 16-token step on fields `cur` (tokens base .. base + 15)
+  auto step = [&](const Fields& cur, int base) {
 
     // ---- key scores (exact int32) ----
     uint32_t sel[8];
@@ -1053,17 +1049,14 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
 #pragma unroll
       for (int t = 0; t < 8; ++t) sel[t] = (cur.kw[t >> 2] >> (2 * (t & 3))) & 0x03030303u;
     }
-    i32x4 C0 = i32x4{0, 0, 0, 0}, C1 = C0, Cq = C0;
+    i32x4 C0 = i32x4{0, 0, 0, 0}, Cq = C0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const i32x4 a = i32x4{(int)__builtin_amdgcn_perm(th[1], th[0], sel[2 * j]),
                             (int)__builtin_amdgcn_perm(th[1], th[0], sel[2 * j + 1]),
                             (int)__builtin_amdgcn_perm(tl[1], tl[0], sel[2 * j]),
                             (int)__builtin_amdgcn_perm(tl[1], tl[0], sel[2 * j + 1])};
-      if (j & 1)
-        C1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, Bc[j], C1, 0, 0, 0);
-      else
-        C0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, Bc[j], C0, 0, 0, 0);
+      C0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, Bc[j], C0, 0, 0, 0);
       if (QJL && (j & 1)) {
         i32x4 q;
 #pragma unroll
@@ -1074,7 +1067,7 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
     // ---- score tile -> lane per (token slot, head); stage value codes by coordinate octet ----
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      tile[(4 * kg + r) * TS + n] = (float)(C0[r] + C1[r]) * colscale_k;
+      tile[(4 * kg + r) * TS + n] = (float)C0[r] * colscale_k;
       if (QJL) tile[16 * TS + (4 * kg + r) * TS + n] = fmaf((float)Cq[r], colscale_q, coloff_q);
     }
 #pragma unroll
@@ -1138,7 +1131,19 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
       acc[2 * pr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), Bv, acc[2 * pr], 0, 0, 0);
       acc[2 * pr + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), Bv, acc[2 * pr + 1], 0, 0, 0);
     }
-    cur = nxt;
+  };
+  // two-way unrolled so that the prefetched fields alternate between f0 and f1 (no copies)
+  Fields f0, f1;
+  int base = c0 + wave * 16;
+  if (base < c1) fetch(base, f0);
+  while (base < c1) {
+    fetch(base + NW * 16, f1);       // prefetch the next step's record fields (clamped)
+    step(f0, base);
+    base += NW * 16;
+    if (base >= c1) break;
+    fetch(base + NW * 16, f0);
+    step(f1, base);
+    base += NW * 16;
   }
 
   // ---- merge: sum the two w halves (columns 2h, 2h+1), the slots' l, then the waves ----
@@ -1324,7 +1329,7 @@ bool plan_decode(const Consts& c, int batch, int q_heads, int kv_heads, int64_t 
   // split-K: aim at ~2 blocks per CU (3 on the matrix-core path, whose 256-thread blocks fit
   // three to a CU)
   const int64_t units = (int64_t)std::max(batch, 1) * kv_heads;
-  const int64_t target_blocks = 2 * (int64_t)num_cus();
+  const int64_t target_blocks = (plan->mfma ? 3 : 2) * (int64_t)num_cus();
   int64_t chunk = (n_max * units + target_blocks - 1) / std::max<int64_t>(target_blocks, 1);
   chunk = std::max<int64_t>(chunk, 256);
   chunk = std::min<int64_t>(chunk, 16384);
