@@ -323,8 +323,11 @@ tq_status tq_create(const tq_config* cfg, tq_handle** out) {
   std::vector<float> s = m ? make_qjl(cfg->qjl_seed, m, d) : std::vector<float>();
   std::vector<float> pi_m = mfma_order(pi, d, d);
   std::vector<float> s_m = m ? mfma_order(s, m, d) : std::vector<float>();
+  std::vector<float> pi_t((size_t)d * d);
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j) pi_t[(size_t)j * d + i] = pi[(size_t)i * d + j];
   const size_t n_pi = (size_t)d * d, n_s = (size_t)m * d;
-  const size_t total = (2 * n_pi + 2 * n_s) * sizeof(float);
+  const size_t total = (3 * n_pi + 2 * n_s) * sizeof(float);
   if (hipGetDevice(&h->device) != hipSuccess) { delete h; return fail(TQ_ERR_DEVICE, "no HIP device"); }
   if (hipMalloc(&h->dev_block, total) != hipSuccess) {
     delete h;
@@ -337,6 +340,7 @@ tq_status tq_create(const tq_config* cfg, tq_handle** out) {
   host.insert(host.end(), pi_m.begin(), pi_m.end());
   host.insert(host.end(), s.begin(), s.end());
   host.insert(host.end(), s_m.begin(), s_m.end());
+  host.insert(host.end(), pi_t.begin(), pi_t.end());
   hipError_t e = hipMemcpy(base, host.data(), total, hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     (void)hipFree(h->dev_block);
@@ -347,6 +351,7 @@ tq_status tq_create(const tq_config* cfg, tq_handle** out) {
   h->dc.pi_mfma = base + n_pi;
   h->dc.s = m ? base + 2 * n_pi : nullptr;
   h->dc.s_mfma = m ? base + 2 * n_pi + n_s : nullptr;
+  h->dc.pi_t = base + 2 * n_pi + 2 * n_s;
   *out = h;
   return ok();
 }

@@ -41,6 +41,7 @@ struct Consts {
 // Device buffers a handle owns.
 struct DevConsts {
   const float* pi;        // [d][d] row-major (x = Pi k)
+  const float* pi_t;      // Pi transposed, [d][d] row-major (row k = column k of Pi)
   const float* s;         // [m][d] row-major
   const float* pi_mfma;   // Pi in the order the compress kernel's MFMA A operand reads it
   const float* s_mfma;    // S in the same order

@@ -1185,8 +1185,30 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
 
 // Merge: log-sum-exp of the chunk partials, the exact (hot) segment in the same softmax
 // (Monarch v3 page, "Wie es funktioniert"), and o = Pi^T o_x + o_hot, divided by the sum.
+// One output of y = M v (M [rows][D] row-major float32, v float32 in LDS), split over two
+// threads (half h of the row each): 64 contiguous floats as independent 16-byte loads (one memory
+// round trip), combined with a shuffle.
+template <int D>
+__device__ __forceinline__ float gemv_row_half_f32(const float* __restrict__ mrow, const float* v, int h) {
+  constexpr int H = D / 2;
+  const float4* p = reinterpret_cast<const float4*>(mrow + h * H);
+  float4 w[H / 4];
+#pragma unroll
+  for (int j = 0; j < H / 4; ++j) w[j] = p[j];
+  float acc = 0.0f;
+#pragma unroll
+  for (int j = 0; j < H / 4; ++j) {
+    const float* vv = v + h * H + 4 * j;
+    acc = fmaf(w[j].x, vv[0], acc);
+    acc = fmaf(w[j].y, vv[1], acc);
+    acc = fmaf(w[j].z, vv[2], acc);
+    acc = fmaf(w[j].w, vv[3], acc);
+  }
+  return acc + __shfl_xor(acc, 1);
+}
+
 struct MergeArgs {
-  const float* pi;
+  const float* pi_t;      // Pi transposed
   const float* part;
   const void* q;
   tq_dtype q_dt;
@@ -1204,17 +1226,32 @@ struct MergeArgs {
 
 constexpr int kMergeThreads = 256;
 
+template <int D>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs A) {
   __shared__ float qv[256];
   __shared__ float ox[256];
   __shared__ float oh[256];
   __shared__ float hl[kMergeThreads];
   __shared__ float red[kMergeThreads];
-  __shared__ float s_stat[2];
   const int hq = blockIdx.x, b = blockIdx.y, d = A.d, hkv = hq / A.G;
   const int64_t row = (int64_t)b * A.q_heads + hq;
   const int stride = d + 2;
   const float* pr = A.part + row * A.n_chunks * stride;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // block-wide max / sum: wave shuffles, then one LDS word per wave
+  auto block_reduce = [&](float v, bool is_max) {
+#pragma unroll
+    for (int msk = 32; msk > 0; msk >>= 1) {
+      const float o = __shfl_xor(v, msk);
+      v = is_max ? fmaxf(v, o) : v + o;
+    }
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    v = red[0];
+    for (int w2 = 1; w2 < kMergeThreads / 64; ++w2) v = is_max ? fmaxf(v, red[w2]) : v + red[w2];
+    __syncthreads();
+    return v;
+  };
   for (int i = threadIdx.x; i < d; i += blockDim.x) {
     qv[i] = load_elem(A.q, A.q_dt, row * d + i);
     oh[i] = 0.0f;
@@ -1232,30 +1269,21 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs A
     mx = fmaxf(mx, lg);
     if (A.logits) A.logits[row * A.logit_stride + A.logit_hot_off + t] = lg;
   }
-  red[threadIdx.x] = mx;
-  __syncthreads();
-  for (int s = blockDim.x / 2; s > 0; s >>= 1) {
-    if (threadIdx.x < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  __syncthreads();
-  // sum of weights
+  const float M = block_reduce(mx, true);
+  // sum of weights and the cold rotated-domain output (loads unconditional, weight 0 for an
+  // empty chunk, whose partial holds zeros)
   float l = 0.0f;
-  if (M != kNegInf) {
-    for (int c = threadIdx.x; c < A.n_chunks; c += blockDim.x) {
-      const float mc = pr[(int64_t)c * stride];
-      if (mc != kNegInf) l += pr[(int64_t)c * stride + 1] * __expf(mc - M);
-    }
+  for (int c = threadIdx.x; c < A.n_chunks; c += blockDim.x) {
+    const float mc = pr[(int64_t)c * stride];
+    l += (M != kNegInf && mc != kNegInf) ? pr[(int64_t)c * stride + 1] * __expf(mc - M) : 0.0f;
   }
-  // cold rotated-domain output
   for (int i = threadIdx.x; i < d; i += blockDim.x) {
     float acc = 0.0f;
-    if (M != kNegInf)
-      for (int c = 0; c < A.n_chunks; ++c) {
-        const float mc = pr[(int64_t)c * stride];
-        if (mc != kNegInf) acc += pr[(int64_t)c * stride + 2 + i] * __expf(mc - M);
-      }
+    for (int c = 0; c < A.n_chunks; ++c) {
+      const float mc = pr[(int64_t)c * stride];
+      const float wgt = (M != kNegInf && mc != kNegInf) ? __expf(mc - M) : 0.0f;
+      acc = fmaf(pr[(int64_t)c * stride + 2 + i], wgt, acc);
+    }
     ox[i] = acc;
   }
   // hot tokens, in tiles of blockDim: weights, then value sums
@@ -1279,27 +1307,17 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs A
       oh[i] = acc;
     }
   }
-  red[threadIdx.x] = l;
-  __syncthreads();
-  for (int s = blockDim.x / 2; s > 0; s >>= 1) {
-    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    s_stat[0] = red[0];
-    s_stat[1] = M;
-  }
-  __syncthreads();
-  const float L = s_stat[0];
-  for (int i = threadIdx.x; i < d; i += blockDim.x) {
-    float o = 0.0f;
-    if (L > 0.0f) {
-      for (int k = 0; k < d; ++k) o = fmaf(A.pi[(int64_t)k * d + i], ox[k], o);
-      o = (o + oh[i]) / L;
+  const float L = block_reduce(l, false);   // (its barriers also order the ox / oh writes)
+  // o = Pi^T o_x: output i = row i of the transposed rotation against o_x
+  {
+    const int r = threadIdx.x >> 1, h = threadIdx.x & 1;
+    for (int i0 = 0; i0 < D; i0 += kMergeThreads / 2) {
+      const int i = i0 + r;
+      const float o = gemv_row_half_f32<D>(A.pi_t + (int64_t)min(i, D - 1) * D, ox, h);
+      if (h == 0 && i < D) A.out[row * D + i] = L > 0.0f ? (o + oh[i]) / L : 0.0f;
     }
-    A.out[row * d + i] = o;
   }
-  if (threadIdx.x == 0 && A.lse) A.lse[row] = L > 0.0f ? s_stat[1] + logf(L) : kNegInf;
+  if (threadIdx.x == 0 && A.lse) A.lse[row] = L > 0.0f ? M + logf(L) : kNegInf;
 }
 
 static bool mfma_path(const Consts& c, int G) {
@@ -1392,6 +1410,9 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
   const int rows = batch * q_heads;
   hipLaunchKernelGGL(query_prep_kernel, dim3(rows), dim3(128), 0, stream, dc.pi, dc.s, c.d, c.m, q,
                      q_dt, qx, qs);
+  // the matrix-core kernel addresses a (sequence, head) run with 32-bit byte offsets
+  const bool mfma = plan.mfma && capacity < (int64_t(1) << 24) &&
+                    capacity * (int64_t)c.rec_bytes < (int64_t(1) << 31);
   const int64_t n_cold = sel_idx ? k_sel : capacity;
   const int64_t lstride = n_cold + (hot_lens ? hot_capacity : 0);
   DecodeArgs a;
@@ -1427,9 +1448,6 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
   }
   dim3 grid(plan.n_chunks, kv_heads, batch);
   ev.before(stream);
-  // the matrix-core kernel addresses a (sequence, head) run with 32-bit byte offsets
-  const bool mfma = plan.mfma && capacity < (int64_t(1) << 24) &&
-                    capacity * (int64_t)c.rec_bytes < (int64_t(1) << 31);
   if (mfma) {
     launch_mfma_scan(a, c.kb, c.m > 0, sel_idx != nullptr, logits != nullptr, grid, stream);
   } else if (plan.hpl == 4) {
@@ -1439,7 +1457,7 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
   }
   ev.after(stream);
   MergeArgs mg;
-  mg.pi = dc.pi;
+  mg.pi_t = dc.pi_t;
   mg.part = part;
   mg.q = q;
   mg.q_dt = q_dt;
@@ -1459,7 +1477,10 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
   mg.kv_heads = kv_heads;
   mg.n_chunks = plan.n_chunks;
   mg.scale = sc;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(q_heads, batch), dim3(kMergeThreads), 0, stream, mg);
+  if (c.d == 128)
+    hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(q_heads, batch), dim3(kMergeThreads), 0, stream, mg);
+  else
+    hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(q_heads, batch), dim3(kMergeThreads), 0, stream, mg);
   return hipGetLastError();
 }
 
