@@ -326,8 +326,15 @@ tq_status tq_create(const tq_config* cfg, tq_handle** out) {
   std::vector<float> pi_t((size_t)d * d);
   for (int i = 0; i < d; ++i)
     for (int j = 0; j < d; ++j) pi_t[(size_t)j * d + i] = pi[(size_t)i * d + j];
+  std::vector<float> s_pi((size_t)m * d);
+  for (int k = 0; k < m; ++k)
+    for (int j = 0; j < d; ++j) {
+      double acc = 0.0;
+      for (int i = 0; i < d; ++i) acc += (double)s[(size_t)k * d + i] * (double)pi[(size_t)i * d + j];
+      s_pi[(size_t)k * d + j] = (float)acc;
+    }
   const size_t n_pi = (size_t)d * d, n_s = (size_t)m * d;
-  const size_t total = (3 * n_pi + 2 * n_s) * sizeof(float);
+  const size_t total = (3 * n_pi + 3 * n_s) * sizeof(float);
   if (hipGetDevice(&h->device) != hipSuccess) { delete h; return fail(TQ_ERR_DEVICE, "no HIP device"); }
   if (hipMalloc(&h->dev_block, total) != hipSuccess) {
     delete h;
@@ -341,6 +348,7 @@ tq_status tq_create(const tq_config* cfg, tq_handle** out) {
   host.insert(host.end(), s.begin(), s.end());
   host.insert(host.end(), s_m.begin(), s_m.end());
   host.insert(host.end(), pi_t.begin(), pi_t.end());
+  host.insert(host.end(), s_pi.begin(), s_pi.end());
   hipError_t e = hipMemcpy(base, host.data(), total, hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     (void)hipFree(h->dev_block);
@@ -352,6 +360,7 @@ tq_status tq_create(const tq_config* cfg, tq_handle** out) {
   h->dc.s = m ? base + 2 * n_pi : nullptr;
   h->dc.s_mfma = m ? base + 2 * n_pi + n_s : nullptr;
   h->dc.pi_t = base + 2 * n_pi + 2 * n_s;
+  h->dc.s_pi = m ? base + 3 * n_pi + 2 * n_s : nullptr;
   *out = h;
   return ok();
 }

@@ -42,6 +42,7 @@ struct Consts {
 struct DevConsts {
   const float* pi;        // [d][d] row-major (x = Pi k)
   const float* pi_t;      // Pi transposed, [d][d] row-major (row k = column k of Pi)
+  const float* s_pi;      // S Pi ([m][d], float64 product rounded to float32): q_s = (S Pi) q
   const float* s;         // [m][d] row-major
   const float* pi_mfma;   // Pi in the order the compress kernel's MFMA A operand reads it
   const float* s_mfma;    // S in the same order
@@ -68,7 +69,7 @@ struct DecodePlan {
   bool sign_bytes;  // QJL LUT indexed by bytes (else nibbles)
   bool mfma;        // matrix-core scan (head_dim 128, 4 query heads per KV head)
   size_t lds_bytes;
-  size_t ws_qx, ws_qs, ws_part, ws_total;   // workspace offsets / size
+  size_t ws_qx, ws_qs, ws_part, ws_bop, ws_total;   // workspace offsets / size
 };
 
 bool plan_decode(const Consts& c, int batch, int q_heads, int kv_heads, int64_t n_max,

@@ -527,6 +527,7 @@ constexpr int kDecodeThreads = 512;
 struct DecodeArgs {
   const float* qx;
   const float* qs;
+  const uint32_t* bop;    // matrix-core kernel: per-lane query operands (mfma_prep_kernel)
   const uint8_t* records;
   const int32_t* seq_lens;
   const int32_t* sel_idx;
@@ -843,6 +844,153 @@ __device__ __forceinline__ uint32_t bf16_pair(float x) {      // hi | lo << 16
   return hi | (bf16_rn_bits(x - bf16_bits_f(hi)) << 16);
 }
 
+// Per (sequence, KV head) preparation for the matrix-core scan: q_x = Pi q and q_s = (S Pi) q
+// for the group's G query heads in one pass (float64 sums rounded once to float32; thread
+// (row o, half hf) holds half a row of Pi and of S Pi, loaded up front), then the lanes' query
+// operands: bop[group][lane][32 words] = Bc (16 words), Bq (8), column scales (3), pad.
+template <int BK, bool QJL>
+__global__ __launch_bounds__(256) void mfma_prep_kernel(const float* __restrict__ pi,
+                                                        const float* __restrict__ s_pi, const void* q,
+                                                        tq_dtype q_dt, int q_heads, int kv_heads,
+                                                        float fk, uint32_t* bop) {
+  constexpr int D = 128, G = 4, H = D / 2;
+  __shared__ double qv[G][D];
+  __shared__ __attribute__((aligned(16))) float xf[G][D], sf[G][D];
+  const int group = blockIdx.x, b = group / kv_heads, hkv = group % kv_heads;
+  const int64_t qrow0 = (int64_t)b * q_heads + (int64_t)hkv * G;
+  const int o = threadIdx.x >> 1, hf = threadIdx.x & 1;
+  float4 wp[H / 4], ws[H / 4];
+  {
+    const float4* pp = reinterpret_cast<const float4*>(pi + o * D + hf * H);
+#pragma unroll
+    for (int j = 0; j < H / 4; ++j) wp[j] = pp[j];
+    if (QJL) {
+      const float4* sp = reinterpret_cast<const float4*>(s_pi + o * D + hf * H);
+#pragma unroll
+      for (int j = 0; j < H / 4; ++j) ws[j] = sp[j];
+    }
+  }
+  for (int e = threadIdx.x; e < G * D; e += blockDim.x)
+    qv[e / D][e % D] = (double)load_elem(q, q_dt, (qrow0 + e / D) * D + e % D);
+  __syncthreads();
+  double ax[G], as[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) ax[h] = as[h] = 0.0;
+#pragma unroll
+  for (int j = 0; j < H / 4; ++j)
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const double* vv = qv[h] + hf * H + 4 * j;
+      ax[h] = fma((double)wp[j].x, vv[0], ax[h]);
+      ax[h] = fma((double)wp[j].y, vv[1], ax[h]);
+      ax[h] = fma((double)wp[j].z, vv[2], ax[h]);
+      ax[h] = fma((double)wp[j].w, vv[3], ax[h]);
+      if (QJL) {
+        as[h] = fma((double)ws[j].x, vv[0], as[h]);
+        as[h] = fma((double)ws[j].y, vv[1], as[h]);
+        as[h] = fma((double)ws[j].z, vv[2], as[h]);
+        as[h] = fma((double)ws[j].w, vv[3], as[h]);
+      }
+    }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    ax[h] += __shfl_xor(ax[h], 1);
+    as[h] += __shfl_xor(as[h], 1);
+  }
+  if (hf == 0)
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      xf[h][o] = (float)ax[h];
+      sf[h][o] = (float)as[h];
+    }
+  __syncthreads();
+  // per head: fixed-point scales (three int8 limbs against the largest |entry|) and the sum of
+  // the sketch's fixed-point values
+  __shared__ float s_fq[G], s_fs[G];
+  __shared__ int s_ssum[G];
+  {
+    const int h = threadIdx.x >> 6, l = threadIdx.x & 63;   // wave h reduces head h
+    float mx = fmaxf(fabsf(xf[h][l]), fabsf(xf[h][l + 64]));
+    float ms = QJL ? fmaxf(fabsf(sf[h][l]), fabsf(sf[h][l + 64])) : 0.0f;
+#pragma unroll
+    for (int msk = 32; msk > 0; msk >>= 1) {
+      mx = fmaxf(mx, __shfl_xor(mx, msk));
+      ms = fmaxf(ms, __shfl_xor(ms, msk));
+    }
+    constexpr float kFix3 = 8323072.0f;   // 127 * 65536: the three-limb range
+    const float fq = mx > 0.0f ? kFix3 / mx : 1.0f, fs = ms > 0.0f ? kFix3 / ms : 1.0f;
+    int ss = QJL ? (int)rintf(sf[h][l] * fs) + (int)rintf(sf[h][l + 64] * fs) : 0;
+#pragma unroll
+    for (int msk = 32; msk > 0; msk >>= 1) ss += __shfl_xor(ss, msk);
+    if (l == 0) {
+      s_fq[h] = fq;
+      s_fs[h] = fs;
+      s_ssum[h] = ss;
+    }
+  }
+  __syncthreads();
+  // operand words: scan lane L = (column n = L % 16, K slice kg = L / 16), head n / 4, part n % 4.
+  //  code word (j, w): byte k <-> coordinate 32 kg + sel_coord(2j + (w & 1), k); w < 2: high
+  //    level limb slots, w >= 2: low limb slots.  part 0 (weight 2^24): hi x q2; part 1 (2^16):
+  //    hi x q1 + lo x q2; part 2 (2^8): hi x q0 + lo x q1; part 3: zero.
+  //  QJL word (j, w): byte k <-> sketch coordinate 32 kg + 8k + 4j + w; part p < 3 holds limb
+  //    2 - p of the sketch (weight 2^(8 (2 - p))); part 3: zero.
+  // one role per wave (no divergence): waves 0 and 1 write code words 0..7 and 8..15, wave 2
+  // the QJL words, wave 3 the column scales, each for scan lane L = its own lane
+  const int L = threadIdx.x & 63, role = threadIdx.x >> 6;
+  const int n = L & 15, kg = L >> 4, hB = n >> 2, part = n & 3;
+  const float fq = s_fq[hB], fs = s_fs[hB];
+  u32x4* gdst = reinterpret_cast<u32x4*>(bop + ((int64_t)group * 64 + L) * 32);
+  if (role < 2) {
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int j = 2 * role + jj;
+      u32x4 words;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int coord = sel_coord<BK>(2 * j + (w & 1), k);
+          int l2, l1, l0;
+          int8_limbs3((int)rintf(xf[hB][32 * kg + coord] * fq), l2, l1, l0);
+          const bool hi_slot = w < 2;
+          const int v = part == 0 ? (hi_slot ? l2 : 0) : part == 1 ? (hi_slot ? l1 : l2)
+                      : part == 2 ? (hi_slot ? l0 : l1) : 0;
+          word |= (uint32_t)(v & 0xFF) << (8 * k);
+        }
+        words[w] = word;
+      }
+      gdst[j] = words;
+    }
+  } else if (role == 2) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      u32x4 words;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t word = 0;
+        if (QJL)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            int l2, l1, l0;
+            int8_limbs3((int)rintf(sf[hB][32 * kg + 8 * k + 4 * j + w] * fs), l2, l1, l0);
+            const int v = part == 0 ? l2 : part == 1 ? l1 : part == 2 ? l0 : 0;
+            word |= (uint32_t)(v & 0xFF) << (8 * k);
+          }
+        words[w] = word;
+      }
+      gdst[4 + j] = words;
+    }
+  } else {
+    const float wpart = part == 0 ? 16777216.0f : part == 1 ? 65536.0f : part == 2 ? 256.0f : 0.0f;
+    const float ck = wpart / (fq * fk);
+    const float cq = QJL ? 2.0f * (wpart / 256.0f) / fs : 0.0f;
+    const float oq = (QJL && part == 0) ? -(float)s_ssum[hB] / fs : 0.0f;
+    gdst[6] = u32x4{__float_as_uint(ck), __float_as_uint(cq), __float_as_uint(oq), 0u};
+  }
+}
+
 constexpr int kMfmaThreads = 256;
 
 template <int BK, bool QJL, bool GATHER, bool LOGITS>
@@ -882,83 +1030,22 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
     tl[c >> 2] |= (uint32_t)(lo & 0xFF) << (8 * (c & 3));
   }
 
-  // query operands (B): lane column n = (head n / 4, part n % 4), K slice kg holding the
-  // lane's coordinates 32 kg .. 32 kg + 31 (sketch coordinates likewise).
-  //  code MFMA j: elements 0..7 <-> high level limb of selectors 2j, 2j+1, 8..15 <-> low limb;
-  //    part 0 (weight 2^24): hi x q2; part 1 (2^16): hi x q1 + lo x q2; part 2 (2^8):
-  //    hi x q0 + lo x q1; part 3 unused.
-  //  QJL MFMA j: element 4w + k <-> sketch coordinate 32 kg + 8k + 4j + w; part p < 3 holds
-  //    sketch limb 2 - p (weight 2^(8 (2 - p))); part 3 unused.
+  // query operands (B) and column scales, prepared per (sequence, KV head) by mfma_prep_kernel
   const int n = lane & 15, kg = lane >> 4;
   i32x4 Bc[4], Bq[2];
   float colscale_k, colscale_q, coloff_q;
   {
-    const int hB = n >> 2, part = n & 3;
-    const f32x4* qx4 = reinterpret_cast<const f32x4*>(A.qx + (qrow0 + hB) * D + 32 * kg);
-    const f32x4* qs4 = reinterpret_cast<const f32x4*>(A.qs + (qrow0 + hB) * (QJL ? A.m : 0) + (QJL ? 32 * kg : 0));
-    f32x4 xv[8], sv[8];
+    const u32x4* bp = reinterpret_cast<const u32x4*>(A.bop + (((int64_t)b * A.kv_heads + hkv) * 64 + lane) * 32);
+    u32x4 w[7];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      xv[i] = qx4[i];
-      sv[i] = QJL ? qs4[i] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-    float mx = 0.0f, ms = 0.0f;
+    for (int i = 0; i < 7; ++i) w[i] = bp[i];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int j = 0; j < 4; ++j) Bc[j] = __builtin_bit_cast(i32x4, w[j]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        mx = fmaxf(mx, fabsf(xv[i][e]));
-        ms = fmaxf(ms, fabsf(sv[i][e]));
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    ms = fmaxf(ms, __shfl_xor(ms, 16));
-    ms = fmaxf(ms, __shfl_xor(ms, 32));
-    constexpr float kFix3 = 8323072.0f;   // 127 * 65536: the three-limb range
-    const float fq = mx > 0.0f ? kFix3 / mx : 1.0f, fs = ms > 0.0f ? kFix3 / ms : 1.0f;
-    int ssum = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ssum += (int)rintf(sv[i][e] * fs);
-    ssum += __shfl_xor(ssum, 16);
-    ssum += __shfl_xor(ssum, 32);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int coord = sel_coord<BK>(2 * j + (w & 1), k);
-          int l2, l1, l0;
-          int8_limbs3((int)rintf(xv[coord >> 2][coord & 3] * fq), l2, l1, l0);
-          const bool hi_slot = w < 2;
-          const int v = part == 0 ? (hi_slot ? l2 : 0) : part == 1 ? (hi_slot ? l1 : l2)
-                      : part == 2 ? (hi_slot ? l0 : l1) : 0;
-          word |= (uint32_t)(v & 0xFF) << (8 * k);
-        }
-        Bc[j][w] = (int)word;
-      }
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int coord = 8 * k + 4 * j + w;
-          int l2, l1, l0;
-          int8_limbs3((int)rintf(sv[coord >> 2][coord & 3] * fs), l2, l1, l0);
-          const int v = part == 0 ? l2 : part == 1 ? l1 : part == 2 ? l0 : 0;
-          word |= (uint32_t)(v & 0xFF) << (8 * k);
-        }
-        Bq[j][w] = (int)word;
-      }
-    const float wpart = part == 0 ? 16777216.0f : part == 1 ? 65536.0f : part == 2 ? 256.0f : 0.0f;
-    colscale_k = wpart / (fq * fk);
-    colscale_q = QJL ? 2.0f * (wpart / 256.0f) / fs : 0.0f;
-    coloff_q = (QJL && part == 0) ? -(float)ssum / fs : 0.0f;
+    for (int j = 0; j < 2; ++j) Bq[j] = __builtin_bit_cast(i32x4, w[4 + j]);
+    colscale_k = __uint_as_float(w[6][0]);
+    colscale_q = __uint_as_float(w[6][1]);
+    coloff_q = __uint_as_float(w[6][2]);
   }
   __syncthreads();
 
@@ -1358,8 +1445,23 @@ bool plan_decode(const Consts& c, int batch, int q_heads, int kv_heads, int64_t 
   plan->ws_qx = 0;
   plan->ws_qs = align256(rows * c.d * 4);
   plan->ws_part = plan->ws_qs + align256(rows * std::max(c.m, 1) * 4);
-  plan->ws_total = plan->ws_part + align256(rows * plan->n_chunks * (c.d + 2) * 4);
+  plan->ws_bop = plan->ws_part + align256(rows * plan->n_chunks * (c.d + 2) * 4);
+  plan->ws_total = plan->ws_bop + (plan->mfma ? (size_t)std::max(batch, 1) * kv_heads * 64 * 32 * 4 : 0);
   return true;
+}
+
+static void launch_mfma_prep(const Consts& c, const DevConsts& dc, const void* q, tq_dtype q_dt,
+                             int batch, int q_heads, int kv_heads, uint32_t* bop, hipStream_t st) {
+  const dim3 grid((unsigned)(batch * kv_heads));
+  const bool qjl = c.m > 0;
+  if (c.kb == 3 && qjl)
+    hipLaunchKernelGGL((mfma_prep_kernel<3, true>), grid, dim3(256), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
+  else if (c.kb == 3)
+    hipLaunchKernelGGL((mfma_prep_kernel<3, false>), grid, dim3(256), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
+  else if (qjl)
+    hipLaunchKernelGGL((mfma_prep_kernel<2, true>), grid, dim3(256), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
+  else
+    hipLaunchKernelGGL((mfma_prep_kernel<2, false>), grid, dim3(256), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
 }
 
 template <int BK, bool QJL>
@@ -1408,16 +1510,21 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
   float* part = reinterpret_cast<float*>(ws + plan.ws_part);
   const float sc = scale > 0.0f ? scale : c.inv_sqrt_d;
   const int rows = batch * q_heads;
-  hipLaunchKernelGGL(query_prep_kernel, dim3(rows), dim3(128), 0, stream, dc.pi, dc.s, c.d, c.m, q,
-                     q_dt, qx, qs);
+  uint32_t* bop = reinterpret_cast<uint32_t*>(ws + plan.ws_bop);
   // the matrix-core kernel addresses a (sequence, head) run with 32-bit byte offsets
   const bool mfma = plan.mfma && capacity < (int64_t(1) << 24) &&
                     capacity * (int64_t)c.rec_bytes < (int64_t(1) << 31);
+  if (mfma)
+    launch_mfma_prep(c, dc, q, q_dt, batch, q_heads, kv_heads, bop, stream);
+  else
+    hipLaunchKernelGGL(query_prep_kernel, dim3(rows), dim3(128), 0, stream, dc.pi, dc.s, c.d, c.m, q,
+                       q_dt, qx, qs);
   const int64_t n_cold = sel_idx ? k_sel : capacity;
   const int64_t lstride = n_cold + (hot_lens ? hot_capacity : 0);
   DecodeArgs a;
   a.qx = qx;
   a.qs = qs;
+  a.bop = bop;
   a.records = static_cast<const uint8_t*>(records);
   a.seq_lens = seq_lens;
   a.sel_idx = sel_idx;
