@@ -1,18 +1,26 @@
 #!/usr/bin/env python3
-"""Benchmark of the compressed-KV decode path on one MI355X.
+"""Benchmark of the compressed-KV hot path on one MI355X.
 
-A step is one decode pass of the hot path over the resident compressed cache: query
-preparation (q_x = Pi q, q_s = S q_x), the split-K scan over every packed record (score
+Default workload (the configuration the metric is quoted on): the Llama-3-8B-shaped 32K-context
+decode - batch 16, 32 query heads, 8 KV heads, head_dim 128, 3-bit keys + 128-bit QJL sketch,
+4-bit values, Student-t(4) K/V in bf16.  A step is one decode pass of the hot path over the
+resident compressed cache: query preparation, the split-K scan over every packed record (score
 estimates from the codes, online softmax, rotated-domain value aggregation) and the merge
-(log-sum-exp combine, exact segment, un-rotation).  The cache is compressed once before the timed region
-(that compress is timed separately and reported beside the step).  The default workload is
-the Llama-3-8B-shaped 32K-context decode (batch 16, 32 query heads, 8 KV heads, head_dim
-128, 3-bit keys + 128-bit QJL sketch, 4-bit values, Student-t(4) K/V in bf16).
+(log-sum-exp combine, exact segment, un-rotation).  The cache is compressed once before the
+timed region; that compress is timed on its own and reported beside the step.
 
-Prints ONE JSON line.  `roofline` describes the decode scan kernel: algorithmic bytes per
-launch (140 B per token-head x token-heads) over its average duration, timed with HIP
-events recorded on the kernel's own stream around every scan launch of the timed steps.
-`cpu_baseline` times the oracle (single thread) on a bounded sample of the same workload.
+Other workloads (``--workload``), each with its own step:
+  * ``sparse_128k_top2048``: Self-Indexing top-k over the 1-bit sign index (integer LUT scores
+    of every token, radix selection of 2,048 per KV head) followed by attention over the
+    selected tokens' records (gather mode); the index and the records are built once.
+  * ``bulk_64k_scan``: the score scan of 256 queries per KV head against all 65,536 compressed
+    tokens of 8 heads (score matrix written to HBM).
+  * ``tinyllama_layer``, ``single_head_1k``: small decode steps (latency-bound).
+
+Prints ONE JSON line.  `roofline` describes the step's dominant kernel: algorithmic bytes per
+launch over its average duration, timed with HIP events the library records on the kernel's own
+stream around every launch of the timed steps.  `cpu_baseline` times the oracle (one thread) on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -29,7 +37,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "compressed_key_attention_amd", "csrc", "tq_kernels.hip")
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_scan_llama8b_decode_32k_traffic.json")
+PROFILES = os.path.join(ROOT, "profiles")
+DECODE_WORKLOADS = ["llama8b_decode_32k", "tinyllama_layer", "single_head_1k"]
 
 
 class HipEvents:
@@ -61,11 +70,11 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_profile(workload: str, launches_bytes: float):
-    """HBM bytes per scan launch from the committed rocprofv3 counter summary, if it was
+def traffic_from_profile(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, if it was
     taken from the current kernel source (else null)."""
     try:
-        with open(PMC_SUMMARY) as f:
+        with open(os.path.join(PROFILES, f"{kernel}_{workload}_traffic.json")) as f:
             s = json.load(f)
     except (OSError, ValueError):
         return None
@@ -74,7 +83,7 @@ def traffic_from_profile(workload: str, launches_bytes: float):
     return s.get("hbm_bytes_per_launch")
 
 
-def scan_kernel_name(w) -> str:
+def decode_kernel_name(w) -> str:
     """The scan kernel the library picks for this shape (matrix-core path for head_dim 128,
     4 query heads per KV head, 2/3-bit keys, 4-bit values, m in {0, 128})."""
     mfma = (w.head_dim == 128 and w.q_heads == 4 * w.kv_heads and w.value_bits == 4
@@ -82,26 +91,276 @@ def scan_kernel_name(w) -> str:
     return "decode_mfma_kernel" if mfma else "decode_scan_kernel"
 
 
-def cpu_baseline(w, h, q, records, budget_s: float = 12.0):
-    """The oracle, as it is, on whole sequences of the same cache until ~budget_s of CPU work."""
-    import numpy as np
+def record_payload_bytes(w) -> int:
+    return w.head_dim * w.key_bits // 8 + w.qjl_dim // 8 + w.head_dim * w.value_bits // 8 + 12
+
+
+def time_steps(ev, tq, step, steps, warmup):
+    """Runs warmup + steps; events around the dominant kernel of every timed step."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    pairs = [(ev.create(), ev.create()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in pairs:
+        tq.set_profile_events(a, b)
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = sum(ev.elapsed_ms(a, b) for a, b in pairs) / len(pairs)
+    for a, b in pairs:
+        ev.destroy(a)
+        ev.destroy(b)
+    return wall * 1000.0 / steps, kernel_ms
+
+
+def roofline(kernel, workload, alg_bytes, kernel_ms, extra=None):
+    achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
+    r = {"bound": "hbm", "kernel": kernel, "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+         "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_from_profile(kernel, workload),
+         "algorithmic_bytes_per_launch": alg_bytes, "kernel_ms": kernel_ms}
+    if extra:
+        r.update(extra)
+    return r
+
+
+def compress_once(ev, tq, h, K, V, records):
+    """One-time compress of the whole cache (warm-up call first), timed on its own."""
+    import torch
+    h.compress_kv(K, V, records)
+    torch.cuda.synchronize()
+    c0, c1 = ev.create(), ev.create()
+    tq.set_profile_events(c0, c1)
+    h.compress_kv(K, V, records)
+    torch.cuda.synchronize()
+    ms = ev.elapsed_ms(c0, c1)
+    ev.destroy(c0)
+    ev.destroy(c1)
+    return ms
+
+
+def oracle_budget_loop(units, fetch, run_one, budget_s):
+    """For units in order: `fetch(u)` copies the unit's inputs to host memory (untimed), then
+    `run_one(*inputs)` is timed; stops after ~budget_s of CPU time.  Returns (done, seconds)."""
     from threadpoolctl import threadpool_limits
-    from oracle import tq_oracle as O
-    codec = O.Codec(w.head_dim, w.key_bits, w.qjl_dim, w.value_bits, h.rotation_seed, h.qjl_seed)
-    qn = q.float().cpu().numpy()
     done, elapsed = 0, 0.0
     with threadpool_limits(limits=1):
-        for b in range(w.batch):
-            rec = records[b:b + 1].cpu().numpy()
+        for u in units:
+            inputs = fetch(u)
             t0 = time.perf_counter()
-            O.decode_attention(codec, qn[b:b + 1], rec, [w.tokens])
+            run_one(*inputs)
             elapsed += time.perf_counter() - t0
             done += 1
             if elapsed >= budget_s:
                 break
-    return {"value": done * w.tokens / elapsed, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {w.batch} sequences ({done * w.tokens} tokens x {w.q_heads} query heads), "
+    return done, elapsed
+
+
+def base_line(args, w, ms_per_step, tokens_per_step):
+    return {
+        "metric": "compressed KV tokens attended/sec per GPU + % of HBM roofline (GB/s)",
+        "value": tokens_per_step / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
+                   "head_dim": w.head_dim, "context": w.tokens, "key_bits": w.key_bits,
+                   "qjl_dim": w.qjl_dim, "value_bits": w.value_bits, "kv_dtype": w.kv_dtype,
+                   "q_dtype": w.q_dtype, "seed": w.seed},
+    }
+
+
+# ---------------------------------------------------------------------------------------------
+def run_decode(args, tq, W, ev):
+    import torch
+    w = W.WORKLOADS[args.workload]
+    dev = "cuda"
+    h = tq.Handle(w.head_dim, w.key_bits, w.qjl_dim, w.value_bits, w.seed * 3 + 1, w.seed * 3 + 2)
+    K, V = W.make_kv(w, dev)
+    q = W.make_queries(w, dev)
+    records = h.new_cache(w.batch, w.kv_heads, w.tokens, dev)
+    compress_ms = compress_once(ev, tq, h, K, V, records)
+    del K, V
+    token_heads = w.batch * w.kv_heads * w.tokens
+    flops_th = 2 * (2 * w.head_dim * w.head_dim + w.qjl_dim * w.head_dim)
+    hot = {}
+    if w.hot_tokens:
+        hk, hv = W.make_hot(w, dev)
+        hot = dict(hot_k=hk, hot_v=hv,
+                   hot_lens=torch.full((w.batch,), w.hot_tokens, dtype=torch.int32, device=dev))
+    seq_lens = torch.full((w.batch,), w.tokens, dtype=torch.int32, device=dev)
+    out = torch.empty((w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    ws = torch.empty(h.decode_workspace_size(w.batch, w.q_heads, w.kv_heads, w.tokens), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        h.decode_attention(q, records, seq_lens, out=out, workspace=ws, **hot)
+
+    ms_per_step, scan_ms = time_steps(ev, tq, step, args.steps, args.warmup)
+    alg_bytes = record_payload_bytes(w) * token_heads
+    line = base_line(args, w, ms_per_step, w.batch * (w.tokens + w.hot_tokens))
+    line["config"].update({"hot_tokens": w.hot_tokens, "record_bytes": h.record_bytes})
+    line["roofline"] = roofline(decode_kernel_name(w), w.name, alg_bytes, scan_ms, {"scan_ms": scan_ms})
+    line["token_heads_per_s"] = token_heads / (ms_per_step * 1e-3)
+    line["compress"] = {"ms": compress_ms, "token_heads_per_s": token_heads / (compress_ms * 1e-3),
+                        "mfma_f64_tflops": flops_th * token_heads / (compress_ms * 1e-3) / 1e12,
+                        "mfma_f64_peak_tflops": 78.6}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_decode(w, h, q, records, hot)
+    return line
+
+
+def cpu_baseline_decode(w, h, q, records, hot, budget_s: float = 12.0):
+    """The oracle, as it is, on whole sequences of the same cache until ~budget_s of CPU work."""
+    from oracle import tq_oracle as O
+    codec = O.Codec(w.head_dim, w.key_bits, w.qjl_dim, w.value_bits, w.seed * 3 + 1, w.seed * 3 + 2)
+    qn = q.float().cpu().numpy()
+    hk = hot["hot_k"].float().cpu().numpy() if hot else None
+    hv = hot["hot_v"].float().cpu().numpy() if hot else None
+
+    def fetch(b):
+        return b, records[b:b + 1].cpu().numpy()
+
+    def one(b, rec):
+        if hot:
+            O.decode_attention(codec, qn[b:b + 1], rec, [w.tokens], hk[b:b + 1], hv[b:b + 1], [w.hot_tokens])
+        else:
+            O.decode_attention(codec, qn[b:b + 1], rec, [w.tokens])
+
+    done, elapsed = oracle_budget_loop(range(w.batch), fetch, one, budget_s)
+    tokens = done * (w.tokens + w.hot_tokens)
+    return {"value": tokens / elapsed, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {w.batch} sequences ({tokens} tokens x {w.q_heads} query heads), "
                       f"numpy float64 oracle, BLAS limited to 1 thread, {elapsed:.1f} s"}
+
+
+# ---------------------------------------------------------------------------------------------
+def run_sparse(args, tq, W, ev):
+    import torch
+    w = W.WORKLOADS["sparse_128k_top2048"]
+    dev = "cuda"
+    h = tq.Handle(w.head_dim, w.key_bits, w.qjl_dim, w.value_bits, w.seed * 3 + 1, w.seed * 3 + 2)
+    K, V = W.make_kv(w, dev)
+    B, T, H, d = K.shape
+    index = torch.empty((B, H, T, d // 8), dtype=torch.uint8, device=dev)
+    book = torch.empty((B, H, d // 4, 16, 4), dtype=torch.float32, device=dev)
+    h.build_sign_index(K, index, book)
+    records = h.new_cache(B, H, T, dev)
+    compress_ms = compress_once(ev, tq, h, K, V, records)
+    del K, V
+    q = W.make_queries(w, dev)
+    seq_lens = torch.full((B,), T, dtype=torch.int32, device=dev)
+    sel = torch.empty((B, H, w.top_k), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, H), dtype=torch.int32, device=dev)
+    sws = torch.empty(h.select_workspace_size(B, H, T), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, w.q_heads, d), dtype=torch.float32, device=dev)
+    dws = torch.empty(h.decode_workspace_size(B, w.q_heads, H, T, k_sel=w.top_k), dtype=torch.uint8,
+                      device=dev)
+
+    def step():
+        h.select_topk(q, index, book, seq_lens, w.top_k, out_idx=sel, out_count=cnt, workspace=sws)
+        h.decode_attention(q, records, seq_lens, sel_idx=sel, out=out, workspace=dws)
+
+    ms_per_step, score_ms = time_steps(ev, tq, step, args.steps, args.warmup)
+    token_heads = B * H * T
+    alg_bytes = token_heads * (d // 8)            # 1-bit sign index: d/8 bytes per token-head
+    line = base_line(args, w, ms_per_step, B * T)
+    line["metric"] = "tokens scored per second (sign-index top-k + sparse attention) + % of HBM roofline"
+    line["config"].update({"top_k": w.top_k, "index_bytes_per_token_head": d // 8})
+    line["roofline"] = roofline("select_score_kernel", w.name, alg_bytes, score_ms)
+    line["tokens_attended_per_s"] = B * H * w.top_k / (ms_per_step * 1e-3)
+    line["compress"] = {"ms": compress_ms}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_sparse(w, q, index, book, records)
+    return line
+
+
+def cpu_baseline_sparse(w, q, index, book, records, budget_s: float = 12.0):
+    from oracle import tq_oracle as O
+    codec = O.Codec(w.head_dim, w.key_bits, w.qjl_dim, w.value_bits, w.seed * 3 + 1, w.seed * 3 + 2)
+    qn = q.float().cpu().numpy()
+    T = w.tokens
+    G = w.q_heads // w.kv_heads
+    units = [(b, hh) for b in range(w.batch) for hh in range(w.kv_heads)]
+
+    def fetch(u):
+        b, hh = u
+        return (qn[b:b + 1, hh * G:(hh + 1) * G], index[b:b + 1, hh:hh + 1].cpu().numpy(),
+                book[b:b + 1, hh:hh + 1].cpu().numpy(), records[b:b + 1, hh:hh + 1].cpu().numpy())
+
+    def one(qh, gi, gb, rec):
+        ri, _, _ = O.select_topk(codec, qh, gi, gb, [T], w.top_k)
+        O.decode_attention(codec, qh, rec, [T], sel_idx=ri)
+
+    done, elapsed = oracle_budget_loop(units, fetch, one, budget_s)
+    # units are (sequence, KV head) pairs: done * T token-heads = done * T / H tokens of the workload
+    return {"value": done * T / w.kv_heads / elapsed, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {len(units)} (sequence, KV head) units ({done * T} token-heads scored, "
+                      f"top-{w.top_k} attended), numpy float64 oracle, 1 thread, {elapsed:.1f} s"}
+
+
+# ---------------------------------------------------------------------------------------------
+def run_bulk_scan(args, tq, W, ev):
+    import torch
+    w = W.WORKLOADS["bulk_64k_scan"]
+    dev = "cuda"
+    h = tq.Handle(w.head_dim, w.key_bits, w.qjl_dim, w.value_bits, w.seed * 3 + 1, w.seed * 3 + 2)
+    K, V = W.make_kv(w, dev)
+    B, T, H, d = K.shape
+    records = h.new_cache(B, H, T, dev)
+    compress_ms = compress_once(ev, tq, h, K, V, records)
+    del K, V
+    q = W.make_queries(w, dev)                     # [B, H, n_queries, d]
+    nq = w.scan_queries
+    scores = torch.empty((B, H, nq, T), dtype=torch.float32, device=dev)
+    ws = torch.empty(h.scan_workspace_size(B, H, nq), dtype=torch.uint8, device=dev)
+
+    def step():
+        h.score_scan(q, records, T, scores=scores, workspace=ws)
+
+    ms_per_step, scan_ms = time_steps(ev, tq, step, args.steps, args.warmup)
+    key_bytes = d * w.key_bits // 8 + w.qjl_dim // 8 + 8      # codes + sketch + r_k, rho
+    alg_bytes = B * H * T * key_bytes + B * H * nq * T * 4     # key records read + scores written
+    line = base_line(args, w, ms_per_step, B * T)
+    line["metric"] = "compressed tokens scanned per second (256 queries per KV head) + % of HBM roofline"
+    line["config"].update({"scan_queries": nq})
+    line["roofline"] = roofline("scan_kernel", w.name, alg_bytes, scan_ms)
+    line["scores_per_s"] = B * H * nq * T / (ms_per_step * 1e-3)
+    line["compress"] = {"ms": compress_ms, "token_heads_per_s": B * H * T / (compress_ms * 1e-3)}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_scan(w, q, records)
+    return line
+
+
+def cpu_baseline_scan(w, q, records, budget_s: float = 12.0):
+    from oracle import tq_oracle as O
+    codec = O.Codec(w.head_dim, w.key_bits, w.qjl_dim, w.value_bits, w.seed * 3 + 1, w.seed * 3 + 2)
+    qn = q.float().cpu().numpy()
+    T = w.tokens
+    chunk = 4096
+    units = [(hh, t0) for hh in range(w.kv_heads) for t0 in range(0, T, chunk)]
+
+    def fetch(u):
+        hh, t0 = u
+        return qn[0:1, hh:hh + 1], records[0:1, hh:hh + 1, t0:t0 + chunk].cpu().numpy()
+
+    def one(qh, rec):
+        O.score_scan(codec, qh, rec, chunk)
+
+    done, elapsed = oracle_budget_loop(units, fetch, one, budget_s)
+    return {"value": done * chunk / w.kv_heads / elapsed, "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{done} blocks of {chunk} tokens x {w.scan_queries} queries of one KV head, "
+                      f"numpy float64 oracle, 1 thread, {elapsed:.1f} s"}
 
 
 def main():
@@ -110,7 +369,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b_decode_32k",
-                    choices=["llama8b_decode_32k", "tinyllama_layer", "single_head_1k"])
+                    choices=DECODE_WORKLOADS + ["sparse_128k_top2048", "bulk_64k_scan"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 device-to-device copies of 1 GiB (HBM counter calibration)")
@@ -133,90 +392,14 @@ def main():
     import compressed_key_attention_amd as tq
     from compressed_key_attention_amd import workloads as W
 
-    w = W.WORKLOADS[args.workload]
-    dev = "cuda"
     torch.cuda.set_device(0)
-    h = tq.Handle(w.head_dim, w.key_bits, w.qjl_dim, w.value_bits, w.seed * 3 + 1, w.seed * 3 + 2)
-    K, V = W.make_kv(w, dev)
-    q = W.make_queries(w, dev)
-    records = h.new_cache(w.batch, w.kv_heads, w.tokens, dev)
     ev = HipEvents()
-
-    # ---- one-time compress of the whole cache (timed on its own) ----
-    h.compress_kv(K, V, records)                 # warm-up (module load, LDS attribute)
-    torch.cuda.synchronize()
-    c0, c1 = ev.create(), ev.create()
-    tq.set_profile_events(c0, c1)
-    h.compress_kv(K, V, records)
-    torch.cuda.synchronize()
-    compress_ms = ev.elapsed_ms(c0, c1)
-    del K, V
-    token_heads = w.batch * w.kv_heads * w.tokens
-    flops_th = 2 * (2 * w.head_dim * w.head_dim + w.qjl_dim * w.head_dim)
-
-    hot = {}
-    if w.hot_tokens:
-        hk, hv = W.make_hot(w, dev)
-        hot = dict(hot_k=hk, hot_v=hv,
-                   hot_lens=torch.full((w.batch,), w.hot_tokens, dtype=torch.int32, device=dev))
-    seq_lens = torch.full((w.batch,), w.tokens, dtype=torch.int32, device=dev)
-    out = torch.empty((w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device=dev)
-    ws = torch.empty(h.decode_workspace_size(w.batch, w.q_heads, w.kv_heads, w.tokens), dtype=torch.uint8,
-                     device=dev)
-
-    def step():
-        h.decode_attention(q, records, seq_lens, out=out, workspace=ws, **hot)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for a, b in pairs:
-        tq.set_profile_events(a, b)
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    scan_ms = sum(ev.elapsed_ms(a, b) for a, b in pairs) / len(pairs)
-    ms_per_step = wall * 1000.0 / args.steps
-
-    tokens_per_step = w.batch * (w.tokens + w.hot_tokens)
-    rec_alg = w.head_dim * w.key_bits // 8 + w.qjl_dim // 8 + w.head_dim * w.value_bits // 8 + 12
-    alg_bytes = rec_alg * token_heads
-    achieved = alg_bytes / (scan_ms * 1e-3) / 1e9
-    line = {
-        "metric": "compressed KV tokens attended/sec per GPU + % of HBM roofline (GB/s)",
-        "value": tokens_per_step / (ms_per_step * 1e-3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
-                   "head_dim": w.head_dim, "context": w.tokens, "hot_tokens": w.hot_tokens,
-                   "key_bits": w.key_bits, "qjl_dim": w.qjl_dim, "value_bits": w.value_bits,
-                   "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype, "record_bytes": h.record_bytes,
-                   "seed": w.seed},
-        "roofline": {"bound": "hbm", "kernel": scan_kernel_name(w), "achieved": achieved,
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": traffic_from_profile(w.name, alg_bytes),
-                     "algorithmic_bytes_per_launch": alg_bytes, "scan_ms": scan_ms},
-        "token_heads_per_s": token_heads / (ms_per_step * 1e-3),
-        "compress": {"ms": compress_ms, "token_heads_per_s": token_heads / (compress_ms * 1e-3),
-                     "mfma_f64_tflops": flops_th * token_heads / (compress_ms * 1e-3) / 1e12,
-                     "mfma_f64_peak_tflops": 78.6},
-    }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, h, q, records)
-    for a, b in pairs:
-        ev.destroy(a)
-        ev.destroy(b)
+    if args.workload in DECODE_WORKLOADS:
+        line = run_decode(args, tq, W, ev)
+    elif args.workload == "sparse_128k_top2048":
+        line = run_sparse(args, tq, W, ev)
+    else:
+        line = run_bulk_scan(args, tq, W, ev)
     print(json.dumps(line), flush=True)
 
 

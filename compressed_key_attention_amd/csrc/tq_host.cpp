@@ -469,6 +469,8 @@ tq_status tq_decode_attention(const tq_handle* h, const void* q, tq_dtype q_dt, 
     if (!elem_size(hot_dt, &hs)) return fail(TQ_ERR_INVALID_ARGUMENT, "unknown hot dtype");
     if (hot_capacity <= 0 || !hot_k || !hot_v)
       return fail(TQ_ERR_INVALID_ARGUMENT, "exact segment needs hot_k, hot_v and hot_capacity > 0");
+    if (!aligned(hot_k, hs * 8) || !aligned(hot_v, hs * 8))
+      return fail(TQ_ERR_INVALID_ARGUMENT, "hot_k and hot_v must be aligned to 8 elements");
   }
   tq::DecodePlan plan;
   if (!tq::plan_decode(h->c, batch, q_heads, kv_heads, sel_idx ? k_sel : capacity, &plan))
@@ -532,6 +534,7 @@ tq_status tq_select_topk(const tq_handle* h, const void* q, tq_dtype q_dt, int32
   if (batch < 0 || q_heads <= 0 || kv_heads <= 0 || q_heads % kv_heads || capacity < 0 || k < 0)
     return fail(TQ_ERR_INVALID_ARGUMENT, "bad select shape");
   if (q_heads / kv_heads > 16) return fail(TQ_ERR_UNSUPPORTED, "group size above 16");
+  if (capacity > (int64_t(1) << 26)) return fail(TQ_ERR_UNSUPPORTED, "select capacity above 2^26 tokens");
   if (batch == 0) return ok();
   if (!q || !seq_lens || !out_count || (k > 0 && !out_idx) || (capacity > 0 && (!index || !codebook)))
     return fail(TQ_ERR_INVALID_ARGUMENT, "NULL input or output");

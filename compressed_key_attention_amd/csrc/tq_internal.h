@@ -96,7 +96,8 @@ hipError_t launch_sign_index(const Consts& c, const IndexPlan& plan, const void*
                              void* workspace, hipStream_t stream);
 
 struct SelectPlan {
-  size_t ws_lut, ws_scores, ws_total;
+  int n_chunks;                 // 4096-token chunks of the capacity
+  size_t ws_lut, ws_scores, ws_hist, ws_cand, ws_chunk_cand, ws_chunk_above, ws_chunk_off, ws_params, ws_total;
 };
 SelectPlan plan_select(const Consts& c, int batch, int heads, int64_t capacity);
 hipError_t launch_select(const Consts& c, const SelectPlan& plan, const void* q, tq_dtype q_dt,

@@ -564,42 +564,57 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_scan_kernel(DecodeArgs 
   float* gam_v = lut_s + NHG * sgrp * sent * HPL;               // [16]
 
   const int64_t qrow0 = ((int64_t)b * A.q_heads + (int64_t)hkv * G);  // first query head row
-  // ---- LUT build ----
+  // ---- LUT build: one thread per table row (head group, table, head), whose one or two query
+  // coordinates are loaded once; the row's entries are then written from registers ----
   {
     const float* qx = A.qx + qrow0 * d;
-    const int nk = NHG * nkt * kEnt * HPL;
-    for (int e = threadIdx.x; e < nk; e += blockDim.x) {
-      const int j = e % HPL;
-      const int ent = (e / HPL) % kEnt;
-      const int tbl = (e / HPL / kEnt) % nkt;
-      const int hg = e / HPL / kEnt / nkt;
+    const int nrow_k = NHG * nkt * HPL;
+    for (int r = threadIdx.x; r < nrow_k; r += blockDim.x) {
+      const int j = r % HPL, tbl = (r / HPL) % nkt, hg = r / HPL / nkt;
       const float* qh = qx + (int64_t)(hg * HPL + j) * d;
-      float val;
+      float* dst = lut_k + (int64_t)(hg * nkt + tbl) * kEnt * HPL + j;
       if (kPairs) {
         // pair p of a 32-coordinate group: 2-bit codes (2p, 2p+1), adjacent in the bitstream;
         // 3-bit codes (8 (p / 4) + p % 4, that + 4), one 6-bit byte field of the group layout
-        const int c0 = ent & ((1 << BK) - 1), c1 = ent >> BK;
         const int pp = tbl & 15, g32 = 32 * (tbl >> 4);
         const int i0 = BK == 3 ? g32 + 8 * (pp >> 2) + (pp & 3) : 2 * tbl;
         const int i1 = BK == 3 ? i0 + 4 : 2 * tbl + 1;
-        val = fmaf(qh[i1], A.key_levels[c1], qh[i0] * A.key_levels[c0]);
+        const float q0 = qh[i0], q1 = qh[i1];
+#pragma unroll
+        for (int ent = 0; ent < kEnt; ++ent) {
+          const int c0 = ent & ((1 << BK) - 1), c1 = ent >> BK;
+          dst[ent * HPL] = fmaf(q1, A.key_levels[c1], q0 * A.key_levels[c0]);
+        }
       } else {
-        val = qh[tbl] * A.key_levels[ent];
+        const float q0 = qh[tbl];
+#pragma unroll
+        for (int ent = 0; ent < kEnt; ++ent) dst[ent * HPL] = q0 * A.key_levels[ent];
       }
-      lut_k[e] = val;
     }
+    // sign tables: one thread per (head group, table, head, 16 consecutive entries)
     const float* qs = A.qs + qrow0 * A.m;
-    const int ns = NHG * sgrp * sent * HPL;
     const int per = A.sign_bytes ? 8 : 4;
-    for (int e = threadIdx.x; e < ns; e += blockDim.x) {
-      const int j = e % HPL;
-      const int ent = (e / HPL) % sent;
-      const int grp = (e / HPL / sent) % sgrp;
-      const int hg = e / HPL / sent / sgrp;
+    const int nsub = sent / 16;
+    const int nrow_s = NHG * sgrp * HPL * nsub;
+    for (int r = threadIdx.x; r < nrow_s; r += blockDim.x) {
+      const int sub = r % nsub, j = (r / nsub) % HPL, grp = (r / nsub / HPL) % sgrp, hg = r / nsub / HPL / sgrp;
       const float* qh = qs + (int64_t)(hg * HPL + j) * A.m + grp * per;
-      float val = 0.0f;
-      for (int k = 0; k < per; ++k) val += ((ent >> k) & 1) ? qh[k] : -qh[k];
-      lut_s[e] = val;
+      float qv8[8];
+#pragma unroll
+      for (int kq = 0; kq < 8; ++kq) {
+        qv8[kq] = 0.0f;
+        if (kq < per) qv8[kq] = qh[kq];
+      }
+      float* dst = lut_s + ((int64_t)(hg * sgrp + grp) * sent + 16 * sub) * HPL + j;
+#pragma unroll
+      for (int e16 = 0; e16 < 16; ++e16) {
+        const int ent = 16 * sub + e16;
+        float val = 0.0f;
+#pragma unroll
+        for (int kq = 0; kq < 8; ++kq)
+          if (kq < per) val += ((ent >> kq) & 1) ? qv8[kq] : -qv8[kq];
+        dst[e16 * HPL] = val;
+      }
     }
     if (threadIdx.x < kMaxLevels) gam_v[threadIdx.x] = A.val_levels[threadIdx.x];
   }
@@ -736,7 +751,21 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_scan_kernel(DecodeArgs 
     }
   }
 
-  // ---- merge all (wave, token slot) partials of the block through LDS, one head at a time --
+  // ---- combine the TPW token slots of each wave (butterfly over the slot bits of the lane),
+  // then the waves of the block through LDS, one head at a time ----
+  for (int o = LPT; o < 64; o <<= 1) {
+#pragma unroll
+    for (int j = 0; j < HPL; ++j) {
+      const float mo = __shfl_xor(mrun[j], o), lo = __shfl_xor(lsum[j], o);
+      const float mn = fmaxf(mrun[j], mo);
+      const float f = mrun[j] == kNegInf ? 0.0f : __expf(mrun[j] - mn);
+      const float fo = mo == kNegInf ? 0.0f : __expf(mo - mn);
+      lsum[j] = fmaf(lsum[j], f, lo * fo);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) acc[j][i] = fmaf(acc[j][i], f, __shfl_xor(acc[j][i], o) * fo);
+      mrun[j] = mn;
+    }
+  }
   __syncthreads();   // the LUTs are no longer needed
   const int nthr = blockDim.x;
   float* pacc = lds;                     // [nthr][33]  accumulators of head j (+1 pad)
@@ -750,10 +779,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_scan_kernel(DecodeArgs 
     pf[threadIdx.x] = mrun[j];
     pl[threadIdx.x] = lsum[j];
     __syncthreads();
-    // block maximum of head (hg, j) over the lanes that own it (cq = 0 lanes carry m and l)
+    // block maximum of head (hg, j) over the waves (slot 0 of each wave holds its combined
+    // partial; cq = 0 lanes carry m and l)
     for (int hh = threadIdx.x; hh < NHG; hh += nthr) {
       float mx = kNegInf;
-      for (int t2 = hh * LPTc; t2 < nthr; t2 += LPT) mx = fmaxf(mx, pf[t2]);
+      for (int t2 = hh * LPTc; t2 < nthr; t2 += 64) mx = fmaxf(mx, pf[t2]);
       pm[hh] = mx;
     }
     __syncthreads();
@@ -772,11 +802,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_scan_kernel(DecodeArgs 
         v = pm[hh];
       } else if (col == 1) {
         v = 0.0f;
-        for (int t2 = hh * LPTc; t2 < nthr; t2 += LPT) v += pl[t2] * pf[t2];
+        for (int t2 = hh * LPTc; t2 < nthr; t2 += 64) v += pl[t2] * pf[t2];
       } else {
         const int i = col - 2, cqo = i / 32, io = i % 32;
         v = 0.0f;
-        for (int t2 = hh * LPTc + cqo; t2 < nthr; t2 += LPT) v += pacc[t2 * 33 + io] * pf[t2];
+        for (int t2 = hh * LPTc + cqo; t2 < nthr; t2 += 64) v += pacc[t2 * 33 + io] * pf[t2];
       }
       A.part[((qrow0 + hh * HPL + j) * A.n_chunks + chunk) * stride + col] = v;
     }
@@ -1294,6 +1324,24 @@ __device__ __forceinline__ float gemv_row_half_f32(const float* __restrict__ mro
   return acc + __shfl_xor(acc, 1);
 }
 
+// Eight consecutive elements [off, off + 8) as float32 (16-byte aligned for 16-bit types,
+// 32-byte aligned for float32).
+__device__ __forceinline__ void load8(const void* base, tq_dtype dt, int64_t off, float (&v)[8]) {
+  if (dt == TQ_F32) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+    const float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = dt == TQ_BF16 ? bf16_bits_to_f32(w[i] & 0xffffu) : f16_bits_to_f32(w[i] & 0xffffu);
+      v[2 * i + 1] = dt == TQ_BF16 ? bf16_bits_to_f32(w[i] >> 16) : f16_bits_to_f32(w[i] >> 16);
+    }
+  }
+}
+
 struct MergeArgs {
   const float* pi_t;      // Pi transposed
   const float* part;
@@ -1313,16 +1361,20 @@ struct MergeArgs {
 
 constexpr int kMergeThreads = 256;
 
+constexpr int kMergeHotLds = 2048;   // exact-segment logits kept in LDS (beyond: recomputed)
+
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs A) {
-  __shared__ float qv[256];
-  __shared__ float ox[256];
-  __shared__ float oh[256];
-  __shared__ float hl[kMergeThreads];
+  // exact segment layout: LPK lanes per token, each owning 8 consecutive coordinates
+  constexpr int LPK = D / 8, TPWK = 64 / LPK, TPB = TPWK * (kMergeThreads / 64);
+  __shared__ float qv[D];
+  __shared__ float ox[D];
+  __shared__ float ohw[kMergeThreads / 64][D];
+  __shared__ float hlog[kMergeHotLds];
   __shared__ float red[kMergeThreads];
-  const int hq = blockIdx.x, b = blockIdx.y, d = A.d, hkv = hq / A.G;
+  const int hq = blockIdx.x, b = blockIdx.y, hkv = hq / A.G;
   const int64_t row = (int64_t)b * A.q_heads + hq;
-  const int stride = d + 2;
+  constexpr int stride = D + 2;
   const float* pr = A.part + row * A.n_chunks * stride;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // block-wide max / sum: wave shuffles, then one LDS word per wave
@@ -1339,24 +1391,40 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs A
     __syncthreads();
     return v;
   };
-  for (int i = threadIdx.x; i < d; i += blockDim.x) {
-    qv[i] = load_elem(A.q, A.q_dt, row * d + i);
-    oh[i] = 0.0f;
-  }
+  for (int i = threadIdx.x; i < D; i += blockDim.x) qv[i] = load_elem(A.q, A.q_dt, row * D + i);
   // global max over chunk partials and hot logits
   float mx = kNegInf;
   for (int c = threadIdx.x; c < A.n_chunks; c += blockDim.x) mx = fmaxf(mx, pr[(int64_t)c * stride]);
   const int nh = A.hot_lens ? (int)min((int64_t)A.hot_lens[b], A.hot_capacity) : 0;
-  const int64_t hbase = ((int64_t)b * A.kv_heads + hkv) * A.hot_capacity * d;
+  const int64_t hbase = ((int64_t)b * A.kv_heads + hkv) * A.hot_capacity * D;
+  const int sub = lane % LPK, slot = wave * TPWK + lane / LPK;
   __syncthreads();
-  for (int t = threadIdx.x; t < nh; t += blockDim.x) {
+  float q8[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q8[i] = qv[8 * sub + i];
+  // logit of hot token t: the LPK lanes of its slot each take 8 coordinates, then a shuffle sum
+  auto hot_logit = [&](int t) {
+    float kv[8];
+    load8(A.hot_k, A.hot_dt, hbase + (int64_t)min(t, nh - 1) * D + 8 * sub, kv);
     float dot = 0.0f;
-    for (int i = 0; i < d; ++i) dot = fmaf(qv[i], load_elem(A.hot_k, A.hot_dt, hbase + (int64_t)t * d + i), dot);
-    const float lg = A.scale * dot;
-    mx = fmaxf(mx, lg);
-    if (A.logits) A.logits[row * A.logit_stride + A.logit_hot_off + t] = lg;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dot = fmaf(q8[i], kv[i], dot);
+#pragma unroll
+    for (int msk = 1; msk < LPK; msk <<= 1) dot += __shfl_xor(dot, msk);
+    return A.scale * dot;
+  };
+  for (int t0 = 0; t0 < nh; t0 += TPB) {
+    const int t = t0 + slot;
+    const float lg = hot_logit(t);
+    if (t < nh) {
+      mx = fmaxf(mx, lg);
+      if (sub == 0) {
+        if (t < kMergeHotLds) hlog[t] = lg;
+        if (A.logits) A.logits[row * A.logit_stride + A.logit_hot_off + t] = lg;
+      }
+    }
   }
-  const float M = block_reduce(mx, true);
+  const float M = block_reduce(mx, true);   // (its barriers also order the hlog writes)
   // sum of weights and the cold rotated-domain output (loads unconditional, weight 0 for an
   // empty chunk, whose partial holds zeros)
   float l = 0.0f;
@@ -1364,7 +1432,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs A
     const float mc = pr[(int64_t)c * stride];
     l += (M != kNegInf && mc != kNegInf) ? pr[(int64_t)c * stride + 1] * __expf(mc - M) : 0.0f;
   }
-  for (int i = threadIdx.x; i < d; i += blockDim.x) {
+  for (int i = threadIdx.x; i < D; i += blockDim.x) {
     float acc = 0.0f;
     for (int c = 0; c < A.n_chunks; ++c) {
       const float mc = pr[(int64_t)c * stride];
@@ -1373,26 +1441,30 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs A
     }
     ox[i] = acc;
   }
-  // hot tokens, in tiles of blockDim: weights, then value sums
-  for (int t0 = 0; t0 < nh; t0 += blockDim.x) {
-    const int t = t0 + threadIdx.x;
-    float p = 0.0f;
-    if (t < nh) {
-      float dot = 0.0f;
-      for (int i = 0; i < d; ++i) dot = fmaf(qv[i], load_elem(A.hot_k, A.hot_dt, hbase + (int64_t)t * d + i), dot);
-      p = __expf(A.scale * dot - M);
-    }
-    l += p;
-    __syncthreads();
-    hl[threadIdx.x] = p;
-    __syncthreads();
-    const int nt = min((int)blockDim.x, nh - t0);
-    for (int i = threadIdx.x; i < d; i += blockDim.x) {
-      float acc = oh[i];
-      for (int u = 0; u < nt; ++u)
-        acc = fmaf(hl[u], load_elem(A.hot_v, A.hot_dt, hbase + (int64_t)(t0 + u) * d + i), acc);
-      oh[i] = acc;
-    }
+  // hot values: each lane accumulates its 8 coordinates over the tokens of its slot
+  float oh8[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) oh8[i] = 0.0f;
+  for (int t0 = 0; t0 < nh; t0 += TPB) {
+    const int t = t0 + slot;
+    float lg;
+    if (t0 + TPB <= kMergeHotLds) lg = hlog[min(t, kMergeHotLds - 1)];
+    else lg = hot_logit(t);
+    const float p = t < nh ? __expf(lg - M) : 0.0f;
+    if (sub == 0) l += p;
+    float vv[8];
+    load8(A.hot_v, A.hot_dt, hbase + (int64_t)min(t, nh - 1) * D + 8 * sub, vv);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) oh8[i] = fmaf(p, vv[i], oh8[i]);
+  }
+  // reduce over the token slots of the wave (lanes with the same sub), then over the waves
+#pragma unroll
+  for (int msk = LPK; msk < 64; msk <<= 1)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) oh8[i] += __shfl_xor(oh8[i], msk);
+  if (lane < LPK) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ohw[wave][8 * sub + i] = oh8[i];
   }
   const float L = block_reduce(l, false);   // (its barriers also order the ox / oh writes)
   // o = Pi^T o_x: output i = row i of the transposed rotation against o_x
@@ -1401,7 +1473,12 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs A
     for (int i0 = 0; i0 < D; i0 += kMergeThreads / 2) {
       const int i = i0 + r;
       const float o = gemv_row_half_f32<D>(A.pi_t + (int64_t)min(i, D - 1) * D, ox, h);
-      if (h == 0 && i < D) A.out[row * D + i] = L > 0.0f ? (o + oh[i]) / L : 0.0f;
+      if (h == 0 && i < D) {
+        float hsum = 0.0f;
+#pragma unroll
+        for (int w2 = 0; w2 < kMergeThreads / 64; ++w2) hsum += ohw[w2][i];
+        A.out[row * D + i] = L > 0.0f ? (o + hsum) / L : 0.0f;
+      }
     }
   }
   if (threadIdx.x == 0 && A.lse) A.lse[row] = L > 0.0f ? M + logf(L) : kNegInf;
@@ -1780,12 +1857,23 @@ hipError_t launch_sign_index(const Consts& c, const IndexPlan& plan, const void*
 // rint(LUT 2^s) (half to even) summed over the group's heads: integer scores, exact and
 // independent of summation order.  Ranking: score descending, then token index ascending.
 // =========================================================================================
+constexpr int kSelBinsTotal = 4096;       // histogram bins per unit (top 12 bits of the order key)
+
 SelectPlan plan_select(const Consts& c, int batch, int heads, int64_t capacity) {
   SelectPlan p;
   const size_t units = (size_t)std::max(batch, 1) * heads;
-  p.ws_lut = 0;                                                 // i32 [units][d/8][256]
-  p.ws_scores = align256(units * (c.d / 8) * 256 * 4);          // i32 [units][capacity]
-  p.ws_total = p.ws_scores + align256(units * std::max<int64_t>(capacity, 1) * 4);
+  const size_t cap = (size_t)std::max<int64_t>(capacity, 1);
+  p.n_chunks = (int)((cap + 4095) / 4096);
+  p.ws_lut = 0;                                                       // i32 [units][d/8][256]
+  p.ws_scores = p.ws_lut + align256(units * (c.d / 8) * 256 * 4);     // i32 [units][capacity]
+  p.ws_hist = p.ws_scores + align256(units * cap * 4);                // i32 [units][4096]
+  p.ws_cand = p.ws_hist + align256(units * kSelBinsTotal * 4);        // u32x2 [units][capacity]:
+                                                                      // chunk c's candidates at 4096 c
+  p.ws_chunk_cand = p.ws_cand + align256(units * cap * 8);            // i32 [units][n_chunks]
+  p.ws_chunk_above = p.ws_chunk_cand + align256(units * p.n_chunks * 4);
+  p.ws_chunk_off = p.ws_chunk_above + align256(units * p.n_chunks * 4);
+  p.ws_params = p.ws_chunk_off + align256(units * p.n_chunks * 4);    // 24 B [units]
+  p.ws_total = p.ws_params + align256(units * 32);
   return p;
 }
 
@@ -1800,7 +1888,7 @@ __device__ __forceinline__ double lut_entry(double q0, double q1, double q2, dou
 
 __global__ __launch_bounds__(256) void select_lut_kernel(const void* q, tq_dtype q_dt, const float* codebook,
                                                          int d, int G, int q_heads, int heads,
-                                                         int32_t* lut_out) {
+                                                         int32_t* lut_out, int32_t* hist_all) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int h = blockIdx.x, b = blockIdx.y, ng = d / 4;
   const int64_t unit = (int64_t)b * heads + h;
@@ -1808,6 +1896,7 @@ __global__ __launch_bounds__(256) void select_lut_kernel(const void* q, tq_dtype
   int32_t* comb = reinterpret_cast<int32_t*>(lut + G * ng * 16);  // [ng][16]
   __shared__ double mx[256];
   const float* cb = codebook + unit * ng * 64;
+  for (int e = threadIdx.x; e < kSelBinsTotal; e += blockDim.x) hist_all[unit * kSelBinsTotal + e] = 0;
   double m = 0.0;
   for (int e = threadIdx.x; e < G * ng * 16; e += blockDim.x) {
     const int j = e / (ng * 16), g = (e / 16) % ng, p = e % 16;
@@ -1844,136 +1933,369 @@ __global__ __launch_bounds__(256) void select_lut_kernel(const void* q, tq_dtype
   }
 }
 
-__global__ __launch_bounds__(256) void select_score_kernel(const uint8_t* index, const int32_t* lut_all,
-                                                           const int32_t* seq_lens, int d, int heads,
-                                                           int64_t capacity, int32_t* scores) {
-  __shared__ int32_t lut[16 * 256];
-  const int h = blockIdx.y, b = blockIdx.z, nb = d / 8;
-  const int64_t unit = (int64_t)b * heads + h;
-  for (int e = threadIdx.x; e < nb * 256; e += blockDim.x) lut[e] = lut_all[unit * nb * 256 + e];
-  __syncthreads();
-  const int64_t n = min((int64_t)seq_lens[b], capacity);
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= n) return;
-  const uint8_t* rec = index + (unit * capacity + t) * nb;
-  int32_t s = 0;
-  if (nb == 16) {
-    const uint4 u = *reinterpret_cast<const uint4*>(rec);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s += lut[i * 256 + ((w[i / 4] >> (8 * (i % 4))) & 255u)];
-  } else {
-    for (int i = 0; i < nb; ++i) s += lut[i * 256 + rec[i]];
-  }
-  scores[unit * capacity + t] = s;
-}
-
-constexpr int kSelThreads = 1024;
+// Selection runs in five launches (lut and exact: one workgroup per unit; score, filter and
+// write: one workgroup per 4096-token chunk of every unit):
+//   lut    (unit)          per-query byte tables; clears the unit's histogram
+//   score  (chunk, unit)   integer score of each token, stored; 4096-bin histogram of the top
+//                          12 bits of the order key, merged into the unit's histogram
+//   filter (chunk, unit)   finds the bin B holding the k-th largest score; counts the chunk's
+//                          tokens above B and writes the tokens in B to its own candidate
+//                          region (slots 4096 c onwards; LDS counter, no global atomics)
+//   exact  (unit)          radix passes over the candidates on the 64-bit key
+//                          (order key << 32 | ~index), unique per token, so that exactly k tokens
+//                          satisfy (key & M) >= P; per-chunk counts -> output offsets
+//   write  (chunk, unit)   ordered compaction of the chunk's selected tokens at its offset
+// The composite key ranks score descending then index ascending, the oracle's order.
+constexpr int kSelChunk = 4096;           // tokens per workgroup in score / filter / write
+constexpr int kSelBins = kSelBinsTotal;
+constexpr int kSelDigitShift = 20;
+constexpr int kSelExactThreads = 1024;
 
 __device__ __forceinline__ uint32_t order_key(int32_t s) { return (uint32_t)s ^ 0x80000000u; }
 
-// Block-wide exclusive prefix sum of 0/1 flags; returns the prefix, *total the block total.
-__device__ __forceinline__ int block_flag_scan(bool f, int* wsum, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  const uint64_t bal = __ballot(f);
-  const int in_wave = __popcll(bal & ((1ull << lane) - 1ull));
+__device__ __forceinline__ uint64_t select_key(uint32_t u, int32_t t) {
+  return ((uint64_t)u << 32) | (uint64_t)(~(uint32_t)t);
+}
+
+// Exclusive prefix sum over the block of one value per thread; *total gets the block sum.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_sum(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
   __syncthreads();
-  if (lane == 0) wsum[wave] = __popcll(bal);
+  if (lane == 63) wsum[wave] = incl;
   __syncthreads();
   int off = 0, tot = 0;
-  for (int w = 0; w < nw; ++w) {
-    if (w < wave) off += wsum[w];
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    off += w < wave ? wsum[w] : 0;
     tot += wsum[w];
   }
   *total = tot;
-  return off + in_wave;
+  return off + incl - v;
 }
 
-__global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const int32_t* scores, const int32_t* seq_lens,
-                                                                  int heads, int64_t capacity, int k,
-                                                                  int32_t* out_idx, int32_t* out_count,
-                                                                  int32_t* out_scores) {
+template <int NB>
+__global__ __launch_bounds__(256) void select_score_kernel(const uint8_t* index, const int32_t* lut_all,
+                                                           const int32_t* seq_lens, int heads, int64_t capacity,
+                                                           int32_t* scores, int32_t* hist_all) {
+  __shared__ int32_t lut[NB * 256];
+  __shared__ int32_t hist[kSelBins];
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int64_t unit = (int64_t)b * heads + h;
+  const int64_t n = min((int64_t)seq_lens[b], capacity);
+  const int64_t t0 = (int64_t)blockIdx.x * kSelChunk;
+  if (t0 >= n) return;
+  for (int e = threadIdx.x; e < NB * 256; e += 256) lut[e] = lut_all[unit * NB * 256 + e];
+  for (int e = threadIdx.x; e < kSelBins; e += 256) hist[e] = 0;
+  __syncthreads();
+  const uint8_t* base = index + (unit * capacity + t0) * NB;
+  int32_t* sc = scores + unit * capacity + t0;
+  const int m = (int)min((int64_t)kSelChunk, n - t0);
+  using Rec = typename std::conditional<NB == 16, uint4, uint2>::type;
+  constexpr int kBatch = 8;
+  for (int i0 = 0; i0 < kSelChunk / 256; i0 += kBatch) {
+    Rec r[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int t = (i0 + j) * 256 + threadIdx.x;
+      r[j] = *reinterpret_cast<const Rec*>(base + (size_t)min(t, m - 1) * NB);   // clamped, unbranched
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int t = (i0 + j) * 256 + threadIdx.x;
+      if (t >= m) continue;
+      uint32_t w[NB / 4];
+      if constexpr (NB == 16) {
+        w[0] = r[j].x; w[1] = r[j].y; w[2] = r[j].z; w[3] = r[j].w;
+      } else {
+        w[0] = r[j].x; w[1] = r[j].y;
+      }
+      int32_t s = 0;
+#pragma unroll
+      for (int g = 0; g < NB; ++g) s += lut[g * 256 + ((w[g / 4] >> (8 * (g % 4))) & 255u)];
+      sc[t] = s;
+      atomicAdd(&hist[order_key(s) >> kSelDigitShift], 1);
+    }
+  }
+  __syncthreads();
+  int32_t* gh = hist_all + unit * kSelBins;
+  for (int e = threadIdx.x; e < kSelBins; e += 256) {
+    const int v = hist[e];
+    if (v) atomicAdd(&gh[e], v);
+  }
+}
+
+struct SelectParams {
+  uint32_t bin, above;                    // bin of the k-th score; tokens in higher bins
+  uint64_t prefix, mask;                  // selected iff (select_key & mask) >= prefix
+};
+
+__global__ __launch_bounds__(256) void select_filter_kernel(const int32_t* scores, const int32_t* hist_all,
+                                                            const int32_t* seq_lens, int heads, int64_t capacity,
+                                                            int k, int n_chunks, uint2* cand_all,
+                                                            int32_t* chunk_cand, int32_t* chunk_above,
+                                                            SelectParams* params) {
+  __shared__ int wsum[4];
+  __shared__ uint32_t s_bin, s_above;
+  __shared__ int s_ncand;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int64_t unit = (int64_t)b * heads + h;
+  const int64_t n = min((int64_t)seq_lens[b], capacity);
+  const int64_t kk = min((int64_t)k, n);
+  const int64_t t0 = (int64_t)blockIdx.x * kSelChunk;
+  if (kk == 0 || kk == n || t0 >= n) return;
+  if (threadIdx.x == 0) s_ncand = 0;
+  // bin holding the kk-th largest key: thread i owns bins [16 i, 16 i + 16), higher threads
+  // hold higher bins; an exclusive sum over the reversed thread order counts what lies above.
+  const int32_t* gh = hist_all + unit * kSelBins;
+  const int32_t* sc = scores + unit * capacity + t0;
+  const int m = (int)min((int64_t)kSelChunk, n - t0);
+  // the chunk's scores are loaded first, so their latency overlaps the bin search
+  uint32_t u[kSelChunk / 256];
+#pragma unroll
+  for (int i = 0; i < kSelChunk / 256; ++i) {
+    const int t = i * 256 + threadIdx.x;
+    const uint32_t v = order_key(sc[min(t, m - 1)]);      // clamped: no branch around the load
+    u[i] = t < m ? v : 0u;
+  }
+  int own = 0;
+  int hv[16];
+#pragma unroll
+  for (int j = 0; j < 16; j += 4) {
+    const int4 v = *reinterpret_cast<const int4*>(gh + 16 * threadIdx.x + j);
+    hv[j] = v.x; hv[j + 1] = v.y; hv[j + 2] = v.z; hv[j + 3] = v.w;
+    own += v.x + v.y + v.z + v.w;
+  }
+  // count above thread i's bins = exclusive sum over slots in reversed thread order
+  // (slot j holds thread 255 - j)
+  __shared__ int owns[256];
+  int tot;
+  const int rev = 255 - (int)threadIdx.x;
+  owns[rev] = own;
+  __syncthreads();
+  const int ex = block_exclusive_sum<256>(owns[threadIdx.x], wsum, &tot);
+  __syncthreads();
+  owns[threadIdx.x] = ex;         // count above the bins of thread 255 - threadIdx.x
+  __syncthreads();
+  {
+    const int above = owns[rev];
+    if (above < kk && above + own >= kk) {
+      int cum = above;
+      for (int j = 15; j >= 0; --j) {
+        if (cum + hv[j] >= kk) {
+          s_bin = 16u * threadIdx.x + (uint32_t)j;
+          s_above = (uint32_t)cum;
+          break;
+        }
+        cum += hv[j];
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t bin = s_bin;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    params[unit].bin = bin;
+    params[unit].above = s_above;
+  }
+  uint2* cand = cand_all + unit * capacity + t0;   // this chunk's candidate region
+  const int lane = threadIdx.x & 63;
+  int cnt_above = 0;
+#pragma unroll
+  for (int i = 0; i < kSelChunk / 256; ++i) {
+    const int t = i * 256 + threadIdx.x;
+    const uint32_t dig = u[i] >> kSelDigitShift;
+    const bool in = t < m;
+    cnt_above += (in && dig > bin) ? 1 : 0;
+    const bool eq = in && dig == bin;
+    const uint64_t bal = __ballot(eq);
+    if (bal) {
+      const int leader = __ffsll((long long)bal) - 1;
+      int basepos = 0;
+      if (lane == leader) basepos = atomicAdd(&s_ncand, __popcll(bal));   // LDS counter
+      basepos = __shfl(basepos, leader);
+      if (eq) cand[basepos + __popcll(bal & ((1ull << lane) - 1ull))] = make_uint2(u[i], (uint32_t)(t0 + t));
+    }
+  }
+  (void)block_exclusive_sum<256>(cnt_above, wsum, &tot);   // (its barriers also settle s_ncand)
+  if (threadIdx.x == 0) {
+    chunk_above[unit * n_chunks + blockIdx.x] = tot;
+    chunk_cand[unit * n_chunks + blockIdx.x] = s_ncand;
+  }
+}
+
+__global__ __launch_bounds__(kSelExactThreads) void select_exact_kernel(
+    const int32_t* seq_lens, int heads, int64_t capacity, int k, int n_chunks, const uint2* cand_all,
+    const int32_t* chunk_cand, const int32_t* chunk_above, int32_t* chunk_off, SelectParams* params,
+    int32_t* out_idx, int32_t* out_count, int32_t* out_scores) {
+  extern __shared__ int32_t chunk_cnt[];          // [n_chunks] selected counts, then [n_chunks]
+                                                  // exclusive prefix of candidate counts
   __shared__ int hist[256];
-  __shared__ int wsum[kSelThreads / 64];
-  __shared__ uint32_t s_prefix, s_remaining;
+  __shared__ int wsum[kSelExactThreads / 64];
+  __shared__ uint32_t s_digit, s_rem, s_cnt;
   const int h = blockIdx.x, b = blockIdx.y;
   const int64_t unit = (int64_t)b * heads + h;
-  const int n = (int)min((int64_t)seq_lens[b], capacity);
-  const int kk = min(k, n);
-  const int32_t* sc = scores + unit * capacity;
-  int32_t* oi = out_idx ? out_idx + unit * k : nullptr;
-  int32_t* os = out_scores ? out_scores + unit * k : nullptr;
-  if (threadIdx.x == 0) out_count[unit] = kk;
-  for (int i = kk + threadIdx.x; i < k; i += blockDim.x) {
-    oi[i] = -1;
-    if (os) os[i] = 0;
+  const int64_t n = min((int64_t)seq_lens[b], capacity);
+  const int64_t kk = min((int64_t)k, n);
+  if (threadIdx.x == 0) out_count[unit] = (int32_t)kk;
+  for (int64_t i = kk + threadIdx.x; i < k; i += blockDim.x) {
+    out_idx[unit * k + i] = -1;
+    if (out_scores) out_scores[unit * k + i] = 0;
   }
   if (kk == 0) return;
-  uint32_t prefix = 0, mask = 0;
-  uint32_t remaining = (uint32_t)kk;
-  bool take_all = kk == n;
-  if (!take_all) {
-    for (int pass = 3; pass >= 0; --pass) {
-      for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0;
-      __syncthreads();
-      const int sh = 8 * pass;
-      for (int t = threadIdx.x; t < n; t += blockDim.x) {
-        const uint32_t u = order_key(sc[t]);
-        if ((u & mask) == prefix) atomicAdd(&hist[(u >> sh) & 255u], 1);
-      }
-      __syncthreads();
-      if (threadIdx.x < 64) {
-        // lane l owns digits [4l, 4l+4); suffix sums from the top digit down
-        const int l = threadIdx.x;
-        int own = 0;
-        for (int j = 0; j < 4; ++j) own += hist[4 * l + j];
-        // inclusive suffix scan of `own` over lanes (higher lanes hold higher digits)
-        int suf = own;
-        for (int o = 1; o < 64; o <<= 1) {
-          const int v = __shfl_down(suf, o);
-          if (l + o < 64) suf += v;
-        }
-        const int above = suf - own;   // elements whose digit is above 4l+3
-        if (above < (int)remaining && suf >= (int)remaining) {
-          int cum = above;
-          for (int j = 3; j >= 0; --j) {
-            const int hv = hist[4 * l + j];
-            if (cum + hv >= (int)remaining) {
-              s_prefix = prefix | ((uint32_t)(4 * l + j) << sh);
-              s_remaining = remaining - (uint32_t)cum;
-              break;
-            }
-            cum += hv;
-          }
-        }
-      }
-      __syncthreads();
-      prefix = s_prefix;
-      remaining = s_remaining;
-      mask |= 255u << sh;
-      __syncthreads();
+  const int nch = (int)((n + kSelChunk - 1) / kSelChunk);
+  int32_t* off = chunk_off + unit * n_chunks;
+  if (kk == n) {
+    for (int c = threadIdx.x; c < nch; c += blockDim.x) off[c] = c * kSelChunk;
+    if (threadIdx.x == 0) {
+      params[unit].prefix = 0;
+      params[unit].mask = 0;
     }
+    return;
   }
-  // ordered compaction: all keys > T, then the first `remaining` keys == T in index order
-  const uint32_t T = prefix;
-  int out_base = 0, eq_base = 0;
-  for (int t0 = 0; t0 < n; t0 += blockDim.x) {
-    const int t = t0 + threadIdx.x;
-    uint32_t u = 0;
-    if (t < n) u = order_key(sc[t]);
-    const bool in = t < n;
-    const bool eq = in && !take_all && u == T;
-    int eq_tot;
-    const int eq_before = eq_base + block_flag_scan(eq, wsum, &eq_tot);
-    const bool take = in && (take_all || u > T || (eq && eq_before < (int)remaining));
-    int tk_tot;
-    const int pos = out_base + block_flag_scan(take, wsum, &tk_tot);
-    if (take) {
-      oi[pos] = t;
-      if (os) os[pos] = sc[t];
+  const uint2* cand = cand_all + unit * capacity;
+  // candidate i lives in the region of chunk c = last chunk with cpre[c] <= i
+  int32_t* cpre = chunk_cnt + n_chunks;
+  int nc = 0;
+  for (int c0 = 0; c0 < nch; c0 += blockDim.x) {
+    const int c = c0 + threadIdx.x;
+    const int v = c < nch ? chunk_cand[unit * n_chunks + c] : 0;
+    int tot;
+    const int ex = block_exclusive_sum<kSelExactThreads>(v, wsum, &tot);
+    if (c < nch) cpre[c] = nc + ex;
+    nc += tot;
+  }
+  __syncthreads();
+  auto cand_at = [&](int i) {
+    int lo = 0, hi = nch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cpre[mid] <= i) lo = mid; else hi = mid - 1;
     }
-    out_base += tk_tot;
-    eq_base += eq_tot;
+    return cand[(int64_t)lo * kSelChunk + (i - cpre[lo])];
+  };
+  const SelectParams p0 = params[unit];
+  uint64_t prefix = (uint64_t)p0.bin << (32 + kSelDigitShift);
+  uint64_t mask = (uint64_t)(kSelBins - 1) << (32 + kSelDigitShift);
+  uint32_t rem = (uint32_t)(kk - p0.above);
+  uint32_t cnt = (uint32_t)nc;                 // candidates matching the prefix
+  // digit fields below the 12 histogrammed bits: order-key bits 19..12, 11..4, 3..0 (key bits
+  // 51..32), then the inverted index in four bytes (key bits 31..0)
+  for (int pass = 0; pass < 7 && cnt != rem; ++pass) {
+    const int sh = pass < 2 ? 44 - 8 * pass : (pass == 2 ? 32 : 24 - 8 * (pass - 3));
+    const uint32_t dm = pass == 2 ? 15u : 255u;
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < nc; i += blockDim.x) {
+      const uint2 cu = cand_at(i);
+      const uint64_t key = select_key(cu.x, (int32_t)cu.y);
+      if ((key & mask) == prefix) atomicAdd(&hist[(uint32_t)(key >> sh) & dm], 1);
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      // lane l owns digits [4 l, 4 l + 4); inclusive suffix sums over the lanes above
+      const int l = threadIdx.x;
+      const int own = hist[4 * l] + hist[4 * l + 1] + hist[4 * l + 2] + hist[4 * l + 3];
+      int suf = own;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_down(suf, o);
+        if (l + o < 64) suf += v;
+      }
+      const int above = suf - own;
+      if (above < (int)rem && suf >= (int)rem) {
+        int cum = above;
+        for (int j = 3; j >= 0; --j) {
+          const int hvv = hist[4 * l + j];
+          if (cum + hvv >= (int)rem) {
+            s_digit = (uint32_t)(4 * l + j);
+            s_rem = rem - (uint32_t)cum;
+            s_cnt = (uint32_t)hvv;
+            break;
+          }
+          cum += hvv;
+        }
+      }
+    }
+    __syncthreads();
+    prefix |= (uint64_t)s_digit << sh;
+    mask |= (uint64_t)dm << sh;
+    rem = s_rem;
+    cnt = s_cnt;
+    __syncthreads();
+  }
+  // per-chunk selected counts, then exclusive offsets
+  for (int c = threadIdx.x; c < nch; c += blockDim.x) chunk_cnt[c] = chunk_above[unit * n_chunks + c];
+  __syncthreads();
+  for (int i = threadIdx.x; i < nc; i += blockDim.x) {
+    const uint2 cu = cand_at(i);
+    if ((select_key(cu.x, (int32_t)cu.y) & mask) >= prefix) atomicAdd(&chunk_cnt[cu.y / kSelChunk], 1);
+  }
+  __syncthreads();
+  int carry = 0;
+  for (int c0 = 0; c0 < nch; c0 += blockDim.x) {
+    const int c = c0 + threadIdx.x;
+    const int v = c < nch ? chunk_cnt[c] : 0;
+    int tot;
+    const int ex = block_exclusive_sum<kSelExactThreads>(v, wsum, &tot);
+    if (c < nch) off[c] = carry + ex;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) {
+    params[unit].prefix = prefix;
+    params[unit].mask = mask;
+  }
+}
+
+__global__ __launch_bounds__(256) void select_write_kernel(const int32_t* scores, const int32_t* seq_lens, int heads,
+                                                           int64_t capacity, int k, int n_chunks,
+                                                           const int32_t* chunk_off, const SelectParams* params,
+                                                           int32_t* out_idx, int32_t* out_scores) {
+  __shared__ int wsum[4];
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int64_t unit = (int64_t)b * heads + h;
+  const int64_t n = min((int64_t)seq_lens[b], capacity);
+  const int64_t kk = min((int64_t)k, n);
+  const int64_t t0 = (int64_t)blockIdx.x * kSelChunk;
+  if (kk == 0 || t0 >= n) return;
+  const uint64_t prefix = params[unit].prefix, mask = params[unit].mask;
+  const int32_t* sc = scores + unit * capacity + t0;
+  const int m = (int)min((int64_t)kSelChunk, n - t0);
+  constexpr int kPer = kSelChunk / 256;
+  const int tb = (int)threadIdx.x * kPer;        // this thread's tokens [tb, tb + 16) in index order
+  int32_t s[kPer];
+  if (tb + kPer <= m) {
+#pragma unroll
+    for (int j = 0; j < kPer; j += 4) {
+      const int4 v = *reinterpret_cast<const int4*>(sc + tb + j);
+      s[j] = v.x; s[j + 1] = v.y; s[j + 2] = v.z; s[j + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) s[j] = tb + j < m ? sc[tb + j] : 0;
+  }
+  uint32_t sel = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int t = tb + j;
+    const bool take = t < m && (select_key(order_key(s[j]), (int32_t)(t0 + t)) & mask) >= prefix;
+    sel |= (take ? 1u : 0u) << j;
+  }
+  int tot;
+  int pos = chunk_off[unit * n_chunks + blockIdx.x] + block_exclusive_sum<256>(__popc(sel), wsum, &tot);
+  int32_t* oi = out_idx + unit * k;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    if ((sel & (1u << j)) && pos < kk) {
+      oi[pos] = (int32_t)(t0 + tb + j);
+      if (out_scores) out_scores[unit * k + pos] = s[j];
+      ++pos;
+    }
   }
 }
 
@@ -1985,19 +2307,37 @@ hipError_t launch_select(const Consts& c, const SelectPlan& plan, const void* q,
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   int32_t* lut = reinterpret_cast<int32_t*>(ws + plan.ws_lut);
   int32_t* scores = reinterpret_cast<int32_t*>(ws + plan.ws_scores);
+  int32_t* hist = reinterpret_cast<int32_t*>(ws + plan.ws_hist);
+  uint2* cand = reinterpret_cast<uint2*>(ws + plan.ws_cand);
+  int32_t* chunk_cand = reinterpret_cast<int32_t*>(ws + plan.ws_chunk_cand);
+  int32_t* chunk_above = reinterpret_cast<int32_t*>(ws + plan.ws_chunk_above);
+  int32_t* chunk_off = reinterpret_cast<int32_t*>(ws + plan.ws_chunk_off);
+  SelectParams* params = reinterpret_cast<SelectParams*>(ws + plan.ws_params);
   const int G = q_heads / kv_heads, ng = c.d / 4;
+  const int n_chunks = plan.n_chunks;
   if (capacity > 0) {
     const size_t lds = (size_t)G * ng * 16 * 8 + (size_t)ng * 16 * 4;
     hipLaunchKernelGGL(select_lut_kernel, dim3(kv_heads, batch), dim3(256), lds, stream, q, q_dt, codebook,
-                       c.d, G, q_heads, kv_heads, lut);
+                       c.d, G, q_heads, kv_heads, lut, hist);
+    const dim3 grid((unsigned)n_chunks, kv_heads, batch);
     ev.before(stream);
-    hipLaunchKernelGGL(select_score_kernel, dim3((unsigned)((capacity + 255) / 256), kv_heads, batch), dim3(256),
-                       0, stream, static_cast<const uint8_t*>(index), lut, seq_lens, c.d, kv_heads, capacity,
-                       scores);
+    if (c.d == 128)
+      hipLaunchKernelGGL(select_score_kernel<16>, grid, dim3(256), 0, stream, static_cast<const uint8_t*>(index),
+                         lut, seq_lens, kv_heads, capacity, scores, hist);
+    else
+      hipLaunchKernelGGL(select_score_kernel<8>, grid, dim3(256), 0, stream, static_cast<const uint8_t*>(index),
+                         lut, seq_lens, kv_heads, capacity, scores, hist);
     ev.after(stream);
+    hipLaunchKernelGGL(select_filter_kernel, grid, dim3(256), 0, stream, scores, hist, seq_lens, kv_heads, capacity,
+                       k, n_chunks, cand, chunk_cand, chunk_above, params);
   }
-  hipLaunchKernelGGL(select_topk_kernel, dim3(kv_heads, batch), dim3(kSelThreads), 0, stream, scores, seq_lens,
-                     kv_heads, capacity, k, out_idx, out_count, out_scores);
+  const size_t exact_lds = (size_t)std::max(n_chunks, 1) * 8;
+  allow_lds(select_exact_kernel, exact_lds);
+  hipLaunchKernelGGL(select_exact_kernel, dim3(kv_heads, batch), dim3(kSelExactThreads), exact_lds, stream, seq_lens, kv_heads, capacity, k, n_chunks, cand,
+                     chunk_cand, chunk_above, chunk_off, params, out_idx, out_count, out_scores);
+  if (capacity > 0 && k > 0)
+    hipLaunchKernelGGL(select_write_kernel, dim3((unsigned)n_chunks, kv_heads, batch), dim3(256), 0, stream, scores,
+                       seq_lens, kv_heads, capacity, k, n_chunks, chunk_off, params, out_idx, out_scores);
   return hipGetLastError();
 }
 

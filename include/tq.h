@@ -139,7 +139,8 @@ tq_status tq_debug_quantize(const tq_handle* h, const float* z_k, const float* p
  *    s_t = (r_k/sqrt(d)) <Pi q, gamma_k[c_t]> + sqrt(pi/2)/m rho_t <S Pi q, 2 bit_t - 1>
  *  (the QJL estimator; the second term is absent when m = 0).
  *  Exact segment (optional, hot_lens != NULL): hot_k/hot_v[b][h][hot_capacity][d] in
- *  hot_dt, tokens [0, hot_lens[b]); logit = scale * <q, k>; one softmax over cold+hot
+ *  hot_dt (each pointer aligned to 8 elements), tokens [0, hot_lens[b]);
+ *  logit = scale * <q, k>; one softmax over cold+hot
  *  (Monarch v3 page, "Wie es funktioniert").  scale = 0 selects 1/sqrt(d).
  *  out[b][hq][d] float32 = (Pi^T sum_cold p_t vhat_t + sum_hot p_t v_t) / sum_t p_t,
  *  vhat_t = (r_v/sqrt(d)) gamma_v[c^v_t]; zero when no token is attended.

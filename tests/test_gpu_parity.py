@@ -262,6 +262,15 @@ def test_decode_group_sizes_and_empty_sequences():
     _decode_case(w2, [0, 299], hot_lens=[17, 0], scale=0.3)
 
 
+def test_decode_long_exact_segment():
+    """Exact segments longer than the merge kernel keeps in LDS (logits recomputed past 2,048),
+    float32 and bfloat16 hot tokens, head_dim 128, ragged hot lengths."""
+    w = W.small(W.WORKLOADS["single_head_1k"], tokens=500, hot_tokens=2600)
+    _decode_case(w, [500], hot_lens=[2600])
+    w2 = W.small(W.WORKLOADS["llama8b_decode_32k"], tokens=900, batch=2, hot_tokens=2100)
+    _decode_case(w2, [900, 333], hot_lens=[2100, 2049])
+
+
 def test_decode_gather_mode():
     w = W.small(W.WORKLOADS["sparse_128k_top2048"], tokens=4000, batch=2)
     rng = np.random.default_rng(1)
@@ -350,6 +359,35 @@ def test_topk_edge_cases(k, lens):
 def test_topk_with_ties_and_grouped_heads():
     w = W.small(W.WORKLOADS["sparse_128k_top2048"], tokens=2048, batch=1)
     _index_case(w, [2048], 333, q_heads=32)       # G = 4: one selection per KV head
+
+
+@pytest.mark.parametrize("patterns,k", [(3, 5000), (1, 777), (40, 9000)])
+def test_topk_heavy_ties(patterns, k):
+    """Index rows drawn from a few distinct patterns: long runs of equal scores across chunks,
+    so the cut falls inside a tie and the lowest indices must win."""
+    w = W.small(W.WORKLOADS["sparse_128k_top2048"], tokens=20000, batch=1)
+    h = _handle(w)
+    codec = _codec(h)
+    K, _ = W.make_kv(w, "cuda")
+    B, T, H, d = K.shape
+    index = torch.empty((B, H, T, d // 8), dtype=torch.uint8, device="cuda")
+    book = torch.empty((B, H, d // 4, 16, 4), device="cuda")
+    h.build_sign_index(K, index, book)
+    g = torch.Generator().manual_seed(patterns)
+    rows = torch.randint(0, T, (patterns,), generator=g)
+    pick = torch.randint(0, patterns, (T,), generator=g)
+    index = index[:, :, rows[pick]].contiguous()
+    q = W.make_queries(w, "cuda")
+    sl = torch.tensor([T], dtype=torch.int32, device="cuda")
+    out_idx = torch.full((B, H, k), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((B, H), -7, dtype=torch.int32, device="cuda")
+    scs = torch.full((B, H, k), -7, dtype=torch.int32, device="cuda")
+    h.select_topk(q, index, book, sl, k, out_idx=out_idx, out_count=cnt, out_scores=scs)
+    torch.cuda.synchronize()
+    ri, rc, rs = O.select_topk(codec, _np(q), index.cpu().numpy(), book.cpu().numpy(), [T], k)
+    assert np.array_equal(cnt.cpu().numpy(), rc)
+    assert np.array_equal(out_idx.cpu().numpy(), ri)
+    assert np.array_equal(scs.cpu().numpy(), rs)
 
 
 def test_select_then_gather_attention():
