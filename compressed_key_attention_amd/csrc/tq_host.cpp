@@ -235,6 +235,11 @@ void fill_consts(const tq_config* cfg, tq::Consts* c) {
   for (size_t i = 0; i < lv.size(); ++i) c->key_levels[i] = (float)lv[i];
   for (size_t i = 0; i < bd.size(); ++i) c->key_bounds[i] = (float)bd[i];
   c->key_fix = key_fixed_point_scale(c->key_levels, 1 << c->kb);
+  {
+    double gmax = 0.0;
+    for (int i = 0; i < (1 << c->kb); ++i) gmax = std::max(gmax, std::fabs((double)c->key_levels[i]));
+    c->key_fix3 = gmax > 0.0 ? (float)(8323072.0 / gmax) : 1.0f;
+  }
   lloyd_max(c->vb, &lv, &bd);
   for (size_t i = 0; i < lv.size(); ++i) c->val_levels[i] = (float)lv[i];
   for (size_t i = 0; i < bd.size(); ++i) c->val_bounds[i] = (float)bd[i];

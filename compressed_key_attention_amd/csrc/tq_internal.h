@@ -36,6 +36,7 @@ struct Consts {
   float qjl_coef;                 // sqrt(pi/2)/m rounded to float32 (0 when m = 0)
   float key_fix;                  // fixed-point scale of the key levels for integer products:
                                   // |level| * key_fix <= 32512, levels * key_fix near integers
+  float key_fix3;                 // three-limb scale: max |level| * key_fix3 = 127 * 65536
 };
 
 // Device buffers a handle owns.
@@ -107,6 +108,8 @@ hipError_t launch_select(const Consts& c, const SelectPlan& plan, const void* q,
                          void* workspace, hipStream_t stream, const ProfileEvents& ev);
 
 struct ScanPlan {
+  bool mfma;        // matrix-core scan (head_dim 128, 2/3-bit keys, m in {0, 128})
+  int n_groups;     // groups of 4 queries per (sequence, KV head)
   size_t ws_q, ws_total;
 };
 ScanPlan plan_scan(const Consts& c, int batch, int heads, int n_queries);

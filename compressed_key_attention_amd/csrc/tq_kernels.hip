@@ -878,7 +878,14 @@ __device__ __forceinline__ uint32_t bf16_pair(float x) {      // hi | lo << 16
 // for the group's G query heads in one pass (float64 sums rounded once to float32; thread
 // (row o, half hf) holds half a row of Pi and of S Pi, loaded up front), then the lanes' query
 // operands: bop[group][lane][32 words] = Bc (16 words), Bq (8), column scales (3), pad.
-template <int BK, bool QJL>
+// SCAN: the same for a group of 4 consecutive bulk-scan queries of one (sequence, KV head)
+// (q_heads = queries per unit, kv_heads = groups per unit; rows past the last query are
+// zero), against three-limb key levels (fk = their scale F_k): bop[group][lane][36 words] =
+// 6 code chunks (key limb plane 2 - j / 2, selectors 4 (j % 2) .. + 3), 2 QJL chunks, and the
+// scales {1 / (F_q F_k), 2 / F_s, -sum / F_s} of lane L's query L / 16.
+constexpr int kScanLaneWords = 36;   // bulk-scan query operand words per lane (9 chunks of 16 B)
+
+template <int BK, bool QJL, bool SCAN>
 __global__ __launch_bounds__(256) void mfma_prep_kernel(const float* __restrict__ pi,
                                                         const float* __restrict__ s_pi, const void* q,
                                                         tq_dtype q_dt, int q_heads, int kv_heads,
@@ -888,6 +895,7 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(const float* __restrict_
   __shared__ __attribute__((aligned(16))) float xf[G][D], sf[G][D];
   const int group = blockIdx.x, b = group / kv_heads, hkv = group % kv_heads;
   const int64_t qrow0 = (int64_t)b * q_heads + (int64_t)hkv * G;
+  const int rows = SCAN ? min(G, q_heads - hkv * G) : G;
   const int o = threadIdx.x >> 1, hf = threadIdx.x & 1;
   float4 wp[H / 4], ws[H / 4];
   {
@@ -901,7 +909,7 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(const float* __restrict_
     }
   }
   for (int e = threadIdx.x; e < G * D; e += blockDim.x)
-    qv[e / D][e % D] = (double)load_elem(q, q_dt, (qrow0 + e / D) * D + e % D);
+    qv[e / D][e % D] = e / D < rows ? (double)load_elem(q, q_dt, (qrow0 + e / D) * D + e % D) : 0.0;
   __syncthreads();
   double ax[G], as[G];
 #pragma unroll
@@ -970,8 +978,31 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(const float* __restrict_
   const int L = threadIdx.x & 63, role = threadIdx.x >> 6;
   const int n = L & 15, kg = L >> 4, hB = n >> 2, part = n & 3;
   const float fq = s_fq[hB], fs = s_fs[hB];
-  u32x4* gdst = reinterpret_cast<u32x4*>(bop + ((int64_t)group * 64 + L) * 32);
-  if (role < 2) {
+  u32x4* gdst = reinterpret_cast<u32x4*>(bop + ((int64_t)group * 64 + L) * (SCAN ? kScanLaneWords : 32));
+  if (SCAN && role < 2) {
+    // key part n of weight 2^(32 - 8n) pairs key limb plane p (weight 2^(8p)) with query limb
+    // 4 - n - p (weight 2^(8 (4 - n - p))) when that is 0, 1 or 2
+#pragma unroll
+    for (int jj = 0; jj < 3; ++jj) {
+      const int j = 3 * role + jj, plane = 2 - (j >> 1), hh = j & 1;
+      const int ql = 4 - part - plane;
+      u32x4 words;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int coord = sel_coord<BK>(4 * hh + w, kk);
+          int l2, l1, l0;
+          int8_limbs3((int)rintf(xf[hB][32 * kg + coord] * fq), l2, l1, l0);
+          const int v = ql == 2 ? l2 : ql == 1 ? l1 : ql == 0 ? l0 : 0;
+          word |= (uint32_t)(v & 0xFF) << (8 * kk);
+        }
+        words[w] = word;
+      }
+      gdst[j] = words;
+    }
+  } else if (role < 2) {
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
       const int j = 2 * role + jj;
@@ -1010,8 +1041,14 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(const float* __restrict_
           }
         words[w] = word;
       }
-      gdst[4 + j] = words;
+      gdst[(SCAN ? 6 : 4) + j] = words;
     }
+  } else if (SCAN) {
+    const float fqk = s_fq[kg], fsk = s_fs[kg];
+    const float bk = 1.0f / (fqk * fk);
+    const float bq = QJL ? 2.0f / fsk : 0.0f;
+    const float oq = QJL ? -(float)s_ssum[kg] / fsk : 0.0f;
+    gdst[8] = u32x4{__float_as_uint(bk), __float_as_uint(bq), __float_as_uint(oq), 0u};
   } else {
     const float wpart = part == 0 ? 16777216.0f : part == 1 ? 65536.0f : part == 2 ? 256.0f : 0.0f;
     const float ck = wpart / (fq * fk);
@@ -1532,13 +1569,13 @@ static void launch_mfma_prep(const Consts& c, const DevConsts& dc, const void* q
   const dim3 grid((unsigned)(batch * kv_heads));
   const bool qjl = c.m > 0;
   if (c.kb == 3 && qjl)
-    hipLaunchKernelGGL((mfma_prep_kernel<3, true>), grid, dim3(256), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
+    hipLaunchKernelGGL((mfma_prep_kernel<3, true, false>), grid, dim3(256), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
   else if (c.kb == 3)
-    hipLaunchKernelGGL((mfma_prep_kernel<3, false>), grid, dim3(256), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
+    hipLaunchKernelGGL((mfma_prep_kernel<3, false, false>), grid, dim3(256), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
   else if (qjl)
-    hipLaunchKernelGGL((mfma_prep_kernel<2, true>), grid, dim3(256), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
+    hipLaunchKernelGGL((mfma_prep_kernel<2, true, false>), grid, dim3(256), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
   else
-    hipLaunchKernelGGL((mfma_prep_kernel<2, false>), grid, dim3(256), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
+    hipLaunchKernelGGL((mfma_prep_kernel<2, false, false>), grid, dim3(256), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
 }
 
 template <int BK, bool QJL>
@@ -2347,10 +2384,18 @@ hipError_t launch_select(const Consts& c, const SelectPlan& plan, const void* q,
 // A block dequantizes 64 records and stages 64 prepared queries in LDS, then each thread
 // computes a 4 x 4 tile of scores.
 // =========================================================================================
+static bool scan_mfma_path(const Consts& c) {
+  return c.d == 128 && (c.kb == 2 || c.kb == 3) && (c.m == 0 || c.m == 128);
+}
+
 ScanPlan plan_scan(const Consts& c, int batch, int heads, int n_queries) {
   ScanPlan p;
+  const size_t units = (size_t)std::max(batch, 1) * heads;
+  p.mfma = scan_mfma_path(c);
+  p.n_groups = (std::max(n_queries, 1) + 3) / 4;
   p.ws_q = 0;
-  p.ws_total = align256((size_t)std::max(batch, 1) * heads * std::max(n_queries, 1) * (c.d + c.m) * 4);
+  p.ws_total = p.mfma ? align256(units * p.n_groups * 64 * kScanLaneWords * 4)   // query operands
+                      : align256(units * std::max(n_queries, 1) * (c.d + c.m) * 4);
   return p;
 }
 
@@ -2465,10 +2510,233 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs A) {
   }
 }
 
+// -----------------------------------------------------------------------------------------
+// Matrix-core bulk scan (head_dim 128, 2- or 3-bit keys, m in {0, 128}): the decode's exact
+// int32 estimator with the roles of the operands swapped.  A = query operands (rows = 4
+// queries x 4 limb parts, from mfma_prep_kernel in SCAN mode), B = token operands (columns =
+// 16 tokens: key level limbs by v_perm_b32, QJL bits as 0/1 bytes), so lane (K slice kg,
+// column n) ends with all parts of query kg for token n and combines them in registers.
+// Unscaled estimates carry the key norm's full size, so the levels take three int8 limbs
+// here (24 bits, F_k = 127 * 65536 / max |level|): part n sums the limb products of weight
+// 2^(32 - 8n), n = 0..3, and
+//   s = (r_k/sqrt(d)) ((256 C0 + C1) 2^24 + (256 C2 + C3) 2^8) / (F_q F_k)
+//     + coef rho ((2^16 Cq0 + 2^8 Cq1 + Cq2) 2 / F_s - sum / F_s).
+// A workgroup holds the operands of 32 queries in LDS (9 x 16 B per lane and group) and its
+// four waves walk 64-token blocks of a 2048-token range: each wave keeps the 64 tokens'
+// operands in registers and sweeps the 8 query groups over them (8 MFMAs per 16 x 4 tile).
+// -----------------------------------------------------------------------------------------
+constexpr int kScanQB = 32;                 // queries per workgroup
+constexpr int kScanGroups = kScanQB / 4;
+constexpr int kScanWaveTok = 64;            // tokens per wave step (4 tiles of 16)
+constexpr int kScanBlockTok = 2048;         // tokens per workgroup
+
+struct ScanMfmaArgs {
+  const uint32_t* qop;     // [unit][group][lane][32 words]
+  const uint8_t* records;
+  float* scores;
+  int64_t capacity, n_tokens;
+  int rec_bytes, kbytes, norm_off, n_queries, n_groups;
+  float inv_sqrt_d, qjl_coef, key_fix3;
+  float key_levels[kMaxLevels];
+};
+
+constexpr int kScanChunks = kScanLaneWords / 4;
+constexpr size_t kScanLds = (size_t)kScanGroups * kScanChunks * 64 * 16;
+
+template <int BK, bool QJL>
+__global__ __launch_bounds__(256, 2) void scan_mfma_kernel(ScanMfmaArgs A) {
+  constexpr int NT = kScanWaveTok / 16;
+  extern __shared__ u32x4 qop_lds[];                   // [group][16-byte chunk][lane]
+  auto qop = [&](int g, int c, int l) -> u32x4& { return qop_lds[(g * kScanChunks + c) * 64 + l]; };
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int unit = blockIdx.z, qb = blockIdx.y;
+  const int n = lane & 15, kg = lane >> 4;
+  const int g_end = min(kScanGroups, A.n_groups - qb * kScanGroups);   // groups present
+  {
+    const u32x4* src = reinterpret_cast<const u32x4*>(A.qop + ((int64_t)unit * A.n_groups + qb * kScanGroups) * 64 * kScanLaneWords);
+    for (int e = threadIdx.x; e < kScanGroups * kScanChunks * 64; e += blockDim.x) {
+      const int g = e / (kScanChunks * 64), c = (e / 64) % kScanChunks, l = e % 64;
+      qop(g, c, l) = g < g_end ? src[((int64_t)g * 64 + l) * kScanChunks + c] : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  // key levels as three int8 limbs: gamma ~= (65536 l2 + 256 l1 + l0) / F_k; byte c of each
+  // table word = code c, one table per limb plane
+  const float fk = A.key_fix3;
+  uint32_t tp[3][2] = {{0, 0}, {0, 0}, {0, 0}};
+#pragma unroll
+  for (int c = 0; c < (1 << BK); ++c) {
+    int l2, l1, l0;
+    int8_limbs3((int)rintf(A.key_levels[c] * fk), l2, l1, l0);
+    tp[2][c >> 2] |= (uint32_t)(l2 & 0xFF) << (8 * (c & 3));
+    tp[1][c >> 2] |= (uint32_t)(l1 & 0xFF) << (8 * (c & 3));
+    tp[0][c >> 2] |= (uint32_t)(l0 & 0xFF) << (8 * (c & 3));
+  }
+  __syncthreads();
+
+  const uint8_t* recs = A.records + (int64_t)unit * A.capacity * A.rec_bytes;
+  float* out = A.scores + ((int64_t)unit * A.n_queries + (int64_t)qb * kScanQB) * A.n_tokens;
+  const int64_t tlast = A.n_tokens - 1;
+  const size_t kofs = (size_t)kg * 4 * BK, sofs = (size_t)A.kbytes + 4 * kg, nofs = (size_t)A.norm_off;
+  struct Raw {
+    uint32_t kw[NT][BK];
+    uint32_t sw[NT];
+    float nk[NT], nr[NT];
+  };
+  auto fetch = [&](int64_t t0, Raw& r) {
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      const uint8_t* rec = recs + (size_t)min(t0 + 16 * tt + n, tlast) * A.rec_bytes;
+      if constexpr (BK == 3) {
+        typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+        const u32x3 w = *reinterpret_cast<const u32x3*>(rec + kofs);
+        r.kw[tt][0] = w[0];
+        r.kw[tt][BK > 1 ? 1 : 0] = w[1];
+        r.kw[tt][BK > 2 ? 2 : 0] = w[2];
+      } else {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(rec + kofs);
+        r.kw[tt][0] = w[0];
+        r.kw[tt][BK > 1 ? 1 : 0] = w[1];
+      }
+      r.sw[tt] = QJL ? *reinterpret_cast<const uint32_t*>(rec + sofs) : 0u;
+      const float* nrm = reinterpret_cast<const float*>(rec + nofs);
+      r.nk[tt] = nrm[0];
+      r.nr[tt] = nrm[1];
+    }
+  };
+  const int64_t tb0 = (int64_t)blockIdx.x * kScanBlockTok;
+  const int64_t tb1 = min(A.n_tokens, tb0 + kScanBlockTok);
+  int64_t t0 = tb0 + (int64_t)wave * kScanWaveTok;
+  Raw cur;
+  if (t0 < tb1) fetch(t0, cur);
+  for (; t0 < tb1; t0 += 4 * kScanWaveTok) {
+    Raw nxt;
+    const int64_t t1 = t0 + 4 * kScanWaveTok;
+    if (t1 < tb1) fetch(t1, nxt);
+    // token operands of the 4 tiles
+    i32x4 Bk[NT][6], Bs[NT][2];
+    float ak[NT], aq[NT];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      uint32_t sel[8];
+      if constexpr (BK == 3) {
+        const uint32_t top = group3_top(cur.kw[tt][0], cur.kw[tt][1], cur.kw[tt][2]);
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
+          sel[2 * s] = cur.kw[tt][s] & 0x07070707u;
+          sel[2 * s + 1] = (cur.kw[tt][s] >> 3) & 0x07070707u;
+        }
+        sel[6] = top & 0x07070707u;
+        sel[7] = (top >> 3) & 0x07070707u;
+      } else {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) sel[s] = (cur.kw[tt][s >> 2] >> (2 * (s & 3))) & 0x03030303u;
+      }
+#pragma unroll
+      for (int j = 0; j < 6; ++j) {
+        const int plane = 2 - (j >> 1), hh = j & 1;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          Bk[tt][j][w] = (int)__builtin_amdgcn_perm(tp[plane][1], tp[plane][0], sel[4 * hh + w]);
+      }
+      if (QJL)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) Bs[tt][jj][w] = (int)((cur.sw[tt] >> (4 * jj + w)) & 0x01010101u);
+      ak[tt] = cur.nk[tt] * A.inv_sqrt_d;
+      aq[tt] = A.qjl_coef * cur.nr[tt];
+    }
+    for (int g = 0; g < g_end; ++g) {
+      i32x4 Ak[6], Aq[2];
+#pragma unroll
+      for (int j = 0; j < 6; ++j) Ak[j] = __builtin_bit_cast(i32x4, qop(g, j, lane));
+      if (QJL)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) Aq[j] = __builtin_bit_cast(i32x4, qop(g, 6 + j, lane));
+      const u32x4 scw = qop(g, 8, lane);
+      const float bk = __uint_as_float(scw[0]), bq = __uint_as_float(scw[1]), oq = __uint_as_float(scw[2]);
+      const bool qok = qb * kScanQB + 4 * g + kg < A.n_queries;
+      float* o = out + (int64_t)(4 * g + kg) * A.n_tokens + t0 + n;
+      const float sk_hi = 16777216.0f * bk, sk_lo = 256.0f * bk;
+      // the tiles' MFMA chains interleaved (independent accumulators), then the epilogues
+      i32x4 C0[NT], Cq[NT];
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) C0[tt] = Cq[tt] = i32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < 6; ++j)
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) C0[tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ak[j], Bk[tt][j], C0[tt], 0, 0, 0);
+      if (QJL)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt) Cq[tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aq[j], Bs[tt][j], Cq[tt], 0, 0, 0);
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+        // parts pairwise in int32 (|C0| < 2^21, |C1| < 2^22, |C2| < 2^23, |C3| < 2^22 fit with the
+        // shifts), one conversion per pair
+        const float key = fmaf((float)((C0[tt][0] << 8) + C0[tt][1]), sk_hi, (float)((C0[tt][2] << 8) + C0[tt][3]) * sk_lo);
+        float s = ak[tt] * key;
+        if (QJL) {
+          // sum_j bit_j S_j in int32: |Cq0| 2^16 + |Cq1| 2^8 + |Cq2| < 2^31
+          const float qj = fmaf((float)((Cq[tt][0] << 16) + (Cq[tt][1] << 8) + Cq[tt][2]), bq, oq);
+          s = fmaf(aq[tt], qj, s);
+        }
+        if (qok && t0 + 16 * tt + n < tb1) o[16 * tt] = s;
+      }
+    }
+    if (t1 < tb1) cur = nxt;
+  }
+}
+
+template <int BK, bool QJL>
+static void launch_scan_mfma(dim3 grid, const ScanMfmaArgs& a, hipStream_t stream) {
+  allow_lds(scan_mfma_kernel<BK, QJL>, kScanLds);
+  hipLaunchKernelGGL((scan_mfma_kernel<BK, QJL>), grid, dim3(256), kScanLds, stream, a);
+}
+
 hipError_t launch_scan(const Consts& c, const DevConsts& dc, const ScanPlan& plan, const void* q, tq_dtype q_dt,
                        int batch, int heads, int n_queries, const void* records, int64_t capacity,
                        int64_t n_tokens, float* scores, void* workspace, hipStream_t stream,
                        const ProfileEvents& ev) {
+  if (plan.mfma) {
+    uint32_t* qop = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + plan.ws_q);
+    const dim3 pgrid((unsigned)(batch * heads * plan.n_groups));
+    const bool qjl = c.m > 0;
+    // q viewed as [units][n_queries] rows: "heads" of the prep = queries per unit, groups per unit
+    if (c.kb == 3 && qjl)
+      hipLaunchKernelGGL((mfma_prep_kernel<3, true, true>), pgrid, dim3(256), 0, stream, dc.pi, dc.s_pi, q, q_dt, n_queries, plan.n_groups, c.key_fix3, qop);
+    else if (c.kb == 3)
+      hipLaunchKernelGGL((mfma_prep_kernel<3, false, true>), pgrid, dim3(256), 0, stream, dc.pi, dc.s_pi, q, q_dt, n_queries, plan.n_groups, c.key_fix3, qop);
+    else if (qjl)
+      hipLaunchKernelGGL((mfma_prep_kernel<2, true, true>), pgrid, dim3(256), 0, stream, dc.pi, dc.s_pi, q, q_dt, n_queries, plan.n_groups, c.key_fix3, qop);
+    else
+      hipLaunchKernelGGL((mfma_prep_kernel<2, false, true>), pgrid, dim3(256), 0, stream, dc.pi, dc.s_pi, q, q_dt, n_queries, plan.n_groups, c.key_fix3, qop);
+    ScanMfmaArgs a;
+    a.qop = qop;
+    a.records = static_cast<const uint8_t*>(records);
+    a.scores = scores;
+    a.capacity = capacity;
+    a.n_tokens = n_tokens;
+    a.rec_bytes = c.rec_bytes;
+    a.kbytes = c.kbytes;
+    a.norm_off = c.norm_off;
+    a.n_queries = n_queries;
+    a.n_groups = plan.n_groups;
+    a.inv_sqrt_d = c.inv_sqrt_d;
+    a.qjl_coef = c.qjl_coef;
+    a.key_fix3 = c.key_fix3;
+    for (int i = 0; i < kMaxLevels; ++i) a.key_levels[i] = c.key_levels[i];
+    const dim3 grid((unsigned)((n_tokens + kScanBlockTok - 1) / kScanBlockTok),
+                    (unsigned)((n_queries + kScanQB - 1) / kScanQB), (unsigned)(batch * heads));
+    ev.before(stream);
+    if (c.kb == 3 && qjl) launch_scan_mfma<3, true>(grid, a, stream);
+    else if (c.kb == 3) launch_scan_mfma<3, false>(grid, a, stream);
+    else if (qjl) launch_scan_mfma<2, true>(grid, a, stream);
+    else launch_scan_mfma<2, false>(grid, a, stream);
+    ev.after(stream);
+    return hipGetLastError();
+  }
   float* qprep = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + plan.ws_q);
   const int rows = batch * heads * n_queries;
   hipLaunchKernelGGL(scan_prep_kernel, dim3(rows), dim3(128), 0, stream, dc.pi, dc.s, c.d, c.m, q, q_dt, qprep);

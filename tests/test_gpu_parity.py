@@ -418,6 +418,27 @@ def test_score_scan_reduced():
     _close(sc.cpu().numpy(), ref, "scan scores")
 
 
+@pytest.mark.parametrize("kb,m,d,nq,T,n_tok", [(3, 128, 128, 70, 1000, 1000), (2, 128, 128, 37, 2100, 2093),
+                                                (3, 0, 128, 33, 4097, 4097), (2, 0, 128, 5, 300, 17),
+                                                (3, 64, 64, 20, 500, 500)])
+def test_score_scan_variants(kb, m, d, nq, T, n_tok):
+    """Matrix-core scan for both key widths with and without the sketch, query counts that are
+    not multiples of the 4-query groups or 32-query blocks, token counts past the 2048-token
+    blocks and below the capacity; head_dim 64 (and m = 64) takes the generic kernel."""
+    base = W.small(W.WORKLOADS["bulk_64k_scan"], tokens=T, scan_queries=nq)
+    w = W.Workload(**{**base.__dict__, "key_bits": kb, "qjl_dim": m, "head_dim": d})
+    h = _handle(w)
+    codec = _codec(h)
+    K, V = W.make_kv(w, "cuda")
+    rec = _compress(w, h, K, V)
+    q = W.make_queries(w, "cuda")
+    sc = torch.full((1, w.kv_heads, nq, n_tok), float("nan"), device="cuda")
+    h.score_scan(q, rec, n_tok, scores=sc)
+    torch.cuda.synchronize()
+    ref = O.score_scan(codec, _np(q), rec.cpu().numpy(), n_tok)
+    _close(sc.cpu().numpy(), ref, f"scan scores kb={kb} m={m} d={d}")
+
+
 # ------------------------------------------------------------------ full sizes, sampled --
 def test_llama8b_decode_full_size_sampled():
     w = W.WORKLOADS["llama8b_decode_32k"]
