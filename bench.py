@@ -333,7 +333,17 @@ def run_bulk_scan(args, tq, W, ev):
     line = base_line(args, w, ms_per_step, B * T)
     line["metric"] = "compressed tokens scanned per second (256 queries per KV head) + % of HBM roofline"
     line["config"].update({"scan_queries": nq})
-    line["roofline"] = roofline("scan_kernel", w.name, alg_bytes, scan_ms)
+    mfma = w.head_dim == 128 and w.key_bits in (2, 3) and w.qjl_dim in (0, 128)
+    kname = "scan_mfma_kernel" if mfma else "scan_kernel"
+    extra = None
+    if mfma:
+        # int8 matrix-core work the kernel executes: 8 (6 without the sketch) 16x16x64 MFMAs per
+        # 16 tokens x 4 queries
+        n_mfma = (8 if w.qjl_dim else 6) * (B * H * T / 16) * (nq / 4)
+        tops = n_mfma * 2 * 16 * 16 * 64 / (scan_ms * 1e-3) / 1e12
+        extra = {"mfma_int8_executed_tops": tops, "mfma_int8_peak_tops": 5000.0,
+                 "mfma_int8_frac": tops / 5000.0}
+    line["roofline"] = roofline(kname, w.name, alg_bytes, scan_ms, extra)
     line["scores_per_s"] = B * H * nq * T / (ms_per_step * 1e-3)
     line["compress"] = {"ms": compress_ms, "token_heads_per_s": B * H * T / (compress_ms * 1e-3)}
     if not args.no_cpu_baseline:
