@@ -818,19 +818,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_scan_kernel(DecodeArgs 
 // Matrix-core decode scan for head_dim 128 and 4 query heads per KV head (2- or 3-bit keys,
 // 4-bit values).  Same arithmetic as decode_scan_kernel, laid out for gfx950.  Each wave
 // takes 16 tokens per step:
-//  * key scores on v_mfma_i32_16x16x64_i8, exact in int32: rows = tokens, columns = (head,
-//    part).  Key levels are two-limb fixed point (level ~= (256 hi + lo) / F with int8 limbs,
+//  * key scores on v_mfma_i32_16x16x64_i8, exact in int32: rows = (head, part), columns =
+//    tokens.  Key levels are two-limb fixed point (level ~= (256 hi + lo) / F with int8 limbs,
 //    F chosen on the host so the levels sit near integers); queries and query sketches are
 //    three-limb fixed point (24 bits against the head's largest entry).  The code product
-//    keeps the limb products of weight 2^24, 2^16 and 2^8 (three columns per head) and drops
-//    only low x low (2^-24 relative); the QJL product has its own accumulator with one column
+//    keeps the limb products of weight 2^24, 2^16 and 2^8 (three rows per head) and drops
+//    only low x low (2^-24 relative); the QJL product has its own accumulator with one row
 //    per sketch limb.  Level limbs come from registers (v_perm_b32, 4 codes per
 //    instruction); QJL bits enter as 0/1 bytes and the sketch sum is subtracted afterwards.
-//  * the score tile goes through LDS to a lane-per-(token, head) layout; the running maximum of
-//    each head is shared by the wave (raised lazily), p and w = p r_v / sqrt(d) per lane;
+//    Lane (kg, n) receives every part of head kg for token n and combines them in registers;
+//  * the running maximum of each head is shared by its 16 lanes (raised lazily), p and
+//    w = p r_v / sqrt(d) per lane;
 //  * value aggregation on v_mfma_f32_16x16x32_bf16: rows = coordinates, K = (token, level
 //    half), columns = (head, w half); the 16 tokens' value codes are transposed through 1 KB
-//    of LDS and their level halves read as pairs from a 256-entry LDS table.
+//    of LDS and their level halves read as pairs from a 16-entry LDS table.
 // -----------------------------------------------------------------------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -877,12 +878,13 @@ __device__ __forceinline__ uint32_t bf16_pair(float x) {      // hi | lo << 16
 // Per (sequence, KV head) preparation for the matrix-core scan: q_x = Pi q and q_s = (S Pi) q
 // for the group's G query heads in one pass (float64 sums rounded once to float32; thread
 // (row o, half hf) holds half a row of Pi and of S Pi, loaded up front), then the lanes' query
-// operands: bop[group][lane][32 words] = Bc (16 words), Bq (8), column scales (3), pad.
+// operands: bop[group][lane][32 words] = code words (16), QJL words (8), and the scales of lane
+// L's head L / 16, {1 / (F_q F_k), 2 / F_s, -sum / F_s} (3), pad.
 // SCAN: the same for a group of 4 consecutive bulk-scan queries of one (sequence, KV head)
 // (q_heads = queries per unit, kv_heads = groups per unit; rows past the last query are
 // zero), against three-limb key levels (fk = their scale F_k): bop[group][lane][36 words] =
 // 6 code chunks (key limb plane 2 - j / 2, selectors 4 (j % 2) .. + 3), 2 QJL chunks, and the
-// scales {1 / (F_q F_k), 2 / F_s, -sum / F_s} of lane L's query L / 16.
+// same scales for lane L's query L / 16.
 constexpr int kScanLaneWords = 36;   // bulk-scan query operand words per lane (9 chunks of 16 B)
 
 template <int BK, bool QJL, bool SCAN>
@@ -967,7 +969,8 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(const float* __restrict_
     }
   }
   __syncthreads();
-  // operand words: scan lane L = (column n = L % 16, K slice kg = L / 16), head n / 4, part n % 4.
+  // operand words (A of the score products): lane L = (row n = L % 16, K slice kg = L / 16),
+  // head n / 4, part n % 4.
   //  code word (j, w): byte k <-> coordinate 32 kg + sel_coord(2j + (w & 1), k); w < 2: high
   //    level limb slots, w >= 2: low limb slots.  part 0 (weight 2^24): hi x q2; part 1 (2^16):
   //    hi x q1 + lo x q2; part 2 (2^8): hi x q0 + lo x q1; part 3: zero.
@@ -1043,18 +1046,13 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(const float* __restrict_
       }
       gdst[(SCAN ? 6 : 4) + j] = words;
     }
-  } else if (SCAN) {
+  } else {
+    // the score lanes of head / query kg combine its parts with these
     const float fqk = s_fq[kg], fsk = s_fs[kg];
     const float bk = 1.0f / (fqk * fk);
     const float bq = QJL ? 2.0f / fsk : 0.0f;
     const float oq = QJL ? -(float)s_ssum[kg] / fsk : 0.0f;
-    gdst[8] = u32x4{__float_as_uint(bk), __float_as_uint(bq), __float_as_uint(oq), 0u};
-  } else {
-    const float wpart = part == 0 ? 16777216.0f : part == 1 ? 65536.0f : part == 2 ? 256.0f : 0.0f;
-    const float ck = wpart / (fq * fk);
-    const float cq = QJL ? 2.0f * (wpart / 256.0f) / fs : 0.0f;
-    const float oq = (QJL && part == 0) ? -(float)s_ssum[hB] / fs : 0.0f;
-    gdst[6] = u32x4{__float_as_uint(ck), __float_as_uint(cq), __float_as_uint(oq), 0u};
+    gdst[SCAN ? 8 : 6] = u32x4{__float_as_uint(bk), __float_as_uint(bq), __float_as_uint(oq), 0u};
   }
 }
 
@@ -1066,15 +1064,11 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
   // value code -> bf16 (hi, lo) pair of its level: 16 words in 16 distinct banks, so lookups
   // never conflict (equal codes are broadcast)
   __shared__ uint32_t vtab[16];
-  // Staging tiles, rows padded to TS words so that the four K-slices of a write (and the 16
-  // rows of a 16-byte read) fall on distinct LDS banks.  The cross-wave merge reuses them.
+  // Value-code staging, rows padded to TS words so that the four K-slices of a write (and the
+  // 16 rows of a 16-byte read) fall on distinct LDS banks.  The cross-wave merge reuses it.
   constexpr int TS = 20;
-  struct Stage {
-    float tile[NW][2][16 * TS];      // score tiles (code, QJL): [token][column]
-    uint32_t vst[NW][16 * TS];       // value codes: [coordinate octet][token]
-  };
   __shared__ __attribute__((aligned(16))) union {
-    Stage st;
+    uint32_t vst[NW][16 * TS];       // value codes: [coordinate octet][token]
     float red[NW][G][D + 2];         // cross-wave merge
   } sh;
   __shared__ __attribute__((aligned(16))) uint32_t wstage[NW][2][4 * 16];  // [w half][head][token] bf16 in high 16 bits
@@ -1097,22 +1091,27 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
     tl[c >> 2] |= (uint32_t)(lo & 0xFF) << (8 * (c & 3));
   }
 
-  // query operands (B) and column scales, prepared per (sequence, KV head) by mfma_prep_kernel
+  // Score products with the query operands as A (rows = (head, part), from mfma_prep_kernel)
+  // and the 16 tokens' operands as B, so lane (K slice / head kg, column n) ends with every
+  // part of head kg for token n: the lane owns score (token n, head kg), and each lane loads
+  // only its own token's fields (key group kg, sketch word kg, value quarter kg, norms).
   const int n = lane & 15, kg = lane >> 4;
-  i32x4 Bc[4], Bq[2];
-  float colscale_k, colscale_q, coloff_q;
+  i32x4 Aq[4], Aj[2];
+  float bk16, bk8, bq, oq;
   {
     const u32x4* bp = reinterpret_cast<const u32x4*>(A.bop + (((int64_t)b * A.kv_heads + hkv) * 64 + lane) * 32);
     u32x4 w[7];
 #pragma unroll
     for (int i = 0; i < 7; ++i) w[i] = bp[i];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) Bc[j] = __builtin_bit_cast(i32x4, w[j]);
+    for (int j = 0; j < 4; ++j) Aq[j] = __builtin_bit_cast(i32x4, w[j]);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) Bq[j] = __builtin_bit_cast(i32x4, w[4 + j]);
-    colscale_k = __uint_as_float(w[6][0]);
-    colscale_q = __uint_as_float(w[6][1]);
-    coloff_q = __uint_as_float(w[6][2]);
+    for (int j = 0; j < 2; ++j) Aj[j] = __builtin_bit_cast(i32x4, w[4 + j]);
+    const float bk = __uint_as_float(w[6][0]);
+    bk16 = 65536.0f * bk;
+    bk8 = 256.0f * bk;
+    bq = __uint_as_float(w[6][1]);
+    oq = __uint_as_float(w[6][2]);
   }
   __syncthreads();
 
@@ -1120,9 +1119,7 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
   const int c0 = chunk * A.chunk, c1 = min(n_tok, c0 + A.chunk);
   const uint8_t* recs = A.records + ((int64_t)b * A.kv_heads + hkv) * A.capacity * A.rec_bytes;
   const int32_t* sel = GATHER ? A.sel_idx + ((int64_t)b * A.kv_heads + hkv) * A.k_sel : nullptr;
-  const int vslot = lane >> 2, vj = lane & 3;   // softmax layout: token slot, head (also coordinate quarter)
-  float* tile = sh.st.tile[wave][0];
-  uint32_t* vst = sh.st.vst[wave];
+  uint32_t* vst = sh.vst[wave];
   uint32_t* wst = wstage[wave][0];
 
   // value accumulators: lane (column n = 2 h + w half, K slice kg) holds rows 4 kg + r of
@@ -1130,8 +1127,8 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
   f32x4 acc[8];
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) acc[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float mrun = kNegInf;    // running maximum of head vj (uniform across the wave for each head)
-  float lsum = 0.0f;       // this lane's share of sum_t p_t for head vj
+  float mrun = kNegInf;    // running maximum of head kg (uniform across its 16 lanes)
+  float lsum = 0.0f;       // this lane's share of sum_t p_t for head kg
   const int vh = n >> 1;   // head of this lane's value column (n < 8)
   // B rows of the value product: the w half (n & 1) of head vh for tokens 4 kg .. 4 kg + 3
   const uint32_t* wsrc = n < 8 ? wstage[wave][n & 1] + (vh & 3) * 16 + 4 * kg : wzero;
@@ -1148,38 +1145,31 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
   // (sequence, head) run fit in 32 bits (the host routes larger caches to the generic kernel).
   const uint32_t rb = (uint32_t)A.rec_bytes;
   const uint32_t kofs = (uint32_t)(kg * 4 * BK), sofs = (uint32_t)(A.kbytes + 4 * kg);
-  const uint32_t vofs = (uint32_t)(A.kbytes + A.sbytes + 16 * vj), nofs = (uint32_t)A.norm_off;
+  const uint32_t vofs = (uint32_t)(A.kbytes + A.sbytes + 16 * kg), nofs = (uint32_t)A.norm_off;
   auto fetch = [&](int base, Fields& f) {
-    const int pk = min(base + n, c1 - 1);
-    uint32_t tk = (uint32_t)pk;
+    const int p = base + n;
+    uint32_t t = (uint32_t)min(p, c1 - 1);
+    f.valid = p < c1;
     if (GATHER) {
-      const int t = sel[pk];
-      tk = (t < 0 || (int64_t)t >= A.capacity) ? 0u : (uint32_t)t;
+      const int ts = sel[t];
+      f.valid = f.valid && ts >= 0 && (int64_t)ts < A.capacity;
+      t = f.valid ? (uint32_t)ts : 0u;
     }
-    const uint32_t ok = (uint32_t)__umul24(tk, rb);
+    const uint32_t o = (uint32_t)__umul24(t, rb);
     if constexpr (BK == 3) {
       typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
-      const u32x3 w = *reinterpret_cast<const u32x3*>(recs + (size_t)(ok + kofs));
+      const u32x3 w = *reinterpret_cast<const u32x3*>(recs + (size_t)(o + kofs));
       f.kw[0] = w[0];
       f.kw[1] = w[1];
       f.kw[2] = w[2];
     } else {
-      const u32x2 w = *reinterpret_cast<const u32x2*>(recs + (size_t)(ok + kofs));
+      const u32x2 w = *reinterpret_cast<const u32x2*>(recs + (size_t)(o + kofs));
       f.kw[0] = w[0];
       f.kw[1] = w[1];
     }
-    f.sw = QJL ? *reinterpret_cast<const uint32_t*>(recs + (size_t)(ok + sofs)) : 0u;
-    const int pv = base + vslot;
-    uint32_t tv = (uint32_t)min(pv, c1 - 1);
-    f.valid = pv < c1;
-    if (GATHER) {
-      const int t = sel[tv];
-      f.valid = f.valid && t >= 0 && (int64_t)t < A.capacity;
-      tv = f.valid ? (uint32_t)t : 0u;
-    }
-    const uint32_t ov = (uint32_t)__umul24(tv, rb);
-    f.vw = *reinterpret_cast<const u32x4*>(recs + (size_t)(ov + vofs));
-    const float* nrm = reinterpret_cast<const float*>(recs + (size_t)(ov + nofs));
+    f.sw = QJL ? *reinterpret_cast<const uint32_t*>(recs + (size_t)(o + sofs)) : 0u;
+    f.vw = *reinterpret_cast<const u32x4*>(recs + (size_t)(o + vofs));
+    const float* nrm = reinterpret_cast<const float*>(recs + (size_t)(o + nofs));
     f.nk = nrm[0];
     f.nrho = nrm[1];
     f.nv = nrm[2];
@@ -1188,7 +1178,7 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
   // one 16-token step on fields `cur` (tokens base .. base + 15)
   auto step = [&](const Fields& cur, int base) {
 
-    // ---- key scores (exact int32) ----
+    // ---- key scores (exact int32), token operands from the level tables ----
     uint32_t sel[8];
     if constexpr (BK == 3) {
       const uint32_t top = group3_top(cur.kw[0], cur.kw[1], cur.kw[2]);
@@ -1206,46 +1196,38 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
     i32x4 C0 = i32x4{0, 0, 0, 0}, Cq = C0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const i32x4 a = i32x4{(int)__builtin_amdgcn_perm(th[1], th[0], sel[2 * j]),
-                            (int)__builtin_amdgcn_perm(th[1], th[0], sel[2 * j + 1]),
-                            (int)__builtin_amdgcn_perm(tl[1], tl[0], sel[2 * j]),
-                            (int)__builtin_amdgcn_perm(tl[1], tl[0], sel[2 * j + 1])};
-      C0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, Bc[j], C0, 0, 0, 0);
+      const i32x4 bt = i32x4{(int)__builtin_amdgcn_perm(th[1], th[0], sel[2 * j]),
+                             (int)__builtin_amdgcn_perm(th[1], th[0], sel[2 * j + 1]),
+                             (int)__builtin_amdgcn_perm(tl[1], tl[0], sel[2 * j]),
+                             (int)__builtin_amdgcn_perm(tl[1], tl[0], sel[2 * j + 1])};
+      C0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aq[j], bt, C0, 0, 0, 0);
       if (QJL && (j & 1)) {
         i32x4 q;
 #pragma unroll
         for (int w = 0; w < 4; ++w) q[w] = (int)((cur.sw >> (2 * (j & 2) + w)) & 0x01010101u);
-        Cq = __builtin_amdgcn_mfma_i32_16x16x64_i8(q, Bq[j >> 1], Cq, 0, 0, 0);
+        Cq = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aj[j >> 1], q, Cq, 0, 0, 0);
       }
     }
-    // ---- score tile -> lane per (token slot, head); stage value codes by coordinate octet ----
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      tile[(4 * kg + r) * TS + n] = (float)C0[r] * colscale_k;
-      if (QJL) tile[16 * TS + (4 * kg + r) * TS + n] = fmaf((float)Cq[r], colscale_q, coloff_q);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) vst[(4 * vj + r) * TS + vslot] = cur.vw[r];
-    wave_lds_sync();
-    const f32x4 sk = *reinterpret_cast<const f32x4*>(tile + vslot * TS + 4 * vj);
-    float shat = cur.nk * A.inv_sqrt_d * ((sk[0] + sk[1]) + sk[2]);
+    // parts of head kg for token n: weights 2^24, 2^16, 2^8 (|C0[0]| < 2^21 and |C0[1]| < 2^22,
+    // so 256 C0[0] + C0[1] fits in int32); sketch sum 2^16 Cq0 + 2^8 Cq1 + Cq2 < 2^31
+    float shat = cur.nk * A.inv_sqrt_d * fmaf((float)((C0[0] << 8) + C0[1]), bk16, (float)C0[2] * bk8);
     if (QJL) {
-      const f32x4 sq = *reinterpret_cast<const f32x4*>(tile + 16 * TS + vslot * TS + 4 * vj);
-      shat = fmaf(A.qjl_coef * cur.nrho, (sq[0] + sq[1]) + sq[2], shat);
+      const float qj = fmaf((float)((Cq[0] << 16) + (Cq[1] << 8) + Cq[2]), bq, oq);
+      shat = fmaf(A.qjl_coef * cur.nrho, qj, shat);
     }
     const float logit = cur.valid ? A.scale * shat : kNegInf;
-    if (LOGITS && cur.valid) A.logits[(qrow0 + vj) * A.logit_stride + base + vslot] = logit;
-    // ---- running maximum per head, shared by the wave, raised lazily (rare branch) ----
+    if (LOGITS && cur.valid) A.logits[(qrow0 + kg) * A.logit_stride + base + n] = logit;
+    // ---- running maximum per head, shared by its 16 lanes, raised lazily (rare branch) ----
     if (__ballot(logit > mrun + kLazy) != 0ull) {
       float tmax = logit;
 #pragma unroll
-      for (int msk = 4; msk < 64; msk <<= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, msk));
+      for (int msk = 1; msk < 16; msk <<= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, msk));
       const bool raise = tmax > mrun + kLazy;         // uniform within each head
       const float fct = raise ? (mrun == kNegInf ? 0.0f : __expf(mrun - tmax)) : 1.0f;
       lsum *= fct;
       mrun = raise ? tmax : mrun;
       // rescale the value accumulators of head vh by that head's factor
-      const float fv = __shfl(fct, vh);               // lane vh (slot 0) holds head vh's factor
+      const float fv = __shfl(fct, 16 * (vh & 3));    // lane 16 h holds head h's factor
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) acc[mt] *= fv;
     }
@@ -1256,9 +1238,12 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
       const uint32_t wb = __float_as_uint(p * cur.nv * A.inv_sqrt_d);
       const uint32_t hi = (wb + 0x7FFFu + ((wb >> 16) & 1u)) & 0xFFFF0000u;
       const uint32_t lo = __float_as_uint(__uint_as_float(wb) - __uint_as_float(hi)) & 0xFFFF0000u;
-      wst[vj * 16 + vslot] = hi;
-      wst[64 + vj * 16 + vslot] = lo;
+      wst[kg * 16 + n] = hi;
+      wst[64 + kg * 16 + n] = lo;
     }
+    // this token's value codes, coordinate quarter kg: word r = coordinate octet 4 kg + r
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vst[(4 * kg + r) * TS + n] = cur.vw[r];
     wave_lds_sync();
     // ---- values: B = w halves of (head vh) for tokens 4 kg .. 4 kg + 3, A = level halves ----
     const u32x4 w4 = *reinterpret_cast<const u32x4*>(wsrc);
@@ -1268,19 +1253,26 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
 #pragma unroll
     for (int d = 0; d < 4; ++d) bw[d] = __builtin_amdgcn_perm(w4[d], w4[d], 0x03020302u);
     const bf16x8 Bv = __builtin_bit_cast(bf16x8, bw);
-    u32x4 nib[2];                                     // low / high nibbles of the code bytes
+    // low / high nibbles of the code bytes, pre-scaled to LDS byte offsets into vtab, so each
+    // lookup address is one byte extract
+    u32x4 nib[2];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      nib[0][d] = codes[d] & 0x0F0F0F0Fu;
-      nib[1][d] = (codes[d] >> 4) & 0x0F0F0F0Fu;
+      nib[0][d] = (codes[d] << 2) & 0x3C3C3C3Cu;
+      nib[1][d] = (codes[d] >> 2) & 0x3C3C3C3Cu;
+      // opaque to the optimizer, which would otherwise fold the scaling back into every
+      // extract (shift + mask per lookup instead of one bit-field extract)
+      asm volatile("" : "+v"(nib[0][d]));
+      asm volatile("" : "+v"(nib[1][d]));
     }
+    const uint8_t* vt = reinterpret_cast<const uint8_t*>(vtab);
 #pragma unroll
     for (int pr = 0; pr < 4; ++pr) {                  // coordinate tiles 2 pr, 2 pr + 1
       u32x4 a0, a1;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        a0[d] = vtab[(nib[0][d] >> (8 * pr)) & 0xFFu];
-        a1[d] = vtab[(nib[1][d] >> (8 * pr)) & 0xFFu];
+        a0[d] = *reinterpret_cast<const uint32_t*>(vt + ((nib[0][d] >> (8 * pr)) & 0xFFu));
+        a1[d] = *reinterpret_cast<const uint32_t*>(vt + ((nib[1][d] >> (8 * pr)) & 0xFFu));
       }
       acc[2 * pr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), Bv, acc[2 * pr], 0, 0, 0);
       acc[2 * pr + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), Bv, acc[2 * pr + 1], 0, 0, 0);
@@ -1300,18 +1292,18 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
     base += NW * 16;
   }
 
-  // ---- merge: sum the two w halves (columns 2h, 2h+1), the slots' l, then the waves ----
+  // ---- merge: sum the two w halves (columns 2h, 2h+1), the token lanes' l, then the waves ----
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[mt][r] += __shfl_xor(acc[mt][r], 1);
 #pragma unroll
-  for (int msk = 4; msk < 64; msk <<= 1) lsum += __shfl_xor(lsum, msk);
-  __syncthreads();              // every wave is done with the staging tiles the merge reuses
+  for (int msk = 1; msk < 16; msk <<= 1) lsum += __shfl_xor(lsum, msk);
+  __syncthreads();              // every wave is done with the staging area the merge reuses
   float (*red)[G][D + 2] = sh.red;
-  if (lane < 4) {               // slot 0 lanes: head vj's m and l
-    red[wave][vj][0] = mrun;
-    red[wave][vj][1] = lsum;
+  if (n == 0) {                 // lane 16 h: head h's m and l
+    red[wave][kg][0] = mrun;
+    red[wave][kg][1] = lsum;
   }
   if (n < 8 && (n & 1) == 0) {  // column (h, hi half) lanes: o[h][8 (4 kg + r) + mt]
 #pragma unroll
