@@ -31,6 +31,7 @@ EXPORTED = [
     "tq_compress_kv", "tq_debug_quantize", "tq_decode_workspace_size", "tq_decode_attention",
     "tq_index_workspace_size", "tq_build_sign_index", "tq_select_workspace_size",
     "tq_select_topk", "tq_scan_workspace_size", "tq_score_scan", "tq_set_profile_events",
+    "tq_stream_read",
 ]
 
 
@@ -79,11 +80,18 @@ _select = _sig("tq_select_topk", _P, _P, ctypes.c_int, _I32, _I32, _I32, _P, _P,
 _scan_ws = _sig("tq_scan_workspace_size", _P, _I32, _I32, _I32, _PSZ)
 _scan = _sig("tq_score_scan", _P, _P, ctypes.c_int, _I32, _I32, _I32, _P, _I64, _I64, _P, _P, _SZ, _P)
 _set_events = _sig("tq_set_profile_events", _P, _P)
+_stream_read = _sig("tq_stream_read", _P, _SZ, _P, _SZ, _P)
 
 
 def set_profile_events(start, stop):
     """Arm raw hipEvent_t handles (ints) around the main kernel of the next call on this thread."""
     check(_set_events(_P(start) if start else None, _P(stop) if stop else None))
+
+
+def stream_read(buf, sink, stream=None):
+    """Enqueue the library's streaming read of `buf` (a 16-byte aligned device tensor) into
+    `sink` (device uint32 tensor) - measurement support for the bench's read ceiling."""
+    check(_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), sink.numel(), _stream(stream)))
 
 
 def last_error() -> str:

@@ -293,6 +293,15 @@ tq_status tq_set_profile_events(hipEvent_t start, hipEvent_t stop) {
   return ok();
 }
 
+tq_status tq_stream_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words, hipStream_t stream) {
+  if (!buf || !sink) return fail(TQ_ERR_INVALID_ARGUMENT, "NULL buffer or sink");
+  if (!aligned(buf, 16) || bytes % 16) return fail(TQ_ERR_INVALID_ARGUMENT, "buffer must be 16-byte aligned and sized");
+  const int blocks = tq::stream_read_blocks();
+  if (sink_words < tq::stream_read_sink_words())
+    return fail(TQ_ERR_WORKSPACE_TOO_SMALL, "sink needs %zu words", tq::stream_read_sink_words());
+  return device_status(tq::launch_stream_read(buf, bytes, sink, blocks, stream, take_events()), "stream read launch");
+}
+
 tq_status tq_host_constants(const tq_config* cfg, float* pi, float* s, float* key_levels,
                             float* key_bounds, float* value_levels, float* value_bounds) {
   tq_status st = check_config(cfg);

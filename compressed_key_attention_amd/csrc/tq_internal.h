@@ -118,4 +118,9 @@ hipError_t launch_scan(const Consts& c, const DevConsts& dc, const ScanPlan& pla
                        int64_t capacity, int64_t n_tokens, float* scores, void* workspace,
                        hipStream_t stream, const ProfileEvents& ev);
 
+int stream_read_blocks();          // workgroups of the streaming read (256 threads each)
+size_t stream_read_sink_words();   // one word per wave
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int blocks, hipStream_t stream,
+                              const ProfileEvents& ev);
+
 }  // namespace tq

@@ -2759,4 +2759,44 @@ hipError_t launch_scan(const Consts& c, const DevConsts& dc, const ScanPlan& pla
   return hipGetLastError();
 }
 
+// =========================================================================================
+// Measurement support: a streaming read of `bytes` bytes.  Each of ~16 workgroups per CU reads
+// one contiguous slice with 16-byte loads, eight in flight per thread, and folds it into one
+// word per wave so the loads cannot be dropped.  It gives the bench its own read ceiling.
+// =========================================================================================
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ src, size_t n16,
+                                                          uint32_t* sink) {
+  constexpr int U = 8;
+  uint32_t x = 0;
+  const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t b0 = min((size_t)blockIdx.x * per, n16), b1 = min(b0 + per, n16);
+  size_t i = b0 + threadIdx.x;
+  for (; i + (U - 1) * 256 < b1; i += U * 256) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = src[i + u * 256];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  for (; i < b1; i += 256) {
+    const u32x4 a = src[i];
+    x ^= a[0] ^ a[1] ^ a[2] ^ a[3];
+  }
+#pragma unroll
+  for (int msk = 32; msk > 0; msk >>= 1) x ^= __shfl_xor(x, msk);
+  if ((threadIdx.x & 63) == 0) sink[blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6)] = x;
+}
+
+int stream_read_blocks() { return 16 * num_cus(); }
+size_t stream_read_sink_words() { return (size_t)stream_read_blocks() * 4; }
+
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int blocks, hipStream_t stream,
+                              const ProfileEvents& ev) {
+  ev.before(stream);
+  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<const u32x4*>(buf), bytes / 16, sink);
+  ev.after(stream);
+  return hipGetLastError();
+}
+
 }  // namespace tq

@@ -210,6 +210,15 @@ tq_status tq_score_scan(const tq_handle* h, const void* q, tq_dtype q_dt, int32_
  * Events are caller-created (hipEventCreate) and caller-owned; NULL, NULL clears. */
 tq_status tq_set_profile_events(hipEvent_t start, hipEvent_t stop);
 
+/* Measurement support: enqueue a streaming read of buf[0, bytes) (device memory, 16-byte
+ * aligned, bytes a multiple of 16) that folds the data into sink (device uint32, at least
+ * 64 x the device's compute-unit count words: one per wave, their XOR is the XOR of every
+ * 32-bit word of the buffer).  The bench times it with
+ * tq_set_profile_events to obtain its own HBM read ceiling.  Nothing else in the library
+ * depends on it. */
+tq_status tq_stream_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words,
+                         hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
