@@ -403,6 +403,40 @@ def test_select_then_gather_attention():
     _close(out.cpu().numpy(), ref, "gather attention")
 
 
+@pytest.mark.parametrize("kb,vb", [(4, 4), (2, 2)])
+def test_sparse_with_exact_sinks(kb, vb):
+    """Self-Indexing decode with 64 full-precision sink tokens always attended (as the exact
+    segment, outside the compressed and indexed range) and top-k gather over the rest, for the
+    4-bit payload and the 2-bit variant."""
+    base = W.small(W.WORKLOADS["sparse_128k_top2048"], tokens=5000, batch=2, top_k=300)
+    w = W.Workload(**{**base.__dict__, "key_bits": kb, "value_bits": vb})
+    h = _handle(w)
+    codec = _codec(h)
+    K, V = W.make_kv(w, "cuda")
+    B, T, H, d = K.shape
+    S = 64
+    Kc, Vc = K[:, S:].contiguous(), V[:, S:].contiguous()       # compressed + indexed: tokens S..T-1
+    sinks_k = K[:, :S].permute(0, 2, 1, 3).contiguous()          # exact: [B, H, S, d]
+    sinks_v = V[:, :S].permute(0, 2, 1, 3).contiguous()
+    index = torch.empty((B, H, T - S, d // 8), dtype=torch.uint8, device="cuda")
+    book = torch.empty((B, H, d // 4, 16, 4), device="cuda")
+    h.build_sign_index(Kc, index, book)
+    rec = _compress(w, h, Kc, Vc)
+    q = W.make_queries(w, "cuda")
+    lens = [T - S, 3000]
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    hl = torch.tensor([S, S], dtype=torch.int32, device="cuda")
+    sel, cnt = h.select_topk(q, index, book, sl, w.top_k)
+    out = torch.full((B, w.q_heads, d), float("nan"), device="cuda")
+    h.decode_attention(q, rec, sl, hot_k=sinks_k, hot_v=sinks_v, hot_lens=hl, sel_idx=sel, out=out)
+    torch.cuda.synchronize()
+    ri, rc, _ = O.select_topk(codec, _np(q), index.cpu().numpy(), book.cpu().numpy(), lens, w.top_k)
+    assert np.array_equal(sel.cpu().numpy(), ri) and np.array_equal(cnt.cpu().numpy(), rc)
+    ref, _, _ = O.decode_attention(codec, _np(q), rec.cpu().numpy(), lens, _np(sinks_k), _np(sinks_v), [S, S],
+                                   sel_idx=ri)
+    _close(out.cpu().numpy(), ref, f"sparse + sinks kb={kb} vb={vb}")
+
+
 # ------------------------------------------------------------------ bulk scan -----------
 def test_score_scan_reduced():
     w = W.small(W.WORKLOADS["bulk_64k_scan"], tokens=1000, scan_queries=70)
