@@ -31,7 +31,7 @@ EXPORTED = [
     "tq_compress_kv", "tq_debug_quantize", "tq_decode_workspace_size", "tq_decode_attention",
     "tq_index_workspace_size", "tq_build_sign_index", "tq_select_workspace_size",
     "tq_select_topk", "tq_scan_workspace_size", "tq_score_scan", "tq_set_profile_events",
-    "tq_stream_read",
+    "tq_stream_read", "tq_monarch_workspace_size", "tq_monarch_step",
 ]
 
 
@@ -39,6 +39,19 @@ class TqConfig(ctypes.Structure):
     _fields_ = [("head_dim", ctypes.c_int32), ("key_bits", ctypes.c_int32),
                 ("qjl_dim", ctypes.c_int32), ("value_bits", ctypes.c_int32),
                 ("rotation_seed", ctypes.c_uint64), ("qjl_seed", ctypes.c_uint64)]
+
+
+class MonarchConfig(ctypes.Structure):
+    _fields_ = [("window", ctypes.c_int32), ("cold_gate", ctypes.c_float),
+                ("promote_weight", ctypes.c_float), ("promote_steps", ctypes.c_int32)]
+
+
+class MonarchState(ctypes.Structure):
+    _fields_ = [("hot_k", ctypes.c_void_p), ("hot_v", ctypes.c_void_p), ("hot_dt", ctypes.c_int),
+                ("hot_capacity", ctypes.c_int64), ("hot_start", ctypes.c_void_p),
+                ("hot_len", ctypes.c_void_p), ("records", ctypes.c_void_p),
+                ("cold_capacity", ctypes.c_int64), ("cold_len", ctypes.c_void_p),
+                ("hits", ctypes.c_void_p), ("overflow", ctypes.c_void_p)]
 
 
 class TqError(RuntimeError):
@@ -81,6 +94,9 @@ _scan_ws = _sig("tq_scan_workspace_size", _P, _I32, _I32, _I32, _PSZ)
 _scan = _sig("tq_score_scan", _P, _P, ctypes.c_int, _I32, _I32, _I32, _P, _I64, _I64, _P, _P, _SZ, _P)
 _set_events = _sig("tq_set_profile_events", _P, _P)
 _stream_read = _sig("tq_stream_read", _P, _SZ, _P, _SZ, _P)
+_monarch_ws = _sig("tq_monarch_workspace_size", _P, _I32, _I32, _I32, _I64, _I64, _PSZ)
+_monarch_step = _sig("tq_monarch_step", _P, ctypes.POINTER(MonarchConfig), ctypes.POINTER(MonarchState), _P,
+                     ctypes.c_int, _I32, _I32, _I32, _P, _P, _F, _P, _P, _P, _P, _SZ, _P)
 
 
 def set_profile_events(start, stop):
@@ -264,3 +280,53 @@ class Handle:
         check(_scan(self._h, _ptr(q), _dtype_code(q), B, H, nq, _ptr(records), records.shape[2], n_tokens,
                     _ptr(scores), _ptr(workspace), workspace.numel(), _stream(stream)))
         return scores
+
+
+class HotCold:
+    """Device state of the hot/cold step: the exact ring and the compressed cold region of
+    every sequence (tensors owned here, laid out as tq_monarch_state describes)."""
+
+    def __init__(self, handle, batch, kv_heads, hot_capacity, cold_capacity, dtype, device="cuda"):
+        import torch
+        d = handle.head_dim
+        self.hot_k = torch.zeros((batch, kv_heads, hot_capacity, d), dtype=dtype, device=device)
+        self.hot_v = torch.zeros_like(self.hot_k)
+        self.hot_start = torch.zeros((batch,), dtype=torch.int32, device=device)
+        self.hot_len = torch.zeros((batch,), dtype=torch.int32, device=device)
+        self.records = handle.new_cache(batch, kv_heads, cold_capacity, device)
+        self.cold_len = torch.zeros((batch,), dtype=torch.int32, device=device)
+        self.hits = torch.zeros((batch, max(cold_capacity, 1)), dtype=torch.int32, device=device)
+        self.overflow = torch.zeros((batch,), dtype=torch.int32, device=device)
+
+    def c_state(self):
+        return MonarchState(self.hot_k.data_ptr(), self.hot_v.data_ptr(), _dtype_code(self.hot_k),
+                            self.hot_k.shape[2], self.hot_start.data_ptr(), self.hot_len.data_ptr(),
+                            self.records.data_ptr(), self.records.shape[2], self.cold_len.data_ptr(),
+                            self.hits.data_ptr(), self.overflow.data_ptr())
+
+
+def _monarch_ws_size(h, batch, q_heads, kv_heads, hot_cap, cold_cap) -> int:
+    n = ctypes.c_size_t()
+    check(_monarch_ws(h._h, batch, q_heads, kv_heads, hot_cap, cold_cap, ctypes.byref(n)))
+    return n.value
+
+
+def monarch_step(h, state, q, k_new, v_new, window, cold_gate=float("inf"), promote_weight=0.15,
+                 promote_steps=3, scale=0.0, out=None, lse=None, gate_out=None, workspace=None, stream=None):
+    """One hot/cold decode step (tq_monarch_step) on `state` (a HotCold); q [batch, q_heads, d],
+    k_new / v_new [batch, kv_heads, d] in the state's hot dtype.  Returns out [batch, q_heads, d]."""
+    import torch
+    B, Hq, d = q.shape
+    Hkv = k_new.shape[1]
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = _workspace(_monarch_ws_size(h, B, Hq, Hkv, state.hot_k.shape[2], state.records.shape[2]),
+                               q.device)
+    cfg = MonarchConfig(window, cold_gate, promote_weight, promote_steps)
+    st = state.c_state()
+    check(_monarch_step(h._h, ctypes.byref(cfg), ctypes.byref(st), _ptr(q), _dtype_code(q), B, Hq, Hkv,
+                        _ptr(k_new), _ptr(v_new), scale, _ptr(out), _ptr(lse), _ptr(gate_out), _ptr(workspace),
+                        workspace.numel(), _stream(stream)))
+    return out
+

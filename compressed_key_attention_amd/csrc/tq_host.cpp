@@ -293,6 +293,91 @@ tq_status tq_set_profile_events(hipEvent_t start, hipEvent_t stop) {
   return ok();
 }
 
+tq_status tq_monarch_workspace_size(const tq_handle* h, int32_t batch, int32_t q_heads, int32_t kv_heads,
+                                    int64_t hot_capacity, int64_t cold_capacity, size_t* bytes) {
+  if (!h || !bytes) return fail(TQ_ERR_INVALID_ARGUMENT, "NULL handle or output");
+  if (batch < 0 || q_heads <= 0 || kv_heads <= 0 || q_heads % kv_heads || hot_capacity <= 0 || cold_capacity < 0)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "bad hot/cold shape");
+  bool okp = false;
+  tq::MonarchPlan plan = tq::plan_monarch(h->c, batch, q_heads, kv_heads, hot_capacity, cold_capacity, &okp);
+  if (!okp) return fail(TQ_ERR_UNSUPPORTED, "group size %d not supported", q_heads / kv_heads);
+  *bytes = plan.ws_total;
+  return ok();
+}
+
+tq_status tq_monarch_step(const tq_handle* h, const tq_monarch_config* cfg, const tq_monarch_state* st,
+                          const void* q, tq_dtype q_dt, int32_t batch, int32_t q_heads, int32_t kv_heads,
+                          const void* k_new, const void* v_new, float scale, float* out, float* lse,
+                          int32_t* gate_out, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!h || !cfg || !st) return fail(TQ_ERR_INVALID_ARGUMENT, "handle, config or state is NULL");
+  size_t es, hs;
+  if (!elem_size(q_dt, &es)) return fail(TQ_ERR_INVALID_ARGUMENT, "unknown query dtype");
+  if (!elem_size(st->hot_dt, &hs)) return fail(TQ_ERR_INVALID_ARGUMENT, "unknown hot dtype");
+  if (batch < 0 || q_heads <= 0 || kv_heads <= 0 || q_heads % kv_heads)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "q_heads must be a positive multiple of kv_heads");
+  if (q_heads / kv_heads > 16 || q_heads > 64)
+    return fail(TQ_ERR_UNSUPPORTED, "hot/cold step supports up to 16 query heads per KV head and 64 per sequence");
+  if (!(scale >= 0.0f) || std::isinf(scale)) return fail(TQ_ERR_INVALID_ARGUMENT, "scale must be finite and >= 0");
+  if (cfg->window < 0 || cfg->promote_steps < 0 || std::isnan(cfg->cold_gate))
+    return fail(TQ_ERR_INVALID_ARGUMENT, "window and promote_steps must be >= 0, cold_gate not NaN");
+  int64_t promote_max = 0;
+  if (cfg->promote_steps > 0) {
+    if (!(cfg->promote_weight > 0.0f) || std::isinf(cfg->promote_weight))
+      return fail(TQ_ERR_INVALID_ARGUMENT, "promote_weight must be > 0 and finite when promotion is on");
+    // a head's weights sum to 1, so at most floor(1 / w) of its tokens reach w
+    promote_max = (int64_t)std::floor(1.0 / (double)cfg->promote_weight) * q_heads;
+    if (promote_max > 1024) return fail(TQ_ERR_UNSUPPORTED, "more than 1024 possible promotions per step");
+    promote_max = std::min<int64_t>(promote_max, st->cold_capacity);
+  }
+  if (st->hot_capacity < (int64_t)cfg->window + 1 + promote_max)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "hot_capacity must be >= window + 1 + %lld possible promotions",
+                (long long)promote_max);
+  if (st->cold_capacity < 0) return fail(TQ_ERR_INVALID_ARGUMENT, "negative cold_capacity");
+  if (batch == 0) return ok();
+  if (!q || !out || !k_new || !v_new || !st->hot_k || !st->hot_v || !st->hot_start || !st->hot_len ||
+      !st->cold_len || !st->hits || !st->overflow || (st->cold_capacity > 0 && !st->records))
+    return fail(TQ_ERR_INVALID_ARGUMENT, "NULL input, output or state buffer");
+  if (!aligned(st->hot_k, hs * 8) || !aligned(st->hot_v, hs * 8) || !aligned(k_new, hs * 8) ||
+      !aligned(v_new, hs * 8))
+    return fail(TQ_ERR_INVALID_ARGUMENT, "hot buffers and k_new / v_new must be aligned to 8 elements");
+  if (st->records && !aligned(st->records, 16)) return fail(TQ_ERR_INVALID_ARGUMENT, "records not 16-byte aligned");
+  bool okp = false;
+  tq::MonarchPlan plan = tq::plan_monarch(h->c, batch, q_heads, kv_heads, st->hot_capacity, st->cold_capacity, &okp);
+  if (!okp) return fail(TQ_ERR_UNSUPPORTED, "group size %d not supported", q_heads / kv_heads);
+  if (!workspace || ws_bytes < plan.ws_total || !aligned(workspace, 256))
+    return fail(TQ_ERR_WORKSPACE_TOO_SMALL, "hot/cold step needs %zu bytes of 256-byte aligned workspace",
+                plan.ws_total);
+  tq::MonarchStep s;
+  s.q = q;
+  s.q_dt = q_dt;
+  s.k_new = k_new;
+  s.v_new = v_new;
+  s.hot_k = st->hot_k;
+  s.hot_v = st->hot_v;
+  s.hot_dt = st->hot_dt;
+  s.hot_cap = st->hot_capacity;
+  s.cold_cap = st->cold_capacity;
+  s.hot_start = st->hot_start;
+  s.hot_len = st->hot_len;
+  s.records = st->records;
+  s.cold_len = st->cold_len;
+  s.hits = st->hits;
+  s.overflow = st->overflow;
+  s.out = out;
+  s.lse = lse;
+  s.gate_out = gate_out;
+  s.batch = batch;
+  s.q_heads = q_heads;
+  s.kv_heads = kv_heads;
+  s.window = cfg->window;
+  s.promote_steps = cfg->promote_steps;
+  s.cold_gate = cfg->cold_gate;
+  s.promote_weight = cfg->promote_weight;
+  s.scale = scale;
+  return device_status(tq::launch_monarch_step(h->c, h->dc, plan, s, workspace, stream, take_events()),
+                       "hot/cold step launch");
+}
+
 tq_status tq_stream_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words, hipStream_t stream) {
   if (!buf || !sink) return fail(TQ_ERR_INVALID_ARGUMENT, "NULL buffer or sink");
   if (!aligned(buf, 16) || bytes % 16) return fail(TQ_ERR_INVALID_ARGUMENT, "buffer must be 16-byte aligned and sized");

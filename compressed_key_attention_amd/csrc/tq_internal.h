@@ -76,6 +76,13 @@ struct DecodePlan {
 bool plan_decode(const Consts& c, int batch, int q_heads, int kv_heads, int64_t n_max,
                  DecodePlan* plan);
 
+// Extra inputs of a decode inside a hot/cold step: per-head gates and a ring-buffered hot
+// region holding hot_lens[b] + hot_add tokens from slot hot_start[b].
+struct DecodeHooks {
+  const int32_t* gate;       // [B][Hq]
+  const int32_t* hot_start;  // [B]
+  int hot_add;
+};
 hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan& plan,
                          const void* q, tq_dtype q_dt, int batch, int q_heads, int kv_heads,
                          const void* records, int64_t capacity, const int32_t* seq_lens,
@@ -83,7 +90,7 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
                          const int32_t* hot_lens, int64_t hot_capacity,
                          const int32_t* sel_idx, int k_sel, float scale, float* out, float* lse,
                          float* logits, void* workspace, hipStream_t stream,
-                         const ProfileEvents& ev);
+                         const ProfileEvents& ev, const DecodeHooks* hooks = nullptr);
 
 struct IndexPlan {
   int chunk, n_chunks;
@@ -122,5 +129,38 @@ int stream_read_blocks();          // workgroups of the streaming read (256 thre
 size_t stream_read_sink_words();   // one word per wave
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int blocks, hipStream_t stream,
                               const ProfileEvents& ev);
+
+// Hot/cold step (tq_monarch_step).
+struct MonarchPlan {
+  DecodePlan decode;
+  int64_t logit_stride;
+  size_t ws_decode, ws_gate, ws_lse, ws_logits, ws_counts, ws_total;
+};
+struct MonarchStep {
+  const void* q;
+  tq_dtype q_dt;
+  const void* k_new;
+  const void* v_new;
+  void* hot_k;
+  void* hot_v;
+  tq_dtype hot_dt;
+  int64_t hot_cap, cold_cap;
+  int32_t* hot_start;
+  int32_t* hot_len;
+  void* records;
+  int32_t* cold_len;
+  int32_t* hits;
+  int32_t* overflow;
+  float* out;
+  float* lse;
+  int32_t* gate_out;
+  int batch, q_heads, kv_heads, window, promote_steps;
+  float cold_gate, promote_weight, scale;
+};
+MonarchPlan plan_monarch(const Consts& c, int batch, int q_heads, int kv_heads, int64_t hot_cap,
+                         int64_t cold_cap, bool* ok);
+hipError_t launch_monarch_step(const Consts& c, const DevConsts& dc, const MonarchPlan& plan,
+                               const MonarchStep& s, void* workspace, hipStream_t stream,
+                               const ProfileEvents& ev);
 
 }  // namespace tq

@@ -531,6 +531,7 @@ struct DecodeArgs {
   const uint8_t* records;
   const int32_t* seq_lens;
   const int32_t* sel_idx;
+  const int32_t* gate;    // [B][Hq] nonzero: the head reads the cold tokens (NULL: all do)
   float* part;
   float* logits;
   int64_t capacity, logit_stride;
@@ -564,6 +565,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_scan_kernel(DecodeArgs 
   float* gam_v = lut_s + NHG * sgrp * sent * HPL;               // [16]
 
   const int64_t qrow0 = ((int64_t)b * A.q_heads + (int64_t)hkv * G);  // first query head row
+  if (A.gate) {            // no head of the group reads the cold tokens: the merge ignores them
+    bool any = false;
+    for (int j = 0; j < G; ++j) any = any || A.gate[qrow0 + j] != 0;
+    if (!any) return;
+  }
   // ---- LUT build: one thread per table row (head group, table, head), whose one or two query
   // coordinates are loaded once; the row's entries are then written from registers ----
   {
@@ -1076,6 +1082,8 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = blockIdx.z, hkv = blockIdx.y, chunk = blockIdx.x;
   const int64_t qrow0 = (int64_t)b * A.q_heads + (int64_t)hkv * G;
+  if (A.gate && !(A.gate[qrow0] | A.gate[qrow0 + 1] | A.gate[qrow0 + 2] | A.gate[qrow0 + 3]))
+    return;                // no head of the group reads the cold tokens: the merge ignores them
 
   if (threadIdx.x < 16) vtab[threadIdx.x] = bf16_pair(A.val_levels[threadIdx.x]);
   if (threadIdx.x < 4) wzero[threadIdx.x] = 0u;
@@ -1380,6 +1388,9 @@ struct MergeArgs {
   const void* hot_v;
   tq_dtype hot_dt;
   const int32_t* hot_lens;
+  const int32_t* hot_start;   // ring start of each sequence's hot tokens (NULL: slot t = token t)
+  const int32_t* gate;        // [B][Hq] nonzero: the head's cold partials count (NULL: all do)
+  int hot_add;                // tokens appended past hot_lens in this step (ring mode)
   int64_t hot_capacity, logit_hot_off, logit_stride;
   float* out;
   float* lse;
@@ -1405,6 +1416,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs A
   const int64_t row = (int64_t)b * A.q_heads + hq;
   constexpr int stride = D + 2;
   const float* pr = A.part + row * A.n_chunks * stride;
+  const int n_chunks = (A.gate && A.gate[row] == 0) ? 0 : A.n_chunks;   // gated: hot tokens only
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // block-wide max / sum: wave shuffles, then one LDS word per wave
   auto block_reduce = [&](float v, bool is_max) {
@@ -1423,8 +1435,14 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs A
   for (int i = threadIdx.x; i < D; i += blockDim.x) qv[i] = load_elem(A.q, A.q_dt, row * D + i);
   // global max over chunk partials and hot logits
   float mx = kNegInf;
-  for (int c = threadIdx.x; c < A.n_chunks; c += blockDim.x) mx = fmaxf(mx, pr[(int64_t)c * stride]);
-  const int nh = A.hot_lens ? (int)min((int64_t)A.hot_lens[b], A.hot_capacity) : 0;
+  for (int c = threadIdx.x; c < n_chunks; c += blockDim.x) mx = fmaxf(mx, pr[(int64_t)c * stride]);
+  const int nh = A.hot_lens ? (int)min((int64_t)A.hot_lens[b] + A.hot_add, A.hot_capacity) : 0;
+  const int64_t hs0 = A.hot_start ? A.hot_start[b] : 0;
+  // ring slot of hot token t
+  auto hslot = [&](int t) -> int64_t {
+    const int64_t s = hs0 + t;
+    return s >= A.hot_capacity ? s - A.hot_capacity : s;
+  };
   const int64_t hbase = ((int64_t)b * A.kv_heads + hkv) * A.hot_capacity * D;
   const int sub = lane % LPK, slot = wave * TPWK + lane / LPK;
   __syncthreads();
@@ -1434,7 +1452,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs A
   // logit of hot token t: the LPK lanes of its slot each take 8 coordinates, then a shuffle sum
   auto hot_logit = [&](int t) {
     float kv[8];
-    load8(A.hot_k, A.hot_dt, hbase + (int64_t)min(t, nh - 1) * D + 8 * sub, kv);
+    load8(A.hot_k, A.hot_dt, hbase + hslot(min(t, nh - 1)) * D + 8 * sub, kv);
     float dot = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) dot = fmaf(q8[i], kv[i], dot);
@@ -1457,13 +1475,13 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs A
   // sum of weights and the cold rotated-domain output (loads unconditional, weight 0 for an
   // empty chunk, whose partial holds zeros)
   float l = 0.0f;
-  for (int c = threadIdx.x; c < A.n_chunks; c += blockDim.x) {
+  for (int c = threadIdx.x; c < n_chunks; c += blockDim.x) {
     const float mc = pr[(int64_t)c * stride];
     l += (M != kNegInf && mc != kNegInf) ? pr[(int64_t)c * stride + 1] * __expf(mc - M) : 0.0f;
   }
   for (int i = threadIdx.x; i < D; i += blockDim.x) {
     float acc = 0.0f;
-    for (int c = 0; c < A.n_chunks; ++c) {
+    for (int c = 0; c < n_chunks; ++c) {
       const float mc = pr[(int64_t)c * stride];
       const float wgt = (M != kNegInf && mc != kNegInf) ? __expf(mc - M) : 0.0f;
       acc = fmaf(pr[(int64_t)c * stride + 2 + i], wgt, acc);
@@ -1482,7 +1500,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs A
     const float p = t < nh ? __expf(lg - M) : 0.0f;
     if (sub == 0) l += p;
     float vv[8];
-    load8(A.hot_v, A.hot_dt, hbase + (int64_t)min(t, nh - 1) * D + 8 * sub, vv);
+    load8(A.hot_v, A.hot_dt, hbase + hslot(min(t, nh - 1)) * D + 8 * sub, vv);
 #pragma unroll
     for (int i = 0; i < 8; ++i) oh8[i] = fmaf(p, vv[i], oh8[i]);
   }
@@ -1609,7 +1627,7 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
                          const void* hot_v, tq_dtype hot_dt, const int32_t* hot_lens,
                          int64_t hot_capacity, const int32_t* sel_idx, int k_sel, float scale,
                          float* out, float* lse, float* logits, void* workspace,
-                         hipStream_t stream, const ProfileEvents& ev) {
+                         hipStream_t stream, const ProfileEvents& ev, const DecodeHooks* hooks) {
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   float* qx = reinterpret_cast<float*>(ws + plan.ws_qx);
   float* qs = reinterpret_cast<float*>(ws + plan.ws_qs);
@@ -1634,6 +1652,7 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
   a.records = static_cast<const uint8_t*>(records);
   a.seq_lens = seq_lens;
   a.sel_idx = sel_idx;
+  a.gate = hooks ? hooks->gate : nullptr;
   a.part = part;
   a.logits = logits;
   a.capacity = capacity;
@@ -1678,6 +1697,9 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
   mg.hot_v = hot_v;
   mg.hot_dt = hot_dt;
   mg.hot_lens = hot_lens;
+  mg.hot_start = hooks ? hooks->hot_start : nullptr;
+  mg.gate = hooks ? hooks->gate : nullptr;
+  mg.hot_add = hooks ? hooks->hot_add : 0;
   mg.hot_capacity = hot_capacity;
   mg.logit_hot_off = n_cold;
   mg.logit_stride = lstride;
@@ -2796,6 +2818,417 @@ hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int
   hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                      static_cast<const u32x4*>(buf), bytes / 16, sink);
   ev.after(stream);
+  return hipGetLastError();
+}
+
+// =========================================================================================
+// Hot/cold step (Monarch v3 page, "Wie es funktioniert" and its decode loop): recent tokens
+// exact in a per-sequence ring, older ones compressed; a query head reads the cold region only
+// when its best hot logit is below a gate; cold tokens that keep a large attention weight for
+// several consecutive steps are decompressed back into the ring (page swap); the ring keeps a
+// sliding window and compresses its oldest tokens into the cold region.
+//   monarch_prep_kernel     append the step's token to the ring, per-head gates
+//   (decode)                cold scan (skipped for fully gated KV-head groups) + merge
+//   monarch_promote_kernel  sticky counters, dequantize promoted tokens into the ring,
+//                           swap-remove them from the cold region
+//   monarch_evict_kernel    compress the ring's oldest tokens past the window (float64) and
+//                           commit the new state
+// =========================================================================================
+constexpr int kMonarchMaxHeads = 64;      // query heads per sequence in the promotion kernel
+constexpr int kMonarchMaxPromote = 1024;  // promotions per sequence and step
+
+struct MonarchArgs {
+  Consts c;
+  const float* pi;        // [d][d]
+  const float* pi_t;      // [d][d] transposed
+  const float* s;         // [m][d]
+  const void* q;
+  tq_dtype q_dt;
+  const void* k_new;
+  const void* v_new;
+  void* hot_k;
+  void* hot_v;
+  tq_dtype hot_dt;
+  int64_t hot_cap, cold_cap, logit_stride;
+  int32_t* hot_start;
+  int32_t* hot_len;
+  uint8_t* records;
+  int32_t* cold_len;
+  int32_t* hits;
+  int32_t* overflow;
+  int32_t* gate;          // [B][Hq]
+  const float* logits;    // [B][Hq][logit_stride] cold logits of the step
+  const float* lse;       // [B][Hq]
+  int32_t* promo_count;   // [B] (workspace)
+  int32_t* cold_after;    // [B] (workspace)
+  int32_t* gate_out;      // [B][Hq] copy of the gates for the caller (NULL: none)
+  int batch, q_heads, kv_heads, G, window, promote_steps;
+  float cold_gate, promote_weight, scale;
+};
+
+__device__ __forceinline__ void copy_elem(void* dst, const void* src, tq_dtype dt, int64_t di, int64_t si) {
+  if (dt == TQ_F32) static_cast<float*>(dst)[di] = static_cast<const float*>(src)[si];
+  else static_cast<uint16_t*>(dst)[di] = static_cast<const uint16_t*>(src)[si];
+}
+
+// float64 -> float32 rounded to odd (toward zero, low bit set when inexact): a following
+// round-to-nearest-even to bf16 / f16 then equals the correctly rounded float64 value.
+__device__ __forceinline__ float f64_to_f32_odd(double x) {
+  float f = __double2float_rz(x);
+  if ((double)f != x) f = __uint_as_float(__float_as_uint(f) | 1u);
+  return f;
+}
+__device__ __forceinline__ void store_f64(void* base, tq_dtype dt, int64_t off, double x) {
+  if (dt == TQ_F32) {
+    static_cast<float*>(base)[off] = (float)x;
+  } else if (dt == TQ_BF16) {
+    const uint32_t u = __float_as_uint(f64_to_f32_odd(x));
+    static_cast<uint16_t*>(base)[off] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+  } else {
+    static_cast<uint16_t*>(base)[off] = __builtin_bit_cast(uint16_t, (_Float16)f64_to_f32_odd(x));
+  }
+}
+
+// Code j of a packed code field (3-bit: the 32-code group layout; 2/4-bit: bitstream).
+__device__ __forceinline__ uint32_t field_code(const uint8_t* field, int j, int bits) {
+  if (bits == 3) {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(field + 12 * (j >> 5));
+    return group3_code(w[0], w[1], w[2], j & 31);
+  }
+  const int pos = j * bits;
+  return (field[pos >> 3] >> (pos & 7)) & ((1u << bits) - 1u);
+}
+
+// One record from its codes, sign bits and norms (the layout compress_kernel writes).
+__device__ void pack_record(const Consts& c, const uint32_t* ck, const uint32_t* bits, const uint32_t* cv,
+                            float rk, float rho, float rv, uint8_t* rec) {
+  auto put = [&](uint8_t* field, const uint32_t* codes, int nbits) {
+    if (nbits == 3) {
+      for (int gi = 0; gi < c.d / 32; ++gi) {
+        uint32_t w[3] = {0u, 0u, 0u};
+        for (int j = 0; j < 32; ++j) group3_put(w, j, codes[32 * gi + j]);
+        uint32_t* dst = reinterpret_cast<uint32_t*>(field + 12 * gi);
+        dst[0] = w[0];
+        dst[1] = w[1];
+        dst[2] = w[2];
+      }
+    } else {
+      ByteWriter w{field, 0, 0};
+      for (int i = 0; i < c.d; ++i) w.put(codes[i], nbits);
+    }
+  };
+  put(rec, ck, c.kb);
+  ByteWriter ws{rec + c.kbytes, 0, 0};
+  for (int j = 0; j < c.m; ++j) ws.put(bits[j], 1);
+  put(rec + c.kbytes + c.sbytes, cv, c.vb);
+  float* nrm = reinterpret_cast<float*>(rec + c.norm_off);
+  nrm[0] = rk;
+  nrm[1] = rho;
+  nrm[2] = rv;
+  for (int i = c.norm_off + 12; i < c.rec_bytes; ++i) rec[i] = 0;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void monarch_prep_kernel(MonarchArgs M) {
+  __shared__ float qv[16][D];
+  __shared__ float red[4][16];
+  const int hkv = blockIdx.x, b = blockIdx.y, G = M.G;
+  const int64_t unit = (int64_t)b * M.kv_heads + hkv;
+  const int n = M.hot_len[b];
+  const int64_t st = M.hot_start[b];
+  int64_t slot = st + n;
+  if (slot >= M.hot_cap) slot -= M.hot_cap;
+  for (int i = threadIdx.x; i < D; i += blockDim.x) {
+    copy_elem(M.hot_k, M.k_new, M.hot_dt, (unit * M.hot_cap + slot) * D + i, unit * D + i);
+    copy_elem(M.hot_v, M.v_new, M.hot_dt, (unit * M.hot_cap + slot) * D + i, unit * D + i);
+  }
+  const int64_t qrow0 = (int64_t)b * M.q_heads + (int64_t)hkv * G;
+  for (int e = threadIdx.x; e < G * D; e += blockDim.x) qv[e / D][e % D] = load_elem(M.q, M.q_dt, qrow0 * D + e);
+  __syncthreads();
+  // best hot logit per head over the ring's tokens and the step's token (read from k_new)
+  float mx[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) mx[j] = kNegInf;
+  for (int t = threadIdx.x; t <= n; t += blockDim.x) {
+    int64_t rs = st + t;
+    if (rs >= M.hot_cap) rs -= M.hot_cap;
+    const void* src = t < n ? M.hot_k : M.k_new;
+    const int64_t off = t < n ? (unit * M.hot_cap + rs) * D : unit * D;
+    float dot[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) dot[j] = 0.0f;
+    for (int c8 = 0; c8 < D; c8 += 8) {
+      float kv[8];
+      load8(src, M.hot_dt, off + c8, kv);
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (j < G)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) dot[j] = fmaf(qv[j][c8 + i], kv[i], dot[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) mx[j] = fmaxf(mx[j], M.scale * dot[j]);
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    float v = mx[j];
+#pragma unroll
+    for (int msk = 32; msk > 0; msk >>= 1) v = fmaxf(v, __shfl_xor(v, msk));
+    if (lane == 0) red[wave][j] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    float v = red[0][threadIdx.x];
+    for (int w2 = 1; w2 < 4; ++w2) v = fmaxf(v, red[w2][threadIdx.x]);
+    M.gate[qrow0 + threadIdx.x] = v < M.cold_gate ? 1 : 0;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(1024) void monarch_promote_kernel(MonarchArgs M) {
+  __shared__ float s_lse[kMonarchMaxHeads];
+  __shared__ int s_gate[kMonarchMaxHeads];
+  __shared__ int plist[kMonarchMaxPromote];
+  __shared__ int moves[kMonarchMaxPromote][2];
+  __shared__ int wsum[16];
+  __shared__ int s_np;
+  __shared__ double lev[2][D];
+  const int b = blockIdx.x, Hq = M.q_heads;
+  const int n_cold = M.cold_len[b];
+  for (int h = threadIdx.x; h < Hq; h += blockDim.x) {
+    s_lse[h] = M.lse[(int64_t)b * Hq + h];
+    s_gate[h] = M.gate[(int64_t)b * Hq + h];
+    if (M.gate_out) M.gate_out[(int64_t)b * Hq + h] = s_gate[h];
+  }
+  if (threadIdx.x == 0) s_np = 0;
+  __syncthreads();
+  int32_t* hits = M.hits + (int64_t)b * M.cold_cap;
+  if (M.promote_steps > 0) {
+    for (int t0 = 0; t0 < n_cold; t0 += blockDim.x) {
+      const int t = t0 + threadIdx.x;
+      bool prom = false;
+      if (t < n_cold) {
+        float w = 0.0f;
+        for (int h = 0; h < Hq; ++h)
+          if (s_gate[h]) w = fmaxf(w, __expf(M.logits[((int64_t)b * Hq + h) * M.logit_stride + t] - s_lse[h]));
+        const int hc = w >= M.promote_weight ? hits[t] + 1 : 0;
+        prom = hc >= M.promote_steps;
+        hits[t] = prom ? 0 : hc;
+      }
+      int tot;
+      const int pos = block_exclusive_sum<1024>(prom ? 1 : 0, wsum, &tot);
+      if (prom && s_np + pos < kMonarchMaxPromote) plist[s_np + pos] = t;
+      __syncthreads();
+      if (threadIdx.x == 0) s_np = min(s_np + tot, kMonarchMaxPromote);
+      __syncthreads();
+    }
+  }
+  const int P = s_np;
+  // dequantize the promoted tokens (ascending cold index) into the ring after the step's token:
+  // k = Pi^T ((r_k / sqrt(d)) gamma_k[c]), v = Pi^T ((r_v / sqrt(d)) gamma_v[c_v]), float64
+  const Consts& c = M.c;
+  const int64_t st = M.hot_start[b], n_hot = (int64_t)M.hot_len[b] + 1;
+  for (int pi = 0; pi < P; ++pi) {
+    for (int h = 0; h < M.kv_heads; ++h) {
+      const int64_t unit = (int64_t)b * M.kv_heads + h;
+      const uint8_t* rec = M.records + (unit * M.cold_cap + plist[pi]) * c.rec_bytes;
+      const float* nrm = reinterpret_cast<const float*>(rec + c.norm_off);
+      for (int i = threadIdx.x; i < 2 * D; i += blockDim.x) {
+        if (i < D) lev[0][i] = ((double)nrm[0] / c.sqrt_d) * (double)c.key_levels[field_code(rec, i, c.kb)];
+        else lev[1][i - D] = ((double)nrm[2] / c.sqrt_d) *
+                             (double)c.val_levels[field_code(rec + c.kbytes + c.sbytes, i - D, c.vb)];
+      }
+      __syncthreads();
+      int64_t slot = st + n_hot + pi;
+      slot %= M.hot_cap;
+      for (int i = threadIdx.x; i < 2 * D; i += blockDim.x) {
+        const int which = i / D, o = i % D;
+        double acc = 0.0;
+        for (int j = 0; j < D; ++j) acc = fma((double)M.pi_t[o * D + j], lev[which][j], acc);
+        store_f64(which ? M.hot_v : M.hot_k, M.hot_dt, (unit * M.hot_cap + slot) * D + o, acc);
+      }
+      __syncthreads();
+    }
+  }
+  // swap-remove in descending index order: the current last cold token fills each hole
+  if (threadIdx.x == 0) {
+    int nc = n_cold;
+    for (int i = P - 1; i >= 0; --i) {
+      const int p = plist[i], last = nc - 1;
+      moves[i][0] = last;
+      moves[i][1] = p;
+      --nc;
+    }
+  }
+  __syncthreads();
+  // each thread owns the same 16-byte pieces of a token's records in every move (program order
+  // keeps the chain of moves consistent without cross-thread synchronisation)
+  const int pieces = M.kv_heads * (c.rec_bytes / 16);
+  for (int i = P - 1; i >= 0; --i) {
+    const int src = moves[i][0], dst = moves[i][1];
+    if (src == dst) continue;
+    for (int e = threadIdx.x; e < pieces; e += blockDim.x) {
+      const int h = e / (c.rec_bytes / 16), pc = e % (c.rec_bytes / 16);
+      const int64_t unit = (int64_t)b * M.kv_heads + h;
+      const u32x4* s4 = reinterpret_cast<const u32x4*>(M.records + (unit * M.cold_cap + src) * c.rec_bytes) + pc;
+      u32x4* d4 = reinterpret_cast<u32x4*>(M.records + (unit * M.cold_cap + dst) * c.rec_bytes) + pc;
+      *d4 = *s4;
+    }
+    if (threadIdx.x == 0) hits[dst] = hits[src];
+  }
+  if (threadIdx.x == 0) {
+    M.promo_count[b] = P;
+    M.cold_after[b] = n_cold - P;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void monarch_evict_kernel(MonarchArgs M) {
+  __shared__ double xd[D], kd[D], ed[D];
+  __shared__ double dred[256];
+  __shared__ uint32_t ck[D], cv[D], bits[256];
+  const int b = blockIdx.x;
+  const Consts& c = M.c;
+  const int64_t st = M.hot_start[b];
+  const int n_hot = M.hot_len[b] + 1 + M.promo_count[b];
+  const int e = max(0, n_hot - M.window);
+  const int c0 = M.cold_after[b];
+  const int es = (int)min((int64_t)e, M.cold_cap - c0);
+  auto block_sum = [&](double v) {
+    dred[threadIdx.x] = v;
+    __syncthreads();
+    for (int s2 = blockDim.x / 2; s2 > 0; s2 >>= 1) {
+      if (threadIdx.x < s2) dred[threadIdx.x] += dred[threadIdx.x + s2];
+      __syncthreads();
+    }
+    const double r = dred[0];
+    __syncthreads();
+    return r;
+  };
+  // Step 1 of the TurboQuant page ("Funktionsweise") on one vector in float64: r = |x|,
+  // y = Pi x, z = y sqrt(d) / r rounded to float32, codes against the float32 boundaries.
+  auto rotate_code = [&](const void* src, int64_t off, const float* bounds, uint32_t* codes) {
+    for (int i = threadIdx.x; i < D; i += blockDim.x) kd[i] = (double)load_elem(src, M.hot_dt, off + i);
+    __syncthreads();
+    const double r = sqrt(block_sum(threadIdx.x < D ? kd[threadIdx.x] * kd[threadIdx.x] : 0.0));
+    const double scale = r > 0.0 ? c.sqrt_d / r : 0.0;
+    for (int i = threadIdx.x; i < D; i += blockDim.x) {
+      double acc = 0.0;
+      for (int j = 0; j < D; ++j) acc = fma((double)M.pi[i * D + j], kd[j], acc);
+      xd[i] = acc;
+      codes[i] = quantize_code((float)(acc * scale), bounds);
+    }
+    __syncthreads();
+    return (float)r;
+  };
+  for (int i = 0; i < es; ++i) {
+    int64_t rs = st + i;
+    rs %= M.hot_cap;
+    for (int h = 0; h < M.kv_heads; ++h) {
+      const int64_t unit = (int64_t)b * M.kv_heads + h;
+      const int64_t off = (unit * M.hot_cap + rs) * D;
+      const float rk = rotate_code(M.hot_k, off, c.key_bounds, ck);
+      // residual in the rotated basis, its norm, and the QJL signs of S e
+      for (int j = threadIdx.x; j < D; j += blockDim.x)
+        ed[j] = xd[j] - ((double)rk / c.sqrt_d) * (double)c.key_levels[ck[j]];
+      __syncthreads();
+      const float rho = (float)sqrt(block_sum(threadIdx.x < D ? ed[threadIdx.x] * ed[threadIdx.x] : 0.0));
+      for (int j = threadIdx.x; j < c.m; j += blockDim.x) {
+        double acc = 0.0;
+        for (int k2 = 0; k2 < D; ++k2) acc = fma((double)M.s[j * D + k2], ed[k2], acc);
+        bits[j] = (float)acc >= 0.0f ? 1u : 0u;
+      }
+      __syncthreads();
+      const float rv = rotate_code(M.hot_v, off, c.val_bounds, cv);
+      if (threadIdx.x == 0) {
+        pack_record(c, ck, bits, cv, rk, rho, rv, M.records + (unit * M.cold_cap + c0 + i) * c.rec_bytes);
+      }
+      __syncthreads();
+    }
+  }
+  if (threadIdx.x == 0) {
+    int32_t* hits = M.hits + (int64_t)b * M.cold_cap;
+    for (int i = 0; i < es; ++i) hits[c0 + i] = 0;
+    M.hot_start[b] = (int32_t)((st + e) % M.hot_cap);
+    M.hot_len[b] = n_hot - e;
+    M.cold_len[b] = c0 + es;
+    if (es < e) M.overflow[b] = 1;
+  }
+}
+
+MonarchPlan plan_monarch(const Consts& c, int batch, int q_heads, int kv_heads, int64_t hot_cap,
+                         int64_t cold_cap, bool* ok) {
+  MonarchPlan p;
+  *ok = plan_decode(c, batch, q_heads, kv_heads, cold_cap, &p.decode);
+  const size_t rows = (size_t)std::max(batch, 1) * q_heads;
+  p.logit_stride = cold_cap + hot_cap;
+  p.ws_decode = 0;
+  p.ws_gate = align256(p.decode.ws_total);
+  p.ws_lse = p.ws_gate + align256(rows * 4);
+  p.ws_logits = p.ws_lse + align256(rows * 4);
+  p.ws_counts = p.ws_logits + align256(rows * (size_t)p.logit_stride * 4);
+  p.ws_total = p.ws_counts + align256((size_t)std::max(batch, 1) * 8);
+  return p;
+}
+
+hipError_t launch_monarch_step(const Consts& c, const DevConsts& dc, const MonarchPlan& plan,
+                               const MonarchStep& s, void* workspace, hipStream_t stream,
+                               const ProfileEvents& ev) {
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  MonarchArgs M;
+  M.c = c;
+  M.pi = dc.pi;
+  M.pi_t = dc.pi_t;
+  M.s = dc.s;
+  M.q = s.q;
+  M.q_dt = s.q_dt;
+  M.k_new = s.k_new;
+  M.v_new = s.v_new;
+  M.hot_k = s.hot_k;
+  M.hot_v = s.hot_v;
+  M.hot_dt = s.hot_dt;
+  M.hot_cap = s.hot_cap;
+  M.cold_cap = s.cold_cap;
+  M.logit_stride = plan.logit_stride;
+  M.hot_start = s.hot_start;
+  M.hot_len = s.hot_len;
+  M.records = static_cast<uint8_t*>(s.records);
+  M.cold_len = s.cold_len;
+  M.hits = s.hits;
+  M.overflow = s.overflow;
+  M.gate_out = s.gate_out;
+  M.gate = reinterpret_cast<int32_t*>(ws + plan.ws_gate);
+  float* lse = s.lse ? s.lse : reinterpret_cast<float*>(ws + plan.ws_lse);
+  float* logits = reinterpret_cast<float*>(ws + plan.ws_logits);
+  M.logits = logits;
+  M.lse = lse;
+  M.promo_count = reinterpret_cast<int32_t*>(ws + plan.ws_counts);
+  M.cold_after = M.promo_count + std::max(s.batch, 1);
+  M.batch = s.batch;
+  M.q_heads = s.q_heads;
+  M.kv_heads = s.kv_heads;
+  M.G = s.q_heads / s.kv_heads;
+  M.window = s.window;
+  M.promote_steps = s.promote_steps;
+  M.cold_gate = s.cold_gate;
+  M.promote_weight = s.promote_weight;
+  M.scale = s.scale > 0.0f ? s.scale : c.inv_sqrt_d;
+  const dim3 g1(s.kv_heads, s.batch);
+  if (c.d == 128) hipLaunchKernelGGL(monarch_prep_kernel<128>, g1, dim3(256), 0, stream, M);
+  else hipLaunchKernelGGL(monarch_prep_kernel<64>, g1, dim3(256), 0, stream, M);
+  DecodeHooks hk{M.gate, s.hot_start, 1};
+  hipError_t e = launch_decode(c, dc, plan.decode, s.q, s.q_dt, s.batch, s.q_heads, s.kv_heads, s.records,
+                               s.cold_cap, s.cold_len, s.hot_k, s.hot_v, s.hot_dt, s.hot_len, s.hot_cap,
+                               nullptr, 0, M.scale, s.out, lse, logits, ws + plan.ws_decode, stream, ev, &hk);
+  if (e != hipSuccess) return e;
+  if (c.d == 128) {
+    hipLaunchKernelGGL(monarch_promote_kernel<128>, dim3(s.batch), dim3(1024), 0, stream, M);
+    hipLaunchKernelGGL(monarch_evict_kernel<128>, dim3(s.batch), dim3(256), 0, stream, M);
+  } else {
+    hipLaunchKernelGGL(monarch_promote_kernel<64>, dim3(s.batch), dim3(1024), 0, stream, M);
+    hipLaunchKernelGGL(monarch_evict_kernel<64>, dim3(s.batch), dim3(256), 0, stream, M);
+  }
   return hipGetLastError();
 }
 

@@ -210,6 +210,59 @@ tq_status tq_score_scan(const tq_handle* h, const void* q, tq_dtype q_dt, int32_
  * Events are caller-created (hipEventCreate) and caller-owned; NULL, NULL clears. */
 tq_status tq_set_profile_events(hipEvent_t start, hipEvent_t stop);
 
+/* Hot/cold decode step (Monarch v3 page, "Wie es funktioniert" and its decode loop; the
+ * choices the page leaves open are stated here).  Per sequence b the state holds:
+ *  - a hot ring: hot_k/hot_v[b][h][hot_capacity][head_dim] in hot_dt, hot_len[b] exact tokens
+ *    from ring slot hot_start[b] (oldest first); hot_len[b] <= window before each step;
+ *  - a cold region: records[b][h][cold_capacity] (tq_compress_kv layout), cold_len[b] tokens,
+ *    hits[b][cold_capacity] consecutive qualifying steps per cold token, overflow[b] set to 1
+ *    once an eviction found the cold region full (those tokens were dropped).
+ * One step, for queries q[b][hq][d] and the step's token k_new/v_new[b][h][d] (hot_dt):
+ *  1. the step's token joins the ring (newest);
+ *  2. query head hq reads the cold tokens iff scale * max_t <q, k_t> over the ring is below
+ *     cfg->cold_gate (+inf: always); out / lse = attention over the ring plus, for open heads,
+ *     the cold tokens (TurboQuant estimator, as tq_decode_attention), one softmax;
+ *  3. a cold token whose weight p (maximum over the open heads) is >= cfg->promote_weight
+ *     counts one more consecutive step, else its count resets; at cfg->promote_steps (0: never)
+ *     it is promoted: k = Pi^T (r_k/sqrt(d)) gamma_k[c], v = Pi^T (r_v/sqrt(d)) gamma_v[c_v]
+ *     (float64, rounded to hot_dt) join the ring as its newest tokens in ascending cold order,
+ *     and the cold slots are freed by moving the last cold token into each, highest slot first;
+ *  4. while the ring holds more than cfg->window tokens, its oldest are compressed (float64
+ *     rotation, as tq_compress_kv) and appended to the cold region with count 0.
+ * hot_capacity must be >= window + 1 + floor(1 / promote_weight) * q_heads (when promotion is
+ * on).  gate_out (optional, [b][hq]) receives the step-2 decisions; lse is optional.
+ * workspace: tq_monarch_workspace_size bytes.  All state stays on the device; the host is
+ * never synchronised. */
+typedef struct {
+  int32_t window;          /* hot tokens kept per sequence after each step */
+  float cold_gate;         /* a head reads the cold tokens iff its best hot logit is below this */
+  float promote_weight;    /* attention weight a cold token needs in a step (e.g. 0.15) */
+  int32_t promote_steps;   /* consecutive such steps before promotion (e.g. 3; 0 = never) */
+} tq_monarch_config;
+
+typedef struct {
+  void* hot_k;
+  void* hot_v;
+  tq_dtype hot_dt;
+  int64_t hot_capacity;
+  int32_t* hot_start;
+  int32_t* hot_len;
+  void* records;
+  int64_t cold_capacity;
+  int32_t* cold_len;
+  int32_t* hits;
+  int32_t* overflow;
+} tq_monarch_state;
+
+tq_status tq_monarch_workspace_size(const tq_handle* h, int32_t batch, int32_t q_heads,
+                                    int32_t kv_heads, int64_t hot_capacity, int64_t cold_capacity,
+                                    size_t* bytes);
+tq_status tq_monarch_step(const tq_handle* h, const tq_monarch_config* cfg,
+                          const tq_monarch_state* state, const void* q, tq_dtype q_dt,
+                          int32_t batch, int32_t q_heads, int32_t kv_heads, const void* k_new,
+                          const void* v_new, float scale, float* out, float* lse,
+                          int32_t* gate_out, void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* Measurement support: enqueue a streaming read of buf[0, bytes) (device memory, 16-byte
  * aligned, bytes a multiple of 16) that folds the data into sink (device uint32, at least
  * 64 x the device's compute-unit count words: one per wave, their XOR is the XOR of every
