@@ -512,13 +512,96 @@ def cpu_baseline_scan(w, q, records, budget_s: float = 12.0):
                            f"4096-token blocks x {w.scan_queries} queries", budget_s)
 
 
+# ---------------------------------------------------------------------------------------------
+def run_monarch(args, tq, W, ev):
+    """Hot/cold decode steps on the TinyLlama-shaped layer: 512 exact fp16 tokens in the ring,
+    1,024 compressed cold tokens, one new token per step (so one eviction per step)."""
+    import torch
+    w = W.WORKLOADS["tinyllama_layer"]
+    dev = "cuda"
+    h = tq.Handle(w.head_dim, w.key_bits, w.qjl_dim, w.value_bits, w.seed * 3 + 1, w.seed * 3 + 2)
+    n_steps = args.warmup + args.steps + 20
+    window, Hq, H, d = w.hot_tokens, w.q_heads, w.kv_heads, w.head_dim
+    hot_cap = window + 1 + 6 * Hq
+    cold_cap = w.tokens + n_steps + 32
+    st = tq.HotCold(h, w.batch, H, hot_cap, cold_cap, torch.float16, dev)
+    K, V = W.make_kv(w, dev)
+    h.compress_kv(K, V, st.records)
+    hk, hv = W.make_hot(w, dev)
+    st.hot_k[:, :, :window].copy_(hk)
+    st.hot_v[:, :, :window].copy_(hv)
+    st.hot_len.fill_(window)
+    st.cold_len.fill_(w.tokens)
+    g = torch.Generator(device=dev).manual_seed(w.seed * 977 + 3)
+    qs = torch.randn((n_steps, w.batch, Hq, d), generator=g, device=dev).to(torch.float16)
+    ks = torch.randn((n_steps, w.batch, H, d), generator=g, device=dev).to(torch.float16)
+    vs = torch.randn((n_steps, w.batch, H, d), generator=g, device=dev).to(torch.float16)
+    out = torch.empty((w.batch, Hq, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(tq.monarch_workspace_size(h, w.batch, Hq, H, hot_cap, cold_cap), dtype=torch.uint8, device=dev)
+    state = {"i": 0}
+    snapshot = None
+    if not args.no_cpu_baseline:
+        snapshot = (st.records.cpu().numpy(), hk.float().cpu().numpy(), hv.float().cpu().numpy())
+
+    def step():
+        i = state["i"]
+        state["i"] += 1
+        tq.monarch_step(h, st, qs[i], ks[i], vs[i], window, out=out, workspace=ws)
+
+    ms_per_step, scan_ms = time_steps(ev, tq, step, args.steps, args.warmup)
+    torch.cuda.synchronize()
+    tokens = window + w.tokens
+    line = base_line(args, w, ms_per_step, w.batch * tokens)
+    line["metric"] = "hot/cold decode steps: tokens attended/sec (512 exact + ~1,024 compressed per step)"
+    line["config"].update({"window": window, "hot_capacity": hot_cap, "cold_gate": "inf",
+                           "promote_weight": 0.15, "promote_steps": 3, "ring_dtype": "f16"})
+    rec_alg = record_payload_bytes(w)
+    alg = rec_alg * w.batch * H * (w.tokens + args.warmup + args.steps // 2)
+    line["roofline"] = roofline("decode_scan_kernel", "monarch_tinyllama", alg, scan_ms,
+                                {"note": "latency-bound: the step is ~7 small launches; report us/step"})
+    line["us_per_step"] = ms_per_step * 1e3
+    line["state_after"] = {"hot_len": int(st.hot_len[0]), "cold_len": int(st.cold_len[0]),
+                           "overflow": int(st.overflow[0])}
+    if snapshot is not None:
+        line["cpu_baseline"] = cpu_baseline_monarch(w, h, snapshot, qs, ks, vs, window)
+    return line
+
+
+def cpu_baseline_monarch(w, h, snapshot, qs, ks, vs, window, budget_s: float = 8.0):
+    """The hot/cold oracle stepping the same initial state on one core."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import monarch as MO
+    codec = _codec((w.head_dim, w.key_bits, w.qjl_dim, w.value_bits, w.seed * 3 + 1, w.seed * 3 + 2))
+    rec, hk, hv = snapshot
+    o = MO.HotColdOracle(codec, w.batch, w.kv_heads, "float16", rec.shape[2])
+    for b in range(w.batch):
+        o.hot_k[b], o.hot_v[b] = hk[b].astype(np.float64), hv[b].astype(np.float64)
+        o.cold[b] = rec[b][:, :w.tokens].copy()
+        o.hits[b] = np.zeros(w.tokens, np.int64)
+    qn, kn, vn = qs.float().cpu().numpy(), ks.float().cpu().numpy(), vs.float().cpu().numpy()
+    done, elapsed = 0, 0.0
+    with threadpool_limits(limits=1):
+        for i in range(qn.shape[0]):
+            t0 = time.perf_counter()
+            o.step(qn[i], kn[i], vn[i], window)
+            elapsed += time.perf_counter() - t0
+            done += 1
+            if elapsed >= budget_s:
+                break
+    tokens = done * (window + w.tokens)
+    return {"value": tokens / elapsed, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} hot/cold steps from the same initial state, {elapsed:.1f} s",
+            "cpu_model": cpu_model()}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b_decode_32k",
-                    choices=DECODE_WORKLOADS + ["sparse_128k_top2048", "bulk_64k_scan"])
+                    choices=DECODE_WORKLOADS + ["sparse_128k_top2048", "bulk_64k_scan", "monarch_tinyllama"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 device-to-device copies of 1 GiB (HBM counter calibration)")
@@ -547,6 +630,8 @@ def main():
         line = run_decode(args, tq, W, ev)
     elif args.workload == "sparse_128k_top2048":
         line = run_sparse(args, tq, W, ev)
+    elif args.workload == "monarch_tinyllama":
+        line = run_monarch(args, tq, W, ev)
     else:
         line = run_bulk_scan(args, tq, W, ev)
     print(json.dumps(line), flush=True)

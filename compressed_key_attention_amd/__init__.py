@@ -305,7 +305,8 @@ class HotCold:
                             self.hits.data_ptr(), self.overflow.data_ptr())
 
 
-def _monarch_ws_size(h, batch, q_heads, kv_heads, hot_cap, cold_cap) -> int:
+def monarch_workspace_size(h, batch, q_heads, kv_heads, hot_cap, cold_cap) -> int:
+    """Workspace bytes tq_monarch_step needs for these shapes."""
     n = ctypes.c_size_t()
     check(_monarch_ws(h._h, batch, q_heads, kv_heads, hot_cap, cold_cap, ctypes.byref(n)))
     return n.value
@@ -321,7 +322,7 @@ def monarch_step(h, state, q, k_new, v_new, window, cold_gate=float("inf"), prom
     if out is None:
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
     if workspace is None:
-        workspace = _workspace(_monarch_ws_size(h, B, Hq, Hkv, state.hot_k.shape[2], state.records.shape[2]),
+        workspace = _workspace(monarch_workspace_size(h, B, Hq, Hkv, state.hot_k.shape[2], state.records.shape[2]),
                                q.device)
     cfg = MonarchConfig(window, cold_gate, promote_weight, promote_steps)
     st = state.c_state()

@@ -315,8 +315,9 @@ tq_status tq_monarch_step(const tq_handle* h, const tq_monarch_config* cfg, cons
   if (!elem_size(st->hot_dt, &hs)) return fail(TQ_ERR_INVALID_ARGUMENT, "unknown hot dtype");
   if (batch < 0 || q_heads <= 0 || kv_heads <= 0 || q_heads % kv_heads)
     return fail(TQ_ERR_INVALID_ARGUMENT, "q_heads must be a positive multiple of kv_heads");
-  if (q_heads / kv_heads > 16 || q_heads > 64)
-    return fail(TQ_ERR_UNSUPPORTED, "hot/cold step supports up to 16 query heads per KV head and 64 per sequence");
+  if (q_heads / kv_heads > 16 || q_heads > 64 || kv_heads > 16)
+    return fail(TQ_ERR_UNSUPPORTED,
+                "hot/cold step supports up to 16 query heads per KV head, 64 query and 16 KV heads per sequence");
   if (!(scale >= 0.0f) || std::isinf(scale)) return fail(TQ_ERR_INVALID_ARGUMENT, "scale must be finite and >= 0");
   if (cfg->window < 0 || cfg->promote_steps < 0 || std::isnan(cfg->cold_gate))
     return fail(TQ_ERR_INVALID_ARGUMENT, "window and promote_steps must be >= 0, cold_gate not NaN");

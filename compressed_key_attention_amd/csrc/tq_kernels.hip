@@ -1399,19 +1399,20 @@ struct MergeArgs {
   float scale;
 };
 
-constexpr int kMergeThreads = 256;
+constexpr int kMergeThreads = 256;        // without an exact segment
+constexpr int kMergeThreadsHot = 1024;    // with one: more token slots per pass
 
 constexpr int kMergeHotLds = 2048;   // exact-segment logits kept in LDS (beyond: recomputed)
 
-template <int D>
-__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs A) {
+template <int D, int NT>
+__global__ __launch_bounds__(NT) void decode_merge_kernel(MergeArgs A) {
   // exact segment layout: LPK lanes per token, each owning 8 consecutive coordinates
-  constexpr int LPK = D / 8, TPWK = 64 / LPK, TPB = TPWK * (kMergeThreads / 64);
+  constexpr int LPK = D / 8, TPWK = 64 / LPK, TPB = TPWK * (NT / 64);
   __shared__ float qv[D];
   __shared__ float ox[D];
-  __shared__ float ohw[kMergeThreads / 64][D];
+  __shared__ float ohw[NT / 64][D];
   __shared__ float hlog[kMergeHotLds];
-  __shared__ float red[kMergeThreads];
+  __shared__ float red[NT];
   const int hq = blockIdx.x, b = blockIdx.y, hkv = hq / A.G;
   const int64_t row = (int64_t)b * A.q_heads + hq;
   constexpr int stride = D + 2;
@@ -1428,7 +1429,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs A
     if (lane == 0) red[wave] = v;
     __syncthreads();
     v = red[0];
-    for (int w2 = 1; w2 < kMergeThreads / 64; ++w2) v = is_max ? fmaxf(v, red[w2]) : v + red[w2];
+    for (int w2 = 1; w2 < NT / 64; ++w2) v = is_max ? fmaxf(v, red[w2]) : v + red[w2];
     __syncthreads();
     return v;
   };
@@ -1517,13 +1518,13 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(MergeArgs A
   // o = Pi^T o_x: output i = row i of the transposed rotation against o_x
   {
     const int r = threadIdx.x >> 1, h = threadIdx.x & 1;
-    for (int i0 = 0; i0 < D; i0 += kMergeThreads / 2) {
+    for (int i0 = 0; i0 < D; i0 += NT / 2) {
       const int i = i0 + r;
       const float o = gemv_row_half_f32<D>(A.pi_t + (int64_t)min(i, D - 1) * D, ox, h);
       if (h == 0 && i < D) {
         float hsum = 0.0f;
 #pragma unroll
-        for (int w2 = 0; w2 < kMergeThreads / 64; ++w2) hsum += ohw[w2][i];
+        for (int w2 = 0; w2 < NT / 64; ++w2) hsum += ohw[w2][i];
         A.out[row * D + i] = L > 0.0f ? (o + hsum) / L : 0.0f;
       }
     }
@@ -1712,10 +1713,14 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
   mg.kv_heads = kv_heads;
   mg.n_chunks = plan.n_chunks;
   mg.scale = sc;
-  if (c.d == 128)
-    hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(q_heads, batch), dim3(kMergeThreads), 0, stream, mg);
-  else
-    hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(q_heads, batch), dim3(kMergeThreads), 0, stream, mg);
+  const dim3 mgrid(q_heads, batch);
+  if (hot_lens) {
+    if (c.d == 128) hipLaunchKernelGGL((decode_merge_kernel<128, kMergeThreadsHot>), mgrid, dim3(kMergeThreadsHot), 0, stream, mg);
+    else hipLaunchKernelGGL((decode_merge_kernel<64, kMergeThreadsHot>), mgrid, dim3(kMergeThreadsHot), 0, stream, mg);
+  } else {
+    if (c.d == 128) hipLaunchKernelGGL((decode_merge_kernel<128, kMergeThreads>), mgrid, dim3(kMergeThreads), 0, stream, mg);
+    else hipLaunchKernelGGL((decode_merge_kernel<64, kMergeThreads>), mgrid, dim3(kMergeThreads), 0, stream, mg);
+  }
   return hipGetLastError();
 }
 
@@ -2929,9 +2934,11 @@ __device__ void pack_record(const Consts& c, const uint32_t* ck, const uint32_t*
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void monarch_prep_kernel(MonarchArgs M) {
+__global__ __launch_bounds__(1024) void monarch_prep_kernel(MonarchArgs M) {
+  // lanes split a token's coordinates 8 at a time (LPK lanes per token), as the merge does
+  constexpr int LPK = D / 8, TPI = 1024 / LPK;
   __shared__ float qv[16][D];
-  __shared__ float red[4][16];
+  __shared__ float red[16][16];
   const int hkv = blockIdx.x, b = blockIdx.y, G = M.G;
   const int64_t unit = (int64_t)b * M.kv_heads + hkv;
   const int n = M.hot_len[b];
@@ -2946,32 +2953,31 @@ __global__ __launch_bounds__(256) void monarch_prep_kernel(MonarchArgs M) {
   for (int e = threadIdx.x; e < G * D; e += blockDim.x) qv[e / D][e % D] = load_elem(M.q, M.q_dt, qrow0 * D + e);
   __syncthreads();
   // best hot logit per head over the ring's tokens and the step's token (read from k_new)
+  const int sub = threadIdx.x % LPK, tok = threadIdx.x / LPK;
   float mx[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) mx[j] = kNegInf;
-  for (int t = threadIdx.x; t <= n; t += blockDim.x) {
+  for (int t0 = 0; t0 <= n; t0 += TPI) {
+    const int t = min(t0 + tok, n);
     int64_t rs = st + t;
     if (rs >= M.hot_cap) rs -= M.hot_cap;
-    const void* src = t < n ? M.hot_k : M.k_new;
-    const int64_t off = t < n ? (unit * M.hot_cap + rs) * D : unit * D;
-    float dot[16];
+    float kv[8];
+    load8(t < n ? M.hot_k : M.k_new, M.hot_dt, (t < n ? (unit * M.hot_cap + rs) * D : unit * D) + 8 * sub, kv);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) dot[j] = 0.0f;
-    for (int c8 = 0; c8 < D; c8 += 8) {
-      float kv[8];
-      load8(src, M.hot_dt, off + c8, kv);
+    for (int j = 0; j < 16; ++j) {
+      if (j >= G) break;
+      float dot = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (j < G)
+      for (int i = 0; i < 8; ++i) dot = fmaf(qv[j][8 * sub + i], kv[i], dot);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) dot[j] = fmaf(qv[j][c8 + i], kv[i], dot[j]);
+      for (int msk = 1; msk < LPK; msk <<= 1) dot += __shfl_xor(dot, msk);
+      mx[j] = fmaxf(mx[j], M.scale * dot);    // tokens past n repeat token n: the max is unchanged
     }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) mx[j] = fmaxf(mx[j], M.scale * dot[j]);
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
+    if (j >= G) break;
     float v = mx[j];
 #pragma unroll
     for (int msk = 32; msk > 0; msk >>= 1) v = fmaxf(v, __shfl_xor(v, msk));
@@ -2980,7 +2986,7 @@ __global__ __launch_bounds__(256) void monarch_prep_kernel(MonarchArgs M) {
   __syncthreads();
   if (threadIdx.x < G) {
     float v = red[0][threadIdx.x];
-    for (int w2 = 1; w2 < 4; ++w2) v = fmaxf(v, red[w2][threadIdx.x]);
+    for (int w2 = 1; w2 < 16; ++w2) v = fmaxf(v, red[w2][threadIdx.x]);
     M.gate[qrow0 + threadIdx.x] = v < M.cold_gate ? 1 : 0;
   }
 }
@@ -3010,8 +3016,12 @@ __global__ __launch_bounds__(1024) void monarch_promote_kernel(MonarchArgs M) {
       bool prom = false;
       if (t < n_cold) {
         float w = 0.0f;
-        for (int h = 0; h < Hq; ++h)
-          if (s_gate[h]) w = fmaxf(w, __expf(M.logits[((int64_t)b * Hq + h) * M.logit_stride + t] - s_lse[h]));
+        const float* lg = M.logits + (int64_t)b * Hq * M.logit_stride + t;
+#pragma unroll 8
+        for (int h = 0; h < Hq; ++h) {
+          const float v = lg[(int64_t)h * M.logit_stride];          // unconditional: loads in flight
+          if (s_gate[h]) w = fmaxf(w, __expf(v - s_lse[h]));
+        }
         const int hc = w >= M.promote_weight ? hits[t] + 1 : 0;
         prom = hc >= M.promote_steps;
         hits[t] = prom ? 0 : hc;
@@ -3083,69 +3093,84 @@ __global__ __launch_bounds__(1024) void monarch_promote_kernel(MonarchArgs M) {
   }
 }
 
+// Eviction: every KV head of an evicted token at once.  Threads split (head, K/V, coordinate)
+// work in each phase; float64 throughout, as compress_kernel and the oracle.
+constexpr int kMonarchMaxKvHeads = 16;
+
 template <int D>
-__global__ __launch_bounds__(256) void monarch_evict_kernel(MonarchArgs M) {
-  __shared__ double xd[D], kd[D], ed[D];
-  __shared__ double dred[256];
-  __shared__ uint32_t ck[D], cv[D], bits[256];
-  const int b = blockIdx.x;
+__global__ __launch_bounds__(512) void monarch_evict_kernel(MonarchArgs M) {
+  constexpr int HM = kMonarchMaxKvHeads;
+  extern __shared__ __attribute__((aligned(16))) double ev_lds[];
+  double* vin = ev_lds;                         // [H][2][D] inputs (K, V)
+  double* xr = vin + HM * 2 * D;                // [H][2][D] rotated
+  double* er = xr + HM * 2 * D;                 // [H][D] key residual
+  uint32_t* codes = reinterpret_cast<uint32_t*>(er + HM * D);   // [H][2][D]
+  uint32_t* bits = codes + HM * 2 * D;          // [H][m]
+  __shared__ double nrm[HM][3];                 // r_k, r_v (float64), rho
+  const int b = blockIdx.x, H = M.kv_heads;
   const Consts& c = M.c;
   const int64_t st = M.hot_start[b];
   const int n_hot = M.hot_len[b] + 1 + M.promo_count[b];
   const int e = max(0, n_hot - M.window);
   const int c0 = M.cold_after[b];
   const int es = (int)min((int64_t)e, M.cold_cap - c0);
-  auto block_sum = [&](double v) {
-    dred[threadIdx.x] = v;
-    __syncthreads();
-    for (int s2 = blockDim.x / 2; s2 > 0; s2 >>= 1) {
-      if (threadIdx.x < s2) dred[threadIdx.x] += dred[threadIdx.x + s2];
-      __syncthreads();
-    }
-    const double r = dred[0];
-    __syncthreads();
-    return r;
-  };
-  // Step 1 of the TurboQuant page ("Funktionsweise") on one vector in float64: r = |x|,
-  // y = Pi x, z = y sqrt(d) / r rounded to float32, codes against the float32 boundaries.
-  auto rotate_code = [&](const void* src, int64_t off, const float* bounds, uint32_t* codes) {
-    for (int i = threadIdx.x; i < D; i += blockDim.x) kd[i] = (double)load_elem(src, M.hot_dt, off + i);
-    __syncthreads();
-    const double r = sqrt(block_sum(threadIdx.x < D ? kd[threadIdx.x] * kd[threadIdx.x] : 0.0));
-    const double scale = r > 0.0 ? c.sqrt_d / r : 0.0;
-    for (int i = threadIdx.x; i < D; i += blockDim.x) {
-      double acc = 0.0;
-      for (int j = 0; j < D; ++j) acc = fma((double)M.pi[i * D + j], kd[j], acc);
-      xd[i] = acc;
-      codes[i] = quantize_code((float)(acc * scale), bounds);
-    }
-    __syncthreads();
-    return (float)r;
-  };
   for (int i = 0; i < es; ++i) {
     int64_t rs = st + i;
     rs %= M.hot_cap;
-    for (int h = 0; h < M.kv_heads; ++h) {
-      const int64_t unit = (int64_t)b * M.kv_heads + h;
-      const int64_t off = (unit * M.hot_cap + rs) * D;
-      const float rk = rotate_code(M.hot_k, off, c.key_bounds, ck);
-      // residual in the rotated basis, its norm, and the QJL signs of S e
-      for (int j = threadIdx.x; j < D; j += blockDim.x)
-        ed[j] = xd[j] - ((double)rk / c.sqrt_d) * (double)c.key_levels[ck[j]];
-      __syncthreads();
-      const float rho = (float)sqrt(block_sum(threadIdx.x < D ? ed[threadIdx.x] * ed[threadIdx.x] : 0.0));
-      for (int j = threadIdx.x; j < c.m; j += blockDim.x) {
-        double acc = 0.0;
-        for (int k2 = 0; k2 < D; ++k2) acc = fma((double)M.s[j * D + k2], ed[k2], acc);
-        bits[j] = (float)acc >= 0.0f ? 1u : 0u;
-      }
-      __syncthreads();
-      const float rv = rotate_code(M.hot_v, off, c.val_bounds, cv);
-      if (threadIdx.x == 0) {
-        pack_record(c, ck, bits, cv, rk, rho, rv, M.records + (unit * M.cold_cap + c0 + i) * c.rec_bytes);
-      }
-      __syncthreads();
+    // inputs
+    for (int t = threadIdx.x; t < H * 2 * D; t += blockDim.x) {
+      const int h = t / (2 * D), w = (t / D) & 1, j = t % D;
+      const int64_t unit = (int64_t)b * H + h;
+      vin[t] = (double)load_elem(w ? M.hot_v : M.hot_k, M.hot_dt, (unit * M.hot_cap + rs) * D + j);
     }
+    __syncthreads();
+    // norms r_k, r_v
+    for (int t = threadIdx.x; t < H * 2; t += blockDim.x) {
+      double s = 0.0;
+      for (int j = 0; j < D; ++j) s = fma(vin[t * D + j], vin[t * D + j], s);
+      nrm[t >> 1][t & 1] = sqrt(s);
+    }
+    __syncthreads();
+    // rotation and codes: z = (Pi x) sqrt(d) / r rounded to float32
+    for (int t = threadIdx.x; t < H * 2 * D; t += blockDim.x) {
+      const int h = t / (2 * D), w = (t / D) & 1, o = t % D;
+      const double* xv = vin + (h * 2 + w) * D;
+      double acc = 0.0;
+#pragma unroll 8
+      for (int j = 0; j < D; ++j) acc = fma((double)M.pi[o * D + j], xv[j], acc);
+      xr[t] = acc;
+      const double r = nrm[h][w];
+      const double scale = r > 0.0 ? c.sqrt_d / r : 0.0;
+      codes[t] = quantize_code((float)(acc * scale), w ? c.val_bounds : c.key_bounds);
+    }
+    __syncthreads();
+    // key residual e = x - (r_k / sqrt(d)) gamma[c] with r_k stored as float32
+    for (int t = threadIdx.x; t < H * D; t += blockDim.x) {
+      const int h = t / D, j = t % D;
+      const double rk = (double)(float)nrm[h][0];
+      er[t] = xr[h * 2 * D + j] - (rk / c.sqrt_d) * (double)c.key_levels[codes[h * 2 * D + j]];
+    }
+    __syncthreads();
+    for (int h = threadIdx.x; h < H; h += blockDim.x) {
+      double s = 0.0;
+      for (int j = 0; j < D; ++j) s = fma(er[h * D + j], er[h * D + j], s);
+      nrm[h][2] = sqrt(s);
+    }
+    // QJL signs of S e
+    for (int t = threadIdx.x; t < H * c.m; t += blockDim.x) {
+      const int h = t / c.m, j = t % c.m;
+      double acc = 0.0;
+#pragma unroll 8
+      for (int k2 = 0; k2 < D; ++k2) acc = fma((double)M.s[j * D + k2], er[h * D + k2], acc);
+      bits[t] = (float)acc >= 0.0f ? 1u : 0u;
+    }
+    __syncthreads();
+    for (int h = threadIdx.x; h < H; h += blockDim.x) {
+      const int64_t unit = (int64_t)b * H + h;
+      pack_record(c, codes + h * 2 * D, bits + h * c.m, codes + h * 2 * D + D, (float)nrm[h][0],
+                  (float)nrm[h][2], (float)nrm[h][1], M.records + (unit * M.cold_cap + c0 + i) * c.rec_bytes);
+    }
+    __syncthreads();
   }
   if (threadIdx.x == 0) {
     int32_t* hits = M.hits + (int64_t)b * M.cold_cap;
@@ -3155,6 +3180,11 @@ __global__ __launch_bounds__(256) void monarch_evict_kernel(MonarchArgs M) {
     M.cold_len[b] = c0 + es;
     if (es < e) M.overflow[b] = 1;
   }
+}
+
+template <int D>
+size_t monarch_evict_lds(int m) {
+  return (size_t)kMonarchMaxKvHeads * (2 * D * 8 * 2 + D * 8 + 2 * D * 4 + (size_t)m * 4);
 }
 
 MonarchPlan plan_monarch(const Consts& c, int batch, int q_heads, int kv_heads, int64_t hot_cap,
@@ -3215,8 +3245,8 @@ hipError_t launch_monarch_step(const Consts& c, const DevConsts& dc, const Monar
   M.promote_weight = s.promote_weight;
   M.scale = s.scale > 0.0f ? s.scale : c.inv_sqrt_d;
   const dim3 g1(s.kv_heads, s.batch);
-  if (c.d == 128) hipLaunchKernelGGL(monarch_prep_kernel<128>, g1, dim3(256), 0, stream, M);
-  else hipLaunchKernelGGL(monarch_prep_kernel<64>, g1, dim3(256), 0, stream, M);
+  if (c.d == 128) hipLaunchKernelGGL(monarch_prep_kernel<128>, g1, dim3(1024), 0, stream, M);
+  else hipLaunchKernelGGL(monarch_prep_kernel<64>, g1, dim3(1024), 0, stream, M);
   DecodeHooks hk{M.gate, s.hot_start, 1};
   hipError_t e = launch_decode(c, dc, plan.decode, s.q, s.q_dt, s.batch, s.q_heads, s.kv_heads, s.records,
                                s.cold_cap, s.cold_len, s.hot_k, s.hot_v, s.hot_dt, s.hot_len, s.hot_cap,
@@ -3224,10 +3254,14 @@ hipError_t launch_monarch_step(const Consts& c, const DevConsts& dc, const Monar
   if (e != hipSuccess) return e;
   if (c.d == 128) {
     hipLaunchKernelGGL(monarch_promote_kernel<128>, dim3(s.batch), dim3(1024), 0, stream, M);
-    hipLaunchKernelGGL(monarch_evict_kernel<128>, dim3(s.batch), dim3(256), 0, stream, M);
+    const size_t lds = monarch_evict_lds<128>(c.m);
+    allow_lds(monarch_evict_kernel<128>, lds);
+    hipLaunchKernelGGL(monarch_evict_kernel<128>, dim3(s.batch), dim3(512), lds, stream, M);
   } else {
     hipLaunchKernelGGL(monarch_promote_kernel<64>, dim3(s.batch), dim3(1024), 0, stream, M);
-    hipLaunchKernelGGL(monarch_evict_kernel<64>, dim3(s.batch), dim3(256), 0, stream, M);
+    const size_t lds = monarch_evict_lds<64>(c.m);
+    allow_lds(monarch_evict_kernel<64>, lds);
+    hipLaunchKernelGGL(monarch_evict_kernel<64>, dim3(s.batch), dim3(512), lds, stream, M);
   }
   return hipGetLastError();
 }
