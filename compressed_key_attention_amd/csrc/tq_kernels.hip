@@ -883,7 +883,7 @@ __device__ __forceinline__ uint32_t bf16_pair(float x) {      // hi | lo << 16
 
 // Per (sequence, KV head) preparation for the matrix-core scan: q_x = Pi q and q_s = (S Pi) q
 // for the group's G query heads in one pass (float64 sums rounded once to float32; thread
-// (row o, half hf) holds half a row of Pi and of S Pi, loaded up front), then the lanes' query
+// (row o, slice) holds 16 coordinates of row o of Pi and of S Pi, loaded up front), then the lanes' query
 // operands: bop[group][lane][32 words] = code words (16), QJL words (8), and the scales of lane
 // L's head L / 16, {1 / (F_q F_k), 2 / F_s, -sum / F_s} (3), pad.
 // SCAN: the same for a group of 4 consecutive bulk-scan queries of one (sequence, KV head)
@@ -893,68 +893,74 @@ __device__ __forceinline__ uint32_t bf16_pair(float x) {      // hi | lo << 16
 // same scales for lane L's query L / 16.
 constexpr int kScanLaneWords = 36;   // bulk-scan query operand words per lane (9 chunks of 16 B)
 
+constexpr int kPrepThreads = 1024;
+
 template <int BK, bool QJL, bool SCAN>
-__global__ __launch_bounds__(256) void mfma_prep_kernel(const float* __restrict__ pi,
-                                                        const float* __restrict__ s_pi, const void* q,
-                                                        tq_dtype q_dt, int q_heads, int kv_heads,
-                                                        float fk, uint32_t* bop) {
-  constexpr int D = 128, G = 4, H = D / 2;
+__global__ __launch_bounds__(kPrepThreads) void mfma_prep_kernel(const float* __restrict__ pi,
+                                                                 const float* __restrict__ s_pi, const void* q,
+                                                                 tq_dtype q_dt, int q_heads, int kv_heads,
+                                                                 float fk, uint32_t* bop) {
+  constexpr int D = 128, G = 4;
   __shared__ double qv[G][D];
   __shared__ __attribute__((aligned(16))) float xf[G][D], sf[G][D];
   const int group = blockIdx.x, b = group / kv_heads, hkv = group % kv_heads;
   const int64_t qrow0 = (int64_t)b * q_heads + (int64_t)hkv * G;
   const int rows = SCAN ? min(G, q_heads - hkv * G) : G;
-  const int o = threadIdx.x >> 1, hf = threadIdx.x & 1;
-  float4 wp[H / 4], ws[H / 4];
-  {
-    const float4* pp = reinterpret_cast<const float4*>(pi + o * D + hf * H);
+  // thread (row o, slice ks): coordinates 32 jj + 4 ks .. + 3 (jj < 4) of row o of Pi and of
+  // S Pi against the group's G queries, so that the eight lanes of a row read whole 128-byte
+  // lines; the eight slices are summed across adjacent lanes
+  const int o = threadIdx.x >> 3, ks = threadIdx.x & 7;
+  float4 wp[4], ws[4];
 #pragma unroll
-    for (int j = 0; j < H / 4; ++j) wp[j] = pp[j];
-    if (QJL) {
-      const float4* sp = reinterpret_cast<const float4*>(s_pi + o * D + hf * H);
-#pragma unroll
-      for (int j = 0; j < H / 4; ++j) ws[j] = sp[j];
-    }
+  for (int jj = 0; jj < 4; ++jj) {
+    wp[jj] = *reinterpret_cast<const float4*>(pi + o * D + 32 * jj + 4 * ks);
+    if (QJL) ws[jj] = *reinterpret_cast<const float4*>(s_pi + o * D + 32 * jj + 4 * ks);
   }
-  for (int e = threadIdx.x; e < G * D; e += blockDim.x)
-    qv[e / D][e % D] = e / D < rows ? (double)load_elem(q, q_dt, (qrow0 + e / D) * D + e % D) : 0.0;
+  if (threadIdx.x < G * D) {
+    const int h = threadIdx.x / D, i = threadIdx.x % D;
+    qv[h][i] = h < rows ? (double)load_elem(q, q_dt, (qrow0 + h) * D + i) : 0.0;
+  }
   __syncthreads();
-  double ax[G], as[G];
+  {
+    double ax[G], as[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) ax[h] = as[h] = 0.0;
+    for (int h = 0; h < G; ++h) ax[h] = as[h] = 0.0;
 #pragma unroll
-  for (int j = 0; j < H / 4; ++j)
+    for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const double* vv = qv[h] + hf * H + 4 * j;
-      ax[h] = fma((double)wp[j].x, vv[0], ax[h]);
-      ax[h] = fma((double)wp[j].y, vv[1], ax[h]);
-      ax[h] = fma((double)wp[j].z, vv[2], ax[h]);
-      ax[h] = fma((double)wp[j].w, vv[3], ax[h]);
-      if (QJL) {
-        as[h] = fma((double)ws[j].x, vv[0], as[h]);
-        as[h] = fma((double)ws[j].y, vv[1], as[h]);
-        as[h] = fma((double)ws[j].z, vv[2], as[h]);
-        as[h] = fma((double)ws[j].w, vv[3], as[h]);
+      for (int h = 0; h < G; ++h) {
+        const double* vv = qv[h] + 32 * jj + 4 * ks;
+        ax[h] = fma((double)wp[jj].x, vv[0], ax[h]);
+        ax[h] = fma((double)wp[jj].y, vv[1], ax[h]);
+        ax[h] = fma((double)wp[jj].z, vv[2], ax[h]);
+        ax[h] = fma((double)wp[jj].w, vv[3], ax[h]);
+        if (QJL) {
+          as[h] = fma((double)ws[jj].x, vv[0], as[h]);
+          as[h] = fma((double)ws[jj].y, vv[1], as[h]);
+          as[h] = fma((double)ws[jj].z, vv[2], as[h]);
+          as[h] = fma((double)ws[jj].w, vv[3], as[h]);
+        }
       }
-    }
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    ax[h] += __shfl_xor(ax[h], 1);
-    as[h] += __shfl_xor(as[h], 1);
+    for (int msk = 1; msk < 8; msk <<= 1)
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        ax[h] += __shfl_xor(ax[h], msk);
+        if (QJL) as[h] += __shfl_xor(as[h], msk);
+      }
+    if (ks == 0)
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        xf[h][o] = (float)ax[h];
+        sf[h][o] = (float)as[h];
+      }
   }
-  if (hf == 0)
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      xf[h][o] = (float)ax[h];
-      sf[h][o] = (float)as[h];
-    }
   __syncthreads();
   // per head: fixed-point scales (three int8 limbs against the largest |entry|) and the sum of
   // the sketch's fixed-point values
   __shared__ float s_fq[G], s_fs[G];
   __shared__ int s_ssum[G];
-  {
+  if (threadIdx.x < G * 64) {
     const int h = threadIdx.x >> 6, l = threadIdx.x & 63;   // wave h reduces head h
     float mx = fmaxf(fabsf(xf[h][l]), fabsf(xf[h][l + 64]));
     float ms = QJL ? fmaxf(fabsf(sf[h][l]), fabsf(sf[h][l + 64])) : 0.0f;
@@ -982,84 +988,155 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(const float* __restrict_
   //    hi x q1 + lo x q2; part 2 (2^8): hi x q0 + lo x q1; part 3: zero.
   //  QJL word (j, w): byte k <-> sketch coordinate 32 kg + 8k + 4j + w; part p < 3 holds limb
   //    2 - p of the sketch (weight 2^(8 (2 - p))); part 3: zero.
-  // one role per wave (no divergence): waves 0 and 1 write code words 0..7 and 8..15, wave 2
-  // the QJL words, wave 3 the column scales, each for scan lane L = its own lane
+  // one 16-byte chunk per wave (no divergence): waves 0 .. NC - 1 the code chunks, the next two
+  // the QJL chunks, the next one the scales, each for lane L = its own lane
+  constexpr int NC = SCAN ? 6 : 4;
   const int L = threadIdx.x & 63, role = threadIdx.x >> 6;
+  if (role > NC + 2) return;
   const int n = L & 15, kg = L >> 4, hB = n >> 2, part = n & 3;
   const float fq = s_fq[hB], fs = s_fs[hB];
   u32x4* gdst = reinterpret_cast<u32x4*>(bop + ((int64_t)group * 64 + L) * (SCAN ? kScanLaneWords : 32));
-  if (SCAN && role < 2) {
-    // key part n of weight 2^(32 - 8n) pairs key limb plane p (weight 2^(8p)) with query limb
-    // 4 - n - p (weight 2^(8 (4 - n - p))) when that is 0, 1 or 2
+  if (role < NC) {
+    const int j = role;
+    u32x4 words;
 #pragma unroll
-    for (int jj = 0; jj < 3; ++jj) {
-      const int j = 3 * role + jj, plane = 2 - (j >> 1), hh = j & 1;
-      const int ql = 4 - part - plane;
-      u32x4 words;
+    for (int w = 0; w < 4; ++w) {
+      uint32_t word = 0;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int coord = sel_coord<BK>(4 * hh + w, kk);
+      for (int kk = 0; kk < 4; ++kk) {
+        int v;
+        if (SCAN) {
+          // key part n of weight 2^(32 - 8n) pairs key limb plane p (weight 2^(8p)) with query
+          // limb 4 - n - p (weight 2^(8 (4 - n - p))) when that is 0, 1 or 2
+          const int plane = 2 - (j >> 1), ql = 4 - part - plane;
+          const int coord = sel_coord<BK>(4 * (j & 1) + w, kk);
           int l2, l1, l0;
           int8_limbs3((int)rintf(xf[hB][32 * kg + coord] * fq), l2, l1, l0);
-          const int v = ql == 2 ? l2 : ql == 1 ? l1 : ql == 0 ? l0 : 0;
-          word |= (uint32_t)(v & 0xFF) << (8 * kk);
-        }
-        words[w] = word;
-      }
-      gdst[j] = words;
-    }
-  } else if (role < 2) {
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int j = 2 * role + jj;
-      u32x4 words;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int coord = sel_coord<BK>(2 * j + (w & 1), k);
+          v = ql == 2 ? l2 : ql == 1 ? l1 : ql == 0 ? l0 : 0;
+        } else {
+          const int coord = sel_coord<BK>(2 * j + (w & 1), kk);
           int l2, l1, l0;
           int8_limbs3((int)rintf(xf[hB][32 * kg + coord] * fq), l2, l1, l0);
           const bool hi_slot = w < 2;
-          const int v = part == 0 ? (hi_slot ? l2 : 0) : part == 1 ? (hi_slot ? l1 : l2)
-                      : part == 2 ? (hi_slot ? l0 : l1) : 0;
+          v = part == 0 ? (hi_slot ? l2 : 0) : part == 1 ? (hi_slot ? l1 : l2)
+            : part == 2 ? (hi_slot ? l0 : l1) : 0;
+        }
+        word |= (uint32_t)(v & 0xFF) << (8 * kk);
+      }
+      words[w] = word;
+    }
+    gdst[j] = words;
+  } else if (role < NC + 2) {
+    const int j = role - NC;
+    u32x4 words;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t word = 0;
+      if (QJL)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          int l2, l1, l0;
+          int8_limbs3((int)rintf(sf[hB][32 * kg + 8 * k + 4 * j + w] * fs), l2, l1, l0);
+          const int v = part == 0 ? l2 : part == 1 ? l1 : part == 2 ? l0 : 0;
           word |= (uint32_t)(v & 0xFF) << (8 * k);
         }
-        words[w] = word;
-      }
-      gdst[j] = words;
+      words[w] = word;
     }
-  } else if (role == 2) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      u32x4 words;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint32_t word = 0;
-        if (QJL)
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            int l2, l1, l0;
-            int8_limbs3((int)rintf(sf[hB][32 * kg + 8 * k + 4 * j + w] * fs), l2, l1, l0);
-            const int v = part == 0 ? l2 : part == 1 ? l1 : part == 2 ? l0 : 0;
-            word |= (uint32_t)(v & 0xFF) << (8 * k);
-          }
-        words[w] = word;
-      }
-      gdst[(SCAN ? 6 : 4) + j] = words;
-    }
+    gdst[NC + j] = words;
   } else {
     // the score lanes of head / query kg combine its parts with these
     const float fqk = s_fq[kg], fsk = s_fs[kg];
     const float bk = 1.0f / (fqk * fk);
     const float bq = QJL ? 2.0f / fsk : 0.0f;
     const float oq = QJL ? -(float)s_ssum[kg] / fsk : 0.0f;
-    gdst[SCAN ? 8 : 6] = u32x4{__float_as_uint(bk), __float_as_uint(bq), __float_as_uint(oq), 0u};
+    gdst[NC + 2] = u32x4{__float_as_uint(bk), __float_as_uint(bq), __float_as_uint(oq), 0u};
   }
+}
+
+// Merge without an exact segment, one block per (sequence, KV head): the GG query heads of the
+// group share one read of Pi^T (D / 2 entries per thread, applied to all GG vectors).
+// 256 threads; rows row0 .. row0 + GG - 1 of part [rows][nch][D + 2] = (m, l, o_x[D]) in, out
+// [rows][D] and lse [rows] (if not NULL) out.
+template <int D, int GG>
+__device__ __forceinline__ void merge_group(const float* __restrict__ pi_t, const float* part,
+                                            float* out, float* lse, int64_t row0, int nch) {
+  __shared__ __attribute__((aligned(16))) float ox[GG][D];
+  __shared__ float sM[GG], sL[GG];
+  constexpr int stride = D + 2;
+  // thread (slice ks, rows orow + (256 / 8) r): coordinates 32 jj + 4 ks .. + 3 (jj < D / 32)
+  // of D / 32 rows of Pi^T, loaded up front so that eight lanes read whole 128-byte lines
+  constexpr int NJ = D / 32, RS = 256 / 8, NR = D / RS;
+  const int ks = threadIdx.x & 7, orow = threadIdx.x >> 3;
+  float4 w[NR][NJ];
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj)
+      w[r][jj] = *reinterpret_cast<const float4*>(pi_t + (int64_t)(orow + RS * r) * D + 32 * jj + 4 * ks);
+  // rotated-domain output of head h, coordinate i: one pass over the chunk partials with a
+  // running maximum (eight chunks' loads in flight at a time; a chunk with m = -inf weighs 0);
+  // every thread of a head forms the same maximum and weight sum
+  for (int e = threadIdx.x; e < GG * D; e += blockDim.x) {
+    const int h = e / D, i = e % D;
+    const float* pr = part + (row0 + h) * nch * stride;
+    float M = kNegInf, L = 0.0f, acc = 0.0f;
+    for (int c = 0; c < nch; c += 8) {
+      float mc[8], lc[8], ov[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int cc = min(c + u, nch - 1);
+        mc[u] = c + u < nch ? pr[(int64_t)cc * stride] : kNegInf;
+        lc[u] = pr[(int64_t)cc * stride + 1];
+        ov[u] = pr[(int64_t)cc * stride + 2 + i];
+      }
+      float Mn = M;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) Mn = fmaxf(Mn, mc[u]);
+      if (Mn == kNegInf) continue;
+      const float sc = M == kNegInf ? 0.0f : __expf(M - Mn);
+      acc *= sc;
+      L *= sc;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wgt = mc[u] == kNegInf ? 0.0f : __expf(mc[u] - Mn);
+        acc = fmaf(ov[u], wgt, acc);
+        L = fmaf(lc[u], wgt, L);
+      }
+      M = Mn;
+    }
+    ox[h][i] = acc;
+    if (i == 0) {
+      sM[h] = M;
+      sL[h] = L;
+    }
+  }
+  __syncthreads();
+  // o = Pi^T o_x / L for the GG heads
+#pragma unroll
+  for (int h = 0; h < GG; ++h) {
+    float acc[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) acc[r] = 0.0f;
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) {
+      const float4 xv = *reinterpret_cast<const float4*>(ox[h] + 32 * jj + 4 * ks);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        acc[r] = fmaf(w[r][jj].x, xv.x, acc[r]);
+        acc[r] = fmaf(w[r][jj].y, xv.y, acc[r]);
+        acc[r] = fmaf(w[r][jj].z, xv.z, acc[r]);
+        acc[r] = fmaf(w[r][jj].w, xv.w, acc[r]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+#pragma unroll
+      for (int msk = 1; msk < 8; msk <<= 1) acc[r] += __shfl_xor(acc[r], msk);
+      if (ks == 0) out[(row0 + h) * D + orow + RS * r] = sL[h] > 0.0f ? acc[r] / sL[h] : 0.0f;
+    }
+  }
+  if (threadIdx.x < GG && lse)
+    lse[row0 + threadIdx.x] = sL[threadIdx.x] > 0.0f ? sM[threadIdx.x] + logf(sL[threadIdx.x]) : kNegInf;
 }
 
 constexpr int kMfmaThreads = 256;
@@ -1379,6 +1456,29 @@ __device__ __forceinline__ void load8(const void* base, tq_dtype dt, int64_t off
   }
 }
 
+// sum_c o_c[i] exp(m_c - M) over a row's chunk partials [nch][stride] = (m, l, o[0..]), eight
+// chunks' loads in flight at a time (a chunk with m = -inf weighs 0)
+__device__ __forceinline__ float merge_chunks(const float* pr, int nch, int stride, int i, float M) {
+  float acc = 0.0f;
+  int c = 0;
+  for (; c + 8 <= nch; c += 8) {
+    float mc[8], ov[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      mc[u] = pr[(int64_t)(c + u) * stride];
+      ov[u] = pr[(int64_t)(c + u) * stride + 2 + i];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      acc = fmaf(ov[u], (M != kNegInf && mc[u] != kNegInf) ? __expf(mc[u] - M) : 0.0f, acc);
+  }
+  for (; c < nch; ++c) {
+    const float mc = pr[(int64_t)c * stride];
+    acc = fmaf(pr[(int64_t)c * stride + 2 + i], (M != kNegInf && mc != kNegInf) ? __expf(mc - M) : 0.0f, acc);
+  }
+  return acc;
+}
+
 struct MergeArgs {
   const float* pi_t;      // Pi transposed
   const float* part;
@@ -1480,15 +1580,7 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(MergeArgs A) {
     const float mc = pr[(int64_t)c * stride];
     l += (M != kNegInf && mc != kNegInf) ? pr[(int64_t)c * stride + 1] * __expf(mc - M) : 0.0f;
   }
-  for (int i = threadIdx.x; i < D; i += blockDim.x) {
-    float acc = 0.0f;
-    for (int c = 0; c < n_chunks; ++c) {
-      const float mc = pr[(int64_t)c * stride];
-      const float wgt = (M != kNegInf && mc != kNegInf) ? __expf(mc - M) : 0.0f;
-      acc = fmaf(pr[(int64_t)c * stride + 2 + i], wgt, acc);
-    }
-    ox[i] = acc;
-  }
+  for (int i = threadIdx.x; i < D; i += blockDim.x) ox[i] = merge_chunks(pr, n_chunks, stride, i, M);
   // hot values: each lane accumulates its 8 coordinates over the tokens of its slot
   float oh8[8];
 #pragma unroll
@@ -1530,6 +1622,12 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(MergeArgs A) {
     }
   }
   if (threadIdx.x == 0 && A.lse) A.lse[row] = L > 0.0f ? M + logf(L) : kNegInf;
+}
+
+template <int D, int GG>
+__global__ __launch_bounds__(256) void decode_merge_group_kernel(MergeArgs A) {
+  merge_group<D, GG>(A.pi_t, A.part, A.out, A.lse,
+                     (int64_t)blockIdx.y * A.q_heads + (int64_t)blockIdx.x * GG, A.n_chunks);
 }
 
 static bool mfma_path(const Consts& c, int G) {
@@ -1580,13 +1678,13 @@ static void launch_mfma_prep(const Consts& c, const DevConsts& dc, const void* q
   const dim3 grid((unsigned)(batch * kv_heads));
   const bool qjl = c.m > 0;
   if (c.kb == 3 && qjl)
-    hipLaunchKernelGGL((mfma_prep_kernel<3, true, false>), grid, dim3(256), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
+    hipLaunchKernelGGL((mfma_prep_kernel<3, true, false>), grid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
   else if (c.kb == 3)
-    hipLaunchKernelGGL((mfma_prep_kernel<3, false, false>), grid, dim3(256), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
+    hipLaunchKernelGGL((mfma_prep_kernel<3, false, false>), grid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
   else if (qjl)
-    hipLaunchKernelGGL((mfma_prep_kernel<2, true, false>), grid, dim3(256), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
+    hipLaunchKernelGGL((mfma_prep_kernel<2, true, false>), grid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
   else
-    hipLaunchKernelGGL((mfma_prep_kernel<2, false, false>), grid, dim3(256), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
+    hipLaunchKernelGGL((mfma_prep_kernel<2, false, false>), grid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
 }
 
 template <int BK, bool QJL>
@@ -1717,6 +1815,12 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
   if (hot_lens) {
     if (c.d == 128) hipLaunchKernelGGL((decode_merge_kernel<128, kMergeThreadsHot>), mgrid, dim3(kMergeThreadsHot), 0, stream, mg);
     else hipLaunchKernelGGL((decode_merge_kernel<64, kMergeThreadsHot>), mgrid, dim3(kMergeThreadsHot), 0, stream, mg);
+  } else if (plan.group == 4 || plan.group == 2) {
+    const dim3 ggrid(kv_heads, batch);
+    if (c.d == 128 && plan.group == 4) hipLaunchKernelGGL((decode_merge_group_kernel<128, 4>), ggrid, dim3(256), 0, stream, mg);
+    else if (c.d == 128) hipLaunchKernelGGL((decode_merge_group_kernel<128, 2>), ggrid, dim3(256), 0, stream, mg);
+    else if (plan.group == 4) hipLaunchKernelGGL((decode_merge_group_kernel<64, 4>), ggrid, dim3(256), 0, stream, mg);
+    else hipLaunchKernelGGL((decode_merge_group_kernel<64, 2>), ggrid, dim3(256), 0, stream, mg);
   } else {
     if (c.d == 128) hipLaunchKernelGGL((decode_merge_kernel<128, kMergeThreads>), mgrid, dim3(kMergeThreads), 0, stream, mg);
     else hipLaunchKernelGGL((decode_merge_kernel<64, kMergeThreads>), mgrid, dim3(kMergeThreads), 0, stream, mg);
@@ -2724,13 +2828,13 @@ hipError_t launch_scan(const Consts& c, const DevConsts& dc, const ScanPlan& pla
     const bool qjl = c.m > 0;
     // q viewed as [units][n_queries] rows: "heads" of the prep = queries per unit, groups per unit
     if (c.kb == 3 && qjl)
-      hipLaunchKernelGGL((mfma_prep_kernel<3, true, true>), pgrid, dim3(256), 0, stream, dc.pi, dc.s_pi, q, q_dt, n_queries, plan.n_groups, c.key_fix3, qop);
+      hipLaunchKernelGGL((mfma_prep_kernel<3, true, true>), pgrid, dim3(kPrepThreads), 0, stream, dc.pi, dc.s_pi, q, q_dt, n_queries, plan.n_groups, c.key_fix3, qop);
     else if (c.kb == 3)
-      hipLaunchKernelGGL((mfma_prep_kernel<3, false, true>), pgrid, dim3(256), 0, stream, dc.pi, dc.s_pi, q, q_dt, n_queries, plan.n_groups, c.key_fix3, qop);
+      hipLaunchKernelGGL((mfma_prep_kernel<3, false, true>), pgrid, dim3(kPrepThreads), 0, stream, dc.pi, dc.s_pi, q, q_dt, n_queries, plan.n_groups, c.key_fix3, qop);
     else if (qjl)
-      hipLaunchKernelGGL((mfma_prep_kernel<2, true, true>), pgrid, dim3(256), 0, stream, dc.pi, dc.s_pi, q, q_dt, n_queries, plan.n_groups, c.key_fix3, qop);
+      hipLaunchKernelGGL((mfma_prep_kernel<2, true, true>), pgrid, dim3(kPrepThreads), 0, stream, dc.pi, dc.s_pi, q, q_dt, n_queries, plan.n_groups, c.key_fix3, qop);
     else
-      hipLaunchKernelGGL((mfma_prep_kernel<2, false, true>), pgrid, dim3(256), 0, stream, dc.pi, dc.s_pi, q, q_dt, n_queries, plan.n_groups, c.key_fix3, qop);
+      hipLaunchKernelGGL((mfma_prep_kernel<2, false, true>), pgrid, dim3(kPrepThreads), 0, stream, dc.pi, dc.s_pi, q, q_dt, n_queries, plan.n_groups, c.key_fix3, qop);
     ScanMfmaArgs a;
     a.qop = qop;
     a.records = static_cast<const uint8_t*>(records);
