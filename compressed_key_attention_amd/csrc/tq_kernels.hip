@@ -522,6 +522,7 @@ __global__ void query_prep_kernel(const float* __restrict__ pi, const float* __r
 // are merged across lanes and waves at the end of the chunk.
 // -----------------------------------------------------------------------------------------
 constexpr float kLazy = 8.0f;
+constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
 constexpr int kDecodeThreads = 512;
 
 struct DecodeArgs {
@@ -1035,8 +1036,15 @@ __global__ __launch_bounds__(kPrepThreads) void mfma_prep_kernel(const float* __
       if (QJL)
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
+          // decode: the token side holds bit s = 4 j + w of each sketch byte in place (byte
+          // value 2^s b, -128 b for s = 7), so this side holds the sketch scaled by 2^-s
+          // (negated for s = 7)
+          const int s = 4 * j + w;
+          const float sv = sf[hB][32 * kg + 8 * k + 4 * j + w] * fs;
+          const int qv = SCAN ? (int)rintf(sv) : s == 7 ? -(int)rintf(sv * 0.0078125f)
+                                                         : (int)rintf(sv * (1.0f / (float)(1 << s)));
           int l2, l1, l0;
-          int8_limbs3((int)rintf(sf[hB][32 * kg + 8 * k + 4 * j + w] * fs), l2, l1, l0);
+          int8_limbs3(qv, l2, l1, l0);
           const int v = part == 0 ? l2 : part == 1 ? l1 : part == 2 ? l0 : 0;
           word |= (uint32_t)(v & 0xFF) << (8 * k);
         }
@@ -1144,7 +1152,7 @@ constexpr int kMfmaThreads = 256;
 template <int BK, bool QJL, bool GATHER, bool LOGITS>
 __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs A) {
   constexpr int D = 128, G = 4, NW = kMfmaThreads / 64;
-  // value code -> bf16 (hi, lo) pair of its level: 16 words in 16 distinct banks, so lookups
+  // value code -> bf16 (hi, lo) pair of its level / sqrt(d): 16 words in 16 distinct banks, so lookups
   // never conflict (equal codes are broadcast)
   __shared__ uint32_t vtab[16];
   // Value-code staging, rows padded to TS words so that the four K-slices of a write (and the
@@ -1156,13 +1164,13 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
   } sh;
   __shared__ __attribute__((aligned(16))) uint32_t wstage[NW][2][4 * 16];  // [w half][head][token] bf16 in high 16 bits
   __shared__ __attribute__((aligned(16))) uint32_t wzero[4];              // B rows of the unused value columns
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = blockIdx.z, hkv = blockIdx.y, chunk = blockIdx.x;
   const int64_t qrow0 = (int64_t)b * A.q_heads + (int64_t)hkv * G;
   if (A.gate && !(A.gate[qrow0] | A.gate[qrow0 + 1] | A.gate[qrow0 + 2] | A.gate[qrow0 + 3]))
     return;                // no head of the group reads the cold tokens: the merge ignores them
 
-  if (threadIdx.x < 16) vtab[threadIdx.x] = bf16_pair(A.val_levels[threadIdx.x]);
+  if (threadIdx.x < 16) vtab[threadIdx.x] = bf16_pair(A.val_levels[threadIdx.x] * A.inv_sqrt_d);
   if (threadIdx.x < 4) wzero[threadIdx.x] = 0u;
 
   // key levels as int8 limbs: gamma ~= (256 hi + lo) / F, byte c of each table word = code c
@@ -1192,11 +1200,14 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
     for (int j = 0; j < 4; ++j) Aq[j] = __builtin_bit_cast(i32x4, w[j]);
 #pragma unroll
     for (int j = 0; j < 2; ++j) Aj[j] = __builtin_bit_cast(i32x4, w[4 + j]);
+    // logits in base-2 units (exp2(l2 - m2) = exp(logit - m)): the softmax scale, 1 / sqrt(d)
+    // and log2(e) ride on the part weights, the QJL coefficient on the sketch's
+    const float ks = A.scale * A.inv_sqrt_d * kLog2e, qs = A.scale * A.qjl_coef * kLog2e;
     const float bk = __uint_as_float(w[6][0]);
-    bk16 = 65536.0f * bk;
-    bk8 = 256.0f * bk;
-    bq = __uint_as_float(w[6][1]);
-    oq = __uint_as_float(w[6][2]);
+    bk16 = 65536.0f * bk * ks;
+    bk8 = 256.0f * bk * ks;
+    bq = __uint_as_float(w[6][1]) * qs;
+    oq = __uint_as_float(w[6][2]) * qs;
   }
   __syncthreads();
 
@@ -1212,7 +1223,8 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
   f32x4 acc[8];
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) acc[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float mrun = kNegInf;    // running maximum of head kg (uniform across its 16 lanes)
+  float mrun = kNegInf;    // running maximum (base-2 units) of head kg, uniform across its 16 lanes
+  float mthr = kNegInf;    // mrun + kLazy
   float lsum = 0.0f;       // this lane's share of sum_t p_t for head kg
   const int vh = n >> 1;   // head of this lane's value column (n < 8)
   // B rows of the value product: the w half (n & 1) of head vh for tokens 4 kg .. 4 kg + 3
@@ -1231,6 +1243,8 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
   const uint32_t rb = (uint32_t)A.rec_bytes;
   const uint32_t kofs = (uint32_t)(kg * 4 * BK), sofs = (uint32_t)(A.kbytes + 4 * kg);
   const uint32_t vofs = (uint32_t)(A.kbytes + A.sbytes + 16 * kg), nofs = (uint32_t)A.norm_off;
+  // lane offsets of the fields within a token's record run for the unclamped path
+  const uint32_t lrec = (uint32_t)n * rb;
   auto fetch = [&](int base, Fields& f) {
     const int p = base + n;
     uint32_t t = (uint32_t)min(p, c1 - 1);
@@ -1289,42 +1303,41 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
       if (QJL && (j & 1)) {
         i32x4 q;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) q[w] = (int)((cur.sw >> (2 * (j & 2) + w)) & 0x01010101u);
+        for (int w = 0; w < 4; ++w) q[w] = (int)(cur.sw & (0x01010101u << (2 * (j & 2) + w)));
         Cq = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aj[j >> 1], q, Cq, 0, 0, 0);
       }
     }
     // parts of head kg for token n: weights 2^24, 2^16, 2^8 (|C0[0]| < 2^21 and |C0[1]| < 2^22,
     // so 256 C0[0] + C0[1] fits in int32); sketch sum 2^16 Cq0 + 2^8 Cq1 + Cq2 < 2^31
-    float shat = cur.nk * A.inv_sqrt_d * fmaf((float)((C0[0] << 8) + C0[1]), bk16, (float)C0[2] * bk8);
-    if (QJL) {
-      const float qj = fmaf((float)((Cq[0] << 16) + (Cq[1] << 8) + Cq[2]), bq, oq);
-      shat = fmaf(A.qjl_coef * cur.nrho, qj, shat);
-    }
-    const float logit = cur.valid ? A.scale * shat : kNegInf;
-    if (LOGITS && cur.valid) A.logits[(qrow0 + kg) * A.logit_stride + base + n] = logit;
+    float l2 = cur.nk * fmaf((float)((C0[0] << 8) + C0[1]), bk16, (float)C0[2] * bk8);
+    if (QJL) l2 = fmaf(cur.nrho, fmaf((float)((Cq[0] << 16) + (Cq[1] << 8) + Cq[2]), bq, oq), l2);
+    const float logit = cur.valid ? l2 : kNegInf;
+    if (LOGITS && cur.valid) A.logits[(qrow0 + kg) * A.logit_stride + base + n] = logit * kLn2;
     // ---- running maximum per head, shared by its 16 lanes, raised lazily (rare branch) ----
-    if (__ballot(logit > mrun + kLazy) != 0ull) {
+    if (__ballot(logit > mthr) != 0ull) {
       float tmax = logit;
 #pragma unroll
       for (int msk = 1; msk < 16; msk <<= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, msk));
-      const bool raise = tmax > mrun + kLazy;         // uniform within each head
-      const float fct = raise ? (mrun == kNegInf ? 0.0f : __expf(mrun - tmax)) : 1.0f;
+      const bool raise = tmax > mthr;                 // uniform within each head
+      const float fct = raise ? (mrun == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mrun - tmax)) : 1.0f;
       lsum *= fct;
       mrun = raise ? tmax : mrun;
+      mthr = mrun + kLazy;
       // rescale the value accumulators of head vh by that head's factor
       const float fv = __shfl(fct, 16 * (vh & 3));    // lane 16 h holds head h's factor
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) acc[mt] *= fv;
     }
-    const float p = cur.valid ? __expf(logit - mrun) : 0.0f;
+    // an invalid token's logit is -inf, and mrun is finite once a step has run (its first
+    // token is valid), so only a gathered step (invalid indices anywhere) needs the select
+    const float p = (GATHER && !cur.valid) ? 0.0f : __builtin_amdgcn_exp2f(logit - mrun);
     lsum += p;
     {
-      // w = hi + lo: hi rounded to bf16, lo the remainder truncated to bf16 (2^-17 relative)
-      const uint32_t wb = __float_as_uint(p * cur.nv * A.inv_sqrt_d);
-      const uint32_t hi = (wb + 0x7FFFu + ((wb >> 16) & 1u)) & 0xFFFF0000u;
-      const uint32_t lo = __float_as_uint(__uint_as_float(wb) - __uint_as_float(hi)) & 0xFFFF0000u;
-      wst[kg * 16 + n] = hi;
-      wst[64 + kg * 16 + n] = lo;
+      // w = hi + lo, hi = w truncated to bf16, lo = w - hi; the value products read the top 16
+      // bits of each word, so lo is truncated to bf16 as well (w within 2^-14 relative)
+      const float w = p * cur.nv;
+      wst[kg * 16 + n] = __float_as_uint(w);
+      wst[64 + kg * 16 + n] = __float_as_uint(w - __uint_as_float(__float_as_uint(w) & 0xFFFF0000u));
     }
     // this token's value codes, coordinate quarter kg: word r = coordinate octet 4 kg + r
 #pragma unroll
@@ -1386,8 +1399,8 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
   for (int msk = 1; msk < 16; msk <<= 1) lsum += __shfl_xor(lsum, msk);
   __syncthreads();              // every wave is done with the staging area the merge reuses
   float (*red)[G][D + 2] = sh.red;
-  if (n == 0) {                 // lane 16 h: head h's m and l
-    red[wave][kg][0] = mrun;
+  if (n == 0) {                 // lane 16 h: head h's m (natural units) and l
+    red[wave][kg][0] = mrun * kLn2;
     red[wave][kg][1] = lsum;
   }
   if (n < 8 && (n & 1) == 0) {  // column (h, hi half) lanes: o[h][8 (4 kg + r) + mt]
