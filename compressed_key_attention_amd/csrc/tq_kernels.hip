@@ -2664,6 +2664,8 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs A) {
 constexpr int kScanQB = 32;                 // queries per workgroup
 constexpr int kScanGroups = kScanQB / 4;
 constexpr int kScanWaveTok = 64;            // tokens per wave step (4 tiles of 16)
+constexpr int kScanWaves = 4;               // waves per workgroup
+constexpr int kScanThreads = 64 * kScanWaves;
 constexpr int kScanBlockTok = 2048;         // tokens per workgroup
 
 struct ScanMfmaArgs {
@@ -2680,7 +2682,7 @@ constexpr int kScanChunks = kScanLaneWords / 4;
 constexpr size_t kScanLds = (size_t)kScanGroups * kScanChunks * 64 * 16;
 
 template <int BK, bool QJL>
-__global__ __launch_bounds__(256, 2) void scan_mfma_kernel(ScanMfmaArgs A) {
+__global__ __launch_bounds__(kScanThreads, 2) void scan_mfma_kernel(ScanMfmaArgs A) {
   constexpr int NT = kScanWaveTok / 16;
   extern __shared__ u32x4 qop_lds[];                   // [group][16-byte chunk][lane]
   auto qop = [&](int g, int c, int l) -> u32x4& { return qop_lds[(g * kScanChunks + c) * 64 + l]; };
@@ -2744,9 +2746,9 @@ __global__ __launch_bounds__(256, 2) void scan_mfma_kernel(ScanMfmaArgs A) {
   int64_t t0 = tb0 + (int64_t)wave * kScanWaveTok;
   Raw cur;
   if (t0 < tb1) fetch(t0, cur);
-  for (; t0 < tb1; t0 += 4 * kScanWaveTok) {
+  for (; t0 < tb1; t0 += kScanWaves * kScanWaveTok) {
     Raw nxt;
-    const int64_t t1 = t0 + 4 * kScanWaveTok;
+    const int64_t t1 = t0 + kScanWaves * kScanWaveTok;
     if (t1 < tb1) fetch(t1, nxt);
     // token operands of the 4 tiles
     i32x4 Bk[NT][6], Bs[NT][2];
@@ -2828,7 +2830,7 @@ __global__ __launch_bounds__(256, 2) void scan_mfma_kernel(ScanMfmaArgs A) {
 template <int BK, bool QJL>
 static void launch_scan_mfma(dim3 grid, const ScanMfmaArgs& a, hipStream_t stream) {
   allow_lds(scan_mfma_kernel<BK, QJL>, kScanLds);
-  hipLaunchKernelGGL((scan_mfma_kernel<BK, QJL>), grid, dim3(256), kScanLds, stream, a);
+  hipLaunchKernelGGL((scan_mfma_kernel<BK, QJL>), grid, dim3(kScanThreads), kScanLds, stream, a);
 }
 
 hipError_t launch_scan(const Consts& c, const DevConsts& dc, const ScanPlan& plan, const void* q, tq_dtype q_dt,
