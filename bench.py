@@ -603,8 +603,8 @@ def cpu_baseline_monarch(w, h, snapshot, qs, ks, vs, window, budget_s: float = 8
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="llama8b_decode_32k",
                     choices=DECODE_WORKLOADS + ["sparse_128k_top2048", "bulk_64k_scan", "monarch_tinyllama"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
