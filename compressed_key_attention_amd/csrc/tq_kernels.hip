@@ -2037,8 +2037,8 @@ SelectPlan plan_select(const Consts& c, int batch, int heads, int64_t capacity) 
   const size_t units = (size_t)std::max(batch, 1) * heads;
   const size_t cap = (size_t)std::max<int64_t>(capacity, 1);
   p.n_chunks = (int)((cap + 4095) / 4096);
-  p.ws_lut = 0;                                                       // i32 [units][d/8][256]
-  p.ws_scores = p.ws_lut + align256(units * (c.d / 8) * 256 * 4);     // i32 [units][capacity]
+  p.ws_lut = 0;                                                       // i32 [units][d/4][16]
+  p.ws_scores = p.ws_lut + align256(units * (c.d / 4) * 16 * 4);      // i32 [units][capacity]
   p.ws_hist = p.ws_scores + align256(units * cap * 4);                // i32 [units][4096]
   p.ws_cand = p.ws_hist + align256(units * kSelBinsTotal * 4);        // u32x2 [units][capacity]:
                                                                       // chunk c's candidates at 4096 c
@@ -2099,11 +2099,7 @@ __global__ __launch_bounds__(256) void select_lut_kernel(const void* q, tq_dtype
     comb[e] = (int32_t)s;
   }
   __syncthreads();
-  // byte table: two groups per index byte (low nibble = even group)
-  for (int e = threadIdx.x; e < (ng / 2) * 256; e += blockDim.x) {
-    const int pg = e / 256, byte = e % 256;
-    lut_out[unit * (ng / 2) * 256 + e] = comb[(2 * pg) * 16 + (byte & 15)] + comb[(2 * pg + 1) * 16 + (byte >> 4)];
-  }
+  for (int e = threadIdx.x; e < ng * 16; e += blockDim.x) lut_out[unit * ng * 16 + e] = comb[e];
 }
 
 // Selection runs in five launches (lut and exact: one workgroup per unit; score, filter and
@@ -2157,14 +2153,17 @@ template <int NB>
 __global__ __launch_bounds__(256) void select_score_kernel(const uint8_t* index, const int32_t* lut_all,
                                                            const int32_t* seq_lens, int heads, int64_t capacity,
                                                            int32_t* scores, int32_t* hist_all) {
-  __shared__ int32_t lut[NB * 256];
+  // one 16-entry table per 4-channel group: a lookup instruction reads one table, whose 16
+  // words sit in 16 distinct banks, so lookups never conflict (equal patterns broadcast)
+  constexpr int NG = 2 * NB;
+  __shared__ int32_t lut[NG * 16];
   __shared__ int32_t hist[kSelBins];
   const int h = blockIdx.y, b = blockIdx.z;
   const int64_t unit = (int64_t)b * heads + h;
   const int64_t n = min((int64_t)seq_lens[b], capacity);
   const int64_t t0 = (int64_t)blockIdx.x * kSelChunk;
   if (t0 >= n) return;
-  for (int e = threadIdx.x; e < NB * 256; e += 256) lut[e] = lut_all[unit * NB * 256 + e];
+  for (int e = threadIdx.x; e < NG * 16; e += 256) lut[e] = lut_all[unit * NG * 16 + e];
   for (int e = threadIdx.x; e < kSelBins; e += 256) hist[e] = 0;
   __syncthreads();
   const uint8_t* base = index + (unit * capacity + t0) * NB;
@@ -2189,9 +2188,22 @@ __global__ __launch_bounds__(256) void select_score_kernel(const uint8_t* index,
       } else {
         w[0] = r[j].x; w[1] = r[j].y;
       }
+      // index byte k holds groups 2 k (low nibble) and 2 k + 1; nibbles pre-scaled to byte
+      // offsets within a table, so each lookup address is one byte extract
+      const uint8_t* lb = reinterpret_cast<const uint8_t*>(lut);
       int32_t s = 0;
 #pragma unroll
-      for (int g = 0; g < NB; ++g) s += lut[g * 256 + ((w[g / 4] >> (8 * (g % 4))) & 255u)];
+      for (int i = 0; i < NB / 4; ++i) {
+        uint32_t lo = (w[i] << 2) & 0x3C3C3C3Cu, hi = (w[i] >> 2) & 0x3C3C3C3Cu;
+        asm volatile("" : "+v"(lo));
+        asm volatile("" : "+v"(hi));
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const int g = 2 * (4 * i + kb);
+          s += *reinterpret_cast<const int32_t*>(lb + 64 * g + ((lo >> (8 * kb)) & 0xFFu));
+          s += *reinterpret_cast<const int32_t*>(lb + 64 * (g + 1) + ((hi >> (8 * kb)) & 0xFFu));
+        }
+      }
       sc[t] = s;
       atomicAdd(&hist[order_key(s) >> kSelDigitShift], 1);
     }
