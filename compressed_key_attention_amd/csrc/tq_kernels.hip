@@ -1848,7 +1848,7 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
 // sub-vectors (0 for a pattern without members).  Sums are float64 and taken in a fixed
 // order (per-chunk partial sums, then chunks in order), so the result is deterministic.
 // =========================================================================================
-constexpr int kIndexSub = 128;   // tokens staged per sub-tile in the centroid pass
+constexpr int kIndexSub = 64;    // tokens staged per sub-tile in the pattern / centroid pass
 
 IndexPlan plan_index(const Consts& c, int batch, int heads, int64_t n_tokens) {
   IndexPlan p;
@@ -1882,21 +1882,69 @@ struct IndexArgs {
   float* mean_out;
 };
 
+// Eight consecutive elements of a key row as raw words (16-bit types: 4 words, float32: 8),
+// converted later, so that a load can stay in flight across other work.
+template <tq_dtype DT>
+__device__ __forceinline__ void load8_raw(const void* base, int64_t off, uint32_t (&r)[8]) {
+  if constexpr (DT == TQ_F32) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + off);
+    const uint4 a = p[0], b = p[1];
+    r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w; r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
+  } else {
+    const uint4 a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+    r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
+  }
+}
+template <tq_dtype DT>
+__device__ __forceinline__ void cvt8(const uint32_t (&r)[8], float (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if constexpr (DT == TQ_F32) v[i] = __uint_as_float(r[i]);
+    else {
+      const uint32_t h = (i & 1) ? r[i / 2] >> 16 : r[i / 2] & 0xFFFFu;
+      v[i] = DT == TQ_BF16 ? bf16_bits_to_f32(h) : f16_bits_to_f32(h);
+    }
+  }
+}
+
+// Per-chunk channel sums of the keys.  Thread (token lane tl, channel octet cg) sums channels
+// 8 cg .. 8 cg + 7 of tokens t0 + tl, t0 + tl + L, ... in order (16-byte loads; the host checks
+// that base and strides are 16-byte aligned); the L lanes' sums are then added in lane order.
+template <tq_dtype DT>
 __global__ __launch_bounds__(256) void index_mean_kernel(IndexArgs A) {
-  __shared__ double part[256];
+  __shared__ double part[256 * 8];
   const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z, d = A.d;
-  const int lanes_per_ch = blockDim.x / d;  // token lanes
-  const int ch = threadIdx.x % d, tl = threadIdx.x / d;
+  const int ncg = d / 8, L = 256 / ncg;
+  const int cg = threadIdx.x % ncg, tl = threadIdx.x / ncg;
   const int64_t t0 = (int64_t)chunk * A.chunk, t1 = min(A.n_tokens, t0 + A.chunk);
-  double s = 0.0;
-  for (int64_t t = t0 + tl; t < t1; t += lanes_per_ch)
-    s += (double)load_elem(A.k, A.dt, b * A.seq_stride + t * A.tok_stride + h * A.head_stride + ch);
-  part[threadIdx.x] = s;
+  const int64_t base = (int64_t)b * A.seq_stride + (int64_t)h * A.head_stride + 8 * cg;
+  double s[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s[i] = 0.0;
+  // four rows in flight per round (clamped loads; rows past t1 are not added)
+  for (int64_t t = t0 + tl; t < t1; t += 4 * L) {
+    uint32_t raw[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load8_raw<DT>(A.k, base + min(t + u * L, t1 - 1) * A.tok_stride, raw[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float v[8];
+      cvt8<DT>(raw[u], v);
+      if (t + u * L < t1)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s[i] += (double)v[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) part[threadIdx.x * 8 + i] = s[i];
   __syncthreads();
   if (tl == 0) {
-    double tot = 0.0;
-    for (int u = 0; u < lanes_per_ch; ++u) tot += part[u * d + ch];
-    A.mean_part[(((int64_t)b * A.heads + h) * A.n_chunks + chunk) * d + ch] = tot;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      double tot = 0.0;
+      for (int u = 0; u < L; ++u) tot += part[(u * ncg + cg) * 8 + i];
+      A.mean_part[(((int64_t)b * A.heads + h) * A.n_chunks + chunk) * d + 8 * cg + i] = tot;
+    }
   }
 }
 
@@ -1912,75 +1960,128 @@ __global__ void index_mean_final_kernel(IndexArgs A) {
   }
 }
 
-// Patterns of a chunk of tokens (index records) and per-chunk centroid sums.
+// Patterns of a chunk of tokens (index records) and per-chunk centroid sums, one sub-tile of
+// kIndexSub tokens at a time, all 256 threads in every phase:
+//   load     thread (token, channel octet): 16-byte loads into a padded float tile
+//   pattern  thread (token, index byte): 8 comparisons with mu, one record byte
+//   centroid thread (channel, slice): the slice's tokens in order, sum[slice][pattern][channel]
+//            += k - mu (float64, in LDS).  Four tokens per round: their four partial sums are
+//            read together and a later token of the same pattern adds to the earlier one's
+//            result, so every sum still takes its tokens in order.
+// The chunk's sums are the slices' sums in slice order (the tokens of a sub-tile are split
+// into contiguous slices), so the result is deterministic.
+template <int D, tq_dtype DT>
 __global__ __launch_bounds__(256) void index_pattern_kernel(IndexArgs A) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z, d = A.d, ng = d / 4;
+  constexpr int NG = D / 4, NCG = D / 8, S = 256 / D, TPS = kIndexSub / S, KS = D + 4;
+  static_assert(TPS % 4 == 0, "slices take whole rounds of four tokens");
+  __shared__ float mu[D];
+  __shared__ __attribute__((aligned(16))) float kt[kIndexSub * KS];
+  __shared__ __attribute__((aligned(4))) uint8_t pat[NG * kIndexSub];   // [group][token]
+  __shared__ double acc[S * 16 * D];          // [slice][pattern][channel]
+  __shared__ int32_t cnt[S * NG * 16];        // [slice][group][pattern]
+  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int64_t unit = (int64_t)b * A.heads + h;
-  float* mu = reinterpret_cast<float*>(smem);                       // [d]
-  float* kt = mu + d;                                               // [kIndexSub][d] (k - mu as float64 later)
-  uint8_t* pat = reinterpret_cast<uint8_t*>(kt + kIndexSub * d);    // [kIndexSub][ng]
-  double* acc = reinterpret_cast<double*>(pat + ((kIndexSub * ng + 7) / 8) * 8);  // [d][16]
-  int32_t* cnt = reinterpret_cast<int32_t*>(acc + d * 16);          // [ng][16]
-  for (int i = threadIdx.x; i < d; i += blockDim.x) mu[i] = A.mu[unit * d + i];
-  for (int i = threadIdx.x; i < d * 16; i += blockDim.x) acc[i] = 0.0;
-  for (int i = threadIdx.x; i < ng * 16; i += blockDim.x) cnt[i] = 0;
-  __syncthreads();
+  for (int i = threadIdx.x; i < D; i += 256) mu[i] = A.mu[unit * D + i];
+  for (int i = threadIdx.x; i < S * 16 * D; i += 256) acc[i] = 0.0;
+  for (int i = threadIdx.x; i < S * NG * 16; i += 256) cnt[i] = 0;
+  const int64_t base = (int64_t)b * A.seq_stride + (int64_t)h * A.head_stride;
   const int64_t t0 = (int64_t)chunk * A.chunk, t1 = min(A.n_tokens, t0 + A.chunk);
+  const int ch = threadIdx.x % D, sl = threadIdx.x / D, g = ch / 4;
+  double* as = acc + sl * 16 * D + ch;
+  // the next sub-tile's keys are loaded into registers while this one is processed
+  constexpr int NL = kIndexSub * NCG / 256;    // (token, octet) items per thread
+  uint32_t nxt[NL][8];                         // raw, converted when stored
+  auto load_tile = [&](int64_t s0) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int e = threadIdx.x + 256 * i, tt = e / NCG, cg = e % NCG;
+      load8_raw<DT>(A.k, base + min(s0 + tt, t1 - 1) * A.tok_stride + 8 * cg, nxt[i]);   // clamped
+    }
+  };
+  if (t0 < t1) load_tile(t0);
   for (int64_t s0 = t0; s0 < t1; s0 += kIndexSub) {
     const int ns = (int)min((int64_t)kIndexSub, t1 - s0);
-    for (int e = threadIdx.x; e < ns * d; e += blockDim.x) {
-      const int tt = e / d, ch = e % d;
-      kt[e] = load_elem(A.k, A.dt, b * A.seq_stride + (s0 + tt) * A.tok_stride + h * A.head_stride + ch);
+    __syncthreads();            // the previous sub-tile's readers are done
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int e = threadIdx.x + 256 * i, tt = e / NCG, cg = e % NCG;
+      float v[8];
+      cvt8<DT>(nxt[i], v);
+      if (tt >= ns)             // rows past the sub-tile's tokens: k = mu, pattern 0 (adds 0)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = mu[8 * cg + j];
+      float4* dst = reinterpret_cast<float4*>(kt + tt * KS + 8 * cg);
+      dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+      dst[1] = make_float4(v[4], v[5], v[6], v[7]);
     }
+    if (s0 + kIndexSub < t1) load_tile(s0 + kIndexSub);
     __syncthreads();
-    // one thread per token: pattern bits, index record
-    for (int tt = threadIdx.x; tt < ns; tt += blockDim.x) {
-      uint8_t* rec = A.index + (unit * A.capacity + A.first_slot + s0 + tt) * (d / 8);
-      for (int g2 = 0; g2 < ng; g2 += 2) {
-        uint32_t byte = 0;
-        for (int u = 0; u < 2; ++u) {
-          uint32_t p = 0;
-          for (int j = 0; j < 4; ++j) p |= (kt[tt * d + 4 * (g2 + u) + j] >= mu[4 * (g2 + u) + j] ? 1u : 0u) << j;
-          pat[tt * ng + g2 + u] = (uint8_t)p;
-          byte |= p << (4 * u);
-        }
-        rec[g2 / 2] = (uint8_t)byte;
+    for (int e = threadIdx.x; e < kIndexSub * NCG; e += 256) {
+      const int tt = e / NCG, pg = e % NCG;     // index byte pg: groups 2 pg (low nibble), 2 pg + 1
+      uint32_t byte = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) byte |= (kt[tt * KS + 8 * pg + j] >= mu[8 * pg + j] ? 1u : 0u) << j;
+      if (tt >= ns) byte = 0;
+      pat[(2 * pg) * kIndexSub + tt] = (uint8_t)(byte & 15u);
+      pat[(2 * pg + 1) * kIndexSub + tt] = (uint8_t)(byte >> 4);
+      if (tt < ns) {
+        int32_t* cs = cnt + (tt / TPS) * NG * 16;
+        atomicAdd(&cs[(2 * pg) * 16 + (byte & 15u)], 1);
+        atomicAdd(&cs[(2 * pg + 1) * 16 + (byte >> 4)], 1);
+        A.index[(unit * A.capacity + A.first_slot + s0 + tt) * (D / 8) + pg] = (uint8_t)byte;
       }
     }
     __syncthreads();
-    // one thread per channel: members' (k - mu) summed in token order
-    for (int ch = threadIdx.x; ch < d; ch += blockDim.x) {
-      const int g = ch / 4;
-      for (int tt = 0; tt < ns; ++tt) {
-        const int p = pat[tt * ng + g];
-        acc[ch * 16 + p] += (double)kt[tt * d + ch] - (double)mu[ch];
-        if ((ch & 3) == 0) cnt[g * 16 + p] += 1;
+    const double m = (double)mu[ch];
+    for (int r = 0; r < TPS; r += 4) {
+      int pp[4];
+      double vv[4], old[4];
+      const uint32_t p4 = *reinterpret_cast<const uint32_t*>(pat + g * kIndexSub + sl * TPS + r);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int tt = sl * TPS + r + u;
+        pp[u] = (p4 >> (8 * u)) & 15u;
+        vv[u] = (double)kt[tt * KS + ch] - m;   // 0 on padding rows
       }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) old[u] = as[pp[u] * D];
+      double nw[4];
+      nw[0] = old[0] + vv[0];
+      nw[1] = (pp[1] == pp[0] ? nw[0] : old[1]) + vv[1];
+      nw[2] = (pp[2] == pp[1] ? nw[1] : pp[2] == pp[0] ? nw[0] : old[2]) + vv[2];
+      nw[3] = (pp[3] == pp[2] ? nw[2] : pp[3] == pp[1] ? nw[1] : pp[3] == pp[0] ? nw[0] : old[3]) + vv[3];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) as[pp[u] * D] = nw[u];   // a later equal pattern's write wins
     }
-    __syncthreads();
   }
-  for (int e = threadIdx.x; e < ng * 16 * 4; e += blockDim.x) {
-    const int g = e / 64, p = (e / 4) % 16, j = e % 4;
-    A.csum[((unit * A.n_chunks + chunk) * ng + g) * 64 + p * 4 + j] = acc[(4 * g + j) * 16 + p];
+  __syncthreads();
+  for (int e = threadIdx.x; e < NG * 64; e += 256) {
+    const int gg = e / 64, p = (e / 4) % 16, j = e % 4;
+    double s = 0.0;
+#pragma unroll
+    for (int q = 0; q < S; ++q) s += acc[(q * 16 + p) * D + 4 * gg + j];
+    A.csum[((unit * A.n_chunks + chunk) * NG + gg) * 64 + p * 4 + j] = s;
   }
-  for (int e = threadIdx.x; e < ng * 16; e += blockDim.x)
-    A.ccnt[(unit * A.n_chunks + chunk) * ng * 16 + e] = cnt[e];
+  for (int e = threadIdx.x; e < NG * 16; e += 256) {
+    int n = 0;
+#pragma unroll
+    for (int q = 0; q < S; ++q) n += cnt[q * NG * 16 + e];
+    A.ccnt[(unit * A.n_chunks + chunk) * NG * 16 + e] = n;
+  }
 }
 
-__global__ void index_centroid_final_kernel(IndexArgs A) {
-  const int h = blockIdx.x, b = blockIdx.y, ng = A.d / 4;
+// One workgroup per (group, KV head, sequence); thread (pattern, channel) sums the chunks in
+// order.
+__global__ __launch_bounds__(64) void index_centroid_final_kernel(IndexArgs A) {
+  const int g = blockIdx.x, h = blockIdx.y, b = blockIdx.z, ng = A.d / 4, e = threadIdx.x, p = e / 4;
   const int64_t unit = (int64_t)b * A.heads + h;
-  for (int e = threadIdx.x; e < ng * 64; e += blockDim.x) {
-    const int g = e / 64, p = (e / 4) % 16;
-    double s = 0.0;
-    int64_t n = 0;
-    for (int c = 0; c < A.n_chunks; ++c) {
-      s += A.csum[((unit * A.n_chunks + c) * ng + g) * 64 + (e % 64)];
-      n += A.ccnt[(unit * A.n_chunks + c) * ng * 16 + g * 16 + p];
-    }
-    A.codebook[unit * ng * 64 + e] = n > 0 ? (float)(s / (double)n) : 0.0f;
+  double s = 0.0;
+  int64_t n = 0;
+  for (int c = 0; c < A.n_chunks; ++c) {
+    s += A.csum[((unit * A.n_chunks + c) * ng + g) * 64 + e];
+    n += A.ccnt[(unit * A.n_chunks + c) * ng * 16 + g * 16 + p];
   }
+  A.codebook[(unit * ng + g) * 64 + e] = n > 0 ? (float)(s / (double)n) : 0.0f;
 }
 
 hipError_t launch_sign_index(const Consts& c, const IndexPlan& plan, const void* k, tq_dtype dt,
@@ -2012,14 +2113,17 @@ hipError_t launch_sign_index(const Consts& c, const IndexPlan& plan, const void*
   A.codebook = codebook;
   A.mean_out = mean;
   dim3 grid(plan.n_chunks, heads, batch);
-  hipLaunchKernelGGL(index_mean_kernel, grid, dim3(256), 0, stream, A);
+  if (dt == TQ_F32) hipLaunchKernelGGL(index_mean_kernel<TQ_F32>, grid, dim3(256), 0, stream, A);
+  else if (dt == TQ_F16) hipLaunchKernelGGL(index_mean_kernel<TQ_F16>, grid, dim3(256), 0, stream, A);
+  else hipLaunchKernelGGL(index_mean_kernel<TQ_BF16>, grid, dim3(256), 0, stream, A);
   hipLaunchKernelGGL(index_mean_final_kernel, dim3(heads, batch), dim3(128), 0, stream, A);
-  const int ng = c.d / 4;
-  const size_t lds = c.d * 4 + (size_t)kIndexSub * c.d * 4 + ((kIndexSub * ng + 7) / 8) * 8 +
-                     (size_t)c.d * 16 * 8 + (size_t)ng * 16 * 4;
-  allow_lds(index_pattern_kernel, lds);
-  hipLaunchKernelGGL(index_pattern_kernel, grid, dim3(256), lds, stream, A);
-  hipLaunchKernelGGL(index_centroid_final_kernel, dim3(heads, batch), dim3(256), 0, stream, A);
+  if (c.d == 128 && dt == TQ_F32) hipLaunchKernelGGL((index_pattern_kernel<128, TQ_F32>), grid, dim3(256), 0, stream, A);
+  else if (c.d == 128 && dt == TQ_F16) hipLaunchKernelGGL((index_pattern_kernel<128, TQ_F16>), grid, dim3(256), 0, stream, A);
+  else if (c.d == 128) hipLaunchKernelGGL((index_pattern_kernel<128, TQ_BF16>), grid, dim3(256), 0, stream, A);
+  else if (dt == TQ_F32) hipLaunchKernelGGL((index_pattern_kernel<64, TQ_F32>), grid, dim3(256), 0, stream, A);
+  else if (dt == TQ_F16) hipLaunchKernelGGL((index_pattern_kernel<64, TQ_F16>), grid, dim3(256), 0, stream, A);
+  else hipLaunchKernelGGL((index_pattern_kernel<64, TQ_BF16>), grid, dim3(256), 0, stream, A);
+  hipLaunchKernelGGL(index_centroid_final_kernel, dim3(c.d / 4, heads, batch), dim3(64), 0, stream, A);
   return hipGetLastError();
 }
 
