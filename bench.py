@@ -405,6 +405,14 @@ def run_sparse(args, tq, W, ev):
     index = torch.empty((B, H, T, d // 8), dtype=torch.uint8, device=dev)
     book = torch.empty((B, H, d // 4, 16, 4), dtype=torch.float32, device=dev)
     h.build_sign_index(K, index, book)
+    # sign-index build (one-time): a warm call timed with events on the library's stream
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    h.build_sign_index(K, index, book)
+    e1.record()
+    torch.cuda.synchronize()
+    index_ms = e0.elapsed_time(e1)
     records = h.new_cache(B, H, T, dev)
     compress_ms = compress_once(ev, tq, h, K, V, records)
     del K, V
@@ -432,6 +440,10 @@ def run_sparse(args, tq, W, ev):
     line["roofline"] = roofline("select_score_kernel", w.name, alg_bytes, score_ms, None, fl_ms, ceiling)
     line["tokens_attended_per_s"] = B * H * w.top_k / (ms_per_step * 1e-3)
     line["compress"] = {"ms": compress_ms}
+    key_bytes = B * T * H * d * 2
+    line["sign_index_build"] = {"ms": index_ms, "key_bytes": key_bytes,
+                                "key_read_gbps": key_bytes / (index_ms * 1e-3) / 1e9,
+                                "note": "two passes over the bf16 keys (channel mean, then patterns and centroids)"}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_sparse(w, q, index, book, records)
     return line

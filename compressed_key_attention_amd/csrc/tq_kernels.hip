@@ -1657,25 +1657,27 @@ bool plan_decode(const Consts& c, int batch, int q_heads, int kv_heads, int64_t 
   plan->group = G;
   plan->hpl = hpl;
   plan->key_pairs = c.kb <= 3;
+  // split-K: aim at ~2 blocks per CU (3 on the matrix-core path, whose 256-thread blocks fit
+  // three to a CU); chunks of at least 64 tokens
+  const int64_t units = (int64_t)std::max(batch, 1) * kv_heads;
+  const int64_t target_blocks = (plan->mfma ? 3 : 2) * (int64_t)num_cus();
+  int64_t chunk = (n_max * units + target_blocks - 1) / std::max<int64_t>(target_blocks, 1);
+  chunk = std::max<int64_t>(chunk, 64);
+  chunk = std::min<int64_t>(chunk, 16384);
+  chunk = (chunk + 63) / 64 * 64;
+  plan->chunk = (int)chunk;
   const size_t key_tab = (size_t)G * (plan->key_pairs ? (c.d / 2) * (1 << (2 * c.kb)) : c.d * (1 << c.kb));
   const size_t sign_bytes_tab = (size_t)G * (c.m / 8) * 256;
   const size_t sign_nib_tab = (size_t)G * (c.m / 4) * 16;
   const size_t budget = 150 * 1024 / 4;
-  plan->sign_bytes = key_tab + sign_bytes_tab + kMaxLevels <= budget;
+  // byte-indexed sign tables halve the lookups but cost 8x the table build: only for chunks
+  // long enough to amortise it
+  plan->sign_bytes = chunk >= 2048 && key_tab + sign_bytes_tab + kMaxLevels <= budget;
   const size_t lut = key_tab + (plan->sign_bytes ? sign_bytes_tab : sign_nib_tab) + kMaxLevels;
   const size_t red = (size_t)kDecodeThreads * 36 + 64;
   const size_t floats = std::max(lut, red);
   if (floats > 160 * 1024 / 4) return false;
   plan->lds_bytes = floats * 4;
-  // split-K: aim at ~2 blocks per CU (3 on the matrix-core path, whose 256-thread blocks fit
-  // three to a CU)
-  const int64_t units = (int64_t)std::max(batch, 1) * kv_heads;
-  const int64_t target_blocks = (plan->mfma ? 3 : 2) * (int64_t)num_cus();
-  int64_t chunk = (n_max * units + target_blocks - 1) / std::max<int64_t>(target_blocks, 1);
-  chunk = std::max<int64_t>(chunk, 256);
-  chunk = std::min<int64_t>(chunk, 16384);
-  chunk = (chunk + 255) / 256 * 256;
-  plan->chunk = (int)chunk;
   plan->n_chunks = (int)std::max<int64_t>(1, (n_max + chunk - 1) / chunk);
   const size_t rows = (size_t)std::max(batch, 1) * q_heads;
   plan->ws_qx = 0;
