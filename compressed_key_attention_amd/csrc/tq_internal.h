@@ -69,6 +69,7 @@ struct DecodePlan {
   bool key_pairs;   // key LUT indexed by pairs of codes (else single codes)
   bool sign_bytes;  // QJL LUT indexed by bytes (else nibbles)
   bool mfma;        // matrix-core scan (head_dim 128, 4 query heads per KV head)
+  bool small;       // direct scan for short caches (chunks of at most 64 tokens)
   size_t lds_bytes;
   size_t ws_qx, ws_qs, ws_part, ws_bop, ws_total;   // workspace offsets / size
 };

@@ -822,6 +822,164 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_scan_kernel(DecodeArgs 
 }
 
 // -----------------------------------------------------------------------------------------
+// Direct scan for short caches (up to a few thousand tokens per (sequence, KV head)): one
+// workgroup per (chunk of at most 64 tokens, KV head, sequence).  The chunk's codes are
+// unpacked into LDS, then every (token, head) estimate, the chunk's softmax and every (head,
+// coordinate) output are computed directly from q_x, q_s and the level tables, with no
+// per-query lookup tables, whose build would outweigh a few dozen tokens.  Same estimator and
+// the same partial format (m, l, o_x) as decode_scan_kernel.
+// -----------------------------------------------------------------------------------------
+constexpr int kSmallThreads = 256;
+constexpr int64_t kSmallMaxN = 4096;      // tokens per (sequence, KV head) for the direct kernel
+constexpr int kSmallMaxTok = 64;
+constexpr int kSmallMaxG = 16;
+constexpr int kSmallMaxM = 128;
+
+template <int D, int BK, int BV>
+__global__ __launch_bounds__(kSmallThreads) void decode_small_kernel(DecodeArgs A) {
+  constexpr int NG32 = D / 32;
+  __shared__ float qx[kSmallMaxG][D + 1];
+  __shared__ float qs[kSmallMaxG][kSmallMaxM + 1];
+  __shared__ __attribute__((aligned(4))) uint8_t kc[kSmallMaxTok][D];          // key codes
+  __shared__ __attribute__((aligned(4))) uint8_t vc[kSmallMaxTok][D];          // value codes
+  __shared__ __attribute__((aligned(4))) uint8_t sb[kSmallMaxTok][kSmallMaxM]; // QJL bits
+  __shared__ float nr[kSmallMaxTok][3];            // r_k, rho, r_v
+  __shared__ int ok_t[kSmallMaxTok];
+  __shared__ float lg[kSmallMaxG][kSmallMaxTok + 1];   // logits, then weights p r_v / sqrt(d)
+  __shared__ float hm[kSmallMaxG], hl[kSmallMaxG];
+  __shared__ float kl[kMaxLevels], vl[kMaxLevels];
+  const int G = A.G, m = A.m, TOK = A.chunk, tid = threadIdx.x;
+  const int b = blockIdx.z, hkv = blockIdx.y, chunk = blockIdx.x;
+  const int64_t qrow0 = (int64_t)b * A.q_heads + (int64_t)hkv * G;
+  if (A.gate) {            // no head of the group reads the cold tokens: the merge ignores them
+    bool any = false;
+    for (int j = 0; j < G; ++j) any = any || A.gate[qrow0 + j] != 0;
+    if (!any) return;
+  }
+  const bool gather = A.sel_idx != nullptr;
+  const int n = gather ? A.k_sel : (int)min((int64_t)A.seq_lens[b], A.capacity);
+  const int c0 = chunk * TOK, nt = max(0, min(TOK, n - c0));
+  const uint8_t* recs = A.records + ((int64_t)b * A.kv_heads + hkv) * A.capacity * A.rec_bytes;
+  for (int e = tid; e < G * D; e += kSmallThreads) qx[e / D][e % D] = A.qx[(qrow0 + e / D) * D + e % D];
+  for (int e = tid; e < G * m; e += kSmallThreads) qs[e / m][e % m] = A.qs[(qrow0 + e / m) * m + e % m];
+  if (tid < kMaxLevels) {
+    kl[tid] = A.key_levels[tid];
+    vl[tid] = A.val_levels[tid];
+  }
+  // unpack: per token, NG32 key groups, NG32 value groups, m / 32 sign words and the norms
+  const int nsw = m / 32, per_t = 2 * NG32 + nsw + 1;
+  for (int e = tid; e < nt * per_t; e += kSmallThreads) {
+    const int t = e / per_t, pt = e % per_t;
+    int64_t tok = c0 + t;
+    bool ok = true;
+    if (gather) {
+      tok = A.sel_idx[((int64_t)b * A.kv_heads + hkv) * A.k_sel + c0 + t];
+      ok = tok >= 0 && tok < A.capacity;
+    }
+    const uint8_t* rec = recs + (ok ? tok : 0) * A.rec_bytes;
+    if (pt < 2 * NG32) {
+      const bool key = pt < NG32;
+      const int g = key ? pt : pt - NG32;
+      uint32_t w[4];
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(
+          rec + (key ? g * 4 * BK : A.kbytes + A.sbytes + g * 4 * BV));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = i < (key ? BK : BV) ? src[i] : 0u;
+      uint32_t* dst = reinterpret_cast<uint32_t*>(key ? &kc[t][32 * g] : &vc[t][32 * g]);
+      const int nb = key ? BK : BV;
+#pragma unroll
+      for (int j4 = 0; j4 < 8; ++j4) {          // four codes per word
+        uint32_t word = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int j = 4 * j4 + u;
+          const uint32_t code = nb == 3 ? group3_code(w[0], w[1], w[2], j) : field<4>(w, j * nb, nb);
+          word |= code << (8 * u);
+        }
+        dst[j4] = word;
+      }
+    } else if (pt < 2 * NG32 + nsw) {
+      const int wi = pt - 2 * NG32;
+      const uint32_t sw = reinterpret_cast<const uint32_t*>(rec + A.kbytes)[wi];
+      uint32_t* dst = reinterpret_cast<uint32_t*>(&sb[t][32 * wi]);
+#pragma unroll
+      for (int j4 = 0; j4 < 8; ++j4) {
+        const uint32_t nib = (sw >> (4 * j4)) & 15u;   // bits 4 j4 .. 4 j4 + 3, one per byte
+        dst[j4] = (nib & 1u) | ((nib & 2u) << 7) | ((nib & 4u) << 14) | ((nib & 8u) << 21);
+      }
+    } else {
+      const float* f = reinterpret_cast<const float*>(rec + A.norm_off);
+      nr[t][0] = f[0];
+      nr[t][1] = f[1];
+      nr[t][2] = f[2];
+      ok_t[t] = ok ? 1 : 0;
+    }
+  }
+  __syncthreads();
+  // estimates: L adjacent lanes per (token, head), each over every L-th coordinate and bit
+  const int items = nt * G;
+  int L = 1;
+  while (L < 8 && items * L * 2 <= kSmallThreads) L *= 2;
+  for (int i0 = 0; i0 < items; i0 += kSmallThreads / L) {
+    const int it = i0 + tid / L, s = tid % L;
+    const int t = it / G, h = it % G;
+    float dot = 0.0f, qd = 0.0f;
+    if (it < items) {
+      for (int i = s; i < D; i += L) dot = fmaf(qx[h][i], kl[kc[t][i]], dot);
+      for (int j = s; j < m; j += L) qd += sb[t][j] ? qs[h][j] : -qs[h][j];
+    }
+    for (int msk = 1; msk < L; msk <<= 1) {
+      dot += __shfl_xor(dot, msk);
+      qd += __shfl_xor(qd, msk);
+    }
+    if (it < items && s == 0) {
+      const float logit = ok_t[t] ? A.scale * fmaf(A.qjl_coef * nr[t][1], qd, nr[t][0] * A.inv_sqrt_d * dot)
+                                  : kNegInf;
+      lg[h][t] = logit;
+      if (A.logits && ok_t[t]) A.logits[(qrow0 + h) * A.logit_stride + c0 + t] = logit;
+    }
+  }
+  __syncthreads();
+  // the chunk's softmax per head: m, l, and the value weights p r_v / sqrt(d)
+  for (int h = tid; h < G; h += kSmallThreads) {
+    float mx = kNegInf;
+    for (int t = 0; t < nt; ++t) mx = fmaxf(mx, lg[h][t]);
+    float l = 0.0f;
+    for (int t = 0; t < nt; ++t) {
+      const float p = (mx == kNegInf || lg[h][t] == kNegInf) ? 0.0f : __expf(lg[h][t] - mx);
+      l += p;
+      lg[h][t] = p * nr[t][2] * A.inv_sqrt_d;
+    }
+    hm[h] = mx;
+    hl[h] = l;
+  }
+  __syncthreads();
+  const int stride = D + 2;
+  for (int e = tid; e < G * D; e += kSmallThreads) {
+    const int h = e / D, i = e % D;
+    float o = 0.0f;
+    for (int t = 0; t < nt; ++t) o = fmaf(lg[h][t], vl[vc[t][i]], o);
+    A.part[((qrow0 + h) * A.n_chunks + chunk) * stride + 2 + i] = o;
+  }
+  for (int h = tid; h < G; h += kSmallThreads) {
+    A.part[((qrow0 + h) * A.n_chunks + chunk) * stride] = hm[h];
+    A.part[((qrow0 + h) * A.n_chunks + chunk) * stride + 1] = hl[h];
+  }
+}
+
+template <int D>
+static void launch_small_d(const DecodeArgs& a, int kb, int vb, dim3 grid, hipStream_t st) {
+#define TQ_SM(BK_, BV_)                                                                           \
+  if (kb == BK_ && vb == BV_) {                                                                   \
+    hipLaunchKernelGGL((decode_small_kernel<D, BK_, BV_>), grid, dim3(kSmallThreads), 0, st, a);  \
+    return;                                                                                       \
+  }
+  TQ_SM(2, 2) TQ_SM(2, 3) TQ_SM(2, 4) TQ_SM(3, 2) TQ_SM(3, 3) TQ_SM(3, 4)
+  TQ_SM(4, 2) TQ_SM(4, 3) TQ_SM(4, 4)
+#undef TQ_SM
+}
+
+// -----------------------------------------------------------------------------------------
 // Matrix-core decode scan for head_dim 128 and 4 query heads per KV head (2- or 3-bit keys,
 // 4-bit values).  Same arithmetic as decode_scan_kernel, laid out for gfx950.  Each wave
 // takes 16 tokens per step:
@@ -1657,6 +1815,12 @@ bool plan_decode(const Consts& c, int batch, int q_heads, int kv_heads, int64_t 
   plan->group = G;
   plan->hpl = hpl;
   plan->key_pairs = c.kb <= 3;
+  // short caches off the matrix-core path with 4+ query heads per KV head (whose per-query
+  // tables cost the most to build): the direct kernel, chunks of 8 .. 64 tokens aiming at ~2
+  // workgroups per CU
+  plan->small = !plan->mfma && n_max <= kSmallMaxN && G >= 4 && G <= kSmallMaxG && c.m <= kSmallMaxM &&
+                c.m % 32 == 0 &&
+                (c.d == 64 || c.d == 128);
   // split-K: aim at ~2 blocks per CU (3 on the matrix-core path, whose 256-thread blocks fit
   // three to a CU); chunks of at least 64 tokens
   const int64_t units = (int64_t)std::max(batch, 1) * kv_heads;
@@ -1665,6 +1829,11 @@ bool plan_decode(const Consts& c, int batch, int q_heads, int kv_heads, int64_t 
   chunk = std::max<int64_t>(chunk, 64);
   chunk = std::min<int64_t>(chunk, 16384);
   chunk = (chunk + 63) / 64 * 64;
+  if (plan->small) {
+    const int64_t want = (n_max * units + 2 * num_cus() - 1) / (2 * (int64_t)num_cus());
+    chunk = 8;
+    while (chunk < want && chunk < kSmallMaxTok) chunk *= 2;
+  }
   plan->chunk = (int)chunk;
   const size_t key_tab = (size_t)G * (plan->key_pairs ? (c.d / 2) * (1 << (2 * c.kb)) : c.d * (1 << c.kb));
   const size_t sign_bytes_tab = (size_t)G * (c.m / 8) * 256;
@@ -1796,6 +1965,9 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
   ev.before(stream);
   if (mfma) {
     launch_mfma_scan(a, c.kb, c.m > 0, sel_idx != nullptr, logits != nullptr, grid, stream);
+  } else if (plan.small) {
+    if (c.d == 128) launch_small_d<128>(a, c.kb, c.vb, grid, stream);
+    else launch_small_d<64>(a, c.kb, c.vb, grid, stream);
   } else if (plan.hpl == 4) {
     launch_scan_hpl<4>(a, c.kb, c.vb, grid, plan.lds_bytes, stream);
   } else {

@@ -298,6 +298,25 @@ def test_decode_matrix_core_path_variants(kb, m):
     _decode_case(w, [1500, 1500], sel=torch.from_numpy(sel).cuda())
 
 
+@pytest.mark.parametrize("d,kb,vb,m,hq", [(64, 2, 2, 0, 16), (128, 4, 3, 64, 32), (64, 3, 3, 128, 32),
+                                           (128, 2, 4, 128, 64), (64, 4, 4, 32, 16)])
+def test_decode_short_cache_direct_kernel(d, kb, vb, m, hq):
+    """Short caches with 4 or more query heads per KV head off the matrix-core path run the
+    direct kernel (codes unpacked per chunk, no per-query tables): key and value widths 2-4,
+    sketches of 0-128 bits, group sizes 4-16, ragged lengths, an empty chunk tail, gather."""
+    base = W.small(W.WORKLOADS["tinyllama_layer"], tokens=900, batch=2, hot_tokens=0)
+    w = W.Workload(**{**base.__dict__, "head_dim": d, "key_bits": kb, "value_bits": vb, "qjl_dim": m,
+                      "q_heads": hq})
+    _decode_case(w, [900, 333])
+    rng = np.random.default_rng(d + kb + vb + m)
+    sel = np.full((2, w.kv_heads, 150), -1, np.int32)
+    for b in range(2):
+        for hh in range(w.kv_heads):
+            k = rng.integers(1, 150)
+            sel[b, hh, :k] = np.sort(rng.choice(900, size=k, replace=False))
+    _decode_case(w, [900, 900], sel=torch.from_numpy(sel).cuda())
+
+
 def test_decode_rejects_small_workspace():
     tq = _tq()
     h = tq.Handle(128, 3, 128, 4, 1, 2)
