@@ -3359,19 +3359,31 @@ __global__ __launch_bounds__(1024) void monarch_prep_kernel(MonarchArgs M) {
     copy_elem(M.hot_v, M.v_new, M.hot_dt, (unit * M.hot_cap + slot) * D + i, unit * D + i);
   }
   const int64_t qrow0 = (int64_t)b * M.q_heads + (int64_t)hkv * G;
+  if (M.cold_gate == INFINITY) {      // no gate: every head reads the cold tokens
+    if (threadIdx.x < G) M.gate[qrow0 + threadIdx.x] = 1;
+    return;
+  }
   for (int e = threadIdx.x; e < G * D; e += blockDim.x) qv[e / D][e % D] = load_elem(M.q, M.q_dt, qrow0 * D + e);
   __syncthreads();
-  // best hot logit per head over the ring's tokens and the step's token (read from k_new)
+  // best hot logit per head over the ring's tokens and the step's token (read from k_new); the
+  // next round's keys are loaded while this round's are used
   const int sub = threadIdx.x % LPK, tok = threadIdx.x / LPK;
   float mx[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) mx[j] = kNegInf;
-  for (int t0 = 0; t0 <= n; t0 += TPI) {
+  auto load_key = [&](int t0, float (&kv)[8]) {
     const int t = min(t0 + tok, n);
     int64_t rs = st + t;
     if (rs >= M.hot_cap) rs -= M.hot_cap;
-    float kv[8];
     load8(t < n ? M.hot_k : M.k_new, M.hot_dt, (t < n ? (unit * M.hot_cap + rs) * D : unit * D) + 8 * sub, kv);
+  };
+  float kn[8];
+  load_key(0, kn);
+  for (int t0 = 0; t0 <= n; t0 += TPI) {
+    float kv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kv[i] = kn[i];
+    if (t0 + TPI <= n) load_key(t0 + TPI, kn);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       if (j >= G) break;
@@ -3426,10 +3438,13 @@ __global__ __launch_bounds__(1024) void monarch_promote_kernel(MonarchArgs M) {
       if (t < n_cold) {
         float w = 0.0f;
         const float* lg = M.logits + (int64_t)b * Hq * M.logit_stride + t;
-#pragma unroll 8
-        for (int h = 0; h < Hq; ++h) {
-          const float v = lg[(int64_t)h * M.logit_stride];          // unconditional: loads in flight
-          if (s_gate[h]) w = fmaxf(w, __expf(v - s_lse[h]));
+        for (int h0 = 0; h0 < Hq; h0 += 32) {
+          float v[32];
+#pragma unroll
+          for (int u = 0; u < 32; ++u) v[u] = lg[(int64_t)min(h0 + u, Hq - 1) * M.logit_stride];   // 32 loads in flight
+#pragma unroll
+          for (int u = 0; u < 32; ++u)
+            if (h0 + u < Hq && s_gate[h0 + u]) w = fmaxf(w, __expf(v[u] - s_lse[h0 + u]));
         }
         const int hc = w >= M.promote_weight ? hits[t] + 1 : 0;
         prom = hc >= M.promote_steps;
@@ -3464,7 +3479,13 @@ __global__ __launch_bounds__(1024) void monarch_promote_kernel(MonarchArgs M) {
       for (int i = threadIdx.x; i < 2 * D; i += blockDim.x) {
         const int which = i / D, o = i % D;
         double acc = 0.0;
-        for (int j = 0; j < D; ++j) acc = fma((double)M.pi_t[o * D + j], lev[which][j], acc);
+        for (int j0 = 0; j0 < D; j0 += 32) {      // 32 loads of the row of Pi^T in flight
+          float pv[32];
+#pragma unroll
+          for (int u = 0; u < 32; ++u) pv[u] = M.pi_t[o * D + j0 + u];
+#pragma unroll
+          for (int u = 0; u < 32; ++u) acc = fma((double)pv[u], lev[which][j0 + u], acc);
+        }
         store_f64(which ? M.hot_v : M.hot_k, M.hot_dt, (unit * M.hot_cap + slot) * D + o, acc);
       }
       __syncthreads();
@@ -3545,8 +3566,13 @@ __global__ __launch_bounds__(512) void monarch_evict_kernel(MonarchArgs M) {
       const int h = t / (2 * D), w = (t / D) & 1, o = t % D;
       const double* xv = vin + (h * 2 + w) * D;
       double acc = 0.0;
-#pragma unroll 8
-      for (int j = 0; j < D; ++j) acc = fma((double)M.pi[o * D + j], xv[j], acc);
+      for (int j0 = 0; j0 < D; j0 += 32) {        // 32 loads of the row of Pi in flight
+        float pv[32];
+#pragma unroll
+        for (int u = 0; u < 32; ++u) pv[u] = M.pi[o * D + j0 + u];
+#pragma unroll
+        for (int u = 0; u < 32; ++u) acc = fma((double)pv[u], xv[j0 + u], acc);
+      }
       xr[t] = acc;
       const double r = nrm[h][w];
       const double scale = r > 0.0 ? c.sqrt_d / r : 0.0;
@@ -3569,8 +3595,13 @@ __global__ __launch_bounds__(512) void monarch_evict_kernel(MonarchArgs M) {
     for (int t = threadIdx.x; t < H * c.m; t += blockDim.x) {
       const int h = t / c.m, j = t % c.m;
       double acc = 0.0;
-#pragma unroll 8
-      for (int k2 = 0; k2 < D; ++k2) acc = fma((double)M.s[j * D + k2], er[h * D + k2], acc);
+      for (int k0 = 0; k0 < D; k0 += 32) {        // 32 loads of the row of S in flight
+        float sv[32];
+#pragma unroll
+        for (int u = 0; u < 32; ++u) sv[u] = M.s[j * D + k0 + u];
+#pragma unroll
+        for (int u = 0; u < 32; ++u) acc = fma((double)sv[u], er[h * D + k0 + u], acc);
+      }
       bits[t] = (float)acc >= 0.0f ? 1u : 0u;
     }
     __syncthreads();

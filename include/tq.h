@@ -220,7 +220,8 @@ tq_status tq_set_profile_events(hipEvent_t start, hipEvent_t stop);
  * One step, for queries q[b][hq][d] and the step's token k_new/v_new[b][h][d] (hot_dt):
  *  1. the step's token joins the ring (newest);
  *  2. query head hq reads the cold tokens iff scale * max_t <q, k_t> over the ring is below
- *     cfg->cold_gate (+inf: always); out / lse = attention over the ring plus, for open heads,
+ *     cfg->cold_gate (+inf: always, and the ring logits are then not formed for the gate); out /
+ *     lse = attention over the ring plus, for open heads,
  *     the cold tokens (TurboQuant estimator, as tq_decode_attention), one softmax;
  *  3. a cold token whose weight p (maximum over the open heads) is >= cfg->promote_weight
  *     counts one more consecutive step, else its count resets; at cfg->promote_steps (0: never)
