@@ -290,6 +290,19 @@ def oracle_baseline(units, make_job, tokens_per_unit, total_units, unit_name, bu
             "cpu_model": cpu_model()}
 
 
+def compute_dtype(w) -> str:
+    """Arithmetic of the step's scan: int8 matrix-core key products (exact in int32) and bf16
+    matrix-core value products accumulated in fp32 on the matrix-core paths (decode at head_dim
+    128 with 4 query heads per KV head; the bulk scan's int8 products), fp32 elsewhere."""
+    if w.name == "bulk_64k_scan" and w.head_dim == 128 and w.key_bits in (2, 3) and w.qjl_dim in (0, 128):
+        return "i8 (int32 accumulate)"
+    if w.name == "sparse_128k_top2048":
+        return "i32 (selection scores) + f32 (attention)"
+    if decode_kernel_name(w) == "decode_mfma_kernel":
+        return "i8 + bf16 (int32 / fp32 accumulate)"
+    return "f32"
+
+
 def base_line(args, w, ms_per_step, tokens_per_step):
     return {
         "metric": "compressed KV tokens attended/sec per GPU + % of HBM roofline (GB/s)",
@@ -302,7 +315,7 @@ def base_line(args, w, ms_per_step, tokens_per_step):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": compute_dtype(w),
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
                    "head_dim": w.head_dim, "context": w.tokens, "key_bits": w.key_bits,
