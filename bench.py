@@ -438,10 +438,17 @@ def run_sparse(args, tq, W, ev):
     dws = torch.empty(h.decode_workspace_size(B, w.q_heads, H, T, k_sel=w.top_k), dtype=torch.uint8,
                       device=dev)
 
+    pws = torch.empty(h.sparse_workspace_size(B, w.q_heads, H, T), dtype=torch.uint8, device=dev)
+
     def step():
+        # selection and attention over the selected compressed tokens in one call
+        h.sparse_attention(q, index, book, records, seq_lens, w.top_k, out=out, workspace=pws)
+
+    def step_two_calls():
         h.select_topk(q, index, book, seq_lens, w.top_k, out_idx=sel, out_count=cnt, workspace=sws)
         h.decode_attention(q, records, seq_lens, sel_idx=sel, out=out, workspace=dws)
 
+    two_call_ms, _ = time_steps(ev, tq, step_two_calls, args.steps, args.warmup)
     ms_per_step, score_ms = time_steps(ev, tq, step, args.steps, args.warmup)
     fl_ms = flushed_kernel_ms(tq, ev, step)
     ceiling = read_ceiling_gbps(tq, ev)
@@ -452,6 +459,8 @@ def run_sparse(args, tq, W, ev):
     line["config"].update({"top_k": w.top_k, "index_bytes_per_token_head": d // 8})
     line["roofline"] = roofline("select_score_kernel", w.name, alg_bytes, score_ms, None, fl_ms, ceiling)
     line["tokens_attended_per_s"] = B * H * w.top_k / (ms_per_step * 1e-3)
+    line["step"] = "tq_sparse_attention (one call)"
+    line["two_call_ms_per_step"] = two_call_ms        # tq_select_topk + tq_decode_attention(sel_idx)
     line["compress"] = {"ms": compress_ms}
     key_bytes = B * T * H * d * 2
     line["sign_index_build"] = {"ms": index_ms, "key_bytes": key_bytes,

@@ -31,7 +31,8 @@ EXPORTED = [
     "tq_compress_kv", "tq_debug_quantize", "tq_decode_workspace_size", "tq_decode_attention",
     "tq_index_workspace_size", "tq_build_sign_index", "tq_select_workspace_size",
     "tq_select_topk", "tq_scan_workspace_size", "tq_score_scan", "tq_set_profile_events",
-    "tq_stream_read", "tq_monarch_workspace_size", "tq_monarch_step",
+    "tq_stream_read", "tq_monarch_workspace_size", "tq_monarch_step", "tq_sparse_workspace_size",
+    "tq_sparse_attention",
 ]
 
 
@@ -90,6 +91,9 @@ _index = _sig("tq_build_sign_index", _P, _P, ctypes.c_int, _I32, _I64, _I32, _I6
 _select_ws = _sig("tq_select_workspace_size", _P, _I32, _I32, _I64, _PSZ)
 _select = _sig("tq_select_topk", _P, _P, ctypes.c_int, _I32, _I32, _I32, _P, _P, _I64, _P, _I32,
                _P, _P, _P, _P, _SZ, _P)
+_sparse_ws = _sig("tq_sparse_workspace_size", _P, _I32, _I32, _I32, _I64, _PSZ)
+_sparse = _sig("tq_sparse_attention", _P, _P, ctypes.c_int, _I32, _I32, _I32, _P, _P, _P, _I64, _P, _I32,
+               _P, _P, ctypes.c_int, _P, _I64, _F, _P, _P, _P, _SZ, _P)
 _scan_ws = _sig("tq_scan_workspace_size", _P, _I32, _I32, _I32, _PSZ)
 _scan = _sig("tq_score_scan", _P, _P, ctypes.c_int, _I32, _I32, _I32, _P, _I64, _I64, _P, _P, _SZ, _P)
 _set_events = _sig("tq_set_profile_events", _P, _P)
@@ -262,6 +266,31 @@ class Handle:
                       _ptr(seq_lens), k, _ptr(out_idx), _ptr(out_count), _ptr(out_scores),
                       _ptr(workspace), workspace.numel(), _stream(stream)))
         return out_idx, out_count
+
+    # ---------------------------------------------------------------- sparse attention -
+    def sparse_workspace_size(self, batch, q_heads, kv_heads, capacity) -> int:
+        n = ctypes.c_size_t()
+        check(_sparse_ws(self._h, batch, q_heads, kv_heads, capacity, ctypes.byref(n)))
+        return n.value
+
+    def sparse_attention(self, q, index, codebook, records, seq_lens, k, hot_k=None, hot_v=None,
+                         hot_lens=None, scale=0.0, out=None, lse=None, workspace=None, stream=None):
+        """Top-k selection from the sign index and attention over the selected compressed
+        tokens (plus an optional exact segment) in one call; q [batch, q_heads, d]."""
+        import torch
+        B, Hq, d = q.shape
+        Hkv, cap = records.shape[1], records.shape[2]
+        if out is None:
+            out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            workspace = _workspace(self.sparse_workspace_size(B, Hq, Hkv, cap), q.device)
+        hot_cap = 0 if hot_k is None else hot_k.shape[2]
+        hot_dt = TQ_F32 if hot_k is None else _dtype_code(hot_k)
+        check(_sparse(self._h, _ptr(q), _dtype_code(q), B, Hq, Hkv, _ptr(index), _ptr(codebook),
+                      _ptr(records), cap, _ptr(seq_lens), k, _ptr(hot_k), _ptr(hot_v), hot_dt,
+                      _ptr(hot_lens), hot_cap, scale, _ptr(out), _ptr(lse), _ptr(workspace),
+                      workspace.numel(), _stream(stream)))
+        return out
 
     # ---------------------------------------------------------------- bulk scan --------
     def scan_workspace_size(self, batch, kv_heads, n_queries) -> int:

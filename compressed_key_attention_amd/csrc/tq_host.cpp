@@ -647,6 +647,55 @@ tq_status tq_select_topk(const tq_handle* h, const void* q, tq_dtype q_dt, int32
                        "select launch");
 }
 
+tq_status tq_sparse_workspace_size(const tq_handle* h, int32_t batch, int32_t q_heads,
+                                   int32_t kv_heads, int64_t capacity, size_t* bytes) {
+  if (!h || !bytes) return fail(TQ_ERR_INVALID_ARGUMENT, "NULL handle or output");
+  if (batch < 0 || q_heads <= 0 || kv_heads <= 0 || q_heads % kv_heads || capacity < 0)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "bad shape");
+  *bytes = tq::plan_sparse(h->c, batch, q_heads, kv_heads, capacity).ws_total;
+  return ok();
+}
+
+tq_status tq_sparse_attention(const tq_handle* h, const void* q, tq_dtype q_dt, int32_t batch,
+                              int32_t q_heads, int32_t kv_heads, const void* index,
+                              const float* codebook, const void* records, int64_t capacity,
+                              const int32_t* seq_lens, int32_t k, const void* hot_k,
+                              const void* hot_v, tq_dtype hot_dt, const int32_t* hot_lens,
+                              int64_t hot_capacity, float scale, float* out, float* lse,
+                              void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!h) return fail(TQ_ERR_INVALID_ARGUMENT, "handle is NULL");
+  size_t es;
+  if (!elem_size(q_dt, &es)) return fail(TQ_ERR_INVALID_ARGUMENT, "unknown query dtype");
+  if (batch < 0 || q_heads <= 0 || kv_heads <= 0 || q_heads % kv_heads || capacity < 0 || k < 0)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "bad sparse attention shape");
+  if (q_heads / kv_heads > 16) return fail(TQ_ERR_UNSUPPORTED, "group size above 16");
+  if (h->c.m > 128 || h->c.m % 32) return fail(TQ_ERR_UNSUPPORTED, "qjl_dim must be 0, 32, 64, 96 or 128");
+  if (capacity > (int64_t(1) << 26)) return fail(TQ_ERR_UNSUPPORTED, "capacity above 2^26 tokens");
+  if (!(scale >= 0.0f) || std::isinf(scale)) return fail(TQ_ERR_INVALID_ARGUMENT, "scale must be finite and >= 0");
+  if (batch == 0) return ok();
+  if (!q || !out || !seq_lens) return fail(TQ_ERR_INVALID_ARGUMENT, "q, out and seq_lens are required");
+  if (capacity > 0 && (!index || !codebook || !records))
+    return fail(TQ_ERR_INVALID_ARGUMENT, "index, codebook and records are required");
+  if (records && !aligned(records, 16)) return fail(TQ_ERR_INVALID_ARGUMENT, "records not 16-byte aligned");
+  if (hot_lens) {
+    size_t hs;
+    if (!elem_size(hot_dt, &hs)) return fail(TQ_ERR_INVALID_ARGUMENT, "unknown hot dtype");
+    if (hot_capacity <= 0 || !hot_k || !hot_v)
+      return fail(TQ_ERR_INVALID_ARGUMENT, "exact segment needs hot_k, hot_v and hot_capacity > 0");
+    if (!aligned(hot_k, hs * 8) || !aligned(hot_v, hs * 8))
+      return fail(TQ_ERR_INVALID_ARGUMENT, "hot_k and hot_v must be aligned to 8 elements");
+  }
+  tq::SparsePlan plan = tq::plan_sparse(h->c, batch, q_heads, kv_heads, capacity);
+  if (!workspace || ws_bytes < plan.ws_total || !aligned(workspace, 256))
+    return fail(TQ_ERR_WORKSPACE_TOO_SMALL, "sparse attention needs %zu bytes of 256-byte aligned workspace",
+                plan.ws_total);
+  return device_status(tq::launch_sparse(h->c, h->dc, plan, q, q_dt, batch, q_heads, kv_heads, index,
+                                         codebook, records, capacity, seq_lens, k, hot_k, hot_v, hot_dt,
+                                         hot_lens, hot_capacity, scale, out, lse, workspace, stream,
+                                         take_events()),
+                       "sparse attention launch");
+}
+
 tq_status tq_scan_workspace_size(const tq_handle* h, int32_t batch, int32_t kv_heads,
                                  int32_t n_queries, size_t* bytes) {
   if (!h || !bytes) return fail(TQ_ERR_INVALID_ARGUMENT, "NULL handle or output");

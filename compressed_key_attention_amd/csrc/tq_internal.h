@@ -109,11 +109,24 @@ struct SelectPlan {
   size_t ws_lut, ws_scores, ws_hist, ws_cand, ws_chunk_cand, ws_chunk_above, ws_chunk_off, ws_params, ws_total;
 };
 SelectPlan plan_select(const Consts& c, int batch, int heads, int64_t capacity);
+
+struct SparsePlan {
+  SelectPlan select;
+  size_t ws_select, ws_qx, ws_qs, ws_part, ws_total;
+};
+SparsePlan plan_sparse(const Consts& c, int batch, int q_heads, int kv_heads, int64_t capacity);
 hipError_t launch_select(const Consts& c, const SelectPlan& plan, const void* q, tq_dtype q_dt,
                          int batch, int q_heads, int kv_heads, const void* index,
                          const float* codebook, int64_t capacity, const int32_t* seq_lens,
                          int k, int32_t* out_idx, int32_t* out_count, int32_t* out_scores,
                          void* workspace, hipStream_t stream, const ProfileEvents& ev);
+hipError_t launch_sparse(const Consts& c, const DevConsts& dc, const SparsePlan& plan, const void* q,
+                         tq_dtype q_dt, int batch, int q_heads, int kv_heads, const void* index,
+                         const float* codebook, const void* records, int64_t capacity,
+                         const int32_t* seq_lens, int k, const void* hot_k, const void* hot_v,
+                         tq_dtype hot_dt, const int32_t* hot_lens, int64_t hot_capacity, float scale,
+                         float* out, float* lse, void* workspace, hipStream_t stream,
+                         const ProfileEvents& ev);
 
 struct ScanPlan {
   bool mfma;        // matrix-core scan (head_dim 128, 2/3-bit keys, m in {0, 128})

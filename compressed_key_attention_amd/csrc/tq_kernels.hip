@@ -1904,6 +1904,8 @@ static void launch_scan_hpl(const DecodeArgs& a, int kb, int vb, dim3 grid, size
 #undef TQ_DEC
 }
 
+static hipError_t launch_merge(const Consts& c, const MergeArgs& mg, int batch, hipStream_t stream);
+
 hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan& plan, const void* q,
                          tq_dtype q_dt, int batch, int q_heads, int kv_heads, const void* records,
                          int64_t capacity, const int32_t* seq_lens, const void* hot_k,
@@ -1998,15 +2000,21 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
   mg.kv_heads = kv_heads;
   mg.n_chunks = plan.n_chunks;
   mg.scale = sc;
+  return launch_merge(c, mg, batch, stream);
+}
+
+// The merge of chunk partials (and the exact segment, if any) into out / lse.
+static hipError_t launch_merge(const Consts& c, const MergeArgs& mg, int batch, hipStream_t stream) {
+  const int q_heads = mg.q_heads, kv_heads = mg.kv_heads;
   const dim3 mgrid(q_heads, batch);
-  if (hot_lens) {
+  if (mg.hot_lens) {
     if (c.d == 128) hipLaunchKernelGGL((decode_merge_kernel<128, kMergeThreadsHot>), mgrid, dim3(kMergeThreadsHot), 0, stream, mg);
     else hipLaunchKernelGGL((decode_merge_kernel<64, kMergeThreadsHot>), mgrid, dim3(kMergeThreadsHot), 0, stream, mg);
-  } else if (plan.group == 4 || plan.group == 2) {
+  } else if (mg.G == 4 || mg.G == 2) {
     const dim3 ggrid(kv_heads, batch);
-    if (c.d == 128 && plan.group == 4) hipLaunchKernelGGL((decode_merge_group_kernel<128, 4>), ggrid, dim3(256), 0, stream, mg);
+    if (c.d == 128 && mg.G == 4) hipLaunchKernelGGL((decode_merge_group_kernel<128, 4>), ggrid, dim3(256), 0, stream, mg);
     else if (c.d == 128) hipLaunchKernelGGL((decode_merge_group_kernel<128, 2>), ggrid, dim3(256), 0, stream, mg);
-    else if (plan.group == 4) hipLaunchKernelGGL((decode_merge_group_kernel<64, 4>), ggrid, dim3(256), 0, stream, mg);
+    else if (mg.G == 4) hipLaunchKernelGGL((decode_merge_group_kernel<64, 4>), ggrid, dim3(256), 0, stream, mg);
     else hipLaunchKernelGGL((decode_merge_group_kernel<64, 2>), ggrid, dim3(256), 0, stream, mg);
   } else {
     if (c.d == 128) hipLaunchKernelGGL((decode_merge_kernel<128, kMergeThreads>), mgrid, dim3(kMergeThreads), 0, stream, mg);
@@ -2605,11 +2613,12 @@ __global__ __launch_bounds__(kSelExactThreads) void select_exact_kernel(
   const int64_t unit = (int64_t)b * heads + h;
   const int64_t n = min((int64_t)seq_lens[b], capacity);
   const int64_t kk = min((int64_t)k, n);
-  if (threadIdx.x == 0) out_count[unit] = (int32_t)kk;
-  for (int64_t i = kk + threadIdx.x; i < k; i += blockDim.x) {
-    out_idx[unit * k + i] = -1;
-    if (out_scores) out_scores[unit * k + i] = 0;
-  }
+  if (out_count && threadIdx.x == 0) out_count[unit] = (int32_t)kk;
+  if (out_idx)
+    for (int64_t i = kk + threadIdx.x; i < k; i += blockDim.x) {
+      out_idx[unit * k + i] = -1;
+      if (out_scores) out_scores[unit * k + i] = 0;
+    }
   if (kk == 0) return;
   const int nch = (int)((n + kSelChunk - 1) / kSelChunk);
   int32_t* off = chunk_off + unit * n_chunks;
@@ -2798,10 +2807,348 @@ hipError_t launch_select(const Consts& c, const SelectPlan& plan, const void* q,
   allow_lds(select_exact_kernel, exact_lds);
   hipLaunchKernelGGL(select_exact_kernel, dim3(kv_heads, batch), dim3(kSelExactThreads), exact_lds, stream, seq_lens, kv_heads, capacity, k, n_chunks, cand,
                      chunk_cand, chunk_above, chunk_off, params, out_idx, out_count, out_scores);
-  if (capacity > 0 && k > 0)
+  if (capacity > 0 && k > 0 && out_idx)
     hipLaunchKernelGGL(select_write_kernel, dim3((unsigned)n_chunks, kv_heads, batch), dim3(256), 0, stream, scores,
                        seq_lens, kv_heads, capacity, k, n_chunks, chunk_off, params, out_idx, out_scores);
   return hipGetLastError();
+}
+
+// =========================================================================================
+// Sparse attention in one pass over the selection (Self-Indexing page, "Methodologie" 3-5):
+// after the selection's lut / score / filter / exact launches, every 4,096-token chunk of a
+// (sequence, KV head) re-derives its selected tokens from the stored scores and the unit's
+// predicate (the write launch's rule, including its cap at k), and attends to them directly:
+// their codes are unpacked into LDS 64 tokens at a time, the G heads' estimates formed from
+// q_x / q_s and the level tables, and an online softmax with the value sums kept per (head,
+// coordinate); the chunk's partial (m, l, o_x) then goes through the decode merge, with the
+// exact segment (e.g. sink tokens) in the same softmax.  No index list is materialised.
+// =========================================================================================
+struct SparseArgs {
+  DecodeArgs a;             // records, layout, qx / qs, levels, scale, part, n_chunks (= select chunks)
+  const int32_t* scores;    // [units][capacity] selection scores
+  const SelectParams* params;
+  const int32_t* chunk_off;
+  int k;
+};
+
+template <int D, int BK, int BV, int MG>
+__global__ __launch_bounds__(kSmallThreads) void sparse_attend_kernel(SparseArgs S) {
+  const DecodeArgs& A = S.a;
+  constexpr int NG32 = D / 32, TB = kSmallMaxTok, kPer = kSelChunk / kSmallThreads;
+  __shared__ uint16_t list[kSelChunk];             // selected tokens, offsets within the chunk
+  __shared__ int wsum[kSmallThreads / 64];
+  __shared__ int s_nsel;
+  __shared__ float qx[MG][D + 1];
+  __shared__ float qs[MG][kSmallMaxM + 1];
+  __shared__ __attribute__((aligned(4))) uint8_t kc[TB][D];
+  __shared__ __attribute__((aligned(4))) uint8_t vc[TB][D];
+  __shared__ __attribute__((aligned(4))) uint8_t sb[TB][kSmallMaxM];
+  __shared__ float nr[TB][3];
+  __shared__ float lg[MG][TB + 1];
+  __shared__ float hm[MG], hl[MG], hf[MG];
+  __shared__ float kl[kMaxLevels], vl[kMaxLevels];
+  const int G = A.G, m = A.m, tid = threadIdx.x;
+  const int c = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+  const int64_t unit = (int64_t)b * A.kv_heads + hkv;
+  const int64_t qrow0 = (int64_t)b * A.q_heads + (int64_t)hkv * G;
+  const int64_t n = min((int64_t)A.seq_lens[b], A.capacity);
+  const int64_t kk = min((int64_t)S.k, n);
+  const int64_t t0 = (int64_t)c * kSelChunk;
+  // this chunk's selected tokens, in index order, capped at k overall
+  {
+    const int tb = tid * kPer;
+    uint32_t sel = 0;
+    if (kk > 0 && t0 < n) {
+      const uint64_t prefix = S.params[unit].prefix, mask = S.params[unit].mask;
+      const int mm = (int)min((int64_t)kSelChunk, n - t0);
+      const int32_t* sc = S.scores + unit * A.capacity + t0;
+      int32_t s[kPer];
+      if (tb + kPer <= mm) {
+#pragma unroll
+        for (int j = 0; j < kPer; j += 4) {
+          const int4 v = *reinterpret_cast<const int4*>(sc + tb + j);
+          s[j] = v.x; s[j + 1] = v.y; s[j + 2] = v.z; s[j + 3] = v.w;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) s[j] = tb + j < mm ? sc[tb + j] : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int t = tb + j;
+        const bool take = t < mm && (select_key(order_key(s[j]), (int32_t)(t0 + t)) & mask) >= prefix;
+        sel |= (take ? 1u : 0u) << j;
+      }
+    }
+    int tot;
+    int pos = block_exclusive_sum<kSmallThreads>(__popc(sel), wsum, &tot);
+    const int base = (kk > 0 && t0 < n) ? S.chunk_off[unit * A.n_chunks + c] : 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (sel & (1u << j)) {
+        if (base + pos < kk) list[pos] = (uint16_t)(tb + j);
+        ++pos;
+      }
+    if (tid == 0) s_nsel = (int)max<int64_t>(0, min<int64_t>(tot, kk - base));
+  }
+  for (int e = tid; e < G * D; e += kSmallThreads) qx[e / D][e % D] = A.qx[(qrow0 + e / D) * D + e % D];
+  for (int e = tid; e < G * m; e += kSmallThreads) qs[e / m][e % m] = A.qs[(qrow0 + e / m) * m + e % m];
+  if (tid < kMaxLevels) {
+    kl[tid] = A.key_levels[tid];
+    vl[tid] = A.val_levels[tid];
+  }
+  if (tid < G) {
+    hm[tid] = kNegInf;
+    hl[tid] = 0.0f;
+  }
+  constexpr int kMaxOut = (MG * D + kSmallThreads - 1) / kSmallThreads;
+  float o[kMaxOut];
+#pragma unroll
+  for (int r = 0; r < kMaxOut; ++r) o[r] = 0.0f;
+  __syncthreads();
+  const int nsel = s_nsel;
+  // SP adjacent threads per (head, coordinate) output when the outputs are fewer than the
+  // threads (each sums every SP-th token; the SP partial sums are added at the end)
+  int SP = 1;
+  while (SP < 4 && G * D * SP * 2 <= kSmallThreads) SP *= 2;
+  const uint8_t* recs = A.records + unit * A.capacity * A.rec_bytes;
+  const int nsw = m / 32, per_t = 2 * NG32 + nsw + 1;
+  for (int s0 = 0; s0 < nsel; s0 += TB) {
+    const int nt = min(TB, nsel - s0);
+    for (int e = tid; e < nt * per_t; e += kSmallThreads) {
+      const int t = e / per_t, pt = e % per_t;
+      const uint8_t* rec = recs + (t0 + list[s0 + t]) * A.rec_bytes;
+      if (pt < 2 * NG32) {
+        const bool key = pt < NG32;
+        const int g = key ? pt : pt - NG32;
+        uint32_t w[4];
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(
+            rec + (key ? g * 4 * BK : A.kbytes + A.sbytes + g * 4 * BV));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = i < (key ? BK : BV) ? src[i] : 0u;
+        uint32_t* dst = reinterpret_cast<uint32_t*>(key ? &kc[t][32 * g] : &vc[t][32 * g]);
+        const int nb = key ? BK : BV;
+        if (nb == 4) {
+          // 4-bit codes: nibble j of the word stream -> byte j (low nibbles, high nibbles, then
+          // interleaved by byte permutes)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = w[i] & 0x0F0F0F0Fu, hi = (w[i] >> 4) & 0x0F0F0F0Fu;
+            dst[2 * i] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+            dst[2 * i + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+          }
+        } else {
+#pragma unroll
+          for (int j4 = 0; j4 < 8; ++j4) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int j = 4 * j4 + u;
+              const uint32_t code = nb == 3 ? group3_code(w[0], w[1], w[2], j) : field<4>(w, j * nb, nb);
+              word |= code << (8 * u);
+            }
+            dst[j4] = word;
+          }
+        }
+      } else if (pt < 2 * NG32 + nsw) {
+        const int wi = pt - 2 * NG32;
+        const uint32_t sw = reinterpret_cast<const uint32_t*>(rec + A.kbytes)[wi];
+        uint32_t* dst = reinterpret_cast<uint32_t*>(&sb[t][32 * wi]);
+#pragma unroll
+        for (int j4 = 0; j4 < 8; ++j4) {
+          const uint32_t nib = (sw >> (4 * j4)) & 15u;
+          dst[j4] = (nib & 1u) | ((nib & 2u) << 7) | ((nib & 4u) << 14) | ((nib & 8u) << 21);
+        }
+      } else {
+        const float* f = reinterpret_cast<const float*>(rec + A.norm_off);
+        nr[t][0] = f[0];
+        nr[t][1] = f[1];
+        nr[t][2] = f[2];
+      }
+    }
+    __syncthreads();
+    const int items = nt * G;
+    int L = 1;
+    while (L < 8 && items * L * 2 <= kSmallThreads) L *= 2;
+    for (int i0 = 0; i0 < items; i0 += kSmallThreads / L) {
+      const int it = i0 + tid / L, s = tid % L;
+      const int t = it / G, h = it % G;
+      float dot = 0.0f, qd = 0.0f;
+      if (it < items) {
+        for (int i = s; i < D; i += L) dot = fmaf(qx[h][i], kl[kc[t][i]], dot);
+        for (int j = s; j < m; j += L) qd += sb[t][j] ? qs[h][j] : -qs[h][j];
+      }
+      for (int msk = 1; msk < L; msk <<= 1) {
+        dot += __shfl_xor(dot, msk);
+        qd += __shfl_xor(qd, msk);
+      }
+      if (it < items && s == 0)
+        lg[h][t] = A.scale * fmaf(A.qjl_coef * nr[t][1], qd, nr[t][0] * A.inv_sqrt_d * dot);
+    }
+    __syncthreads();
+    // online softmax over this batch: one wave per head, one lane per token
+    {
+      const int lane = tid & 63, wv = tid >> 6;
+      for (int h = wv; h < G; h += kSmallThreads / 64) {
+        const float x = lane < nt ? lg[h][lane] : kNegInf;
+        float bm = x;
+#pragma unroll
+        for (int msk = 32; msk > 0; msk >>= 1) bm = fmaxf(bm, __shfl_xor(bm, msk));
+        const float mo = hm[h], mn = fmaxf(mo, bm);
+        const float p = x == kNegInf ? 0.0f : __expf(x - mn);
+        float ps = p;
+#pragma unroll
+        for (int msk = 32; msk > 0; msk >>= 1) ps += __shfl_xor(ps, msk);
+        if (lane < nt) lg[h][lane] = p * nr[lane][2] * A.inv_sqrt_d;
+        if (lane == 0) {
+          const float f = mo == kNegInf ? 0.0f : __expf(mo - mn);
+          hf[h] = f;
+          hm[h] = mn;
+          hl[h] = hl[h] * f + ps;
+        }
+      }
+    }
+    __syncthreads();
+    if (SP > 1) {
+      const int e = tid / SP, sp = tid % SP;
+      if (e < G * D) {
+        const int h = e / D, i = e % D;
+        float acc = o[0] * hf[h];
+        for (int t = sp; t < nt; t += SP) acc = fmaf(lg[h][t], vl[vc[t][i]], acc);
+        o[0] = acc;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < kMaxOut; ++r) {
+        const int e = tid + kSmallThreads * r;
+        if (e < G * D) {
+          const int h = e / D, i = e % D;
+          float acc = o[r] * hf[h];
+          for (int t = 0; t < nt; ++t) acc = fmaf(lg[h][t], vl[vc[t][i]], acc);
+          o[r] = acc;
+        }
+      }
+    }
+    __syncthreads();            // the next batch overwrites the codes and weights
+  }
+  const int stride = D + 2;
+  if (SP > 1) {
+    float v = o[0];
+    for (int msk = 1; msk < SP; msk <<= 1) v += __shfl_xor(v, msk);
+    const int e = tid / SP;
+    if (tid % SP == 0 && e < G * D) A.part[((qrow0 + e / D) * A.n_chunks + c) * stride + 2 + e % D] = v;
+  } else {
+#pragma unroll
+    for (int r = 0; r < kMaxOut; ++r) {
+      const int e = tid + kSmallThreads * r;
+      if (e < G * D) A.part[((qrow0 + e / D) * A.n_chunks + c) * stride + 2 + e % D] = o[r];
+    }
+  }
+  for (int h = tid; h < G; h += kSmallThreads) {
+    A.part[((qrow0 + h) * A.n_chunks + c) * stride] = hm[h];
+    A.part[((qrow0 + h) * A.n_chunks + c) * stride + 1] = hl[h];
+  }
+}
+
+SparsePlan plan_sparse(const Consts& c, int batch, int q_heads, int kv_heads, int64_t capacity) {
+  SparsePlan p;
+  p.select = plan_select(c, batch, kv_heads, capacity);
+  const size_t rows = (size_t)std::max(batch, 1) * q_heads;
+  p.ws_select = 0;
+  p.ws_qx = align256(p.select.ws_total);
+  p.ws_qs = p.ws_qx + align256(rows * c.d * 4);
+  p.ws_part = p.ws_qs + align256(rows * std::max(c.m, 1) * 4);
+  p.ws_total = p.ws_part + align256(rows * (size_t)std::max(p.select.n_chunks, 1) * (c.d + 2) * 4);
+  return p;
+}
+
+template <int D, int MG>
+static void launch_sparse_d(const SparseArgs& s, int kb, int vb, dim3 grid, hipStream_t st) {
+#define TQ_SP(BK_, BV_)                                                                               \
+  if (kb == BK_ && vb == BV_) {                                                                       \
+    hipLaunchKernelGGL((sparse_attend_kernel<D, BK_, BV_, MG>), grid, dim3(kSmallThreads), 0, st, s); \
+    return;                                                                                           \
+  }
+  TQ_SP(2, 2) TQ_SP(2, 3) TQ_SP(2, 4) TQ_SP(3, 2) TQ_SP(3, 3) TQ_SP(3, 4)
+  TQ_SP(4, 2) TQ_SP(4, 3) TQ_SP(4, 4)
+#undef TQ_SP
+}
+
+hipError_t launch_sparse(const Consts& c, const DevConsts& dc, const SparsePlan& plan, const void* q,
+                         tq_dtype q_dt, int batch, int q_heads, int kv_heads, const void* index,
+                         const float* codebook, const void* records, int64_t capacity,
+                         const int32_t* seq_lens, int k, const void* hot_k, const void* hot_v,
+                         tq_dtype hot_dt, const int32_t* hot_lens, int64_t hot_capacity, float scale,
+                         float* out, float* lse, void* workspace, hipStream_t stream,
+                         const ProfileEvents& ev) {
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const SelectPlan& sp = plan.select;
+  hipError_t e = launch_select(c, sp, q, q_dt, batch, q_heads, kv_heads, index, codebook, capacity, seq_lens, k,
+                               nullptr, nullptr, nullptr, ws + plan.ws_select, stream, ev);
+  if (e != hipSuccess) return e;
+  float* qx = reinterpret_cast<float*>(ws + plan.ws_qx);
+  float* qs = reinterpret_cast<float*>(ws + plan.ws_qs);
+  float* part = reinterpret_cast<float*>(ws + plan.ws_part);
+  const int rows = batch * q_heads;
+  hipLaunchKernelGGL(query_prep_kernel, dim3(rows), dim3(128), 0, stream, dc.pi, dc.s, c.d, c.m, q, q_dt, qx, qs);
+  const int n_chunks = std::max(sp.n_chunks, 1);
+  const float sc = scale > 0.0f ? scale : c.inv_sqrt_d;
+  SparseArgs s;
+  DecodeArgs& a = s.a;
+  a = DecodeArgs{};
+  a.qx = qx;
+  a.qs = qs;
+  a.records = static_cast<const uint8_t*>(records);
+  a.seq_lens = seq_lens;
+  a.part = part;
+  a.capacity = capacity;
+  a.d = c.d;
+  a.m = c.m;
+  a.kbytes = c.kbytes;
+  a.sbytes = c.sbytes;
+  a.rec_bytes = c.rec_bytes;
+  a.norm_off = c.norm_off;
+  a.G = q_heads / kv_heads;
+  a.q_heads = q_heads;
+  a.kv_heads = kv_heads;
+  a.n_chunks = n_chunks;
+  a.scale = sc;
+  a.inv_sqrt_d = c.inv_sqrt_d;
+  a.qjl_coef = c.qjl_coef;
+  for (int i = 0; i < kMaxLevels; ++i) {
+    a.key_levels[i] = c.key_levels[i];
+    a.val_levels[i] = c.val_levels[i];
+  }
+  s.scores = reinterpret_cast<const int32_t*>(ws + plan.ws_select + sp.ws_scores);
+  s.params = reinterpret_cast<const SelectParams*>(ws + plan.ws_select + sp.ws_params);
+  s.chunk_off = reinterpret_cast<const int32_t*>(ws + plan.ws_select + sp.ws_chunk_off);
+  s.k = k;
+  const dim3 grid((unsigned)n_chunks, kv_heads, batch);
+  // query rows held in LDS sized for the group (a smaller footprint keeps more workgroups per CU)
+  const int G = q_heads / kv_heads;
+  if (c.d == 128 && G <= 4) launch_sparse_d<128, 4>(s, c.kb, c.vb, grid, stream);
+  else if (c.d == 128) launch_sparse_d<128, kSmallMaxG>(s, c.kb, c.vb, grid, stream);
+  else if (G <= 4) launch_sparse_d<64, 4>(s, c.kb, c.vb, grid, stream);
+  else launch_sparse_d<64, kSmallMaxG>(s, c.kb, c.vb, grid, stream);
+  MergeArgs mg{};
+  mg.pi_t = dc.pi_t;
+  mg.part = part;
+  mg.q = q;
+  mg.q_dt = q_dt;
+  mg.hot_k = hot_k;
+  mg.hot_v = hot_v;
+  mg.hot_dt = hot_dt;
+  mg.hot_lens = hot_lens;
+  mg.hot_capacity = hot_capacity;
+  mg.out = out;
+  mg.lse = lse;
+  mg.d = c.d;
+  mg.G = q_heads / kv_heads;
+  mg.q_heads = q_heads;
+  mg.kv_heads = kv_heads;
+  mg.n_chunks = n_chunks;
+  mg.scale = sc;
+  return launch_merge(c, mg, batch, stream);
 }
 
 // =========================================================================================

@@ -192,6 +192,25 @@ tq_status tq_select_topk(const tq_handle* h, const void* q, tq_dtype q_dt, int32
                          int32_t k, int32_t* out_idx, int32_t* out_count, int32_t* out_scores,
                          void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Sparse attention in one call (Self-Indexing page, "Methodologie" 3-5: select from the
+ * sign index, then attend to the selected tokens' compressed keys and values).  out / lse as
+ * tq_decode_attention(q, records, seq_lens, exact segment, sel_idx = the out_idx that
+ * tq_select_topk(q, index, codebook, seq_lens, k) returns, scale): the same top-k set (same
+ * ranking and tie rule), the same estimator, one softmax with the optional exact segment
+ * (hot_k / hot_v / hot_lens, e.g. always-attended sink tokens).  The selected indices are
+ * not written out.  Requires qjl_dim in {0, 32, 64, 96, 128} and at most 16 query heads per
+ * KV head.  workspace: tq_sparse_workspace_size bytes (256-byte aligned).  Nothing is
+ * allocated; the host is not synchronised. */
+tq_status tq_sparse_workspace_size(const tq_handle* h, int32_t batch, int32_t q_heads,
+                                   int32_t kv_heads, int64_t capacity, size_t* bytes);
+tq_status tq_sparse_attention(const tq_handle* h, const void* q, tq_dtype q_dt, int32_t batch,
+                              int32_t q_heads, int32_t kv_heads, const void* index,
+                              const float* codebook, const void* records, int64_t capacity,
+                              const int32_t* seq_lens, int32_t k, const void* hot_k,
+                              const void* hot_v, tq_dtype hot_dt, const int32_t* hot_lens,
+                              int64_t hot_capacity, float scale, float* out, float* lse,
+                              void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* Bulk scan (TurboQuant page, "Leistung bei der Vektorsuche"): for q[b][h][i][d]
  * (i < n_queries) and every slot t < n_tokens of records[b][h], scores[b][h][i][t] =
  * s_t as in tq_decode_attention (unscaled estimate, no softmax).  float32 output.
@@ -204,7 +223,7 @@ tq_status tq_score_scan(const tq_handle* h, const void* q, tq_dtype q_dt, int32_
                         size_t ws_bytes, hipStream_t stream);
 
 /* Measurement support: on this thread, the next tq_decode_attention, tq_compress_kv,
- * tq_select_topk or tq_score_scan call records `start` on its stream just before its main
+ * tq_select_topk, tq_sparse_attention or tq_score_scan call records `start` on its stream just before its main
  * kernel (decode: the split-K scan; compress: the compress kernel; select: the sign-index
  * score kernel; scan: the score kernel) and `stop` just after it, then forgets both.
  * Events are caller-created (hipEventCreate) and caller-owned; NULL, NULL clears. */

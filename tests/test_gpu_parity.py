@@ -456,6 +456,59 @@ def test_sparse_with_exact_sinks(kb, vb):
     _close(out.cpu().numpy(), ref, f"sparse + sinks kb={kb} vb={vb}")
 
 
+@pytest.mark.parametrize("kb,vb,m,hq,k,lens,sinks", [
+    (4, 4, 0, 8, 300, [5000, 4097], 0),       # one query head per KV head (the sparse family)
+    (2, 2, 0, 8, 1000, [9000, 123], 64),      # 2-bit payload, 64 exact sink tokens
+    (3, 4, 128, 32, 500, [6000, 6000], 0),    # 4 query heads per KV head, 128-bit sketch
+    (4, 4, 64, 16, 0, [300, 300], 16),        # k = 0: the sink tokens only
+    (4, 4, 0, 8, 5000, [4500, 100], 0),       # k >= n: every token
+])
+def test_sparse_attention_one_call(kb, vb, m, hq, k, lens, sinks):
+    """tq_sparse_attention (selection and attention in one call, no index list) against the
+    oracle's select_topk followed by its gathered decode, with the exact segment as sinks."""
+    T = max(lens) + sinks
+    base = W.small(W.WORKLOADS["sparse_128k_top2048"], tokens=T, batch=len(lens), top_k=max(k, 1))
+    w = W.Workload(**{**base.__dict__, "key_bits": kb, "value_bits": vb, "qjl_dim": m, "q_heads": hq})
+    h = _handle(w)
+    codec = _codec(h)
+    K, V = W.make_kv(w, "cuda")
+    B, _, H, d = K.shape
+    S = sinks
+    Kc, Vc = K[:, S:].contiguous(), V[:, S:].contiguous()
+    index = torch.empty((B, H, T - S, d // 8), dtype=torch.uint8, device="cuda")
+    book = torch.empty((B, H, d // 4, 16, 4), device="cuda")
+    h.build_sign_index(Kc, index, book)
+    rec = _compress(w, h, Kc, Vc)
+    q = W.make_queries(w, "cuda")
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    hot, hk, hv, hlens = {}, None, None, None
+    if S:
+        hk = K[:, :S].permute(0, 2, 1, 3).contiguous()
+        hv = V[:, :S].permute(0, 2, 1, 3).contiguous()
+        hlens = [S] * B
+        hot = dict(hot_k=hk, hot_v=hv, hot_lens=torch.tensor(hlens, dtype=torch.int32, device="cuda"))
+    out = torch.full((B, hq, d), float("nan"), device="cuda")
+    lse = torch.full((B, hq), float("nan"), device="cuda")
+    h.sparse_attention(q, index, book, rec, sl, k, out=out, lse=lse, **hot)
+    out2 = h.sparse_attention(q, index, book, rec, sl, k, **hot)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2), "sparse attention is not deterministic"
+    gi, gb = index.cpu().numpy(), book.cpu().numpy()
+    if k > 0:
+        ri, _, _ = O.select_topk(codec, _np(q), gi, gb, lens, k)
+    else:
+        ri = np.full((B, H, 1), -1, np.int32)
+    ref, ref_lse, _ = O.decode_attention(codec, _np(q), rec.cpu().numpy(), lens,
+                                         None if hk is None else _np(hk), None if hv is None else _np(hv),
+                                         hlens, sel_idx=ri)
+    o, L = out.cpu().numpy(), lse.cpu().numpy()
+    _close(o, ref, f"sparse attention kb={kb} vb={vb} m={m} G={hq // H} k={k}")
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(np.isfinite(L), fin)
+    _close(L[fin], ref_lse[fin], "sparse attention lse")
+    assert np.all(o[~fin] == 0)
+
+
 # ------------------------------------------------------------------ bulk scan -----------
 def test_score_scan_reduced():
     w = W.small(W.WORKLOADS["bulk_64k_scan"], tokens=1000, scan_queries=70)
