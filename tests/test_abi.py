@@ -77,6 +77,10 @@ def test_null_handle_is_rejected_everywhere():
                       None, None, None, None, 0, None) == 1
     assert tq._select(None, None, 0, 1, 1, 1, None, None, 1, None, 1, None, None, None, None, 0, None) == 1
     assert tq._scan(None, None, 0, 1, 1, 1, None, 1, 1, None, None, 0, None) == 1
+    assert tq._sparse_ws(None, 1, 1, 1, 1, ctypes.byref(n)) == 1
+    assert tq._sparse(None, None, 0, 1, 1, 1, None, None, None, 1, None, 1, None, None, 0, None, 0, 0.0,
+                      None, None, None, 0, None) == 1
+    assert tq._monarch_ws(None, 1, 1, 1, 1, 1, ctypes.byref(n)) == 1
     assert "NULL" in tq.last_error()
 
 
