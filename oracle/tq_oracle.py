@@ -205,6 +205,21 @@ class Codec:
     def index_bytes(self):
         return self.head_dim // 8
 
+    # per-codec steps (the polar variant of stage 1 replaces these four) ----------------
+    def compress_fields(self, k, v):
+        return compress(self, k, v)
+
+    def pack(self, f):
+        return pack_records(self, f)
+
+    def unpack(self, rec):
+        return unpack_records(self, rec)
+
+    def key_part(self, qx, f):
+        """First term of the estimator: <q_x, xhat_t> with xhat_t = (r_t/sqrt(d)) gamma[c_t]."""
+        gk = self.key_levels.astype(np.float64)
+        return (f["r_k"].astype(np.float64) / math.sqrt(self.head_dim)) * (gk[f["kc"]] @ qx)
+
 
 # ----------------------------------------------------------------------------------------
 # Compression (TurboQuant page, "Funktionsweise" steps 1 and 2)
@@ -369,7 +384,7 @@ def compress_cache(codec: Codec, K: np.ndarray, V: np.ndarray, capacity: int | N
     out = np.zeros((B, H, cap, codec.record_bytes), np.uint8)
     kk = np.transpose(K, (0, 2, 1, 3))
     vv = np.transpose(V, (0, 2, 1, 3))
-    out[:, :, :T] = pack_records(codec, compress(codec, kk, vv))
+    out[:, :, :T] = codec.pack(codec.compress_fields(kk, vv))
     return out
 
 
@@ -403,9 +418,8 @@ def score_estimates(codec: Codec, qx: np.ndarray, qs: np.ndarray, f: dict) -> np
     E[sign(<s, e>) <s, q>] = sqrt(2/pi) <q, e> / |e| for s ~ N(0, I) (reading: the page
     names only "a special estimator" that is unbiased).
     """
-    d, m = codec.head_dim, codec.qjl_dim
-    gk = codec.key_levels.astype(np.float64)
-    s = (f["r_k"].astype(np.float64) / math.sqrt(d)) * (gk[f["kc"]] @ qx)
+    m = codec.qjl_dim
+    s = codec.key_part(qx, f)
     if m:
         sgn = 2.0 * f["bits"].astype(np.float64) - 1.0
         s = s + math.sqrt(math.pi / 2.0) / m * f["rho"].astype(np.float64) * (sgn @ qs)
@@ -452,7 +466,7 @@ def decode_attention(codec: Codec, q, records, seq_lens, hot_k=None, hot_v=None,
                 idx = idx[idx >= 0]
             else:
                 idx = np.arange(int(seq_lens[b]))
-            f = unpack_records(codec, records[b, g, idx])
+            f = codec.unpack(records[b, g, idx])
             qx, qs = prepare_query(codec, q[b, h])
             lc = sc * score_estimates(codec, qx, qs, f)
             nh = 0 if hot_lens is None else int(hot_lens[b])
@@ -483,7 +497,7 @@ def score_scan(codec: Codec, q, records, n_tokens: int):
     out = np.zeros((B, H, nq, n_tokens))
     for b in range(B):
         for h in range(H):
-            f = unpack_records(codec, records[b, h, :n_tokens])
+            f = codec.unpack(records[b, h, :n_tokens])
             for i in range(nq):
                 qx, qs = prepare_query(codec, q[b, h, i])
                 out[b, h, i] = score_estimates(codec, qx, qs, f)
