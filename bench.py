@@ -38,7 +38,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "compressed_key_attention_amd", "csrc", "tq_kernels.hip")
 PROFILES = os.path.join(ROOT, "profiles")
-DECODE_WORKLOADS = ["llama8b_decode_32k", "tinyllama_layer", "single_head_1k"]
+DECODE_WORKLOADS = ["llama8b_decode_32k", "tinyllama_layer", "single_head_1k", "llama8b_decode_32k_polar"]
 
 
 class HipEvents:
@@ -92,12 +92,15 @@ def decode_kernel_name(w) -> str:
     """The scan kernel the library picks for this shape (matrix-core path for head_dim 128,
     4 query heads per KV head, 2/3-bit keys, 4-bit values, m in {0, 128})."""
     mfma = (w.head_dim == 128 and w.q_heads == 4 * w.kv_heads and w.value_bits == 4
-            and w.key_bits in (2, 3) and w.qjl_dim in (0, 128))
+            and w.key_bits in (2, 3) and w.qjl_dim in (0, 128) and not w.polar_upper_bits)
     return "decode_mfma_kernel" if mfma else "decode_scan_kernel"
 
 
 def record_payload_bytes(w) -> int:
-    return w.head_dim * w.key_bits // 8 + w.qjl_dim // 8 + w.head_dim * w.value_bits // 8 + 12
+    kbytes = w.head_dim * w.key_bits // 8
+    if w.polar_upper_bits:   # level-1 angle stream + upper-level stream in whole 32-bit words
+        kbytes = w.head_dim // 2 * w.key_bits // 8 + 4 * (((w.head_dim // 2 - 1) * w.polar_upper_bits + 31) // 32)
+    return kbytes + w.qjl_dim // 8 + w.head_dim * w.value_bits // 8 + 12
 
 
 KERNEL_STATS = {}   # median / min of the last time_steps' dominant-kernel durations
@@ -207,11 +210,19 @@ def compress_once(ev, tq, h, K, V, records):
 _CODECS = {}
 
 
+def codec_args_of(w):
+    """The oracle codec's constructor arguments for a workload (last: polar upper-level bits)."""
+    return (w.head_dim, w.key_bits, w.qjl_dim, w.value_bits, w.seed * 3 + 1, w.seed * 3 + 2,
+            w.polar_upper_bits)
+
+
 def _codec(codec_args):
     """The oracle's handle constants, built once per process (outside any timed region)."""
     if codec_args not in _CODECS:
+        from oracle import polar as P
         from oracle import tq_oracle as O
-        _CODECS[codec_args] = O.Codec(*codec_args)
+        *base, ub = codec_args
+        _CODECS[codec_args] = P.PolarCodec(*base, upper_bits=ub) if ub else O.Codec(*base)
     return _CODECS[codec_args]
 
 
@@ -320,7 +331,9 @@ def base_line(args, w, ms_per_step, tokens_per_step):
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
                    "head_dim": w.head_dim, "context": w.tokens, "key_bits": w.key_bits,
                    "qjl_dim": w.qjl_dim, "value_bits": w.value_bits, "kv_dtype": w.kv_dtype,
-                   "q_dtype": w.q_dtype, "seed": w.seed},
+                   "q_dtype": w.q_dtype, "seed": w.seed,
+                   "key_codec": "polar" if w.polar_upper_bits else "scalar",
+                   "polar_upper_bits": w.polar_upper_bits},
     }
 
 
@@ -329,7 +342,8 @@ def run_decode(args, tq, W, ev):
     import torch
     w = W.WORKLOADS[args.workload]
     dev = "cuda"
-    h = tq.Handle(w.head_dim, w.key_bits, w.qjl_dim, w.value_bits, w.seed * 3 + 1, w.seed * 3 + 2)
+    h = tq.Handle(w.head_dim, w.key_bits, w.qjl_dim, w.value_bits, w.seed * 3 + 1, w.seed * 3 + 2,
+                  polar_upper_bits=w.polar_upper_bits)
     K, V = W.make_kv(w, dev)
     q = W.make_queries(w, dev)
     records = h.new_cache(w.batch, w.kv_heads, w.tokens, dev)
@@ -370,7 +384,7 @@ def run_decode(args, tq, W, ev):
 
 def cpu_baseline_decode(w, h, q, records, hot, budget_s: float = 12.0):
     """Oracle decode of whole sequences of the same cache (all query heads)."""
-    codec_args = (w.head_dim, w.key_bits, w.qjl_dim, w.value_bits, w.seed * 3 + 1, w.seed * 3 + 2)
+    codec_args = codec_args_of(w)
     qn = q.float().cpu().numpy()
     hk = hot["hot_k"].float().cpu().numpy() if hot else None
     hv = hot["hot_v"].float().cpu().numpy() if hot else None
@@ -388,7 +402,7 @@ def cpu_baseline_compress(w, budget_s: float = 4.0):
     """Oracle compress (one core) of 4096-token blocks of one head of the same synthetic K/V."""
     from threadpoolctl import threadpool_limits
     from compressed_key_attention_amd import workloads as W
-    codec_args = (w.head_dim, w.key_bits, w.qjl_dim, w.value_bits, w.seed * 3 + 1, w.seed * 3 + 2)
+    codec_args = codec_args_of(w)
     codec = _codec(codec_args)
     from oracle import tq_oracle as O
     K, V = W.make_kv(w, "cpu", tokens=4096, batch=1)
@@ -398,7 +412,7 @@ def cpu_baseline_compress(w, budget_s: float = 4.0):
             k = K[0, :, hh].float().numpy()
             v = V[0, :, hh].float().numpy()
             t0 = time.perf_counter()
-            O.compress(codec, k, v)
+            codec.compress_fields(k, v)
             elapsed += time.perf_counter() - t0
             done += 1
             if elapsed >= budget_s:
@@ -412,7 +426,8 @@ def run_sparse(args, tq, W, ev):
     import torch
     w = W.WORKLOADS["sparse_128k_top2048"]
     dev = "cuda"
-    h = tq.Handle(w.head_dim, w.key_bits, w.qjl_dim, w.value_bits, w.seed * 3 + 1, w.seed * 3 + 2)
+    h = tq.Handle(w.head_dim, w.key_bits, w.qjl_dim, w.value_bits, w.seed * 3 + 1, w.seed * 3 + 2,
+                  polar_upper_bits=w.polar_upper_bits)
     K, V = W.make_kv(w, dev)
     B, T, H, d = K.shape
     index = torch.empty((B, H, T, d // 8), dtype=torch.uint8, device=dev)
@@ -474,7 +489,7 @@ def run_sparse(args, tq, W, ev):
 def cpu_baseline_sparse(w, q, index, book, records, budget_s: float = 12.0):
     """Oracle select + gathered attention per (sequence, KV head) unit; a unit scores T tokens
     of one KV head, so T / kv_heads tokens of the workload."""
-    codec_args = (w.head_dim, w.key_bits, w.qjl_dim, w.value_bits, w.seed * 3 + 1, w.seed * 3 + 2)
+    codec_args = codec_args_of(w)
     qn = q.float().cpu().numpy()
     T, G = w.tokens, w.q_heads // w.kv_heads
     units = [(b, hh) for b in range(w.batch) for hh in range(w.kv_heads)]
@@ -494,7 +509,8 @@ def run_bulk_scan(args, tq, W, ev):
     import torch
     w = W.WORKLOADS["bulk_64k_scan"]
     dev = "cuda"
-    h = tq.Handle(w.head_dim, w.key_bits, w.qjl_dim, w.value_bits, w.seed * 3 + 1, w.seed * 3 + 2)
+    h = tq.Handle(w.head_dim, w.key_bits, w.qjl_dim, w.value_bits, w.seed * 3 + 1, w.seed * 3 + 2,
+                  polar_upper_bits=w.polar_upper_bits)
     K, V = W.make_kv(w, dev)
     B, T, H, d = K.shape
     records = h.new_cache(B, H, T, dev)
@@ -537,7 +553,7 @@ def run_bulk_scan(args, tq, W, ev):
 def cpu_baseline_scan(w, q, records, budget_s: float = 12.0):
     """Oracle bulk scan on 4096-token blocks of one KV head (all its queries); a block is
     4096 / kv_heads tokens of the workload."""
-    codec_args = (w.head_dim, w.key_bits, w.qjl_dim, w.value_bits, w.seed * 3 + 1, w.seed * 3 + 2)
+    codec_args = codec_args_of(w)
     qn = q.float().cpu().numpy()
     chunk = 4096
     units = [(hh, t0) for hh in range(w.kv_heads) for t0 in range(0, w.tokens, chunk)]
@@ -558,7 +574,8 @@ def run_monarch(args, tq, W, ev):
     import torch
     w = W.WORKLOADS["tinyllama_layer"]
     dev = "cuda"
-    h = tq.Handle(w.head_dim, w.key_bits, w.qjl_dim, w.value_bits, w.seed * 3 + 1, w.seed * 3 + 2)
+    h = tq.Handle(w.head_dim, w.key_bits, w.qjl_dim, w.value_bits, w.seed * 3 + 1, w.seed * 3 + 2,
+                  polar_upper_bits=w.polar_upper_bits)
     n_steps = args.warmup + args.steps + 20
     window, Hq, H, d = w.hot_tokens, w.q_heads, w.kv_heads, w.head_dim
     hot_cap = window + 1 + 6 * Hq

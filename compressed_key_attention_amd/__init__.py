@@ -32,14 +32,16 @@ EXPORTED = [
     "tq_index_workspace_size", "tq_build_sign_index", "tq_select_workspace_size",
     "tq_select_topk", "tq_scan_workspace_size", "tq_score_scan", "tq_set_profile_events",
     "tq_stream_read", "tq_monarch_workspace_size", "tq_monarch_step", "tq_sparse_workspace_size",
-    "tq_sparse_attention",
+    "tq_sparse_attention", "tq_polar_host_constants",
 ]
+TQ_KEY_SCALAR, TQ_KEY_POLAR = 0, 1
 
 
 class TqConfig(ctypes.Structure):
     _fields_ = [("head_dim", ctypes.c_int32), ("key_bits", ctypes.c_int32),
                 ("qjl_dim", ctypes.c_int32), ("value_bits", ctypes.c_int32),
-                ("rotation_seed", ctypes.c_uint64), ("qjl_seed", ctypes.c_uint64)]
+                ("rotation_seed", ctypes.c_uint64), ("qjl_seed", ctypes.c_uint64),
+                ("key_codec", ctypes.c_int32), ("polar_upper_bits", ctypes.c_int32)]
 
 
 class MonarchConfig(ctypes.Structure):
@@ -78,6 +80,7 @@ _lib.tq_last_error.argtypes = []
 _create = _sig("tq_create", ctypes.POINTER(TqConfig), ctypes.POINTER(_P))
 _destroy = _sig("tq_destroy", _P)
 _host_constants = _sig("tq_host_constants", ctypes.POINTER(TqConfig), _P, _P, _P, _P, _P, _P)
+_polar_host_constants = _sig("tq_polar_host_constants", ctypes.POINTER(TqConfig), _P, _P)
 _record_bytes = _sig("tq_record_bytes", _P, _PSZ, _PSZ)
 _compress = _sig("tq_compress_kv", _P, _P, _P, ctypes.c_int, _I32, _I64, _I32, _I64, _I64, _I64,
                  _P, _I64, _I64, _P)
@@ -123,8 +126,22 @@ def check(status: int):
         raise TqError(status, last_error())
 
 
-def _config(head_dim, key_bits, qjl_dim, value_bits, rotation_seed, qjl_seed) -> TqConfig:
-    return TqConfig(head_dim, key_bits, qjl_dim, value_bits, rotation_seed, qjl_seed)
+def _config(head_dim, key_bits, qjl_dim, value_bits, rotation_seed, qjl_seed, polar_upper_bits=0) -> TqConfig:
+    """polar_upper_bits > 0 selects the polar key codec (key_bits = level-1 angle bits)."""
+    codec = TQ_KEY_POLAR if polar_upper_bits else TQ_KEY_SCALAR
+    return TqConfig(head_dim, key_bits, qjl_dim, value_bits, rotation_seed, qjl_seed, codec,
+                    polar_upper_bits)
+
+
+def polar_host_constants(head_dim, key_bits, qjl_dim, value_bits, rotation_seed, qjl_seed,
+                         polar_upper_bits):
+    """The polar angle grids computed on the host (no GPU): levels, bounds [L][16]."""
+    cfg = _config(head_dim, key_bits, qjl_dim, value_bits, rotation_seed, qjl_seed, polar_upper_bits)
+    L = head_dim.bit_length() - 1
+    lv = np.full((L, 16), np.nan, np.float32)
+    bd = np.full((L, 16), np.nan, np.float32)
+    check(_polar_host_constants(ctypes.byref(cfg), lv.ctypes.data_as(_P), bd.ctypes.data_as(_P)))
+    return lv, bd
 
 
 def host_constants(head_dim, key_bits, qjl_dim, value_bits, rotation_seed, qjl_seed):
@@ -165,10 +182,11 @@ class Handle:
     """A tq_handle: the seeded rotation, QJL matrix and codebooks on the current device."""
 
     def __init__(self, head_dim=128, key_bits=3, qjl_dim=128, value_bits=4,
-                 rotation_seed=1, qjl_seed=2):
+                 rotation_seed=1, qjl_seed=2, polar_upper_bits=0):
         self.head_dim, self.key_bits, self.qjl_dim, self.value_bits = head_dim, key_bits, qjl_dim, value_bits
         self.rotation_seed, self.qjl_seed = rotation_seed, qjl_seed
-        cfg = _config(head_dim, key_bits, qjl_dim, value_bits, rotation_seed, qjl_seed)
+        self.polar_upper_bits = polar_upper_bits
+        cfg = _config(head_dim, key_bits, qjl_dim, value_bits, rotation_seed, qjl_seed, polar_upper_bits)
         h = _P()
         check(_create(ctypes.byref(cfg), ctypes.byref(h)))
         self._h = h

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -175,6 +176,124 @@ void lloyd_max(int bits, std::vector<double>* levels, std::vector<double>* bound
   for (int i = 0; i + 1 < L; ++i) (*bounds)[i] = 0.5 * (lev[i] + lev[i + 1]);
 }
 
+// ---------------------------------------------------------------------------------------
+// Polar angle grids.  Level 1: uniform on the circle, 2^b cells of width 2 pi / 2^b from -pi,
+// reconstruction at the centres.  Level l >= 2: the angle of two child radii over
+// n = 2^(l-1) coordinates each has density proportional to sin(2 psi)^(n-1) on [0, pi/2]
+// (sin^2 psi ~ Beta(n/2, n/2) for a random direction); its Lloyd-Max grid is iterated in
+// float64 with cell masses and first moments from composite 16-point Gauss-Legendre
+// quadrature (32 panels per cell), levels kept mirror-symmetric about pi/4.
+// ---------------------------------------------------------------------------------------
+constexpr double kPi = 3.141592653589793;
+
+struct GaussLegendre16 {
+  double x[16], w[16];
+  GaussLegendre16() {
+    // roots of P_16 by Newton's method from the Chebyshev-like guesses cos(pi (i + 3/4) / (n + 1/2))
+    const int n = 16;
+    for (int i = 0; i < n; ++i) {
+      double z = std::cos(kPi * (i + 0.75) / (n + 0.5)), dp = 0.0;
+      for (int it = 0; it < 100; ++it) {
+        double p0 = 1.0, p1 = 0.0;
+        for (int j = 1; j <= n; ++j) {   // Bonnet's recurrence
+          const double p2 = p1;
+          p1 = p0;
+          p0 = ((2.0 * j - 1.0) * z * p1 - (j - 1.0) * p2) / j;
+        }
+        dp = n * (z * p0 - p1) / (z * z - 1.0);
+        const double dz = p0 / dp;
+        z -= dz;
+        if (std::fabs(dz) < 1e-16) break;
+      }
+      x[i] = z;
+      w[i] = 2.0 / ((1.0 - z * z) * dp * dp);
+    }
+  }
+};
+
+void angle_cell(int n, double lo, double hi, double* mass, double* moment) {
+  static const GaussLegendre16 gl;
+  const int panels = 32;
+  const double h = (hi - lo) / panels;
+  double m0 = 0.0, m1 = 0.0;
+  for (int p = 0; p < panels; ++p) {
+    const double a = lo + p * h, half = 0.5 * h, mid = a + half;
+    for (int i = 0; i < 16; ++i) {
+      const double t = mid + half * gl.x[i];
+      const double f = std::pow(std::sin(2.0 * t), n - 1) * gl.w[i] * half;
+      m0 += f;
+      m1 += t * f;
+    }
+  }
+  *mass = m0;
+  *moment = m1;
+}
+
+void angle_lloyd_max(int level, int bits, std::vector<double>* levels, std::vector<double>* bounds) {
+  const int n = 1 << (level - 1), L = 1 << bits;
+  const double half_pi = 0.5 * kPi, quarter = 0.25 * kPi;
+  // start: evenly spread over about two standard deviations of the law, sd ~ 1 / (2 sqrt(n - 1))
+  const double spread = std::min(0.9 * quarter, 1.0 / std::sqrt((double)(n - 1)));
+  std::vector<double> lev(L), nxt(L);
+  for (int i = 0; i < L; ++i) lev[i] = quarter + spread * (-1.0 + 2.0 * (i + 0.5) / L);
+  for (int it = 0; it < 200000; ++it) {
+    for (int i = 0; i < L; ++i) {
+      const double lo = i == 0 ? 0.0 : 0.5 * (lev[i - 1] + lev[i]);
+      const double hi = i == L - 1 ? half_pi : 0.5 * (lev[i] + lev[i + 1]);
+      double mass, mom;
+      angle_cell(n, lo, hi, &mass, &mom);
+      nxt[i] = mom / mass;
+    }
+    double delta = 0.0;
+    for (int i = 0; i < L; ++i) {
+      const double a = 0.5 * (nxt[i] + (half_pi - nxt[L - 1 - i]));
+      delta = std::fmax(delta, std::fabs(a - lev[i]));
+      lev[i] = a;
+    }
+    if (delta < 1e-13) break;
+  }
+  levels->assign(lev.begin(), lev.end());
+  bounds->resize(L - 1);
+  for (int i = 0; i + 1 < L; ++i) (*bounds)[i] = 0.5 * (lev[i] + lev[i + 1]);
+}
+
+// float32 grids of every level: levels[l][16], bounds[l][16] (+inf past the used entries).
+// Computed once per (head_dim, b1, bh) and kept for the process.
+void polar_grids(int d, int b1, int bh, float (*levels)[16], float (*bounds)[16]) {
+  struct Entry { int d, b1, bh; float lv[tq::kMaxPolarLevels][16], bd[tq::kMaxPolarLevels][16]; };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  const Entry* hit = nullptr;
+  for (const Entry& e : cache)
+    if (e.d == d && e.b1 == b1 && e.bh == bh) hit = &e;
+  if (!hit) {
+    Entry e;
+    e.d = d;
+    e.b1 = b1;
+    e.bh = bh;
+    for (int l = 0; l < tq::kMaxPolarLevels; ++l)
+      for (int i = 0; i < 16; ++i) {
+        e.lv[l][i] = 0.0f;
+        e.bd[l][i] = INFINITY;
+      }
+    const int L = (int)std::lround(std::log2((double)d));
+    const double w = 2.0 * kPi / (1 << b1);
+    for (int i = 0; i < (1 << b1); ++i) e.lv[0][i] = (float)(-kPi + (i + 0.5) * w);
+    for (int j = 1; j < (1 << b1); ++j) e.bd[0][j - 1] = (float)(-kPi + j * w);
+    for (int l = 2; l <= L; ++l) {
+      std::vector<double> lv, bd;
+      angle_lloyd_max(l, bh, &lv, &bd);
+      for (size_t i = 0; i < lv.size(); ++i) e.lv[l - 1][i] = (float)lv[i];
+      for (size_t i = 0; i < bd.size(); ++i) e.bd[l - 1][i] = (float)bd[i];
+    }
+    cache.push_back(e);
+    hit = &cache.back();
+  }
+  std::memcpy(levels, hit->lv, sizeof hit->lv);
+  std::memcpy(bounds, hit->bd, sizeof hit->bd);
+}
+
 // Scale F for two-limb fixed-point key levels (level ~= round(level * F) / F, |round| <= 32512):
 // among F in [F_max / 2, F_max] the one whose products with the float32 levels lie closest
 // to integers (worst case over the levels), so integer score products lose the least.
@@ -212,6 +331,17 @@ tq_status check_config(const tq_config* cfg) {
     return fail(TQ_ERR_UNSUPPORTED, "head_dim %d not built (64 or 128)", cfg->head_dim);
   if (cfg->key_bits < 2 || cfg->value_bits < 2)
     return fail(TQ_ERR_UNSUPPORTED, "1-bit stage-1 codes are not built (key/value bits 2..4)");
+  if (cfg->key_codec == TQ_KEY_SCALAR) {
+    if (cfg->polar_upper_bits != 0)
+      return fail(TQ_ERR_INVALID_ARGUMENT, "polar_upper_bits must be 0 for the scalar key codec");
+  } else if (cfg->key_codec == TQ_KEY_POLAR) {
+    if (cfg->key_bits != 2 && cfg->key_bits != 4)
+      return fail(TQ_ERR_UNSUPPORTED, "polar keys: key_bits (level-1 angle bits) must be 2 or 4");
+    if (cfg->polar_upper_bits != 1 && cfg->polar_upper_bits != 2 && cfg->polar_upper_bits != 4)
+      return fail(TQ_ERR_UNSUPPORTED, "polar keys: polar_upper_bits must be 1, 2 or 4");
+  } else {
+    return fail(TQ_ERR_INVALID_ARGUMENT, "unknown key_codec %d", cfg->key_codec);
+  }
   return TQ_OK;
 }
 
@@ -222,6 +352,14 @@ void fill_consts(const tq_config* cfg, tq::Consts* c) {
   c->m = cfg->qjl_dim;
   c->vb = cfg->value_bits;
   c->kbytes = c->d * c->kb / 8;
+  if (cfg->key_codec == TQ_KEY_POLAR) {
+    c->polar = 1;
+    c->pb1 = cfg->key_bits;
+    c->pbh = cfg->polar_upper_bits;
+    c->plevels = (int)std::lround(std::log2((double)c->d));
+    c->l1_bytes = c->d / 2 * c->pb1 / 8;
+    c->kbytes = c->l1_bytes + 4 * (((c->d / 2 - 1) * c->pbh + 31) / 32);
+  }
   c->sbytes = c->m / 8;
   c->vbytes = c->d * c->vb / 8;
   c->norm_off = c->kbytes + c->sbytes + c->vbytes;
@@ -281,6 +419,19 @@ struct tq_handle {
   int device;
 };
 
+namespace {
+
+// Calls built for the scalar key codec only.
+bool polar_unsupported(const tq_handle* h, const char* what, tq_status* st) {
+  if (h && h->c.polar) {
+    *st = fail(TQ_ERR_UNSUPPORTED, "%s is not built for polar key codes", what);
+    return true;
+  }
+  return false;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* tq_last_error(void) { return g_last_error.c_str(); }
@@ -295,6 +446,10 @@ tq_status tq_set_profile_events(hipEvent_t start, hipEvent_t stop) {
 
 tq_status tq_monarch_workspace_size(const tq_handle* h, int32_t batch, int32_t q_heads, int32_t kv_heads,
                                     int64_t hot_capacity, int64_t cold_capacity, size_t* bytes) {
+  {
+    tq_status pst;
+    if (polar_unsupported(h, "the hot/cold step", &pst)) return pst;
+  }
   if (!h || !bytes) return fail(TQ_ERR_INVALID_ARGUMENT, "NULL handle or output");
   if (batch < 0 || q_heads <= 0 || kv_heads <= 0 || q_heads % kv_heads || hot_capacity <= 0 || cold_capacity < 0)
     return fail(TQ_ERR_INVALID_ARGUMENT, "bad hot/cold shape");
@@ -309,6 +464,10 @@ tq_status tq_monarch_step(const tq_handle* h, const tq_monarch_config* cfg, cons
                           const void* q, tq_dtype q_dt, int32_t batch, int32_t q_heads, int32_t kv_heads,
                           const void* k_new, const void* v_new, float scale, float* out, float* lse,
                           int32_t* gate_out, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  {
+    tq_status pst;
+    if (polar_unsupported(h, "the hot/cold step", &pst)) return pst;
+  }
   if (!h || !cfg || !st) return fail(TQ_ERR_INVALID_ARGUMENT, "handle, config or state is NULL");
   size_t es, hs;
   if (!elem_size(q_dt, &es)) return fail(TQ_ERR_INVALID_ARGUMENT, "unknown query dtype");
@@ -409,6 +568,23 @@ tq_status tq_host_constants(const tq_config* cfg, float* pi, float* s, float* ke
   return ok();
 }
 
+tq_status tq_polar_host_constants(const tq_config* cfg, float* levels, float* bounds) {
+  tq_status st = check_config(cfg);
+  if (st != TQ_OK) return st;
+  if (cfg->key_codec != TQ_KEY_POLAR) return fail(TQ_ERR_INVALID_ARGUMENT, "config is not a polar key codec");
+  float lv[tq::kMaxPolarLevels][16], bd[tq::kMaxPolarLevels][16];
+  polar_grids(cfg->head_dim, cfg->key_bits, cfg->polar_upper_bits, lv, bd);
+  const int L = (int)std::lround(std::log2((double)cfg->head_dim));
+  for (int l = 0; l < L; ++l) {
+    const int bits = l == 0 ? cfg->key_bits : cfg->polar_upper_bits;
+    for (int i = 0; i < (1 << bits); ++i)
+      if (levels) levels[l * 16 + i] = lv[l][i];
+    for (int i = 0; i + 1 < (1 << bits); ++i)
+      if (bounds) bounds[l * 16 + i] = bd[l][i];
+  }
+  return ok();
+}
+
 tq_status tq_create(const tq_config* cfg, tq_handle** out) {
   if (!out) return fail(TQ_ERR_INVALID_ARGUMENT, "out is NULL");
   *out = nullptr;
@@ -434,7 +610,11 @@ tq_status tq_create(const tq_config* cfg, tq_handle** out) {
       s_pi[(size_t)k * d + j] = (float)acc;
     }
   const size_t n_pi = (size_t)d * d, n_s = (size_t)m * d;
-  const size_t total = (3 * n_pi + 3 * n_s) * sizeof(float);
+  // polar tables: bounds f32 [8][16], cos/sin f64 [8][16][2], cos/sin f32 [8][16][2]
+  constexpr size_t kPT = (size_t)tq::kMaxPolarLevels * 16;
+  const size_t polar_bytes = h->c.polar ? kPT * 4 + kPT * 16 + kPT * 8 : 0;
+  const size_t main_bytes = (3 * n_pi + 3 * n_s) * sizeof(float);
+  const size_t total = main_bytes + polar_bytes;
   if (hipGetDevice(&h->device) != hipSuccess) { delete h; return fail(TQ_ERR_DEVICE, "no HIP device"); }
   if (hipMalloc(&h->dev_block, total) != hipSuccess) {
     delete h;
@@ -449,7 +629,26 @@ tq_status tq_create(const tq_config* cfg, tq_handle** out) {
   host.insert(host.end(), s_m.begin(), s_m.end());
   host.insert(host.end(), pi_t.begin(), pi_t.end());
   host.insert(host.end(), s_pi.begin(), s_pi.end());
-  hipError_t e = hipMemcpy(base, host.data(), total, hipMemcpyHostToDevice);
+  std::vector<uint8_t> ptab(polar_bytes);
+  if (h->c.polar) {
+    float lv[tq::kMaxPolarLevels][16], bd[tq::kMaxPolarLevels][16];
+    polar_grids(d, h->c.pb1, h->c.pbh, lv, bd);
+    float* pb = reinterpret_cast<float*>(ptab.data());
+    double* c64 = reinterpret_cast<double*>(ptab.data() + kPT * 4);
+    float* c32 = reinterpret_cast<float*>(ptab.data() + kPT * 4 + kPT * 16);
+    for (size_t i = 0; i < kPT; ++i) {
+      pb[i] = bd[i / 16][i % 16];
+      const double a = (double)lv[i / 16][i % 16];
+      c64[2 * i] = std::cos(a);
+      c64[2 * i + 1] = std::sin(a);
+      c32[2 * i] = (float)c64[2 * i];
+      c32[2 * i + 1] = (float)c64[2 * i + 1];
+    }
+  }
+  hipError_t e = hipMemcpy(base, host.data(), main_bytes, hipMemcpyHostToDevice);
+  if (e == hipSuccess && polar_bytes)
+    e = hipMemcpy(reinterpret_cast<uint8_t*>(h->dev_block) + main_bytes, ptab.data(), polar_bytes,
+                  hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     (void)hipFree(h->dev_block);
     delete h;
@@ -461,6 +660,13 @@ tq_status tq_create(const tq_config* cfg, tq_handle** out) {
   h->dc.s_mfma = m ? base + 2 * n_pi + n_s : nullptr;
   h->dc.pi_t = base + 2 * n_pi + 2 * n_s;
   h->dc.s_pi = m ? base + 3 * n_pi + 2 * n_s : nullptr;
+  h->dc.polar = tq::PolarTables{nullptr, nullptr, nullptr};
+  if (h->c.polar) {
+    uint8_t* pt = reinterpret_cast<uint8_t*>(h->dev_block) + main_bytes;
+    h->dc.polar.bounds = reinterpret_cast<const float*>(pt);
+    h->dc.polar.cs64 = reinterpret_cast<const double*>(pt + kPT * 4);
+    h->dc.polar.cs32 = reinterpret_cast<const float*>(pt + kPT * 4 + kPT * 16);
+  }
   *out = h;
   return ok();
 }
@@ -522,6 +728,10 @@ tq_status tq_compress_kv(const tq_handle* h, const void* k, const void* v, tq_dt
 tq_status tq_debug_quantize(const tq_handle* h, const float* z_k, const float* p,
                             const float* r_k, const float* rho, const float* z_v,
                             const float* r_v, int64_t n, void* records, hipStream_t stream) {
+  {
+    tq_status pst;
+    if (polar_unsupported(h, "the debug quantize entry", &pst)) return pst;
+  }
   if (!h) return fail(TQ_ERR_INVALID_ARGUMENT, "handle is NULL");
   if (n < 0) return fail(TQ_ERR_INVALID_ARGUMENT, "n < 0");
   if (n == 0) return ok();
@@ -649,6 +859,10 @@ tq_status tq_select_topk(const tq_handle* h, const void* q, tq_dtype q_dt, int32
 
 tq_status tq_sparse_workspace_size(const tq_handle* h, int32_t batch, int32_t q_heads,
                                    int32_t kv_heads, int64_t capacity, size_t* bytes) {
+  {
+    tq_status pst;
+    if (polar_unsupported(h, "sparse attention", &pst)) return pst;
+  }
   if (!h || !bytes) return fail(TQ_ERR_INVALID_ARGUMENT, "NULL handle or output");
   if (batch < 0 || q_heads <= 0 || kv_heads <= 0 || q_heads % kv_heads || capacity < 0)
     return fail(TQ_ERR_INVALID_ARGUMENT, "bad shape");
@@ -663,6 +877,10 @@ tq_status tq_sparse_attention(const tq_handle* h, const void* q, tq_dtype q_dt, 
                               const void* hot_v, tq_dtype hot_dt, const int32_t* hot_lens,
                               int64_t hot_capacity, float scale, float* out, float* lse,
                               void* workspace, size_t ws_bytes, hipStream_t stream) {
+  {
+    tq_status pst;
+    if (polar_unsupported(h, "sparse attention", &pst)) return pst;
+  }
   if (!h) return fail(TQ_ERR_INVALID_ARGUMENT, "handle is NULL");
   size_t es;
   if (!elem_size(q_dt, &es)) return fail(TQ_ERR_INVALID_ARGUMENT, "unknown query dtype");
@@ -698,6 +916,10 @@ tq_status tq_sparse_attention(const tq_handle* h, const void* q, tq_dtype q_dt, 
 
 tq_status tq_scan_workspace_size(const tq_handle* h, int32_t batch, int32_t kv_heads,
                                  int32_t n_queries, size_t* bytes) {
+  {
+    tq_status pst;
+    if (polar_unsupported(h, "the bulk scan", &pst)) return pst;
+  }
   if (!h || !bytes) return fail(TQ_ERR_INVALID_ARGUMENT, "NULL handle or output");
   if (batch < 0 || kv_heads <= 0 || n_queries < 0) return fail(TQ_ERR_INVALID_ARGUMENT, "bad shape");
   *bytes = tq::plan_scan(h->c, batch, kv_heads, n_queries).ws_total;
@@ -708,6 +930,10 @@ tq_status tq_score_scan(const tq_handle* h, const void* q, tq_dtype q_dt, int32_
                         int32_t kv_heads, int32_t n_queries, const void* records,
                         int64_t capacity, int64_t n_tokens, float* scores, void* workspace,
                         size_t ws_bytes, hipStream_t stream) {
+  {
+    tq_status pst;
+    if (polar_unsupported(h, "the bulk scan", &pst)) return pst;
+  }
   if (!h) return fail(TQ_ERR_INVALID_ARGUMENT, "handle is NULL");
   size_t es;
   if (!elem_size(q_dt, &es)) return fail(TQ_ERR_INVALID_ARGUMENT, "unknown query dtype");

@@ -37,6 +37,23 @@ struct Consts {
   float key_fix;                  // fixed-point scale of the key levels for integer products:
                                   // |level| * key_fix <= 32512, levels * key_fix near integers
   float key_fix3;                 // three-limb scale: max |level| * key_fix3 = 127 * 65536
+  // polar key codes (0 / unused for the scalar codec)
+  int polar;                      // 1: keys are recursive polar angle codes
+  int pb1, pbh;                   // bits per level-1 angle / per higher angle
+  int plevels;                    // L = log2 d
+  int l1_bytes;                   // bytes of the level-1 code stream (the rest of kbytes: levels 2..L)
+};
+
+constexpr int kMaxPolarLevels = 8;   // log2 of the largest head_dim (128) is 7
+
+// Polar angle tables in device memory, row l-1 = level l, 16 entries per row:
+//   bounds  float  [8][16]  (unused entries +inf)
+//   cs64    double [8][16][2]  cos, sin of the float32 grid levels (float64)
+//   cs32    float  [8][16][2]  the same rounded to float32
+struct PolarTables {
+  const float* bounds;
+  const double* cs64;
+  const float* cs32;
 };
 
 // Device buffers a handle owns.
@@ -47,6 +64,7 @@ struct DevConsts {
   const float* s;         // [m][d] row-major
   const float* pi_mfma;   // Pi in the order the compress kernel's MFMA A operand reads it
   const float* s_mfma;    // S in the same order
+  PolarTables polar;      // polar key codec only (null pointers otherwise)
 };
 
 // ---- launchers (tq_kernels.hip) ----------------------------------------------------------

@@ -193,6 +193,7 @@ struct CompressArgs {
   int64_t capacity, first_slot;
   int64_t tiles_per_bh, n_tiles;
   int s_in_lds;
+  PolarTables polar;
 };
 
 template <int D>
@@ -270,6 +271,98 @@ __device__ __forceinline__ void quantize_rotated(f64x4 (&acc)[D / 16], double zs
   }
 }
 
+// -----------------------------------------------------------------------------------------
+// Polar key codes (TurboQuant page, section "PolarQuant"): the rotated key's coordinate pairs
+// become (radius, angle), radii are paired again up to one radius.  This lane group holds
+// coordinates [Q g, Q g + Q) (Q = d/4): levels 1 .. log2 Q are a subtree inside the lane, the
+// two top levels pair the lane groups (g, g^1) and ({0,1}, {2,3}) by shuffles.  Angles are
+// float64 atan2 (0 for two zeros); code = #{j : angle >= bound_j} on the float32 grid.  Codes
+// go to `codes` (one byte per angle at d - (d >> (l-1)) + node for level l, packed later);
+// x becomes the residual x - r u, u rebuilt top-down from the float64 cos / sin of the grid.
+// Every lane of the wave must call this (shuffles).
+// -----------------------------------------------------------------------------------------
+__device__ __forceinline__ double polar_angle(double a, double b) {
+  return (a == 0.0 && b == 0.0) ? 0.0 : atan2(b, a);
+}
+
+__device__ __forceinline__ uint32_t polar_code(double ang, const float* bounds_row, int nb) {
+  uint32_t c = 0;
+  for (int j = 0; j < nb; ++j) c += ang >= (double)bounds_row[j] ? 1u : 0u;
+  return c;
+}
+
+template <int D>
+__device__ __forceinline__ void polar_encode(f64x4 (&x)[D / 16], double r32, const PolarTables& pt,
+                                             int b1, int bh, uint8_t* codes, int g) {
+  constexpr int Q = D / 4, LQ = D == 128 ? 5 : 4;
+  const int nb1 = (1 << b1) - 1, nbh = (1 << bh) - 1;
+  double v[Q];
+#pragma unroll
+  for (int i = 0; i < Q; ++i) v[i] = x[i / 4][i % 4];
+  uint32_t cd[Q];   // codes of the lane's subtree: level l at Q - (Q >> (l-1)) + node
+#pragma unroll
+  for (int l = 1, cnt = Q, off = 0; l <= LQ; ++l) {
+#pragma unroll
+    for (int i = 0; i < cnt / 2; ++i) {
+      const double a = v[2 * i], b = v[2 * i + 1];
+      const uint32_t c = polar_code(polar_angle(a, b), pt.bounds + (l - 1) * 16, l == 1 ? nb1 : nbh);
+      cd[off + i] = c;
+      codes[D - (D >> (l - 1)) + (Q >> l) * g + i] = (uint8_t)c;
+      v[i] = sqrt(a * a + b * b);
+    }
+    off += cnt / 2;
+    cnt /= 2;
+  }
+  // the two levels above the lane: pairs of lane groups
+  const double r0 = v[0];
+  const double o1 = __shfl_xor(r0, 16);
+  const double l1 = (g & 1) ? o1 : r0, h1 = (g & 1) ? r0 : o1;
+  const uint32_t c1 = polar_code(polar_angle(l1, h1), pt.bounds + LQ * 16, nbh);
+  if ((g & 1) == 0) codes[D - (D >> LQ) + (g >> 1)] = (uint8_t)c1;
+  const double r1 = sqrt(l1 * l1 + h1 * h1);
+  const double o2 = __shfl_xor(r1, 32);
+  const double l2 = (g & 2) ? o2 : r1, h2 = (g & 2) ? r1 : o2;
+  const uint32_t c2 = polar_code(polar_angle(l2, h2), pt.bounds + (LQ + 1) * 16, nbh);
+  if (g == 0) codes[D - (D >> (LQ + 1))] = (uint8_t)c2;
+  // unit vector of the grid angles, top-down
+  const double* top = pt.cs64 + 2 * ((LQ + 1) * 16 + c2);
+  const double* mid = pt.cs64 + 2 * (LQ * 16 + c1);
+  double u[Q];
+  u[0] = ((g & 2) ? top[1] : top[0]) * ((g & 1) ? mid[1] : mid[0]);
+#pragma unroll
+  for (int l = LQ, cnt = 1; l >= 1; --l) {
+    const int off = Q - (Q >> (l - 1));
+#pragma unroll
+    for (int i = cnt - 1; i >= 0; --i) {
+      const double* cs = pt.cs64 + 2 * ((l - 1) * 16 + cd[off + i]);
+      const double ui = u[i];
+      u[2 * i + 1] = ui * cs[1];
+      u[2 * i] = ui * cs[0];
+    }
+    cnt *= 2;
+  }
+#pragma unroll
+  for (int i = 0; i < Q; ++i) x[i / 4][i % 4] = x[i / 4][i % 4] - r32 * u[i];
+}
+
+// Packs one token's polar code bytes into the key field: the level-1 stream (b1 bits per code)
+// then levels 2..L (bh bits, zero-padded to whole 32-bit words).  `part` of 4 lanes per token.
+__device__ __forceinline__ void polar_pack(const uint8_t* codes, int d, int b1, int bh, int l1_bytes,
+                                           int kbytes, uint8_t* rec, int part) {
+  const int nw1 = l1_bytes / 4, nw = kbytes / 4, n_up = d / 2 - 1;
+  for (int w = part; w < nw; w += 4) {
+    const bool lvl1 = w < nw1;
+    const int bits = lvl1 ? b1 : bh, per = 32 / bits;
+    const int first = (lvl1 ? w : w - nw1) * per;
+    uint32_t word = 0;
+    for (int i = 0; i < per; ++i) {
+      const int idx = first + i;
+      if (lvl1 || idx < n_up) word |= (uint32_t)codes[(lvl1 ? 0 : d / 2) + idx] << (bits * i);
+    }
+    reinterpret_cast<uint32_t*>(rec)[w] = word;
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void compress_kernel(CompressArgs A) {
   constexpr int Q = D / 4, CT = D / 16;
@@ -279,6 +372,7 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs A) {
   float* lds_s = lds_pi + D * D;
   float* lds_tab = lds_s + (A.s_in_lds ? c.m * D : 0);   // 4 x 16 floats
   uint8_t* stage_all = reinterpret_cast<uint8_t*>(lds_tab + 4 * kMaxLevels);
+  uint8_t* codes_all = stage_all + (size_t)(blockDim.x >> 6) * 16 * c.rec_bytes;   // polar: [wave][16][D]
 
   // constants to LDS
   {
@@ -330,7 +424,11 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs A) {
     rotate_tile<D>(lds_pi, in, lane, x);
     const double zs = r > 0.0 ? c.sqrt_d / r : 0.0;
     const double a = (double)r32 / c.sqrt_d;
-    quantize_rotated<D>(x, zs, a, lds_tab, lds_tab + kMaxLevels, c.kb, rec, g, true);
+    uint8_t* pcodes = codes_all + ((size_t)wave * 16 + tok) * D;
+    if (c.polar)
+      polar_encode<D>(x, (double)r32, A.polar, c.pb1, c.pbh, pcodes, g);
+    else
+      quantize_rotated<D>(x, zs, a, lds_tab, lds_tab + kMaxLevels, c.kb, rec, g, true);
     double e2 = 0.0;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
@@ -387,6 +485,10 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs A) {
     } else if (g == 1) {
       for (int i = c.norm_off + 12; i < c.rec_bytes; ++i) rec[i] = 0;
     }
+    if (c.polar) {
+      wave_lds_sync();
+      polar_pack(pcodes, D, c.pb1, c.pbh, c.l1_bytes, c.kbytes, rec, g);
+    }
     wave_lds_sync();
     // copy the staged records (16 consecutive slots of one (b, h)) to global memory
     const int64_t nvalid = min((int64_t)16, A.n_tokens - t0);
@@ -420,8 +522,10 @@ hipError_t launch_compress(const Consts& c, const DevConsts& dc, const void* k, 
   A.first_slot = first_slot;
   A.tiles_per_bh = (n_tokens + 15) / 16;
   A.n_tiles = A.tiles_per_bh * batch * heads;
+  A.polar = dc.polar;
   const int threads = 256, nwaves = threads / 64;
-  const size_t base = (size_t)c.d * c.d * 4 + 4 * kMaxLevels * 4 + (size_t)nwaves * 16 * c.rec_bytes;
+  const size_t base = (size_t)c.d * c.d * 4 + 4 * kMaxLevels * 4 + (size_t)nwaves * 16 * c.rec_bytes +
+                      (c.polar ? (size_t)nwaves * 16 * c.d : 0);
   const size_t with_s = base + (size_t)c.m * c.d * 4;
   A.s_in_lds = with_s <= 160 * 1024 ? 1 : 0;
   const size_t lds = A.s_in_lds ? with_s : base;
@@ -541,6 +645,9 @@ struct DecodeArgs {
   float scale, inv_sqrt_d, qjl_coef, key_fix;
   float key_levels[kMaxLevels];
   float val_levels[kMaxLevels];
+  // polar key codes
+  const float* pcs;       // cos / sin of the float32 angle grids, [8][16][2]
+  int pb1, pbh, plevels, l1_bytes;
 };
 
 template <int NW>
@@ -551,19 +658,22 @@ __device__ __forceinline__ uint32_t field(const uint32_t (&w)[NW], int pos, int 
   return v & ((1u << nbits) - 1u);
 }
 
-template <int HPL, int BK, int BV>
+template <int HPL, int BK, int BV, bool POLAR = false>
 __global__ __launch_bounds__(kDecodeThreads) void decode_scan_kernel(DecodeArgs A) {
-  constexpr bool kPairs = BK <= 3;
+  constexpr bool kPairs = BK <= 3 && !POLAR;
   constexpr int kEnt = kPairs ? (1 << (2 * BK)) : (1 << BK);   // entries per key table
   extern __shared__ __attribute__((aligned(16))) float lds[];
   const int d = A.d, G = A.G, NHG = G / HPL, LPTc = d / 32, LPT = LPTc * NHG, TPW = 64 / LPT;
   const int b = blockIdx.z, hkv = blockIdx.y, chunk = blockIdx.x;
-  const int nkt = kPairs ? d / 2 : d;                          // key tables per head group
+  // polar: one table per level-1 pair, 16 entries (q_2p cos + q_2p+1 sin of each grid angle),
+  // then the cos / sin of the grids of levels 2..L
+  const int nkt = (kPairs || POLAR) ? d / 2 : d;               // key tables per head group
   const int sgrp = A.sign_bytes ? A.m / 8 : A.m / 4;            // sign tables per head group
   const int sent = A.sign_bytes ? 256 : 16;
   float* lut_k = lds;                                           // [NHG][nkt][kEnt][HPL]
   float* lut_s = lut_k + NHG * nkt * kEnt * HPL;                // [NHG][sgrp][sent][HPL]
   float* gam_v = lut_s + NHG * sgrp * sent * HPL;               // [16]
+  float* pcs_up = gam_v + kMaxLevels;                            // polar: [L-1][16][2]
 
   const int64_t qrow0 = ((int64_t)b * A.q_heads + (int64_t)hkv * G);  // first query head row
   if (A.gate) {            // no head of the group reads the cold tokens: the merge ignores them
@@ -580,7 +690,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_scan_kernel(DecodeArgs 
       const int j = r % HPL, tbl = (r / HPL) % nkt, hg = r / HPL / nkt;
       const float* qh = qx + (int64_t)(hg * HPL + j) * d;
       float* dst = lut_k + (int64_t)(hg * nkt + tbl) * kEnt * HPL + j;
-      if (kPairs) {
+      if (POLAR) {
+        const float q0 = qh[2 * tbl], q1 = qh[2 * tbl + 1];
+#pragma unroll
+        for (int ent = 0; ent < kEnt; ++ent)
+          dst[ent * HPL] = fmaf(q1, A.pcs[2 * ent + 1], q0 * A.pcs[2 * ent]);
+      } else if (kPairs) {
         // pair p of a 32-coordinate group: 2-bit codes (2p, 2p+1), adjacent in the bitstream;
         // 3-bit codes (8 (p / 4) + p % 4, that + 4), one 6-bit byte field of the group layout
         const int pp = tbl & 15, g32 = 32 * (tbl >> 4);
@@ -624,11 +739,28 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_scan_kernel(DecodeArgs 
       }
     }
     if (threadIdx.x < kMaxLevels) gam_v[threadIdx.x] = A.val_levels[threadIdx.x];
+    if (POLAR)
+      for (int i = threadIdx.x; i < (A.plevels - 1) * 32; i += blockDim.x) pcs_up[i] = A.pcs[32 + i];
   }
   __syncthreads();
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   const int lt = lane % LPT, cq = lt % LPTc, hg = lt / LPTc, slot = lane / LPT;
+  // polar: this lane's 32 coordinates are the subtree of level-5 node cq.  Byte offset of the
+  // 32-bit word holding each level's codes for it (levels 2..5: 32 >> l consecutive codes;
+  // levels 6..L: the one ancestor), and the bit shift of the first code in that word.
+  int pw[kMaxPolarLevels], psh[kMaxPolarLevels];
+  if (POLAR) {
+#pragma unroll
+    for (int l = 2; l < kMaxPolarLevels + 1; ++l) {
+      if (l > A.plevels) break;
+      const int lev_off = (d / 2 - (d >> (l - 1))) * A.pbh;                  // level start (bits)
+      const int node = l <= 5 ? cq * (32 >> l) : cq >> (l - 5);
+      const int bit = lev_off + node * A.pbh;
+      pw[l - 2] = A.l1_bytes + 4 * (bit >> 5);
+      psh[l - 2] = bit & 31;
+    }
+  }
   const bool gather = A.sel_idx != nullptr;
   int n = gather ? A.k_sel : min((int64_t)A.seq_lens[b], A.capacity);
   const int c0 = chunk * A.chunk, c1 = min(n, c0 + A.chunk);
@@ -655,7 +787,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_scan_kernel(DecodeArgs 
     const uint8_t* rec = recs + (valid ? t : 0) * A.rec_bytes;
     uint32_t kw[BK], vw[BV];
 #pragma unroll
-    for (int i = 0; i < BK; ++i) kw[i] = valid ? reinterpret_cast<const uint32_t*>(rec + cq * 4 * BK)[i] : 0u;
+    for (int i = 0; i < BK; ++i)
+      kw[i] = (valid && !POLAR) ? reinterpret_cast<const uint32_t*>(rec + cq * 4 * BK)[i] : 0u;
 #pragma unroll
     for (int i = 0; i < BV; ++i)
       vw[i] = valid ? reinterpret_cast<const uint32_t*>(rec + A.kbytes + A.sbytes + cq * 4 * BV)[i] : 0u;
@@ -666,7 +799,65 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_scan_kernel(DecodeArgs 
     float cs[HPL];
 #pragma unroll
     for (int j = 0; j < HPL; ++j) cs[j] = 0.0f;
-    if (kPairs) {
+    if (POLAR) {
+      // level-1 codes: 16 codes of b1 bits from byte 2 b1 cq
+      const int b1 = A.pb1, bh = A.pbh;
+      const uint32_t* l1w = reinterpret_cast<const uint32_t*>(rec + 2 * b1 * cq);
+      const uint32_t w0 = valid ? l1w[0] : 0u;
+      const uint32_t w1 = (valid && b1 == 4) ? l1w[1] : 0u;
+      uint32_t uw[kMaxPolarLevels];
+#pragma unroll
+      for (int l = 2; l <= kMaxPolarLevels; ++l)
+        uw[l - 2] = (valid && l <= A.plevels) ? *reinterpret_cast<const uint32_t*>(rec + pw[l - 2]) >> psh[l - 2] : 0u;
+      // scale of the lane's subtree root: cos or sin of each ancestor's angle
+      float sroot = 1.0f;
+#pragma unroll
+      for (int l = 6; l <= kMaxPolarLevels; ++l) {
+        if (l <= A.plevels) {
+          const uint32_t c = uw[l - 2] & ((1u << bh) - 1u);
+          const float2 t = reinterpret_cast<const float2*>(pcs_up)[(l - 2) * 16 + c];
+          sroot *= ((cq >> (l - 6)) & 1) ? t.y : t.x;
+        }
+      }
+      // levels 5..3 inside the lane: scales of the 8 level-2 nodes
+      float sc[8];
+      sc[0] = sroot;
+#pragma unroll
+      for (int l = 5, cnt = 1; l >= 3; --l, cnt *= 2) {
+#pragma unroll
+        for (int i = cnt - 1; i >= 0; --i) {
+          const uint32_t c = (uw[l - 2] >> (bh * i)) & ((1u << bh) - 1u);
+          const float2 t = reinterpret_cast<const float2*>(pcs_up)[(l - 2) * 16 + c];
+          const float si = sc[i];
+          sc[2 * i + 1] = si * t.y;
+          sc[2 * i] = si * t.x;
+        }
+      }
+      // level 2 (angle psi) over level-1 pairs (2k, 2k+1): sum_j q.(s cos psi T1[2k] + s sin psi T1[2k+1])
+      const float* lkp = lut_k + (hg * nkt + 16 * cq) * kEnt * HPL;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t c2 = (uw[0] >> (bh * k)) & ((1u << bh) - 1u);
+        const float2 t = reinterpret_cast<const float2*>(pcs_up)[c2];
+        const float a = sc[k] * t.x, bb = sc[k] * t.y;
+        const int ia = 2 * k, ib = 2 * k + 1;
+        const uint32_t ca = ((b1 == 4 && ia >= 8) ? w1 : w0) >> ((b1 * ia) & 31) & ((1u << b1) - 1u);
+        const uint32_t cb = ((b1 == 4 && ib >= 8) ? w1 : w0) >> ((b1 * ib) & 31) & ((1u << b1) - 1u);
+        const float* ea = lkp + (ia * kEnt + ca) * HPL;
+        const float* eb = lkp + (ib * kEnt + cb) * HPL;
+        if (HPL == 4) {
+          const float4 va = *reinterpret_cast<const float4*>(ea);
+          const float4 vb = *reinterpret_cast<const float4*>(eb);
+          cs[0] = fmaf(bb, vb.x, fmaf(a, va.x, cs[0]));
+          cs[HPL > 1 ? 1 : 0] = fmaf(bb, vb.y, fmaf(a, va.y, cs[HPL > 1 ? 1 : 0]));
+          cs[HPL > 2 ? 2 : 0] = fmaf(bb, vb.z, fmaf(a, va.z, cs[HPL > 2 ? 2 : 0]));
+          cs[HPL > 3 ? 3 : 0] = fmaf(bb, vb.w, fmaf(a, va.w, cs[HPL > 3 ? 3 : 0]));
+        } else {
+#pragma unroll
+          for (int j = 0; j < HPL; ++j) cs[j] = fmaf(bb, eb[j], fmaf(a, ea[j], cs[j]));
+        }
+      }
+    } else if (kPairs) {
       const uint32_t top = BK == 3 ? group3_top(kw[0], kw[BK > 1 ? 1 : 0], kw[BK > 2 ? 2 : 0]) : 0u;
 #pragma unroll
       for (int p = 0; p < 16; ++p) {
@@ -720,7 +911,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_scan_kernel(DecodeArgs 
       }
     }
     float logit[HPL];
-    const float ak = rk * A.inv_sqrt_d, aq = A.qjl_coef * rho;
+    const float ak = POLAR ? rk : rk * A.inv_sqrt_d, aq = A.qjl_coef * rho;
 #pragma unroll
     for (int j = 0; j < HPL; ++j) {
       float sj = fmaf(aq, qsum[j], ak * cs[j]);
@@ -1808,7 +1999,7 @@ static bool mfma_path(const Consts& c, int G) {
 bool plan_decode(const Consts& c, int batch, int q_heads, int kv_heads, int64_t n_max,
                  DecodePlan* plan) {
   const int G = q_heads / kv_heads;
-  plan->mfma = mfma_path(c, G);
+  plan->mfma = !c.polar && mfma_path(c, G);
   const int hpl = (G % 4 == 0) ? 4 : 1;
   const int lpt = (c.d / 32) * (G / hpl);
   if (lpt > 64 || (lpt & (lpt - 1)) != 0) return false;
@@ -1818,7 +2009,7 @@ bool plan_decode(const Consts& c, int batch, int q_heads, int kv_heads, int64_t 
   // short caches off the matrix-core path with 4+ query heads per KV head (whose per-query
   // tables cost the most to build): the direct kernel, chunks of 8 .. 64 tokens aiming at ~2
   // workgroups per CU
-  plan->small = !plan->mfma && n_max <= kSmallMaxN && G >= 4 && G <= kSmallMaxG && c.m <= kSmallMaxM &&
+  plan->small = !c.polar && !plan->mfma && n_max <= kSmallMaxN && G >= 4 && G <= kSmallMaxG && c.m <= kSmallMaxM &&
                 c.m % 32 == 0 &&
                 (c.d == 64 || c.d == 128);
   // split-K: aim at ~2 blocks per CU (3 on the matrix-core path, whose 256-thread blocks fit
@@ -1835,7 +2026,8 @@ bool plan_decode(const Consts& c, int batch, int q_heads, int kv_heads, int64_t 
     while (chunk < want && chunk < kSmallMaxTok) chunk *= 2;
   }
   plan->chunk = (int)chunk;
-  const size_t key_tab = (size_t)G * (plan->key_pairs ? (c.d / 2) * (1 << (2 * c.kb)) : c.d * (1 << c.kb));
+  const size_t key_tab = c.polar ? (size_t)G * (c.d / 2) * 16 + (size_t)(c.plevels - 1) * 32
+                                 : (size_t)G * (plan->key_pairs ? (c.d / 2) * (1 << (2 * c.kb)) : c.d * (1 << c.kb));
   const size_t sign_bytes_tab = (size_t)G * (c.m / 8) * 256;
   const size_t sign_nib_tab = (size_t)G * (c.m / 4) * 16;
   const size_t budget = 150 * 1024 / 4;
@@ -1892,7 +2084,19 @@ static void launch_mfma_scan(const DecodeArgs& a, int kb, bool qjl, bool gather,
 }
 
 template <int HPL>
-static void launch_scan_hpl(const DecodeArgs& a, int kb, int vb, dim3 grid, size_t lds, hipStream_t st) {
+static void launch_scan_hpl(const DecodeArgs& a, int kb, int vb, bool polar, dim3 grid, size_t lds,
+                            hipStream_t st) {
+  if (polar) {
+#define TQ_DECP(BV_)                                                                             \
+    if (vb == BV_) {                                                                             \
+      allow_lds(decode_scan_kernel<HPL, 4, BV_, true>, lds);                                      \
+      hipLaunchKernelGGL((decode_scan_kernel<HPL, 4, BV_, true>), grid, dim3(kDecodeThreads), lds, st, a); \
+      return;                                                                                    \
+    }
+    TQ_DECP(2) TQ_DECP(3) TQ_DECP(4)
+#undef TQ_DECP
+    return;
+  }
 #define TQ_DEC(BK_, BV_)                                                                         \
   if (kb == BK_ && vb == BV_) {                                                                  \
     allow_lds(decode_scan_kernel<HPL, BK_, BV_>, lds);                                            \
@@ -1963,6 +2167,11 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
     a.key_levels[i] = c.key_levels[i];
     a.val_levels[i] = c.val_levels[i];
   }
+  a.pcs = dc.polar.cs32;
+  a.pb1 = c.pb1;
+  a.pbh = c.pbh;
+  a.plevels = c.plevels;
+  a.l1_bytes = c.l1_bytes;
   dim3 grid(plan.n_chunks, kv_heads, batch);
   ev.before(stream);
   if (mfma) {
@@ -1971,9 +2180,9 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
     if (c.d == 128) launch_small_d<128>(a, c.kb, c.vb, grid, stream);
     else launch_small_d<64>(a, c.kb, c.vb, grid, stream);
   } else if (plan.hpl == 4) {
-    launch_scan_hpl<4>(a, c.kb, c.vb, grid, plan.lds_bytes, stream);
+    launch_scan_hpl<4>(a, c.kb, c.vb, c.polar != 0, grid, plan.lds_bytes, stream);
   } else {
-    launch_scan_hpl<1>(a, c.kb, c.vb, grid, plan.lds_bytes, stream);
+    launch_scan_hpl<1>(a, c.kb, c.vb, c.polar != 0, grid, plan.lds_bytes, stream);
   }
   ev.after(stream);
   MergeArgs mg;

@@ -20,6 +20,9 @@ Shapes and value distributions follow the workloads the pages describe:
   Self-Indexing pages report (no dataset or weights are used).
 * ``sparse_128k_top2048`` - 8 KV heads (= 8 query heads), head_dim 128, batch 4,
   131,072 tokens, top-2048 selection; bf16 N(0, 1) K, V and queries.
+* ``llama8b_decode_32k_polar`` - the llama8b_decode_32k shapes and distributions with
+  polar key codes (4-bit level-1 angles, 2-bit higher angles: 48 key bytes, as 3-bit
+  scalar codes) - the PolarQuant variant of stage 1 on the TurboQuant page.
 * ``bulk_64k_scan`` - 65,536 tokens x 8 KV heads x head_dim 128 in bf16, N(0, 1)
   except 10 seeded (head, channel) pairs whose entries are 20 * t4; 256 bf16
   N(0, 1) queries per KV head score the whole compressed cache.  It stands in
@@ -54,6 +57,7 @@ class Workload:
     top_k: int = 0        # > 0: sparse decode over the top-k tokens
     scan_queries: int = 0  # > 0: bulk scan with this many queries per KV head
     seed: int = 0
+    polar_upper_bits: int = 0  # > 0: polar key codes (key_bits = level-1 angle bits)
 
     @property
     def group(self) -> int:
@@ -71,6 +75,8 @@ WORKLOADS = {
                                     "bf16", "bf16", top_k=2048, seed=404),
     "bulk_64k_scan": Workload("bulk_64k_scan", 1, 8, 8, 128, 65536, 0, 3, 128, 4,
                               "bf16", "bf16", scan_queries=256, seed=505),
+    "llama8b_decode_32k_polar": Workload("llama8b_decode_32k_polar", 16, 32, 8, 128, 32768, 0, 4, 128, 4,
+                                         "bf16", "bf16", seed=606, polar_upper_bits=2),
 }
 
 

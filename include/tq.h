@@ -31,6 +31,10 @@
  *    tq_*_workspace_size() bytes of device memory, 256-byte aligned.
  *  - A handle is immutable after tq_create, so concurrent calls on different streams
  *    are allowed.  Calls that share a workspace or output buffer must be ordered.
+ *  - A TQ_KEY_POLAR handle is accepted by tq_compress_kv, tq_decode_workspace_size,
+ *    tq_decode_attention, tq_record_bytes and the sign-index / top-k calls (which read
+ *    raw keys); tq_debug_quantize, tq_score_scan, tq_sparse_attention and the hot/cold
+ *    step return TQ_ERR_UNSUPPORTED for it.
  *  - Inputs must be finite.  Non-finite inputs give unspecified codes and outputs but
  *    never an out-of-bounds access.
  *
@@ -39,6 +43,10 @@
  *    [ QJL signs  : qjl_dim / 8 bytes  (bit j = 1 iff (S e)_j >= 0)     ]
  *    [ value codes: head_dim * value_bits / 8 bytes                    ]
  *    [ r_k float32 | rho float32 | r_v float32 ] [ zero pad to 16 B ]
+ *  Polar key codes (TQ_KEY_POLAR) replace the key code field by
+ *    [ level-1 angle codes: (head_dim/2) * key_bits / 8 bytes ]
+ *    [ codes of levels 2..L, level 2 first, node order: 4 * ceil((head_dim/2 - 1) *
+ *      polar_upper_bits / 32) bytes ]
  *  A code stream is a little-endian bitstream over 32-bit words: code i occupies stream
  *  bits [b*i, b*i + b) and may straddle two words.  A cache is an array
  *  records[batch][kv_heads][capacity][record_bytes].
@@ -70,13 +78,29 @@ typedef enum tq_status {
 
 typedef enum tq_dtype { TQ_F32 = 0, TQ_F16 = 1, TQ_BF16 = 2 } tq_dtype;
 
+/* Stage-1 key codec.  TQ_KEY_SCALAR: a Lloyd-Max code per rotated coordinate.
+ * TQ_KEY_POLAR: the PolarQuant variant (TurboQuant page, section "PolarQuant"): the rotated
+ * key y = Pi k is taken in coordinate pairs; each pair becomes a radius and an angle
+ * atan2(y_2i+1, y_2i) in (-pi, pi]; the radii are paired again (angle atan2(right, left)
+ * in [0, pi/2]) until one radius remains, so d = 2^L gives d - 1 angles on L levels.
+ * Level-1 angles are coded on a uniform grid of 2^key_bits cells from -pi (centres as
+ * reconstruction values); level l >= 2 angles on the Lloyd-Max grid (2^polar_upper_bits
+ * cells) of their exact law for a random direction, density proportional to
+ * sin(2 psi)^(2^(l-1) - 1) on [0, pi/2].  code = #{j : angle >= bound_j} with the angle
+ * in float64 and the float32 bounds; two zero inputs have angle 0.  The key is rebuilt as
+ * r_k * u, u the unit vector of the grid angles; QJL then sketches e = y - r_k u. */
+typedef enum tq_key_codec { TQ_KEY_SCALAR = 0, TQ_KEY_POLAR = 1 } tq_key_codec;
+
 typedef struct tq_config {
   int32_t head_dim;       /* d: 64 or 128                                              */
-  int32_t key_bits;       /* b_k: 1..4 bits per rotated key coordinate                 */
+  int32_t key_bits;       /* b_k: 2..4 bits per rotated key coordinate; polar: bits per
+                             level-1 angle, 2 or 4                                     */
   int32_t qjl_dim;        /* m: 0 (no QJL sketch) or a multiple of 32, at most 256     */
-  int32_t value_bits;     /* b_v: 1..4                                                 */
+  int32_t value_bits;     /* b_v: 2..4                                                 */
   uint64_t rotation_seed; /* seed of the Gaussian matrix whose QR factor is Pi         */
   uint64_t qjl_seed;      /* seed of the QJL projection S                              */
+  int32_t key_codec;      /* tq_key_codec (0 = scalar)                                 */
+  int32_t polar_upper_bits; /* polar: bits per angle above level 1: 1, 2 or 4; else 0  */
 } tq_config;
 
 typedef struct tq_handle tq_handle;
@@ -104,6 +128,14 @@ tq_status tq_destroy(tq_handle* h);
 tq_status tq_host_constants(const tq_config* cfg, float* pi, float* s, float* key_levels,
                             float* key_bounds, float* value_levels, float* value_bounds);
 
+/* Host-only: the polar angle grids tq_create would build for a TQ_KEY_POLAR config,
+ * written to HOST arrays levels[L][16] and bounds[L][16] (L = log2 head_dim; row l-1 is
+ * level l; entries past 2^bits levels / 2^bits - 1 bounds are left untouched).  Row 0 is
+ * the uniform grid of key_bits; rows 1.. the Lloyd-Max grids of polar_upper_bits, iterated
+ * in float64 (cell mass and first moment by composite Gauss-Legendre quadrature) until
+ * the levels move less than 1e-13, rounded to float32.  Needs no GPU. */
+tq_status tq_polar_host_constants(const tq_config* cfg, float* levels, float* bounds);
+
 /* Bytes of one cache record and of one sign-index record (host pointers). */
 tq_status tq_record_bytes(const tq_handle* h, size_t* record_bytes, size_t* index_record_bytes);
 
@@ -114,7 +146,8 @@ tq_status tq_record_bytes(const tq_handle* h, size_t* record_bytes, size_t* inde
  *  requires first_slot + n_tokens <= capacity.  Per token-head: r = |k|;
  *  x = Pi k, z = x * sqrt(d) / r (z = 0 when r = 0), code c_i = #{j : z_i >= tau_j}
  *  (float32 comparison); residual e = x - (r/sqrt(d)) gamma[c]; rho = |e|; QJL bit j =
- *  [(S e)_j >= 0].  Values: codes and r_v only.  The rotation and projection run as
+ *  [(S e)_j >= 0].  Polar keys: angles and codes as tq_key_codec states, e = x - r u.
+ *  Values: codes and r_v only.  The rotation and projection run as
  *  float64 matrix-core (MFMA) products, so codes equal a float64 reference except where
  *  a rotated coordinate lies within rounding of a boundary. */
 tq_status tq_compress_kv(const tq_handle* h, const void* k, const void* v, tq_dtype dt,
@@ -137,7 +170,8 @@ tq_status tq_debug_quantize(const tq_handle* h, const float* z_k, const float* p
  *  sel_idx[b][h][0..k_sel) that are >= 0 (device int32; -1 entries are skipped; each
  *  slot < capacity).  Cold logit = scale * s_t with
  *    s_t = (r_k/sqrt(d)) <Pi q, gamma_k[c_t]> + sqrt(pi/2)/m rho_t <S Pi q, 2 bit_t - 1>
- *  (the QJL estimator; the second term is absent when m = 0).
+ *  (the QJL estimator; the second term is absent when m = 0).  Polar keys: the first
+ *  term is r_k <Pi q, u_t>, u_t the unit vector of the token's grid angles.
  *  Exact segment (optional, hot_lens != NULL): hot_k/hot_v[b][h][hot_capacity][d] in
  *  hot_dt (each pointer aligned to 8 elements), tokens [0, hot_lens[b]);
  *  logit = scale * <q, k>; one softmax over cold+hot

@@ -18,6 +18,7 @@ import pytest
 import torch
 
 from compressed_key_attention_amd import workloads as W
+from oracle import polar as P
 from oracle import tq_oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -50,13 +51,15 @@ _CODECS = {}
 
 def _codec(h):
     key = (h.head_dim, h.key_bits, h.qjl_dim, h.value_bits, h.rotation_seed, h.qjl_seed)
-    if key not in _CODECS:
-        _CODECS[key] = O.Codec(*key)
-    return _CODECS[key]
+    ub = getattr(h, "polar_upper_bits", 0)
+    if (key, ub) not in _CODECS:
+        _CODECS[(key, ub)] = P.PolarCodec(*key, upper_bits=ub) if ub else O.Codec(*key)
+    return _CODECS[(key, ub)]
 
 
 def _handle(w: W.Workload):
-    return _tq().Handle(w.head_dim, w.key_bits, w.qjl_dim, w.value_bits, w.seed * 3 + 1, w.seed * 3 + 2)
+    return _tq().Handle(w.head_dim, w.key_bits, w.qjl_dim, w.value_bits, w.seed * 3 + 1, w.seed * 3 + 2,
+                        polar_upper_bits=w.polar_upper_bits)
 
 
 def check_compress(codec, K, V, rec_gpu):

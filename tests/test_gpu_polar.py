@@ -1,0 +1,157 @@
+"""GPU parity of the PolarQuant key codec (TurboQuant page, section "PolarQuant") against the
+oracle in oracle/polar.py, through the C ABI.
+
+* compress end to end: norms within 1e-6 relative; an angle code may differ only where the
+  oracle's float64 angle lies within 1e-9 of a float32 grid bound; value codes as for the
+  scalar codec; rho and the QJL bits recomputed from the GPU's own codes (a bit may differ
+  only where |p/rho| <= 1e-6);
+* decode on identical records: logits, outputs and lse within 1e-4 + 1e-3 |oracle|.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import test_gpu_parity as GP
+from compressed_key_attention_amd import workloads as W
+from oracle import polar as P
+from oracle import tq_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+BASE = W.WORKLOADS["llama8b_decode_32k_polar"]
+
+
+def _wl(d=128, b1=4, bh=2, m=128, vb=4, hq=32, hkv=8, tokens=700, batch=2, hot=0, kv="bf16", q="bf16",
+        seed=606):
+    return W.Workload("llama8b_decode_32k_polar", batch, hq, hkv, d, tokens, hot, b1, m, vb, kv, q,
+                      seed=seed, polar_upper_bits=bh)
+
+
+def check_polar_compress(codec, K, V, rec_gpu):
+    """End-to-end compress rule on one set of tokens: K, V [n, d] float, rec_gpu [n, R] u8."""
+    fg = codec.unpack(rec_gpu)
+    ref = codec.compress_fields(K, V)
+    for key in ("r_k", "r_v"):
+        assert np.allclose(fg[key], ref[key], rtol=1e-6, atol=0), key
+    assert np.all(rec_gpu[:, codec.kbytes + codec.sbytes + codec.vbytes + 12:] == 0)
+    y = K.astype(np.float64) @ codec.Pi64.T
+    _, angles = P.polar_transform(y)
+    exempt = 0
+    for l, (cg, cr) in enumerate(zip(fg["kc"], ref["kc"])):
+        mism = cg != cr
+        if mism.any():
+            dist = np.min(np.abs(angles[l][..., None] - codec.angle_bounds[l].astype(np.float64)), axis=-1)
+            assert np.all(dist[mism] <= 1e-9), f"level {l + 1}: angle code mismatch away from a bound"
+            exempt += int(mism.sum())
+    _, _, zv, _ = O._rotate_and_code(codec, V, codec.val_bounds)
+    mism = fg["vc"] != ref["vc"]
+    if mism.any():
+        dist = np.min(np.abs(zv[..., None].astype(np.float64) - codec.val_bounds.astype(np.float64)), axis=-1)
+        assert np.all(dist[mism] <= 1e-6), "value code mismatch away from a boundary"
+    # residual from the GPU's own codes
+    e = y - fg["r_k"].astype(np.float64)[:, None] * codec.unit_vector(fg["kc"])
+    rho = np.sqrt(np.sum(e * e, -1))
+    assert np.allclose(fg["rho"], rho.astype(np.float32), rtol=2e-6, atol=1e-30)
+    bits_mism = 0
+    if codec.qjl_dim:
+        p = e @ codec.S64.T
+        mism = (fg["bits"] == 1) != (p.astype(np.float32) >= 0)
+        if mism.any():
+            rel = np.abs(p) / np.maximum(rho, 1e-300)[:, None]
+            assert np.all(rel[mism] <= 1e-6), "QJL bit mismatch away from zero"
+        bits_mism = int(mism.sum())
+    print(f"[polar compress] exempt code mismatches {exempt}, bit mismatches {bits_mism}", flush=True)
+
+
+@pytest.mark.parametrize("d,b1,bh,m,vb,dt", [(128, 4, 2, 128, 4, "bf16"), (64, 2, 1, 64, 2, "f16"),
+                                             (128, 4, 4, 0, 3, "f32"), (64, 4, 2, 256, 4, "bf16"),
+                                             (128, 2, 1, 32, 2, "f32")])
+def test_polar_compress_end_to_end(d, b1, bh, m, vb, dt):
+    w = _wl(d, b1, bh, m, vb, hq=3, hkv=3, tokens=53, batch=2, kv=dt, q=dt)
+    print(f"[case] polar compress d={d} b1={b1} bh={bh} m={m} vb={vb} {dt}", flush=True)
+    h = GP._handle(w)
+    codec = GP._codec(h)
+    assert h.record_bytes == codec.record_bytes
+    K, V = W.make_kv(w, "cuda")
+    rec = GP._compress(w, h, K, V).cpu().numpy()
+    for b in range(w.batch):
+        for hh in range(w.kv_heads):
+            check_polar_compress(codec, GP._np(K[b, :, hh]), GP._np(V[b, :, hh]), rec[b, hh])
+
+
+def test_polar_compress_zero_keys():
+    w = _wl(tokens=20, batch=1, hq=2, hkv=2, kv="f32", q="f32")
+    h = GP._handle(w)
+    codec = GP._codec(h)
+    K, V = W.make_kv(w, "cuda")
+    K[:, 3:7] = 0.0
+    rec = GP._compress(w, h, K, V).cpu().numpy()
+    f = codec.unpack(rec[0, 0, 3:7])
+    assert np.all(f["kc"][0] == 8) and all(np.all(c == 0) for c in f["kc"][1:])
+    assert np.all(f["r_k"] == 0) and np.all(f["rho"] == 0) and np.all(f["bits"] == 1)
+    check_polar_compress(codec, GP._np(K[0, :, 1]), GP._np(V[0, :, 1]), rec[0, 1])
+
+
+def test_polar_decode_llama8b_shape_reduced_ragged():
+    print("[case] polar decode llama8b shape 3000 tokens", flush=True)
+    GP._decode_case(_wl(tokens=3000, batch=3), [3000, 1, 2049])
+
+
+@pytest.mark.parametrize("hq", [8, 16, 64])
+def test_polar_decode_group_sizes_and_empty_sequences(hq):
+    print(f"[case] polar decode hq={hq}", flush=True)
+    GP._decode_case(_wl(hq=hq, tokens=700, batch=2), [700, 0])
+
+
+@pytest.mark.parametrize("d,b1,bh,m,vb", [(64, 2, 1, 64, 2), (64, 4, 4, 0, 3), (128, 2, 4, 256, 3)])
+def test_polar_decode_widths_with_exact_segment(d, b1, bh, m, vb):
+    print(f"[case] polar decode d={d} b1={b1} bh={bh} m={m} vb={vb} + exact segment", flush=True)
+    w = _wl(d, b1, bh, m, vb, hq=32, hkv=4, tokens=1024, batch=1, hot=512, kv="f16", q="f16")
+    GP._decode_case(w, [1000], hot_lens=[300])
+
+
+def test_polar_decode_gather_mode():
+    print("[case] polar decode gather", flush=True)
+    w = _wl(tokens=900, batch=2)
+    g = torch.Generator().manual_seed(7)
+    sel = torch.randint(-1, 900, (2, w.kv_heads, 300), generator=g).to(torch.int32).cuda()
+    GP._decode_case(w, [900, 900], sel=sel)
+
+
+def test_polar_rejected_where_not_built():
+    tq = GP._tq()
+    h = GP._handle(_wl(tokens=16, batch=1))
+    with pytest.raises(tq.TqError) as e:
+        h.scan_workspace_size(1, 8, 16)
+    assert e.value.status == tq.TQ_ERR_UNSUPPORTED
+    with pytest.raises(tq.TqError) as e:
+        h.sparse_workspace_size(1, 8, 8, 4096)
+    assert e.value.status == tq.TQ_ERR_UNSUPPORTED
+
+
+def test_polar_llama8b_full_size_sampled():
+    """The benchmark's polar workload at full size: sampled compress checks and decode
+    outputs of sampled heads against the oracle."""
+    w = BASE
+    print("[case] polar llama8b full size", flush=True)
+    h = GP._handle(w)
+    codec = GP._codec(h)
+    K, V = W.make_kv(w, "cuda")
+    rec = GP._compress(w, h, K, V)
+    r = rec[[0, 15]][:, [0, 7]].cpu().numpy()
+    for bi, b in enumerate([0, 15]):
+        for hi, hh in enumerate([0, 7]):
+            toks = np.r_[0:64, 32700:32768]
+            check_polar_compress(codec, GP._np(K[b, toks, hh]), GP._np(V[b, toks, hh]), r[bi, hi, toks])
+    q = W.make_queries(w, "cuda")
+    sl = torch.full((w.batch,), w.tokens, dtype=torch.int32, device="cuda")
+    lse = torch.empty((w.batch, w.q_heads), device="cuda")
+    out = h.decode_attention(q, rec, sl, lse=lse)
+    torch.cuda.synchronize()
+    for b, hq in [(0, 0), (7, 13), (15, 31)]:
+        ref, ref_lse, _ = O.decode_attention(codec, GP._np(q[b:b + 1]), rec[b:b + 1].cpu().numpy(),
+                                             [w.tokens], heads=[hq])
+        GP._close(out[b, hq].cpu().numpy(), ref[0, hq], f"out[{b},{hq}]")
+        GP._close(lse[b, hq].item(), ref_lse[0, hq], f"lse[{b},{hq}]")
