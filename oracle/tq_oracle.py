@@ -186,7 +186,9 @@ class Codec:
     # record layout ---------------------------------------------------------------------
     @property
     def kbytes(self):
-        return self.head_dim * self.key_bits // 8
+        """Key code field: d * b_k / 8 bytes, padded to a multiple of 4 (every field starts on
+        a 32-bit word; no padding at head_dim 64 or 128)."""
+        return (self.head_dim * self.key_bits // 8 + 3) // 4 * 4
 
     @property
     def sbytes(self):
@@ -194,7 +196,7 @@ class Codec:
 
     @property
     def vbytes(self):
-        return self.head_dim * self.value_bits // 8
+        return (self.head_dim * self.value_bits // 8 + 3) // 4 * 4
 
     @property
     def record_bytes(self):
@@ -279,8 +281,8 @@ def _pack_stream(codes: np.ndarray, b: int) -> np.ndarray:
     24 + r (r = 0..7) occupies the 6-bit value T_k of byte lane k = r % 4 (bits [3*(r // 4), +3)),
     where bit t of T_k is bit 8k + 6 + (t % 2) of W_(t // 2).  (Four codes of one selector
     byte-lane pattern then come out of a word with one shift and one mask.)  A trailing
-    partial group - only fields shorter than a multiple of 32 codes, which no head_dim the
-    library builds has - is a plain bitstream as for the other widths.
+    partial group (head_dim 200: codes 192..199) is a plain bitstream as for the other widths,
+    starting right after the last whole group.
     """
     if codes.shape[-1] == 0:
         return np.zeros(codes.shape[:-1] + (0,), dtype=np.uint8)
@@ -352,14 +354,19 @@ def _unpack_stream(buf: np.ndarray, n: int, b: int) -> np.ndarray:
     return _unpack_plain(buf, n, b)
 
 
+def _pad_to(buf: np.ndarray, nbytes: int) -> np.ndarray:
+    return np.concatenate([buf, np.zeros(buf.shape[:-1] + (nbytes - buf.shape[-1],), np.uint8)], axis=-1)
+
+
 def pack_records(codec: Codec, f: dict) -> np.ndarray:
     """One contiguous record per token-head:
-    [key codes | QJL sign bits | value codes | r_k f32 | rho f32 | r_v f32 | zero pad to 16 B].
+    [key codes | QJL sign bits | value codes | r_k f32 | rho f32 | r_v f32 | zero pad to 16 B],
+    the code fields zero-padded to whole 32-bit words.
     """
     parts = [
-        _pack_stream(f["kc"], codec.key_bits),
+        _pad_to(_pack_stream(f["kc"], codec.key_bits), codec.kbytes),
         _pack_stream(f["bits"], 1),
-        _pack_stream(f["vc"], codec.value_bits),
+        _pad_to(_pack_stream(f["vc"], codec.value_bits), codec.vbytes),
         np.stack([f["r_k"], f["rho"], f["r_v"]], axis=-1).astype("<f4").view(np.uint8),
     ]
     rec = np.concatenate(parts, axis=-1)
@@ -502,6 +509,22 @@ def score_scan(codec: Codec, q, records, n_tokens: int):
                 qx, qs = prepare_query(codec, q[b, h, i])
                 out[b, h, i] = score_estimates(codec, qx, qs, f)
     return out
+
+
+def recall_1_at_k(approx: np.ndarray, exact: np.ndarray, ks) -> dict:
+    """1@k recall (TurboQuant page, "Leistung bei der Vektorsuche"): the fraction of queries
+    whose best database vector by exact inner product is among the k best by the approximate
+    scores.  approx, exact [n_queries, n].  Readings: the exact best is the lowest index
+    among the exact maxima; in the approximate ranking a tie goes to the lower index, so the
+    best's rank is #{j : a_j > a_best} + #{j < best : a_j = a_best}."""
+    approx = np.asarray(approx, np.float64)
+    exact = np.asarray(exact, np.float64)
+    nq, n = exact.shape
+    best = np.argmax(exact, axis=1)
+    a = approx[np.arange(nq), best][:, None]
+    idx = np.arange(n)[None, :]
+    rank = np.sum(approx > a, axis=1) + np.sum((approx == a) & (idx < best[:, None]), axis=1)
+    return {int(k): float(np.mean(rank < k)) for k in ks}
 
 
 # ----------------------------------------------------------------------------------------

@@ -419,3 +419,75 @@ def test_quantize_from_rotated_packs_given_fields():
     zv = ((v @ codec.Pi64.T) * (8.0 / rv)[:, None]).astype(np.float32)
     rec = O.quantize_from_rotated(codec, z, p, f["r_k"], f["rho"], zv, f["r_v"])
     assert np.array_equal(rec, O.pack_records(codec, f))
+
+
+# ---------------------------------------------------------------- vector search ------
+def test_recall_1_at_k_hand_example():
+    """Three queries over four vectors.  Query 0: exact best 2, approximate order 2 first
+    -> found at k = 1.  Query 1: exact best 0, approximate scores rank it third -> found
+    from k = 3.  Query 2: exact best 3 tied in the approximate scores with index 1, which
+    wins the tie -> rank 1, found from k = 2."""
+    exact = np.array([[0.1, 0.2, 0.9, 0.3], [0.8, 0.1, 0.2, 0.3], [0.0, 0.5, 0.2, 0.7]])
+    approx = np.array([[0.0, 0.1, 0.5, 0.2], [0.3, 0.1, 0.5, 0.4], [0.1, 0.6, 0.2, 0.6]])
+    r = O.recall_1_at_k(approx, exact, [1, 2, 3, 4])
+    assert r == {1: 1 / 3, 2: 2 / 3, 3: 1.0, 4: 1.0}
+
+
+def test_recall_equals_sort_based_definition_and_exact_scores_give_one():
+    rng = np.random.default_rng(4)
+    exact = rng.standard_normal((50, 300))
+    approx = exact + 0.3 * rng.standard_normal((50, 300))
+    ks = [1, 2, 5, 10, 50]
+    got = O.recall_1_at_k(approx, exact, ks)
+    order = np.argsort(-approx, axis=1, kind="stable")      # ties: lower index first
+    best = np.argmax(exact, axis=1)
+    for k in ks:
+        want = np.mean([best[i] in order[i, :k] for i in range(50)])
+        assert got[k] == pytest.approx(want, abs=0)
+    assert O.recall_1_at_k(exact, exact, [1])[1] == 1.0
+    assert all(got[a] <= got[b] for a, b in zip(ks, ks[1:]))
+
+
+@pytest.mark.parametrize("kb,vb,m", [(3, 2, 192), (2, 4, 0), (4, 3, 32)])
+def test_head_dim_200_layout(kb, vb, m):
+    """head_dim 200: code fields padded to whole words; a 3-bit field is 6 groups of 32
+    codes (72 bytes) plus the last 8 codes as a plain 24-bit stream; pack/unpack round trip."""
+    codec = O.Codec(200, kb, m, vb, 3, 4)
+    assert codec.kbytes == (200 * kb // 8 + 3) // 4 * 4 and codec.kbytes % 4 == 0
+    rng = np.random.default_rng(kb)
+    f = dict(kc=rng.integers(0, 1 << kb, (5, 200)), bits=rng.integers(0, 2, (5, m)),
+             vc=rng.integers(0, 1 << vb, (5, 200)), r_k=np.float32(rng.random(5)),
+             rho=np.float32(rng.random(5)), r_v=np.float32(rng.random(5)))
+    rec = O.pack_records(codec, f)
+    assert rec.shape == (5, codec.record_bytes) and codec.record_bytes % 16 == 0
+    g = O.unpack_records(codec, rec)
+    for key in ("kc", "bits", "vc", "r_k", "rho", "r_v"):
+        assert np.array_equal(g[key], f[key]), key
+    if kb == 3:
+        # tail: code 192 + i at bits 3 i of the little-endian 24-bit value after byte 72
+        tail = rec[:, 72].astype(np.int64) | rec[:, 73].astype(np.int64) << 8 | rec[:, 74].astype(np.int64) << 16
+        for i in range(8):
+            assert np.array_equal((tail >> (3 * i)) & 7, f["kc"][:, 192 + i])
+        assert np.all(rec[:, 75] == 0)
+
+
+def test_head_dim_200_compress_decodes_exactly_without_quantization_error_terms():
+    """With 4-bit codes and QJL (m = 224) at d = 200: the estimator equals
+    <q_x, xhat> + coef rho <q_s, signs> recomputed from first principles, and the
+    reconstruction error |x - xhat|^2 / |x|^2 sits near the 4-bit Lloyd-Max MSE / 1
+    (0.0095 per coordinate)."""
+    d = 200
+    codec = O.Codec(d, 4, 224, 4, 5, 6)
+    rng = np.random.default_rng(0)
+    k = rng.standard_normal((300, d))
+    f = O.compress(codec, k, k)
+    x = k @ codec.Pi64.T
+    xhat = (f["r_k"].astype(np.float64) / math.sqrt(d))[:, None] * codec.key_levels.astype(np.float64)[f["kc"]]
+    rel = np.mean(np.sum((x - xhat) ** 2, 1) / np.sum(x * x, 1))
+    lm, lb = O.lloyd_max(4)
+    assert abs(rel - O.quantizer_mse(lm, lb)) < 0.002
+    q = rng.standard_normal(d)
+    qx, qs = O.prepare_query(codec, q)
+    s = O.score_estimates(codec, qx, qs, f)
+    ref = xhat @ qx + math.sqrt(math.pi / 2) / 224 * f["rho"].astype(np.float64) * ((2.0 * f["bits"] - 1) @ qs)
+    assert np.allclose(s, ref, rtol=1e-12, atol=1e-12)
