@@ -217,7 +217,7 @@ class PolarCodec(O.Codec):
             O._pack_stream(codes[0], self.key_bits),
             upb,
             O._pack_stream(f["bits"], 1),
-            O._pack_stream(f["vc"], self.value_bits),
+            O._pad_to(O._pack_stream(f["vc"], self.value_bits), self.vbytes),
             np.stack([f["r_k"], f["rho"], f["r_v"]], axis=-1).astype("<f4").view(np.uint8),
         ]
         rec = np.concatenate(parts, axis=-1)
