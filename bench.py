@@ -505,9 +505,20 @@ def cpu_baseline_sparse(w, q, index, book, records, budget_s: float = 12.0):
 
 
 # ---------------------------------------------------------------------------------------------
+def recall_1_at_k(approx, exact, ks):
+    """Measurement only: share of queries whose exact best inner product is among the k best
+    approximate scores (ties to the lower index), for approx / exact [queries, vectors]."""
+    import numpy as np
+    best = np.argmax(exact, axis=1)
+    a = approx[np.arange(len(best)), best][:, None]
+    idx = np.arange(approx.shape[1])[None, :]
+    rank = np.sum(approx > a, axis=1) + np.sum((approx == a) & (idx < best[:, None]), axis=1)
+    return {str(k): float(np.mean(rank < k)) for k in ks}
+
+
 def run_bulk_scan(args, tq, W, ev):
     import torch
-    w = W.WORKLOADS["bulk_64k_scan"]
+    w = W.WORKLOADS[args.workload]
     dev = "cuda"
     h = tq.Handle(w.head_dim, w.key_bits, w.qjl_dim, w.value_bits, w.seed * 3 + 1, w.seed * 3 + 2,
                   polar_upper_bits=w.polar_upper_bits)
@@ -515,6 +526,7 @@ def run_bulk_scan(args, tq, W, ev):
     B, T, H, d = K.shape
     records = h.new_cache(B, H, T, dev)
     compress_ms = compress_once(ev, tq, h, K, V, records)
+    k_host = K[0, :, 0].double().cpu().numpy() if w.name == "vector_search_d200" else None
     del K, V
     q = W.make_queries(w, dev)                     # [B, H, n_queries, d]
     nq = w.scan_queries
@@ -530,7 +542,8 @@ def run_bulk_scan(args, tq, W, ev):
     key_bytes = d * w.key_bits // 8 + w.qjl_dim // 8 + 8      # codes + sketch + r_k, rho
     alg_bytes = B * H * T * key_bytes + B * H * nq * T * 4     # key records read + scores written
     line = base_line(args, w, ms_per_step, B * T)
-    line["metric"] = "compressed tokens scanned per second (256 queries per KV head) + % of HBM roofline"
+    line["metric"] = (f"compressed tokens scanned per second ({nq} queries per KV head) + % of "
+                      + ("HBM" if w.name == "bulk_64k_scan" else "fp32 vector ALU") + " roofline")
     line["config"].update({"scan_queries": nq})
     mfma = w.head_dim == 128 and w.key_bits in (2, 3) and w.qjl_dim in (0, 128)
     kname = "scan_mfma_kernel" if mfma else "scan_kernel"
@@ -543,7 +556,21 @@ def run_bulk_scan(args, tq, W, ev):
         extra = {"mfma_int8_executed_tops": tops, "mfma_int8_peak_tops": 5000.0,
                  "mfma_int8_frac": tops / 5000.0}
     line["roofline"] = roofline(kname, w.name, alg_bytes, scan_ms, extra, fl_ms, ceiling)
+    if not mfma:
+        # float32 contraction over d + m operands per (query, vector) pair on the vector ALUs
+        flops = 2.0 * (d + w.qjl_dim) * B * H * nq * T
+        tf = flops / (scan_ms * 1e-3) / 1e12
+        hbm = line["roofline"]
+        line["roofline"] = {"bound": "alu", "kernel": kname, "achieved": tf, "peak": 157.3, "unit": "TFLOP/s",
+                            "frac": tf / 157.3, "traffic": hbm["traffic"], "algorithmic_flops_per_launch": flops,
+                            "kernel_ms": scan_ms, "kernel_ms_median": hbm["kernel_ms_median"],
+                            "kernel_ms_min": hbm["kernel_ms_min"], "hbm_gbps": hbm["achieved"],
+                            "hbm_frac": hbm["frac"], "algorithmic_bytes_per_launch": alg_bytes}
     line["scores_per_s"] = B * H * nq * T / (ms_per_step * 1e-3)
+    if k_host is not None:
+        exact = q[0, 0].double().cpu().numpy() @ k_host.T
+        line["recall_1_at_k"] = recall_1_at_k(scores[0, 0].double().cpu().numpy(), exact,
+                                              [1, 2, 4, 8, 16, 32, 64])
     line["compress"] = {"ms": compress_ms, "token_heads_per_s": B * H * T / (compress_ms * 1e-3)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_scan(w, q, records)
@@ -556,7 +583,7 @@ def cpu_baseline_scan(w, q, records, budget_s: float = 12.0):
     codec_args = codec_args_of(w)
     qn = q.float().cpu().numpy()
     chunk = 4096
-    units = [(hh, t0) for hh in range(w.kv_heads) for t0 in range(0, w.tokens, chunk)]
+    units = [(hh, t0) for hh in range(w.kv_heads) for t0 in range(0, w.tokens - chunk + 1, chunk)]
 
     def make_job(u):
         hh, t0 = u
@@ -657,7 +684,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="llama8b_decode_32k",
-                    choices=DECODE_WORKLOADS + ["sparse_128k_top2048", "bulk_64k_scan", "monarch_tinyllama"])
+                    choices=DECODE_WORKLOADS + ["sparse_128k_top2048", "bulk_64k_scan", "monarch_tinyllama",
+                                                "vector_search_d200"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 device-to-device copies of 1 GiB (HBM counter calibration)")

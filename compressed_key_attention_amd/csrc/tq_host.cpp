@@ -327,8 +327,10 @@ tq_status check_config(const tq_config* cfg) {
     return fail(TQ_ERR_INVALID_ARGUMENT, "key_bits and value_bits must be in 1..4");
   if (cfg->qjl_dim % 32 != 0 || cfg->qjl_dim > 256)
     return fail(TQ_ERR_INVALID_ARGUMENT, "qjl_dim must be 0 or a multiple of 32 up to 256");
-  if (cfg->head_dim != 64 && cfg->head_dim != 128)
-    return fail(TQ_ERR_UNSUPPORTED, "head_dim %d not built (64 or 128)", cfg->head_dim);
+  if (cfg->head_dim % 8 != 0 || cfg->head_dim > 256)
+    return fail(TQ_ERR_UNSUPPORTED, "head_dim %d not built (a multiple of 8 up to 256)", cfg->head_dim);
+  if (cfg->key_codec == TQ_KEY_POLAR && cfg->head_dim != 64 && cfg->head_dim != 128)
+    return fail(TQ_ERR_UNSUPPORTED, "polar keys need head_dim 64 or 128");
   if (cfg->key_bits < 2 || cfg->value_bits < 2)
     return fail(TQ_ERR_UNSUPPORTED, "1-bit stage-1 codes are not built (key/value bits 2..4)");
   if (cfg->key_codec == TQ_KEY_SCALAR) {
@@ -351,7 +353,7 @@ void fill_consts(const tq_config* cfg, tq::Consts* c) {
   c->kb = cfg->key_bits;
   c->m = cfg->qjl_dim;
   c->vb = cfg->value_bits;
-  c->kbytes = c->d * c->kb / 8;
+  c->kbytes = (c->d * c->kb / 8 + 3) / 4 * 4;   // fields start on 32-bit words
   if (cfg->key_codec == TQ_KEY_POLAR) {
     c->polar = 1;
     c->pb1 = cfg->key_bits;
@@ -361,7 +363,7 @@ void fill_consts(const tq_config* cfg, tq::Consts* c) {
     c->kbytes = c->l1_bytes + 4 * (((c->d / 2 - 1) * c->pbh + 31) / 32);
   }
   c->sbytes = c->m / 8;
-  c->vbytes = c->d * c->vb / 8;
+  c->vbytes = (c->d * c->vb / 8 + 3) / 4 * 4;
   c->norm_off = c->kbytes + c->sbytes + c->vbytes;
   c->rec_bytes = (c->norm_off + 12 + 15) / 16 * 16;
   c->sqrt_d = std::sqrt((double)c->d);
@@ -421,6 +423,16 @@ struct tq_handle {
 
 namespace {
 
+// Calls built for head_dim 64 and 128 only (every other supported head_dim has compress and
+// the bulk scan).
+bool dim_unsupported(const tq_handle* h, const char* what, tq_status* st) {
+  if (h && h->c.d != 64 && h->c.d != 128) {
+    *st = fail(TQ_ERR_UNSUPPORTED, "%s is built for head_dim 64 and 128 only (handle has %d)", what, h->c.d);
+    return true;
+  }
+  return false;
+}
+
 // Calls built for the scalar key codec only.
 bool polar_unsupported(const tq_handle* h, const char* what, tq_status* st) {
   if (h && h->c.polar) {
@@ -447,6 +459,10 @@ tq_status tq_set_profile_events(hipEvent_t start, hipEvent_t stop) {
 tq_status tq_monarch_workspace_size(const tq_handle* h, int32_t batch, int32_t q_heads, int32_t kv_heads,
                                     int64_t hot_capacity, int64_t cold_capacity, size_t* bytes) {
   {
+    tq_status dst;
+    if (dim_unsupported(h, "the hot/cold step", &dst)) return dst;
+  }
+  {
     tq_status pst;
     if (polar_unsupported(h, "the hot/cold step", &pst)) return pst;
   }
@@ -464,6 +480,10 @@ tq_status tq_monarch_step(const tq_handle* h, const tq_monarch_config* cfg, cons
                           const void* q, tq_dtype q_dt, int32_t batch, int32_t q_heads, int32_t kv_heads,
                           const void* k_new, const void* v_new, float scale, float* out, float* lse,
                           int32_t* gate_out, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  {
+    tq_status dst;
+    if (dim_unsupported(h, "the hot/cold step", &dst)) return dst;
+  }
   {
     tq_status pst;
     if (polar_unsupported(h, "the hot/cold step", &pst)) return pst;
@@ -613,7 +633,10 @@ tq_status tq_create(const tq_config* cfg, tq_handle** out) {
   // polar tables: bounds f32 [8][16], cos/sin f64 [8][16][2], cos/sin f32 [8][16][2]
   constexpr size_t kPT = (size_t)tq::kMaxPolarLevels * 16;
   const size_t polar_bytes = h->c.polar ? kPT * 4 + kPT * 16 + kPT * 8 : 0;
-  const size_t main_bytes = (3 * n_pi + 3 * n_s) * sizeof(float);
+  std::vector<float> s_t(n_s);
+  for (int k = 0; k < m; ++k)
+    for (int i = 0; i < d; ++i) s_t[(size_t)i * m + k] = s[(size_t)k * d + i];
+  const size_t main_bytes = (3 * n_pi + 4 * n_s) * sizeof(float);
   const size_t total = main_bytes + polar_bytes;
   if (hipGetDevice(&h->device) != hipSuccess) { delete h; return fail(TQ_ERR_DEVICE, "no HIP device"); }
   if (hipMalloc(&h->dev_block, total) != hipSuccess) {
@@ -629,6 +652,7 @@ tq_status tq_create(const tq_config* cfg, tq_handle** out) {
   host.insert(host.end(), s_m.begin(), s_m.end());
   host.insert(host.end(), pi_t.begin(), pi_t.end());
   host.insert(host.end(), s_pi.begin(), s_pi.end());
+  host.insert(host.end(), s_t.begin(), s_t.end());
   std::vector<uint8_t> ptab(polar_bytes);
   if (h->c.polar) {
     float lv[tq::kMaxPolarLevels][16], bd[tq::kMaxPolarLevels][16];
@@ -660,6 +684,7 @@ tq_status tq_create(const tq_config* cfg, tq_handle** out) {
   h->dc.s_mfma = m ? base + 2 * n_pi + n_s : nullptr;
   h->dc.pi_t = base + 2 * n_pi + 2 * n_s;
   h->dc.s_pi = m ? base + 3 * n_pi + 2 * n_s : nullptr;
+  h->dc.s_t = m ? base + 3 * n_pi + 3 * n_s : nullptr;
   h->dc.polar = tq::PolarTables{nullptr, nullptr, nullptr};
   if (h->c.polar) {
     uint8_t* pt = reinterpret_cast<uint8_t*>(h->dev_block) + main_bytes;
@@ -729,6 +754,10 @@ tq_status tq_debug_quantize(const tq_handle* h, const float* z_k, const float* p
                             const float* r_k, const float* rho, const float* z_v,
                             const float* r_v, int64_t n, void* records, hipStream_t stream) {
   {
+    tq_status dst;
+    if (dim_unsupported(h, "the debug quantize entry", &dst)) return dst;
+  }
+  {
     tq_status pst;
     if (polar_unsupported(h, "the debug quantize entry", &pst)) return pst;
   }
@@ -745,6 +774,10 @@ tq_status tq_debug_quantize(const tq_handle* h, const float* z_k, const float* p
 tq_status tq_decode_workspace_size(const tq_handle* h, int32_t batch, int32_t q_heads,
                                    int32_t kv_heads, int64_t capacity, int32_t k_sel,
                                    size_t* bytes) {
+  {
+    tq_status dst;
+    if (dim_unsupported(h, "decode attention", &dst)) return dst;
+  }
   if (!h || !bytes) return fail(TQ_ERR_INVALID_ARGUMENT, "NULL handle or output");
   if (batch < 0 || q_heads <= 0 || kv_heads <= 0 || q_heads % kv_heads || capacity < 0 || k_sel < 0)
     return fail(TQ_ERR_INVALID_ARGUMENT, "bad decode shape");
@@ -762,6 +795,10 @@ tq_status tq_decode_attention(const tq_handle* h, const void* q, tq_dtype q_dt, 
                               int64_t hot_capacity, const int32_t* sel_idx, int32_t k_sel,
                               float scale, float* out, float* lse, float* logits,
                               void* workspace, size_t ws_bytes, hipStream_t stream) {
+  {
+    tq_status dst;
+    if (dim_unsupported(h, "decode attention", &dst)) return dst;
+  }
   if (!h) return fail(TQ_ERR_INVALID_ARGUMENT, "handle is NULL");
   size_t es;
   if (!elem_size(q_dt, &es)) return fail(TQ_ERR_INVALID_ARGUMENT, "unknown query dtype");
@@ -797,6 +834,10 @@ tq_status tq_decode_attention(const tq_handle* h, const void* q, tq_dtype q_dt, 
 
 tq_status tq_index_workspace_size(const tq_handle* h, int32_t batch, int32_t kv_heads,
                                   size_t* bytes) {
+  {
+    tq_status dst;
+    if (dim_unsupported(h, "the sign index", &dst)) return dst;
+  }
   if (!h || !bytes) return fail(TQ_ERR_INVALID_ARGUMENT, "NULL handle or output");
   if (batch < 0 || kv_heads <= 0) return fail(TQ_ERR_INVALID_ARGUMENT, "bad shape");
   // worst case over n_tokens: the plan caps the number of chunks
@@ -810,6 +851,10 @@ tq_status tq_build_sign_index(const tq_handle* h, const void* k, tq_dtype dt, in
                               float* codebook, float* mean, int64_t capacity,
                               int64_t first_slot, void* workspace, size_t ws_bytes,
                               hipStream_t stream) {
+  {
+    tq_status dst;
+    if (dim_unsupported(h, "the sign index", &dst)) return dst;
+  }
   if (!h) return fail(TQ_ERR_INVALID_ARGUMENT, "handle is NULL");
   tq_status st = check_kv_addressing(h, k, dt, batch, n_tokens, kv_heads, seq_stride, tok_stride,
                                      head_stride, capacity, first_slot);
@@ -827,6 +872,10 @@ tq_status tq_build_sign_index(const tq_handle* h, const void* k, tq_dtype dt, in
 
 tq_status tq_select_workspace_size(const tq_handle* h, int32_t batch, int32_t kv_heads,
                                    int64_t capacity, size_t* bytes) {
+  {
+    tq_status dst;
+    if (dim_unsupported(h, "top-k selection", &dst)) return dst;
+  }
   if (!h || !bytes) return fail(TQ_ERR_INVALID_ARGUMENT, "NULL handle or output");
   if (batch < 0 || kv_heads <= 0 || capacity < 0) return fail(TQ_ERR_INVALID_ARGUMENT, "bad shape");
   *bytes = tq::plan_select(h->c, batch, kv_heads, capacity).ws_total;
@@ -838,6 +887,10 @@ tq_status tq_select_topk(const tq_handle* h, const void* q, tq_dtype q_dt, int32
                          const float* codebook, int64_t capacity, const int32_t* seq_lens,
                          int32_t k, int32_t* out_idx, int32_t* out_count, int32_t* out_scores,
                          void* workspace, size_t ws_bytes, hipStream_t stream) {
+  {
+    tq_status dst;
+    if (dim_unsupported(h, "top-k selection", &dst)) return dst;
+  }
   if (!h) return fail(TQ_ERR_INVALID_ARGUMENT, "handle is NULL");
   size_t es;
   if (!elem_size(q_dt, &es)) return fail(TQ_ERR_INVALID_ARGUMENT, "unknown query dtype");
@@ -860,6 +913,10 @@ tq_status tq_select_topk(const tq_handle* h, const void* q, tq_dtype q_dt, int32
 tq_status tq_sparse_workspace_size(const tq_handle* h, int32_t batch, int32_t q_heads,
                                    int32_t kv_heads, int64_t capacity, size_t* bytes) {
   {
+    tq_status dst;
+    if (dim_unsupported(h, "sparse attention", &dst)) return dst;
+  }
+  {
     tq_status pst;
     if (polar_unsupported(h, "sparse attention", &pst)) return pst;
   }
@@ -877,6 +934,10 @@ tq_status tq_sparse_attention(const tq_handle* h, const void* q, tq_dtype q_dt, 
                               const void* hot_v, tq_dtype hot_dt, const int32_t* hot_lens,
                               int64_t hot_capacity, float scale, float* out, float* lse,
                               void* workspace, size_t ws_bytes, hipStream_t stream) {
+  {
+    tq_status dst;
+    if (dim_unsupported(h, "sparse attention", &dst)) return dst;
+  }
   {
     tq_status pst;
     if (polar_unsupported(h, "sparse attention", &pst)) return pst;
@@ -940,8 +1001,6 @@ tq_status tq_score_scan(const tq_handle* h, const void* q, tq_dtype q_dt, int32_
   if (batch < 0 || kv_heads <= 0 || n_queries < 0 || n_tokens < 0 || n_tokens > capacity)
     return fail(TQ_ERR_INVALID_ARGUMENT, "bad scan shape (n_tokens must be <= capacity)");
   if ((int64_t)batch * n_queries * n_tokens == 0) return ok();
-  if (2 * 64 * (h->c.d + h->c.m + 4) * 4 > 160 * 1024)
-    return fail(TQ_ERR_UNSUPPORTED, "scan tile does not fit in LDS for head_dim %d, qjl_dim %d", h->c.d, h->c.m);
   if (!q || !records || !scores) return fail(TQ_ERR_INVALID_ARGUMENT, "NULL input or output");
   if (!aligned(records, 16)) return fail(TQ_ERR_INVALID_ARGUMENT, "records not 16-byte aligned");
   tq::ScanPlan plan = tq::plan_scan(h->c, batch, kv_heads, n_queries);

@@ -62,6 +62,7 @@ struct DevConsts {
   const float* pi_t;      // Pi transposed, [d][d] row-major (row k = column k of Pi)
   const float* s_pi;      // S Pi ([m][d], float64 product rounded to float32): q_s = (S Pi) q
   const float* s;         // [m][d] row-major
+  const float* s_t;       // S transposed, [d][m] row-major
   const float* pi_mfma;   // Pi in the order the compress kernel's MFMA A operand reads it
   const float* s_mfma;    // S in the same order
   PolarTables polar;      // polar key codec only (null pointers otherwise)

@@ -194,6 +194,8 @@ struct CompressArgs {
   int64_t tiles_per_bh, n_tiles;
   int s_in_lds;
   PolarTables polar;
+  const float* pi_t;      // generic kernel: Pi transposed [d][d], S transposed [d][m]
+  const float* s_t;
 };
 
 template <int D>
@@ -500,6 +502,130 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs A) {
   }
 }
 
+// -----------------------------------------------------------------------------------------
+// Compression at a head_dim without a matrix-core layout (a multiple of 8 up to 256, e.g. 200):
+// one wave per token-head, lane i owns coordinates i, i + 64, ...; the rotation, residual and
+// QJL projection are float64 FMA loops over the transposed matrices (coalesced rows), with the
+// same decisions as the matrix-core kernel: z rounded to float32 against the float32 bounds,
+// bit = [(float)(S e) >= 0].  The record is assembled in LDS and copied out as words.
+// -----------------------------------------------------------------------------------------
+constexpr int kGenMaxD = 256;
+constexpr int kGenRecWords = 80;   // >= (256 * 4 / 8 + 256 / 8 + 256 * 4 / 8 + 12 rounded to 16) / 4
+
+// Code field from one code byte per coordinate: 3-bit groups of 32 codes (the v_perm layout),
+// a plain bitstream for the trailing partial group and for the other widths.  dst is zeroed.
+__device__ __forceinline__ void pack_code_field(const uint8_t* codes, int d, int bits, uint32_t* dst, int lane) {
+  if (bits == 3) {
+    const int ng = d / 32;
+    for (int g = lane; g < ng; g += 64) {
+      uint32_t w[3] = {0u, 0u, 0u};
+      for (int j = 0; j < 32; ++j) group3_put(w, j, codes[32 * g + j]);
+      dst[3 * g] = w[0];
+      dst[3 * g + 1] = w[1];
+      dst[3 * g + 2] = w[2];
+    }
+    if (lane == 0) {
+      for (int i = 32 * ng; i < d; ++i) {
+        const int pos = 96 * ng + 3 * (i - 32 * ng);
+        for (int t = 0; t < 3; ++t)
+          dst[(pos + t) >> 5] |= (((uint32_t)codes[i] >> t) & 1u) << ((pos + t) & 31);
+      }
+    }
+  } else {
+    const int per = 32 / bits, nw = (d * bits + 31) / 32;
+    for (int w = lane; w < nw; w += 64) {
+      uint32_t word = 0u;
+      for (int i = 0; i < per; ++i) {
+        const int idx = w * per + i;
+        if (idx < d) word |= (uint32_t)codes[idx] << (bits * i);
+      }
+      dst[w] = word;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void compress_generic_kernel(CompressArgs A) {
+  const Consts& c = A.c;
+  __shared__ double vin[4][kGenMaxD];
+  __shared__ uint8_t cb[4][kGenMaxD];
+  __shared__ uint32_t rw[4][kGenRecWords];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int d = c.d, m = c.m, nrw = c.rec_bytes / 4;
+  for (int64_t item = (int64_t)blockIdx.x * 4 + wave; item < A.n_tiles; item += (int64_t)gridDim.x * 4) {
+    const int64_t bh = item / A.n_tokens, t = item % A.n_tokens;
+    const int64_t b = bh / A.heads;
+    const int h = (int)(bh % A.heads);
+    const int64_t row = b * A.seq_stride + t * A.tok_stride + h * A.head_stride;
+    for (int w = lane; w < nrw; w += 64) rw[wave][w] = 0u;
+    float norms[3] = {0.0f, 0.0f, 0.0f};
+    for (int pass = 0; pass < 2; ++pass) {
+      const void* src = pass == 0 ? A.k : A.v;
+      for (int i = lane; i < d; i += 64) vin[wave][i] = (double)load_elem(src, A.dt, row + i);
+      wave_lds_sync();
+      double n2 = 0.0;
+      for (int i = lane; i < d; i += 64) n2 += vin[wave][i] * vin[wave][i];
+      for (int o = 32; o >= 1; o >>= 1) n2 += __shfl_xor(n2, o);
+      const double r = sqrt(n2);
+      const float r32 = (float)r;
+      const double zs = r > 0.0 ? c.sqrt_d / r : 0.0;
+      const double a = (double)r32 / c.sqrt_d;
+      const float* bounds = pass == 0 ? c.key_bounds : c.val_bounds;
+      const float* levels = pass == 0 ? c.key_levels : c.val_levels;
+      double e[kGenMaxD / 64];
+#pragma unroll
+      for (int j = 0; j < kGenMaxD / 64; ++j) {
+        const int i = lane + 64 * j;
+        e[j] = 0.0;
+        if (i < d) {
+          double x = 0.0;
+          for (int jj = 0; jj < d; ++jj) x = fma((double)A.pi_t[(size_t)jj * d + i], vin[wave][jj], x);
+          const uint32_t code = quantize_code((float)(x * zs), bounds);
+          cb[wave][i] = (uint8_t)code;
+          e[j] = x - a * (double)levels[code];
+        }
+      }
+      wave_lds_sync();   // every lane is done reading vin and has written its codes
+      const int fofs = pass == 0 ? 0 : (c.kbytes + c.sbytes) / 4;
+      pack_code_field(cb[wave], d, pass == 0 ? c.kb : c.vb, rw[wave] + fofs, lane);
+      norms[pass == 0 ? 0 : 2] = r32;
+      if (pass == 0) {
+        double e2 = 0.0;
+#pragma unroll
+        for (int j = 0; j < kGenMaxD / 64; ++j) {
+          const int i = lane + 64 * j;
+          if (i < d) {
+            vin[wave][i] = e[j];
+            e2 += e[j] * e[j];
+          }
+        }
+        for (int o = 32; o >= 1; o >>= 1) e2 += __shfl_xor(e2, o);
+        norms[1] = (float)sqrt(e2);
+        wave_lds_sync();
+        for (int k0 = 0; k0 < m; k0 += 64) {
+          const int k = k0 + lane;
+          bool bit = false;
+          if (k < m) {
+            double p = 0.0;
+            for (int i = 0; i < d; ++i) p = fma((double)A.s_t[(size_t)i * m + k], vin[wave][i], p);
+            bit = (float)p >= 0.0f;
+          }
+          const uint64_t bal = __ballot(bit);
+          if (lane == 0) {
+            rw[wave][c.kbytes / 4 + k0 / 32] = (uint32_t)bal;
+            if (k0 + 32 < m) rw[wave][c.kbytes / 4 + k0 / 32 + 1] = (uint32_t)(bal >> 32);
+          }
+        }
+      }
+      wave_lds_sync();   // vin is reloaded by the next pass
+    }
+    if (lane < 3) rw[wave][c.norm_off / 4 + lane] = __float_as_uint(norms[lane]);
+    wave_lds_sync();
+    uint32_t* dst = reinterpret_cast<uint32_t*>(A.records + (bh * A.capacity + A.first_slot + t) * c.rec_bytes);
+    for (int w = lane; w < nrw; w += 64) dst[w] = rw[wave][w];
+    wave_lds_sync();   // rw is cleared for the next item
+  }
+}
+
 hipError_t launch_compress(const Consts& c, const DevConsts& dc, const void* k, const void* v,
                            tq_dtype dt, int batch, int64_t n_tokens, int heads, int64_t seq_stride,
                            int64_t tok_stride, int64_t head_stride, void* records,
@@ -523,6 +649,17 @@ hipError_t launch_compress(const Consts& c, const DevConsts& dc, const void* k, 
   A.tiles_per_bh = (n_tokens + 15) / 16;
   A.n_tiles = A.tiles_per_bh * batch * heads;
   A.polar = dc.polar;
+  A.pi_t = dc.pi_t;
+  A.s_t = dc.s_t;
+  if (c.d != 64 && c.d != 128) {
+    A.n_tiles = (int64_t)batch * heads * n_tokens;     // one wave per token-head
+    const int64_t blocks = std::min<int64_t>((A.n_tiles + 3) / 4, (int64_t)num_cus() * 8);
+    ev.before(stream);
+    if (blocks > 0)
+      hipLaunchKernelGGL(compress_generic_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, A);
+    ev.after(stream);
+    return hipGetLastError();
+  }
   const int threads = 256, nwaves = threads / 64;
   const size_t base = (size_t)c.d * c.d * 4 + 4 * kMaxLevels * 4 + (size_t)nwaves * 16 * c.rec_bytes +
                       (c.polar ? (size_t)nwaves * 16 * c.d : 0);
@@ -3415,71 +3552,90 @@ struct ScanArgs {
   float key_levels[kMaxLevels];
 };
 
+// Generic bulk scan: 64 queries x 64 tokens per workgroup, the contraction (d key coordinates,
+// then m signs) in slabs of kScanSlab: each slab stages the queries' prepared operands and
+// the tokens' dequantized operands (r_k/sqrt(d) gamma[c], +-coef rho) in LDS, then a 4 x 4
+// register tile per thread accumulates in float32.
+constexpr int kScanSlab = 128;
+
+__device__ __forceinline__ uint32_t key_code_at(const uint32_t* kw, int i, int d, int kb) {
+  if (kb == 3) {
+    const int ng = d / 32;
+    if (i < 32 * ng) {
+      const uint32_t* gw = kw + 3 * (i >> 5);
+      return group3_code(gw[0], gw[1], gw[2], i & 31);
+    }
+    const int pos = 96 * ng + 3 * (i - 32 * ng), wi = pos >> 5, sh = pos & 31;
+    uint32_t v = kw[wi] >> sh;
+    if (sh + 3 > 32) v |= kw[wi + 1] << (32 - sh);
+    return v & 7u;
+  }
+  const int pos = i * kb, wi = pos >> 5, sh = pos & 31;   // 1-, 2-, 4-bit codes never straddle
+  return (kw[wi] >> sh) & ((1u << kb) - 1u);
+}
+
 __global__ __launch_bounds__(256) void scan_kernel(ScanArgs A) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
-  const int K = A.d + A.m, KP = K + 4;   // padded row
+  constexpr int KP = kScanSlab + 4;       // padded row
+  const int K = A.d + A.m;
   float* qt = lds;                        // [64][KP]
   float* kt = lds + kScanTile * KP;       // [64][KP]
   const int unit = blockIdx.z;
   const int64_t tok0 = (int64_t)blockIdx.x * kScanTile;
   const int q0 = blockIdx.y * kScanTile;
   const uint8_t* recs = A.records + (int64_t)unit * A.capacity * A.rec_bytes;
-  // stage queries
-  for (int e = threadIdx.x; e < kScanTile * K; e += blockDim.x) {
-    const int qi = e / K, kk = e % K;
-    qt[qi * KP + kk] = (q0 + qi < A.n_queries) ? A.qprep[((int64_t)unit * A.n_queries + q0 + qi) * K + kk] : 0.0f;
-  }
-  // dequantize records: 4 threads per token
-  {
-    const int tt = threadIdx.x / 4, part = threadIdx.x % 4;
-    const int64_t t = tok0 + tt;
-    const bool valid = t < A.n_tokens;
-    const uint8_t* rec = recs + (valid ? t : 0) * A.rec_bytes;
-    const float* nrm = reinterpret_cast<const float*>(rec + A.norm_off);
-    const float ak = valid ? nrm[0] * A.inv_sqrt_d : 0.0f;
-    const float aq = valid ? A.qjl_coef * nrm[1] : 0.0f;
-    const uint32_t* kw = reinterpret_cast<const uint32_t*>(rec);
-    for (int i = part; i < A.d; i += 4) {
-      uint32_t v;
-      if (A.kb == 3) {
-        const uint32_t* gw = kw + 3 * (i >> 5);
-        v = group3_code(gw[0], gw[1], gw[2], i & 31);
-      } else {
-        const int pos = i * A.kb, wi = pos >> 5, sh = pos & 31;
-        v = kw[wi] >> sh;
-        if (sh + A.kb > 32) v |= kw[wi + 1] << (32 - sh);
-        v &= (1u << A.kb) - 1u;
-      }
-      kt[tt * KP + i] = ak * A.key_levels[v];
-    }
-    const uint32_t* sw = reinterpret_cast<const uint32_t*>(rec + A.kbytes);
-    for (int j = part; j < A.m; j += 4) {
-      const uint32_t bit = (sw[j >> 5] >> (j & 31)) & 1u;
-      kt[tt * KP + A.d + j] = bit ? aq : -aq;
-    }
-  }
-  __syncthreads();
+  // this thread dequantizes every fourth operand of token tt
+  const int tt = threadIdx.x / 4, part = threadIdx.x % 4;
+  const int64_t t = tok0 + tt;
+  const bool valid = t < A.n_tokens;
+  const uint8_t* rec = recs + (valid ? t : 0) * A.rec_bytes;
+  const float* nrm = reinterpret_cast<const float*>(rec + A.norm_off);
+  const float ak = valid ? nrm[0] * A.inv_sqrt_d : 0.0f;
+  const float aq = valid ? A.qjl_coef * nrm[1] : 0.0f;
+  const uint32_t* kw = reinterpret_cast<const uint32_t*>(rec);
+  const uint32_t* sw = reinterpret_cast<const uint32_t*>(rec + A.kbytes);
   const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;   // tokens tx + 16 j, queries 4 ty + i
   float acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
-  for (int kk = 0; kk < K; kk += 4) {
-    float4 qa[4], ka[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) qa[i] = *reinterpret_cast<const float4*>(qt + (4 * ty + i) * KP + kk);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) ka[j] = *reinterpret_cast<const float4*>(kt + (tx + 16 * j) * KP + kk);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[i][j] = fmaf(qa[i].x, ka[j].x, acc[i][j]);
-        acc[i][j] = fmaf(qa[i].y, ka[j].y, acc[i][j]);
-        acc[i][j] = fmaf(qa[i].z, ka[j].z, acc[i][j]);
-        acc[i][j] = fmaf(qa[i].w, ka[j].w, acc[i][j]);
+  for (int k0 = 0; k0 < K; k0 += kScanSlab) {
+    const int kn = min(kScanSlab, K - k0);
+    __syncthreads();   // the previous slab has been consumed
+    for (int e = threadIdx.x; e < kScanTile * kScanSlab; e += blockDim.x) {
+      const int qi = e / kScanSlab, kk = e % kScanSlab;
+      qt[qi * KP + kk] = (kk < kn && q0 + qi < A.n_queries)
+                             ? A.qprep[((int64_t)unit * A.n_queries + q0 + qi) * K + k0 + kk] : 0.0f;
+    }
+    for (int kk = part; kk < kScanSlab; kk += 4) {
+      const int i = k0 + kk;
+      float val = 0.0f;
+      if (i < A.d) {
+        val = ak * A.key_levels[key_code_at(kw, i, A.d, A.kb)];
+      } else if (i < K) {
+        const int j = i - A.d;
+        val = ((sw[j >> 5] >> (j & 31)) & 1u) ? aq : -aq;
       }
+      kt[tt * KP + kk] = val;
+    }
+    __syncthreads();
+    for (int kk = 0; kk < kScanSlab; kk += 4) {
+      float4 qa[4], ka[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qa[i] = *reinterpret_cast<const float4*>(qt + (4 * ty + i) * KP + kk);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ka[j] = *reinterpret_cast<const float4*>(kt + (tx + 16 * j) * KP + kk);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[i][j] = fmaf(qa[i].x, ka[j].x, acc[i][j]);
+          acc[i][j] = fmaf(qa[i].y, ka[j].y, acc[i][j]);
+          acc[i][j] = fmaf(qa[i].z, ka[j].z, acc[i][j]);
+          acc[i][j] = fmaf(qa[i].w, ka[j].w, acc[i][j]);
+        }
+    }
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -3741,7 +3897,7 @@ hipError_t launch_scan(const Consts& c, const DevConsts& dc, const ScanPlan& pla
   a.inv_sqrt_d = c.inv_sqrt_d;
   a.qjl_coef = c.qjl_coef;
   for (int i = 0; i < kMaxLevels; ++i) a.key_levels[i] = c.key_levels[i];
-  const size_t lds = (size_t)2 * kScanTile * (c.d + c.m + 4) * 4;
+  const size_t lds = (size_t)2 * kScanTile * (kScanSlab + 4) * 4;
   dim3 grid((unsigned)((n_tokens + kScanTile - 1) / kScanTile), (unsigned)((n_queries + kScanTile - 1) / kScanTile),
             (unsigned)(batch * heads));
   allow_lds(scan_kernel, lds);

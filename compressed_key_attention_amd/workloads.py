@@ -23,6 +23,12 @@ Shapes and value distributions follow the workloads the pages describe:
 * ``llama8b_decode_32k_polar`` - the llama8b_decode_32k shapes and distributions with
   polar key codes (4-bit level-1 angles, 2-bit higher angles: 48 key bytes, as 3-bit
   scalar codes) - the PolarQuant variant of stage 1 on the TurboQuant page.
+* ``vector_search_d200`` - 100,000 database vectors and 1,000 queries of dimension 200
+  (the GloVe d=200 shape of the TurboQuant page's vector-search section; GloVe itself is not
+  used): every vector and query is mu + sigma * N(0, I) with seeded per-channel mean
+  mu_i ~ 0.3 N(0, 1) and scale sigma_i = exp(0.4 N(0, 1)), i.e. dense embeddings with a
+  shared offset and uneven channel energy.  2-bit codes plus a 192-bit QJL sketch (about 3
+  bits per coordinate); the bulk scan scores every query against every vector.
 * ``bulk_64k_scan`` - 65,536 tokens x 8 KV heads x head_dim 128 in bf16, N(0, 1)
   except 10 seeded (head, channel) pairs whose entries are 20 * t4; 256 bf16
   N(0, 1) queries per KV head score the whole compressed cache.  It stands in
@@ -75,6 +81,8 @@ WORKLOADS = {
                                     "bf16", "bf16", top_k=2048, seed=404),
     "bulk_64k_scan": Workload("bulk_64k_scan", 1, 8, 8, 128, 65536, 0, 3, 128, 4,
                               "bf16", "bf16", scan_queries=256, seed=505),
+    "vector_search_d200": Workload("vector_search_d200", 1, 1, 1, 200, 100000, 0, 2, 192, 2,
+                                   "f32", "f32", scan_queries=1000, seed=707),
     "llama8b_decode_32k_polar": Workload("llama8b_decode_32k_polar", 16, 32, 8, 128, 32768, 0, 4, 128, 4,
                                          "bf16", "bf16", seed=606, polar_upper_bits=2),
 }
@@ -109,6 +117,8 @@ def make_kv(w: Workload, device="cpu", tokens: int | None = None, batch: int | N
     dt = _DT[w.kv_dtype]
     shape = (T, w.kv_heads, w.head_dim)
     gsel = generator(w.seed * 7919 + 17 + seed_offset, "cpu")
+    if w.name == "vector_search_d200":
+        mu, sigma = embedding_channels(w)
     if w.name == "tinyllama_layer":
         outlier = torch.randperm(w.head_dim, generator=gsel)[:2]
     elif w.name == "bulk_64k_scan":
@@ -122,6 +132,8 @@ def make_kv(w: Workload, device="cpu", tokens: int | None = None, batch: int | N
             g = generator(w.seed * 1_000_003 + 2 * b + which + seed_offset, device)
             if w.name == "llama8b_decode_32k":
                 x = student_t4(shape, g, device)
+            elif w.name == "vector_search_d200":
+                x = mu.to(device) + sigma.to(device) * normal(shape, g, device)
             elif w.name == "bulk_64k_scan":
                 x = normal(shape, g, device)
                 t = 20.0 * student_t4((T, len(outlier)), g, device)
@@ -133,6 +145,13 @@ def make_kv(w: Workload, device="cpu", tokens: int | None = None, batch: int | N
                     x[..., outlier.to(device)] *= 8.0
             X[b].copy_(x.to(dt))
     return K, V
+
+
+def embedding_channels(w: Workload):
+    """Per-channel mean and scale of the embedding-like vectors (CPU float32 [head_dim])."""
+    g = generator(w.seed * 104729 + 3, "cpu")
+    z = torch.randn((2, w.head_dim), generator=g, dtype=torch.float32)
+    return 0.3 * z[0], torch.exp(0.4 * z[1])
 
 
 def make_hot(w: Workload, device="cpu", seed_offset: int = 0):
@@ -158,7 +177,11 @@ def make_queries(w: Workload, device="cpu", seed_offset: int = 0) -> torch.Tenso
         shape = (w.batch, w.kv_heads, w.scan_queries, w.head_dim)
     else:
         shape = (w.batch, w.q_heads, w.head_dim)
-    return normal(shape, g, device).to(_DT[w.q_dtype])
+    x = normal(shape, g, device)
+    if w.name == "vector_search_d200":        # queries from the database's distribution
+        mu, sigma = embedding_channels(w)
+        x = mu.to(device) + sigma.to(device) * x
+    return x.to(_DT[w.q_dtype])
 
 
 def small(w: Workload, tokens: int, batch: int | None = None, hot_tokens: int | None = None,

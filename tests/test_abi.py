@@ -54,7 +54,10 @@ def _cfg(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(head_dim=96), 2), (dict(head_dim=0), 1), (dict(key_bits=5), 1), (dict(value_bits=0), 1),
+    (dict(head_dim=100), 2), (dict(head_dim=264), 2), (dict(head_dim=0), 1),
+    (dict(key_codec=1, key_bits=3, polar_upper_bits=2), 2), (dict(key_codec=1, polar_upper_bits=3), 2),
+    (dict(key_codec=2), 1), (dict(polar_upper_bits=1), 1),
+    (dict(key_codec=1, head_dim=200, key_bits=4, polar_upper_bits=2), 2), (dict(key_bits=5), 1), (dict(value_bits=0), 1),
     (dict(qjl_dim=48), 1), (dict(qjl_dim=512), 1), (dict(key_bits=1), 2), (dict(qjl_dim=-32), 1)])
 def test_config_validation_on_host(kw, status):
     import compressed_key_attention_amd as tq
@@ -64,6 +67,21 @@ def test_config_validation_on_host(kw, status):
     h = ctypes.c_void_p()
     assert tq._create(ctypes.byref(cfg), ctypes.byref(h)) == status
     assert not h.value
+
+
+def test_polar_and_head_dim_200_host_constants():
+    """Polar grids come back for a polar config (and are refused for a scalar one); a
+    head_dim of 200 builds the scalar constants (orthogonal Pi, codebooks)."""
+    import compressed_key_attention_amd as tq
+    lv, bd = tq.polar_host_constants(128, 4, 128, 4, 1, 2, 2)
+    assert lv.shape == (7, 16) and np.all(np.diff(lv[0]) > 0) and np.all(np.diff(lv[1, :4]) > 0)
+    assert np.all(np.isnan(lv[1, 4:])) and np.all((bd[1, :3] > 0) & (bd[1, :3] < np.pi / 2))
+    cfg = _cfg()
+    out = (ctypes.c_float * 256)()
+    assert tq._polar_host_constants(ctypes.byref(cfg), out, out) == tq.TQ_ERR_INVALID_ARGUMENT
+    c = tq.host_constants(200, 2, 192, 2, 5, 6)
+    pi = c["pi"].astype(np.float64)
+    assert np.abs(pi.T @ pi - np.eye(200)).max() < 1e-5
 
 
 def test_null_handle_is_rejected_everywhere():
