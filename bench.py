@@ -91,8 +91,12 @@ def traffic_from_profile(kernel: str, workload: str):
 def decode_kernel_name(w) -> str:
     """The scan kernel the library picks for this shape (matrix-core path for head_dim 128,
     4 query heads per KV head, 2/3-bit keys, 4-bit values, m in {0, 128})."""
-    mfma = (w.head_dim == 128 and w.q_heads == 4 * w.kv_heads and w.value_bits == 4
-            and w.key_bits in (2, 3) and w.qjl_dim in (0, 128) and not w.polar_upper_bits)
+    if w.polar_upper_bits:   # polar keys: 4-bit level-1 / 2-bit higher angles on the same shape
+        mfma = (w.head_dim == 128 and w.q_heads == 4 * w.kv_heads and w.value_bits == 4
+                and w.key_bits == 4 and w.polar_upper_bits == 2 and w.qjl_dim in (0, 128))
+    else:
+        mfma = (w.head_dim == 128 and w.q_heads == 4 * w.kv_heads and w.value_bits == 4
+                and w.key_bits in (2, 3) and w.qjl_dim in (0, 128))
     return "decode_mfma_kernel" if mfma else "decode_scan_kernel"
 
 
@@ -309,6 +313,8 @@ def compute_dtype(w) -> str:
         return "i8 (int32 accumulate)"
     if w.name == "sparse_128k_top2048":
         return "i32 (selection scores) + f32 (attention)"
+    if decode_kernel_name(w) == "decode_mfma_kernel" and w.polar_upper_bits:
+        return "bf16 hi/lo key products + i8 sketch + bf16 values (fp32 / int32 accumulate)"
     if decode_kernel_name(w) == "decode_mfma_kernel":
         return "i8 + bf16 (int32 / fp32 accumulate)"
     return "f32"

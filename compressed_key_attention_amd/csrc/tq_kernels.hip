@@ -1381,8 +1381,14 @@ __device__ __forceinline__ uint32_t bf16_pair(float x) {      // hi | lo << 16
 constexpr int kScanLaneWords = 36;   // bulk-scan query operand words per lane (9 chunks of 16 B)
 
 constexpr int kPrepThreads = 1024;
+// POLAR (decode only): the key chunks are bf16 query operands instead of int8 limbs: chunks
+// 0..3 (against the tokens' u_hi) and 4..7 (against u_lo), chunk j & 3 covering coordinates
+// 32 kg + 8 (j & 3) + e of lane L's head n / 4: part 0 = bf16 hi of q_x, part 1 = its bf16 lo
+// (first four chunks only), parts 2, 3 zero.  Then QJL chunks 8, 9 and the scales, 48 words
+// per lane.
+constexpr int kPolarLaneWords = 48;
 
-template <int BK, bool QJL, bool SCAN>
+template <int BK, bool QJL, bool SCAN, bool POLAR = false>
 __global__ __launch_bounds__(kPrepThreads) void mfma_prep_kernel(const float* __restrict__ pi,
                                                                  const float* __restrict__ s_pi, const void* q,
                                                                  tq_dtype q_dt, int q_heads, int kv_heads,
@@ -1477,13 +1483,29 @@ __global__ __launch_bounds__(kPrepThreads) void mfma_prep_kernel(const float* __
   //    2 - p of the sketch (weight 2^(8 (2 - p))); part 3: zero.
   // one 16-byte chunk per wave (no divergence): waves 0 .. NC - 1 the code chunks, the next two
   // the QJL chunks, the next one the scales, each for lane L = its own lane
-  constexpr int NC = SCAN ? 6 : 4;
+  constexpr int NC = SCAN ? 6 : POLAR ? 8 : 4;
   const int L = threadIdx.x & 63, role = threadIdx.x >> 6;
   if (role > NC + 2) return;
   const int n = L & 15, kg = L >> 4, hB = n >> 2, part = n & 3;
   const float fq = s_fq[hB], fs = s_fs[hB];
-  u32x4* gdst = reinterpret_cast<u32x4*>(bop + ((int64_t)group * 64 + L) * (SCAN ? kScanLaneWords : 32));
-  if (role < NC) {
+  u32x4* gdst = reinterpret_cast<u32x4*>(
+      bop + ((int64_t)group * 64 + L) * (SCAN ? kScanLaneWords : POLAR ? kPolarLaneWords : 32));
+  if (POLAR && role < NC) {
+    const int j = role, chain = j >> 2, jj = j & 3;
+    u32x4 words;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const float x = xf[hB][32 * kg + 8 * jj + 2 * w + h2];
+        const uint32_t v = part == 0 ? bf16_half(x, 0) : (part == 1 && chain == 0) ? bf16_half(x, 1) : 0u;
+        word |= v << (16 * h2);
+      }
+      words[w] = word;
+    }
+    gdst[j] = words;
+  } else if (role < NC) {
     const int j = role;
     u32x4 words;
 #pragma unroll
@@ -1635,9 +1657,18 @@ __device__ __forceinline__ void merge_group(const float* __restrict__ pi_t, cons
 
 constexpr int kMfmaThreads = 256;
 
-template <int BK, bool QJL, bool GATHER, bool LOGITS>
+// POLAR: keys are polar codes (4-bit level-1, 2-bit higher angles, head_dim 128).  Lane
+// (token n, K slice kg) rebuilds the unit vector u of its token on coordinates
+// [32 kg, 32 kg + 32) (the subtree of level-5 node kg): the scale of the subtree root from its
+// two ancestors, levels 5..3 by cos / sin multiplies, then levels 2 and 1 together from the
+// tables TA[c2][c1] = cos psi (cos, sin) theta and TB = sin psi (cos, sin) theta.  u = u_hi + u_lo
+// (bf16 truncations) is the B operand of eight bf16 products with the query parts (q_hi, q_lo),
+// so part 0 + part 1 = <q_x, u> to about 2^-16 relative.
+template <int BK, bool QJL, bool GATHER, bool LOGITS, bool POLAR = false>
 __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs A) {
   constexpr int D = 128, G = 4, NW = kMfmaThreads / 64;
+  // polar tables: TA [4][16], TB [4][16], cos / sin of levels 3..7 [5][4]
+  __shared__ float2 ptab[POLAR ? 2 * 64 + 5 * 4 : 1];
   // value code -> bf16 (hi, lo) pair of its level / sqrt(d): 16 words in 16 distinct banks, so lookups
   // never conflict (equal codes are broadcast)
   __shared__ uint32_t vtab[16];
@@ -1658,6 +1689,16 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
 
   if (threadIdx.x < 16) vtab[threadIdx.x] = bf16_pair(A.val_levels[threadIdx.x] * A.inv_sqrt_d);
   if (threadIdx.x < 4) wzero[threadIdx.x] = 0u;
+  if constexpr (POLAR) {
+    if (threadIdx.x < 128) {
+      const int tb = threadIdx.x >> 6, c2 = (threadIdx.x >> 4) & 3, c1 = threadIdx.x & 15;
+      const float f = A.pcs[2 * (16 + c2) + tb];          // cos psi (TA) or sin psi (TB), level 2
+      ptab[threadIdx.x] = make_float2(f * A.pcs[2 * c1], f * A.pcs[2 * c1 + 1]);
+    } else if (threadIdx.x < 148) {
+      const int i = threadIdx.x - 128, l = i >> 2, c = i & 3;   // level 3 + l
+      ptab[threadIdx.x] = make_float2(A.pcs[2 * ((2 + l) * 16 + c)], A.pcs[2 * ((2 + l) * 16 + c) + 1]);
+    }
+  }
 
   // key levels as int8 limbs: gamma ~= (256 hi + lo) / F, byte c of each table word = code c
   const float fk = A.key_fix;
@@ -1675,25 +1716,34 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
   // part of head kg for token n: the lane owns score (token n, head kg), and each lane loads
   // only its own token's fields (key group kg, sketch word kg, value quarter kg, norms).
   const int n = lane & 15, kg = lane >> 4;
-  i32x4 Aq[4], Aj[2];
-  float bk16, bk8, bq, oq;
+  constexpr int NCK = POLAR ? 8 : 4;                         // key operand chunks
+  i32x4 Aq[POLAR ? 1 : 4], Aj[2];
+  bf16x8 Ap[POLAR ? 8 : 1];
+  float bk16, bk8, bq, oq, kpol;
   {
-    const u32x4* bp = reinterpret_cast<const u32x4*>(A.bop + (((int64_t)b * A.kv_heads + hkv) * 64 + lane) * 32);
-    u32x4 w[7];
+    const u32x4* bp = reinterpret_cast<const u32x4*>(
+        A.bop + (((int64_t)b * A.kv_heads + hkv) * 64 + lane) * (POLAR ? kPolarLaneWords : 32));
+    u32x4 w[NCK + 3];
 #pragma unroll
-    for (int i = 0; i < 7; ++i) w[i] = bp[i];
+    for (int i = 0; i < NCK + 3; ++i) w[i] = bp[i];
+    if constexpr (POLAR) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) Aq[j] = __builtin_bit_cast(i32x4, w[j]);
+      for (int j = 0; j < 8; ++j) Ap[j] = __builtin_bit_cast(bf16x8, w[j]);
+    } else {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) Aj[j] = __builtin_bit_cast(i32x4, w[4 + j]);
+      for (int j = 0; j < 4; ++j) Aq[j] = __builtin_bit_cast(i32x4, w[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) Aj[j] = __builtin_bit_cast(i32x4, w[NCK + j]);
     // logits in base-2 units (exp2(l2 - m2) = exp(logit - m)): the softmax scale, 1 / sqrt(d)
     // and log2(e) ride on the part weights, the QJL coefficient on the sketch's
     const float ks = A.scale * A.inv_sqrt_d * kLog2e, qs = A.scale * A.qjl_coef * kLog2e;
-    const float bk = __uint_as_float(w[6][0]);
+    const float bk = __uint_as_float(w[NCK + 2][0]);
     bk16 = 65536.0f * bk * ks;
     bk8 = 256.0f * bk * ks;
-    bq = __uint_as_float(w[6][1]) * qs;
-    oq = __uint_as_float(w[6][2]) * qs;
+    kpol = A.scale * kLog2e;                                   // polar: r <q_x, u>, u of unit norm
+    bq = __uint_as_float(w[NCK + 2][1]) * qs;
+    oq = __uint_as_float(w[NCK + 2][2]) * qs;
   }
   __syncthreads();
 
@@ -1717,7 +1767,7 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
   const uint32_t* wsrc = n < 8 ? wstage[wave][n & 1] + (vh & 3) * 16 + 4 * kg : wzero;
 
   struct Fields {
-    uint32_t kw[BK];
+    uint32_t kw[POLAR ? 6 : BK];   // polar: level-1 codes of the lane's subtree (2), upper stream (4)
     uint32_t sw;
     u32x4 vw;
     float nk, nrho, nv;
@@ -1741,7 +1791,16 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
       t = f.valid ? (uint32_t)ts : 0u;
     }
     const uint32_t o = (uint32_t)__umul24(t, rb);
-    if constexpr (BK == 3) {
+    if constexpr (POLAR) {
+      const u32x2 w1 = *reinterpret_cast<const u32x2*>(recs + (size_t)(o + 8 * kg));
+      const u32x4 wu = *reinterpret_cast<const u32x4*>(recs + (size_t)(o + 32));
+      f.kw[0] = w1[0];
+      f.kw[1] = w1[1];
+      f.kw[2] = wu[0];
+      f.kw[3] = wu[1];
+      f.kw[4] = wu[2];
+      f.kw[5] = wu[3];
+    } else if constexpr (BK == 3) {
       typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
       const u32x3 w = *reinterpret_cast<const u32x3*>(recs + (size_t)(o + kofs));
       f.kw[0] = w[0];
@@ -1763,6 +1822,65 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
   // one 16-token step on fields `cur` (tokens base .. base + 15)
   auto step = [&](const Fields& cur, int base) {
 
+    float l2;
+    if constexpr (POLAR) {
+      // ---- key scores from the rebuilt unit vector (bf16 hi / lo products) ----
+      const uint32_t u3 = cur.kw[5], u2 = cur.kw[4], uw2 = kg < 2 ? cur.kw[2] : cur.kw[3];
+      const float2* csl = ptab + 128;                                  // levels 3..7
+      const float2 t7 = csl[16 + ((u3 >> 28) & 3u)];
+      const float2 t6 = csl[12 + ((u3 >> (24 + 2 * (kg >> 1))) & 3u)];
+      const float sroot = ((kg >> 1) ? t7.y : t7.x) * ((kg & 1) ? t6.y : t6.x);
+      const float2 t5 = csl[8 + ((u3 >> (16 + 2 * kg)) & 3u)];
+      float s4[2] = {sroot * t5.x, sroot * t5.y}, s3[4], s2[8];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float2 t = csl[4 + ((u3 >> (4 * kg + 2 * i)) & 3u)];
+        s3[2 * i] = s4[i] * t.x;
+        s3[2 * i + 1] = s4[i] * t.y;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float2 t = csl[(u2 >> (8 * kg + 2 * i)) & 3u];
+        s2[2 * i] = s3[i] * t.x;
+        s2[2 * i + 1] = s3[i] * t.y;
+      }
+      f32x4 Ck = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        u32x4 bh, bl;
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {                 // level-2 node 2 jj + k2
+          const int k = 2 * jj + k2;
+          const uint32_t c2 = (uw2 >> (16 * (kg & 1) + 2 * k)) & 3u;
+          const uint32_t ca = (cur.kw[k >> 2] >> (8 * (k & 3))) & 15u;      // level-1 pair 2k
+          const uint32_t cb = (cur.kw[k >> 2] >> (8 * (k & 3) + 4)) & 15u;  // level-1 pair 2k + 1
+          const float2 ta = ptab[c2 * 16 + ca], tb = ptab[64 + c2 * 16 + cb];
+          const float v[4] = {s2[k] * ta.x, s2[k] * ta.y, s2[k] * tb.x, s2[k] * tb.y};
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr) {
+            const uint32_t x0 = __float_as_uint(v[2 * pr]), x1 = __float_as_uint(v[2 * pr + 1]);
+            const float r0 = v[2 * pr] - __uint_as_float(x0 & 0xFFFF0000u);
+            const float r1 = v[2 * pr + 1] - __uint_as_float(x1 & 0xFFFF0000u);
+            bh[2 * k2 + pr] = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
+            bl[2 * k2 + pr] = __builtin_amdgcn_perm(__float_as_uint(r1), __float_as_uint(r0), 0x07060302u);
+          }
+        }
+        Ck = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ap[jj], __builtin_bit_cast(bf16x8, bh), Ck, 0, 0, 0);
+        Ck = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ap[4 + jj], __builtin_bit_cast(bf16x8, bl), Ck, 0, 0, 0);
+      }
+      i32x4 Cq = i32x4{0, 0, 0, 0};
+      if (QJL) {
+#pragma unroll
+        for (int j = 1; j < 4; j += 2) {
+          i32x4 q;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) q[w] = (int)(cur.sw & (0x01010101u << (2 * (j & 2) + w)));
+          Cq = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aj[j >> 1], q, Cq, 0, 0, 0);
+        }
+      }
+      l2 = cur.nk * (Ck[0] + Ck[1]) * kpol;
+      if (QJL) l2 = fmaf(cur.nrho, fmaf((float)((Cq[0] << 16) + (Cq[1] << 8) + Cq[2]), bq, oq), l2);
+    } else {
     // ---- key scores (exact int32), token operands from the level tables ----
     uint32_t sel[8];
     if constexpr (BK == 3) {
@@ -1795,8 +1913,9 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
     }
     // parts of head kg for token n: weights 2^24, 2^16, 2^8 (|C0[0]| < 2^21 and |C0[1]| < 2^22,
     // so 256 C0[0] + C0[1] fits in int32); sketch sum 2^16 Cq0 + 2^8 Cq1 + Cq2 < 2^31
-    float l2 = cur.nk * fmaf((float)((C0[0] << 8) + C0[1]), bk16, (float)C0[2] * bk8);
+    l2 = cur.nk * fmaf((float)((C0[0] << 8) + C0[1]), bk16, (float)C0[2] * bk8);
     if (QJL) l2 = fmaf(cur.nrho, fmaf((float)((Cq[0] << 16) + (Cq[1] << 8) + Cq[2]), bq, oq), l2);
+    }
     const float logit = cur.valid ? l2 : kNegInf;
     if (LOGITS && cur.valid) A.logits[(qrow0 + kg) * A.logit_stride + base + n] = logit * kLn2;
     // ---- running maximum per head, shared by its 16 lanes, raised lazily (rare branch) ----
@@ -2133,10 +2252,15 @@ static bool mfma_path(const Consts& c, int G) {
   return c.d == 128 && G == 4 && c.vb == 4 && (c.kb == 2 || c.kb == 3) && (c.m == 0 || c.m == 128);
 }
 
+// polar keys on the matrix-core path: the shape of the llama8b polar workload
+static bool polar_mfma_path(const Consts& c, int G) {
+  return c.d == 128 && G == 4 && c.vb == 4 && c.pb1 == 4 && c.pbh == 2 && (c.m == 0 || c.m == 128);
+}
+
 bool plan_decode(const Consts& c, int batch, int q_heads, int kv_heads, int64_t n_max,
                  DecodePlan* plan) {
   const int G = q_heads / kv_heads;
-  plan->mfma = !c.polar && mfma_path(c, G);
+  plan->mfma = c.polar ? polar_mfma_path(c, G) : mfma_path(c, G);
   const int hpl = (G % 4 == 0) ? 4 : 1;
   const int lpt = (c.d / 32) * (G / hpl);
   if (lpt > 64 || (lpt & (lpt - 1)) != 0) return false;
@@ -2182,7 +2306,8 @@ bool plan_decode(const Consts& c, int batch, int q_heads, int kv_heads, int64_t 
   plan->ws_qs = align256(rows * c.d * 4);
   plan->ws_part = plan->ws_qs + align256(rows * std::max(c.m, 1) * 4);
   plan->ws_bop = plan->ws_part + align256(rows * plan->n_chunks * (c.d + 2) * 4);
-  plan->ws_total = plan->ws_bop + (plan->mfma ? (size_t)std::max(batch, 1) * kv_heads * 64 * 32 * 4 : 0);
+  plan->ws_total = plan->ws_bop + (plan->mfma ? (size_t)std::max(batch, 1) * kv_heads * 64 *
+                                                    (c.polar ? kPolarLaneWords : 32) * 4 : 0);
   return true;
 }
 
@@ -2190,7 +2315,11 @@ static void launch_mfma_prep(const Consts& c, const DevConsts& dc, const void* q
                              int batch, int q_heads, int kv_heads, uint32_t* bop, hipStream_t st) {
   const dim3 grid((unsigned)(batch * kv_heads));
   const bool qjl = c.m > 0;
-  if (c.kb == 3 && qjl)
+  if (c.polar && qjl)
+    hipLaunchKernelGGL((mfma_prep_kernel<2, true, false, true>), grid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
+  else if (c.polar)
+    hipLaunchKernelGGL((mfma_prep_kernel<2, false, false, true>), grid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
+  else if (c.kb == 3 && qjl)
     hipLaunchKernelGGL((mfma_prep_kernel<3, true, false>), grid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
   else if (c.kb == 3)
     hipLaunchKernelGGL((mfma_prep_kernel<3, false, false>), grid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
@@ -2200,21 +2329,23 @@ static void launch_mfma_prep(const Consts& c, const DevConsts& dc, const void* q
     hipLaunchKernelGGL((mfma_prep_kernel<2, false, false>), grid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
 }
 
-template <int BK, bool QJL>
+template <int BK, bool QJL, bool POLAR = false>
 static void launch_mfma_bk(const DecodeArgs& a, bool gather, bool logits, dim3 grid, hipStream_t st) {
   if (gather && logits)
-    hipLaunchKernelGGL((decode_mfma_kernel<BK, QJL, true, true>), grid, dim3(kMfmaThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<BK, QJL, true, true, POLAR>), grid, dim3(kMfmaThreads), 0, st, a);
   else if (gather)
-    hipLaunchKernelGGL((decode_mfma_kernel<BK, QJL, true, false>), grid, dim3(kMfmaThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<BK, QJL, true, false, POLAR>), grid, dim3(kMfmaThreads), 0, st, a);
   else if (logits)
-    hipLaunchKernelGGL((decode_mfma_kernel<BK, QJL, false, true>), grid, dim3(kMfmaThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<BK, QJL, false, true, POLAR>), grid, dim3(kMfmaThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<BK, QJL, false, false>), grid, dim3(kMfmaThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<BK, QJL, false, false, POLAR>), grid, dim3(kMfmaThreads), 0, st, a);
 }
 
 static void launch_mfma_scan(const DecodeArgs& a, int kb, bool qjl, bool gather, bool logits, dim3 grid,
-                             hipStream_t st) {
-  if (kb == 3 && qjl) launch_mfma_bk<3, true>(a, gather, logits, grid, st);
+                             hipStream_t st, bool polar = false) {
+  if (polar && qjl) launch_mfma_bk<2, true, true>(a, gather, logits, grid, st);
+  else if (polar) launch_mfma_bk<2, false, true>(a, gather, logits, grid, st);
+  else if (kb == 3 && qjl) launch_mfma_bk<3, true>(a, gather, logits, grid, st);
   else if (kb == 3) launch_mfma_bk<3, false>(a, gather, logits, grid, st);
   else if (qjl) launch_mfma_bk<2, true>(a, gather, logits, grid, st);
   else launch_mfma_bk<2, false>(a, gather, logits, grid, st);
@@ -2312,7 +2443,7 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
   dim3 grid(plan.n_chunks, kv_heads, batch);
   ev.before(stream);
   if (mfma) {
-    launch_mfma_scan(a, c.kb, c.m > 0, sel_idx != nullptr, logits != nullptr, grid, stream);
+    launch_mfma_scan(a, c.kb, c.m > 0, sel_idx != nullptr, logits != nullptr, grid, stream, c.polar != 0);
   } else if (plan.small) {
     if (c.d == 128) launch_small_d<128>(a, c.kb, c.vb, grid, stream);
     else launch_small_d<64>(a, c.kb, c.vb, grid, stream);

@@ -112,6 +112,14 @@ def test_polar_decode_widths_with_exact_segment(d, b1, bh, m, vb):
     GP._decode_case(w, [1000], hot_lens=[300])
 
 
+@pytest.mark.parametrize("m,lens", [(0, [2500, 37]), (128, [64, 4097])])
+def test_polar_decode_matrix_core_path(m, lens):
+    """head_dim 128, 4 query heads per KV head, 4-bit values, 4/2-bit angles: the matrix-core
+    kernel (bf16 hi/lo products against the rebuilt unit vectors), with and without the sketch."""
+    print(f"[case] polar matrix-core decode m={m} lens={lens}", flush=True)
+    GP._decode_case(_wl(m=m, tokens=max(lens), batch=2), lens)
+
+
 def test_polar_decode_gather_mode():
     print("[case] polar decode gather", flush=True)
     w = _wl(tokens=900, batch=2)
