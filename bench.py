@@ -311,6 +311,8 @@ def compute_dtype(w) -> str:
     128 with 4 query heads per KV head; the bulk scan's int8 products), fp32 elsewhere."""
     if w.name == "bulk_64k_scan" and w.head_dim == 128 and w.key_bits in (2, 3) and w.qjl_dim in (0, 128):
         return "i8 (int32 accumulate)"
+    if w.scan_queries:
+        return "f16 hi/lo matrix-core products (fp32 accumulate)"
     if w.name == "sparse_128k_top2048":
         return "i32 (selection scores) + f32 (attention)"
     if decode_kernel_name(w) == "decode_mfma_kernel" and w.polar_upper_bits:
@@ -549,10 +551,10 @@ def run_bulk_scan(args, tq, W, ev):
     alg_bytes = B * H * T * key_bytes + B * H * nq * T * 4     # key records read + scores written
     line = base_line(args, w, ms_per_step, B * T)
     line["metric"] = (f"compressed tokens scanned per second ({nq} queries per KV head) + % of "
-                      + ("HBM" if w.name == "bulk_64k_scan" else "fp32 vector ALU") + " roofline")
+                      + ("HBM" if w.name == "bulk_64k_scan" else "fp16 matrix-core") + " roofline")
     line["config"].update({"scan_queries": nq})
     mfma = w.head_dim == 128 and w.key_bits in (2, 3) and w.qjl_dim in (0, 128)
-    kname = "scan_mfma_kernel" if mfma else "scan_kernel"
+    kname = "scan_mfma_kernel" if mfma else "scan_mfma16_kernel"
     extra = None
     if mfma:
         # int8 matrix-core work the kernel executes: 8 (6 without the sketch) 16x16x64 MFMAs per
@@ -563,12 +565,17 @@ def run_bulk_scan(args, tq, W, ev):
                  "mfma_int8_frac": tops / 5000.0}
     line["roofline"] = roofline(kname, w.name, alg_bytes, scan_ms, extra, fl_ms, ceiling)
     if not mfma:
-        # float32 contraction over d + m operands per (query, vector) pair on the vector ALUs
+        # a dense contraction over the d + m operands of every (query, vector) pair, run as three
+        # fp16 matrix-core products (hi.hi, hi.lo, lo.hi) of operands padded to 32-multiples
         flops = 2.0 * (d + w.qjl_dim) * B * H * nq * T
+        kp = (d + w.qjl_dim + 31) // 32 * 32
+        executed = 3 * 2.0 * kp * B * H * (nq + 127) // 128 * 128 * (T + 127) // 128 * 128
         tf = flops / (scan_ms * 1e-3) / 1e12
+        tx = executed / (scan_ms * 1e-3) / 1e12
         hbm = line["roofline"]
-        line["roofline"] = {"bound": "alu", "kernel": kname, "achieved": tf, "peak": 157.3, "unit": "TFLOP/s",
-                            "frac": tf / 157.3, "traffic": hbm["traffic"], "algorithmic_flops_per_launch": flops,
+        line["roofline"] = {"bound": "mfma", "kernel": kname, "achieved": tf, "peak": 2500.0, "unit": "TFLOP/s",
+                            "frac": tf / 2500.0, "traffic": hbm["traffic"], "algorithmic_flops_per_launch": flops,
+                            "mfma_f16_executed_tflops": tx, "mfma_f16_executed_frac": tx / 2500.0,
                             "kernel_ms": scan_ms, "kernel_ms_median": hbm["kernel_ms_median"],
                             "kernel_ms_min": hbm["kernel_ms_min"], "hbm_gbps": hbm["achieved"],
                             "hbm_frac": hbm["frac"], "algorithmic_bytes_per_launch": alg_bytes}

@@ -150,7 +150,8 @@ hipError_t launch_sparse(const Consts& c, const DevConsts& dc, const SparsePlan&
 struct ScanPlan {
   bool mfma;        // matrix-core scan (head_dim 128, 2/3-bit keys, m in {0, 128})
   int n_groups;     // groups of 4 queries per (sequence, KV head)
-  size_t ws_q, ws_total;
+  int kp;           // generic path: d + m rounded up to a multiple of 32
+  size_t ws_q, ws_ql, ws_qscale, ws_total;
 };
 ScanPlan plan_scan(const Consts& c, int batch, int heads, int n_queries);
 hipError_t launch_scan(const Consts& c, const DevConsts& dc, const ScanPlan& plan, const void* q,

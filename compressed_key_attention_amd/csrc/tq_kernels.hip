@@ -9,7 +9,10 @@
 //  decode_merge_kernel   log-sum-exp merge of the partials + exact segment + un-rotation
 //  index_* kernels       Self-Indexing sign index (channel mean, patterns, centroids)
 //  select_* kernels      integer LUT-GEMV scores, radix select, ordered compaction
-//  scan_* kernels        bulk multi-query score scan
+//  compress_generic_kernel  the same at head_dims without a matrix-core layout (float64 loops)
+//  scan_* kernels        bulk multi-query score scan (int8 matrix cores at head_dim 128; fp16
+//                        hi / lo matrix-core products elsewhere)
+//  polar_* helpers       the PolarQuant key codes (compress side) and their decode variants
 //
 // Method sources are cited at each kernel; the arithmetic each performs is stated there.
 
@@ -3644,50 +3647,64 @@ ScanPlan plan_scan(const Consts& c, int batch, int heads, int n_queries) {
   p.mfma = scan_mfma_path(c);
   p.n_groups = (std::max(n_queries, 1) + 3) / 4;
   p.ws_q = 0;
+  // generic path: fp16 hi and lo query rows [units][nq][kp], then the row scales
+  p.kp = (c.d + c.m + 31) / 32 * 32;
+  const size_t rows = units * (size_t)std::max(n_queries, 1);
+  p.ws_ql = align256(rows * p.kp * 2);
+  p.ws_qscale = p.ws_ql + align256(rows * p.kp * 2);
   p.ws_total = p.mfma ? align256(units * p.n_groups * 64 * kScanLaneWords * 4)   // query operands
-                      : align256(units * std::max(n_queries, 1) * (c.d + c.m) * 4);
+                      : p.ws_qscale + align256(rows * 4);
   return p;
 }
 
-__global__ void scan_prep_kernel(const float* __restrict__ pi, const float* __restrict__ s, int d, int m,
-                                 const void* q, tq_dtype q_dt, float* out) {
+// Generic bulk scan (every shape off the int8 matrix-core path, e.g. head_dim 200): a dense
+// contraction over the d + m operands of each (query, vector) pair on fp16 matrix cores.
+// Query rows (q_x | q_s) and token rows (r_k/sqrt(d) gamma[c] | +-coef rho) are each scaled by
+// their largest |entry| and split into fp16 hi + lo (RNE; x ~ hi + lo to ~2^-23), and the
+// products hi.hi + hi.lo + lo.hi (v_mfma_f32_16x16x32_f16) give each estimate to ~2^-22 of
+// sum |q_k t_k|; the two scales multiply the result.
+// Prep (one block per query row): q_x = Pi q and q_s = S q_x in float64, then the scaled fp16
+// hi / lo rows, zero-padded to kp (a multiple of 32), and the row scale.
+__global__ __launch_bounds__(256) void scan_prep_f16_kernel(const float* __restrict__ pi, const float* __restrict__ s,
+                                                            int d, int m, int kp, const void* q, tq_dtype q_dt,
+                                                            uint16_t* qh, uint16_t* ql, float* qscale) {
   __shared__ double qv[256];
   __shared__ double xv[256];
-  const int64_t row = blockIdx.x;
-  for (int i = threadIdx.x; i < d; i += blockDim.x) qv[i] = (double)load_elem(q, q_dt, row * d + i);
+  __shared__ float row[512];
+  __shared__ float red[4];
+  const int64_t r = blockIdx.x;
+  const int K = d + m;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) qv[i] = (double)load_elem(q, q_dt, r * d + i);
   __syncthreads();
-  float* o = out + row * (d + m);
   for (int i = threadIdx.x; i < d; i += blockDim.x) {
     double acc = 0.0;
     for (int j = 0; j < d; ++j) acc += (double)pi[i * d + j] * qv[j];
     xv[i] = acc;
-    o[i] = (float)acc;
+    row[i] = (float)acc;
   }
   __syncthreads();
   for (int k = threadIdx.x; k < m; k += blockDim.x) {
     double acc = 0.0;
     for (int i = 0; i < d; ++i) acc += (double)s[k * d + i] * xv[i];
-    o[d + k] = (float)acc;
+    row[d + k] = (float)acc;
   }
+  __syncthreads();
+  float mx = 0.0f;
+  for (int k = threadIdx.x; k < K; k += blockDim.x) mx = fmaxf(mx, fabsf(row[k]));
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float sc = mx > 0.0f ? mx : 1.0f, inv = 1.0f / sc;
+  for (int k = threadIdx.x; k < kp; k += blockDim.x) {
+    const float v = k < K ? row[k] * inv : 0.0f;
+    const _Float16 h = (_Float16)v;
+    const _Float16 l = (_Float16)(v - (float)h);
+    qh[r * kp + k] = __builtin_bit_cast(uint16_t, h);
+    ql[r * kp + k] = __builtin_bit_cast(uint16_t, l);
+  }
+  if (threadIdx.x == 0) qscale[r] = sc;
 }
-
-constexpr int kScanTile = 64;
-
-struct ScanArgs {
-  const float* qprep;
-  const uint8_t* records;
-  float* scores;
-  int64_t capacity, n_tokens;
-  int d, m, kb, kbytes, rec_bytes, norm_off, heads, n_queries;
-  float inv_sqrt_d, qjl_coef;
-  float key_levels[kMaxLevels];
-};
-
-// Generic bulk scan: 64 queries x 64 tokens per workgroup, the contraction (d key coordinates,
-// then m signs) in slabs of kScanSlab: each slab stages the queries' prepared operands and
-// the tokens' dequantized operands (r_k/sqrt(d) gamma[c], +-coef rho) in LDS, then a 4 x 4
-// register tile per thread accumulates in float32.
-constexpr int kScanSlab = 128;
 
 __device__ __forceinline__ uint32_t key_code_at(const uint32_t* kw, int i, int d, int kb) {
   if (kb == 3) {
@@ -3705,78 +3722,178 @@ __device__ __forceinline__ uint32_t key_code_at(const uint32_t* kw, int i, int d
   return (kw[wi] >> sh) & ((1u << kb) - 1u);
 }
 
-__global__ __launch_bounds__(256) void scan_kernel(ScanArgs A) {
-  extern __shared__ __attribute__((aligned(16))) float lds[];
-  constexpr int KP = kScanSlab + 4;       // padded row
-  const int K = A.d + A.m;
-  float* qt = lds;                        // [64][KP]
-  float* kt = lds + kScanTile * KP;       // [64][KP]
+constexpr int kS16Tile = 128;   // queries and vectors per workgroup
+constexpr int kS16Row = 40;     // LDS row: 32 fp16 of one K step + 8 pad (80 B)
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+struct Scan16Args {
+  const uint16_t* qh;
+  const uint16_t* ql;
+  const float* qscale;
+  const uint8_t* records;
+  float* scores;
+  int64_t capacity, n_tokens;
+  int d, m, kp, kb, kbytes, rec_bytes, norm_off, n_queries;
+  float inv_sqrt_d, qjl_coef, gmax;
+  float key_levels[kMaxLevels];
+};
+
+// 128 queries x 128 vectors per workgroup; wave w computes queries 64 (w / 2) .. + 63 against
+// vectors 64 (w % 2) .. + 63 as 4 x 4 tiles of 16 x 16.  Per K step of 32: thread (row
+// tid / 2, half tid % 2) stages 16 operands of one query row (copied) and of one vector, then
+// every wave reads its A (queries) and B (vectors) hi / lo operands and issues 48 products.
+// A vector's scale is r_k/sqrt(d) max|gamma|, so its key operands gamma[c] / max|gamma| are
+// per-code constants: pairs of codes index tables of packed fp16 hi (and lo) pairs.  Its sign
+// operands are +-coef rho / scale: one fp16 hi / lo pair per vector, the sign bit flipped by
+// the QJL bit.
+__global__ __launch_bounds__(256, 2) void scan_mfma16_kernel(Scan16Args A) {
+  __shared__ __attribute__((aligned(16))) uint16_t sq[2][kS16Tile * kS16Row];
+  __shared__ __attribute__((aligned(16))) uint16_t st[2][kS16Tile * kS16Row];
+  __shared__ float sts[kS16Tile];
+  __shared__ uint32_t ptab[2][256];    // code pair (c0 | c1 << kb) -> packed fp16 hi / lo pair
   const int unit = blockIdx.z;
-  const int64_t tok0 = (int64_t)blockIdx.x * kScanTile;
-  const int q0 = blockIdx.y * kScanTile;
-  const uint8_t* recs = A.records + (int64_t)unit * A.capacity * A.rec_bytes;
-  // this thread dequantizes every fourth operand of token tt
-  const int tt = threadIdx.x / 4, part = threadIdx.x % 4;
-  const int64_t t = tok0 + tt;
-  const bool valid = t < A.n_tokens;
-  const uint8_t* rec = recs + (valid ? t : 0) * A.rec_bytes;
+  const int64_t t0 = (int64_t)blockIdx.x * kS16Tile;
+  const int q0 = blockIdx.y * kS16Tile;
+  const int K = A.d + A.m, kb = A.kb;
+  const float ginv = A.gmax > 0.0f ? 1.0f / A.gmax : 0.0f;
+  for (int e = threadIdx.x; e < (1 << (2 * kb)); e += blockDim.x) {
+    uint32_t hp = 0u, lp = 0u;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const float v = A.key_levels[(e >> (kb * u)) & ((1 << kb) - 1)] * ginv;
+      const _Float16 h = (_Float16)v;
+      const _Float16 l = (_Float16)(v - (float)h);
+      hp |= (uint32_t)__builtin_bit_cast(uint16_t, h) << (16 * u);
+      lp |= (uint32_t)__builtin_bit_cast(uint16_t, l) << (16 * u);
+    }
+    ptab[0][e] = hp;
+    ptab[1][e] = lp;
+  }
+  // staging role
+  const int ri = threadIdx.x >> 1, half = threadIdx.x & 1;
+  const int64_t t = t0 + ri;
+  const bool tv = t < A.n_tokens;
+  const uint8_t* rec = A.records + ((int64_t)unit * A.capacity + (tv ? t : 0)) * A.rec_bytes;
   const float* nrm = reinterpret_cast<const float*>(rec + A.norm_off);
-  const float ak = valid ? nrm[0] * A.inv_sqrt_d : 0.0f;
-  const float aq = valid ? A.qjl_coef * nrm[1] : 0.0f;
+  const float ak = tv ? nrm[0] * A.inv_sqrt_d : 0.0f, aq = tv ? A.qjl_coef * nrm[1] : 0.0f;
+  const float tsc = ak * A.gmax;                       // 0 for an invalid or zero vector (then aq = 0)
+  const float sv = tsc > 0.0f ? aq / tsc : 0.0f;
+  uint32_t sgh, sgl;                                   // +sv as an fp16 hi / lo pair in both halves
+  {
+    const _Float16 h = (_Float16)sv;
+    const _Float16 l = (_Float16)(sv - (float)h);
+    sgh = (uint32_t)__builtin_bit_cast(uint16_t, h) * 0x10001u;
+    sgl = (uint32_t)__builtin_bit_cast(uint16_t, l) * 0x10001u;
+  }
+  if (half == 0) sts[ri] = tsc;
   const uint32_t* kw = reinterpret_cast<const uint32_t*>(rec);
   const uint32_t* sw = reinterpret_cast<const uint32_t*>(rec + A.kbytes);
-  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;   // tokens tx + 16 j, queries 4 ty + i
-  float acc[4][4];
+  const int qi = q0 + ri;
+  const bool qv = qi < A.n_queries;
+  const int64_t qrow = ((int64_t)unit * A.n_queries + (qv ? qi : 0)) * A.kp;
+  // compute role
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, kg = lane >> 4;
+  const int qb = (wave >> 1) * 64, tb = (wave & 1) * 64;
+  f32x4 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
-  for (int k0 = 0; k0 < K; k0 += kScanSlab) {
-    const int kn = min(kScanSlab, K - k0);
-    __syncthreads();   // the previous slab has been consumed
-    for (int e = threadIdx.x; e < kScanTile * kScanSlab; e += blockDim.x) {
-      const int qi = e / kScanSlab, kk = e % kScanSlab;
-      qt[qi * KP + kk] = (kk < kn && q0 + qi < A.n_queries)
-                             ? A.qprep[((int64_t)unit * A.n_queries + q0 + qi) * K + k0 + kk] : 0.0f;
-    }
-    for (int kk = part; kk < kScanSlab; kk += 4) {
-      const int i = k0 + kk;
-      float val = 0.0f;
-      if (i < A.d) {
-        val = ak * A.key_levels[key_code_at(kw, i, A.d, A.kb)];
-      } else if (i < K) {
-        const int j = i - A.d;
-        val = ((sw[j >> 5] >> (j & 31)) & 1u) ? aq : -aq;
+    for (int ct = 0; ct < 4; ++ct) acc[rt][ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  __syncthreads();   // ptab
+  for (int k0 = 0; k0 < A.kp; k0 += 32) {
+    {
+      const int c0 = k0 + 16 * half;
+      u32x4 h0 = u32x4{0u, 0u, 0u, 0u}, h1 = h0, l0 = h0, l1 = h0;
+      if (qv) {
+        const u32x4* ph = reinterpret_cast<const u32x4*>(A.qh + qrow + c0);
+        const u32x4* pl = reinterpret_cast<const u32x4*>(A.ql + qrow + c0);
+        h0 = ph[0];
+        h1 = ph[1];
+        l0 = pl[0];
+        l1 = pl[1];
       }
-      kt[tt * KP + kk] = val;
+      u32x4* dh = reinterpret_cast<u32x4*>(&sq[0][ri * kS16Row + 16 * half]);
+      u32x4* dl = reinterpret_cast<u32x4*>(&sq[1][ri * kS16Row + 16 * half]);
+      dh[0] = h0;
+      dh[1] = h1;
+      dl[0] = l0;
+      dl[1] = l1;
+      // 8 operand pairs (c0 + 2 e2, + 1); d and K are even, so a pair never mixes regions
+      uint32_t hw[8], lw[8];
+      const bool plain = kb != 3 && c0 + 16 <= A.d;   // 16 key codes of 2 or 4 bits: one run of bits
+      uint32_t kr0 = 0u, kr1 = 0u;
+      if (plain) {
+        const int bit = c0 * kb;
+        kr0 = kw[bit >> 5] >> (bit & 31);
+        kr1 = kb == 4 ? kw[(bit >> 5) + 1] : 0u;
+      }
+#pragma unroll
+      for (int e2 = 0; e2 < 8; ++e2) {
+        const int k = c0 + 2 * e2;
+        uint32_t hp = 0u, lp = 0u;
+        if (k < A.d) {
+          uint32_t pidx;
+          if (plain) {
+            const int sh = 2 * kb * e2;                 // < 32 for kb = 2; kb = 4: words of 4 pairs
+            pidx = kb == 4 ? ((e2 < 4 ? kr0 : kr1) >> (8 * (e2 & 3))) & 0xFFu : (kr0 >> sh) & 0xFu;
+          } else {
+            pidx = key_code_at(kw, k, A.d, kb) | (key_code_at(kw, k + 1, A.d, kb) << kb);
+          }
+          hp = ptab[0][pidx];
+          lp = ptab[1][pidx];
+        } else if (k < K) {
+          const int j = k - A.d;
+          const uint32_t b2 = (sw[j >> 5] >> (j & 31)) & 3u;
+          const uint32_t neg = ((b2 & 1u) ? 0u : 0x8000u) | ((b2 & 2u) ? 0u : 0x80000000u);
+          hp = sgh ^ neg;
+          lp = sgl ^ neg;
+        }
+        hw[e2] = hp;
+        lw[e2] = lp;
+      }
+      u32x4* th = reinterpret_cast<u32x4*>(&st[0][ri * kS16Row + 16 * half]);
+      u32x4* tl = reinterpret_cast<u32x4*>(&st[1][ri * kS16Row + 16 * half]);
+      th[0] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+      th[1] = u32x4{hw[4], hw[5], hw[6], hw[7]};
+      tl[0] = u32x4{lw[0], lw[1], lw[2], lw[3]};
+      tl[1] = u32x4{lw[4], lw[5], lw[6], lw[7]};
     }
     __syncthreads();
-    for (int kk = 0; kk < kScanSlab; kk += 4) {
-      float4 qa[4], ka[4];
+    f16x8 ah[4], al[4], bh[4], bl[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) qa[i] = *reinterpret_cast<const float4*>(qt + (4 * ty + i) * KP + kk);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) ka[j] = *reinterpret_cast<const float4*>(kt + (tx + 16 * j) * KP + kk);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc[i][j] = fmaf(qa[i].x, ka[j].x, acc[i][j]);
-          acc[i][j] = fmaf(qa[i].y, ka[j].y, acc[i][j]);
-          acc[i][j] = fmaf(qa[i].z, ka[j].z, acc[i][j]);
-          acc[i][j] = fmaf(qa[i].w, ka[j].w, acc[i][j]);
-        }
+    for (int i = 0; i < 4; ++i) {
+      ah[i] = *reinterpret_cast<const f16x8*>(&sq[0][(qb + 16 * i + n) * kS16Row + 8 * kg]);
+      al[i] = *reinterpret_cast<const f16x8*>(&sq[1][(qb + 16 * i + n) * kS16Row + 8 * kg]);
+      bh[i] = *reinterpret_cast<const f16x8*>(&st[0][(tb + 16 * i + n) * kS16Row + 8 * kg]);
+      bl[i] = *reinterpret_cast<const f16x8*>(&st[1][(tb + 16 * i + n) * kS16Row + 8 * kg]);
     }
-  }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int qi = q0 + 4 * ty + i;
-    if (qi >= A.n_queries) continue;
-    float* o = A.scores + ((int64_t)unit * A.n_queries + qi) * A.n_tokens + tok0 + tx;
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (tok0 + tx + 16 * j < A.n_tokens) o[16 * j] = acc[i][j];
+      for (int ct = 0; ct < 4; ++ct) {
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[rt], bh[ct], acc[rt][ct], 0, 0, 0);
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[rt], bl[ct], acc[rt][ct], 0, 0, 0);
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[rt], bh[ct], acc[rt][ct], 0, 0, 0);
+      }
+    __syncthreads();   // the next step restages sq / st
   }
+  // lane (n, kg) of tile (rt, ct) holds query qb + 16 rt + 4 kg + r against vector tb + 16 ct + n
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int qq = q0 + qb + 16 * rt + 4 * kg + r;
+      if (qq >= A.n_queries) continue;
+      const float qs = A.qscale[(int64_t)unit * A.n_queries + qq];
+      float* o = A.scores + ((int64_t)unit * A.n_queries + qq) * A.n_tokens;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int tl = tb + 16 * ct + n;
+        if (t0 + tl < A.n_tokens) o[t0 + tl] = acc[rt][ct][r] * qs * sts[tl];
+      }
+    }
 }
 
 // -----------------------------------------------------------------------------------------
@@ -4008,32 +4125,40 @@ hipError_t launch_scan(const Consts& c, const DevConsts& dc, const ScanPlan& pla
     ev.after(stream);
     return hipGetLastError();
   }
-  float* qprep = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + plan.ws_q);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint16_t* qh = reinterpret_cast<uint16_t*>(ws + plan.ws_q);
+  uint16_t* ql = reinterpret_cast<uint16_t*>(ws + plan.ws_ql);
+  float* qscale = reinterpret_cast<float*>(ws + plan.ws_qscale);
   const int rows = batch * heads * n_queries;
-  hipLaunchKernelGGL(scan_prep_kernel, dim3(rows), dim3(128), 0, stream, dc.pi, dc.s, c.d, c.m, q, q_dt, qprep);
-  ScanArgs a;
-  a.qprep = qprep;
+  hipLaunchKernelGGL(scan_prep_f16_kernel, dim3(rows), dim3(256), 0, stream, dc.pi, dc.s, c.d, c.m, plan.kp, q,
+                     q_dt, qh, ql, qscale);
+  Scan16Args a;
+  a.qh = qh;
+  a.ql = ql;
+  a.qscale = qscale;
   a.records = static_cast<const uint8_t*>(records);
   a.scores = scores;
   a.capacity = capacity;
   a.n_tokens = n_tokens;
   a.d = c.d;
   a.m = c.m;
+  a.kp = plan.kp;
   a.kb = c.kb;
   a.kbytes = c.kbytes;
   a.rec_bytes = c.rec_bytes;
   a.norm_off = c.norm_off;
-  a.heads = heads;
   a.n_queries = n_queries;
   a.inv_sqrt_d = c.inv_sqrt_d;
   a.qjl_coef = c.qjl_coef;
-  for (int i = 0; i < kMaxLevels; ++i) a.key_levels[i] = c.key_levels[i];
-  const size_t lds = (size_t)2 * kScanTile * (kScanSlab + 4) * 4;
-  dim3 grid((unsigned)((n_tokens + kScanTile - 1) / kScanTile), (unsigned)((n_queries + kScanTile - 1) / kScanTile),
+  a.gmax = 0.0f;
+  for (int i = 0; i < kMaxLevels; ++i) {
+    a.key_levels[i] = c.key_levels[i];
+    if (i < (1 << c.kb)) a.gmax = std::max(a.gmax, std::fabs(c.key_levels[i]));
+  }
+  dim3 grid((unsigned)((n_tokens + kS16Tile - 1) / kS16Tile), (unsigned)((n_queries + kS16Tile - 1) / kS16Tile),
             (unsigned)(batch * heads));
-  allow_lds(scan_kernel, lds);
   ev.before(stream);
-  hipLaunchKernelGGL(scan_kernel, grid, dim3(256), lds, stream, a);
+  hipLaunchKernelGGL(scan_mfma16_kernel, grid, dim3(256), 0, stream, a);
   ev.after(stream);
   return hipGetLastError();
 }
