@@ -569,7 +569,7 @@ def run_bulk_scan(args, tq, W, ev):
         # fp16 matrix-core products (hi.hi, hi.lo, lo.hi) of operands padded to 32-multiples
         flops = 2.0 * (d + w.qjl_dim) * B * H * nq * T
         kp = (d + w.qjl_dim + 31) // 32 * 32
-        executed = 3 * 2.0 * kp * B * H * (nq + 127) // 128 * 128 * (T + 127) // 128 * 128
+        executed = 3 * 2.0 * kp * B * H * (((nq + 127) // 128) * 128) * (((T + 127) // 128) * 128)
         tf = flops / (scan_ms * 1e-3) / 1e12
         tx = executed / (scan_ms * 1e-3) / 1e12
         hbm = line["roofline"]
