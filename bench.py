@@ -668,7 +668,7 @@ def cpu_baseline_monarch(w, h, snapshot, qs, ks, vs, window, budget_s: float = 8
     import numpy as np
     from threadpoolctl import threadpool_limits
     from oracle import monarch as MO
-    codec = _codec((w.head_dim, w.key_bits, w.qjl_dim, w.value_bits, w.seed * 3 + 1, w.seed * 3 + 2))
+    codec = _codec(codec_args_of(w))
     rec, hk, hv = snapshot
     o = MO.HotColdOracle(codec, w.batch, w.kv_heads, "float16", rec.shape[2])
     for b in range(w.batch):

