@@ -25,11 +25,11 @@ def _wl(kb=2, m=192, vb=2, tokens=3000, nq=64, d=200, dt="f32"):
                       scan_queries=nq, seed=BASE.seed)
 
 
-@pytest.mark.parametrize("kb,m,vb,dt", [(2, 192, 2, "f32"), (3, 0, 4, "bf16"), (4, 32, 3, "f16"),
-                                        (3, 256, 2, "f32")])
-def test_compress_head_dim_200(kb, m, vb, dt):
-    print(f"[case] d=200 compress kb={kb} m={m} vb={vb} {dt}", flush=True)
-    w = _wl(kb, m, vb, tokens=77, dt=dt)
+@pytest.mark.parametrize("kb,m,vb,dt,d", [(2, 192, 2, "f32", 200), (3, 0, 4, "bf16", 200), (4, 32, 3, "f16", 200),
+                                           (3, 256, 2, "f32", 200), (3, 32, 4, "f32", 40), (4, 256, 4, "bf16", 256)])
+def test_compress_head_dim_200(kb, m, vb, dt, d):
+    print(f"[case] d={d} compress kb={kb} m={m} vb={vb} {dt}", flush=True)
+    w = _wl(kb, m, vb, tokens=77, dt=dt, d=d)
     h = GP._handle(w)
     codec = GP._codec(h)
     assert h.record_bytes == codec.record_bytes
@@ -46,7 +46,8 @@ def _scan(w, h, rec, q, n_tokens):
     return scores.cpu().numpy()
 
 
-@pytest.mark.parametrize("kb,m,vb,d", [(2, 192, 2, 200), (3, 0, 4, 200), (4, 32, 3, 200), (3, 256, 4, 128)])
+@pytest.mark.parametrize("kb,m,vb,d", [(2, 192, 2, 200), (3, 0, 4, 200), (4, 32, 3, 200), (3, 256, 4, 128),
+                                        (3, 32, 4, 40), (4, 256, 4, 256)])
 def test_scan_head_dim_200_and_long_contractions(kb, m, vb, d):
     print(f"[case] scan d={d} kb={kb} m={m}", flush=True)
     w = _wl(kb, m, vb, tokens=1000, nq=70, d=d)
