@@ -977,10 +977,6 @@ tq_status tq_sparse_attention(const tq_handle* h, const void* q, tq_dtype q_dt, 
 
 tq_status tq_scan_workspace_size(const tq_handle* h, int32_t batch, int32_t kv_heads,
                                  int32_t n_queries, size_t* bytes) {
-  {
-    tq_status pst;
-    if (polar_unsupported(h, "the bulk scan", &pst)) return pst;
-  }
   if (!h || !bytes) return fail(TQ_ERR_INVALID_ARGUMENT, "NULL handle or output");
   if (batch < 0 || kv_heads <= 0 || n_queries < 0) return fail(TQ_ERR_INVALID_ARGUMENT, "bad shape");
   *bytes = tq::plan_scan(h->c, batch, kv_heads, n_queries).ws_total;
@@ -991,10 +987,6 @@ tq_status tq_score_scan(const tq_handle* h, const void* q, tq_dtype q_dt, int32_
                         int32_t kv_heads, int32_t n_queries, const void* records,
                         int64_t capacity, int64_t n_tokens, float* scores, void* workspace,
                         size_t ws_bytes, hipStream_t stream) {
-  {
-    tq_status pst;
-    if (polar_unsupported(h, "the bulk scan", &pst)) return pst;
-  }
   if (!h) return fail(TQ_ERR_INVALID_ARGUMENT, "handle is NULL");
   size_t es;
   if (!elem_size(q_dt, &es)) return fail(TQ_ERR_INVALID_ARGUMENT, "unknown query dtype");

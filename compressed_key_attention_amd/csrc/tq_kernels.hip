@@ -3638,7 +3638,7 @@ hipError_t launch_sparse(const Consts& c, const DevConsts& dc, const SparsePlan&
 // computes a 4 x 4 tile of scores.
 // =========================================================================================
 static bool scan_mfma_path(const Consts& c) {
-  return c.d == 128 && (c.kb == 2 || c.kb == 3) && (c.m == 0 || c.m == 128);
+  return !c.polar && c.d == 128 && (c.kb == 2 || c.kb == 3) && (c.m == 0 || c.m == 128);
 }
 
 ScanPlan plan_scan(const Consts& c, int batch, int heads, int n_queries) {
@@ -3665,9 +3665,13 @@ ScanPlan plan_scan(const Consts& c, int batch, int heads, int n_queries) {
 // sum |q_k t_k|; the two scales multiply the result.
 // Prep (one block per query row): q_x = Pi q and q_s = S q_x in float64, then the scaled fp16
 // hi / lo rows, zero-padded to kp (a multiple of 32), and the row scale.
+// The sketch part q_s (about sqrt(d) times the size of q_x's entries) is divided by sfix, a
+// power of two near sqrt(d), and the vectors' sign operands are multiplied by it, so both rows
+// keep entries of similar size and their fp16 lo halves stay clear of the subnormal range.
 __global__ __launch_bounds__(256) void scan_prep_f16_kernel(const float* __restrict__ pi, const float* __restrict__ s,
-                                                            int d, int m, int kp, const void* q, tq_dtype q_dt,
-                                                            uint16_t* qh, uint16_t* ql, float* qscale) {
+                                                            int d, int m, int kp, float sfix, const void* q,
+                                                            tq_dtype q_dt, uint16_t* qh, uint16_t* ql,
+                                                            float* qscale) {
   __shared__ double qv[256];
   __shared__ double xv[256];
   __shared__ float row[512];
@@ -3686,7 +3690,7 @@ __global__ __launch_bounds__(256) void scan_prep_f16_kernel(const float* __restr
   for (int k = threadIdx.x; k < m; k += blockDim.x) {
     double acc = 0.0;
     for (int i = 0; i < d; ++i) acc += (double)s[k * d + i] * xv[i];
-    row[d + k] = (float)acc;
+    row[d + k] = (float)acc / sfix;
   }
   __syncthreads();
   float mx = 0.0f;
@@ -3735,8 +3739,11 @@ struct Scan16Args {
   float* scores;
   int64_t capacity, n_tokens;
   int d, m, kp, kb, kbytes, rec_bytes, norm_off, n_queries;
-  float inv_sqrt_d, qjl_coef, gmax;
+  float inv_sqrt_d, qjl_coef, gmax, sfix;
   float key_levels[kMaxLevels];
+  // polar keys: cos / sin of the grids [8][16][2] (float64), code widths, levels, level-1 stream bytes
+  const double* pcs;
+  int pb1, pbh, plevels, l1_bytes;
 };
 
 // 128 queries x 128 vectors per workgroup; wave w computes queries 64 (w / 2) .. + 63 against
@@ -3747,11 +3754,20 @@ struct Scan16Args {
 // per-code constants: pairs of codes index tables of packed fp16 hi (and lo) pairs.  Its sign
 // operands are +-coef rho / scale: one fp16 hi / lo pair per vector, the sign bit flipped by
 // the QJL bit.
+// POLAR: a vector's scale is r_k and its key operands are the unit vector u of its grid
+// angles; the thread staging 16 coordinates (the subtree of one level-4 node) takes the
+// subtree root's scale from its ancestors' cos / sin and rebuilds the 16 coordinates top-down
+// in float64 (unscaled estimates carry r_k |q|, so float32 products of up to seven table
+// entries would cost ~1e-4 absolute), rounded once to float32 before the split.
+template <bool POLAR>
 __global__ __launch_bounds__(256, 2) void scan_mfma16_kernel(Scan16Args A) {
   __shared__ __attribute__((aligned(16))) uint16_t sq[2][kS16Tile * kS16Row];
   __shared__ __attribute__((aligned(16))) uint16_t st[2][kS16Tile * kS16Row];
   __shared__ float sts[kS16Tile];
   __shared__ uint32_t ptab[2][256];    // code pair (c0 | c1 << kb) -> packed fp16 hi / lo pair
+  __shared__ double2 pcs[POLAR ? kMaxPolarLevels * 16 : 1];
+  if (POLAR && threadIdx.x < kMaxPolarLevels * 16)
+    pcs[threadIdx.x] = make_double2(A.pcs[2 * threadIdx.x], A.pcs[2 * threadIdx.x + 1]);
   const int unit = blockIdx.z;
   const int64_t t0 = (int64_t)blockIdx.x * kS16Tile;
   const int q0 = blockIdx.y * kS16Tile;
@@ -3777,8 +3793,8 @@ __global__ __launch_bounds__(256, 2) void scan_mfma16_kernel(Scan16Args A) {
   const uint8_t* rec = A.records + ((int64_t)unit * A.capacity + (tv ? t : 0)) * A.rec_bytes;
   const float* nrm = reinterpret_cast<const float*>(rec + A.norm_off);
   const float ak = tv ? nrm[0] * A.inv_sqrt_d : 0.0f, aq = tv ? A.qjl_coef * nrm[1] : 0.0f;
-  const float tsc = ak * A.gmax;                       // 0 for an invalid or zero vector (then aq = 0)
-  const float sv = tsc > 0.0f ? aq / tsc : 0.0f;
+  const float tsc = POLAR ? (tv ? nrm[0] : 0.0f) : ak * A.gmax;   // 0 for an invalid or zero vector (then aq = 0)
+  const float sv = tsc > 0.0f ? aq * A.sfix / tsc : 0.0f;
   uint32_t sgh, sgl;                                   // +sv as an fp16 hi / lo pair in both halves
   {
     const _Float16 h = (_Float16)sv;
@@ -3822,6 +3838,50 @@ __global__ __launch_bounds__(256, 2) void scan_mfma16_kernel(Scan16Args A) {
       dl[1] = l1;
       // 8 operand pairs (c0 + 2 e2, + 1); d and K are even, so a pair never mixes regions
       uint32_t hw[8], lw[8];
+      float pu[16];                                   // polar: the subtree's unit-vector coordinates
+      if (POLAR && c0 < A.d) {
+        const int bh = A.pbh, b1 = A.pb1, d = A.d;
+        const uint32_t mh = (1u << bh) - 1u;
+        auto up_code = [&](int l, int node) -> uint32_t {
+          const int bit = (d / 2 - (d >> (l - 1)) + node) * bh;
+          return (*reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(kw) + A.l1_bytes +
+                                                     4 * (bit >> 5)) >> (bit & 31)) & mh;
+        };
+        double sc = 1.0;
+#pragma unroll
+        for (int l = kMaxPolarLevels - 1; l >= 5; --l) {
+          if (l <= A.plevels) {
+            const double2 tc = pcs[(l - 1) * 16 + up_code(l, c0 >> l)];
+            sc *= ((c0 >> (l - 1)) & 1) ? tc.y : tc.x;
+          }
+        }
+        double s3[2], s2[4], s1[8];
+        {
+          const double2 tc = pcs[3 * 16 + up_code(4, c0 >> 4)];
+          s3[0] = sc * tc.x;
+          s3[1] = sc * tc.y;
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const double2 tc = pcs[2 * 16 + up_code(3, (c0 >> 3) + i)];
+          s2[2 * i] = s3[i] * tc.x;
+          s2[2 * i + 1] = s3[i] * tc.y;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const double2 tc = pcs[16 + up_code(2, (c0 >> 2) + i)];
+          s1[2 * i] = s2[i] * tc.x;
+          s1[2 * i + 1] = s2[i] * tc.y;
+        }
+        const int b0 = (c0 >> 1) * b1;                // the 8 level-1 codes: one run of 16 or 32 bits
+        const uint32_t w1 = kw[b0 >> 5] >> (b0 & 31);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const double2 tc = pcs[(w1 >> (b1 * i)) & ((1u << b1) - 1u)];
+          pu[2 * i] = (float)(s1[i] * tc.x);
+          pu[2 * i + 1] = (float)(s1[i] * tc.y);
+        }
+      }
       const bool plain = kb != 3 && c0 + 16 <= A.d;   // 16 key codes of 2 or 4 bits: one run of bits
       uint32_t kr0 = 0u, kr1 = 0u;
       if (plain) {
@@ -3833,7 +3893,13 @@ __global__ __launch_bounds__(256, 2) void scan_mfma16_kernel(Scan16Args A) {
       for (int e2 = 0; e2 < 8; ++e2) {
         const int k = c0 + 2 * e2;
         uint32_t hp = 0u, lp = 0u;
-        if (k < A.d) {
+        if (POLAR && k < A.d) {
+          const float v0 = pu[2 * e2], v1 = pu[2 * e2 + 1];
+          const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
+          const _Float16 r0 = (_Float16)(v0 - (float)h0), r1 = (_Float16)(v1 - (float)h1);
+          hp = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+          lp = (uint32_t)__builtin_bit_cast(uint16_t, r0) | ((uint32_t)__builtin_bit_cast(uint16_t, r1) << 16);
+        } else if (k < A.d) {
           uint32_t pidx;
           if (plain) {
             const int sh = 2 * kb * e2;                 // < 32 for kb = 2; kb = 4: words of 4 pairs
@@ -4130,8 +4196,9 @@ hipError_t launch_scan(const Consts& c, const DevConsts& dc, const ScanPlan& pla
   uint16_t* ql = reinterpret_cast<uint16_t*>(ws + plan.ws_ql);
   float* qscale = reinterpret_cast<float*>(ws + plan.ws_qscale);
   const int rows = batch * heads * n_queries;
-  hipLaunchKernelGGL(scan_prep_f16_kernel, dim3(rows), dim3(256), 0, stream, dc.pi, dc.s, c.d, c.m, plan.kp, q,
-                     q_dt, qh, ql, qscale);
+  const float sfix = std::ldexp(1.0f, (int)std::lround(0.5 * std::log2((double)c.d)));   // ~sqrt(d)
+  hipLaunchKernelGGL(scan_prep_f16_kernel, dim3(rows), dim3(256), 0, stream, dc.pi, dc.s, c.d, c.m, plan.kp, sfix,
+                     q, q_dt, qh, ql, qscale);
   Scan16Args a;
   a.qh = qh;
   a.ql = ql;
@@ -4151,6 +4218,7 @@ hipError_t launch_scan(const Consts& c, const DevConsts& dc, const ScanPlan& pla
   a.inv_sqrt_d = c.inv_sqrt_d;
   a.qjl_coef = c.qjl_coef;
   a.gmax = 0.0f;
+  a.sfix = sfix;
   for (int i = 0; i < kMaxLevels; ++i) {
     a.key_levels[i] = c.key_levels[i];
     if (i < (1 << c.kb)) a.gmax = std::max(a.gmax, std::fabs(c.key_levels[i]));
@@ -4158,7 +4226,15 @@ hipError_t launch_scan(const Consts& c, const DevConsts& dc, const ScanPlan& pla
   dim3 grid((unsigned)((n_tokens + kS16Tile - 1) / kS16Tile), (unsigned)((n_queries + kS16Tile - 1) / kS16Tile),
             (unsigned)(batch * heads));
   ev.before(stream);
-  hipLaunchKernelGGL(scan_mfma16_kernel, grid, dim3(256), 0, stream, a);
+  a.pcs = dc.polar.cs64;
+  a.pb1 = c.pb1;
+  a.pbh = c.pbh;
+  a.plevels = c.plevels;
+  a.l1_bytes = c.l1_bytes;
+  if (c.polar)
+    hipLaunchKernelGGL(scan_mfma16_kernel<true>, grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(scan_mfma16_kernel<false>, grid, dim3(256), 0, stream, a);
   ev.after(stream);
   return hipGetLastError();
 }

@@ -130,7 +130,7 @@ def make_kv(w: Workload, device="cpu", tokens: int | None = None, batch: int | N
     for b in range(B):
         for X, which in ((K, 0), (V, 1)):
             g = generator(w.seed * 1_000_003 + 2 * b + which + seed_offset, device)
-            if w.name == "llama8b_decode_32k":
+            if w.name in ("llama8b_decode_32k", "llama8b_decode_32k_polar"):
                 x = student_t4(shape, g, device)
             elif w.name == "vector_search_d200":
                 x = mu.to(device) + sigma.to(device) * normal(shape, g, device)

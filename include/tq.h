@@ -32,9 +32,9 @@
  *  - A handle is immutable after tq_create, so concurrent calls on different streams
  *    are allowed.  Calls that share a workspace or output buffer must be ordered.
  *  - A TQ_KEY_POLAR handle is accepted by tq_compress_kv, tq_decode_workspace_size,
- *    tq_decode_attention, tq_record_bytes and the sign-index / top-k calls (which read
- *    raw keys); tq_debug_quantize, tq_score_scan, tq_sparse_attention and the hot/cold
- *    step return TQ_ERR_UNSUPPORTED for it.
+ *    tq_decode_attention, tq_scan_workspace_size, tq_score_scan, tq_record_bytes and the
+ *    sign-index / top-k calls (which read raw keys); tq_debug_quantize,
+ *    tq_sparse_attention and the hot/cold step return TQ_ERR_UNSUPPORTED for it.
  *  - Inputs must be finite.  Non-finite inputs give unspecified codes and outputs but
  *    never an out-of-bounds access.
  *
@@ -247,8 +247,11 @@ tq_status tq_sparse_attention(const tq_handle* h, const void* q, tq_dtype q_dt, 
 
 /* Bulk scan (TurboQuant page, "Leistung bei der Vektorsuche"): for q[b][h][i][d]
  * (i < n_queries) and every slot t < n_tokens of records[b][h], scores[b][h][i][t] =
- * s_t as in tq_decode_attention (unscaled estimate, no softmax).  float32 output.
- * workspace: tq_scan_workspace_size bytes. */
+ * s_t as in tq_decode_attention (unscaled estimate, no softmax; polar keys included).
+ * float32 output.  At head_dim 128 with 2/3-bit scalar keys and m in {0, 128} the products
+ * are exact int32 limb products; elsewhere fp16 hi + lo matrix-core products of operands
+ * scaled to their row maxima (error ~2^-22 of sum_k |q_k t_k|).  workspace:
+ * tq_scan_workspace_size bytes. */
 tq_status tq_scan_workspace_size(const tq_handle* h, int32_t batch, int32_t kv_heads,
                                  int32_t n_queries, size_t* bytes);
 tq_status tq_score_scan(const tq_handle* h, const void* q, tq_dtype q_dt, int32_t batch,

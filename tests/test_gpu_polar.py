@@ -128,12 +128,29 @@ def test_polar_decode_gather_mode():
     GP._decode_case(w, [900, 900], sel=sel)
 
 
+@pytest.mark.parametrize("d,b1,bh,m,vb", [(128, 4, 2, 128, 4), (64, 2, 1, 0, 2), (128, 4, 4, 32, 3),
+                                          (128, 2, 2, 0, 4)])
+def test_polar_bulk_scan(d, b1, bh, m, vb):
+    """Bulk scan over polar records (fp16 hi / lo matrix-core path) against the oracle's
+    estimates, ragged in queries and tokens."""
+    print(f"[case] polar scan d={d} b1={b1} bh={bh} m={m}", flush=True)
+    w = W.Workload("llama8b_decode_32k_polar", 1, 2, 2, d, 1000, 0, b1, m, vb, "bf16", "bf16",
+                   scan_queries=37, seed=606, polar_upper_bits=bh)
+    h = GP._handle(w)
+    codec = GP._codec(h)
+    K, V = W.make_kv(w, "cuda")
+    rec = GP._compress(w, h, K, V)
+    q = W.make_queries(w, "cuda")
+    scores = torch.full((1, 2, 37, 997), float("nan"), device="cuda")
+    h.score_scan(q, rec, 997, scores)
+    torch.cuda.synchronize()
+    ref = O.score_scan(codec, GP._np(q), rec.cpu().numpy(), 997)
+    GP._close(scores.cpu().numpy(), ref, "polar scan estimates")
+
+
 def test_polar_rejected_where_not_built():
     tq = GP._tq()
     h = GP._handle(_wl(tokens=16, batch=1))
-    with pytest.raises(tq.TqError) as e:
-        h.scan_workspace_size(1, 8, 16)
-    assert e.value.status == tq.TQ_ERR_UNSUPPORTED
     with pytest.raises(tq.TqError) as e:
         h.sparse_workspace_size(1, 8, 8, 4096)
     assert e.value.status == tq.TQ_ERR_UNSUPPORTED
