@@ -97,7 +97,12 @@ def decode_kernel_name(w) -> str:
     else:
         mfma = (w.head_dim == 128 and w.q_heads == 4 * w.kv_heads and w.value_bits == 4
                 and w.key_bits in (2, 3) and w.qjl_dim in (0, 128))
-    return "decode_mfma_kernel" if mfma else "decode_scan_kernel"
+    if mfma:
+        return "decode_mfma_kernel"
+    G = w.q_heads // w.kv_heads
+    small = (not w.polar_upper_bits and w.tokens <= 4096 and 4 <= G <= 16 and w.qjl_dim <= 128
+             and w.qjl_dim % 32 == 0 and w.head_dim in (64, 128))
+    return "decode_small_kernel" if small else "decode_scan_kernel"
 
 
 def record_payload_bytes(w) -> int:
@@ -653,7 +658,7 @@ def run_monarch(args, tq, W, ev):
                            "promote_weight": 0.15, "promote_steps": 3, "ring_dtype": "f16"})
     rec_alg = record_payload_bytes(w)
     alg = rec_alg * w.batch * H * (w.tokens + args.warmup + args.steps // 2)
-    line["roofline"] = roofline("decode_scan_kernel", "monarch_tinyllama", alg, scan_ms,
+    line["roofline"] = roofline(decode_kernel_name(w), "monarch_tinyllama", alg, scan_ms,
                                 {"note": "latency-bound: the step is ~7 small launches; report us/step"})
     line["us_per_step"] = ms_per_step * 1e3
     line["state_after"] = {"hot_len": int(st.hot_len[0]), "cold_len": int(st.cold_len[0]),
