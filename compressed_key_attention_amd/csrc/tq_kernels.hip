@@ -368,7 +368,7 @@ __device__ __forceinline__ void polar_pack(const uint8_t* codes, int d, int b1, 
   }
 }
 
-template <int D>
+template <int D, bool POLAR>
 __global__ __launch_bounds__(256) void compress_kernel(CompressArgs A) {
   constexpr int Q = D / 4, CT = D / 16;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -430,7 +430,7 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs A) {
     const double zs = r > 0.0 ? c.sqrt_d / r : 0.0;
     const double a = (double)r32 / c.sqrt_d;
     uint8_t* pcodes = codes_all + ((size_t)wave * 16 + tok) * D;
-    if (c.polar)
+    if constexpr (POLAR)
       polar_encode<D>(x, (double)r32, A.polar, c.pb1, c.pbh, pcodes, g);
     else
       quantize_rotated<D>(x, zs, a, lds_tab, lds_tab + kMaxLevels, c.kb, rec, g, true);
@@ -490,7 +490,7 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs A) {
     } else if (g == 1) {
       for (int i = c.norm_off + 12; i < c.rec_bytes; ++i) rec[i] = 0;
     }
-    if (c.polar) {
+    if constexpr (POLAR) {
       wave_lds_sync();
       polar_pack(pcodes, D, c.pb1, c.pbh, c.l1_bytes, c.kbytes, rec, g);
     }
@@ -672,13 +672,16 @@ hipError_t launch_compress(const Consts& c, const DevConsts& dc, const void* k, 
   int64_t blocks = (A.n_tiles + nwaves - 1) / nwaves;
   blocks = std::min<int64_t>(blocks, (int64_t)num_cus());
   ev.before(stream);
-  if (c.d == 128) {
-    allow_lds(compress_kernel<128>, lds);
-    hipLaunchKernelGGL(compress_kernel<128>, dim3((unsigned)blocks), dim3(threads), lds, stream, A);
-  } else {
-    allow_lds(compress_kernel<64>, lds);
-    hipLaunchKernelGGL(compress_kernel<64>, dim3((unsigned)blocks), dim3(threads), lds, stream, A);
+#define TQ_COMPRESS(D_, P_)                                                                      \
+  {                                                                                              \
+    allow_lds(compress_kernel<D_, P_>, lds);                                                     \
+    hipLaunchKernelGGL((compress_kernel<D_, P_>), dim3((unsigned)blocks), dim3(threads), lds, stream, A); \
   }
+  if (c.d == 128 && c.polar) TQ_COMPRESS(128, true)
+  else if (c.d == 128) TQ_COMPRESS(128, false)
+  else if (c.polar) TQ_COMPRESS(64, true)
+  else TQ_COMPRESS(64, false)
+#undef TQ_COMPRESS
   ev.after(stream);
   return hipGetLastError();
 }
