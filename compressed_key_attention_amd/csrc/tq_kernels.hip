@@ -547,84 +547,132 @@ __device__ __forceinline__ void pack_code_field(const uint8_t* codes, int d, int
   }
 }
 
+// A wave compresses kGenTok consecutive tokens of one (sequence, head) together: every Pi^T or
+// S^T entry it loads feeds one FMA per token, and the tokens' inputs sit side by side in LDS
+// ([coordinate][token]), so one 16- or 32-byte LDS read serves all of them.
+constexpr int kGenTok = 4;
+
 __global__ __launch_bounds__(256) void compress_generic_kernel(CompressArgs A) {
   const Consts& c = A.c;
-  __shared__ double vin[4][kGenMaxD];
-  __shared__ uint8_t cb[4][kGenMaxD];
-  __shared__ uint32_t rw[4][kGenRecWords];
+  __shared__ __attribute__((aligned(16))) double vin[4][kGenMaxD][kGenTok];
+  __shared__ uint8_t cb[4][kGenTok][kGenMaxD];
+  __shared__ uint32_t rw[4][kGenTok][kGenRecWords];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int d = c.d, m = c.m, nrw = c.rec_bytes / 4;
+  const int64_t tiles_per_bh = (A.n_tokens + kGenTok - 1) / kGenTok;
   for (int64_t item = (int64_t)blockIdx.x * 4 + wave; item < A.n_tiles; item += (int64_t)gridDim.x * 4) {
-    const int64_t bh = item / A.n_tokens, t = item % A.n_tokens;
+    const int64_t bh = item / tiles_per_bh, t0 = (item % tiles_per_bh) * kGenTok;
     const int64_t b = bh / A.heads;
     const int h = (int)(bh % A.heads);
-    const int64_t row = b * A.seq_stride + t * A.tok_stride + h * A.head_stride;
-    for (int w = lane; w < nrw; w += 64) rw[wave][w] = 0u;
-    float norms[3] = {0.0f, 0.0f, 0.0f};
+    const int ntok = (int)min((int64_t)kGenTok, A.n_tokens - t0);
+    for (int w = lane; w < kGenTok * nrw; w += 64) rw[wave][w / nrw][w % nrw] = 0u;
+    float norms[kGenTok][3];
     for (int pass = 0; pass < 2; ++pass) {
       const void* src = pass == 0 ? A.k : A.v;
-      for (int i = lane; i < d; i += 64) vin[wave][i] = (double)load_elem(src, A.dt, row + i);
+      for (int e = lane; e < kGenTok * d; e += 64) {
+        const int tt = e / d, i = e % d;
+        const int64_t row = b * A.seq_stride + (t0 + tt) * A.tok_stride + h * A.head_stride;
+        vin[wave][i][tt] = tt < ntok ? (double)load_elem(src, A.dt, row + i) : 0.0;
+      }
       wave_lds_sync();
-      double n2 = 0.0;
-      for (int i = lane; i < d; i += 64) n2 += vin[wave][i] * vin[wave][i];
-      for (int o = 32; o >= 1; o >>= 1) n2 += __shfl_xor(n2, o);
-      const double r = sqrt(n2);
-      const float r32 = (float)r;
-      const double zs = r > 0.0 ? c.sqrt_d / r : 0.0;
-      const double a = (double)r32 / c.sqrt_d;
+      double zs[kGenTok], a[kGenTok];
+      float r32[kGenTok];
+#pragma unroll
+      for (int tt = 0; tt < kGenTok; ++tt) {
+        double n2 = 0.0;
+        for (int i = lane; i < d; i += 64) n2 += vin[wave][i][tt] * vin[wave][i][tt];
+        for (int o = 32; o >= 1; o >>= 1) n2 += __shfl_xor(n2, o);
+        const double r = sqrt(n2);
+        r32[tt] = (float)r;
+        zs[tt] = r > 0.0 ? c.sqrt_d / r : 0.0;
+        a[tt] = (double)r32[tt] / c.sqrt_d;
+      }
       const float* bounds = pass == 0 ? c.key_bounds : c.val_bounds;
       const float* levels = pass == 0 ? c.key_levels : c.val_levels;
-      double e[kGenMaxD / 64];
+      double e[kGenMaxD / 64][kGenTok];
 #pragma unroll
       for (int j = 0; j < kGenMaxD / 64; ++j) {
         const int i = lane + 64 * j;
-        e[j] = 0.0;
+#pragma unroll
+        for (int tt = 0; tt < kGenTok; ++tt) e[j][tt] = 0.0;
         if (i < d) {
-          double x = 0.0;
-          for (int jj = 0; jj < d; ++jj) x = fma((double)A.pi_t[(size_t)jj * d + i], vin[wave][jj], x);
-          const uint32_t code = quantize_code((float)(x * zs), bounds);
-          cb[wave][i] = (uint8_t)code;
-          e[j] = x - a * (double)levels[code];
+          double x[kGenTok] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+          for (int jj = 0; jj < d; ++jj) {
+            const double p = (double)A.pi_t[(size_t)jj * d + i];
+            const double4 v = *reinterpret_cast<const double4*>(&vin[wave][jj][0]);
+            x[0] = fma(p, v.x, x[0]);
+            x[1] = fma(p, v.y, x[1]);
+            x[2] = fma(p, v.z, x[2]);
+            x[3] = fma(p, v.w, x[3]);
+          }
+#pragma unroll
+          for (int tt = 0; tt < kGenTok; ++tt) {
+            const uint32_t code = quantize_code((float)(x[tt] * zs[tt]), bounds);
+            cb[wave][tt][i] = (uint8_t)code;
+            e[j][tt] = x[tt] - a[tt] * (double)levels[code];
+          }
         }
       }
       wave_lds_sync();   // every lane is done reading vin and has written its codes
       const int fofs = pass == 0 ? 0 : (c.kbytes + c.sbytes) / 4;
-      pack_code_field(cb[wave], d, pass == 0 ? c.kb : c.vb, rw[wave] + fofs, lane);
-      norms[pass == 0 ? 0 : 2] = r32;
+      for (int tt = 0; tt < kGenTok; ++tt) {
+        pack_code_field(cb[wave][tt], d, pass == 0 ? c.kb : c.vb, rw[wave][tt] + fofs, lane);
+        norms[tt][pass == 0 ? 0 : 2] = r32[tt];
+      }
       if (pass == 0) {
-        double e2 = 0.0;
 #pragma unroll
-        for (int j = 0; j < kGenMaxD / 64; ++j) {
-          const int i = lane + 64 * j;
-          if (i < d) {
-            vin[wave][i] = e[j];
-            e2 += e[j] * e[j];
+        for (int tt = 0; tt < kGenTok; ++tt) {
+          double e2 = 0.0;
+#pragma unroll
+          for (int j = 0; j < kGenMaxD / 64; ++j) {
+            const int i = lane + 64 * j;
+            if (i < d) {
+              vin[wave][i][tt] = e[j][tt];
+              e2 += e[j][tt] * e[j][tt];
+            }
           }
+          for (int o = 32; o >= 1; o >>= 1) e2 += __shfl_xor(e2, o);
+          norms[tt][1] = (float)sqrt(e2);
         }
-        for (int o = 32; o >= 1; o >>= 1) e2 += __shfl_xor(e2, o);
-        norms[1] = (float)sqrt(e2);
         wave_lds_sync();
         for (int k0 = 0; k0 < m; k0 += 64) {
           const int k = k0 + lane;
-          bool bit = false;
+          double p[kGenTok] = {0.0, 0.0, 0.0, 0.0};
           if (k < m) {
-            double p = 0.0;
-            for (int i = 0; i < d; ++i) p = fma((double)A.s_t[(size_t)i * m + k], vin[wave][i], p);
-            bit = (float)p >= 0.0f;
+#pragma unroll 4
+            for (int i = 0; i < d; ++i) {
+              const double sv = (double)A.s_t[(size_t)i * m + k];
+              const double4 v = *reinterpret_cast<const double4*>(&vin[wave][i][0]);
+              p[0] = fma(sv, v.x, p[0]);
+              p[1] = fma(sv, v.y, p[1]);
+              p[2] = fma(sv, v.z, p[2]);
+              p[3] = fma(sv, v.w, p[3]);
+            }
           }
-          const uint64_t bal = __ballot(bit);
-          if (lane == 0) {
-            rw[wave][c.kbytes / 4 + k0 / 32] = (uint32_t)bal;
-            if (k0 + 32 < m) rw[wave][c.kbytes / 4 + k0 / 32 + 1] = (uint32_t)(bal >> 32);
+#pragma unroll
+          for (int tt = 0; tt < kGenTok; ++tt) {
+            const uint64_t bal = __ballot(k < m && (float)p[tt] >= 0.0f);
+            if (lane == 0) {
+              rw[wave][tt][c.kbytes / 4 + k0 / 32] = (uint32_t)bal;
+              if (k0 + 32 < m) rw[wave][tt][c.kbytes / 4 + k0 / 32 + 1] = (uint32_t)(bal >> 32);
+            }
           }
         }
       }
       wave_lds_sync();   // vin is reloaded by the next pass
     }
-    if (lane < 3) rw[wave][c.norm_off / 4 + lane] = __float_as_uint(norms[lane]);
+#pragma unroll
+    for (int tt = 0; tt < kGenTok; ++tt)
+#pragma unroll
+      for (int f = 0; f < 3; ++f)
+        if (lane == 3 * tt + f) rw[wave][tt][c.norm_off / 4 + f] = __float_as_uint(norms[tt][f]);
     wave_lds_sync();
-    uint32_t* dst = reinterpret_cast<uint32_t*>(A.records + (bh * A.capacity + A.first_slot + t) * c.rec_bytes);
-    for (int w = lane; w < nrw; w += 64) dst[w] = rw[wave][w];
+    for (int e2 = lane; e2 < ntok * nrw; e2 += 64) {
+      const int tt = e2 / nrw, w = e2 % nrw;
+      uint32_t* dst = reinterpret_cast<uint32_t*>(A.records + (bh * A.capacity + A.first_slot + t0 + tt) * c.rec_bytes);
+      dst[w] = rw[wave][tt][w];
+    }
     wave_lds_sync();   // rw is cleared for the next item
   }
 }
@@ -655,7 +703,7 @@ hipError_t launch_compress(const Consts& c, const DevConsts& dc, const void* k, 
   A.pi_t = dc.pi_t;
   A.s_t = dc.s_t;
   if (c.d != 64 && c.d != 128) {
-    A.n_tiles = (int64_t)batch * heads * n_tokens;     // one wave per token-head
+    A.n_tiles = (int64_t)batch * heads * ((n_tokens + kGenTok - 1) / kGenTok);   // one wave per kGenTok tokens
     const int64_t blocks = std::min<int64_t>((A.n_tiles + 3) / 4, (int64_t)num_cus() * 8);
     ev.before(stream);
     if (blocks > 0)
