@@ -134,11 +134,21 @@ struct SparsePlan {
   size_t ws_select, ws_qx, ws_qs, ws_part, ws_total;
 };
 SparsePlan plan_sparse(const Consts& c, int batch, int q_heads, int kv_heads, int64_t capacity);
+// Query prep (q_x = Pi q, q_s = S q_x for `rows` query rows) that launch_select may run in the
+// same launch as its table build.
+struct QueryPrep {
+  const float* pi;
+  const float* s;
+  int m, rows;
+  float* qx;
+  float* qs;
+};
 hipError_t launch_select(const Consts& c, const SelectPlan& plan, const void* q, tq_dtype q_dt,
                          int batch, int q_heads, int kv_heads, const void* index,
                          const float* codebook, int64_t capacity, const int32_t* seq_lens,
                          int k, int32_t* out_idx, int32_t* out_count, int32_t* out_scores,
-                         void* workspace, hipStream_t stream, const ProfileEvents& ev);
+                         void* workspace, hipStream_t stream, const ProfileEvents& ev,
+                         const QueryPrep* prep = nullptr);
 hipError_t launch_sparse(const Consts& c, const DevConsts& dc, const SparsePlan& plan, const void* q,
                          tq_dtype q_dt, int batch, int q_heads, int kv_heads, const void* index,
                          const float* codebook, const void* records, int64_t capacity,

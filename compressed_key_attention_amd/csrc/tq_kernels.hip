@@ -778,28 +778,58 @@ hipError_t launch_debug_quantize(const Consts& c, const float* z_k, const float*
 }
 
 // =========================================================================================
-// Decode attention.  Query prep: q_x = Pi q, q_s = S q_x in float64 (one block per query).
+// Decode attention.  Query prep: q_x = Pi q, q_s = S q_x in float64 (one block of 256 threads
+// per query).
 // =========================================================================================
-__global__ void query_prep_kernel(const float* __restrict__ pi, const float* __restrict__ s, int d,
-                                  int m, const void* q, tq_dtype q_dt, float* qx_out,
-                                  float* qs_out) {
+// y_i = sum_j M[i][j] v_j for i < rows (M float32 row-major [rows][d], v float64 in LDS, d a
+// multiple of 4), by a block of 256 threads: output i of a pass of 32 rows is summed by eight
+// adjacent lanes, lane ks taking columns 32 jj + 4 ks .. + 3, so that the eight read whole
+// 128-byte lines of the row; the partial sums are combined by shuffles and lane ks = 0 calls
+// out(i, y_i).
+template <typename F>
+__device__ __forceinline__ void block_gemv_f64(const float* __restrict__ M, const double* v, int rows, int d,
+                                               F&& out) {
+  const int ks = threadIdx.x & 7, r0 = threadIdx.x >> 3;
+  for (int i0 = 0; i0 < rows; i0 += 32) {
+    const int i = i0 + r0;
+    double acc = 0.0;
+    if (i < rows) {
+#pragma unroll 4
+      for (int c = 4 * ks; c < d; c += 32) {
+        const float4 w = *reinterpret_cast<const float4*>(M + (int64_t)i * d + c);
+        acc = fma((double)w.x, v[c], acc);
+        acc = fma((double)w.y, v[c + 1], acc);
+        acc = fma((double)w.z, v[c + 2], acc);
+        acc = fma((double)w.w, v[c + 3], acc);
+      }
+    }
+#pragma unroll
+    for (int msk = 1; msk < 8; msk <<= 1) acc += __shfl_xor(acc, msk);
+    if (ks == 0 && i < rows) out(i, acc);
+  }
+}
+
+constexpr int kQueryPrepThreads = 256;
+__device__ __forceinline__ void query_prep_block(const float* __restrict__ pi, const float* __restrict__ s, int d,
+                                                 int m, const void* q, tq_dtype q_dt, float* qx_out,
+                                                 float* qs_out, int64_t row) {
   __shared__ double qv[256];
   __shared__ double xv[256];
-  const int64_t row = blockIdx.x;  // flattened (b, h)
   for (int i = threadIdx.x; i < d; i += blockDim.x) qv[i] = (double)load_elem(q, q_dt, row * d + i);
   __syncthreads();
-  for (int i = threadIdx.x; i < d; i += blockDim.x) {
-    double acc = 0.0;
-    for (int j = 0; j < d; ++j) acc += (double)pi[i * d + j] * qv[j];
-    xv[i] = acc;
-    qx_out[row * d + i] = (float)acc;
-  }
+  block_gemv_f64(pi, qv, d, d, [&](int i, double y) {
+    xv[i] = y;
+    qx_out[row * d + i] = (float)y;
+  });
   __syncthreads();
-  for (int k = threadIdx.x; k < m; k += blockDim.x) {
-    double acc = 0.0;
-    for (int i = 0; i < d; ++i) acc += (double)s[k * d + i] * xv[i];
-    qs_out[row * m + k] = (float)acc;
-  }
+  block_gemv_f64(s, xv, m, d, [&](int k, double y) { qs_out[row * m + k] = (float)y; });
+}
+
+__global__ __launch_bounds__(kQueryPrepThreads) void query_prep_kernel(const float* __restrict__ pi,
+                                                                       const float* __restrict__ s, int d, int m,
+                                                                       const void* q, tq_dtype q_dt,
+                                                                       float* qx_out, float* qs_out) {
+  query_prep_block(pi, s, d, m, q, q_dt, qx_out, qs_out, blockIdx.x);   // row = flattened (b, h)
 }
 
 // -----------------------------------------------------------------------------------------
@@ -1528,6 +1558,30 @@ __global__ __launch_bounds__(kPrepThreads) void mfma_prep_kernel(const float* __
     }
   }
   __syncthreads();
+  // the three int8 limbs of every fixed-point query coordinate and sketch coordinate, formed
+  // once and packed as bytes (l2, l1, l0, 0); coordinate i of head h at h LS + i + i / 32, so
+  // that the 16 (head, K slice) addresses of an operand read below fall on distinct banks.
+  // A sketch coordinate c carries its in-place bit weight s = c % 8 (decode).
+  constexpr int LS = D + 4;
+  __shared__ uint32_t klimb[POLAR ? 1 : G * LS], jlimb[QJL ? G * LS : 1];
+  if constexpr (!POLAR || QJL) {
+    const int h = (threadIdx.x >> 7) & 3, i = threadIdx.x & 127, at = h * LS + i + (i >> 5);
+    int l2, l1, l0;
+    if (threadIdx.x < G * D) {
+      if constexpr (!POLAR) {
+        int8_limbs3((int)rintf(xf[h][i] * s_fq[h]), l2, l1, l0);
+        klimb[at] = (uint32_t)(l2 & 0xFF) | (uint32_t)(l1 & 0xFF) << 8 | (uint32_t)(l0 & 0xFF) << 16;
+      }
+    } else if (QJL) {
+      const int s = i & 7;
+      const float sv = sf[h][i] * s_fs[h];
+      const int qv = SCAN ? (int)rintf(sv) : s == 7 ? -(int)rintf(sv * 0.0078125f)
+                                                     : (int)rintf(sv * (1.0f / (float)(1 << s)));
+      int8_limbs3(qv, l2, l1, l0);
+      jlimb[at] = (uint32_t)(l2 & 0xFF) | (uint32_t)(l1 & 0xFF) << 8 | (uint32_t)(l0 & 0xFF) << 16;
+    }
+    __syncthreads();
+  }
   // operand words (A of the score products): lane L = (row n = L % 16, K slice kg = L / 16),
   // head n / 4, part n % 4.
   //  code word (j, w): byte k <-> coordinate 32 kg + sel_coord(2j + (w & 1), k); w < 2: high
@@ -1541,7 +1595,6 @@ __global__ __launch_bounds__(kPrepThreads) void mfma_prep_kernel(const float* __
   const int L = threadIdx.x & 63, role = threadIdx.x >> 6;
   if (role > NC + 2) return;
   const int n = L & 15, kg = L >> 4, hB = n >> 2, part = n & 3;
-  const float fq = s_fq[hB], fs = s_fs[hB];
   u32x4* gdst = reinterpret_cast<u32x4*>(
       bop + ((int64_t)group * 64 + L) * (SCAN ? kScanLaneWords : POLAR ? kPolarLaneWords : 32));
   if (POLAR && role < NC) {
@@ -1560,56 +1613,45 @@ __global__ __launch_bounds__(kPrepThreads) void mfma_prep_kernel(const float* __
     }
     gdst[j] = words;
   } else if (role < NC) {
+    // byte b of a packed limb word: 0 = l2, 1 = l1, 2 = l0, 3 = zero
     const int j = role;
+    const uint32_t* kl = klimb + hB * LS + 33 * kg;
     u32x4 words;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
+      int bi;
+      if (SCAN) {
+        // key part n of weight 2^(32 - 8n) pairs key limb plane p (weight 2^(8p)) with query
+        // limb 4 - n - p (weight 2^(8 (4 - n - p))) when that is 0, 1 or 2
+        const int plane = 2 - (j >> 1), ql = 4 - part - plane;
+        bi = ql == 2 ? 0 : ql == 1 ? 1 : ql == 0 ? 2 : 3;
+      } else {
+        // high level limb slots (w < 2): part p takes query limb 2 - p; low slots: limb 3 - p
+        const bool hi_slot = w < 2;
+        bi = part == 0 ? (hi_slot ? 0 : 3) : part == 1 ? (hi_slot ? 1 : 0) : part == 2 ? (hi_slot ? 2 : 1) : 3;
+      }
       uint32_t word = 0;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        int v;
-        if (SCAN) {
-          // key part n of weight 2^(32 - 8n) pairs key limb plane p (weight 2^(8p)) with query
-          // limb 4 - n - p (weight 2^(8 (4 - n - p))) when that is 0, 1 or 2
-          const int plane = 2 - (j >> 1), ql = 4 - part - plane;
-          const int coord = sel_coord<BK>(4 * (j & 1) + w, kk);
-          int l2, l1, l0;
-          int8_limbs3((int)rintf(xf[hB][32 * kg + coord] * fq), l2, l1, l0);
-          v = ql == 2 ? l2 : ql == 1 ? l1 : ql == 0 ? l0 : 0;
-        } else {
-          const int coord = sel_coord<BK>(2 * j + (w & 1), kk);
-          int l2, l1, l0;
-          int8_limbs3((int)rintf(xf[hB][32 * kg + coord] * fq), l2, l1, l0);
-          const bool hi_slot = w < 2;
-          v = part == 0 ? (hi_slot ? l2 : 0) : part == 1 ? (hi_slot ? l1 : l2)
-            : part == 2 ? (hi_slot ? l0 : l1) : 0;
-        }
-        word |= (uint32_t)(v & 0xFF) << (8 * kk);
+        const int coord = SCAN ? sel_coord<BK>(4 * (j & 1) + w, kk) : sel_coord<BK>(2 * j + (w & 1), kk);
+        word |= ((kl[coord] >> (8 * bi)) & 0xFFu) << (8 * kk);
       }
       words[w] = word;
     }
     gdst[j] = words;
   } else if (role < NC + 2) {
+    // decode: the token side holds bit s = 4 j + w of each sketch byte in place (byte value
+    // 2^s b, -128 b for s = 7), so this side holds the sketch scaled by 2^-s (negated for
+    // s = 7); part p < 3 takes limb 2 - p, i.e. byte p of the packed word
     const int j = role - NC;
+    const uint32_t* jl = jlimb + hB * LS + 33 * kg;
     u32x4 words;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       uint32_t word = 0;
       if (QJL)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          // decode: the token side holds bit s = 4 j + w of each sketch byte in place (byte
-          // value 2^s b, -128 b for s = 7), so this side holds the sketch scaled by 2^-s
-          // (negated for s = 7)
-          const int s = 4 * j + w;
-          const float sv = sf[hB][32 * kg + 8 * k + 4 * j + w] * fs;
-          const int qv = SCAN ? (int)rintf(sv) : s == 7 ? -(int)rintf(sv * 0.0078125f)
-                                                         : (int)rintf(sv * (1.0f / (float)(1 << s)));
-          int l2, l1, l0;
-          int8_limbs3(qv, l2, l1, l0);
-          const int v = part == 0 ? l2 : part == 1 ? l1 : part == 2 ? l0 : 0;
-          word |= (uint32_t)(v & 0xFF) << (8 * k);
-        }
+        for (int k = 0; k < 4; ++k) word |= ((jl[8 * k + 4 * j + w] >> (8 * part)) & 0xFFu) << (8 * k);
       words[w] = word;
     }
     gdst[NC + j] = words;
@@ -2452,7 +2494,7 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
   if (mfma)
     launch_mfma_prep(c, dc, q, q_dt, batch, q_heads, kv_heads, bop, stream);
   else
-    hipLaunchKernelGGL(query_prep_kernel, dim3(rows), dim3(128), 0, stream, dc.pi, dc.s, c.d, c.m, q,
+    hipLaunchKernelGGL(query_prep_kernel, dim3(rows), dim3(kQueryPrepThreads), 0, stream, dc.pi, dc.s, c.d, c.m, q,
                        q_dt, qx, qs);
   const int64_t n_cold = sel_idx ? k_sel : capacity;
   const int64_t lstride = n_cold + (hot_lens ? hot_capacity : 0);
@@ -2876,11 +2918,11 @@ __device__ __forceinline__ double lut_entry(double q0, double q1, double q2, dou
   return t;
 }
 
-__global__ __launch_bounds__(256) void select_lut_kernel(const void* q, tq_dtype q_dt, const float* codebook,
-                                                         int d, int G, int q_heads, int heads,
-                                                         int32_t* lut_out, int32_t* hist_all) {
+__device__ __forceinline__ void select_lut_block(const void* q, tq_dtype q_dt, const float* codebook, int d, int G,
+                                                 int q_heads, int heads, int32_t* lut_out, int32_t* hist_all,
+                                                 int h, int b) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int h = blockIdx.x, b = blockIdx.y, ng = d / 4;
+  const int ng = d / 4;
   const int64_t unit = (int64_t)b * heads + h;
   double* lut = reinterpret_cast<double*>(smem);           // [G][ng][16]
   int32_t* comb = reinterpret_cast<int32_t*>(lut + G * ng * 16);  // [ng][16]
@@ -2917,6 +2959,25 @@ __global__ __launch_bounds__(256) void select_lut_kernel(const void* q, tq_dtype
   }
   __syncthreads();
   for (int e = threadIdx.x; e < ng * 16; e += blockDim.x) lut_out[unit * ng * 16 + e] = comb[e];
+}
+
+__global__ __launch_bounds__(256) void select_lut_kernel(const void* q, tq_dtype q_dt, const float* codebook,
+                                                         int d, int G, int q_heads, int heads,
+                                                         int32_t* lut_out, int32_t* hist_all) {
+  select_lut_block(q, q_dt, codebook, d, G, q_heads, heads, lut_out, hist_all, blockIdx.x, blockIdx.y);
+}
+
+// The selection tables and the attention's query prep in one launch (sparse attention, whose
+// two first steps are independent one-block-per-unit / per-query jobs): blocks below
+// batch * heads build a unit's tables, the others prepare query row blockIdx.x - batch * heads.
+__global__ __launch_bounds__(256) void select_lut_prep_kernel(const void* q, tq_dtype q_dt, const float* codebook,
+                                                              int d, int G, int q_heads, int heads, int units,
+                                                              int32_t* lut_out, int32_t* hist_all, QueryPrep P) {
+  if ((int)blockIdx.x < units)
+    select_lut_block(q, q_dt, codebook, d, G, q_heads, heads, lut_out, hist_all, blockIdx.x % heads,
+                     blockIdx.x / heads);
+  else
+    query_prep_block(P.pi, P.s, d, P.m, q, q_dt, P.qx, P.qs, (int64_t)blockIdx.x - units);
 }
 
 // Selection runs in five launches (lut and exact: one workgroup per unit; score, filter and
@@ -3306,7 +3367,7 @@ hipError_t launch_select(const Consts& c, const SelectPlan& plan, const void* q,
                          int q_heads, int kv_heads, const void* index, const float* codebook,
                          int64_t capacity, const int32_t* seq_lens, int k, int32_t* out_idx,
                          int32_t* out_count, int32_t* out_scores, void* workspace, hipStream_t stream,
-                         const ProfileEvents& ev) {
+                         const ProfileEvents& ev, const QueryPrep* prep) {
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   int32_t* lut = reinterpret_cast<int32_t*>(ws + plan.ws_lut);
   int32_t* scores = reinterpret_cast<int32_t*>(ws + plan.ws_scores);
@@ -3320,8 +3381,12 @@ hipError_t launch_select(const Consts& c, const SelectPlan& plan, const void* q,
   const int n_chunks = plan.n_chunks;
   if (capacity > 0) {
     const size_t lds = (size_t)G * ng * 16 * 8 + (size_t)ng * 16 * 4;
-    hipLaunchKernelGGL(select_lut_kernel, dim3(kv_heads, batch), dim3(256), lds, stream, q, q_dt, codebook,
-                       c.d, G, q_heads, kv_heads, lut, hist);
+    if (prep)
+      hipLaunchKernelGGL(select_lut_prep_kernel, dim3((unsigned)(batch * kv_heads + prep->rows)), dim3(256), lds,
+                         stream, q, q_dt, codebook, c.d, G, q_heads, kv_heads, batch * kv_heads, lut, hist, *prep);
+    else
+      hipLaunchKernelGGL(select_lut_kernel, dim3(kv_heads, batch), dim3(256), lds, stream, q, q_dt, codebook,
+                         c.d, G, q_heads, kv_heads, lut, hist);
     const dim3 grid((unsigned)n_chunks, kv_heads, batch);
     ev.before(stream);
     if (c.d == 128)
@@ -3614,14 +3679,18 @@ hipError_t launch_sparse(const Consts& c, const DevConsts& dc, const SparsePlan&
                          const ProfileEvents& ev) {
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const SelectPlan& sp = plan.select;
-  hipError_t e = launch_select(c, sp, q, q_dt, batch, q_heads, kv_heads, index, codebook, capacity, seq_lens, k,
-                               nullptr, nullptr, nullptr, ws + plan.ws_select, stream, ev);
-  if (e != hipSuccess) return e;
   float* qx = reinterpret_cast<float*>(ws + plan.ws_qx);
   float* qs = reinterpret_cast<float*>(ws + plan.ws_qs);
   float* part = reinterpret_cast<float*>(ws + plan.ws_part);
   const int rows = batch * q_heads;
-  hipLaunchKernelGGL(query_prep_kernel, dim3(rows), dim3(128), 0, stream, dc.pi, dc.s, c.d, c.m, q, q_dt, qx, qs);
+  // the query prep rides in the selection's table launch (which runs when capacity > 0)
+  const QueryPrep prep{dc.pi, dc.s, c.m, rows, qx, qs};
+  hipError_t e = launch_select(c, sp, q, q_dt, batch, q_heads, kv_heads, index, codebook, capacity, seq_lens, k,
+                               nullptr, nullptr, nullptr, ws + plan.ws_select, stream, ev, &prep);
+  if (e != hipSuccess) return e;
+  if (capacity <= 0)
+    hipLaunchKernelGGL(query_prep_kernel, dim3(rows), dim3(kQueryPrepThreads), 0, stream, dc.pi, dc.s, c.d, c.m, q,
+                       q_dt, qx, qs);
   const int n_chunks = std::max(sp.n_chunks, 1);
   const float sc = scale > 0.0f ? scale : c.inv_sqrt_d;
   SparseArgs s;
@@ -3731,18 +3800,12 @@ __global__ __launch_bounds__(256) void scan_prep_f16_kernel(const float* __restr
   const int K = d + m;
   for (int i = threadIdx.x; i < d; i += blockDim.x) qv[i] = (double)load_elem(q, q_dt, r * d + i);
   __syncthreads();
-  for (int i = threadIdx.x; i < d; i += blockDim.x) {
-    double acc = 0.0;
-    for (int j = 0; j < d; ++j) acc += (double)pi[i * d + j] * qv[j];
-    xv[i] = acc;
-    row[i] = (float)acc;
-  }
+  block_gemv_f64(pi, qv, d, d, [&](int i, double y) {
+    xv[i] = y;
+    row[i] = (float)y;
+  });
   __syncthreads();
-  for (int k = threadIdx.x; k < m; k += blockDim.x) {
-    double acc = 0.0;
-    for (int i = 0; i < d; ++i) acc += (double)s[k * d + i] * xv[i];
-    row[d + k] = (float)acc / sfix;
-  }
+  block_gemv_f64(s, xv, m, d, [&](int k, double y) { row[d + k] = (float)y / sfix; });
   __syncthreads();
   float mx = 0.0f;
   for (int k = threadIdx.x; k < K; k += blockDim.x) mx = fmaxf(mx, fabsf(row[k]));
