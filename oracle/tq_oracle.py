@@ -530,6 +530,32 @@ def recall_1_at_k(approx: np.ndarray, exact: np.ndarray, ks) -> dict:
 # ----------------------------------------------------------------------------------------
 # Self-Indexing sign index and compressed-domain top-k
 # ----------------------------------------------------------------------------------------
+def sign_patterns(k: np.ndarray, mu: np.ndarray) -> np.ndarray:
+    """4-bit sign pattern of every 4-channel group of keys k [n, d] (float32) against the
+    channel mean mu [d] (float32): bit j of group g is [k_(4g+j) >= mu_(4g+j)], a float32
+    comparison.  Self-Indexing page, "Methodologie" 1-2.  Returns [n, d/4] int64."""
+    n, d = k.shape
+    bits = (np.asarray(k, np.float32) >= np.asarray(mu, np.float32)).astype(np.int64).reshape(n, d // 4, 4)
+    return np.sum(bits << np.arange(4), axis=-1)
+
+
+def pattern_centroids(k: np.ndarray, mu: np.ndarray, pat: np.ndarray) -> np.ndarray:
+    """The 16 centroids of every group (Self-Indexing page, "Methodologie" 2, built in one
+    pass): centroid (g, p) is the float64 mean of (k - mu) over the group-g sub-vectors of the
+    tokens whose pattern is p, rounded to float32; 0 when no token has that pattern.
+    k [n, d] float32, mu [d] float32, pat [n, d/4].  Returns [d/4, 16, 4] float32."""
+    n, d = k.shape
+    ng = d // 4
+    book = np.zeros((ng, 16, 4), np.float32)
+    cen = np.asarray(k, np.float64).reshape(n, ng, 4) - np.asarray(mu, np.float64).reshape(ng, 4)
+    for g in range(ng):
+        for p in range(16):
+            sel = pat[:, g] == p
+            if sel.any():
+                book[g, p] = np.mean(cen[sel, g], axis=0).astype(np.float32)
+    return book
+
+
 def build_sign_index(codec: Codec, K: np.ndarray, n_tokens: int):
     """Sign index of keys K [B, T, Hkv, d] over tokens [0, n_tokens).
 
@@ -537,8 +563,8 @@ def build_sign_index(codec: Codec, K: np.ndarray, n_tokens: int):
     balanced), take the sign of each channel, pack the 4 signs of each 4-dim group into a
     pattern 0..15, and build 16 centroids per group in one pass.  Readings: unrotated
     basis; mu is the float32-rounded mean over the tokens indexed; bit = [k >= mu] in
-    float32; centroid = mean of the members' (k - mu) sub-vectors (float32), 0 if the
-    pattern has no member; pattern bit j = channel 4g + j.
+    float32 (sign_patterns); centroid = mean of the members' (k - mu) sub-vectors (float32),
+    0 if the pattern has no member (pattern_centroids); pattern bit j = channel 4g + j.
     Returns index [B, Hkv, cap=T, d/8] u8, codebook [B, Hkv, d/4, 16, 4] f32, mu [B, Hkv, d] f32.
     """
     B, T, H, d = K.shape
@@ -550,14 +576,8 @@ def build_sign_index(codec: Codec, K: np.ndarray, n_tokens: int):
         for h in range(H):
             k = np.asarray(K[b, :n_tokens, h], np.float32)
             mu = np.mean(k.astype(np.float64), axis=0).astype(np.float32)
-            bits = (k >= mu).astype(np.int64).reshape(n_tokens, ng, 4)
-            pat = np.sum(bits << np.arange(4), axis=-1)                     # [n, ng]
-            cen = k.astype(np.float64).reshape(n_tokens, ng, 4) - mu.astype(np.float64).reshape(ng, 4)
-            for g in range(ng):
-                for p in range(16):
-                    sel = pat[:, g] == p
-                    if sel.any():
-                        book[b, h, g, p] = np.mean(cen[sel, g], axis=0).astype(np.float32)
+            pat = sign_patterns(k, mu)                                        # [n, ng]
+            book[b, h] = pattern_centroids(k, mu, pat)
             index[b, h, :n_tokens] = _pack_stream(pat, 4)
             mus[b, h] = mu
     return index, book, mus
