@@ -135,6 +135,17 @@ def test_debug_quantize_is_bit_exact(cfg):
     assert np.array_equal(rec.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("d,kb,m,vb", [(64, 3, 64, 4), (128, 3, 128, 4), (200, 3, 192, 2), (200, 2, 96, 3),
+                                       (128, 4, 0, 4), (128, 2, 256, 3)])
+def test_record_bytes_as_the_header_states(d, kb, m, vb):
+    """tq_record_bytes = 16 ceil((4 ceil(d kb / 32) + m / 8 + 4 ceil(d vb / 32) + 12) / 16), and
+    the sign-index record is d / 8 bytes."""
+    h = _tq().Handle(d, kb, m, vb, 1, 2)
+    KB, VB = 4 * -(-d * kb // 32), 4 * -(-d * vb // 32)
+    assert h.record_bytes == 16 * -(-(KB + m // 8 + VB + 12) // 16)
+    assert h.index_record_bytes == d // 8
+
+
 # ------------------------------------------------------------------ compress ------------
 @pytest.mark.parametrize("name,tokens,batch", [("single_head_1k", 1024, 1), ("tinyllama_layer", 1024, 1),
                                                ("llama8b_decode_32k", 1000, 2), ("sparse_128k_top2048", 777, 1),
@@ -333,6 +344,33 @@ def test_decode_rejects_small_workspace():
 
 
 # ------------------------------------------------------------------ sign index + top-k ---
+def check_sign_index_unit(k, gmu, gpat, gbook, rmu, rpat, rbook, pat_at_gmu, book_at_gpat, what):
+    """Sign index of one (sequence, KV head) unit against the oracle, with no skipped case.
+
+    k [n, d] float32 keys; gmu / gpat / gbook the GPU's mean, patterns [n, d/4] and codebook;
+    rmu / rpat / rbook the oracle's own; pat_at_gmu and book_at_gpat the oracle's pattern and
+    centroid steps taken at the GPU's mean and patterns.  Both sides sum the mean and the
+    centroids in float64 and round once to float32, so they may differ by one float32 rounding;
+    given the same mean the patterns are bit-exact; against the oracle's own mean a pattern bit
+    may differ only where the key lies between the two means.  Returns the flipped-bit count."""
+    n, d = k.shape
+    ulp = np.spacing(np.abs(rmu).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(gmu.astype(np.float64) - rmu) <= ulp), f"{what}: channel means"
+    assert np.array_equal(gpat, pat_at_gmu), f"{what}: patterns at the GPU's mean"
+    bits_g = ((gpat[..., None] >> np.arange(4)) & 1).reshape(n, d)
+    bits_r = ((rpat[..., None] >> np.arange(4)) & 1).reshape(n, d)
+    diff = bits_g != bits_r
+    if diff.any():
+        lo = np.broadcast_to(np.minimum(gmu, rmu), diff.shape)
+        hi = np.broadcast_to(np.maximum(gmu, rmu), diff.shape)
+        assert np.all((k[diff] >= lo[diff]) & (k[diff] <= hi[diff])), f"{what}: index bits away from the mean"
+    np.testing.assert_allclose(gbook, book_at_gpat, rtol=2.4e-7, atol=1e-12,
+                               err_msg=f"{what}: codebook at the GPU's patterns")
+    if not diff.any():
+        np.testing.assert_allclose(gbook, rbook, rtol=2.4e-7, atol=1e-12, err_msg=f"{what}: codebook")
+    return int(diff.sum())
+
+
 def _index_case(w, seq_lens, k, q_heads=None):
     h = _handle(w)
     codec = _codec(h)
@@ -346,11 +384,16 @@ def _index_case(w, seq_lens, k, q_heads=None):
     Kn = _np(K)
     ref_idx, ref_book, ref_mu = O.build_sign_index(codec, Kn, T)
     mu = mean.cpu().numpy()
-    assert np.allclose(mu, ref_mu, rtol=1e-6, atol=1e-7)
     gi, gb = index.cpu().numpy(), book.cpu().numpy()
-    if np.array_equal(mu, ref_mu):
-        assert np.array_equal(gi, ref_idx)
-        assert np.allclose(gb, ref_book, rtol=1e-5, atol=1e-6)
+    ng = d // 4
+    for b in range(B):
+        for hh in range(H):
+            kf = Kn[b, :, hh].astype(np.float32)
+            gpat = O._unpack_stream(gi[b, hh], ng, 4)
+            check_sign_index_unit(kf, mu[b, hh], gpat, gb[b, hh], ref_mu[b, hh],
+                                  O._unpack_stream(ref_idx[b, hh], ng, 4), ref_book[b, hh],
+                                  O.sign_patterns(kf, mu[b, hh]), O.pattern_centroids(kf, mu[b, hh], gpat),
+                                  f"unit {(b, hh)}")
     # selection: GPU vs oracle on the GPU-built index and codebook -> bit-exact
     Hq = q_heads or w.q_heads
     q = W.make_queries(W.Workload(**{**w.__dict__, "q_heads": Hq}), "cuda")
