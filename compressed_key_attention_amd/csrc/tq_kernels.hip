@@ -1411,6 +1411,8 @@ static void launch_small_d(const DecodeArgs& a, int kb, int vb, dim3 grid, hipSt
 //    of LDS and their level halves read as pairs from a 16-entry LDS table.
 // -----------------------------------------------------------------------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __fp16 h16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -1465,11 +1467,12 @@ __device__ __forceinline__ uint32_t bf16_pair(float x) {      // hi | lo << 16
 constexpr int kScanLaneWords = 36;   // bulk-scan query operand words per lane (9 chunks of 16 B)
 
 constexpr int kPrepThreads = 1024;
-// POLAR (decode only): the key chunks are bf16 query operands instead of int8 limbs: chunks
+// POLAR (decode only): the key chunks are fp16 query operands instead of int8 limbs: chunks
 // 0..3 (against the tokens' u_hi) and 4..7 (against u_lo), chunk j & 3 covering coordinates
-// 32 kg + 8 (j & 3) + e of lane L's head n / 4: part 0 = bf16 hi of q_x, part 1 = its bf16 lo
-// (first four chunks only), parts 2, 3 zero.  Then QJL chunks 8, 9 and the scales, 48 words
-// per lane.
+// 32 kg + 8 (j & 3) + e of lane L's head n / 4.  With q' = q_x 2^-e (e the head's power of two
+// above max |q_x|, so |q'| < 1): part 0 = fp16 hi of q' (round to nearest), part 1 = fp16 of
+// q' - hi (first four chunks only), parts 2, 3 zero.  Then QJL chunks 8, 9 and the scales
+// (the first is 2^e), 48 words per lane.
 constexpr int kPolarLaneWords = 48;
 
 template <int BK, bool QJL, bool SCAN, bool POLAR = false>
@@ -1535,7 +1538,7 @@ __global__ __launch_bounds__(kPrepThreads) void mfma_prep_kernel(const float* __
   __syncthreads();
   // per head: fixed-point scales (three int8 limbs against the largest |entry|) and the sum of
   // the sketch's fixed-point values
-  __shared__ float s_fq[G], s_fs[G];
+  __shared__ float s_fq[G], s_fs[G], s_pe[G];
   __shared__ int s_ssum[G];
   if (threadIdx.x < G * 64) {
     const int h = threadIdx.x >> 6, l = threadIdx.x & 63;   // wave h reduces head h
@@ -1555,6 +1558,9 @@ __global__ __launch_bounds__(kPrepThreads) void mfma_prep_kernel(const float* __
       s_fq[h] = fq;
       s_fs[h] = fs;
       s_ssum[h] = ss;
+      int e = 0;
+      if (mx > 0.0f) frexpf(mx, &e);          // mx < 2^e
+      s_pe[h] = (float)e;
     }
   }
   __syncthreads();
@@ -1599,14 +1605,18 @@ __global__ __launch_bounds__(kPrepThreads) void mfma_prep_kernel(const float* __
       bop + ((int64_t)group * 64 + L) * (SCAN ? kScanLaneWords : POLAR ? kPolarLaneWords : 32));
   if (POLAR && role < NC) {
     const int j = role, chain = j >> 2, jj = j & 3;
+    const float sc = ldexpf(1.0f, -(int)s_pe[hB]);      // exact: a power of two
     u32x4 words;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       uint32_t word = 0;
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
-        const float x = xf[hB][32 * kg + 8 * jj + 2 * w + h2];
-        const uint32_t v = part == 0 ? bf16_half(x, 0) : (part == 1 && chain == 0) ? bf16_half(x, 1) : 0u;
+        const float x = xf[hB][32 * kg + 8 * jj + 2 * w + h2] * sc;
+        const _Float16 hi = (_Float16)x;
+        const uint32_t v = part == 0 ? (uint32_t)__builtin_bit_cast(uint16_t, hi)
+                           : (part == 1 && chain == 0) ? (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(x - (float)hi))
+                                                       : 0u;
         word |= v << (16 * h2);
       }
       words[w] = word;
@@ -1658,7 +1668,7 @@ __global__ __launch_bounds__(kPrepThreads) void mfma_prep_kernel(const float* __
   } else {
     // the score lanes of head / query kg combine its parts with these
     const float fqk = s_fq[kg], fsk = s_fs[kg];
-    const float bk = 1.0f / (fqk * fk);
+    const float bk = POLAR ? ldexpf(1.0f, (int)s_pe[kg]) : 1.0f / (fqk * fk);
     const float bq = QJL ? 2.0f / fsk : 0.0f;
     const float oq = QJL ? -(float)s_ssum[kg] / fsk : 0.0f;
     gdst[NC + 2] = u32x4{__float_as_uint(bk), __float_as_uint(bq), __float_as_uint(oq), 0u};
@@ -1757,9 +1767,10 @@ constexpr int kMfmaThreads = 256;
 // (token n, K slice kg) rebuilds the unit vector u of its token on coordinates
 // [32 kg, 32 kg + 32) (the subtree of level-5 node kg): the scale of the subtree root from its
 // two ancestors, levels 5..3 by cos / sin multiplies, then levels 2 and 1 together from the
-// tables TA[c2][c1] = cos psi (cos, sin) theta and TB = sin psi (cos, sin) theta.  u = u_hi + u_lo
-// (bf16 truncations) is the B operand of eight bf16 products with the query parts (q_hi, q_lo),
-// so part 0 + part 1 = <q_x, u> to about 2^-16 relative.
+// tables TA[c2][c1] = cos psi (cos, sin) theta and TB = sin psi (cos, sin) theta.  16 u (the
+// factor keeps the low half in the normal fp16 range) = u_hi + u_lo, both fp16 rounded toward
+// zero, is the B operand of eight fp16 products with the query parts (q'_hi, q'_lo), so
+// part 0 + part 1 = <q', 16 u> to about 2^-20 of sum_i |q'_i u_i|.
 template <int BK, bool QJL, bool GATHER, bool LOGITS, bool POLAR = false>
 __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs A) {
   constexpr int D = 128, G = 4, NW = kMfmaThreads / 64;
@@ -1814,7 +1825,7 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
   const int n = lane & 15, kg = lane >> 4;
   constexpr int NCK = POLAR ? 8 : 4;                         // key operand chunks
   i32x4 Aq[POLAR ? 1 : 4], Aj[2];
-  bf16x8 Ap[POLAR ? 8 : 1];
+  f16x8 Ap[POLAR ? 8 : 1];
   float bk16, bk8, bq, oq, kpol;
   {
     const u32x4* bp = reinterpret_cast<const u32x4*>(
@@ -1824,7 +1835,7 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
     for (int i = 0; i < NCK + 3; ++i) w[i] = bp[i];
     if constexpr (POLAR) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) Ap[j] = __builtin_bit_cast(bf16x8, w[j]);
+      for (int j = 0; j < 8; ++j) Ap[j] = __builtin_bit_cast(f16x8, w[j]);
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) Aq[j] = __builtin_bit_cast(i32x4, w[j]);
@@ -1837,7 +1848,8 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
     const float bk = __uint_as_float(w[NCK + 2][0]);
     bk16 = 65536.0f * bk * ks;
     bk8 = 256.0f * bk * ks;
-    kpol = A.scale * kLog2e;                                   // polar: r <q_x, u>, u of unit norm
+    // polar: r <q_x, u> = r 2^e <q', 16 u> / 16, u of unit norm (the first scale word is 2^e)
+    kpol = A.scale * kLog2e * bk * 0.0625f;
     bq = __uint_as_float(w[NCK + 2][1]) * qs;
     oq = __uint_as_float(w[NCK + 2][2]) * qs;
   }
@@ -1925,7 +1937,7 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
       const float2* csl = ptab + 128;                                  // levels 3..7
       const float2 t7 = csl[16 + ((u3 >> 28) & 3u)];
       const float2 t6 = csl[12 + ((u3 >> (24 + 2 * (kg >> 1))) & 3u)];
-      const float sroot = ((kg >> 1) ? t7.y : t7.x) * ((kg & 1) ? t6.y : t6.x);
+      const float sroot = 16.0f * ((kg >> 1) ? t7.y : t7.x) * ((kg & 1) ? t6.y : t6.x);
       const float2 t5 = csl[8 + ((u3 >> (16 + 2 * kg)) & 3u)];
       float s4[2] = {sroot * t5.x, sroot * t5.y}, s3[4], s2[8];
 #pragma unroll
@@ -1954,15 +1966,15 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
           const float v[4] = {s2[k] * ta.x, s2[k] * ta.y, s2[k] * tb.x, s2[k] * tb.y};
 #pragma unroll
           for (int pr = 0; pr < 2; ++pr) {
-            const uint32_t x0 = __float_as_uint(v[2 * pr]), x1 = __float_as_uint(v[2 * pr + 1]);
-            const float r0 = v[2 * pr] - __uint_as_float(x0 & 0xFFFF0000u);
-            const float r1 = v[2 * pr + 1] - __uint_as_float(x1 & 0xFFFF0000u);
-            bh[2 * k2 + pr] = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
-            bl[2 * k2 + pr] = __builtin_amdgcn_perm(__float_as_uint(r1), __float_as_uint(r0), 0x07060302u);
+            // hi = fp16 pair rounded toward zero; lo = the exact fp32 remainders, again as a pair
+            const h16x2 hp = __builtin_amdgcn_cvt_pkrtz(v[2 * pr], v[2 * pr + 1]);
+            const h16x2 lp = __builtin_amdgcn_cvt_pkrtz(v[2 * pr] - (float)hp[0], v[2 * pr + 1] - (float)hp[1]);
+            bh[2 * k2 + pr] = __builtin_bit_cast(uint32_t, hp);
+            bl[2 * k2 + pr] = __builtin_bit_cast(uint32_t, lp);
           }
         }
-        Ck = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ap[jj], __builtin_bit_cast(bf16x8, bh), Ck, 0, 0, 0);
-        Ck = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ap[4 + jj], __builtin_bit_cast(bf16x8, bl), Ck, 0, 0, 0);
+        Ck = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ap[jj], __builtin_bit_cast(f16x8, bh), Ck, 0, 0, 0);
+        Ck = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ap[4 + jj], __builtin_bit_cast(f16x8, bl), Ck, 0, 0, 0);
       }
       i32x4 Cq = i32x4{0, 0, 0, 0};
       if (QJL) {
@@ -3842,8 +3854,6 @@ __device__ __forceinline__ uint32_t key_code_at(const uint32_t* kw, int i, int d
 
 constexpr int kS16Tile = 128;   // queries and vectors per workgroup
 constexpr int kS16Row = 40;     // LDS row: 32 fp16 of one K step + 8 pad (80 B)
-
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 struct Scan16Args {
   const uint16_t* qh;
