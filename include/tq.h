@@ -38,18 +38,30 @@
  *  - Inputs must be finite.  Non-finite inputs give unspecified codes and outputs but
  *    never an out-of-bounds access.
  *
- * Record layout (one contiguous record per token per KV head, little-endian):
- *    [ key codes  : head_dim * key_bits / 8 bytes                      ]
- *    [ QJL signs  : qjl_dim / 8 bytes  (bit j = 1 iff (S e)_j >= 0)     ]
- *    [ value codes: head_dim * value_bits / 8 bytes                    ]
- *    [ r_k float32 | rho float32 | r_v float32 ] [ zero pad to 16 B ]
+ * Record layout (one contiguous record per token per KV head, little-endian).  Every field
+ * starts on a 32-bit word; padding bytes are zero:
+ *    [ key codes  : KB = 4 * ceil(head_dim * key_bits / 32) bytes                   ]
+ *    [ QJL signs  : qjl_dim / 8 bytes  (stream bit j = 1 iff (S e)_j >= 0)           ]
+ *    [ value codes: VB = 4 * ceil(head_dim * value_bits / 32) bytes                 ]
+ *    [ r_k float32 | rho float32 | r_v float32 ]
+ *    [ zero pad to a multiple of 16 bytes ]
+ *  so record_bytes = 16 * ceil((KB + qjl_dim / 8 + VB + 12) / 16) (tq_record_bytes); e.g.
+ *  head_dim 128, 3-bit keys, qjl_dim 128, 4-bit values: 48 + 16 + 64 + 12 -> 144 bytes.
+ *  2- and 4-bit code fields and the sign field are little-endian bitstreams: code i occupies
+ *  stream bits [b*i, b*i + b), stream bit n being bit n % 8 of byte n / 8.
+ *  3-bit code fields are groups of 32 codes; group g is the 12 bytes at 12 g, read as
+ *  little-endian 32-bit words W0, W1, W2.  Code j < 24 of a group occupies bits
+ *  [8 (j % 4) + 3 floor((j % 8) / 4), +3) of W_floor(j / 8).  Code 24 + r (r < 8) is bits
+ *  [3 floor(r / 4), +3) of the 6-bit value T_k of byte lane k = r % 4, where bit t of T_k is
+ *  bit 8 k + 6 + (t % 2) of W_floor(t / 2).  (Masking a word with 0x07070707, or shifting it by
+ *  3 and masking, gives four codes, one per byte.)  When head_dim is not a multiple of 32 the
+ *  last head_dim % 32 codes follow the whole groups as a plain 3-bit bitstream (head_dim 200:
+ *  6 groups of 72 bytes, then codes 192..199 in 3 bytes, padded to 76 bytes).
  *  Polar key codes (TQ_KEY_POLAR) replace the key code field by
- *    [ level-1 angle codes: (head_dim/2) * key_bits / 8 bytes ]
- *    [ codes of levels 2..L, level 2 first, node order: 4 * ceil((head_dim/2 - 1) *
- *      polar_upper_bits / 32) bytes ]
- *  A code stream is a little-endian bitstream over 32-bit words: code i occupies stream
- *  bits [b*i, b*i + b) and may straddle two words.  A cache is an array
- *  records[batch][kv_heads][capacity][record_bytes].
+ *    [ level-1 angle codes: (head_dim/2) * key_bits / 8 bytes, a key_bits-bit bitstream ]
+ *    [ codes of levels 2..L, level 2 first, node order: a polar_upper_bits-bit bitstream
+ *      in 4 * ceil((head_dim/2 - 1) * polar_upper_bits / 32) bytes ]
+ *  A cache is an array records[batch][kv_heads][capacity][record_bytes].
  *  Sign index: one record of head_dim/8 bytes per token per KV head; the 4-bit pattern of
  *  channel group g (channels 4g..4g+3, bit j = channel 4g+j) sits at stream bits
  *  [4g, 4g+4).  Index array: index[batch][kv_heads][capacity][head_dim/8];
@@ -92,11 +104,14 @@ typedef enum tq_dtype { TQ_F32 = 0, TQ_F16 = 1, TQ_BF16 = 2 } tq_dtype;
 typedef enum tq_key_codec { TQ_KEY_SCALAR = 0, TQ_KEY_POLAR = 1 } tq_key_codec;
 
 typedef struct tq_config {
-  int32_t head_dim;       /* d: 64 or 128                                              */
-  int32_t key_bits;       /* b_k: 2..4 bits per rotated key coordinate; polar: bits per
-                             level-1 angle, 2 or 4                                     */
+  int32_t head_dim;       /* d: 64 or 128 for every call; any multiple of 8 up to 256
+                             for tq_compress_kv and tq_score_scan (the other calls
+                             return TQ_ERR_UNSUPPORTED for such a handle)              */
+  int32_t key_bits;       /* b_k: bits per rotated key coordinate, 2..4 (1 is a valid
+                             width but not built: tq_create returns
+                             TQ_ERR_UNSUPPORTED); polar: bits per level-1 angle, 2 or 4 */
   int32_t qjl_dim;        /* m: 0 (no QJL sketch) or a multiple of 32, at most 256     */
-  int32_t value_bits;     /* b_v: 2..4                                                 */
+  int32_t value_bits;     /* b_v: 2..4 (1: TQ_ERR_UNSUPPORTED, as for keys)            */
   uint64_t rotation_seed; /* seed of the Gaussian matrix whose QR factor is Pi         */
   uint64_t qjl_seed;      /* seed of the QJL projection S                              */
   int32_t key_codec;      /* tq_key_codec (0 = scalar)                                 */

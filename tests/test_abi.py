@@ -107,3 +107,62 @@ def test_record_size_formula_matches_oracle():
     for d, kb, m, vb in [(128, 3, 128, 4), (64, 3, 64, 4), (128, 4, 0, 4), (64, 2, 32, 2)]:
         payload = d * kb // 8 + m // 8 + d * vb // 8 + 12
         assert O.Codec(d, kb, m, vb, 1, 2).record_bytes == (payload + 15) // 16 * 16
+
+
+def _header_codes(field: np.ndarray, d: int, b: int) -> np.ndarray:
+    """Codes of one key or value field [n, bytes] read exactly as include/tq.h states the layout
+    (2/4-bit bitstreams; 3-bit groups of 32 codes in three words, a plain stream for the tail)."""
+    n = field.shape[0]
+    out = np.zeros((n, d), np.int64)
+    stream = lambda buf, i, bits: sum(((int(buf[(bits * i + t) // 8]) >> ((bits * i + t) % 8)) & 1) << t
+                                      for t in range(bits))
+    for r in range(n):
+        f = field[r]
+        if b != 3:
+            out[r] = [stream(f, i, b) for i in range(d)]
+            continue
+        for g in range(d // 32):
+            W = [int.from_bytes(bytes(f[12 * g + 4 * w: 12 * g + 4 * w + 4]), "little") for w in range(3)]
+            for j in range(24):
+                out[r, 32 * g + j] = (W[j // 8] >> (8 * (j % 4) + 3 * ((j % 8) // 4))) & 7
+            for rr in range(8):
+                k = rr % 4
+                T = sum(((W[t // 2] >> (8 * k + 6 + t % 2)) & 1) << t for t in range(6))
+                out[r, 32 * g + 24 + rr] = (T >> (3 * (rr // 4))) & 7
+        tail = f[12 * (d // 32):]
+        for i in range(d % 32):
+            out[r, 32 * (d // 32) + i] = stream(tail, i, 3)
+    return out
+
+
+@pytest.mark.parametrize("d,kb,m,vb", [(64, 3, 64, 4), (128, 3, 128, 4), (128, 2, 256, 3), (200, 3, 192, 2),
+                                       (200, 2, 96, 3), (128, 4, 0, 4)])
+def test_header_record_layout_matches_the_oracle_packer(d, kb, m, vb):
+    """The record layout include/tq.h states (field sizes and offsets on 32-bit words, the 3-bit
+    group layout, the plain tail, the 16-byte record padding), read back from records the oracle
+    packs, gives the codes, bits and norms that went in."""
+    from oracle import tq_oracle as O
+    codec = O.Codec(d, kb, m, vb, 1, 2)
+    KB, VB = 4 * -(-d * kb // 32), 4 * -(-d * vb // 32)
+    rec_bytes = 16 * -(-(KB + m // 8 + VB + 12) // 16)
+    assert (codec.kbytes, codec.sbytes, codec.vbytes, codec.record_bytes) == (KB, m // 8, VB, rec_bytes)
+    rng = np.random.default_rng(d + kb + m + vb)
+    n = 5
+    f = dict(kc=rng.integers(0, 1 << kb, (n, d)), bits=rng.integers(0, 2, (n, m)),
+             vc=rng.integers(0, 1 << vb, (n, d)), r_k=rng.random(n).astype(np.float32),
+             rho=rng.random(n).astype(np.float32), r_v=rng.random(n).astype(np.float32))
+    rec = O.pack_records(codec, f)
+    assert rec.shape == (n, rec_bytes)
+    assert np.array_equal(_header_codes(rec[:, :KB], d, kb), f["kc"])
+    signs = rec[:, KB:KB + m // 8]
+    assert np.array_equal(np.stack([[(signs[r, j // 8] >> (j % 8)) & 1 for j in range(m)] for r in range(n)])
+                          .reshape(n, m), f["bits"])
+    assert np.array_equal(_header_codes(rec[:, KB + m // 8:KB + m // 8 + VB], d, vb), f["vc"])
+    norms = np.ascontiguousarray(rec[:, KB + m // 8 + VB:KB + m // 8 + VB + 12]).view("<f4")
+    assert np.array_equal(norms, np.stack([f["r_k"], f["rho"], f["r_v"]], -1))
+    assert np.all(rec[:, KB + m // 8 + VB + 12:] == 0)
+    # bits past the last code of a field are zero padding
+    for off, nb, b in ((0, KB, kb), (KB + m // 8, VB, vb)):
+        used = d * b
+        tailbits = np.unpackbits(rec[:, off:off + nb], axis=1, bitorder="little")[:, used:]
+        assert not tailbits.any()
