@@ -29,6 +29,19 @@ def test_splitmix64_reference_vector():
     assert got == g["first_outputs_hex"]
 
 
+def test_box_muller_first_pair_worked_by_hand():
+    """The first two normals of seed 0 equal the pair worked by hand from the SplitMix64
+    reference words (golden file): pins the word-to-uniform mapping (>> 11, the + 1 of u1,
+    2^-53), which word feeds the radius, and the cos-then-sin order."""
+    g = _golden("box_muller_seed0_pair0.json")
+    w0, w1 = int(g["w0_hex"], 16), int(g["w1_hex"], 16)
+    assert [w0, w1] == O.splitmix64(g["seed"], 2)
+    assert (w0 >> 11) + 1 == g["u1_numerator"] and w1 >> 11 == g["u2_numerator"]
+    got = O.gaussians(g["seed"], 2)
+    want = np.array([float(g["g0_cos"]), float(g["g1_sin"])])
+    assert np.all(np.abs(got - want) <= 4e-16 * np.abs(want)), (got, want)
+
+
 def test_box_muller_gaussians_are_standard_normal():
     n = 200_000
     x = O.gaussians(12345, n)
