@@ -32,7 +32,7 @@ EXPORTED = [
     "tq_index_workspace_size", "tq_build_sign_index", "tq_select_workspace_size",
     "tq_select_topk", "tq_scan_workspace_size", "tq_score_scan", "tq_set_profile_events",
     "tq_stream_read", "tq_monarch_workspace_size", "tq_monarch_step", "tq_sparse_workspace_size",
-    "tq_sparse_attention", "tq_polar_host_constants",
+    "tq_sparse_attention", "tq_polar_host_constants", "tq_decode_attention_noalloc",
 ]
 TQ_KEY_SCALAR, TQ_KEY_POLAR = 0, 1
 
@@ -88,6 +88,8 @@ _debug_quantize = _sig("tq_debug_quantize", _P, _P, _P, _P, _P, _P, _P, _I64, _P
 _decode_ws = _sig("tq_decode_workspace_size", _P, _I32, _I32, _I32, _I64, _I32, _PSZ)
 _decode = _sig("tq_decode_attention", _P, _P, ctypes.c_int, _I32, _I32, _I32, _P, _I64, _P, _P, _P,
                ctypes.c_int, _P, _I64, _P, _I32, _F, _P, _P, _P, _P, _SZ, _P)
+_decode_noalloc = _sig("tq_decode_attention_noalloc", _P, _P, ctypes.c_int, _I32, _I32, _I32, _P, _I64, _P, _P,
+                       _P, ctypes.c_int, _P, _I64, _P, _I32, _F, _P, _P, _P, _P)
 _index_ws = _sig("tq_index_workspace_size", _P, _I32, _I32, _PSZ)
 _index = _sig("tq_build_sign_index", _P, _P, ctypes.c_int, _I32, _I64, _I32, _I64, _I64, _I64, _P,
               _P, _P, _I64, _I64, _P, _SZ, _P)
@@ -248,6 +250,20 @@ class Handle:
                       _ptr(hot_k), _ptr(hot_v), hot_dt, _ptr(hot_lens), hot_cap, _ptr(sel_idx), k_sel,
                       float(scale), _ptr(out), _ptr(lse), _ptr(logits), _ptr(workspace),
                       workspace.numel(), _stream(stream)))
+        return out
+
+    def decode_attention_noalloc(self, q, records, seq_lens, out, hot_k=None, hot_v=None, hot_lens=None,
+                                 sel_idx=None, scale=0.0, lse=None, logits=None, stream=None):
+        """tq_decode_attention_noalloc: decode_attention with the library's fixed device scratch
+        instead of a workspace (nothing is allocated; `out` must be given).  Returns out."""
+        B, Hq, d = q.shape
+        Hkv, cap = records.shape[1], records.shape[2]
+        k_sel = 0 if sel_idx is None else sel_idx.shape[-1]
+        hot_cap = 0 if hot_k is None else hot_k.shape[2]
+        hot_dt = TQ_F32 if hot_k is None else _dtype_code(hot_k)
+        check(_decode_noalloc(self._h, _ptr(q), _dtype_code(q), B, Hq, Hkv, _ptr(records), cap, _ptr(seq_lens),
+                              _ptr(hot_k), _ptr(hot_v), hot_dt, _ptr(hot_lens), hot_cap, _ptr(sel_idx), k_sel,
+                              float(scale), _ptr(out), _ptr(lse), _ptr(logits), _stream(stream)))
         return out
 
     # ---------------------------------------------------------------- sign index / top-k

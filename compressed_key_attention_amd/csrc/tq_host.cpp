@@ -639,6 +639,14 @@ tq_status tq_create(const tq_config* cfg, tq_handle** out) {
   const size_t main_bytes = (3 * n_pi + 4 * n_s) * sizeof(float);
   const size_t total = main_bytes + polar_bytes;
   if (hipGetDevice(&h->device) != hipSuccess) { delete h; return fail(TQ_ERR_DEVICE, "no HIP device"); }
+  {
+    // once per device: the address of the allocation-free decode's fixed scratch
+    const hipError_t se = tq::scratch_setup();
+    if (se != hipSuccess) {
+      delete h;
+      return device_status(se, "lookup of the fixed device scratch");
+    }
+  }
   if (hipMalloc(&h->dev_block, total) != hipSuccess) {
     delete h;
     return fail(TQ_ERR_OUT_OF_MEMORY, "hipMalloc of %zu bytes failed", total);
@@ -788,13 +796,13 @@ tq_status tq_decode_workspace_size(const tq_handle* h, int32_t batch, int32_t q_
   return ok();
 }
 
-tq_status tq_decode_attention(const tq_handle* h, const void* q, tq_dtype q_dt, int32_t batch,
+// Checks shared by the two decode entry points; fills the plan.
+static tq_status check_decode(const tq_handle* h, const void* q, tq_dtype q_dt, int32_t batch,
                               int32_t q_heads, int32_t kv_heads, const void* records,
                               int64_t capacity, const int32_t* seq_lens, const void* hot_k,
                               const void* hot_v, tq_dtype hot_dt, const int32_t* hot_lens,
                               int64_t hot_capacity, const int32_t* sel_idx, int32_t k_sel,
-                              float scale, float* out, float* lse, float* logits,
-                              void* workspace, size_t ws_bytes, hipStream_t stream) {
+                              float scale, float* out, tq::DecodePlan* plan) {
   {
     tq_status dst;
     if (dim_unsupported(h, "decode attention", &dst)) return dst;
@@ -819,9 +827,22 @@ tq_status tq_decode_attention(const tq_handle* h, const void* q, tq_dtype q_dt, 
     if (!aligned(hot_k, hs * 8) || !aligned(hot_v, hs * 8))
       return fail(TQ_ERR_INVALID_ARGUMENT, "hot_k and hot_v must be aligned to 8 elements");
   }
-  tq::DecodePlan plan;
-  if (!tq::plan_decode(h->c, batch, q_heads, kv_heads, sel_idx ? k_sel : capacity, &plan))
+  if (!tq::plan_decode(h->c, batch, q_heads, kv_heads, sel_idx ? k_sel : capacity, plan))
     return fail(TQ_ERR_UNSUPPORTED, "group size %d not supported", q_heads / kv_heads);
+  return ok();
+}
+
+tq_status tq_decode_attention(const tq_handle* h, const void* q, tq_dtype q_dt, int32_t batch,
+                              int32_t q_heads, int32_t kv_heads, const void* records,
+                              int64_t capacity, const int32_t* seq_lens, const void* hot_k,
+                              const void* hot_v, tq_dtype hot_dt, const int32_t* hot_lens,
+                              int64_t hot_capacity, const int32_t* sel_idx, int32_t k_sel,
+                              float scale, float* out, float* lse, float* logits,
+                              void* workspace, size_t ws_bytes, hipStream_t stream) {
+  tq::DecodePlan plan;
+  const tq_status st = check_decode(h, q, q_dt, batch, q_heads, kv_heads, records, capacity, seq_lens, hot_k,
+                                    hot_v, hot_dt, hot_lens, hot_capacity, sel_idx, k_sel, scale, out, &plan);
+  if (st != TQ_OK || batch == 0) return st;
   if (!workspace || ws_bytes < plan.ws_total || !aligned(workspace, 256))
     return fail(TQ_ERR_WORKSPACE_TOO_SMALL, "decode needs %zu bytes of 256-byte aligned workspace",
                 plan.ws_total);
@@ -829,6 +850,30 @@ tq_status tq_decode_attention(const tq_handle* h, const void* q, tq_dtype q_dt, 
                                          records, capacity, seq_lens, hot_k, hot_v, hot_dt,
                                          hot_lens, hot_capacity, sel_idx, k_sel, scale, out, lse,
                                          logits, workspace, stream, take_events()),
+                       "decode launch");
+}
+
+tq_status tq_decode_attention_noalloc(const tq_handle* h, const void* q, tq_dtype q_dt, int32_t batch,
+                                      int32_t q_heads, int32_t kv_heads, const void* records,
+                                      int64_t capacity, const int32_t* seq_lens, const void* hot_k,
+                                      const void* hot_v, tq_dtype hot_dt, const int32_t* hot_lens,
+                                      int64_t hot_capacity, const int32_t* sel_idx, int32_t k_sel,
+                                      float scale, float* out, float* lse, float* logits,
+                                      hipStream_t stream) {
+  tq::DecodePlan plan;
+  const tq_status st = check_decode(h, q, q_dt, batch, q_heads, kv_heads, records, capacity, seq_lens, hot_k,
+                                    hot_v, hot_dt, hot_lens, hot_capacity, sel_idx, k_sel, scale, out, &plan);
+  if (st != TQ_OK || batch == 0) return st;
+  if (plan.ws_total > tq::kScratchBytes)
+    return fail(TQ_ERR_WORKSPACE_TOO_SMALL,
+                "this decode needs %zu bytes of scratch; the fixed device scratch holds %zu "
+                "(use tq_decode_attention with a workspace)", plan.ws_total, tq::kScratchBytes);
+  void* ws = tq::scratch_address(h->device);
+  if (!ws) return fail(TQ_ERR_DEVICE, "the fixed device scratch is not set up on device %d", h->device);
+  return device_status(tq::launch_decode(h->c, h->dc, plan, q, q_dt, batch, q_heads, kv_heads,
+                                         records, capacity, seq_lens, hot_k, hot_v, hot_dt,
+                                         hot_lens, hot_capacity, sel_idx, k_sel, scale, out, lse,
+                                         logits, ws, stream, take_events()),
                        "decode launch");
 }
 

@@ -201,6 +201,16 @@ struct MonarchStep {
   int batch, q_heads, kv_heads, window, promote_steps;
   float cold_gate, promote_weight, scale;
 };
+// Fixed device scratch of the allocation-free decode (tq_decode_attention_noalloc): one
+// file-scope device array of kScratchBytes in the kernels' source file, so every GPU the
+// library runs on holds its own copy until the process ends.  scratch_setup() looks up the
+// array's address on the current device once (hipGetSymbolAddress) and keeps it per device;
+// scratch_address(device) returns it (nullptr if setup never succeeded there).
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+constexpr int kScratchMaxDevices = 64;
+hipError_t scratch_setup();
+void* scratch_address(int device);
+
 MonarchPlan plan_monarch(const Consts& c, int batch, int q_heads, int kv_heads, int64_t hot_cap,
                          int64_t cold_cap, bool* ok);
 hipError_t launch_monarch_step(const Consts& c, const DevConsts& dc, const MonarchPlan& plan,

@@ -19,6 +19,7 @@
 #include <algorithm>
 #include <cfloat>
 #include <cmath>
+#include <mutex>
 
 #include "tq_internal.h"
 
@@ -4872,6 +4873,38 @@ hipError_t launch_monarch_step(const Consts& c, const DevConsts& dc, const Monar
     hipLaunchKernelGGL(monarch_evict_kernel<64>, dim3(s.batch), dim3(512), lds, stream, M);
   }
   return hipGetLastError();
+}
+
+
+// -----------------------------------------------------------------------------------------
+// Fixed scratch of the allocation-free decode.  In host code `scratch` names a host-side
+// stand-in, not device memory: kernels and copies only ever get the device address that
+// hipGetSymbolAddress returns (one per device, looked up once with that device current).
+// -----------------------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kScratchMaxDevices];
+
+hipError_t scratch_setup() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev]) return hipSuccess;
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (!ptr || reinterpret_cast<uintptr_t>(ptr) % 256 != 0) return hipErrorInvalidSymbol;
+  g_scratch_ptr[dev] = ptr;
+  return hipSuccess;
+}
+
+void* scratch_address(int device) {
+  if (device < 0 || device >= kScratchMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch_ptr[device];
 }
 
 }  // namespace tq

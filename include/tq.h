@@ -209,6 +209,24 @@ tq_status tq_decode_attention(const tq_handle* h, const void* q, tq_dtype q_dt, 
                               float* lse, float* logits, void* workspace, size_t ws_bytes,
                               hipStream_t stream);
 
+/* tq_decode_attention without a workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * Arguments, outputs and errors as tq_decode_attention.  The call allocates nothing: its
+ * scratch is one fixed device array of 16 MiB (16 << 20 bytes) per GPU, built into the
+ * library and held until the process ends; tq_create looks up its address on the handle's
+ * device.  A decode whose tq_decode_workspace_size exceeds 16 MiB returns
+ * TQ_ERR_WORKSPACE_TOO_SMALL with nothing enqueued.  Every call on a GPU shares that GPU's
+ * array (nothing in it needs to start at zero): calls that may overlap on one GPU - on
+ * different streams, or from different threads - race and must be ordered by the caller. */
+tq_status tq_decode_attention_noalloc(const tq_handle* h, const void* q, tq_dtype q_dt,
+                                      int32_t batch, int32_t q_heads, int32_t kv_heads,
+                                      const void* records, int64_t capacity,
+                                      const int32_t* seq_lens, const void* hot_k,
+                                      const void* hot_v, tq_dtype hot_dt, const int32_t* hot_lens,
+                                      int64_t hot_capacity, const int32_t* sel_idx, int32_t k_sel,
+                                      float scale, float* out, float* lse, float* logits,
+                                      hipStream_t stream);
+
 /* Self-Indexing sign index of keys over slots [first_slot, first_slot + n_tokens)
  * (Self-Indexing page, "Methodologie" 1-2).  k addressed as in tq_compress_kv.
  * mean[b][h][i] = float32(mean_t k), bit = [k >= mean] (float32), pattern per 4-channel
