@@ -302,7 +302,11 @@ def oracle_baseline(units, make_job, tokens_per_unit, total_units, unit_name, bu
         list(ex.map(_oracle_job, jobs))
         wall = time.perf_counter() - t0
     rate_w = n_multi * tokens_per_unit / wall
+    host = os.cpu_count() or 1
     return {"value": rate_w, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "host_cores": host,
+            "core_cap": (f"at most {max_workers} worker processes: the CPU share of one GPU on the "
+                         f"benchmark machines ({host} host cores visible)") if host > workers else None,
             "sample": f"{n_multi} of {total_units} {unit_name} over {workers} worker processes "
                       f"(numpy float64 oracle, BLAS 1 thread each), {wall:.1f} s wall",
             "single_thread": {"value": rate1, "cores": 1,
@@ -321,7 +325,7 @@ def compute_dtype(w) -> str:
     if w.name == "sparse_128k_top2048":
         return "i32 (selection scores) + f32 (attention)"
     if decode_kernel_name(w) == "decode_mfma_kernel" and w.polar_upper_bits:
-        return "bf16 hi/lo key products + i8 sketch + bf16 values (fp32 / int32 accumulate)"
+        return "f16 hi/lo key products + i8 sketch + bf16 values (fp32 / int32 accumulate)"
     if decode_kernel_name(w) == "decode_mfma_kernel":
         return "i8 + bf16 (int32 / fp32 accumulate)"
     return "f32"

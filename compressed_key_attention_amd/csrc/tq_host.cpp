@@ -462,10 +462,6 @@ tq_status tq_monarch_workspace_size(const tq_handle* h, int32_t batch, int32_t q
     tq_status dst;
     if (dim_unsupported(h, "the hot/cold step", &dst)) return dst;
   }
-  {
-    tq_status pst;
-    if (polar_unsupported(h, "the hot/cold step", &pst)) return pst;
-  }
   if (!h || !bytes) return fail(TQ_ERR_INVALID_ARGUMENT, "NULL handle or output");
   if (batch < 0 || q_heads <= 0 || kv_heads <= 0 || q_heads % kv_heads || hot_capacity <= 0 || cold_capacity < 0)
     return fail(TQ_ERR_INVALID_ARGUMENT, "bad hot/cold shape");
@@ -483,10 +479,6 @@ tq_status tq_monarch_step(const tq_handle* h, const tq_monarch_config* cfg, cons
   {
     tq_status dst;
     if (dim_unsupported(h, "the hot/cold step", &dst)) return dst;
-  }
-  {
-    tq_status pst;
-    if (polar_unsupported(h, "the hot/cold step", &pst)) return pst;
   }
   if (!h || !cfg || !st) return fail(TQ_ERR_INVALID_ARGUMENT, "handle, config or state is NULL");
   size_t es, hs;

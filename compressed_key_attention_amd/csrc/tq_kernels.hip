@@ -287,6 +287,21 @@ __device__ __forceinline__ void quantize_rotated(f64x4 (&acc)[D / 16], double zs
 // x becomes the residual x - r u, u rebuilt top-down from the float64 cos / sin of the grid.
 // Every lane of the wave must call this (shuffles).
 // -----------------------------------------------------------------------------------------
+// float64 products, sums and differences each rounded on their own (never fused into a
+// multiply-add), in the order the host reference evaluates them
+__device__ __forceinline__ double mul64(double a, double b) {
+#pragma clang fp contract(off)
+  return a * b;
+}
+__device__ __forceinline__ double add64(double a, double b) {
+#pragma clang fp contract(off)
+  return a + b;
+}
+__device__ __forceinline__ double sub64(double a, double b) {
+#pragma clang fp contract(off)
+  return a - b;
+}
+
 __device__ __forceinline__ double polar_angle(double a, double b) {
   return (a == 0.0 && b == 0.0) ? 0.0 : atan2(b, a);
 }
@@ -1696,9 +1711,50 @@ __device__ __forceinline__ void merge_group(const float* __restrict__ pi_t, cons
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj)
       w[r][jj] = *reinterpret_cast<const float4*>(pi_t + (int64_t)(orow + RS * r) * D + 32 * jj + 4 * ks);
-  // rotated-domain output of head h, coordinate i: one pass over the chunk partials with a
-  // running maximum (eight chunks' loads in flight at a time; a chunk with m = -inf weighs 0);
-  // every thread of a head forms the same maximum and weight sum
+  // rotated-domain output of head h, coordinate i
+  constexpr int PER = (GG * D + 255) / 256;   // elements per thread
+  if (nch <= 8) {
+    // one memory round trip: every chunk's (m, l, o_i) of this thread's elements at once
+    float mc[PER][8], lc[PER][8], ov[PER][8];
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int e = min((int)threadIdx.x + 256 * p, GG * D - 1), h = e / D, i = e % D;
+      const float* pr = part + (row0 + h) * nch * stride;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int cc = min(u, nch - 1);
+        mc[p][u] = u < nch ? pr[(int64_t)cc * stride] : kNegInf;
+        lc[p][u] = pr[(int64_t)cc * stride + 1];
+        ov[p][u] = pr[(int64_t)cc * stride + 2 + i];
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int e = (int)threadIdx.x + 256 * p;
+      if (e >= GG * D) break;
+      const int h = e / D, i = e % D;
+      float M = kNegInf;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) M = fmaxf(M, mc[p][u]);
+      float L = 0.0f, acc = 0.0f;
+      if (M != kNegInf) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float wgt = mc[p][u] == kNegInf ? 0.0f : __expf(mc[p][u] - M);
+          acc = fmaf(ov[p][u], wgt, acc);
+          L = fmaf(lc[p][u], wgt, L);
+        }
+      }
+      ox[h][i] = acc;
+      if (i == 0) {
+        sM[h] = M;
+        sL[h] = L;
+      }
+    }
+  } else {
+  // one pass over the chunk partials with a running maximum (eight chunks' loads in flight at a
+  // time; a chunk with m = -inf weighs 0); every thread of a head forms the same maximum and
+  // weight sum
   for (int e = threadIdx.x; e < GG * D; e += blockDim.x) {
     const int h = e / D, i = e % D;
     const float* pr = part + (row0 + h) * nch * stride;
@@ -1732,6 +1788,7 @@ __device__ __forceinline__ void merge_group(const float* __restrict__ pi_t, cons
       sM[h] = M;
       sL[h] = L;
     }
+  }
   }
   __syncthreads();
   // o = Pi^T o_x / L for the GG heads
@@ -4422,6 +4479,7 @@ constexpr int kMonarchMaxPromote = 1024;  // promotions per sequence and step
 
 struct MonarchArgs {
   Consts c;
+  PolarTables pt;         // polar key codes: angle bounds, float64 cos / sin of the grid levels
   const float* pi;        // [d][d]
   const float* pi_t;      // [d][d] transposed
   const float* s;         // [m][d]
@@ -4500,7 +4558,19 @@ __device__ void pack_record(const Consts& c, const uint32_t* ck, const uint32_t*
       for (int i = 0; i < c.d; ++i) w.put(codes[i], nbits);
     }
   };
-  put(rec, ck, c.kb);
+  if (c.polar) {
+    // level-1 angle codes as a pb1-bit stream, then levels 2..L (node order) as a pbh-bit
+    // stream zero-padded to the key field's whole words
+    ByteWriter w1{rec, 0, 0};
+    for (int i = 0; i < c.d / 2; ++i) w1.put(ck[i], c.pb1);
+    ByteWriter w2{rec + c.l1_bytes, 0, 0};
+    for (int i = c.d / 2; i < c.d - 1; ++i) w2.put(ck[i], c.pbh);
+    uint8_t* p = w2.dst;
+    if (w2.n > 0) *p++ = (uint8_t)w2.acc;
+    while (p < rec + c.kbytes) *p++ = 0;
+  } else {
+    put(rec, ck, c.kb);
+  }
   ByteWriter ws{rec + c.kbytes, 0, 0};
   for (int j = 0; j < c.m; ++j) ws.put(bits[j], 1);
   put(rec + c.kbytes + c.sbytes, cv, c.vb);
@@ -4638,9 +4708,25 @@ __global__ __launch_bounds__(1024) void monarch_promote_kernel(MonarchArgs M) {
       const uint8_t* rec = M.records + (unit * M.cold_cap + plist[pi]) * c.rec_bytes;
       const float* nrm = reinterpret_cast<const float*>(rec + c.norm_off);
       for (int i = threadIdx.x; i < 2 * D; i += blockDim.x) {
-        if (i < D) lev[0][i] = ((double)nrm[0] / c.sqrt_d) * (double)c.key_levels[field_code(rec, i, c.kb)];
-        else lev[1][i - D] = ((double)nrm[2] / c.sqrt_d) *
-                             (double)c.val_levels[field_code(rec + c.kbytes + c.sbytes, i - D, c.vb)];
+        if (i < D && c.polar) {
+          // r_k u_i, u_i the product of the cos / sin factors on coordinate i's path from the
+          // root (root first, as the inverse transform multiplies)
+          double u = 1.0;
+          for (int l = c.plevels; l >= 1; --l) {
+            const int node = i >> l, side = (i >> (l - 1)) & 1;
+            const int bits = l == 1 ? c.pb1 : c.pbh;
+            const int idx = l == 1 ? node : (D - (D >> (l - 1)) + node) - D / 2;
+            const uint8_t* fld = l == 1 ? rec : rec + c.l1_bytes;
+            const uint32_t code = (fld[(idx * bits) >> 3] >> ((idx * bits) & 7)) & ((1u << bits) - 1u);
+            u = mul64(u, M.pt.cs64[2 * ((l - 1) * 16 + code) + side]);
+          }
+          lev[0][i] = mul64((double)nrm[0], u);
+        } else if (i < D) {
+          lev[0][i] = ((double)nrm[0] / c.sqrt_d) * (double)c.key_levels[field_code(rec, i, c.kb)];
+        } else {
+          lev[1][i - D] = ((double)nrm[2] / c.sqrt_d) *
+                          (double)c.val_levels[field_code(rec + c.kbytes + c.sbytes, i - D, c.vb)];
+        }
       }
       __syncthreads();
       int64_t slot = st + n_hot + pi;
@@ -4696,6 +4782,9 @@ __global__ __launch_bounds__(1024) void monarch_promote_kernel(MonarchArgs M) {
 // work in each phase; float64 throughout, as compress_kernel and the oracle.
 constexpr int kMonarchMaxKvHeads = 16;
 
+// sketch-bit slots per head in the eviction's LDS, even so that what follows stays 8-byte aligned
+__host__ __device__ constexpr int c_m_words(int m) { return (m + 1) / 2 * 2; }
+
 template <int D>
 __global__ __launch_bounds__(512) void monarch_evict_kernel(MonarchArgs M) {
   constexpr int HM = kMonarchMaxKvHeads;
@@ -4705,6 +4794,7 @@ __global__ __launch_bounds__(512) void monarch_evict_kernel(MonarchArgs M) {
   double* er = xr + HM * 2 * D;                 // [H][D] key residual
   uint32_t* codes = reinterpret_cast<uint32_t*>(er + HM * D);   // [H][2][D]
   uint32_t* bits = codes + HM * 2 * D;          // [H][m]
+  double* pr = reinterpret_cast<double*>(bits + HM * c_m_words(M.c.m));   // [H][D] polar radii / scales
   __shared__ double nrm[HM][3];                 // r_k, r_v (float64), rho
   const int b = blockIdx.x, H = M.kv_heads;
   const Consts& c = M.c;
@@ -4745,16 +4835,56 @@ __global__ __launch_bounds__(512) void monarch_evict_kernel(MonarchArgs M) {
       xr[t] = acc;
       const double r = nrm[h][w];
       const double scale = r > 0.0 ? c.sqrt_d / r : 0.0;
-      codes[t] = quantize_code((float)(acc * scale), w ? c.val_bounds : c.key_bounds);
+      if (w || !c.polar) codes[t] = quantize_code((float)(acc * scale), w ? c.val_bounds : c.key_bounds);
     }
     __syncthreads();
-    // key residual e = x - (r_k / sqrt(d)) gamma[c] with r_k stored as float32
-    for (int t = threadIdx.x; t < H * D; t += blockDim.x) {
-      const int h = t / D, j = t % D;
-      const double rk = (double)(float)nrm[h][0];
-      er[t] = xr[h * 2 * D + j] - (rk / c.sqrt_d) * (double)c.key_levels[codes[h * 2 * D + j]];
+    if (c.polar) {
+      // polar key codes (TurboQuant page, "PolarQuant"), level by level with one thread per
+      // node: level l node i has its code and radius at index D - (D >> (l - 1)) + i
+      const int nb1 = (1 << c.pb1) - 1, nbh = (1 << c.pbh) - 1;
+      for (int l = 1; l <= c.plevels; ++l) {
+        const int cnt = D >> l, off = D - (D >> (l - 1)), coff = l == 1 ? 0 : D - (D >> (l - 2));
+        for (int t = threadIdx.x; t < H * cnt; t += blockDim.x) {
+          const int h = t / cnt, i = t % cnt;
+          const double a = l == 1 ? xr[h * 2 * D + 2 * i] : pr[h * D + coff + 2 * i];
+          const double bv = l == 1 ? xr[h * 2 * D + 2 * i + 1] : pr[h * D + coff + 2 * i + 1];
+          codes[h * 2 * D + off + i] = polar_code(polar_angle(a, bv), M.pt.bounds + (l - 1) * 16, l == 1 ? nb1 : nbh);
+          pr[h * D + off + i] = sqrt(add64(mul64(a, a), mul64(bv, bv)));
+        }
+        __syncthreads();
+      }
+      // the unit vector of the grid angles, top-down: a node's scale times the cos / sin of its
+      // angle is its children's (root scale 1, the multiplication order of the inverse transform)
+      for (int h = threadIdx.x; h < H; h += blockDim.x) pr[h * D + D - 2] = 1.0;
+      __syncthreads();
+      for (int l = c.plevels; l >= 2; --l) {
+        const int cnt = D >> l, off = D - (D >> (l - 1)), coff = D - (D >> (l - 2));
+        for (int t = threadIdx.x; t < H * cnt; t += blockDim.x) {
+          const int h = t / cnt, i = t % cnt;
+          const double sc = pr[h * D + off + i];
+          const double* cs = M.pt.cs64 + 2 * ((l - 1) * 16 + codes[h * 2 * D + off + i]);
+          pr[h * D + coff + 2 * i] = mul64(sc, cs[0]);
+          pr[h * D + coff + 2 * i + 1] = mul64(sc, cs[1]);
+        }
+        __syncthreads();
+      }
+      // key residual e = y - r_k u with r_k stored as float32
+      for (int t = threadIdx.x; t < H * D; t += blockDim.x) {
+        const int h = t / D, j = t % D;
+        const double* cs = M.pt.cs64 + 2 * codes[h * 2 * D + (j >> 1)];
+        const double u = mul64(pr[h * D + (j >> 1)], cs[j & 1]);
+        er[t] = sub64(xr[h * 2 * D + j], mul64((double)(float)nrm[h][0], u));
+      }
+      __syncthreads();
+    } else {
+      // key residual e = x - (r_k / sqrt(d)) gamma[c] with r_k stored as float32
+      for (int t = threadIdx.x; t < H * D; t += blockDim.x) {
+        const int h = t / D, j = t % D;
+        const double rk = (double)(float)nrm[h][0];
+        er[t] = xr[h * 2 * D + j] - (rk / c.sqrt_d) * (double)c.key_levels[codes[h * 2 * D + j]];
+      }
+      __syncthreads();
     }
-    __syncthreads();
     for (int h = threadIdx.x; h < H; h += blockDim.x) {
       double s = 0.0;
       for (int j = 0; j < D; ++j) s = fma(er[h * D + j], er[h * D + j], s);
@@ -4793,7 +4923,7 @@ __global__ __launch_bounds__(512) void monarch_evict_kernel(MonarchArgs M) {
 
 template <int D>
 size_t monarch_evict_lds(int m) {
-  return (size_t)kMonarchMaxKvHeads * (2 * D * 8 * 2 + D * 8 + 2 * D * 4 + (size_t)m * 4);
+  return (size_t)kMonarchMaxKvHeads * (2 * D * 8 * 2 + D * 8 + 2 * D * 4 + (size_t)c_m_words(m) * 4 + D * 8);
 }
 
 MonarchPlan plan_monarch(const Consts& c, int batch, int q_heads, int kv_heads, int64_t hot_cap,
@@ -4853,6 +4983,7 @@ hipError_t launch_monarch_step(const Consts& c, const DevConsts& dc, const Monar
   M.cold_gate = s.cold_gate;
   M.promote_weight = s.promote_weight;
   M.scale = s.scale > 0.0f ? s.scale : c.inv_sqrt_d;
+  M.pt = dc.polar;
   const dim3 g1(s.kv_heads, s.batch);
   if (c.d == 128) hipLaunchKernelGGL(monarch_prep_kernel<128>, g1, dim3(1024), 0, stream, M);
   else hipLaunchKernelGGL(monarch_prep_kernel<64>, g1, dim3(1024), 0, stream, M);

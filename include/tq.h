@@ -32,9 +32,10 @@
  *  - A handle is immutable after tq_create, so concurrent calls on different streams
  *    are allowed.  Calls that share a workspace or output buffer must be ordered.
  *  - A TQ_KEY_POLAR handle is accepted by tq_compress_kv, tq_decode_workspace_size,
- *    tq_decode_attention, tq_scan_workspace_size, tq_score_scan, tq_record_bytes and the
- *    sign-index / top-k calls (which read raw keys); tq_debug_quantize,
- *    tq_sparse_attention and the hot/cold step return TQ_ERR_UNSUPPORTED for it.
+ *    tq_decode_attention, tq_decode_attention_noalloc, tq_scan_workspace_size,
+ *    tq_score_scan, tq_record_bytes, the hot/cold step and the sign-index / top-k calls
+ *    (which read raw keys); tq_debug_quantize and tq_sparse_attention return
+ *    TQ_ERR_UNSUPPORTED for it.
  *  - Inputs must be finite.  Non-finite inputs give unspecified codes and outputs but
  *    never an out-of-bounds access.
  *
@@ -314,11 +315,13 @@ tq_status tq_set_profile_events(hipEvent_t start, hipEvent_t stop);
  *     the cold tokens (TurboQuant estimator, as tq_decode_attention), one softmax;
  *  3. a cold token whose weight p (maximum over the open heads) is >= cfg->promote_weight
  *     counts one more consecutive step, else its count resets; at cfg->promote_steps (0: never)
- *     it is promoted: k = Pi^T (r_k/sqrt(d)) gamma_k[c], v = Pi^T (r_v/sqrt(d)) gamma_v[c_v]
+ *     it is promoted: k = Pi^T (r_k/sqrt(d)) gamma_k[c] (polar keys: k = Pi^T (r_k u), u the
+ *     unit vector of the grid angles), v = Pi^T (r_v/sqrt(d)) gamma_v[c_v]
  *     (float64, rounded to hot_dt) join the ring as its newest tokens in ascending cold order,
  *     and the cold slots are freed by moving the last cold token into each, highest slot first;
  *  4. while the ring holds more than cfg->window tokens, its oldest are compressed (float64
- *     rotation, as tq_compress_kv) and appended to the cold region with count 0.
+ *     rotation, scalar or polar key codes as tq_compress_kv) and appended to the cold region
+ *     with count 0.
  * hot_capacity must be >= window + 1 + floor(1 / promote_weight) * q_heads (when promotion is
  * on).  gate_out (optional, [b][hq]) receives the step-2 decisions; lse is optional.
  * workspace: tq_monarch_workspace_size bytes.  All state stays on the device; the host is

@@ -20,12 +20,18 @@ numbers beyond the two command-line thresholds (0.15, 3) and leaves these readin
   (reset to 0 otherwise); at promote_steps the token is promoted.
 * M5 page swap: a promoted token is decompressed (k = Pi^T (r_k/sqrt(d)) gamma_k[c],
   v = Pi^T (r_v/sqrt(d)) gamma_v[c_v] in float64, rounded to the hot dtype; the QJL bits
-  cannot be undone) and joins the hot region as its newest token, promoted tokens in
-  ascending cold order; its cold slot is filled by the last cold token, slots handled
-  from the highest down.
+  cannot be undone; with polar key codes k = Pi^T (r_k u), u the unit vector of the grid
+  angles) and joins the hot region as its newest token, promoted tokens in ascending cold
+  order; its cold slot is filled by the last cold token, slots handled from the highest
+  down.
 * M6 eviction: while the hot region holds more than `window` tokens its oldest are
-  compressed (as tq_oracle.compress) and appended to the cold region with count 0; when
-  the cold region is full they are dropped and an overflow flag is set.
+  compressed (by the codec's own compress: tq_oracle.compress, or the polar codec's) and
+  appended to the cold region with count 0; when the cold region is full they are dropped
+  and an overflow flag is set.
+
+The codec is either tq_oracle.Codec or polar.PolarCodec (the Monarch page's cold tier codes
+keys with polar angles); the step calls only the codec's compress, pack, unpack and key
+reconstruction.
 """
 from __future__ import annotations
 
@@ -71,9 +77,9 @@ class HotColdOracle:
     def dequantize(self, rec: np.ndarray):
         """Promoted token of one KV head: its record -> (k, v) in the hot dtype (M5)."""
         c = self.codec
-        f = O.unpack_records(c, rec[None])
+        f = c.unpack(rec[None])
         sd = math.sqrt(c.head_dim)
-        xk = (float(f["r_k"][0]) / sd) * c.key_levels.astype(np.float64)[f["kc"][0]]
+        xk = c.key_vector(f)[0]
         xv = (float(f["r_v"][0]) / sd) * c.val_levels.astype(np.float64)[f["vc"][0]]
         return round_to(c.Pi64.T @ xk, self.dtype), round_to(c.Pi64.T @ xv, self.dtype)
 
@@ -142,7 +148,7 @@ class HotColdOracle:
             if keep:
                 kk = self.hot_k[b][:, :keep].astype(np.float32)
                 vv = self.hot_v[b][:, :keep].astype(np.float32)
-                recs = O.pack_records(c, O.compress(c, kk, vv))              # [H, keep, R]
+                recs = c.pack(c.compress_fields(kk, vv))                    # [H, keep, R]
                 self.cold[b] = np.concatenate([self.cold[b], recs], axis=1)
                 self.hits[b] = np.concatenate([self.hits[b], np.zeros(keep, np.int64)])
             if keep < e:

@@ -245,3 +245,8 @@ class PolarCodec(O.Codec):
     def key_part(self, qx, f):
         """r_t <q_x, u_t> (reading P6)."""
         return f["r_k"].astype(np.float64) * (self.unit_vector(f["kc"]) @ qx)
+
+    def key_vector(self, f):
+        """The stage-1 reconstruction of the keys in the rotated basis, r_k u (reading P5),
+        float64."""
+        return f["r_k"].astype(np.float64)[..., None] * self.unit_vector(f["kc"])

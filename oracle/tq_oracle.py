@@ -222,6 +222,12 @@ class Codec:
         gk = self.key_levels.astype(np.float64)
         return (f["r_k"].astype(np.float64) / math.sqrt(self.head_dim)) * (gk[f["kc"]] @ qx)
 
+    def key_vector(self, f):
+        """The stage-1 reconstruction of the keys in the rotated basis, xhat = (r_k/sqrt(d))
+        gamma[c] (float64) - what a promoted cold key is rebuilt from."""
+        gk = self.key_levels.astype(np.float64)
+        return (f["r_k"].astype(np.float64) / math.sqrt(self.head_dim))[..., None] * gk[f["kc"]]
+
 
 # ----------------------------------------------------------------------------------------
 # Compression (TurboQuant page, "Funktionsweise" steps 1 and 2)

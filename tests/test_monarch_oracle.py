@@ -117,3 +117,49 @@ def test_swap_remove_order_and_overflow():
     assert np.array_equal(o.cold[0][:, [0, 2, 3, 5]], before[:, [0, 2, 3, 5]])
     assert o.cold[0].shape[1] == 8 and o.hot_k[0].shape[1] == 2 and o.overflow[0]
     assert np.array_equal(o.hits[0], [0, 0, 0, 0, 0, 0, 0, 0])
+
+
+def _polar_codec():
+    from oracle import polar as P
+    return P.PolarCodec(D, 4, 64, 4, 11, 12, upper_bits=2)
+
+
+def test_polar_keys_evict_through_the_polar_compress():
+    """With polar key codes (the Monarch page's cold tier) eviction writes exactly the polar
+    codec's records of the evicted tokens, in order."""
+    c, rng = _polar_codec(), np.random.default_rng(5)
+    o = M.HotColdOracle(c, 1, 2, "float16", 100)
+    ks, vs = _tok(rng, 9, 2), _tok(rng, 9, 2)
+    q = rng.standard_normal((1, 4, D))
+    for s in range(9):
+        o.step(q, ks[s:s + 1], vs[s:s + 1], window=3, promote_steps=0)
+    ref = c.pack(c.compress_fields(np.transpose(ks[:6], (1, 0, 2)).astype(np.float32),
+                                   np.transpose(vs[:6], (1, 0, 2)).astype(np.float32)))
+    assert np.array_equal(o.cold[0], ref)
+
+
+def test_polar_promoted_key_is_the_rotated_back_polar_reconstruction():
+    """A promoted polar key is Pi^T (r_k u): its norm is the stored radius (u has unit norm and
+    Pi is orthogonal to float32 rounding), it points along the original key, and the step's
+    ring holds exactly that vector rounded to the hot dtype."""
+    from oracle import polar as P
+    c, rng = _polar_codec(), np.random.default_rng(6)
+    o = M.HotColdOracle(c, 1, 1, "float32", 100)
+    ks, vs = _tok(rng, 20), _tok(rng, 20)
+    q0 = rng.standard_normal((1, 1, D))
+    for s in range(8):
+        o.step(q0, ks[s:s + 1], vs[s:s + 1], window=4, promote_steps=0)
+    target = 1
+    rec = o.cold[0][0, target].copy()
+    q = (6.0 * ks[target, 0] / np.linalg.norm(ks[target, 0]) * math.sqrt(D) / 8.0)[None, None]
+    for s in range(8, 11):
+        _, _, gate, w = o.step(q, ks[s:s + 1], vs[s:s + 1], window=4)
+        assert gate[0, 0] and w[0][target] > 0.5
+    f = c.unpack(rec[None])
+    ang = [c.angle_levels[l].astype(np.float64)[f["kc"][l][0]] for l in range(c.L)]
+    u = P.polar_inverse(np.ones(()), ang)
+    assert abs(np.linalg.norm(u) - 1.0) < 1e-14
+    k_prom = M.round_to(c.Pi64.T @ (float(f["r_k"][0]) * u), "float32")
+    assert any(np.array_equal(k_prom, o.hot_k[0][0, j]) for j in range(o.hot_k[0].shape[1]))
+    assert abs(np.linalg.norm(k_prom) / f["r_k"][0] - 1.0) < 1e-6
+    assert np.dot(k_prom, ks[target, 0]) / (np.linalg.norm(k_prom) * np.linalg.norm(ks[target, 0])) > 0.9
