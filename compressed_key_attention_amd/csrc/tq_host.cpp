@@ -953,10 +953,6 @@ tq_status tq_sparse_workspace_size(const tq_handle* h, int32_t batch, int32_t q_
     tq_status dst;
     if (dim_unsupported(h, "sparse attention", &dst)) return dst;
   }
-  {
-    tq_status pst;
-    if (polar_unsupported(h, "sparse attention", &pst)) return pst;
-  }
   if (!h || !bytes) return fail(TQ_ERR_INVALID_ARGUMENT, "NULL handle or output");
   if (batch < 0 || q_heads <= 0 || kv_heads <= 0 || q_heads % kv_heads || capacity < 0)
     return fail(TQ_ERR_INVALID_ARGUMENT, "bad shape");
@@ -974,10 +970,6 @@ tq_status tq_sparse_attention(const tq_handle* h, const void* q, tq_dtype q_dt, 
   {
     tq_status dst;
     if (dim_unsupported(h, "sparse attention", &dst)) return dst;
-  }
-  {
-    tq_status pst;
-    if (polar_unsupported(h, "sparse attention", &pst)) return pst;
   }
   if (!h) return fail(TQ_ERR_INVALID_ARGUMENT, "handle is NULL");
   size_t es;

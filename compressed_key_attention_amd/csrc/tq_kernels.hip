@@ -3497,10 +3497,16 @@ struct SparseArgs {
   int k;
 };
 
-template <int D, int BK, int BV, int MG>
+// POLAR: polar key codes; each token's unit vector u is rebuilt into LDS (float32, one thread
+// per (token, level-1 pair): the root-first product of the cos / sin factors on its path) and
+// the key part of the estimate is r_k <q_x, u>.
+template <int D, int BK, int BV, int MG, bool POLAR = false>
 __global__ __launch_bounds__(kSmallThreads) void sparse_attend_kernel(SparseArgs S) {
   const DecodeArgs& A = S.a;
   constexpr int NG32 = D / 32, TB = kSmallMaxTok, kPer = kSelChunk / kSmallThreads;
+  constexpr int KRW = POLAR ? 16 : 1;              // polar key field words per token (at most 64 bytes)
+  __shared__ uint32_t kraw[POLAR ? TB : 1][KRW];
+  __shared__ float ku[POLAR ? TB : 1][POLAR ? D + 1 : 1];
   __shared__ uint16_t list[kSelChunk];             // selected tokens, offsets within the chunk
   __shared__ int wsum[kSmallThreads / 64];
   __shared__ int s_nsel;
@@ -3584,7 +3590,11 @@ __global__ __launch_bounds__(kSmallThreads) void sparse_attend_kernel(SparseArgs
     for (int e = tid; e < nt * per_t; e += kSmallThreads) {
       const int t = e / per_t, pt = e % per_t;
       const uint8_t* rec = recs + (t0 + list[s0 + t]) * A.rec_bytes;
-      if (pt < 2 * NG32) {
+      if (POLAR && pt < NG32) {
+        // the raw key field (level-1 stream, upper-level stream), unpacked below
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(rec);
+        for (int i = pt; i < A.kbytes / 4; i += NG32) kraw[t][i] = src[i];
+      } else if (pt < 2 * NG32) {
         const bool key = pt < NG32;
         const int g = key ? pt : pt - NG32;
         uint32_t w[4];
@@ -3633,6 +3643,24 @@ __global__ __launch_bounds__(kSmallThreads) void sparse_attend_kernel(SparseArgs
       }
     }
     __syncthreads();
+    if constexpr (POLAR) {
+      const int np = D / 2, l1w = A.l1_bytes / 4;
+      for (int e = tid; e < nt * np; e += kSmallThreads) {
+        const int t = e / np, pair = e % np;
+        float sc = 1.0f;
+        for (int l = A.plevels; l >= 2; --l) {
+          const int node = pair >> (l - 1), side = (pair >> (l - 2)) & 1;
+          const int idx = (D - (D >> (l - 1)) + node) - D / 2, pos = idx * A.pbh;
+          const uint32_t code = (kraw[t][l1w + (pos >> 5)] >> (pos & 31)) & ((1u << A.pbh) - 1u);
+          sc *= A.pcs[2 * ((l - 1) * 16 + code) + side];
+        }
+        const int pos1 = pair * A.pb1;
+        const uint32_t c1 = (kraw[t][pos1 >> 5] >> (pos1 & 31)) & ((1u << A.pb1) - 1u);
+        ku[t][2 * pair] = sc * A.pcs[2 * c1];
+        ku[t][2 * pair + 1] = sc * A.pcs[2 * c1 + 1];
+      }
+      __syncthreads();
+    }
     const int items = nt * G;
     int L = 1;
     while (L < 8 && items * L * 2 <= kSmallThreads) L *= 2;
@@ -3641,7 +3669,10 @@ __global__ __launch_bounds__(kSmallThreads) void sparse_attend_kernel(SparseArgs
       const int t = it / G, h = it % G;
       float dot = 0.0f, qd = 0.0f;
       if (it < items) {
-        for (int i = s; i < D; i += L) dot = fmaf(qx[h][i], kl[kc[t][i]], dot);
+        if constexpr (POLAR)
+          for (int i = s; i < D; i += L) dot = fmaf(qx[h][i], ku[t][i], dot);
+        else
+          for (int i = s; i < D; i += L) dot = fmaf(qx[h][i], kl[kc[t][i]], dot);
         for (int j = s; j < m; j += L) qd += sb[t][j] ? qs[h][j] : -qs[h][j];
       }
       for (int msk = 1; msk < L; msk <<= 1) {
@@ -3649,7 +3680,7 @@ __global__ __launch_bounds__(kSmallThreads) void sparse_attend_kernel(SparseArgs
         qd += __shfl_xor(qd, msk);
       }
       if (it < items && s == 0)
-        lg[h][t] = A.scale * fmaf(A.qjl_coef * nr[t][1], qd, nr[t][0] * A.inv_sqrt_d * dot);
+        lg[h][t] = A.scale * fmaf(A.qjl_coef * nr[t][1], qd, nr[t][0] * (POLAR ? 1.0f : A.inv_sqrt_d) * dot);
     }
     __syncthreads();
     // online softmax over this batch: one wave per head, one lane per token
@@ -3729,7 +3760,13 @@ SparsePlan plan_sparse(const Consts& c, int batch, int q_heads, int kv_heads, in
 }
 
 template <int D, int MG>
-static void launch_sparse_d(const SparseArgs& s, int kb, int vb, dim3 grid, hipStream_t st) {
+static void launch_sparse_d(const SparseArgs& s, int kb, int vb, bool polar, dim3 grid, hipStream_t st) {
+  if (polar) {
+    if (vb == 2) hipLaunchKernelGGL((sparse_attend_kernel<D, 4, 2, MG, true>), grid, dim3(kSmallThreads), 0, st, s);
+    else if (vb == 3) hipLaunchKernelGGL((sparse_attend_kernel<D, 4, 3, MG, true>), grid, dim3(kSmallThreads), 0, st, s);
+    else hipLaunchKernelGGL((sparse_attend_kernel<D, 4, 4, MG, true>), grid, dim3(kSmallThreads), 0, st, s);
+    return;
+  }
 #define TQ_SP(BK_, BV_)                                                                               \
   if (kb == BK_ && vb == BV_) {                                                                       \
     hipLaunchKernelGGL((sparse_attend_kernel<D, BK_, BV_, MG>), grid, dim3(kSmallThreads), 0, st, s); \
@@ -3789,6 +3826,11 @@ hipError_t launch_sparse(const Consts& c, const DevConsts& dc, const SparsePlan&
     a.key_levels[i] = c.key_levels[i];
     a.val_levels[i] = c.val_levels[i];
   }
+  a.pcs = dc.polar.cs32;
+  a.pb1 = c.pb1;
+  a.pbh = c.pbh;
+  a.plevels = c.plevels;
+  a.l1_bytes = c.l1_bytes;
   s.scores = reinterpret_cast<const int32_t*>(ws + plan.ws_select + sp.ws_scores);
   s.params = reinterpret_cast<const SelectParams*>(ws + plan.ws_select + sp.ws_params);
   s.chunk_off = reinterpret_cast<const int32_t*>(ws + plan.ws_select + sp.ws_chunk_off);
@@ -3796,10 +3838,10 @@ hipError_t launch_sparse(const Consts& c, const DevConsts& dc, const SparsePlan&
   const dim3 grid((unsigned)n_chunks, kv_heads, batch);
   // query rows held in LDS sized for the group (a smaller footprint keeps more workgroups per CU)
   const int G = q_heads / kv_heads;
-  if (c.d == 128 && G <= 4) launch_sparse_d<128, 4>(s, c.kb, c.vb, grid, stream);
-  else if (c.d == 128) launch_sparse_d<128, kSmallMaxG>(s, c.kb, c.vb, grid, stream);
-  else if (G <= 4) launch_sparse_d<64, 4>(s, c.kb, c.vb, grid, stream);
-  else launch_sparse_d<64, kSmallMaxG>(s, c.kb, c.vb, grid, stream);
+  if (c.d == 128 && G <= 4) launch_sparse_d<128, 4>(s, c.kb, c.vb, c.polar != 0, grid, stream);
+  else if (c.d == 128) launch_sparse_d<128, kSmallMaxG>(s, c.kb, c.vb, c.polar != 0, grid, stream);
+  else if (G <= 4) launch_sparse_d<64, 4>(s, c.kb, c.vb, c.polar != 0, grid, stream);
+  else launch_sparse_d<64, kSmallMaxG>(s, c.kb, c.vb, c.polar != 0, grid, stream);
   MergeArgs mg{};
   mg.pi_t = dc.pi_t;
   mg.part = part;

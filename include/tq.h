@@ -33,9 +33,9 @@
  *    are allowed.  Calls that share a workspace or output buffer must be ordered.
  *  - A TQ_KEY_POLAR handle is accepted by tq_compress_kv, tq_decode_workspace_size,
  *    tq_decode_attention, tq_decode_attention_noalloc, tq_scan_workspace_size,
- *    tq_score_scan, tq_record_bytes, the hot/cold step and the sign-index / top-k calls
- *    (which read raw keys); tq_debug_quantize and tq_sparse_attention return
- *    TQ_ERR_UNSUPPORTED for it.
+ *    tq_score_scan, tq_record_bytes, the hot/cold step, tq_sparse_attention and the
+ *    sign-index / top-k calls (which read raw keys); tq_debug_quantize (scalar codes from
+ *    given rotated coordinates) returns TQ_ERR_UNSUPPORTED for it.
  *  - Inputs must be finite.  Non-finite inputs give unspecified codes and outputs but
  *    never an out-of-bounds access.
  *
@@ -265,8 +265,8 @@ tq_status tq_select_topk(const tq_handle* h, const void* q, tq_dtype q_dt, int32
  * tq_decode_attention(q, records, seq_lens, exact segment, sel_idx = the out_idx that
  * tq_select_topk(q, index, codebook, seq_lens, k) returns, scale): the same top-k set (same
  * ranking and tie rule), the same estimator, one softmax with the optional exact segment
- * (hot_k / hot_v / hot_lens, e.g. always-attended sink tokens).  The selected indices are
- * not written out.  Requires qjl_dim in {0, 32, 64, 96, 128} and at most 16 query heads per
+ * (hot_k / hot_v / hot_lens, e.g. always-attended sink tokens); scalar or polar key codes.
+ * The selected indices are not written out.  Requires qjl_dim in {0, 32, 64, 96, 128} and at most 16 query heads per
  * KV head.  workspace: tq_sparse_workspace_size bytes (256-byte aligned).  Nothing is
  * allocated; the host is not synchronised. */
 tq_status tq_sparse_workspace_size(const tq_handle* h, int32_t batch, int32_t q_heads,

@@ -502,19 +502,24 @@ def test_sparse_with_exact_sinks(kb, vb):
     _close(out.cpu().numpy(), ref, f"sparse + sinks kb={kb} vb={vb}")
 
 
-@pytest.mark.parametrize("kb,vb,m,hq,k,lens,sinks", [
-    (4, 4, 0, 8, 300, [5000, 4097], 0),       # one query head per KV head (the sparse family)
-    (2, 2, 0, 8, 1000, [9000, 123], 64),      # 2-bit payload, 64 exact sink tokens
-    (3, 4, 128, 32, 500, [6000, 6000], 0),    # 4 query heads per KV head, 128-bit sketch
-    (4, 4, 64, 16, 0, [300, 300], 16),        # k = 0: the sink tokens only
-    (4, 4, 0, 8, 5000, [4500, 100], 0),       # k >= n: every token
+@pytest.mark.parametrize("kb,vb,m,hq,k,lens,sinks,ub,d", [
+    (4, 4, 0, 8, 300, [5000, 4097], 0, 0, 128),       # one query head per KV head (the sparse family)
+    (2, 2, 0, 8, 1000, [9000, 123], 64, 0, 128),      # 2-bit payload, 64 exact sink tokens
+    (3, 4, 128, 32, 500, [6000, 6000], 0, 0, 128),    # 4 query heads per KV head, 128-bit sketch
+    (4, 4, 64, 16, 0, [300, 300], 16, 0, 128),        # k = 0: the sink tokens only
+    (4, 4, 0, 8, 5000, [4500, 100], 0, 0, 128),       # k >= n: every token
+    (4, 4, 0, 8, 700, [5000, 4097], 0, 2, 128),       # polar keys (4-bit level-1, 2-bit upper angles)
+    (4, 4, 128, 32, 500, [6000, 3000], 64, 4, 128),   # polar keys, sketch, G = 4, sinks
+    (2, 3, 64, 16, 400, [3000, 2500], 32, 1, 64),     # polar keys at head_dim 64
 ])
-def test_sparse_attention_one_call(kb, vb, m, hq, k, lens, sinks):
+def test_sparse_attention_one_call(kb, vb, m, hq, k, lens, sinks, ub, d):
     """tq_sparse_attention (selection and attention in one call, no index list) against the
-    oracle's select_topk followed by its gathered decode, with the exact segment as sinks."""
+    oracle's select_topk followed by its gathered decode, with the exact segment as sinks;
+    scalar and polar key codes."""
     T = max(lens) + sinks
     base = W.small(W.WORKLOADS["sparse_128k_top2048"], tokens=T, batch=len(lens), top_k=max(k, 1))
-    w = W.Workload(**{**base.__dict__, "key_bits": kb, "value_bits": vb, "qjl_dim": m, "q_heads": hq})
+    w = W.Workload(**{**base.__dict__, "key_bits": kb, "value_bits": vb, "qjl_dim": m, "q_heads": hq,
+                      "polar_upper_bits": ub, "head_dim": d})
     h = _handle(w)
     codec = _codec(h)
     K, V = W.make_kv(w, "cuda")

@@ -149,10 +149,16 @@ def test_polar_bulk_scan(d, b1, bh, m, vb):
 
 
 def test_polar_rejected_where_not_built():
+    """tq_debug_quantize takes scalar codes from given rotated coordinates: not built for a
+    polar handle."""
     tq = GP._tq()
     h = GP._handle(_wl(tokens=16, batch=1))
+    z = torch.zeros((4, 128), device="cuda")
+    p = torch.zeros((4, 128), device="cuda")
+    r = torch.ones((4,), device="cuda")
+    rec = torch.zeros((4, h.record_bytes), dtype=torch.uint8, device="cuda")
     with pytest.raises(tq.TqError) as e:
-        h.sparse_workspace_size(1, 8, 8, 4096)
+        h.debug_quantize(z, p, r, r, z, r, rec)
     assert e.value.status == tq.TQ_ERR_UNSUPPORTED
 
 
