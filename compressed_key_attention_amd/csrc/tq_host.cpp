@@ -331,8 +331,6 @@ tq_status check_config(const tq_config* cfg) {
     return fail(TQ_ERR_UNSUPPORTED, "head_dim %d not built (a multiple of 8 up to 256)", cfg->head_dim);
   if (cfg->key_codec == TQ_KEY_POLAR && cfg->head_dim != 64 && cfg->head_dim != 128)
     return fail(TQ_ERR_UNSUPPORTED, "polar keys need head_dim 64 or 128");
-  if (cfg->key_bits < 2 || cfg->value_bits < 2)
-    return fail(TQ_ERR_UNSUPPORTED, "1-bit stage-1 codes are not built (key/value bits 2..4)");
   if (cfg->key_codec == TQ_KEY_SCALAR) {
     if (cfg->polar_upper_bits != 0)
       return fail(TQ_ERR_INVALID_ARGUMENT, "polar_upper_bits must be 0 for the scalar key codec");

@@ -1402,6 +1402,7 @@ static void launch_small_d(const DecodeArgs& a, int kb, int vb, dim3 grid, hipSt
     hipLaunchKernelGGL((decode_small_kernel<D, BK_, BV_>), grid, dim3(kSmallThreads), 0, st, a);  \
     return;                                                                                       \
   }
+  TQ_SM(1, 1) TQ_SM(1, 2) TQ_SM(1, 3) TQ_SM(1, 4) TQ_SM(2, 1) TQ_SM(3, 1) TQ_SM(4, 1)
   TQ_SM(2, 2) TQ_SM(2, 3) TQ_SM(2, 4) TQ_SM(3, 2) TQ_SM(3, 3) TQ_SM(3, 4)
   TQ_SM(4, 2) TQ_SM(4, 3) TQ_SM(4, 4)
 #undef TQ_SM
@@ -2527,7 +2528,7 @@ static void launch_scan_hpl(const DecodeArgs& a, int kb, int vb, bool polar, dim
       hipLaunchKernelGGL((decode_scan_kernel<HPL, 4, BV_, true>), grid, dim3(kDecodeThreads), lds, st, a); \
       return;                                                                                    \
     }
-    TQ_DECP(2) TQ_DECP(3) TQ_DECP(4)
+    TQ_DECP(1) TQ_DECP(2) TQ_DECP(3) TQ_DECP(4)
 #undef TQ_DECP
     return;
   }
@@ -2537,6 +2538,7 @@ static void launch_scan_hpl(const DecodeArgs& a, int kb, int vb, bool polar, dim
     hipLaunchKernelGGL((decode_scan_kernel<HPL, BK_, BV_>), grid, dim3(kDecodeThreads), lds, st, a); \
     return;                                                                                      \
   }
+  TQ_DEC(1, 1) TQ_DEC(1, 2) TQ_DEC(1, 3) TQ_DEC(1, 4) TQ_DEC(2, 1) TQ_DEC(3, 1) TQ_DEC(4, 1)
   TQ_DEC(2, 2) TQ_DEC(2, 3) TQ_DEC(2, 4) TQ_DEC(3, 2) TQ_DEC(3, 3) TQ_DEC(3, 4)
   TQ_DEC(4, 2) TQ_DEC(4, 3) TQ_DEC(4, 4)
 #undef TQ_DEC
@@ -3762,7 +3764,8 @@ SparsePlan plan_sparse(const Consts& c, int batch, int q_heads, int kv_heads, in
 template <int D, int MG>
 static void launch_sparse_d(const SparseArgs& s, int kb, int vb, bool polar, dim3 grid, hipStream_t st) {
   if (polar) {
-    if (vb == 2) hipLaunchKernelGGL((sparse_attend_kernel<D, 4, 2, MG, true>), grid, dim3(kSmallThreads), 0, st, s);
+    if (vb == 1) hipLaunchKernelGGL((sparse_attend_kernel<D, 4, 1, MG, true>), grid, dim3(kSmallThreads), 0, st, s);
+    else if (vb == 2) hipLaunchKernelGGL((sparse_attend_kernel<D, 4, 2, MG, true>), grid, dim3(kSmallThreads), 0, st, s);
     else if (vb == 3) hipLaunchKernelGGL((sparse_attend_kernel<D, 4, 3, MG, true>), grid, dim3(kSmallThreads), 0, st, s);
     else hipLaunchKernelGGL((sparse_attend_kernel<D, 4, 4, MG, true>), grid, dim3(kSmallThreads), 0, st, s);
     return;
@@ -3772,6 +3775,7 @@ static void launch_sparse_d(const SparseArgs& s, int kb, int vb, bool polar, dim
     hipLaunchKernelGGL((sparse_attend_kernel<D, BK_, BV_, MG>), grid, dim3(kSmallThreads), 0, st, s); \
     return;                                                                                           \
   }
+  TQ_SP(1, 1) TQ_SP(1, 2) TQ_SP(1, 3) TQ_SP(1, 4) TQ_SP(2, 1) TQ_SP(3, 1) TQ_SP(4, 1)
   TQ_SP(2, 2) TQ_SP(2, 3) TQ_SP(2, 4) TQ_SP(3, 2) TQ_SP(3, 3) TQ_SP(3, 4)
   TQ_SP(4, 2) TQ_SP(4, 3) TQ_SP(4, 4)
 #undef TQ_SP
@@ -4106,7 +4110,7 @@ __global__ __launch_bounds__(256, 2) void scan_mfma16_kernel(Scan16Args A) {
           pu[2 * i + 1] = (float)(s1[i] * tc.y);
         }
       }
-      const bool plain = kb != 3 && c0 + 16 <= A.d;   // 16 key codes of 2 or 4 bits: one run of bits
+      const bool plain = kb != 3 && c0 + 16 <= A.d;   // 16 key codes of 1, 2 or 4 bits: one run of bits
       uint32_t kr0 = 0u, kr1 = 0u;
       if (plain) {
         const int bit = c0 * kb;
@@ -4126,8 +4130,9 @@ __global__ __launch_bounds__(256, 2) void scan_mfma16_kernel(Scan16Args A) {
         } else if (k < A.d) {
           uint32_t pidx;
           if (plain) {
-            const int sh = 2 * kb * e2;                 // < 32 for kb = 2; kb = 4: words of 4 pairs
-            pidx = kb == 4 ? ((e2 < 4 ? kr0 : kr1) >> (8 * (e2 & 3))) & 0xFFu : (kr0 >> sh) & 0xFu;
+            const int sh = 2 * kb * e2;                 // < 32 for kb = 1, 2; kb = 4: words of 4 pairs
+            pidx = kb == 4 ? ((e2 < 4 ? kr0 : kr1) >> (8 * (e2 & 3))) & 0xFFu
+                           : (kr0 >> sh) & ((1u << (2 * kb)) - 1u);
           } else {
             pidx = key_code_at(kw, k, A.d, kb) | (key_code_at(kw, k + 1, A.d, kb) << kb);
           }

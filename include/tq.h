@@ -48,7 +48,7 @@
  *    [ zero pad to a multiple of 16 bytes ]
  *  so record_bytes = 16 * ceil((KB + qjl_dim / 8 + VB + 12) / 16) (tq_record_bytes); e.g.
  *  head_dim 128, 3-bit keys, qjl_dim 128, 4-bit values: 48 + 16 + 64 + 12 -> 144 bytes.
- *  2- and 4-bit code fields and the sign field are little-endian bitstreams: code i occupies
+ *  1-, 2- and 4-bit code fields and the sign field are little-endian bitstreams: code i occupies
  *  stream bits [b*i, b*i + b), stream bit n being bit n % 8 of byte n / 8.
  *  3-bit code fields are groups of 32 codes; group g is the 12 bytes at 12 g, read as
  *  little-endian 32-bit words W0, W1, W2.  Code j < 24 of a group occupies bits
@@ -108,11 +108,10 @@ typedef struct tq_config {
   int32_t head_dim;       /* d: 64 or 128 for every call; any multiple of 8 up to 256
                              for tq_compress_kv and tq_score_scan (the other calls
                              return TQ_ERR_UNSUPPORTED for such a handle)              */
-  int32_t key_bits;       /* b_k: bits per rotated key coordinate, 2..4 (1 is a valid
-                             width but not built: tq_create returns
-                             TQ_ERR_UNSUPPORTED); polar: bits per level-1 angle, 2 or 4 */
+  int32_t key_bits;       /* b_k: bits per rotated key coordinate, 1..4; polar: bits
+                             per level-1 angle, 2 or 4                                 */
   int32_t qjl_dim;        /* m: 0 (no QJL sketch) or a multiple of 32, at most 256     */
-  int32_t value_bits;     /* b_v: 2..4 (1: TQ_ERR_UNSUPPORTED, as for keys)            */
+  int32_t value_bits;     /* b_v: 1..4                                                 */
   uint64_t rotation_seed; /* seed of the Gaussian matrix whose QR factor is Pi         */
   uint64_t qjl_seed;      /* seed of the QJL projection S                              */
   int32_t key_codec;      /* tq_key_codec (0 = scalar)                                 */

@@ -27,7 +27,8 @@ def test_library_exports_every_declared_symbol():
 
 
 @pytest.mark.parametrize("cfg", [(128, 3, 128, 4, 303, 304), (64, 3, 64, 4, 1, 2),
-                                 (128, 4, 0, 4, 7, 8), (64, 2, 32, 2, 11, 12), (128, 2, 256, 3, 5, 6)])
+                                 (128, 4, 0, 4, 7, 8), (64, 2, 32, 2, 11, 12), (128, 2, 256, 3, 5, 6),
+                                 (64, 1, 32, 1, 3, 4), (128, 1, 128, 4, 9, 10)])
 def test_host_constants_equal_oracle(cfg):
     """Library (C++ SplitMix64 + Box-Muller + Householder QR + Lloyd-Max) and oracle
     (Python generator + LAPACK QR + scipy Lloyd-Max) are independent implementations of one
@@ -58,7 +59,8 @@ def _cfg(**kw):
     (dict(key_codec=1, key_bits=3, polar_upper_bits=2), 2), (dict(key_codec=1, polar_upper_bits=3), 2),
     (dict(key_codec=2), 1), (dict(polar_upper_bits=1), 1),
     (dict(key_codec=1, head_dim=200, key_bits=4, polar_upper_bits=2), 2), (dict(key_bits=5), 1), (dict(value_bits=0), 1),
-    (dict(qjl_dim=48), 1), (dict(qjl_dim=512), 1), (dict(key_bits=1), 2), (dict(qjl_dim=-32), 1)])
+    (dict(qjl_dim=48), 1), (dict(qjl_dim=512), 1), (dict(key_codec=1, key_bits=1, polar_upper_bits=2), 2),
+    (dict(qjl_dim=-32), 1)])
 def test_config_validation_on_host(kw, status):
     import compressed_key_attention_amd as tq
     cfg = _cfg(**kw)

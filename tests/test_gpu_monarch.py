@@ -29,20 +29,22 @@ def _close(gpu, ref, what):
     assert not bad.any(), f"{what}: {bad.sum()} of {bad.size} outside tolerance, worst {np.max(np.abs(gpu - ref)):.3e}"
 
 
-@pytest.mark.parametrize("d,m,dtype,gate,ub", [(64, 64, "float16", math.inf, 0), (128, 128, "bfloat16", 6.0, 0),
-                                               (64, 64, "float32", 6.0, 0), (128, 0, "float16", 6.0, 0),
-                                               (128, 128, "bfloat16", 6.0, 2), (64, 64, "float16", math.inf, 2),
-                                               (64, 32, "float32", 6.0, 4), (128, 0, "float16", 6.0, 1)])
-def test_hot_cold_steps_match_the_oracle(d, m, dtype, gate, ub):
+@pytest.mark.parametrize("d,m,dtype,gate,ub,kb,vb", [
+    (64, 64, "float16", math.inf, 0, 3, 4), (128, 128, "bfloat16", 6.0, 0, 3, 4),
+    (64, 64, "float32", 6.0, 0, 3, 4), (128, 0, "float16", 6.0, 0, 3, 4),
+    (128, 128, "bfloat16", 6.0, 2, 4, 4), (64, 64, "float16", math.inf, 2, 4, 4),
+    (64, 32, "float32", 6.0, 4, 4, 4), (128, 0, "float16", 6.0, 1, 4, 4),
+    (64, 64, "float16", math.inf, 0, 1, 1), (128, 128, "bfloat16", 6.0, 0, 1, 4)])
+def test_hot_cold_steps_match_the_oracle(d, m, dtype, gate, ub, kb, vb):
     """ub > 0: polar key codes (4-bit level-1 angles, ub bits per higher angle), the Monarch
-    page's polar cold tier: eviction runs the polar transform, promotion rebuilds r_k u."""
+    page's polar cold tier: eviction runs the polar transform, promotion rebuilds r_k u.
+    kb, vb: scalar key / value code widths (1-bit codes included)."""
     import compressed_key_attention_amd as tq
     from oracle import polar as P
     B, Hq, Hkv, Wn, cold_cap, steps = 2, 8, 2, 16, 40, 64
     G = Hq // Hkv
-    kb = 4 if ub else 3
-    h = tq.Handle(d, kb, m, 4, 31, 32, polar_upper_bits=ub)
-    codec = P.PolarCodec(d, kb, m, 4, 31, 32, upper_bits=ub) if ub else O.Codec(d, kb, m, 4, 31, 32)
+    h = tq.Handle(d, kb, m, vb, 31, 32, polar_upper_bits=ub)
+    codec = P.PolarCodec(d, kb, m, vb, 31, 32, upper_bits=ub) if ub else O.Codec(d, kb, m, vb, 31, 32)
     hot_cap = Wn + 1 + 6 * Hq
     st = tq.HotCold(h, B, Hkv, hot_cap, cold_cap, _DT[dtype])
     ora = MO.HotColdOracle(codec, B, Hkv, dtype, cold_cap)
