@@ -82,10 +82,14 @@ __device__ __forceinline__ float load_elem(const void* base, tq_dtype dt, int64_
 
 // Code of a float32 coordinate: number of boundaries it reaches, c = #{j : z >= tau_j}.
 // Unused boundary slots hold +inf.
+// #{j : z >= bounds[j]} over the kMaxLevels - 1 = 15 ascending bounds (padded with +inf past
+// the codebook's), by a four-step binary search: the same count as comparing all of them
 __device__ __forceinline__ uint32_t quantize_code(float z, const float* bounds) {
   uint32_t c = 0;
-#pragma unroll
-  for (int j = 0; j < kMaxLevels - 1; ++j) c += (z >= bounds[j]) ? 1u : 0u;
+  c += z >= bounds[c + 7] ? 8u : 0u;
+  c += z >= bounds[c + 3] ? 4u : 0u;
+  c += z >= bounds[c + 1] ? 2u : 0u;
+  c += z >= bounds[c] ? 1u : 0u;
   return c;
 }
 
@@ -384,8 +388,13 @@ __device__ __forceinline__ void polar_pack(const uint8_t* codes, int d, int b1, 
   }
 }
 
+// 512 threads (two waves per SIMD, sharing Pi and S in LDS) for scalar codes, so one wave's
+// matrix-core products overlap the other's loads and epilogue; 256 for polar codes, whose
+// angle work needs more registers than two waves per SIMD allow
+constexpr int compress_threads(bool polar) { return polar ? 256 : 512; }
+
 template <int D, bool POLAR>
-__global__ __launch_bounds__(256) void compress_kernel(CompressArgs A) {
+__global__ __launch_bounds__(compress_threads(POLAR)) void compress_kernel(CompressArgs A) {
   constexpr int Q = D / 4, CT = D / 16;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const Consts& c = A.c;
@@ -727,7 +736,7 @@ hipError_t launch_compress(const Consts& c, const DevConsts& dc, const void* k, 
     ev.after(stream);
     return hipGetLastError();
   }
-  const int threads = 256, nwaves = threads / 64;
+  const int threads = compress_threads(c.polar != 0), nwaves = threads / 64;
   const size_t base = (size_t)c.d * c.d * 4 + 4 * kMaxLevels * 4 + (size_t)nwaves * 16 * c.rec_bytes +
                       (c.polar ? (size_t)nwaves * 16 * c.d : 0);
   const size_t with_s = base + (size_t)c.m * c.d * 4;
