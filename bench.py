@@ -19,8 +19,9 @@ Other workloads (``--workload``), each with its own step:
 
 Prints ONE JSON line.  `roofline` describes the step's dominant kernel: algorithmic bytes per
 launch over its average duration, timed with HIP events the library records on the kernel's own
-stream around every launch of the timed steps.  `cpu_baseline` times the oracle (one thread) on a
-bounded sample of the same workload.
+stream around every launch of the timed steps.  `cpu_baseline` times the scalar C oracle (one
+thread per host core, at most 16) on a bounded sample of the same workload, with the numpy oracle
+beside it (polar keys and the hot/cold step: the numpy oracle alone).
 """
 from __future__ import annotations
 
@@ -314,6 +315,47 @@ def oracle_baseline(units, make_job, tokens_per_unit, total_units, unit_name, bu
             "cpu_model": cpu_model()}
 
 
+def _scalar_codec(w):
+    from oracle import scalar as SC
+    key = ("scalar",) + codec_args_of(w)[:6]
+    if key not in _CODECS:
+        _CODECS[key] = SC.ScalarCodec(*codec_args_of(w)[:6])
+    return _CODECS[key]
+
+
+def scalar_baseline(units, run_unit, tokens_per_unit, total_units, unit_name, budget_s=6.0, max_threads=16):
+    """The scalar C oracle (oracle/tq_scalar.c) as it is: one thread on units in order until
+    ~budget_s, then one thread per host core (at most max_threads; the library's calls release
+    the GIL) on a batch sized to about the same wall time.  Inputs are host arrays prepared
+    before the timers start."""
+    from concurrent.futures import ThreadPoolExecutor
+    done, elapsed = 0, 0.0
+    for u in units:
+        t0 = time.perf_counter()
+        run_unit(u)
+        elapsed += time.perf_counter() - t0
+        done += 1
+        if elapsed >= budget_s:
+            break
+    rate1 = done * tokens_per_unit / elapsed
+    threads = max(1, min(max_threads, os.cpu_count() or 1))
+    per_unit = elapsed / done
+    n_multi = min(len(units), threads * max(1, int(budget_s / per_unit / 2)))
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(run_unit, units[:n_multi]))
+        wall = time.perf_counter() - t0
+    host = os.cpu_count() or 1
+    return {"value": n_multi * tokens_per_unit / wall, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "host_cores": host,
+            "core_cap": (f"at most {max_threads} threads: the CPU share of one GPU on the benchmark "
+                         f"machines ({host} host cores visible)") if host > threads else None,
+            "sample": f"{n_multi} of {total_units} {unit_name} over {threads} threads (scalar C oracle, "
+                      f"oracle/tq_scalar.c at -O2, double accumulation), {wall:.1f} s wall",
+            "single_thread": {"value": rate1, "cores": 1, "sample": f"{done} {unit_name}, {elapsed:.1f} s"},
+            "cpu_model": cpu_model()}
+
+
 def compute_dtype(w) -> str:
     """Arithmetic of the step's scan: int8 matrix-core key products (exact in int32) and bf16
     matrix-core value products accumulated in fp32 on the matrix-core paths (decode at head_dim
@@ -399,43 +441,69 @@ def run_decode(args, tq, W, ev):
     return line
 
 
-def cpu_baseline_decode(w, h, q, records, hot, budget_s: float = 12.0):
-    """Oracle decode of whole sequences of the same cache (all query heads)."""
-    codec_args = codec_args_of(w)
+def cpu_baseline_decode(w, h, q, records, hot, budget_s: float = 6.0):
+    """Oracle decode of the same cache: the scalar C oracle per (sequence, query head) - a unit
+    attends (tokens + hot tokens) / q_heads tokens of the metric - and, where it covers the
+    codec (not polar keys), the numpy oracle over whole sequences beside it."""
     qn = q.float().cpu().numpy()
     hk = hot["hot_k"].float().cpu().numpy() if hot else None
     hv = hot["hot_v"].float().cpu().numpy() if hot else None
+    codec_args = codec_args_of(w)
 
     def make_job(b):
         return ("decode", codec_args,
                 (qn[b:b + 1], records[b:b + 1].cpu().numpy(), None if hk is None else hk[b:b + 1],
                  None if hv is None else hv[b:b + 1]), {"tokens": w.tokens, "hot": w.hot_tokens})
 
-    return oracle_baseline(list(range(w.batch)), make_job, w.tokens + w.hot_tokens, w.batch, "sequences",
-                           budget_s)
+    numpy_leg = oracle_baseline(list(range(w.batch)), make_job, w.tokens + w.hot_tokens, w.batch, "sequences",
+                                budget_s)
+    if w.polar_upper_bits:
+        return numpy_leg
+    c = _scalar_codec(w)
+    r = records.cpu().numpy()
+    G = w.q_heads // w.kv_heads
+    units = [(b, hq) for b in range(w.batch) for hq in range(w.q_heads)]
+
+    def run_unit(u):
+        b, hq = u
+        c.decode_head(qn[b, hq], r[b, hq // G], w.tokens, None, None if hk is None else hk[b, hq // G],
+                      None if hv is None else hv[b, hq // G])
+
+    line = scalar_baseline(units, run_unit, (w.tokens + w.hot_tokens) / w.q_heads, len(units),
+                           "(sequence, query head) units", budget_s)
+    line["numpy_oracle"] = numpy_leg
+    return line
 
 
 def cpu_baseline_compress(w, budget_s: float = 4.0):
-    """Oracle compress (one core) of 4096-token blocks of one head of the same synthetic K/V."""
+    """Oracle compress (one core) of 4096-token blocks of one head of the same synthetic K/V: the
+    scalar C oracle and, beside it, the numpy oracle."""
     from threadpoolctl import threadpool_limits
     from compressed_key_attention_amd import workloads as W
-    codec_args = codec_args_of(w)
-    codec = _codec(codec_args)
-    from oracle import tq_oracle as O
+    codec = _codec(codec_args_of(w))
     K, V = W.make_kv(w, "cpu", tokens=4096, batch=1)
-    done, elapsed = 0, 0.0
-    with threadpool_limits(limits=1):
-        for hh in range(w.kv_heads):
-            k = K[0, :, hh].float().numpy()
-            v = V[0, :, hh].float().numpy()
+    blocks = [(K[0, :, hh].float().numpy(), V[0, :, hh].float().numpy()) for hh in range(w.kv_heads)]
+
+    def leg(fn, what):
+        done, elapsed = 0, 0.0
+        for k, v in blocks:
             t0 = time.perf_counter()
-            codec.compress_fields(k, v)
+            fn(k, v)
             elapsed += time.perf_counter() - t0
             done += 1
             if elapsed >= budget_s:
                 break
-    return {"value": done * 4096 / elapsed, "unit": "token-heads/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} blocks of 4096 token-heads, {elapsed:.2f} s"}
+        return {"value": done * 4096 / elapsed, "unit": "token-heads/s", "cores": 1, "kind": "oracle",
+                "sample": f"{done} blocks of 4096 token-heads, {elapsed:.2f} s ({what})"}
+
+    with threadpool_limits(limits=1):
+        numpy_leg = leg(codec.compress_fields, "numpy oracle")
+    if w.polar_upper_bits:
+        return numpy_leg
+    c = _scalar_codec(w)
+    line = leg(c.compress, "scalar C oracle")
+    line["numpy_oracle"] = numpy_leg
+    return line
 
 
 # ---------------------------------------------------------------------------------------------
@@ -503,9 +571,11 @@ def run_sparse(args, tq, W, ev):
     return line
 
 
-def cpu_baseline_sparse(w, q, index, book, records, budget_s: float = 12.0):
+def cpu_baseline_sparse(w, q, index, book, records, budget_s: float = 6.0):
     """Oracle select + gathered attention per (sequence, KV head) unit; a unit scores T tokens
-    of one KV head, so T / kv_heads tokens of the workload."""
+    of one KV head, so T / kv_heads tokens of the workload.  The scalar C oracle, and the numpy
+    oracle beside it."""
+    from oracle import scalar as SC
     codec_args = codec_args_of(w)
     qn = q.float().cpu().numpy()
     T, G = w.tokens, w.q_heads // w.kv_heads
@@ -518,7 +588,20 @@ def cpu_baseline_sparse(w, q, index, book, records, budget_s: float = 12.0):
                  book[b:b + 1, hh:hh + 1].cpu().numpy(), records[b:b + 1, hh:hh + 1].cpu().numpy()),
                 {"tokens": T, "k": w.top_k})
 
-    return oracle_baseline(units, make_job, T / w.kv_heads, len(units), "(sequence, KV head) units", budget_s)
+    numpy_leg = oracle_baseline(units, make_job, T / w.kv_heads, len(units), "(sequence, KV head) units",
+                                budget_s)
+    c = _scalar_codec(w)
+    gi, gb, r = index.cpu().numpy(), book.cpu().numpy(), records.cpu().numpy()
+
+    def run_unit(u):
+        b, hh = u
+        idx, n, _ = SC.select_unit(qn[b, hh * G:(hh + 1) * G], gi[b, hh], gb[b, hh], T, w.top_k)
+        for j in range(G):
+            c.decode_head(qn[b, hh * G + j], r[b, hh], n, idx[:n])
+
+    line = scalar_baseline(units, run_unit, T / w.kv_heads, len(units), "(sequence, KV head) units", budget_s)
+    line["numpy_oracle"] = numpy_leg
+    return line
 
 
 # ---------------------------------------------------------------------------------------------
@@ -599,9 +682,9 @@ def run_bulk_scan(args, tq, W, ev):
     return line
 
 
-def cpu_baseline_scan(w, q, records, budget_s: float = 12.0):
+def cpu_baseline_scan(w, q, records, budget_s: float = 6.0):
     """Oracle bulk scan on 4096-token blocks of one KV head (all its queries); a block is
-    4096 / kv_heads tokens of the workload."""
+    4096 / kv_heads tokens of the workload.  The scalar C oracle, and the numpy oracle beside it."""
     codec_args = codec_args_of(w)
     qn = q.float().cpu().numpy()
     chunk = 4096
@@ -612,8 +695,18 @@ def cpu_baseline_scan(w, q, records, budget_s: float = 12.0):
         return ("scan", codec_args, (qn[0:1, hh:hh + 1], records[0:1, hh:hh + 1, t0:t0 + chunk].cpu().numpy()),
                 {"tokens": chunk})
 
-    return oracle_baseline(units, make_job, chunk / w.kv_heads, len(units),
-                           f"4096-token blocks x {w.scan_queries} queries", budget_s)
+    unit_name = f"4096-token blocks x {w.scan_queries} queries"
+    numpy_leg = oracle_baseline(units, make_job, chunk / w.kv_heads, len(units), unit_name, budget_s)
+    c = _scalar_codec(w)
+    r = records.cpu().numpy()
+
+    def run_unit(u):
+        hh, t0 = u
+        c.score_scan(qn[0:1, hh:hh + 1], r[0:1, hh:hh + 1, t0:t0 + chunk], chunk)
+
+    line = scalar_baseline(units, run_unit, chunk / w.kv_heads, len(units), unit_name, budget_s)
+    line["numpy_oracle"] = numpy_leg
+    return line
 
 
 # ---------------------------------------------------------------------------------------------
