@@ -3137,10 +3137,12 @@ __global__ __launch_bounds__(256) void select_score_kernel(const uint8_t* index,
       const int t = (i0 + j) * 256 + threadIdx.x;
       r[j] = *reinterpret_cast<const Rec*>(base + (size_t)min(t, m - 1) * NB);   // clamped, unbranched
     }
+    // every token of the batch is scored (a clamped one twice) and only the store and the
+    // histogram count are predicated: a branch around the whole body lets the compiler sink
+    // each record load into it, which serialises the loads' latency token by token
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       const int t = (i0 + j) * 256 + threadIdx.x;
-      if (t >= m) continue;
       uint32_t w[NB / 4];
       if constexpr (NB == 16) {
         w[0] = r[j].x; w[1] = r[j].y; w[2] = r[j].z; w[3] = r[j].w;
@@ -3163,8 +3165,10 @@ __global__ __launch_bounds__(256) void select_score_kernel(const uint8_t* index,
           s += *reinterpret_cast<const int32_t*>(lb + 64 * (g + 1) + ((hi >> (8 * kb)) & 0xFFu));
         }
       }
-      sc[t] = s;
-      atomicAdd(&hist[order_key(s) >> kSelDigitShift], 1);
+      if (t < m) {
+        sc[t] = s;
+        atomicAdd(&hist[order_key(s) >> kSelDigitShift], 1);
+      }
     }
   }
   __syncthreads();
@@ -3508,13 +3512,198 @@ struct SparseArgs {
   int k;
 };
 
+// The selected tokens of chunk c of a unit, in index order and capped at k overall (the write
+// launch's rule): offsets within the chunk into list[], their count into *s_nsel (written by
+// thread 0; read after the caller's next barrier).  Called by all kSmallThreads threads.
+__device__ __forceinline__ void sparse_chunk_list(const SparseArgs& S, int64_t unit, int c, int64_t n,
+                                                  int64_t kk, uint16_t* list, int* wsum, int* s_nsel) {
+  constexpr int kPer = kSelChunk / kSmallThreads;
+  const int tid = threadIdx.x;
+  const int64_t t0 = (int64_t)c * kSelChunk;
+  const int tb = tid * kPer;
+  uint32_t sel = 0;
+  if (kk > 0 && t0 < n) {
+    const uint64_t prefix = S.params[unit].prefix, mask = S.params[unit].mask;
+    const int mm = (int)min((int64_t)kSelChunk, n - t0);
+    const int32_t* sc = S.scores + unit * S.a.capacity + t0;
+    int32_t s[kPer];
+    if (tb + kPer <= mm) {
+#pragma unroll
+      for (int j = 0; j < kPer; j += 4) {
+        const int4 v = *reinterpret_cast<const int4*>(sc + tb + j);
+        s[j] = v.x; s[j + 1] = v.y; s[j + 2] = v.z; s[j + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) s[j] = tb + j < mm ? sc[tb + j] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int t = tb + j;
+      const bool take = t < mm && (select_key(order_key(s[j]), (int32_t)(t0 + t)) & mask) >= prefix;
+      sel |= (take ? 1u : 0u) << j;
+    }
+  }
+  int tot;
+  int pos = block_exclusive_sum<kSmallThreads>(__popc(sel), wsum, &tot);
+  const int base = (kk > 0 && t0 < n) ? S.chunk_off[unit * S.a.n_chunks + c] : 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (sel & (1u << j)) {
+      if (base + pos < kk) list[pos] = (uint16_t)(tb + j);
+      ++pos;
+    }
+  if (tid == 0) *s_nsel = (int)max<int64_t>(0, min<int64_t>(tot, kk - base));
+}
+
+// One step of a recursive-halving sum across the lanes that differ in bit MSK: of a[0, N) a lane
+// keeps the half selected by its bit, receives the other half from its partner, and leaves the
+// sums in a[0, N/2) (every index is a compile-time constant, so a[] stays in registers).
+template <int N, int MSK, int NA>
+__device__ __forceinline__ void halve_step(float (&a)[NA], int lane) {
+  constexpr int half = N / 2;
+  const bool up = (lane & MSK) != 0;
+#pragma unroll
+  for (int j = 0; j < half; ++j) {
+    const float send = up ? a[j] : a[half + j];
+    const float keep = up ? a[half + j] : a[j];
+    a[j] = keep + __shfl_xor(send, MSK);
+  }
+}
+
+// Sparse attention, lean form: one query head per KV head, 4-bit key and value codes, no sketch
+// (the Self-Indexing layout: the selection does the coarse work, the payload is codes only).
+// Four threads per selected token, thread (t, s) owning coordinates [s D/4, (s+1) D/4): it loads
+// its slices of the token's key and value fields and the norms straight from the record (three
+// independent loads), forms its part of <q_x, gamma[c]> from the level table in LDS, and after
+// a quad sum and the batch's softmax keeps w gamma_v[c] in D/4 per-thread accumulators (rescaled
+// when the running maximum rises).  At the end the 64 token slots are summed: recursive halving
+// across the 16 lanes of a wave that share s, then the four waves through LDS.
+template <int D>
+__global__ __launch_bounds__(kSmallThreads) void sparse_attend_lean_kernel(SparseArgs S) {
+  const DecodeArgs& A = S.a;
+  constexpr int QW = D / 4;                 // coordinates per thread
+  constexpr int NW = QW / 8;                // 32-bit words of 4-bit codes per thread
+  constexpr int TPB = kSmallThreads / 4;    // tokens per batch
+  constexpr int OUT = QW / 16;              // coordinates per lane after the in-wave reduction
+  using Slice = typename std::conditional<NW == 4, uint4, uint2>::type;
+  __shared__ uint16_t list[kSelChunk];
+  __shared__ int wsum[kSmallThreads / 64];
+  __shared__ int s_nsel;
+  __shared__ float kl[16], vl[16];
+  __shared__ float red[2][kSmallThreads / 64];
+  __shared__ float osum[kSmallThreads / 64][D];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+  const int64_t unit = (int64_t)b * A.kv_heads + hkv;
+  const int64_t qrow = (int64_t)b * A.q_heads + hkv;
+  const int64_t n = min((int64_t)A.seq_lens[b], A.capacity);
+  const int64_t kk = min((int64_t)S.k, n);
+  const int64_t t0 = (int64_t)c * kSelChunk;
+  sparse_chunk_list(S, unit, c, n, kk, list, wsum, &s_nsel);
+  if (tid < 16) {
+    kl[tid] = A.key_levels[tid];
+    vl[tid] = A.val_levels[tid];
+  }
+  const int sq = tid & 3, tq = tid >> 2;
+  float q[QW];
+#pragma unroll
+  for (int j = 0; j < QW; j += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(A.qx + qrow * D + sq * QW + j);
+    q[j] = v.x; q[j + 1] = v.y; q[j + 2] = v.z; q[j + 3] = v.w;
+  }
+  float acc[QW];
+#pragma unroll
+  for (int j = 0; j < QW; ++j) acc[j] = 0.0f;
+  float m_run = kNegInf, l_run = 0.0f;
+  __syncthreads();
+  const int nsel = s_nsel;
+  const uint8_t* recs = A.records + unit * A.capacity * A.rec_bytes;
+  const float lscale = A.scale * A.inv_sqrt_d;
+  for (int s0 = 0; s0 < nsel; s0 += TPB) {
+    const int nt = min(TPB, nsel - s0);
+    const bool live = tq < nt;
+    const uint8_t* rec = recs + (t0 + list[s0 + min(tq, nt - 1)]) * A.rec_bytes;   // clamped
+    const Slice kw = *reinterpret_cast<const Slice*>(rec + sq * (QW / 2));
+    const Slice vw = *reinterpret_cast<const Slice*>(rec + A.kbytes + A.sbytes + sq * (QW / 2));
+    const float r_k = *reinterpret_cast<const float*>(rec + A.norm_off);
+    const float r_v = *reinterpret_cast<const float*>(rec + A.norm_off + 8);
+    uint32_t kwv[NW], vwv[NW];
+    if constexpr (NW == 4) {
+      kwv[0] = kw.x; kwv[1] = kw.y; kwv[2] = kw.z; kwv[3] = kw.w;
+      vwv[0] = vw.x; vwv[1] = vw.y; vwv[2] = vw.z; vwv[3] = vw.w;
+    } else {
+      kwv[0] = kw.x; kwv[1] = kw.y;
+      vwv[0] = vw.x; vwv[1] = vw.y;
+    }
+    // code j of the slice: bits [4 j, 4 j + 4) of the little-endian word stream
+    float dot = 0.0f;
+#pragma unroll
+    for (int wi = 0; wi < NW; ++wi)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) dot = fmaf(q[8 * wi + u], kl[(kwv[wi] >> (4 * u)) & 15u], dot);
+    dot += __shfl_xor(dot, 1);
+    dot += __shfl_xor(dot, 2);
+    const float lg = live ? lscale * (r_k * dot) : kNegInf;
+    float bm = lg;
+#pragma unroll
+    for (int msk = 4; msk < 64; msk <<= 1) bm = fmaxf(bm, __shfl_xor(bm, msk));
+    if (lane == 0) red[0][wave] = bm;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kSmallThreads / 64; ++w) bm = fmaxf(bm, red[0][w]);
+    const float mn = fmaxf(m_run, bm);
+    const float f = m_run == kNegInf ? 0.0f : __expf(m_run - mn);
+    const float p = live ? __expf(lg - mn) : 0.0f;
+    float ps = sq == 0 ? p : 0.0f;
+#pragma unroll
+    for (int msk = 4; msk < 64; msk <<= 1) ps += __shfl_xor(ps, msk);
+    if (lane == 0) red[1][wave] = ps;
+    __syncthreads();
+    float bsum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kSmallThreads / 64; ++w) bsum += red[1][w];
+    l_run = l_run * f + bsum;
+    m_run = mn;
+    const float wt = p * r_v * A.inv_sqrt_d;
+#pragma unroll
+    for (int wi = 0; wi < NW; ++wi)
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        acc[8 * wi + u] = fmaf(wt, vl[(vwv[wi] >> (4 * u)) & 15u], acc[8 * wi + u] * f);
+    __syncthreads();            // red[] is rewritten by the next batch
+  }
+  // sum the 16 token slots of this wave that share sq: recursive halving over lane bits 5..2;
+  // lane (t', sq) then holds coordinates sq QW + OUT t' + [0, OUT)
+  halve_step<QW, 32>(acc, lane);
+  halve_step<QW / 2, 16>(acc, lane);
+  halve_step<QW / 4, 8>(acc, lane);
+  halve_step<QW / 8, 4>(acc, lane);
+  const int tl = lane >> 2;
+#pragma unroll
+  for (int e = 0; e < OUT; ++e) osum[wave][sq * QW + OUT * tl + e] = acc[e];
+  __syncthreads();
+  const int stride = D + 2;
+  float* part = A.part + (qrow * A.n_chunks + c) * stride;
+  for (int i = tid; i < D; i += kSmallThreads) {
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kSmallThreads / 64; ++w) v += osum[w][i];
+    part[2 + i] = v;
+  }
+  if (tid == 0) {
+    part[0] = m_run;
+    part[1] = l_run;
+  }
+}
+
 // POLAR: polar key codes; each token's unit vector u is rebuilt into LDS (float32, one thread
 // per (token, level-1 pair): the root-first product of the cos / sin factors on its path) and
 // the key part of the estimate is r_k <q_x, u>.
 template <int D, int BK, int BV, int MG, bool POLAR = false>
 __global__ __launch_bounds__(kSmallThreads) void sparse_attend_kernel(SparseArgs S) {
   const DecodeArgs& A = S.a;
-  constexpr int NG32 = D / 32, TB = kSmallMaxTok, kPer = kSelChunk / kSmallThreads;
+  constexpr int NG32 = D / 32, TB = kSmallMaxTok;
   constexpr int KRW = POLAR ? 16 : 1;              // polar key field words per token (at most 64 bytes)
   __shared__ uint32_t kraw[POLAR ? TB : 1][KRW];
   __shared__ float ku[POLAR ? TB : 1][POLAR ? D + 1 : 1];
@@ -3537,43 +3726,7 @@ __global__ __launch_bounds__(kSmallThreads) void sparse_attend_kernel(SparseArgs
   const int64_t n = min((int64_t)A.seq_lens[b], A.capacity);
   const int64_t kk = min((int64_t)S.k, n);
   const int64_t t0 = (int64_t)c * kSelChunk;
-  // this chunk's selected tokens, in index order, capped at k overall
-  {
-    const int tb = tid * kPer;
-    uint32_t sel = 0;
-    if (kk > 0 && t0 < n) {
-      const uint64_t prefix = S.params[unit].prefix, mask = S.params[unit].mask;
-      const int mm = (int)min((int64_t)kSelChunk, n - t0);
-      const int32_t* sc = S.scores + unit * A.capacity + t0;
-      int32_t s[kPer];
-      if (tb + kPer <= mm) {
-#pragma unroll
-        for (int j = 0; j < kPer; j += 4) {
-          const int4 v = *reinterpret_cast<const int4*>(sc + tb + j);
-          s[j] = v.x; s[j + 1] = v.y; s[j + 2] = v.z; s[j + 3] = v.w;
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) s[j] = tb + j < mm ? sc[tb + j] : 0;
-      }
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const int t = tb + j;
-        const bool take = t < mm && (select_key(order_key(s[j]), (int32_t)(t0 + t)) & mask) >= prefix;
-        sel |= (take ? 1u : 0u) << j;
-      }
-    }
-    int tot;
-    int pos = block_exclusive_sum<kSmallThreads>(__popc(sel), wsum, &tot);
-    const int base = (kk > 0 && t0 < n) ? S.chunk_off[unit * A.n_chunks + c] : 0;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j)
-      if (sel & (1u << j)) {
-        if (base + pos < kk) list[pos] = (uint16_t)(tb + j);
-        ++pos;
-      }
-    if (tid == 0) s_nsel = (int)max<int64_t>(0, min<int64_t>(tot, kk - base));
-  }
+  sparse_chunk_list(S, unit, c, n, kk, list, wsum, &s_nsel);
   for (int e = tid; e < G * D; e += kSmallThreads) qx[e / D][e % D] = A.qx[(qrow0 + e / D) * D + e % D];
   for (int e = tid; e < G * m; e += kSmallThreads) qs[e / m][e % m] = A.qs[(qrow0 + e / m) * m + e % m];
   if (tid < kMaxLevels) {
@@ -3851,7 +4004,10 @@ hipError_t launch_sparse(const Consts& c, const DevConsts& dc, const SparsePlan&
   const dim3 grid((unsigned)n_chunks, kv_heads, batch);
   // query rows held in LDS sized for the group (a smaller footprint keeps more workgroups per CU)
   const int G = q_heads / kv_heads;
-  if (c.d == 128 && G <= 4) launch_sparse_d<128, 4>(s, c.kb, c.vb, c.polar != 0, grid, stream);
+  const bool lean = G == 1 && c.m == 0 && c.kb == 4 && c.vb == 4 && !c.polar && (c.d == 128 || c.d == 64);
+  if (lean && c.d == 128) hipLaunchKernelGGL(sparse_attend_lean_kernel<128>, grid, dim3(kSmallThreads), 0, stream, s);
+  else if (lean) hipLaunchKernelGGL(sparse_attend_lean_kernel<64>, grid, dim3(kSmallThreads), 0, stream, s);
+  else if (c.d == 128 && G <= 4) launch_sparse_d<128, 4>(s, c.kb, c.vb, c.polar != 0, grid, stream);
   else if (c.d == 128) launch_sparse_d<128, kSmallMaxG>(s, c.kb, c.vb, c.polar != 0, grid, stream);
   else if (G <= 4) launch_sparse_d<64, 4>(s, c.kb, c.vb, c.polar != 0, grid, stream);
   else launch_sparse_d<64, kSmallMaxG>(s, c.kb, c.vb, c.polar != 0, grid, stream);

@@ -511,6 +511,10 @@ def test_sparse_with_exact_sinks(kb, vb):
     (4, 4, 0, 8, 700, [5000, 4097], 0, 2, 128),       # polar keys (4-bit level-1, 2-bit upper angles)
     (4, 4, 128, 32, 500, [6000, 3000], 64, 4, 128),   # polar keys, sketch, G = 4, sinks
     (2, 3, 64, 16, 400, [3000, 2500], 32, 1, 64),     # polar keys at head_dim 64
+    (4, 4, 0, 8, 900, [7000, 3000], 64, 0, 128),      # the lean kernel (G = 1, 4/4-bit, no sketch) with sinks
+    (4, 4, 0, 8, 500, [5000, 2000], 0, 0, 64),        # the lean kernel at head_dim 64
+    (4, 4, 0, 8, 0, [300, 300], 16, 0, 128),          # the lean kernel, k = 0: sinks only
+    (4, 4, 0, 8, 3000, [3000, 2999], 0, 0, 128),      # the lean kernel, whole chunks selected (47 batches)
 ])
 def test_sparse_attention_one_call(kb, vb, m, hq, k, lens, sinks, ub, d):
     """tq_sparse_attention (selection and attention in one call, no index list) against the
