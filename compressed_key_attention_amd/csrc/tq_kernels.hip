@@ -3108,8 +3108,13 @@ __device__ __forceinline__ int block_exclusive_sum(int v, int* wsum, int* total)
   return off + incl - v;
 }
 
+// 512 threads of 8 tokens each (two batches of 4 records in flight, ~48 VGPRs): all 4,096-token
+// chunks of the sparse workload are resident at once (8 waves per SIMD), hiding the record loads
+// and table reads better than 256 threads of 16 tokens (17.6 against 19.4 us at 131,072 tokens).
+constexpr int kScoreThreads = 512;
+
 template <int NB>
-__global__ __launch_bounds__(256) void select_score_kernel(const uint8_t* index, const int32_t* lut_all,
+__global__ __launch_bounds__(kScoreThreads, 8) void select_score_kernel(const uint8_t* index, const int32_t* lut_all,
                                                            const int32_t* seq_lens, int heads, int64_t capacity,
                                                            int32_t* scores, int32_t* hist_all) {
   // one 16-entry table per 4-channel group: a lookup instruction reads one table, whose 16
@@ -3122,19 +3127,19 @@ __global__ __launch_bounds__(256) void select_score_kernel(const uint8_t* index,
   const int64_t n = min((int64_t)seq_lens[b], capacity);
   const int64_t t0 = (int64_t)blockIdx.x * kSelChunk;
   if (t0 >= n) return;
-  for (int e = threadIdx.x; e < NG * 16; e += 256) lut[e] = lut_all[unit * NG * 16 + e];
-  for (int e = threadIdx.x; e < kSelBins; e += 256) hist[e] = 0;
+  for (int e = threadIdx.x; e < NG * 16; e += kScoreThreads) lut[e] = lut_all[unit * NG * 16 + e];
+  for (int e = threadIdx.x; e < kSelBins; e += kScoreThreads) hist[e] = 0;
   __syncthreads();
   const uint8_t* base = index + (unit * capacity + t0) * NB;
   int32_t* sc = scores + unit * capacity + t0;
   const int m = (int)min((int64_t)kSelChunk, n - t0);
   using Rec = typename std::conditional<NB == 16, uint4, uint2>::type;
-  constexpr int kBatch = 8;
-  for (int i0 = 0; i0 < kSelChunk / 256; i0 += kBatch) {
+  constexpr int kBatch = 4;
+  for (int i0 = 0; i0 < kSelChunk / kScoreThreads; i0 += kBatch) {
     Rec r[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      const int t = (i0 + j) * 256 + threadIdx.x;
+      const int t = (i0 + j) * kScoreThreads + threadIdx.x;
       r[j] = *reinterpret_cast<const Rec*>(base + (size_t)min(t, m - 1) * NB);   // clamped, unbranched
     }
     // every token of the batch is scored (a clamped one twice) and only the store and the
@@ -3142,7 +3147,7 @@ __global__ __launch_bounds__(256) void select_score_kernel(const uint8_t* index,
     // each record load into it, which serialises the loads' latency token by token
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      const int t = (i0 + j) * 256 + threadIdx.x;
+      const int t = (i0 + j) * kScoreThreads + threadIdx.x;
       uint32_t w[NB / 4];
       if constexpr (NB == 16) {
         w[0] = r[j].x; w[1] = r[j].y; w[2] = r[j].z; w[3] = r[j].w;
@@ -3173,7 +3178,7 @@ __global__ __launch_bounds__(256) void select_score_kernel(const uint8_t* index,
   }
   __syncthreads();
   int32_t* gh = hist_all + unit * kSelBins;
-  for (int e = threadIdx.x; e < kSelBins; e += 256) {
+  for (int e = threadIdx.x; e < kSelBins; e += kScoreThreads) {
     const int v = hist[e];
     if (v) atomicAdd(&gh[e], v);
   }
@@ -3475,10 +3480,10 @@ hipError_t launch_select(const Consts& c, const SelectPlan& plan, const void* q,
     const dim3 grid((unsigned)n_chunks, kv_heads, batch);
     ev.before(stream);
     if (c.d == 128)
-      hipLaunchKernelGGL(select_score_kernel<16>, grid, dim3(256), 0, stream, static_cast<const uint8_t*>(index),
+      hipLaunchKernelGGL(select_score_kernel<16>, grid, dim3(kScoreThreads), 0, stream, static_cast<const uint8_t*>(index),
                          lut, seq_lens, kv_heads, capacity, scores, hist);
     else
-      hipLaunchKernelGGL(select_score_kernel<8>, grid, dim3(256), 0, stream, static_cast<const uint8_t*>(index),
+      hipLaunchKernelGGL(select_score_kernel<8>, grid, dim3(kScoreThreads), 0, stream, static_cast<const uint8_t*>(index),
                          lut, seq_lens, kv_heads, capacity, scores, hist);
     ev.after(stream);
     hipLaunchKernelGGL(select_filter_kernel, grid, dim3(256), 0, stream, scores, hist, seq_lens, kv_heads, capacity,
