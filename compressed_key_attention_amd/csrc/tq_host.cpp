@@ -421,8 +421,8 @@ struct tq_handle {
 
 namespace {
 
-// Calls built for head_dim 64 and 128 only (every other supported head_dim has compress and
-// the bulk scan).
+// Calls built for head_dim 64 and 128 only (every other supported head_dim has compress,
+// decode attention, the sign index, top-k selection, sparse attention and the bulk scan).
 bool dim_unsupported(const tq_handle* h, const char* what, tq_status* st) {
   if (h && h->c.d != 64 && h->c.d != 128) {
     *st = fail(TQ_ERR_UNSUPPORTED, "%s is built for head_dim 64 and 128 only (handle has %d)", what, h->c.d);
@@ -772,10 +772,6 @@ tq_status tq_debug_quantize(const tq_handle* h, const float* z_k, const float* p
 tq_status tq_decode_workspace_size(const tq_handle* h, int32_t batch, int32_t q_heads,
                                    int32_t kv_heads, int64_t capacity, int32_t k_sel,
                                    size_t* bytes) {
-  {
-    tq_status dst;
-    if (dim_unsupported(h, "decode attention", &dst)) return dst;
-  }
   if (!h || !bytes) return fail(TQ_ERR_INVALID_ARGUMENT, "NULL handle or output");
   if (batch < 0 || q_heads <= 0 || kv_heads <= 0 || q_heads % kv_heads || capacity < 0 || k_sel < 0)
     return fail(TQ_ERR_INVALID_ARGUMENT, "bad decode shape");
@@ -793,10 +789,6 @@ static tq_status check_decode(const tq_handle* h, const void* q, tq_dtype q_dt, 
                               const void* hot_v, tq_dtype hot_dt, const int32_t* hot_lens,
                               int64_t hot_capacity, const int32_t* sel_idx, int32_t k_sel,
                               float scale, float* out, tq::DecodePlan* plan) {
-  {
-    tq_status dst;
-    if (dim_unsupported(h, "decode attention", &dst)) return dst;
-  }
   if (!h) return fail(TQ_ERR_INVALID_ARGUMENT, "handle is NULL");
   size_t es;
   if (!elem_size(q_dt, &es)) return fail(TQ_ERR_INVALID_ARGUMENT, "unknown query dtype");
@@ -869,10 +861,6 @@ tq_status tq_decode_attention_noalloc(const tq_handle* h, const void* q, tq_dtyp
 
 tq_status tq_index_workspace_size(const tq_handle* h, int32_t batch, int32_t kv_heads,
                                   size_t* bytes) {
-  {
-    tq_status dst;
-    if (dim_unsupported(h, "the sign index", &dst)) return dst;
-  }
   if (!h || !bytes) return fail(TQ_ERR_INVALID_ARGUMENT, "NULL handle or output");
   if (batch < 0 || kv_heads <= 0) return fail(TQ_ERR_INVALID_ARGUMENT, "bad shape");
   // worst case over n_tokens: the plan caps the number of chunks
@@ -886,10 +874,6 @@ tq_status tq_build_sign_index(const tq_handle* h, const void* k, tq_dtype dt, in
                               float* codebook, float* mean, int64_t capacity,
                               int64_t first_slot, void* workspace, size_t ws_bytes,
                               hipStream_t stream) {
-  {
-    tq_status dst;
-    if (dim_unsupported(h, "the sign index", &dst)) return dst;
-  }
   if (!h) return fail(TQ_ERR_INVALID_ARGUMENT, "handle is NULL");
   tq_status st = check_kv_addressing(h, k, dt, batch, n_tokens, kv_heads, seq_stride, tok_stride,
                                      head_stride, capacity, first_slot);
@@ -907,10 +891,6 @@ tq_status tq_build_sign_index(const tq_handle* h, const void* k, tq_dtype dt, in
 
 tq_status tq_select_workspace_size(const tq_handle* h, int32_t batch, int32_t kv_heads,
                                    int64_t capacity, size_t* bytes) {
-  {
-    tq_status dst;
-    if (dim_unsupported(h, "top-k selection", &dst)) return dst;
-  }
   if (!h || !bytes) return fail(TQ_ERR_INVALID_ARGUMENT, "NULL handle or output");
   if (batch < 0 || kv_heads <= 0 || capacity < 0) return fail(TQ_ERR_INVALID_ARGUMENT, "bad shape");
   *bytes = tq::plan_select(h->c, batch, kv_heads, capacity).ws_total;
@@ -922,10 +902,6 @@ tq_status tq_select_topk(const tq_handle* h, const void* q, tq_dtype q_dt, int32
                          const float* codebook, int64_t capacity, const int32_t* seq_lens,
                          int32_t k, int32_t* out_idx, int32_t* out_count, int32_t* out_scores,
                          void* workspace, size_t ws_bytes, hipStream_t stream) {
-  {
-    tq_status dst;
-    if (dim_unsupported(h, "top-k selection", &dst)) return dst;
-  }
   if (!h) return fail(TQ_ERR_INVALID_ARGUMENT, "handle is NULL");
   size_t es;
   if (!elem_size(q_dt, &es)) return fail(TQ_ERR_INVALID_ARGUMENT, "unknown query dtype");
@@ -947,10 +923,6 @@ tq_status tq_select_topk(const tq_handle* h, const void* q, tq_dtype q_dt, int32
 
 tq_status tq_sparse_workspace_size(const tq_handle* h, int32_t batch, int32_t q_heads,
                                    int32_t kv_heads, int64_t capacity, size_t* bytes) {
-  {
-    tq_status dst;
-    if (dim_unsupported(h, "sparse attention", &dst)) return dst;
-  }
   if (!h || !bytes) return fail(TQ_ERR_INVALID_ARGUMENT, "NULL handle or output");
   if (batch < 0 || q_heads <= 0 || kv_heads <= 0 || q_heads % kv_heads || capacity < 0)
     return fail(TQ_ERR_INVALID_ARGUMENT, "bad shape");
@@ -965,17 +937,15 @@ tq_status tq_sparse_attention(const tq_handle* h, const void* q, tq_dtype q_dt, 
                               const void* hot_v, tq_dtype hot_dt, const int32_t* hot_lens,
                               int64_t hot_capacity, float scale, float* out, float* lse,
                               void* workspace, size_t ws_bytes, hipStream_t stream) {
-  {
-    tq_status dst;
-    if (dim_unsupported(h, "sparse attention", &dst)) return dst;
-  }
   if (!h) return fail(TQ_ERR_INVALID_ARGUMENT, "handle is NULL");
   size_t es;
   if (!elem_size(q_dt, &es)) return fail(TQ_ERR_INVALID_ARGUMENT, "unknown query dtype");
   if (batch < 0 || q_heads <= 0 || kv_heads <= 0 || q_heads % kv_heads || capacity < 0 || k < 0)
     return fail(TQ_ERR_INVALID_ARGUMENT, "bad sparse attention shape");
   if (q_heads / kv_heads > 16) return fail(TQ_ERR_UNSUPPORTED, "group size above 16");
-  if (h->c.m > 128 || h->c.m % 32) return fail(TQ_ERR_UNSUPPORTED, "qjl_dim must be 0, 32, 64, 96 or 128");
+  const int max_m = (h->c.d == 64 || h->c.d == 128) ? 128 : 256;
+  if (h->c.m > max_m || h->c.m % 32)
+    return fail(TQ_ERR_UNSUPPORTED, "qjl_dim must be a multiple of 32 up to %d at head_dim %d", max_m, h->c.d);
   if (capacity > (int64_t(1) << 26)) return fail(TQ_ERR_UNSUPPORTED, "capacity above 2^26 tokens");
   if (!(scale >= 0.0f) || std::isinf(scale)) return fail(TQ_ERR_INVALID_ARGUMENT, "scale must be finite and >= 0");
   if (batch == 0) return ok();

@@ -89,6 +89,7 @@ struct DecodePlan {
   bool sign_bytes;  // QJL LUT indexed by bytes (else nibbles)
   bool mfma;        // matrix-core scan (head_dim 128, 4 query heads per KV head)
   bool small;       // direct scan for short caches (chunks of at most 64 tokens)
+  bool generic;     // head_dim other than 64 / 128: the generic direct kernel and merge
   size_t lds_bytes;
   size_t ws_qx, ws_qs, ws_part, ws_bop, ws_total;   // workspace offsets / size
 };

@@ -887,6 +887,7 @@ struct DecodeArgs {
   float* logits;
   int64_t capacity, logit_stride;
   int d, m, kbytes, sbytes, rec_bytes, norm_off;
+  int kb, vb;             // code widths (the generic-head_dim kernel reads them at run time)
   int G, q_heads, kv_heads, k_sel, chunk, n_chunks, sign_bytes;
   float scale, inv_sqrt_d, qjl_coef, key_fix;
   float key_levels[kMaxLevels];
@@ -1415,6 +1416,142 @@ static void launch_small_d(const DecodeArgs& a, int kb, int vb, dim3 grid, hipSt
   TQ_SM(2, 2) TQ_SM(2, 3) TQ_SM(2, 4) TQ_SM(3, 2) TQ_SM(3, 3) TQ_SM(3, 4)
   TQ_SM(4, 2) TQ_SM(4, 3) TQ_SM(4, 4)
 #undef TQ_SM
+}
+
+// -----------------------------------------------------------------------------------------
+// Decode for every other head_dim (a multiple of 8 up to 256; the TurboQuant page's
+// vector-search section uses d = 200): the direct kernel's structure with d, the code widths
+// and the sketch width read at run time.  One workgroup per (chunk of kGenTok tokens, KV head,
+// sequence): the chunk's records are copied into LDS as words, the codes unpacked from there
+// (field_code: 1/2/4-bit codes a little-endian bitstream, 3-bit codes in groups of 32 per 12
+// bytes with a trailing partial group as a plain bitstream), then every (token, head)
+// estimate, the chunk's softmax and every (head, coordinate) output, as decode_small_kernel.
+// -----------------------------------------------------------------------------------------
+constexpr int kDecGenTok = 32, kDecGenMaxM = 256, kDecGenMaxRec = 4 * kGenRecWords;
+
+// Code j of a field of n codes of width b, from the field's bytes.  May read one byte past the
+// field's last code, which stays inside the record (another field, the norms or the pad).
+__device__ __forceinline__ uint32_t field_code(const uint8_t* f, int j, int b, int n) {
+  const int whole = b == 3 ? (n & ~31) : 0;
+  if (j < whole) {
+    const uint8_t* g = f + 12 * (j >> 5);
+    const uint32_t w0 = g[0] | (g[1] << 8) | (g[2] << 16) | ((uint32_t)g[3] << 24);
+    const uint32_t w1 = g[4] | (g[5] << 8) | (g[6] << 16) | ((uint32_t)g[7] << 24);
+    const uint32_t w2 = g[8] | (g[9] << 8) | (g[10] << 16) | ((uint32_t)g[11] << 24);
+    return group3_code(w0, w1, w2, j & 31);
+  }
+  const uint8_t* base = f + (whole >> 5) * 12;
+  const int pos = b * (j - whole);
+  const uint32_t v = (uint32_t)base[pos >> 3] | ((uint32_t)base[(pos >> 3) + 1] << 8);
+  return (v >> (pos & 7)) & ((1u << b) - 1u);
+}
+
+__global__ __launch_bounds__(kSmallThreads) void decode_generic_kernel(DecodeArgs A) {
+  __shared__ float qx[kSmallMaxG][kGenMaxD + 1];
+  __shared__ float qs[kSmallMaxG][kDecGenMaxM + 1];
+  __shared__ __attribute__((aligned(16))) uint32_t raw[kDecGenTok][kDecGenMaxRec / 4];
+  __shared__ uint8_t kc[kDecGenTok][kGenMaxD];
+  __shared__ uint8_t vc[kDecGenTok][kGenMaxD];
+  __shared__ uint8_t sb[kDecGenTok][kDecGenMaxM];
+  __shared__ float nr[kDecGenTok][3];
+  __shared__ int ok_t[kDecGenTok];
+  __shared__ float lg[kSmallMaxG][kDecGenTok + 1];
+  __shared__ float hm[kSmallMaxG], hl[kSmallMaxG];
+  __shared__ float kl[kMaxLevels], vl[kMaxLevels];
+  const int G = A.G, m = A.m, d = A.d, TOK = A.chunk, tid = threadIdx.x;
+  const int b = blockIdx.z, hkv = blockIdx.y, chunk = blockIdx.x;
+  const int64_t qrow0 = (int64_t)b * A.q_heads + (int64_t)hkv * G;
+  if (A.gate) {
+    bool any = false;
+    for (int j = 0; j < G; ++j) any = any || A.gate[qrow0 + j] != 0;
+    if (!any) return;
+  }
+  const bool gather = A.sel_idx != nullptr;
+  const int n = gather ? A.k_sel : (int)min((int64_t)A.seq_lens[b], A.capacity);
+  const int c0 = chunk * TOK, nt = max(0, min(TOK, n - c0));
+  const uint8_t* recs = A.records + ((int64_t)b * A.kv_heads + hkv) * A.capacity * A.rec_bytes;
+  for (int e = tid; e < G * d; e += kSmallThreads) qx[e / d][e % d] = A.qx[(qrow0 + e / d) * d + e % d];
+  for (int e = tid; e < G * m; e += kSmallThreads) qs[e / m][e % m] = A.qs[(qrow0 + e / m) * m + e % m];
+  if (tid < kMaxLevels) {
+    kl[tid] = A.key_levels[tid];
+    vl[tid] = A.val_levels[tid];
+  }
+  // the chunk's records as words (records are 16-byte multiples)
+  const int rw = A.rec_bytes / 4;
+  for (int e = tid; e < nt * rw; e += kSmallThreads) {
+    const int t = e / rw, w = e % rw;
+    int64_t tok = c0 + t;
+    bool ok = true;
+    if (gather) {
+      tok = A.sel_idx[((int64_t)b * A.kv_heads + hkv) * A.k_sel + c0 + t];
+      ok = tok >= 0 && tok < A.capacity;
+    }
+    raw[t][w] = reinterpret_cast<const uint32_t*>(recs + (ok ? tok : 0) * A.rec_bytes)[w];
+    if (w == 0) ok_t[t] = ok ? 1 : 0;
+  }
+  __syncthreads();
+  const int per_t = 2 * d + m;
+  for (int e = tid; e < nt * per_t; e += kSmallThreads) {
+    const int t = e / per_t, j = e % per_t;
+    const uint8_t* r = reinterpret_cast<const uint8_t*>(raw[t]);
+    if (j < d) kc[t][j] = (uint8_t)field_code(r, j, A.kb, d);
+    else if (j < 2 * d) vc[t][j - d] = (uint8_t)field_code(r + A.kbytes + A.sbytes, j - d, A.vb, d);
+    else sb[t][j - 2 * d] = (uint8_t)((r[A.kbytes + ((j - 2 * d) >> 3)] >> ((j - 2 * d) & 7)) & 1u);
+  }
+  for (int t = tid; t < nt; t += kSmallThreads) {
+    const float* f = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(raw[t]) + A.norm_off);
+    nr[t][0] = f[0];
+    nr[t][1] = f[1];
+    nr[t][2] = f[2];
+  }
+  __syncthreads();
+  const int items = nt * G;
+  int L = 1;
+  while (L < 8 && items * L * 2 <= kSmallThreads) L *= 2;
+  for (int i0 = 0; i0 < items; i0 += kSmallThreads / L) {
+    const int it = i0 + tid / L, s = tid % L;
+    const int t = it / G, h = it % G;
+    float dot = 0.0f, qd = 0.0f;
+    if (it < items) {
+      for (int i = s; i < d; i += L) dot = fmaf(qx[h][i], kl[kc[t][i]], dot);
+      for (int j = s; j < m; j += L) qd += sb[t][j] ? qs[h][j] : -qs[h][j];
+    }
+    for (int msk = 1; msk < L; msk <<= 1) {
+      dot += __shfl_xor(dot, msk);
+      qd += __shfl_xor(qd, msk);
+    }
+    if (it < items && s == 0) {
+      const float logit = ok_t[t] ? A.scale * fmaf(A.qjl_coef * nr[t][1], qd, nr[t][0] * A.inv_sqrt_d * dot)
+                                  : kNegInf;
+      lg[h][t] = logit;
+      if (A.logits && ok_t[t]) A.logits[(qrow0 + h) * A.logit_stride + c0 + t] = logit;
+    }
+  }
+  __syncthreads();
+  for (int h = tid; h < G; h += kSmallThreads) {
+    float mx = kNegInf;
+    for (int t = 0; t < nt; ++t) mx = fmaxf(mx, lg[h][t]);
+    float l = 0.0f;
+    for (int t = 0; t < nt; ++t) {
+      const float p = (mx == kNegInf || lg[h][t] == kNegInf) ? 0.0f : __expf(lg[h][t] - mx);
+      l += p;
+      lg[h][t] = p * nr[t][2] * A.inv_sqrt_d;
+    }
+    hm[h] = mx;
+    hl[h] = l;
+  }
+  __syncthreads();
+  const int stride = d + 2;
+  for (int e = tid; e < G * d; e += kSmallThreads) {
+    const int h = e / d, i = e % d;
+    float o = 0.0f;
+    for (int t = 0; t < nt; ++t) o = fmaf(lg[h][t], vl[vc[t][i]], o);
+    A.part[((qrow0 + h) * A.n_chunks + chunk) * stride + 2 + i] = o;
+  }
+  for (int h = tid; h < G; h += kSmallThreads) {
+    A.part[((qrow0 + h) * A.n_chunks + chunk) * stride] = hm[h];
+    A.part[((qrow0 + h) * A.n_chunks + chunk) * stride + 1] = hl[h];
+  }
 }
 
 // -----------------------------------------------------------------------------------------
@@ -2418,6 +2555,92 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(MergeArgs A) {
   if (threadIdx.x == 0 && A.lse) A.lse[row] = L > 0.0f ? M + logf(L) : kNegInf;
 }
 
+// The merge for every other head_dim (d read at run time, up to 256): one workgroup per query
+// row.  Pass 1 takes the maximum over the chunk partials and the exact tokens' logits (one
+// thread per token, a plain dot product over d); pass 2 takes the exact tokens 2,048 at a
+// time - their weights into LDS, then one thread per coordinate sums weight x value - beside
+// the chunk partials, and o = Pi^T o_x + the exact part, over the total weight.
+__global__ __launch_bounds__(256) void decode_merge_generic_kernel(MergeArgs A) {
+  constexpr int NT = 256;
+  __shared__ float qv[kGenMaxD], ox[kGenMaxD], oh[kGenMaxD];
+  __shared__ float hp[kMergeHotLds];
+  __shared__ float red[NT / 64];
+  const int hq = blockIdx.x, b = blockIdx.y, hkv = hq / A.G, d = A.d, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int64_t row = (int64_t)b * A.q_heads + hq;
+  const int stride = d + 2;
+  const float* pr = A.part + row * A.n_chunks * stride;
+  const int n_chunks = (A.gate && A.gate[row] == 0) ? 0 : A.n_chunks;
+  auto block_reduce = [&](float v, bool is_max) {
+#pragma unroll
+    for (int msk = 32; msk > 0; msk >>= 1) {
+      const float o = __shfl_xor(v, msk);
+      v = is_max ? fmaxf(v, o) : v + o;
+    }
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    v = red[0];
+    for (int w2 = 1; w2 < NT / 64; ++w2) v = is_max ? fmaxf(v, red[w2]) : v + red[w2];
+    __syncthreads();
+    return v;
+  };
+  for (int i = tid; i < d; i += NT) {
+    qv[i] = load_elem(A.q, A.q_dt, row * d + i);
+    oh[i] = 0.0f;
+  }
+  const int nh = A.hot_lens ? (int)min((int64_t)A.hot_lens[b] + A.hot_add, A.hot_capacity) : 0;
+  const int64_t hs0 = A.hot_start ? A.hot_start[b] : 0;
+  auto hslot = [&](int t) -> int64_t {
+    const int64_t sl = hs0 + t;
+    return sl >= A.hot_capacity ? sl - A.hot_capacity : sl;
+  };
+  const int64_t hbase = ((int64_t)b * A.kv_heads + hkv) * A.hot_capacity * d;
+  __syncthreads();
+  auto hot_logit = [&](int t) {
+    const int64_t o = hbase + hslot(t) * d;
+    float dot = 0.0f;
+    for (int i = 0; i < d; ++i) dot = fmaf(qv[i], load_elem(A.hot_k, A.hot_dt, o + i), dot);
+    return A.scale * dot;
+  };
+  float mx = kNegInf;
+  for (int c = tid; c < n_chunks; c += NT) mx = fmaxf(mx, pr[(int64_t)c * stride]);
+  for (int t = tid; t < nh; t += NT) {
+    const float lgt = hot_logit(t);
+    mx = fmaxf(mx, lgt);
+    if (A.logits) A.logits[row * A.logit_stride + A.logit_hot_off + t] = lgt;
+  }
+  const float M = block_reduce(mx, true);
+  float l = 0.0f;
+  for (int c = tid; c < n_chunks; c += NT) {
+    const float mc = pr[(int64_t)c * stride];
+    l += (M != kNegInf && mc != kNegInf) ? pr[(int64_t)c * stride + 1] * __expf(mc - M) : 0.0f;
+  }
+  for (int i = tid; i < d; i += NT) ox[i] = merge_chunks(pr, n_chunks, stride, i, M);
+  for (int t0 = 0; t0 < nh; t0 += kMergeHotLds) {
+    const int nb = min(kMergeHotLds, nh - t0);
+    for (int t = tid; t < nb; t += NT) {
+      const float p = __expf(hot_logit(t0 + t) - M);
+      hp[t] = p;
+      l += p;
+    }
+    __syncthreads();
+    for (int i = tid; i < d; i += NT) {
+      float acc = oh[i];
+      for (int t = 0; t < nb; ++t) acc = fmaf(hp[t], load_elem(A.hot_v, A.hot_dt, hbase + hslot(t0 + t) * d + i), acc);
+      oh[i] = acc;
+    }
+    __syncthreads();
+  }
+  const float L = block_reduce(l, false);
+  for (int j = tid; j < d; j += NT) {
+    const float* pt = A.pi_t + (int64_t)j * d;
+    float o = 0.0f;
+    for (int i = 0; i < d; ++i) o = fmaf(pt[i], ox[i], o);
+    A.out[row * d + j] = L > 0.0f ? (o + oh[j]) / L : 0.0f;
+  }
+  if (tid == 0 && A.lse) A.lse[row] = L > 0.0f ? M + logf(L) : kNegInf;
+}
+
 template <int D, int GG>
 __global__ __launch_bounds__(256) void decode_merge_group_kernel(MergeArgs A) {
   merge_group<D, GG>(A.pi_t, A.part, A.out, A.lse,
@@ -2436,6 +2659,27 @@ static bool polar_mfma_path(const Consts& c, int G) {
 bool plan_decode(const Consts& c, int batch, int q_heads, int kv_heads, int64_t n_max,
                  DecodePlan* plan) {
   const int G = q_heads / kv_heads;
+  plan->generic = c.d != 64 && c.d != 128;
+  if (plan->generic) {
+    // every other head_dim: the generic direct kernel, chunks of kDecGenTok tokens
+    if (c.polar || G > kSmallMaxG || c.d > kGenMaxD || c.m > kDecGenMaxM || c.rec_bytes > kDecGenMaxRec) return false;
+    plan->mfma = false;
+    plan->small = false;
+    plan->group = G;
+    plan->hpl = 1;
+    plan->key_pairs = false;
+    plan->sign_bytes = false;
+    plan->chunk = kDecGenTok;
+    plan->lds_bytes = 0;
+    plan->n_chunks = (int)std::max<int64_t>(1, (n_max + kDecGenTok - 1) / kDecGenTok);
+    const size_t rows = (size_t)std::max(batch, 1) * q_heads;
+    plan->ws_qx = 0;
+    plan->ws_qs = align256(rows * c.d * 4);
+    plan->ws_part = plan->ws_qs + align256(rows * std::max(c.m, 1) * 4);
+    plan->ws_bop = plan->ws_part + align256(rows * plan->n_chunks * (c.d + 2) * 4);
+    plan->ws_total = plan->ws_bop;
+    return true;
+  }
   plan->mfma = c.polar ? polar_mfma_path(c, G) : mfma_path(c, G);
   const int hpl = (G % 4 == 0) ? 4 : 1;
   const int lpt = (c.d / 32) * (G / hpl);
@@ -2597,6 +2841,8 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
   a.sbytes = c.sbytes;
   a.rec_bytes = c.rec_bytes;
   a.norm_off = c.norm_off;
+  a.kb = c.kb;
+  a.vb = c.vb;
   a.G = plan.group;
   a.q_heads = q_heads;
   a.kv_heads = kv_heads;
@@ -2619,7 +2865,9 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
   a.l1_bytes = c.l1_bytes;
   dim3 grid(plan.n_chunks, kv_heads, batch);
   ev.before(stream);
-  if (mfma) {
+  if (plan.generic) {
+    hipLaunchKernelGGL(decode_generic_kernel, grid, dim3(kSmallThreads), 0, stream, a);
+  } else if (mfma) {
     launch_mfma_scan(a, c.kb, c.m > 0, sel_idx != nullptr, logits != nullptr, grid, stream, c.polar != 0);
   } else if (plan.small) {
     if (c.d == 128) launch_small_d<128>(a, c.kb, c.vb, grid, stream);
@@ -2661,7 +2909,9 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
 static hipError_t launch_merge(const Consts& c, const MergeArgs& mg, int batch, hipStream_t stream) {
   const int q_heads = mg.q_heads, kv_heads = mg.kv_heads;
   const dim3 mgrid(q_heads, batch);
-  if (mg.hot_lens) {
+  if (c.d != 64 && c.d != 128) {
+    hipLaunchKernelGGL(decode_merge_generic_kernel, mgrid, dim3(256), 0, stream, mg);
+  } else if (mg.hot_lens) {
     if (c.d == 128) hipLaunchKernelGGL((decode_merge_kernel<128, kMergeThreadsHot>), mgrid, dim3(kMergeThreadsHot), 0, stream, mg);
     else hipLaunchKernelGGL((decode_merge_kernel<64, kMergeThreadsHot>), mgrid, dim3(kMergeThreadsHot), 0, stream, mg);
   } else if (mg.G == 4 || mg.G == 2) {
@@ -2906,6 +3156,45 @@ __global__ __launch_bounds__(256) void index_pattern_kernel(IndexArgs A) {
   }
 }
 
+// Patterns and per-chunk centroid sums for every other head_dim (d read at run time, a multiple
+// of 8 up to 256): thread ch < d owns channel ch and takes the chunk's tokens in order - bit
+// [k >= mu], the 4-bit pattern of its group and the record byte from a wave ballot (groups
+// and octets never straddle a wave), then sum[pattern][ch] += k - mu in float64 (LDS), the
+// group's first thread counting.  Same per-chunk sums as index_pattern_kernel.
+template <tq_dtype DT>
+__global__ __launch_bounds__(256) void index_pattern_generic_kernel(IndexArgs A) {
+  __shared__ double acc[16 * kGenMaxD];       // [pattern][channel]
+  __shared__ int32_t cnt[kGenMaxD / 4 * 16];  // [group][pattern]
+  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z, d = A.d, ng = d / 4;
+  const int ch = threadIdx.x, lane = ch & 63;
+  const int64_t unit = (int64_t)b * A.heads + h;
+  for (int i = threadIdx.x; i < 16 * kGenMaxD; i += 256) acc[i] = 0.0;
+  for (int i = threadIdx.x; i < ng * 16; i += 256) cnt[i] = 0;
+  __syncthreads();
+  const bool own = ch < d;
+  const float mu = own ? A.mu[unit * d + ch] : 0.0f;
+  const int64_t base = (int64_t)b * A.seq_stride + (int64_t)h * A.head_stride + (own ? ch : 0);
+  const int64_t t0 = (int64_t)chunk * A.chunk, t1 = min(A.n_tokens, t0 + A.chunk);
+  uint8_t* idx = A.index + (unit * A.capacity + A.first_slot) * (d / 8);
+  for (int64_t t = t0; t < t1; ++t) {
+    const float k = load_elem(A.k, DT, base + t * A.tok_stride);
+    const bool bit = own && k >= mu;
+    const uint64_t bal = __ballot(bit);
+    const int p = (int)((bal >> (lane & ~3)) & 15u);
+    if (own) {
+      acc[p * kGenMaxD + ch] += (double)k - (double)mu;
+      if ((ch & 3) == 0) cnt[(ch >> 2) * 16 + p] += 1;
+      if ((ch & 7) == 0) idx[t * (d / 8) + (ch >> 3)] = (uint8_t)((bal >> (lane & ~7)) & 0xFFu);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < ng * 64; e += 256) {
+    const int gg = e / 64, p = (e / 4) % 16, j = e % 4;
+    A.csum[((unit * A.n_chunks + chunk) * ng + gg) * 64 + p * 4 + j] = acc[p * kGenMaxD + 4 * gg + j];
+  }
+  for (int e = threadIdx.x; e < ng * 16; e += 256) A.ccnt[(unit * A.n_chunks + chunk) * ng * 16 + e] = cnt[e];
+}
+
 // One workgroup per (group, KV head, sequence); thread (pattern, channel) sums the chunks in
 // order.
 __global__ __launch_bounds__(64) void index_centroid_final_kernel(IndexArgs A) {
@@ -2953,7 +3242,11 @@ hipError_t launch_sign_index(const Consts& c, const IndexPlan& plan, const void*
   else if (dt == TQ_F16) hipLaunchKernelGGL(index_mean_kernel<TQ_F16>, grid, dim3(256), 0, stream, A);
   else hipLaunchKernelGGL(index_mean_kernel<TQ_BF16>, grid, dim3(256), 0, stream, A);
   hipLaunchKernelGGL(index_mean_final_kernel, dim3(heads, batch), dim3(128), 0, stream, A);
-  if (c.d == 128 && dt == TQ_F32) hipLaunchKernelGGL((index_pattern_kernel<128, TQ_F32>), grid, dim3(256), 0, stream, A);
+  if (c.d != 64 && c.d != 128) {
+    if (dt == TQ_F32) hipLaunchKernelGGL(index_pattern_generic_kernel<TQ_F32>, grid, dim3(256), 0, stream, A);
+    else if (dt == TQ_F16) hipLaunchKernelGGL(index_pattern_generic_kernel<TQ_F16>, grid, dim3(256), 0, stream, A);
+    else hipLaunchKernelGGL(index_pattern_generic_kernel<TQ_BF16>, grid, dim3(256), 0, stream, A);
+  } else if (c.d == 128 && dt == TQ_F32) hipLaunchKernelGGL((index_pattern_kernel<128, TQ_F32>), grid, dim3(256), 0, stream, A);
   else if (c.d == 128 && dt == TQ_F16) hipLaunchKernelGGL((index_pattern_kernel<128, TQ_F16>), grid, dim3(256), 0, stream, A);
   else if (c.d == 128) hipLaunchKernelGGL((index_pattern_kernel<128, TQ_BF16>), grid, dim3(256), 0, stream, A);
   else if (dt == TQ_F32) hipLaunchKernelGGL((index_pattern_kernel<64, TQ_F32>), grid, dim3(256), 0, stream, A);
@@ -3179,6 +3472,43 @@ __global__ __launch_bounds__(kScoreThreads, 8) void select_score_kernel(const ui
   __syncthreads();
   int32_t* gh = hist_all + unit * kSelBins;
   for (int e = threadIdx.x; e < kSelBins; e += kScoreThreads) {
+    const int v = hist[e];
+    if (v) atomicAdd(&gh[e], v);
+  }
+}
+
+// Scores for every other head_dim: index records of d / 8 bytes read byte by byte, one
+// 16-entry table per 4-channel group (d / 4 groups), 16 tokens per thread; the same histogram.
+__global__ __launch_bounds__(256) void select_score_generic_kernel(const uint8_t* index, const int32_t* lut_all,
+                                                                   const int32_t* seq_lens, int heads, int d,
+                                                                   int64_t capacity, int32_t* scores,
+                                                                   int32_t* hist_all) {
+  __shared__ int32_t lut[kGenMaxD / 4 * 16];
+  __shared__ int32_t hist[kSelBins];
+  const int h = blockIdx.y, b = blockIdx.z, ng = d / 4, nb = d / 8;
+  const int64_t unit = (int64_t)b * heads + h;
+  const int64_t n = min((int64_t)seq_lens[b], capacity);
+  const int64_t t0 = (int64_t)blockIdx.x * kSelChunk;
+  if (t0 >= n) return;
+  for (int e = threadIdx.x; e < ng * 16; e += 256) lut[e] = lut_all[unit * ng * 16 + e];
+  for (int e = threadIdx.x; e < kSelBins; e += 256) hist[e] = 0;
+  __syncthreads();
+  const uint8_t* base = index + (unit * capacity + t0) * nb;
+  int32_t* sc = scores + unit * capacity + t0;
+  const int m = (int)min((int64_t)kSelChunk, n - t0);
+  for (int t = threadIdx.x; t < m; t += 256) {
+    const uint8_t* r = base + (int64_t)t * nb;
+    int32_t s = 0;
+    for (int k = 0; k < nb; ++k) {
+      const uint32_t byte = r[k];
+      s += lut[(2 * k) * 16 + (byte & 15u)] + lut[(2 * k + 1) * 16 + (byte >> 4)];
+    }
+    sc[t] = s;
+    atomicAdd(&hist[order_key(s) >> kSelDigitShift], 1);
+  }
+  __syncthreads();
+  int32_t* gh = hist_all + unit * kSelBins;
+  for (int e = threadIdx.x; e < kSelBins; e += 256) {
     const int v = hist[e];
     if (v) atomicAdd(&gh[e], v);
   }
@@ -3479,7 +3809,10 @@ hipError_t launch_select(const Consts& c, const SelectPlan& plan, const void* q,
                          c.d, G, q_heads, kv_heads, lut, hist);
     const dim3 grid((unsigned)n_chunks, kv_heads, batch);
     ev.before(stream);
-    if (c.d == 128)
+    if (c.d != 64 && c.d != 128)
+      hipLaunchKernelGGL(select_score_generic_kernel, grid, dim3(256), 0, stream, static_cast<const uint8_t*>(index),
+                         lut, seq_lens, kv_heads, c.d, capacity, scores, hist);
+    else if (c.d == 128)
       hipLaunchKernelGGL(select_score_kernel<16>, grid, dim3(kScoreThreads), 0, stream, static_cast<const uint8_t*>(index),
                          lut, seq_lens, kv_heads, capacity, scores, hist);
     else
@@ -3916,6 +4249,137 @@ __global__ __launch_bounds__(kSmallThreads) void sparse_attend_kernel(SparseArgs
   }
 }
 
+// Sparse attention for every other head_dim (scalar key codes): the chunk's selected tokens as
+// in the other sparse kernels, taken kDecGenTok at a time with decode_generic_kernel's record
+// staging and unpacking (d, code widths and sketch width read at run time), an online softmax
+// per head across the batches, and the value sums per (head, coordinate) kept in registers.
+__global__ __launch_bounds__(kSmallThreads) void sparse_attend_generic_kernel(SparseArgs S) {
+  const DecodeArgs& A = S.a;
+  constexpr int TB = kDecGenTok, kMaxOut = kSmallMaxG * kGenMaxD / kSmallThreads;
+  __shared__ uint16_t list[kSelChunk];
+  __shared__ int wsum[kSmallThreads / 64];
+  __shared__ int s_nsel;
+  __shared__ float qx[kSmallMaxG][kGenMaxD + 1];
+  __shared__ float qs[kSmallMaxG][kDecGenMaxM + 1];
+  __shared__ __attribute__((aligned(16))) uint32_t raw[TB][kDecGenMaxRec / 4];
+  __shared__ uint8_t kc[TB][kGenMaxD];
+  __shared__ uint8_t vc[TB][kGenMaxD];
+  __shared__ uint8_t sb[TB][kDecGenMaxM];
+  __shared__ float nr[TB][3];
+  __shared__ float lg[kSmallMaxG][TB + 1];
+  __shared__ float hm[kSmallMaxG], hl[kSmallMaxG], hf[kSmallMaxG];
+  __shared__ float kl[kMaxLevels], vl[kMaxLevels];
+  const int G = A.G, m = A.m, d = A.d, tid = threadIdx.x;
+  const int c = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+  const int64_t unit = (int64_t)b * A.kv_heads + hkv;
+  const int64_t qrow0 = (int64_t)b * A.q_heads + (int64_t)hkv * G;
+  const int64_t n = min((int64_t)A.seq_lens[b], A.capacity);
+  const int64_t kk = min((int64_t)S.k, n);
+  const int64_t t0 = (int64_t)c * kSelChunk;
+  sparse_chunk_list(S, unit, c, n, kk, list, wsum, &s_nsel);
+  for (int e = tid; e < G * d; e += kSmallThreads) qx[e / d][e % d] = A.qx[(qrow0 + e / d) * d + e % d];
+  for (int e = tid; e < G * m; e += kSmallThreads) qs[e / m][e % m] = A.qs[(qrow0 + e / m) * m + e % m];
+  if (tid < kMaxLevels) {
+    kl[tid] = A.key_levels[tid];
+    vl[tid] = A.val_levels[tid];
+  }
+  if (tid < G) {
+    hm[tid] = kNegInf;
+    hl[tid] = 0.0f;
+  }
+  float o[kMaxOut];
+#pragma unroll
+  for (int r = 0; r < kMaxOut; ++r) o[r] = 0.0f;
+  __syncthreads();
+  const int nsel = s_nsel;
+  const uint8_t* recs = A.records + unit * A.capacity * A.rec_bytes;
+  const int rw = A.rec_bytes / 4, per_t = 2 * d + m;
+  for (int s0 = 0; s0 < nsel; s0 += TB) {
+    const int nt = min(TB, nsel - s0);
+    for (int e = tid; e < nt * rw; e += kSmallThreads) {
+      const int t = e / rw, w = e % rw;
+      raw[t][w] = reinterpret_cast<const uint32_t*>(recs + (t0 + list[s0 + t]) * A.rec_bytes)[w];
+    }
+    __syncthreads();
+    for (int e = tid; e < nt * per_t; e += kSmallThreads) {
+      const int t = e / per_t, j = e % per_t;
+      const uint8_t* r = reinterpret_cast<const uint8_t*>(raw[t]);
+      if (j < d) kc[t][j] = (uint8_t)field_code(r, j, A.kb, d);
+      else if (j < 2 * d) vc[t][j - d] = (uint8_t)field_code(r + A.kbytes + A.sbytes, j - d, A.vb, d);
+      else sb[t][j - 2 * d] = (uint8_t)((r[A.kbytes + ((j - 2 * d) >> 3)] >> ((j - 2 * d) & 7)) & 1u);
+    }
+    for (int t = tid; t < nt; t += kSmallThreads) {
+      const float* f = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(raw[t]) + A.norm_off);
+      nr[t][0] = f[0];
+      nr[t][1] = f[1];
+      nr[t][2] = f[2];
+    }
+    __syncthreads();
+    const int items = nt * G;
+    int L = 1;
+    while (L < 8 && items * L * 2 <= kSmallThreads) L *= 2;
+    for (int i0 = 0; i0 < items; i0 += kSmallThreads / L) {
+      const int it = i0 + tid / L, sl = tid % L;
+      const int t = it / G, h = it % G;
+      float dot = 0.0f, qd = 0.0f;
+      if (it < items) {
+        for (int i = sl; i < d; i += L) dot = fmaf(qx[h][i], kl[kc[t][i]], dot);
+        for (int j = sl; j < m; j += L) qd += sb[t][j] ? qs[h][j] : -qs[h][j];
+      }
+      for (int msk = 1; msk < L; msk <<= 1) {
+        dot += __shfl_xor(dot, msk);
+        qd += __shfl_xor(qd, msk);
+      }
+      if (it < items && sl == 0)
+        lg[h][t] = A.scale * fmaf(A.qjl_coef * nr[t][1], qd, nr[t][0] * A.inv_sqrt_d * dot);
+    }
+    __syncthreads();
+    {
+      const int lane = tid & 63, wv = tid >> 6;
+      for (int h = wv; h < G; h += kSmallThreads / 64) {
+        const float x = lane < nt ? lg[h][lane] : kNegInf;
+        float bm = x;
+#pragma unroll
+        for (int msk = 32; msk > 0; msk >>= 1) bm = fmaxf(bm, __shfl_xor(bm, msk));
+        const float mo = hm[h], mn = fmaxf(mo, bm);
+        const float p = x == kNegInf ? 0.0f : __expf(x - mn);
+        float ps = p;
+#pragma unroll
+        for (int msk = 32; msk > 0; msk >>= 1) ps += __shfl_xor(ps, msk);
+        if (lane < nt) lg[h][lane] = p * nr[lane][2] * A.inv_sqrt_d;
+        if (lane == 0) {
+          const float f = mo == kNegInf ? 0.0f : __expf(mo - mn);
+          hf[h] = f;
+          hm[h] = mn;
+          hl[h] = hl[h] * f + ps;
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kMaxOut; ++r) {
+      const int e = tid + kSmallThreads * r;
+      if (e < G * d) {
+        const int h = e / d, i = e % d;
+        float acc = o[r] * hf[h];
+        for (int t = 0; t < nt; ++t) acc = fmaf(lg[h][t], vl[vc[t][i]], acc);
+        o[r] = acc;
+      }
+    }
+    __syncthreads();            // the next batch overwrites the records, codes and weights
+  }
+  const int stride = d + 2;
+#pragma unroll
+  for (int r = 0; r < kMaxOut; ++r) {
+    const int e = tid + kSmallThreads * r;
+    if (e < G * d) A.part[((qrow0 + e / d) * A.n_chunks + c) * stride + 2 + e % d] = o[r];
+  }
+  for (int h = tid; h < G; h += kSmallThreads) {
+    A.part[((qrow0 + h) * A.n_chunks + c) * stride] = hm[h];
+    A.part[((qrow0 + h) * A.n_chunks + c) * stride + 1] = hl[h];
+  }
+}
+
 SparsePlan plan_sparse(const Consts& c, int batch, int q_heads, int kv_heads, int64_t capacity) {
   SparsePlan p;
   p.select = plan_select(c, batch, kv_heads, capacity);
@@ -3986,6 +4450,8 @@ hipError_t launch_sparse(const Consts& c, const DevConsts& dc, const SparsePlan&
   a.sbytes = c.sbytes;
   a.rec_bytes = c.rec_bytes;
   a.norm_off = c.norm_off;
+  a.kb = c.kb;
+  a.vb = c.vb;
   a.G = q_heads / kv_heads;
   a.q_heads = q_heads;
   a.kv_heads = kv_heads;
@@ -4010,7 +4476,8 @@ hipError_t launch_sparse(const Consts& c, const DevConsts& dc, const SparsePlan&
   // query rows held in LDS sized for the group (a smaller footprint keeps more workgroups per CU)
   const int G = q_heads / kv_heads;
   const bool lean = G == 1 && c.m == 0 && c.kb == 4 && c.vb == 4 && !c.polar && (c.d == 128 || c.d == 64);
-  if (lean && c.d == 128) hipLaunchKernelGGL(sparse_attend_lean_kernel<128>, grid, dim3(kSmallThreads), 0, stream, s);
+  if (c.d != 64 && c.d != 128) hipLaunchKernelGGL(sparse_attend_generic_kernel, grid, dim3(kSmallThreads), 0, stream, s);
+  else if (lean && c.d == 128) hipLaunchKernelGGL(sparse_attend_lean_kernel<128>, grid, dim3(kSmallThreads), 0, stream, s);
   else if (lean) hipLaunchKernelGGL(sparse_attend_lean_kernel<64>, grid, dim3(kSmallThreads), 0, stream, s);
   else if (c.d == 128 && G <= 4) launch_sparse_d<128, 4>(s, c.kb, c.vb, c.polar != 0, grid, stream);
   else if (c.d == 128) launch_sparse_d<128, kSmallMaxG>(s, c.kb, c.vb, c.polar != 0, grid, stream);

@@ -83,7 +83,7 @@ extern "C" {
 typedef enum tq_status {
   TQ_OK = 0,
   TQ_ERR_INVALID_ARGUMENT = 1,   /* bad pointer, shape, stride, dtype or value        */
-  TQ_ERR_UNSUPPORTED = 2,        /* valid but not built (e.g. head_dim not 64 or 128) */
+  TQ_ERR_UNSUPPORTED = 2,        /* valid but not built (e.g. polar keys at head_dim 200) */
   TQ_ERR_WORKSPACE_TOO_SMALL = 3,
   TQ_ERR_OUT_OF_MEMORY = 4,      /* tq_create only                                   */
   TQ_ERR_DEVICE = 5              /* a HIP call or kernel launch failed               */
@@ -105,9 +105,12 @@ typedef enum tq_dtype { TQ_F32 = 0, TQ_F16 = 1, TQ_BF16 = 2 } tq_dtype;
 typedef enum tq_key_codec { TQ_KEY_SCALAR = 0, TQ_KEY_POLAR = 1 } tq_key_codec;
 
 typedef struct tq_config {
-  int32_t head_dim;       /* d: 64 or 128 for every call; any multiple of 8 up to 256
-                             for tq_compress_kv and tq_score_scan (the other calls
-                             return TQ_ERR_UNSUPPORTED for such a handle)              */
+  int32_t head_dim;       /* d: 64 or 128 for every call; any other multiple of 8 up
+                             to 256 (scalar keys) for tq_compress_kv, tq_score_scan,
+                             decode attention, the sign index, tq_select_topk and
+                             tq_sparse_attention (direct kernels that read d at run
+                             time); tq_debug_quantize and the hot/cold step return
+                             TQ_ERR_UNSUPPORTED for such a handle                      */
   int32_t key_bits;       /* b_k: bits per rotated key coordinate, 1..4; polar: bits
                              per level-1 angle, 2 or 4                                 */
   int32_t qjl_dim;        /* m: 0 (no QJL sketch) or a multiple of 32, at most 256     */
