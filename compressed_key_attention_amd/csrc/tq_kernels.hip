@@ -2444,6 +2444,7 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(MergeArgs A) {
   __shared__ float ohw[NT / 64][D];
   __shared__ float hlog[kMergeHotLds];
   __shared__ float red[NT];
+  __shared__ float oxp[NT];   // per-thread partial sums of the rotated-domain output
   const int hq = blockIdx.x, b = blockIdx.y, hkv = hq / A.G;
   const int64_t row = (int64_t)b * A.q_heads + hq;
   constexpr int stride = D + 2;
@@ -2511,7 +2512,31 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(MergeArgs A) {
     const float mc = pr[(int64_t)c * stride];
     l += (M != kNegInf && mc != kNegInf) ? pr[(int64_t)c * stride + 1] * __expf(mc - M) : 0.0f;
   }
-  for (int i = threadIdx.x; i < D; i += blockDim.x) ox[i] = merge_chunks(pr, n_chunks, stride, i, M);
+  {
+    // NT / D threads per coordinate, each over every (NT / D)-th chunk (eight loads in flight),
+    // then the NT / D partial sums of a coordinate added in LDS: the chunk count (up to a few
+    // hundred for short-chunk scans) no longer sets the number of dependent memory round trips
+    constexpr int SPLIT = NT / D;
+    const int ci = threadIdx.x % D, sp = threadIdx.x / D;
+    float acc = 0.0f;
+    int c = sp;
+    for (; c + 7 * SPLIT < n_chunks; c += 8 * SPLIT) {
+      float mc[8], ov[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        mc[u] = pr[(int64_t)(c + u * SPLIT) * stride];
+        ov[u] = pr[(int64_t)(c + u * SPLIT) * stride + 2 + ci];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        acc = fmaf(ov[u], (M != kNegInf && mc[u] != kNegInf) ? __expf(mc[u] - M) : 0.0f, acc);
+    }
+    for (; c < n_chunks; c += SPLIT) {
+      const float mc = pr[(int64_t)c * stride];
+      acc = fmaf(pr[(int64_t)c * stride + 2 + ci], (M != kNegInf && mc != kNegInf) ? __expf(mc - M) : 0.0f, acc);
+    }
+    oxp[sp * D + ci] = acc;
+  }
   // hot values: each lane accumulates its 8 coordinates over the tokens of its slot
   float oh8[8];
 #pragma unroll
@@ -2537,7 +2562,14 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(MergeArgs A) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) ohw[wave][8 * sub + i] = oh8[i];
   }
-  const float L = block_reduce(l, false);   // (its barriers also order the ox / oh writes)
+  const float L = block_reduce(l, false);   // (its barriers also order the oxp / oh writes)
+  for (int i = threadIdx.x; i < D; i += NT) {
+    float v = 0.0f;
+#pragma unroll
+    for (int q = 0; q < NT / D; ++q) v += oxp[q * D + i];
+    ox[i] = v;
+  }
+  __syncthreads();
   // o = Pi^T o_x: output i = row i of the transposed rotation against o_x
   {
     const int r = threadIdx.x >> 1, h = threadIdx.x & 1;
@@ -2615,7 +2647,26 @@ __global__ __launch_bounds__(256) void decode_merge_generic_kernel(MergeArgs A) 
     const float mc = pr[(int64_t)c * stride];
     l += (M != kNegInf && mc != kNegInf) ? pr[(int64_t)c * stride + 1] * __expf(mc - M) : 0.0f;
   }
-  for (int i = tid; i < d; i += NT) ox[i] = merge_chunks(pr, n_chunks, stride, i, M);
+  {
+    // coordinates 32 at a time, 8 threads per coordinate over every 8th chunk, summed in LDS
+    const int ci = tid & 31, sp = tid >> 5;
+    for (int i0 = 0; i0 < d; i0 += 32) {
+      const int i = min(i0 + ci, d - 1);
+      float acc = 0.0f;
+      for (int c = sp; c < n_chunks; c += NT / 32) {
+        const float mc = pr[(int64_t)c * stride];
+        acc = fmaf(pr[(int64_t)c * stride + 2 + i], (M != kNegInf && mc != kNegInf) ? __expf(mc - M) : 0.0f, acc);
+      }
+      hp[sp * 32 + ci] = acc;
+      __syncthreads();
+      if (tid < 32 && i0 + tid < d) {
+        float v = 0.0f;
+        for (int q = 0; q < NT / 32; ++q) v += hp[q * 32 + tid];
+        ox[i0 + tid] = v;
+      }
+      __syncthreads();
+    }
+  }
   for (int t0 = 0; t0 < nh; t0 += kMergeHotLds) {
     const int nb = min(kMergeHotLds, nh - t0);
     for (int t = tid; t < nb; t += NT) {
