@@ -149,7 +149,7 @@ hipError_t launch_select(const Consts& c, const SelectPlan& plan, const void* q,
                          const float* codebook, int64_t capacity, const int32_t* seq_lens,
                          int k, int32_t* out_idx, int32_t* out_count, int32_t* out_scores,
                          void* workspace, hipStream_t stream, const ProfileEvents& ev,
-                         const QueryPrep* prep = nullptr);
+                         const QueryPrep* prep = nullptr, bool skip_exact = false);
 hipError_t launch_sparse(const Consts& c, const DevConsts& dc, const SparsePlan& plan, const void* q,
                          tq_dtype q_dt, int batch, int q_heads, int kv_heads, const void* index,
                          const float* codebook, const void* records, int64_t capacity,

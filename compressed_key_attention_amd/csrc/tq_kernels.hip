@@ -3838,7 +3838,7 @@ hipError_t launch_select(const Consts& c, const SelectPlan& plan, const void* q,
                          int q_heads, int kv_heads, const void* index, const float* codebook,
                          int64_t capacity, const int32_t* seq_lens, int k, int32_t* out_idx,
                          int32_t* out_count, int32_t* out_scores, void* workspace, hipStream_t stream,
-                         const ProfileEvents& ev, const QueryPrep* prep) {
+                         const ProfileEvents& ev, const QueryPrep* prep, bool skip_exact) {
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   int32_t* lut = reinterpret_cast<int32_t*>(ws + plan.ws_lut);
   int32_t* scores = reinterpret_cast<int32_t*>(ws + plan.ws_scores);
@@ -3873,6 +3873,7 @@ hipError_t launch_select(const Consts& c, const SelectPlan& plan, const void* q,
     hipLaunchKernelGGL(select_filter_kernel, grid, dim3(256), 0, stream, scores, hist, seq_lens, kv_heads, capacity,
                        k, n_chunks, cand, chunk_cand, chunk_above, params);
   }
+  if (skip_exact) return hipGetLastError();     // sparse attention forms the threshold itself
   const size_t exact_lds = (size_t)std::max(n_chunks, 1) * 8;
   allow_lds(select_exact_kernel, exact_lds);
   hipLaunchKernelGGL(select_exact_kernel, dim3(kv_heads, batch), dim3(kSelExactThreads), exact_lds, stream, seq_lens, kv_heads, capacity, k, n_chunks, cand,
@@ -3898,21 +3899,139 @@ struct SparseArgs {
   const int32_t* scores;    // [units][capacity] selection scores
   const SelectParams* params;
   const int32_t* chunk_off;
+  // fused threshold (no exact launch): the filter launch's candidates and per-chunk counts
+  const uint2* cand_all;
+  const int32_t* chunk_cand;
+  const int32_t* chunk_above;
   int k;
+  int fused;
 };
+
+constexpr int kFusedMaxChunks = 1024;    // chunks per unit for which the attention forms the threshold
+
+// The unit's selection predicate ((key & mask) >= prefix) and the output offset of chunk c,
+// formed by the attention workgroup itself from the filter launch's candidates - the exact
+// launch's computation, repeated by every chunk of the unit instead of a launch of its own:
+// radix passes over the candidates (the tokens in the bin of the k-th score) on the 64-bit key
+// until exactly the tokens still needed match, then the tokens above the bin and the chosen
+// candidates in the chunks before c.  Called by all kSmallThreads threads; the results are
+// valid in every thread on return.
+__device__ void sparse_unit_threshold(const SparseArgs& S, int64_t unit, int c, int64_t n, int64_t kk,
+                                      uint64_t* prefix_out, uint64_t* mask_out, int* base_out) {
+  constexpr int NT = kSmallThreads;
+  __shared__ int cpre[kFusedMaxChunks];
+  __shared__ int hist[256];
+  __shared__ int wsum2[NT / 64];
+  __shared__ uint32_t s_digit, s_rem, s_cnt;
+  const int tid = threadIdx.x;
+  if (kk == 0 || kk == n) {           // nothing, or every token, is selected
+    *prefix_out = 0;
+    *mask_out = 0;
+    *base_out = c * kSelChunk;
+    return;
+  }
+  const int nch = (int)((n + kSelChunk - 1) / kSelChunk);
+  const int32_t* ccand = S.chunk_cand + unit * S.a.n_chunks;
+  const int32_t* cabove = S.chunk_above + unit * S.a.n_chunks;
+  int nc = 0;
+  for (int c0 = 0; c0 < nch; c0 += NT) {
+    const int cc = c0 + tid;
+    const int v = cc < nch ? ccand[cc] : 0;
+    int tot;
+    const int ex = block_exclusive_sum<NT>(v, wsum2, &tot);
+    if (cc < nch) cpre[cc] = nc + ex;
+    nc += tot;
+  }
+  __syncthreads();
+  const uint2* cand = S.cand_all + unit * S.a.capacity;
+  auto cand_at = [&](int i) {
+    int lo = 0, hi = nch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cpre[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    return cand[(int64_t)lo * kSelChunk + (i - cpre[lo])];
+  };
+  const SelectParams p0 = S.params[unit];
+  uint64_t prefix = (uint64_t)p0.bin << (32 + kSelDigitShift);
+  uint64_t mask = (uint64_t)(kSelBins - 1) << (32 + kSelDigitShift);
+  uint32_t rem = (uint32_t)(kk - p0.above);
+  uint32_t cnt = (uint32_t)nc;
+  for (int pass = 0; pass < 7 && cnt != rem; ++pass) {
+    const int sh = pass < 2 ? 44 - 8 * pass : (pass == 2 ? 32 : 24 - 8 * (pass - 3));
+    const uint32_t dm = pass == 2 ? 15u : 255u;
+    for (int i = tid; i < 256; i += NT) hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < nc; i += NT) {
+      const uint2 cu = cand_at(i);
+      const uint64_t key = select_key(cu.x, (int32_t)cu.y);
+      if ((key & mask) == prefix) atomicAdd(&hist[(uint32_t)(key >> sh) & dm], 1);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      const int l = tid;
+      const int own = hist[4 * l] + hist[4 * l + 1] + hist[4 * l + 2] + hist[4 * l + 3];
+      int suf = own;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_down(suf, o);
+        if (l + o < 64) suf += v;
+      }
+      const int above = suf - own;
+      if (above < (int)rem && suf >= (int)rem) {
+        int cum = above;
+        for (int j = 3; j >= 0; --j) {
+          const int hvv = hist[4 * l + j];
+          if (cum + hvv >= (int)rem) {
+            s_digit = (uint32_t)(4 * l + j);
+            s_rem = rem - (uint32_t)cum;
+            s_cnt = (uint32_t)hvv;
+            break;
+          }
+          cum += hvv;
+        }
+      }
+    }
+    __syncthreads();
+    prefix |= (uint64_t)s_digit << sh;
+    mask |= (uint64_t)dm << sh;
+    rem = s_rem;
+    cnt = s_cnt;
+    __syncthreads();
+  }
+  int mine = 0;
+  for (int i = tid; i < nc; i += NT) {
+    const uint2 cu = cand_at(i);
+    if ((int)(cu.y / kSelChunk) < c && (select_key(cu.x, (int32_t)cu.y) & mask) >= prefix) ++mine;
+  }
+  for (int cc = tid; cc < c; cc += NT) mine += cabove[cc];
+  int tot;
+  (void)block_exclusive_sum<NT>(mine, wsum2, &tot);
+  *prefix_out = prefix;
+  *mask_out = mask;
+  *base_out = tot;
+}
 
 // The selected tokens of chunk c of a unit, in index order and capped at k overall (the write
 // launch's rule): offsets within the chunk into list[], their count into *s_nsel (written by
 // thread 0; read after the caller's next barrier).  Called by all kSmallThreads threads.
 __device__ __forceinline__ void sparse_chunk_list(const SparseArgs& S, int64_t unit, int c, int64_t n,
                                                   int64_t kk, uint16_t* list, int* wsum, int* s_nsel) {
+  uint64_t prefix = 0, mask = 0;
+  int base = 0;
+  if (S.fused) {
+    sparse_unit_threshold(S, unit, c, n, kk, &prefix, &mask, &base);
+  } else if (kk > 0 && (int64_t)c * kSelChunk < n) {
+    prefix = S.params[unit].prefix;
+    mask = S.params[unit].mask;
+    base = S.chunk_off[unit * S.a.n_chunks + c];
+  }
   constexpr int kPer = kSelChunk / kSmallThreads;
   const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)c * kSelChunk;
   const int tb = tid * kPer;
   uint32_t sel = 0;
   if (kk > 0 && t0 < n) {
-    const uint64_t prefix = S.params[unit].prefix, mask = S.params[unit].mask;
     const int mm = (int)min((int64_t)kSelChunk, n - t0);
     const int32_t* sc = S.scores + unit * S.a.capacity + t0;
     int32_t s[kPer];
@@ -3935,7 +4054,7 @@ __device__ __forceinline__ void sparse_chunk_list(const SparseArgs& S, int64_t u
   }
   int tot;
   int pos = block_exclusive_sum<kSmallThreads>(__popc(sel), wsum, &tot);
-  const int base = (kk > 0 && t0 < n) ? S.chunk_off[unit * S.a.n_chunks + c] : 0;
+  if (!(kk > 0 && t0 < n)) base = 0;
 #pragma unroll
   for (int j = 0; j < kPer; ++j)
     if (sel & (1u << j)) {
@@ -4478,8 +4597,11 @@ hipError_t launch_sparse(const Consts& c, const DevConsts& dc, const SparsePlan&
   const int rows = batch * q_heads;
   // the query prep rides in the selection's table launch (which runs when capacity > 0)
   const QueryPrep prep{dc.pi, dc.s, c.m, rows, qx, qs};
+  // with at most kFusedMaxChunks chunks per unit the attention forms the threshold itself (no
+  // exact launch)
+  const bool fused = sp.n_chunks <= kFusedMaxChunks;
   hipError_t e = launch_select(c, sp, q, q_dt, batch, q_heads, kv_heads, index, codebook, capacity, seq_lens, k,
-                               nullptr, nullptr, nullptr, ws + plan.ws_select, stream, ev, &prep);
+                               nullptr, nullptr, nullptr, ws + plan.ws_select, stream, ev, &prep, fused);
   if (e != hipSuccess) return e;
   if (capacity <= 0)
     hipLaunchKernelGGL(query_prep_kernel, dim3(rows), dim3(kQueryPrepThreads), 0, stream, dc.pi, dc.s, c.d, c.m, q,
@@ -4522,7 +4644,11 @@ hipError_t launch_sparse(const Consts& c, const DevConsts& dc, const SparsePlan&
   s.scores = reinterpret_cast<const int32_t*>(ws + plan.ws_select + sp.ws_scores);
   s.params = reinterpret_cast<const SelectParams*>(ws + plan.ws_select + sp.ws_params);
   s.chunk_off = reinterpret_cast<const int32_t*>(ws + plan.ws_select + sp.ws_chunk_off);
+  s.cand_all = reinterpret_cast<const uint2*>(ws + plan.ws_select + sp.ws_cand);
+  s.chunk_cand = reinterpret_cast<const int32_t*>(ws + plan.ws_select + sp.ws_chunk_cand);
+  s.chunk_above = reinterpret_cast<const int32_t*>(ws + plan.ws_select + sp.ws_chunk_above);
   s.k = k;
+  s.fused = fused ? 1 : 0;
   const dim3 grid((unsigned)n_chunks, kv_heads, batch);
   // query rows held in LDS sized for the group (a smaller footprint keeps more workgroups per CU)
   const int G = q_heads / kv_heads;
