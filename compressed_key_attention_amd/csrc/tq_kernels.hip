@@ -3899,15 +3899,13 @@ struct SparseArgs {
   const int32_t* scores;    // [units][capacity] selection scores
   const SelectParams* params;
   const int32_t* chunk_off;
-  // fused threshold (no exact launch): the filter launch's candidates and per-chunk counts
+  // the threshold is formed by the attention (no exact launch): the filter launch's candidates
+  // and per-chunk counts
   const uint2* cand_all;
   const int32_t* chunk_cand;
   const int32_t* chunk_above;
   int k;
-  int fused;
 };
-
-constexpr int kFusedMaxChunks = 1024;    // chunks per unit for which the attention forms the threshold
 
 // The unit's selection predicate ((key & mask) >= prefix) and the output offset of chunk c,
 // formed by the attention workgroup itself from the filter launch's candidates - the exact
@@ -3915,11 +3913,12 @@ constexpr int kFusedMaxChunks = 1024;    // chunks per unit for which the attent
 // radix passes over the candidates (the tokens in the bin of the k-th score) on the 64-bit key
 // until exactly the tokens still needed match, then the tokens above the bin and the chosen
 // candidates in the chunks before c.  Called by all kSmallThreads threads; the results are
-// valid in every thread on return.
+// valid in every thread on return.  Needs n_chunks ints of dynamic LDS (the exclusive prefix of
+// the chunks' candidate counts).
 __device__ void sparse_unit_threshold(const SparseArgs& S, int64_t unit, int c, int64_t n, int64_t kk,
                                       uint64_t* prefix_out, uint64_t* mask_out, int* base_out) {
   constexpr int NT = kSmallThreads;
-  __shared__ int cpre[kFusedMaxChunks];
+  extern __shared__ int cpre[];
   __shared__ int hist[256];
   __shared__ int wsum2[NT / 64];
   __shared__ uint32_t s_digit, s_rem, s_cnt;
@@ -4019,13 +4018,7 @@ __device__ __forceinline__ void sparse_chunk_list(const SparseArgs& S, int64_t u
                                                   int64_t kk, uint16_t* list, int* wsum, int* s_nsel) {
   uint64_t prefix = 0, mask = 0;
   int base = 0;
-  if (S.fused) {
-    sparse_unit_threshold(S, unit, c, n, kk, &prefix, &mask, &base);
-  } else if (kk > 0 && (int64_t)c * kSelChunk < n) {
-    prefix = S.params[unit].prefix;
-    mask = S.params[unit].mask;
-    base = S.chunk_off[unit * S.a.n_chunks + c];
-  }
+  sparse_unit_threshold(S, unit, c, n, kk, &prefix, &mask, &base);
   constexpr int kPer = kSelChunk / kSmallThreads;
   const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)c * kSelChunk;
@@ -4563,18 +4556,23 @@ SparsePlan plan_sparse(const Consts& c, int batch, int q_heads, int kv_heads, in
 }
 
 template <int D, int MG>
-static void launch_sparse_d(const SparseArgs& s, int kb, int vb, bool polar, dim3 grid, hipStream_t st) {
+static void launch_sparse_d(const SparseArgs& s, int kb, int vb, bool polar, dim3 grid, size_t dyn, hipStream_t st) {
   if (polar) {
-    if (vb == 1) hipLaunchKernelGGL((sparse_attend_kernel<D, 4, 1, MG, true>), grid, dim3(kSmallThreads), 0, st, s);
-    else if (vb == 2) hipLaunchKernelGGL((sparse_attend_kernel<D, 4, 2, MG, true>), grid, dim3(kSmallThreads), 0, st, s);
-    else if (vb == 3) hipLaunchKernelGGL((sparse_attend_kernel<D, 4, 3, MG, true>), grid, dim3(kSmallThreads), 0, st, s);
-    else hipLaunchKernelGGL((sparse_attend_kernel<D, 4, 4, MG, true>), grid, dim3(kSmallThreads), 0, st, s);
+#define TQ_SPP(BV_)                                                                                      \
+  if (vb == BV_) {                                                                                       \
+    allow_lds(sparse_attend_kernel<D, 4, BV_, MG, true>, dyn);                                           \
+    hipLaunchKernelGGL((sparse_attend_kernel<D, 4, BV_, MG, true>), grid, dim3(kSmallThreads), dyn, st, s); \
+    return;                                                                                              \
+  }
+    TQ_SPP(1) TQ_SPP(2) TQ_SPP(3) TQ_SPP(4)
+#undef TQ_SPP
     return;
   }
-#define TQ_SP(BK_, BV_)                                                                               \
-  if (kb == BK_ && vb == BV_) {                                                                       \
-    hipLaunchKernelGGL((sparse_attend_kernel<D, BK_, BV_, MG>), grid, dim3(kSmallThreads), 0, st, s); \
-    return;                                                                                           \
+#define TQ_SP(BK_, BV_)                                                                                 \
+  if (kb == BK_ && vb == BV_) {                                                                         \
+    allow_lds(sparse_attend_kernel<D, BK_, BV_, MG>, dyn);                                              \
+    hipLaunchKernelGGL((sparse_attend_kernel<D, BK_, BV_, MG>), grid, dim3(kSmallThreads), dyn, st, s); \
+    return;                                                                                             \
   }
   TQ_SP(1, 1) TQ_SP(1, 2) TQ_SP(1, 3) TQ_SP(1, 4) TQ_SP(2, 1) TQ_SP(3, 1) TQ_SP(4, 1)
   TQ_SP(2, 2) TQ_SP(2, 3) TQ_SP(2, 4) TQ_SP(3, 2) TQ_SP(3, 3) TQ_SP(3, 4)
@@ -4597,11 +4595,9 @@ hipError_t launch_sparse(const Consts& c, const DevConsts& dc, const SparsePlan&
   const int rows = batch * q_heads;
   // the query prep rides in the selection's table launch (which runs when capacity > 0)
   const QueryPrep prep{dc.pi, dc.s, c.m, rows, qx, qs};
-  // with at most kFusedMaxChunks chunks per unit the attention forms the threshold itself (no
-  // exact launch)
-  const bool fused = sp.n_chunks <= kFusedMaxChunks;
+  // the attention forms the selection threshold itself (no exact launch)
   hipError_t e = launch_select(c, sp, q, q_dt, batch, q_heads, kv_heads, index, codebook, capacity, seq_lens, k,
-                               nullptr, nullptr, nullptr, ws + plan.ws_select, stream, ev, &prep, fused);
+                               nullptr, nullptr, nullptr, ws + plan.ws_select, stream, ev, &prep, true);
   if (e != hipSuccess) return e;
   if (capacity <= 0)
     hipLaunchKernelGGL(query_prep_kernel, dim3(rows), dim3(kQueryPrepThreads), 0, stream, dc.pi, dc.s, c.d, c.m, q,
@@ -4648,18 +4644,24 @@ hipError_t launch_sparse(const Consts& c, const DevConsts& dc, const SparsePlan&
   s.chunk_cand = reinterpret_cast<const int32_t*>(ws + plan.ws_select + sp.ws_chunk_cand);
   s.chunk_above = reinterpret_cast<const int32_t*>(ws + plan.ws_select + sp.ws_chunk_above);
   s.k = k;
-  s.fused = fused ? 1 : 0;
   const dim3 grid((unsigned)n_chunks, kv_heads, batch);
   // query rows held in LDS sized for the group (a smaller footprint keeps more workgroups per CU)
   const int G = q_heads / kv_heads;
   const bool lean = G == 1 && c.m == 0 && c.kb == 4 && c.vb == 4 && !c.polar && (c.d == 128 || c.d == 64);
-  if (c.d != 64 && c.d != 128) hipLaunchKernelGGL(sparse_attend_generic_kernel, grid, dim3(kSmallThreads), 0, stream, s);
-  else if (lean && c.d == 128) hipLaunchKernelGGL(sparse_attend_lean_kernel<128>, grid, dim3(kSmallThreads), 0, stream, s);
-  else if (lean) hipLaunchKernelGGL(sparse_attend_lean_kernel<64>, grid, dim3(kSmallThreads), 0, stream, s);
-  else if (c.d == 128 && G <= 4) launch_sparse_d<128, 4>(s, c.kb, c.vb, c.polar != 0, grid, stream);
-  else if (c.d == 128) launch_sparse_d<128, kSmallMaxG>(s, c.kb, c.vb, c.polar != 0, grid, stream);
-  else if (G <= 4) launch_sparse_d<64, 4>(s, c.kb, c.vb, c.polar != 0, grid, stream);
-  else launch_sparse_d<64, kSmallMaxG>(s, c.kb, c.vb, c.polar != 0, grid, stream);
+  const size_t dyn = (size_t)n_chunks * 4;     // the threshold's prefix of candidate counts
+  if (c.d != 64 && c.d != 128) {
+    allow_lds(sparse_attend_generic_kernel, dyn);
+    hipLaunchKernelGGL(sparse_attend_generic_kernel, grid, dim3(kSmallThreads), dyn, stream, s);
+  } else if (lean && c.d == 128) {
+    allow_lds(sparse_attend_lean_kernel<128>, dyn);
+    hipLaunchKernelGGL(sparse_attend_lean_kernel<128>, grid, dim3(kSmallThreads), dyn, stream, s);
+  } else if (lean) {
+    allow_lds(sparse_attend_lean_kernel<64>, dyn);
+    hipLaunchKernelGGL(sparse_attend_lean_kernel<64>, grid, dim3(kSmallThreads), dyn, stream, s);
+  } else if (c.d == 128 && G <= 4) launch_sparse_d<128, 4>(s, c.kb, c.vb, c.polar != 0, grid, dyn, stream);
+  else if (c.d == 128) launch_sparse_d<128, kSmallMaxG>(s, c.kb, c.vb, c.polar != 0, grid, dyn, stream);
+  else if (G <= 4) launch_sparse_d<64, 4>(s, c.kb, c.vb, c.polar != 0, grid, dyn, stream);
+  else launch_sparse_d<64, kSmallMaxG>(s, c.kb, c.vb, c.polar != 0, grid, dyn, stream);
   MergeArgs mg{};
   mg.pi_t = dc.pi_t;
   mg.part = part;
