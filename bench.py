@@ -295,8 +295,11 @@ def oracle_baseline(units, make_job, tokens_per_unit, total_units, unit_name, bu
     rate1 = done * tokens_per_unit / elapsed
     workers = max(1, min(max_workers, os.cpu_count() or 1))
     per_unit = elapsed / done
-    n_multi = min(len(units), workers * max(1, int(budget_s / per_unit / 2)))
-    jobs = [make_job(u) for u in units[:n_multi]]
+    # at least one unit per worker (units repeated when the workload has fewer)
+    n_multi = workers * max(1, int(budget_s / per_unit / 2))
+    if len(units) >= workers:
+        n_multi = min(len(units), n_multi)
+    jobs = [make_job(units[i % len(units)]) for i in range(n_multi)]
     with ProcessPoolExecutor(max_workers=workers, mp_context=multiprocessing.get_context("spawn")) as ex:
         list(ex.map(_warm_job, [jobs[0][1]] * workers))
         t0 = time.perf_counter()
@@ -308,7 +311,7 @@ def oracle_baseline(units, make_job, tokens_per_unit, total_units, unit_name, bu
             "host_cores": host,
             "core_cap": (f"at most {max_workers} worker processes: the CPU share of one GPU on the "
                          f"benchmark machines ({host} host cores visible)") if host > workers else None,
-            "sample": f"{n_multi} of {total_units} {unit_name} over {workers} worker processes "
+            "sample": f"{n_multi} (of {total_units}, repeated when fewer than the workers) {unit_name} over {workers} worker processes "
                       f"(numpy float64 oracle, BLAS 1 thread each), {wall:.1f} s wall",
             "single_thread": {"value": rate1, "cores": 1,
                               "sample": f"{done} {unit_name}, {elapsed:.1f} s"},
@@ -340,17 +343,22 @@ def scalar_baseline(units, run_unit, tokens_per_unit, total_units, unit_name, bu
     rate1 = done * tokens_per_unit / elapsed
     threads = max(1, min(max_threads, os.cpu_count() or 1))
     per_unit = elapsed / done
-    n_multi = min(len(units), threads * max(1, int(budget_s / per_unit / 2)))
+    # a batch of at least one unit per thread (the units repeated when the workload has fewer),
+    # sized to about half the single-thread budget of wall time
+    n_multi = threads * max(1, int(budget_s / per_unit / 2))
+    if len(units) >= threads:
+        n_multi = min(len(units), n_multi)
+    batch = [units[i % len(units)] for i in range(n_multi)]
     with ThreadPoolExecutor(max_workers=threads) as ex:
         t0 = time.perf_counter()
-        list(ex.map(run_unit, units[:n_multi]))
+        list(ex.map(run_unit, batch))
         wall = time.perf_counter() - t0
     host = os.cpu_count() or 1
     return {"value": n_multi * tokens_per_unit / wall, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "host_cores": host,
             "core_cap": (f"at most {max_threads} threads: the CPU share of one GPU on the benchmark "
                          f"machines ({host} host cores visible)") if host > threads else None,
-            "sample": f"{n_multi} of {total_units} {unit_name} over {threads} threads (scalar C oracle, "
+            "sample": f"{n_multi} (of {total_units}, repeated when fewer than the threads) {unit_name} over {threads} threads (scalar C oracle, "
                       f"oracle/tq_scalar.c at -O2, double accumulation), {wall:.1f} s wall",
             "single_thread": {"value": rate1, "cores": 1, "sample": f"{done} {unit_name}, {elapsed:.1f} s"},
             "cpu_model": cpu_model()}
