@@ -421,8 +421,8 @@ struct tq_handle {
 
 namespace {
 
-// Calls built for head_dim 64 and 128 only (every other supported head_dim has compress,
-// decode attention, the sign index, top-k selection, sparse attention and the bulk scan).
+// Calls built for head_dim 64 and 128 only (every other supported head_dim has every call but
+// the hot/cold step).
 bool dim_unsupported(const tq_handle* h, const char* what, tq_status* st) {
   if (h && h->c.d != 64 && h->c.d != 128) {
     *st = fail(TQ_ERR_UNSUPPORTED, "%s is built for head_dim 64 and 128 only (handle has %d)", what, h->c.d);
@@ -751,10 +751,6 @@ tq_status tq_compress_kv(const tq_handle* h, const void* k, const void* v, tq_dt
 tq_status tq_debug_quantize(const tq_handle* h, const float* z_k, const float* p,
                             const float* r_k, const float* rho, const float* z_v,
                             const float* r_v, int64_t n, void* records, hipStream_t stream) {
-  {
-    tq_status dst;
-    if (dim_unsupported(h, "the debug quantize entry", &dst)) return dst;
-  }
   {
     tq_status pst;
     if (polar_unsupported(h, "the debug quantize entry", &pst)) return pst;

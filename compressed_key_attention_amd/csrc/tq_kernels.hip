@@ -766,7 +766,11 @@ __global__ void debug_quantize_kernel(Consts c, const float* z_k, const float* p
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= n) return;
   uint8_t* rec = records + t * c.rec_bytes;
-  auto put_codes = [&](uint8_t* field, const float* z, const float* bounds, int bits) {
+  // a field of d codes: 3-bit codes in whole 32-code groups, then (d % 32 codes, head_dim 200)
+  // a plain bitstream; every other width a plain bitstream; zero bytes up to the field's size
+  auto put_codes = [&](uint8_t* field, const float* z, const float* bounds, int bits, int fbytes) {
+    int i0 = 0;
+    uint8_t* tail = field;
     if (bits == 3) {
       for (int gi = 0; gi < c.d / 32; ++gi) {
         uint32_t w[3] = {0u, 0u, 0u};
@@ -777,15 +781,19 @@ __global__ void debug_quantize_kernel(Consts c, const float* z_k, const float* p
         dst[1] = w[1];
         dst[2] = w[2];
       }
-    } else {
-      ByteWriter w{field, 0, 0};
-      for (int i = 0; i < c.d; ++i) w.put(quantize_code(z[i], bounds), bits);
+      i0 = c.d / 32 * 32;
+      tail = field + 12 * (c.d / 32);
     }
+    ByteWriter w{tail, 0, 0};
+    for (int i = i0; i < c.d; ++i) w.put(quantize_code(z[i], bounds), bits);
+    uint8_t* e = w.dst;
+    if (w.n > 0) *e++ = (uint8_t)w.acc;
+    while (e < field + fbytes) *e++ = 0;
   };
-  put_codes(rec, z_k + t * c.d, c.key_bounds, c.kb);
+  put_codes(rec, z_k + t * c.d, c.key_bounds, c.kb, c.kbytes);
   ByteWriter ws{rec + c.kbytes, 0, 0};
   for (int j = 0; j < c.m; ++j) ws.put(p[t * c.m + j] >= 0.0f ? 1u : 0u, 1);
-  put_codes(rec + c.kbytes + c.sbytes, z_v + t * c.d, c.val_bounds, c.vb);
+  put_codes(rec + c.kbytes + c.sbytes, z_v + t * c.d, c.val_bounds, c.vb, c.vbytes);
   float* nrm = reinterpret_cast<float*>(rec + c.norm_off);
   nrm[0] = r_k[t];
   nrm[1] = rho[t];

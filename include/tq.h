@@ -106,10 +106,8 @@ typedef enum tq_key_codec { TQ_KEY_SCALAR = 0, TQ_KEY_POLAR = 1 } tq_key_codec;
 
 typedef struct tq_config {
   int32_t head_dim;       /* d: 64 or 128 for every call; any other multiple of 8 up
-                             to 256 (scalar keys) for tq_compress_kv, tq_score_scan,
-                             decode attention, the sign index, tq_select_topk and
-                             tq_sparse_attention (direct kernels that read d at run
-                             time); tq_debug_quantize and the hot/cold step return
+                             to 256 (scalar keys) for every call but the hot/cold step
+                             (direct kernels that read d at run time), which returns
                              TQ_ERR_UNSUPPORTED for such a handle                      */
   int32_t key_bits;       /* b_k: bits per rotated key coordinate, 1..4; polar: bits
                              per level-1 angle, 2 or 4                                 */

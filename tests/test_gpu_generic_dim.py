@@ -1,5 +1,5 @@
-"""GPU parity of decode attention, the sign index, top-k selection and sparse attention at head
-dims other than 64 and 128 (any multiple of 8 up to 256: the TurboQuant page's vector-search
+"""GPU parity of tq_debug_quantize, decode attention, the sign index, top-k selection and sparse
+attention at head dims other than 64 and 128 (any multiple of 8 up to 256: the TurboQuant page's vector-search
 section uses d = 200), through the direct kernels that read d at run time, against the oracle
 with the rules of test_gpu_parity: outputs, lse and every logit within 1e-4 + 1e-3 |oracle|;
 sign index bit-exact at the GPU's channel mean; selected sets and scores bit-exact."""
@@ -17,6 +17,13 @@ def _wl(d, kb, m, vb, hq, hkv, tokens, batch, hot=0):
     base = W.small(W.WORKLOADS["llama8b_decode_32k"], tokens=tokens, batch=batch, hot_tokens=hot)
     return W.Workload(**{**base.__dict__, "head_dim": d, "key_bits": kb, "qjl_dim": m, "value_bits": vb,
                          "q_heads": hq, "kv_heads": hkv})
+
+
+@pytest.mark.parametrize("cfg", [(200, 3, 192, 2), (200, 2, 96, 3), (40, 3, 32, 4), (200, 1, 64, 1), (104, 4, 0, 3)])
+def test_debug_quantize_generic_head_dim(cfg):
+    """Records from given rotated coordinates, byte for byte: the partial 3-bit group of d = 200
+    and 40, the zero pad of fields that are not whole words (d = 200 at 2 bits: 50 + 2 bytes)."""
+    GP.test_debug_quantize_is_bit_exact(cfg)
 
 
 @pytest.mark.parametrize("d,kb,m,vb,hq,hkv,lens,hot", [

@@ -82,15 +82,9 @@ def test_recall_from_gpu_scan_matches_oracle():
 
 
 def test_head_dim_200_rejected_where_not_built():
-    """tq_debug_quantize and the hot/cold step are built for head_dim 64 and 128 only."""
+    """The hot/cold step is built for head_dim 64 and 128 only."""
     tq = GP._tq()
     h = GP._handle(_wl(tokens=16))
-    z = torch.zeros((4, 200), device="cuda")
-    with pytest.raises(tq.TqError) as e:
-        h.debug_quantize(z, torch.zeros((4, 192), device="cuda"), torch.ones(4, device="cuda"),
-                         torch.zeros(4, device="cuda"), z, torch.ones(4, device="cuda"),
-                         torch.zeros((4, h.record_bytes), dtype=torch.uint8, device="cuda"))
-    assert e.value.status == tq.TQ_ERR_UNSUPPORTED
     with pytest.raises(tq.TqError) as e:
         tq.monarch_workspace_size(h, 1, 1, 1, 8, 8)
     assert e.value.status == tq.TQ_ERR_UNSUPPORTED
