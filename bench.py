@@ -657,9 +657,9 @@ def run_bulk_scan(args, tq, W, ev):
     kname = "scan_mfma_kernel" if mfma else "scan_mfma16_kernel"
     extra = None
     if mfma:
-        # int8 matrix-core work the kernel executes: 8 (6 without the sketch) 16x16x64 MFMAs per
-        # 16 tokens x 4 queries
-        n_mfma = (8 if w.qjl_dim else 6) * (B * H * T / 16) * (nq / 4)
+        # int8 matrix-core work the kernel executes: 22 (16 without the sketch) 16x16x64 MFMAs
+        # per tile of 16 tokens x 16 queries
+        n_mfma = (22 if w.qjl_dim else 16) * (B * H * T / 16) * (nq / 16)
         tops = n_mfma * 2 * 16 * 16 * 64 / (scan_ms * 1e-3) / 1e12
         extra = {"mfma_int8_executed_tops": tops, "mfma_int8_peak_tops": 5000.0,
                  "mfma_int8_frac": tops / 5000.0}

@@ -160,7 +160,7 @@ hipError_t launch_sparse(const Consts& c, const DevConsts& dc, const SparsePlan&
 
 struct ScanPlan {
   bool mfma;        // matrix-core scan (head_dim 128, 2/3-bit keys, m in {0, 128})
-  int n_groups;     // groups of 4 queries per (sequence, KV head)
+  int n_groups;     // groups of 4 queries per (sequence, KV head) (matrix-core path: whole 16-query tiles)
   int kp;           // generic path: d + m rounded up to a multiple of 32
   size_t ws_q, ws_ql, ws_qscale, ws_total;
 };

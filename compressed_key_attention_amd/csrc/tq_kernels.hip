@@ -20,6 +20,7 @@
 #include <cfloat>
 #include <cmath>
 #include <mutex>
+#include <type_traits>
 
 #include "tq_internal.h"
 
@@ -1630,12 +1631,18 @@ __device__ __forceinline__ uint32_t bf16_pair(float x) {      // hi | lo << 16
 // (row o, slice) holds 16 coordinates of row o of Pi and of S Pi, loaded up front), then the lanes' query
 // operands: bop[group][lane][32 words] = code words (16), QJL words (8), and the scales of lane
 // L's head L / 16, {1 / (F_q F_k), 2 / F_s, -sum / F_s} (3), pad.
-// SCAN: the same for a group of 4 consecutive bulk-scan queries of one (sequence, KV head)
-// (q_heads = queries per unit, kv_heads = groups per unit; rows past the last query are
-// zero), against three-limb key levels (fk = their scale F_k): bop[group][lane][36 words] =
-// 6 code chunks (key limb plane 2 - j / 2, selectors 4 (j % 2) .. + 3), 2 QJL chunks, and the
-// same scales for lane L's query L / 16.
-constexpr int kScanLaneWords = 36;   // bulk-scan query operand words per lane (9 chunks of 16 B)
+// SCAN: the B operands of the bulk scan's 16-token x 16-query tiles, for a group of 4
+// consecutive queries of one (sequence, KV head) (q_heads = queries per unit, kv_heads = groups
+// per unit, a multiple of 4; rows past the last query are zero).  Group g supplies columns
+// 4 (g % 4) .. + 3 of query tile g / 4, stored chunk-major: bop[tile][chunk][lane][4 words],
+// lane L = (query column L % 16, K slice kg = L / 16):
+//   chunks 0..5: limb 2 - c / 2 of the fixed-point q_x, K chunk c % 2 (word w, byte k <->
+//     coordinate 32 kg + sel_coord(4 (c % 2) + w, k), as the token side's selectors);
+//   chunks 6..11: limb 2 - (c - 6) / 2 of the fixed-point q_s, bit chunk (c - 6) % 2 (word w,
+//     byte k <-> sketch coordinate 32 kg + 8 k + 4 ((c - 6) % 2) + w);
+//   chunk 12: {1 / (F_q F_k), 2 / F_s, -sum / F_s, 0} of the column's query (fk = F_k, the
+//     three-limb key level scale).
+constexpr int kScanChunks = 13;      // bulk-scan operand chunks (16 B per lane) per query tile
 
 constexpr int kPrepThreads = 1024;
 // POLAR (decode only): the key chunks are fp16 query operands instead of int8 limbs: chunks
@@ -1759,6 +1766,44 @@ __global__ __launch_bounds__(kPrepThreads) void mfma_prep_kernel(const float* __
     }
     __syncthreads();
   }
+  if constexpr (SCAN) {
+    // 13 chunks x 16 lanes (this group's 4 columns x 4 K slices), one 16-byte word each
+    const int t = threadIdx.x;
+    if (t >= kScanChunks * 16) return;
+    const int c = t >> 4, h = (t >> 2) & 3, kg = t & 3;
+    const int L = 4 * (group & 3) + h + 16 * kg;   // kv_heads % 4 == 0: group % 4 = column block
+    u32x4 words = u32x4{0u, 0u, 0u, 0u};
+    if (c < 6) {
+      const int bi = c >> 1, hh = c & 1;          // byte bi of a packed word = limb 2 - bi
+      const uint32_t* kl = klimb + h * LS + 33 * kg;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) word |= ((kl[sel_coord<BK>(4 * hh + w, k)] >> (8 * bi)) & 0xFFu) << (8 * k);
+        words[w] = word;
+      }
+    } else if (c < 12) {
+      if (QJL) {
+        const int bi = (c - 6) >> 1, jj = (c - 6) & 1;
+        const uint32_t* jl = jlimb + h * LS + 33 * kg;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) word |= ((jl[8 * k + 4 * jj + w] >> (8 * bi)) & 0xFFu) << (8 * k);
+          words[w] = word;
+        }
+      }
+    } else {
+      const float bk = 1.0f / (s_fq[h] * fk);
+      const float bq = QJL ? 2.0f / s_fs[h] : 0.0f;
+      const float oq = QJL ? -(float)s_ssum[h] / s_fs[h] : 0.0f;
+      words = u32x4{__float_as_uint(bk), __float_as_uint(bq), __float_as_uint(oq), 0u};
+    }
+    reinterpret_cast<u32x4*>(bop)[((int64_t)(group >> 2) * kScanChunks + c) * 64 + L] = words;
+    return;
+  }
   // operand words (A of the score products): lane L = (row n = L % 16, K slice kg = L / 16),
   // head n / 4, part n % 4.
   //  code word (j, w): byte k <-> coordinate 32 kg + sel_coord(2j + (w & 1), k); w < 2: high
@@ -1768,12 +1813,12 @@ __global__ __launch_bounds__(kPrepThreads) void mfma_prep_kernel(const float* __
   //    2 - p of the sketch (weight 2^(8 (2 - p))); part 3: zero.
   // one 16-byte chunk per wave (no divergence): waves 0 .. NC - 1 the code chunks, the next two
   // the QJL chunks, the next one the scales, each for lane L = its own lane
-  constexpr int NC = SCAN ? 6 : POLAR ? 8 : 4;
+  constexpr int NC = POLAR ? 8 : 4;
   const int L = threadIdx.x & 63, role = threadIdx.x >> 6;
   if (role > NC + 2) return;
   const int n = L & 15, kg = L >> 4, hB = n >> 2, part = n & 3;
   u32x4* gdst = reinterpret_cast<u32x4*>(
-      bop + ((int64_t)group * 64 + L) * (SCAN ? kScanLaneWords : POLAR ? kPolarLaneWords : 32));
+      bop + ((int64_t)group * 64 + L) * (POLAR ? kPolarLaneWords : 32));
   if (POLAR && role < NC) {
     const int j = role, chain = j >> 2, jj = j & 3;
     const float sc = ldexpf(1.0f, -(int)s_pe[hB]);      // exact: a power of two
@@ -1800,21 +1845,13 @@ __global__ __launch_bounds__(kPrepThreads) void mfma_prep_kernel(const float* __
     u32x4 words;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      int bi;
-      if (SCAN) {
-        // key part n of weight 2^(32 - 8n) pairs key limb plane p (weight 2^(8p)) with query
-        // limb 4 - n - p (weight 2^(8 (4 - n - p))) when that is 0, 1 or 2
-        const int plane = 2 - (j >> 1), ql = 4 - part - plane;
-        bi = ql == 2 ? 0 : ql == 1 ? 1 : ql == 0 ? 2 : 3;
-      } else {
-        // high level limb slots (w < 2): part p takes query limb 2 - p; low slots: limb 3 - p
-        const bool hi_slot = w < 2;
-        bi = part == 0 ? (hi_slot ? 0 : 3) : part == 1 ? (hi_slot ? 1 : 0) : part == 2 ? (hi_slot ? 2 : 1) : 3;
-      }
+      // high level limb slots (w < 2): part p takes query limb 2 - p; low slots: limb 3 - p
+      const bool hi_slot = w < 2;
+      const int bi = part == 0 ? (hi_slot ? 0 : 3) : part == 1 ? (hi_slot ? 1 : 0) : part == 2 ? (hi_slot ? 2 : 1) : 3;
       uint32_t word = 0;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const int coord = SCAN ? sel_coord<BK>(4 * (j & 1) + w, kk) : sel_coord<BK>(2 * j + (w & 1), kk);
+        const int coord = sel_coord<BK>(2 * j + (w & 1), kk);
         word |= ((kl[coord] >> (8 * bi)) & 0xFFu) << (8 * kk);
       }
       words[w] = word;
@@ -4705,14 +4742,15 @@ ScanPlan plan_scan(const Consts& c, int batch, int heads, int n_queries) {
   ScanPlan p;
   const size_t units = (size_t)std::max(batch, 1) * heads;
   p.mfma = scan_mfma_path(c);
-  p.n_groups = (std::max(n_queries, 1) + 3) / 4;
+  // matrix-core path: groups of 4 queries, whole 16-query tiles of them
+  p.n_groups = (std::max(n_queries, 1) + 15) / 16 * 4;
   p.ws_q = 0;
   // generic path: fp16 hi and lo query rows [units][nq][kp], then the row scales
   p.kp = (c.d + c.m + 31) / 32 * 32;
   const size_t rows = units * (size_t)std::max(n_queries, 1);
   p.ws_ql = align256(rows * p.kp * 2);
   p.ws_qscale = p.ws_ql + align256(rows * p.kp * 2);
-  p.ws_total = p.mfma ? align256(units * p.n_groups * 64 * kScanLaneWords * 4)   // query operands
+  p.ws_total = p.mfma ? align256(units * (p.n_groups / 4) * kScanChunks * 64 * 16)   // query operands
                       : p.ws_qscale + align256(rows * 4);
   return p;
 }
@@ -5017,54 +5055,64 @@ __global__ __launch_bounds__(256, 2) void scan_mfma16_kernel(Scan16Args A) {
 
 // -----------------------------------------------------------------------------------------
 // Matrix-core bulk scan (head_dim 128, 2- or 3-bit keys, m in {0, 128}): the decode's exact
-// int32 estimator with the roles of the operands swapped.  A = query operands (rows = 4
-// queries x 4 limb parts, from mfma_prep_kernel in SCAN mode), B = token operands (columns =
-// 16 tokens: key level limbs by v_perm_b32, QJL bits as 0/1 bytes), so lane (K slice kg,
-// column n) ends with all parts of query kg for token n and combines them in registers.
-// Unscaled estimates carry the key norm's full size, so the levels take three int8 limbs
-// here (24 bits, F_k = 127 * 65536 / max |level|): part n sums the limb products of weight
-// 2^(32 - 8n), n = 0..3, and
+// int32 estimator over tiles of 16 tokens x 16 queries.  A = token operands (rows = 16 tokens:
+// key level limbs by v_perm_b32 from one table per limb plane, QJL bits as 0/1 bytes), B = query
+// operands (columns = 16 queries: the int8 limbs of the fixed-point q_x and q_s from
+// mfma_prep_kernel in SCAN mode), one int32 accumulator per weight class.  Unscaled estimates
+// carry the key norm's full size, so the levels take three int8 limbs here (24 bits,
+// F_k = 127 * 65536 / max |level|).  With level limb b and query limb a the key products of
+// weight 2^(8 (a + b)) go to class e = 4 - a - b; classes 0..3 are kept (1, 2, 3 and 2 limb
+// pairs over two 64-wide K chunks: 16 MFMAs), class 4 (2^0) is dropped; the sketch takes its
+// three query limbs against the bits (6 MFMAs).  Lane (query column n, K slice kg) ends with
+// tokens 4 kg .. 4 kg + 3 of the tile for query n and writes them with one 16-byte store:
 //   s = (r_k/sqrt(d)) ((256 C0 + C1) 2^24 + (256 C2 + C3) 2^8) / (F_q F_k)
 //     + coef rho ((2^16 Cq0 + 2^8 Cq1 + Cq2) 2 / F_s - sum / F_s).
-// A workgroup holds the operands of 32 queries in LDS (9 x 16 B per lane and group) and its
-// four waves walk 64-token blocks of a 2048-token range: each wave keeps the 64 tokens'
-// operands in registers and sweeps the 8 query groups over them (8 MFMAs per 16 x 4 tile).
+// (|C0| < 2^21, |C1| < 2^22, |C2| < 2^23, |C3| < 2^22 and the sketch classes fit the int32
+// pair sums.)  A workgroup holds 4 query tiles (64 queries, 13 x 16 B per lane and tile) in
+// LDS; each wave walks 32-token steps of a 1024-token range, building two token tiles'
+// operands once per step and sweeping the query tiles over them.
 // -----------------------------------------------------------------------------------------
-constexpr int kScanQB = 32;                 // queries per workgroup
-constexpr int kScanGroups = kScanQB / 4;
-constexpr int kScanWaveTok = 64;            // tokens per wave step (4 tiles of 16)
+constexpr int kScanQT = 4;                  // 16-query tiles per workgroup
+constexpr int kScanQB = 16 * kScanQT;       // queries per workgroup
+constexpr int kScanTT = 2;                  // 16-token tiles per wave step
 constexpr int kScanWaves = 4;               // waves per workgroup
 constexpr int kScanThreads = 64 * kScanWaves;
-constexpr int kScanBlockTok = 2048;         // tokens per workgroup
+constexpr int kScanBlockTok = 1024;         // tokens per workgroup
 
 struct ScanMfmaArgs {
-  const uint32_t* qop;     // [unit][group][lane][32 words]
+  const u32x4* qop;        // [unit][query tile][chunk][lane]
   const uint8_t* records;
   float* scores;
   int64_t capacity, n_tokens;
-  int rec_bytes, kbytes, norm_off, n_queries, n_groups;
+  int rec_bytes, kbytes, norm_off, n_queries, n_qtiles, vec_store;
   float inv_sqrt_d, qjl_coef, key_fix3;
   float key_levels[kMaxLevels];
 };
 
-constexpr int kScanChunks = kScanLaneWords / 4;
-constexpr size_t kScanLds = (size_t)kScanGroups * kScanChunks * 64 * 16;
+// after the query operands: each wave's 16-query x 32-token score staging (rows padded to 36
+// floats, 16-byte aligned)
+constexpr int kScanStgRow = 36;
+constexpr size_t kScanLds = (size_t)kScanQT * kScanChunks * 64 * 16 + (size_t)kScanWaves * 16 * kScanStgRow * 4;
+
+// Orders one wave's LDS accesses across its lanes (a wave's LDS instructions execute in order;
+// this keeps the compiler from moving them across each other).
+__device__ __forceinline__ void wave_lds_order() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 template <int BK, bool QJL>
 __global__ __launch_bounds__(kScanThreads, 2) void scan_mfma_kernel(ScanMfmaArgs A) {
-  constexpr int NT = kScanWaveTok / 16;
-  extern __shared__ u32x4 qop_lds[];                   // [group][16-byte chunk][lane]
-  auto qop = [&](int g, int c, int l) -> u32x4& { return qop_lds[(g * kScanChunks + c) * 64 + l]; };
+  constexpr int TT = kScanTT;
+  extern __shared__ u32x4 qop_lds[];                   // [query tile][chunk][lane]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int unit = blockIdx.z, qb = blockIdx.y;
   const int n = lane & 15, kg = lane >> 4;
-  const int g_end = min(kScanGroups, A.n_groups - qb * kScanGroups);   // groups present
+  const int qt_end = min(kScanQT, A.n_qtiles - qb * kScanQT);   // query tiles present
   {
-    const u32x4* src = reinterpret_cast<const u32x4*>(A.qop + ((int64_t)unit * A.n_groups + qb * kScanGroups) * 64 * kScanLaneWords);
-    for (int e = threadIdx.x; e < kScanGroups * kScanChunks * 64; e += blockDim.x) {
-      const int g = e / (kScanChunks * 64), c = (e / 64) % kScanChunks, l = e % 64;
-      qop(g, c, l) = g < g_end ? src[((int64_t)g * 64 + l) * kScanChunks + c] : u32x4{0u, 0u, 0u, 0u};
-    }
+    const u32x4* src = A.qop + ((int64_t)unit * A.n_qtiles + qb * kScanQT) * kScanChunks * 64;
+    for (int e = threadIdx.x; e < qt_end * kScanChunks * 64; e += kScanThreads) qop_lds[e] = src[e];
   }
   // key levels as three int8 limbs: gamma ~= (65536 l2 + 256 l1 + l0) / F_k; byte c of each
   // table word = code c, one table per limb plane
@@ -5081,17 +5129,18 @@ __global__ __launch_bounds__(kScanThreads, 2) void scan_mfma_kernel(ScanMfmaArgs
   __syncthreads();
 
   const uint8_t* recs = A.records + (int64_t)unit * A.capacity * A.rec_bytes;
-  float* out = A.scores + ((int64_t)unit * A.n_queries + (int64_t)qb * kScanQB) * A.n_tokens;
   const int64_t tlast = A.n_tokens - 1;
   const size_t kofs = (size_t)kg * 4 * BK, sofs = (size_t)A.kbytes + 4 * kg, nofs = (size_t)A.norm_off;
+  // lane (row n, K slice kg) of token tile tt reads token 16 tt + n's key words of slice kg,
+  // its sketch word and its two norms
   struct Raw {
-    uint32_t kw[NT][BK];
-    uint32_t sw[NT];
-    float nk[NT], nr[NT];
+    uint32_t kw[TT][BK];
+    uint32_t sw[TT];
+    float2 nrm[TT];
   };
   auto fetch = [&](int64_t t0, Raw& r) {
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) {
+    for (int tt = 0; tt < TT; ++tt) {
       const uint8_t* rec = recs + (size_t)min(t0 + 16 * tt + n, tlast) * A.rec_bytes;
       if constexpr (BK == 3) {
         typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
@@ -5106,24 +5155,20 @@ __global__ __launch_bounds__(kScanThreads, 2) void scan_mfma_kernel(ScanMfmaArgs
       }
       r.sw[tt] = QJL ? *reinterpret_cast<const uint32_t*>(rec + sofs) : 0u;
       const float* nrm = reinterpret_cast<const float*>(rec + nofs);
-      r.nk[tt] = nrm[0];
-      r.nr[tt] = nrm[1];
+      r.nrm[tt] = make_float2(nrm[0], nrm[1]);
     }
   };
   const int64_t tb0 = (int64_t)blockIdx.x * kScanBlockTok;
   const int64_t tb1 = min(A.n_tokens, tb0 + kScanBlockTok);
-  int64_t t0 = tb0 + (int64_t)wave * kScanWaveTok;
-  Raw cur;
-  if (t0 < tb1) fetch(t0, cur);
-  for (; t0 < tb1; t0 += kScanWaves * kScanWaveTok) {
-    Raw nxt;
-    const int64_t t1 = t0 + kScanWaves * kScanWaveTok;
-    if (t1 < tb1) fetch(t1, nxt);
-    // token operands of the 4 tiles
-    i32x4 Bk[NT][6], Bs[NT][2];
-    float ak[NT], aq[NT];
+  constexpr int kStep = 16 * TT;
+  // one step: the token tiles' operands from the raw words, then every query tile against them
+  auto step = [&](int64_t t0, const Raw& cur, auto full_tag) {
+    // token operands of the tiles: Tk[tt][2 pb + hh] = level limb plane 2 - pb, K chunk hh
+    i32x4 Tk[TT][6], Ts[TT][2];
+    // scales of the lane's output tokens 16 tt + 4 kg + r, fetched by lane (4 kg + r, any slice)
+    float ak[TT][4], aq[TT][4];
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) {
+    for (int tt = 0; tt < TT; ++tt) {
       uint32_t sel[8];
       if constexpr (BK == 3) {
         const uint32_t top = group3_top(cur.kw[tt][0], cur.kw[tt][1], cur.kw[tt][2]);
@@ -5143,56 +5188,143 @@ __global__ __launch_bounds__(kScanThreads, 2) void scan_mfma_kernel(ScanMfmaArgs
         const int plane = 2 - (j >> 1), hh = j & 1;
 #pragma unroll
         for (int w = 0; w < 4; ++w)
-          Bk[tt][j][w] = (int)__builtin_amdgcn_perm(tp[plane][1], tp[plane][0], sel[4 * hh + w]);
+          Tk[tt][j][w] = (int)__builtin_amdgcn_perm(tp[plane][1], tp[plane][0], sel[4 * hh + w]);
       }
       if (QJL)
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-          for (int w = 0; w < 4; ++w) Bs[tt][jj][w] = (int)((cur.sw[tt] >> (4 * jj + w)) & 0x01010101u);
-      ak[tt] = cur.nk[tt] * A.inv_sqrt_d;
-      aq[tt] = A.qjl_coef * cur.nr[tt];
-    }
-    for (int g = 0; g < g_end; ++g) {
-      i32x4 Ak[6], Aq[2];
+          for (int w = 0; w < 4; ++w) Ts[tt][jj][w] = (int)((cur.sw[tt] >> (4 * jj + w)) & 0x01010101u);
 #pragma unroll
-      for (int j = 0; j < 6; ++j) Ak[j] = __builtin_bit_cast(i32x4, qop(g, j, lane));
-      if (QJL)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) Aq[j] = __builtin_bit_cast(i32x4, qop(g, 6 + j, lane));
-      const u32x4 scw = qop(g, 8, lane);
-      const float bk = __uint_as_float(scw[0]), bq = __uint_as_float(scw[1]), oq = __uint_as_float(scw[2]);
-      const bool qok = qb * kScanQB + 4 * g + kg < A.n_queries;
-      float* o = out + (int64_t)(4 * g + kg) * A.n_tokens + t0 + n;
-      const float sk_hi = 16777216.0f * bk, sk_lo = 256.0f * bk;
-      // the tiles' MFMA chains interleaved (independent accumulators), then the epilogues
-      i32x4 C0[NT], Cq[NT];
-#pragma unroll
-      for (int tt = 0; tt < NT; ++tt) C0[tt] = Cq[tt] = i32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int j = 0; j < 6; ++j)
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) C0[tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ak[j], Bk[tt][j], C0[tt], 0, 0, 0);
-      if (QJL)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int tt = 0; tt < NT; ++tt) Cq[tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aq[j], Bs[tt][j], Cq[tt], 0, 0, 0);
-#pragma unroll
-      for (int tt = 0; tt < NT; ++tt) {
-        // parts pairwise in int32 (|C0| < 2^21, |C1| < 2^22, |C2| < 2^23, |C3| < 2^22 fit with the
-        // shifts), one conversion per pair
-        const float key = fmaf((float)((C0[tt][0] << 8) + C0[tt][1]), sk_hi, (float)((C0[tt][2] << 8) + C0[tt][3]) * sk_lo);
-        float s = ak[tt] * key;
-        if (QJL) {
-          // sum_j bit_j S_j in int32: |Cq0| 2^16 + |Cq1| 2^8 + |Cq2| < 2^31
-          const float qj = fmaf((float)((Cq[tt][0] << 16) + (Cq[tt][1] << 8) + Cq[tt][2]), bq, oq);
-          s = fmaf(aq[tt], qj, s);
-        }
-        if (qok && t0 + 16 * tt + n < tb1) o[16 * tt] = s;
+      for (int r = 0; r < 4; ++r) {
+        ak[tt][r] = __shfl(cur.nrm[tt].x, 4 * kg + r) * A.inv_sqrt_d;
+        aq[tt][r] = QJL ? A.qjl_coef * __shfl(cur.nrm[tt].y, 4 * kg + r) : 0.0f;
       }
     }
-    if (t1 < tb1) cur = nxt;
+    // one query tile against the step's token tiles; FULL: every query and token of the step
+    // is present and rows take 16-byte stores, so the tile's code has no branch
+    auto qtile = [&](int qt, auto full_tag) {
+      constexpr bool FULL = decltype(full_tag)::value;
+      const u32x4* qo = qop_lds + qt * kScanChunks * 64 + lane;
+      i32x4 Q[6], S[6];
+#pragma unroll
+      for (int c = 0; c < 6; ++c) Q[c] = __builtin_bit_cast(i32x4, qo[c * 64]);
+      if (QJL)
+#pragma unroll
+        for (int c = 0; c < 6; ++c) S[c] = __builtin_bit_cast(i32x4, qo[(6 + c) * 64]);
+      const u32x4 scw = qo[12 * 64];
+      const float bk = __uint_as_float(scw[0]), bq = __uint_as_float(scw[1]), oq = __uint_as_float(scw[2]);
+      const float sk_hi = 16777216.0f * bk, sk_lo = 256.0f * bk;
+      i32x4 C[4][TT], Cq[3][TT];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) C[e][tt] = i32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 3; ++e)
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) Cq[e][tt] = i32x4{0, 0, 0, 0};
+      // level plane 2 - pb against query limb 2 - bi: class pb + bi (kept while <= 3)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int pb = 0; pb < 3; ++pb)
+#pragma unroll
+          for (int bi = 0; bi < 3; ++bi)
+            if (pb + bi <= 3)
+#pragma unroll
+              for (int tt = 0; tt < TT; ++tt)
+                C[pb + bi][tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Tk[tt][2 * pb + hh], Q[2 * bi + hh], C[pb + bi][tt], 0, 0, 0);
+      if (QJL)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int bi = 0; bi < 3; ++bi)
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt)
+              Cq[bi][tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ts[tt][jj], S[2 * bi + jj], Cq[bi][tt], 0, 0, 0);
+      const int q = qb * kScanQB + 16 * qt + n;
+      if (!FULL && q >= A.n_queries) return;
+      float* o = A.scores + ((int64_t)unit * A.n_queries + q) * A.n_tokens;
+      // FULL: the tile's 16 x 32 scores go through the wave's LDS staging, so that each store
+      // writes 8 rows x 128 contiguous bytes (whole lines) instead of 16 rows x 64 bytes
+      float* stg = reinterpret_cast<float*>(qop_lds + kScanQT * kScanChunks * 64) + wave * 16 * kScanStgRow;
+      if (FULL) wave_lds_order();   // the previous tile's staging reads are done
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        float sv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float key = fmaf((float)((C[0][tt][r] << 8) + C[1][tt][r]), sk_hi,
+                                 (float)((C[2][tt][r] << 8) + C[3][tt][r]) * sk_lo);
+          float s = ak[tt][r] * key;
+          if (QJL) {
+            const float qj = fmaf((float)((((Cq[0][tt][r] << 8) + Cq[1][tt][r]) << 8) + Cq[2][tt][r]), bq, oq);
+            s = fmaf(aq[tt][r], qj, s);
+          }
+          sv[r] = s;
+        }
+        const int64_t tok = t0 + 16 * tt + 4 * kg;
+        if (FULL) {
+          *reinterpret_cast<float4*>(stg + n * kScanStgRow + 16 * tt + 4 * kg) = make_float4(sv[0], sv[1], sv[2], sv[3]);
+        } else if (A.vec_store && tok + 3 < tb1) {
+          *reinterpret_cast<float4*>(o + tok) = make_float4(sv[0], sv[1], sv[2], sv[3]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (tok + r < tb1) o[tok + r] = sv[r];
+        }
+      }
+      if (FULL) {
+        wave_lds_order();
+        // lane L: row 8 i + L / 8 of the tile, tokens 4 (L % 8) .. + 3 of the step
+        const int row = lane >> 3, col = 4 * (lane & 7);
+        float* orow = A.scores + ((int64_t)unit * A.n_queries + qb * kScanQB + 16 * qt + row) * A.n_tokens + t0 + col;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          *reinterpret_cast<float4*>(orow + (int64_t)8 * i * A.n_tokens) =
+              *reinterpret_cast<const float4*>(stg + (8 * i + row) * kScanStgRow + col);
+      }
+    };
+    if constexpr (decltype(full_tag)::value) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int qt = 0; qt < kScanQT; ++qt) qtile(qt, std::true_type{});
+    } else {
+      for (int qt = 0; qt < qt_end; ++qt) qtile(qt, std::false_type{});
+    }
+  };
+  int64_t t0 = tb0 + (int64_t)wave * kStep;
+  // Workgroups with all their queries present and 16-byte aligned rows run their whole steps
+  // branch-free, each fetching the records of the step after it (clamped, so always in
+  // bounds) before its own stores, into two register sets used in turn (no copies).  One
+  // counter covers loads and stores, and it counts in order: every wait for a step's records
+  // finds exactly one step's stores and one step's loads issued after them, so it leaves those
+  // in flight.
+  if (qt_end == kScanQT && qb * kScanQB + kScanQB <= A.n_queries && A.vec_store) {
+    const int64_t t_whole = tb0 + (tb1 - tb0) / kStep * kStep;   // end of the whole steps
+    constexpr int64_t kAdv = kScanWaves * kStep;
+    if (t0 < t_whole) {
+      Raw ra, rb;
+      fetch(t0, ra);
+      fetch(t0 + kAdv, rb);
+      step(t0, ra, std::true_type{});
+      t0 += kAdv;
+      while (t0 < t_whole) {
+        fetch(t0 + kAdv, ra);
+        step(t0, rb, std::true_type{});
+        t0 += kAdv;
+        if (t0 >= t_whole) break;
+        fetch(t0 + kAdv, rb);
+        step(t0, ra, std::true_type{});
+        t0 += kAdv;
+      }
+    }
+  }
+  for (; t0 < tb1; t0 += kScanWaves * kStep) {
+    Raw cur;
+    fetch(t0, cur);
+    step(t0, cur, std::false_type{});
   }
 }
 
@@ -5220,7 +5352,7 @@ hipError_t launch_scan(const Consts& c, const DevConsts& dc, const ScanPlan& pla
     else
       hipLaunchKernelGGL((mfma_prep_kernel<2, false, true>), pgrid, dim3(kPrepThreads), 0, stream, dc.pi, dc.s_pi, q, q_dt, n_queries, plan.n_groups, c.key_fix3, qop);
     ScanMfmaArgs a;
-    a.qop = qop;
+    a.qop = reinterpret_cast<const u32x4*>(qop);
     a.records = static_cast<const uint8_t*>(records);
     a.scores = scores;
     a.capacity = capacity;
@@ -5229,13 +5361,15 @@ hipError_t launch_scan(const Consts& c, const DevConsts& dc, const ScanPlan& pla
     a.kbytes = c.kbytes;
     a.norm_off = c.norm_off;
     a.n_queries = n_queries;
-    a.n_groups = plan.n_groups;
+    a.n_qtiles = plan.n_groups / 4;
+    // 16-byte score stores need 16-byte aligned rows
+    a.vec_store = (n_tokens % 4 == 0 && reinterpret_cast<uintptr_t>(scores) % 16 == 0) ? 1 : 0;
     a.inv_sqrt_d = c.inv_sqrt_d;
     a.qjl_coef = c.qjl_coef;
     a.key_fix3 = c.key_fix3;
     for (int i = 0; i < kMaxLevels; ++i) a.key_levels[i] = c.key_levels[i];
     const dim3 grid((unsigned)((n_tokens + kScanBlockTok - 1) / kScanBlockTok),
-                    (unsigned)((n_queries + kScanQB - 1) / kScanQB), (unsigned)(batch * heads));
+                    (unsigned)((a.n_qtiles + kScanQT - 1) / kScanQT), (unsigned)(batch * heads));
     ev.before(stream);
     if (c.kb == 3 && qjl) launch_scan_mfma<3, true>(grid, a, stream);
     else if (c.kb == 3) launch_scan_mfma<3, false>(grid, a, stream);

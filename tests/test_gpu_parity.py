@@ -581,11 +581,12 @@ def test_score_scan_reduced():
 
 @pytest.mark.parametrize("kb,m,d,nq,T,n_tok", [(3, 128, 128, 70, 1000, 1000), (2, 128, 128, 37, 2100, 2093),
                                                 (3, 0, 128, 33, 4097, 4097), (2, 0, 128, 5, 300, 17),
-                                                (3, 64, 64, 20, 500, 500)])
+                                                (3, 128, 128, 150, 3000, 2996), (3, 64, 64, 20, 500, 500)])
 def test_score_scan_variants(kb, m, d, nq, T, n_tok):
     """Matrix-core scan for both key widths with and without the sketch, query counts that are
-    not multiples of the 4-query groups or 32-query blocks, token counts past the 2048-token
-    blocks and below the capacity; head_dim 64 (and m = 64) takes the generic kernel."""
+    not multiples of the 16-query tiles or 64-query workgroup blocks, token counts past the
+    1024-token blocks, below the capacity, with and without whole 16-byte score groups (2996,
+    2093); head_dim 64 (and m = 64) takes the generic kernel."""
     base = W.small(W.WORKLOADS["bulk_64k_scan"], tokens=T, scan_queries=nq)
     w = W.Workload(**{**base.__dict__, "key_bits": kb, "qjl_dim": m, "head_dim": d})
     h = _handle(w)
