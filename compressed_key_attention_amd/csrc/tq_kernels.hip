@@ -4820,6 +4820,7 @@ __device__ __forceinline__ uint32_t key_code_at(const uint32_t* kw, int i, int d
 
 constexpr int kS16Tile = 128;   // queries and vectors per workgroup
 constexpr int kS16Row = 40;     // LDS row: 32 fp16 of one K step + 8 pad (80 B)
+constexpr int kS16OutRow = 68;  // score staging row: 64 floats + 4 pad (16-byte aligned)
 
 struct Scan16Args {
   const uint16_t* qh;
@@ -4851,8 +4852,16 @@ struct Scan16Args {
 // entries would cost ~1e-4 absolute), rounded once to float32 before the split.
 template <bool POLAR>
 __global__ __launch_bounds__(256, 2) void scan_mfma16_kernel(Scan16Args A) {
-  __shared__ __attribute__((aligned(16))) uint16_t sq[2][kS16Tile * kS16Row];
-  __shared__ __attribute__((aligned(16))) uint16_t st[2][kS16Tile * kS16Row];
+  // operand staging; after the last K step each wave's 32 x 64 score halves (the stores' staging)
+  __shared__ __attribute__((aligned(16))) union {
+    struct {
+      uint16_t q[2][kS16Tile * kS16Row];
+      uint16_t t[2][kS16Tile * kS16Row];
+    } op;
+    float out[4][32][kS16OutRow];
+  } s16;
+  uint16_t (&sq)[2][kS16Tile * kS16Row] = s16.op.q;
+  uint16_t (&st)[2][kS16Tile * kS16Row] = s16.op.t;
   __shared__ float sts[kS16Tile];
   __shared__ uint32_t ptab[2][256];    // code pair (c0 | c1 << kb) -> packed fp16 hi / lo pair
   __shared__ double2 pcs[POLAR ? kMaxPolarLevels * 16 : 1];
@@ -5036,21 +5045,43 @@ __global__ __launch_bounds__(256, 2) void scan_mfma16_kernel(Scan16Args A) {
       }
     __syncthreads();   // the next step restages sq / st
   }
-  // lane (n, kg) of tile (rt, ct) holds query qb + 16 rt + 4 kg + r against vector tb + 16 ct + n
+  // lane (n, kg) of tile (rt, ct) holds query qb + 16 rt + 4 kg + r against vector tb + 16 ct + n.
+  // The scores go out through the wave's LDS staging, 32 query rows at a time, so that each
+  // store writes 4 rows x 256 contiguous bytes instead of 4 rows x 64 bytes.
+  const bool vec = A.n_tokens % 4 == 0 && reinterpret_cast<uintptr_t>(A.scores) % 16 == 0;
+  float (*so)[kS16OutRow] = s16.out[wave];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+  for (int hr = 0; hr < 2; ++hr) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int qq = q0 + qb + 16 * rt + 4 * kg + r;
+    for (int rt2 = 0; rt2 < 2; ++rt2)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * rt2 + 4 * kg + r, qq = q0 + qb + 32 * hr + row;
+        const float qs = qq < A.n_queries ? A.qscale[(int64_t)unit * A.n_queries + qq] : 0.0f;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+          so[row][16 * ct + n] = acc[2 * hr + rt2][ct][r] * qs * sts[tb + 16 * ct + n];
+      }
+    wave_lds_sync();
+    const int col = 4 * (lane & 15);
+    const int64_t tok = t0 + tb + col;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = (lane >> 4) + 4 * j, qq = q0 + qb + 32 * hr + row;
       if (qq >= A.n_queries) continue;
-      const float qs = A.qscale[(int64_t)unit * A.n_queries + qq];
-      float* o = A.scores + ((int64_t)unit * A.n_queries + qq) * A.n_tokens;
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const int tl = tb + 16 * ct + n;
-        if (t0 + tl < A.n_tokens) o[t0 + tl] = acc[rt][ct][r] * qs * sts[tl];
+      const float4 v = *reinterpret_cast<const float4*>(&so[row][col]);
+      float* o = A.scores + ((int64_t)unit * A.n_queries + qq) * A.n_tokens + tok;
+      if (vec && tok + 3 < A.n_tokens) {
+        *reinterpret_cast<float4*>(o) = v;
+      } else {
+        if (tok < A.n_tokens) o[0] = v.x;
+        if (tok + 1 < A.n_tokens) o[1] = v.y;
+        if (tok + 2 < A.n_tokens) o[2] = v.z;
+        if (tok + 3 < A.n_tokens) o[3] = v.w;
       }
     }
+    wave_lds_sync();   // the second half's writes follow these reads
+  }
 }
 
 // -----------------------------------------------------------------------------------------
@@ -5093,14 +5124,6 @@ struct ScanMfmaArgs {
 // floats, 16-byte aligned)
 constexpr int kScanStgRow = 36;
 constexpr size_t kScanLds = (size_t)kScanQT * kScanChunks * 64 * 16 + (size_t)kScanWaves * 16 * kScanStgRow * 4;
-
-// Orders one wave's LDS accesses across its lanes (a wave's LDS instructions execute in order;
-// this keeps the compiler from moving them across each other).
-__device__ __forceinline__ void wave_lds_order() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 template <int BK, bool QJL>
 __global__ __launch_bounds__(kScanThreads, 2) void scan_mfma_kernel(ScanMfmaArgs A) {
@@ -5249,7 +5272,7 @@ __global__ __launch_bounds__(kScanThreads, 2) void scan_mfma_kernel(ScanMfmaArgs
       // FULL: the tile's 16 x 32 scores go through the wave's LDS staging, so that each store
       // writes 8 rows x 128 contiguous bytes (whole lines) instead of 16 rows x 64 bytes
       float* stg = reinterpret_cast<float*>(qop_lds + kScanQT * kScanChunks * 64) + wave * 16 * kScanStgRow;
-      if (FULL) wave_lds_order();   // the previous tile's staging reads are done
+      if (FULL) wave_lds_sync();   // the previous tile's staging reads are done
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
         float sv[4];
@@ -5276,7 +5299,7 @@ __global__ __launch_bounds__(kScanThreads, 2) void scan_mfma_kernel(ScanMfmaArgs
         }
       }
       if (FULL) {
-        wave_lds_order();
+        wave_lds_sync();
         // lane L: row 8 i + L / 8 of the tile, tokens 4 (L % 8) .. + 3 of the step
         const int row = lane >> 3, col = 4 * (lane & 7);
         float* orow = A.scores + ((int64_t)unit * A.n_queries + qb * kScanQB + 16 * qt + row) * A.n_tokens + t0 + col;
