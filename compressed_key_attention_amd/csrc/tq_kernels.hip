@@ -1645,19 +1645,16 @@ __device__ __forceinline__ uint32_t bf16_pair(float x) {      // hi | lo << 16
 constexpr int kScanChunks = 13;      // bulk-scan operand chunks (16 B per lane) per query tile
 
 constexpr int kPrepThreads = 1024;
-// POLAR (decode only): the key chunks are fp16 query operands instead of int8 limbs: chunks
-// 0..3 (against the tokens' u_hi) and 4..7 (against u_lo), chunk j & 3 covering coordinates
-// 32 kg + 8 (j & 3) + e of lane L's head n / 4.  With q' = q_x 2^-e (e the head's power of two
-// above max |q_x|, so |q'| < 1): part 0 = fp16 hi of q' (round to nearest), part 1 = fp16 of
-// q' - hi (first four chunks only), parts 2, 3 zero.  Then QJL chunks 8, 9 and the scales
-// (the first is 2^e), 48 words per lane.
-constexpr int kPolarLaneWords = 48;
+// POLAR (decode only): no key chunks; the QJL chunks 0, 1 and the scales (the first is 2^e,
+// e the head's power of two above max |q_x|) as above, 12 words per lane, and q_x itself in
+// float32 to qx_out [rows][128] (the decode builds its per-query pair tables from it).
+constexpr int kPolarLaneWords = 12;
 
 template <int BK, bool QJL, bool SCAN, bool POLAR = false>
 __global__ __launch_bounds__(kPrepThreads) void mfma_prep_kernel(const float* __restrict__ pi,
                                                                  const float* __restrict__ s_pi, const void* q,
                                                                  tq_dtype q_dt, int q_heads, int kv_heads,
-                                                                 float fk, uint32_t* bop) {
+                                                                 float fk, uint32_t* bop, float* qx_out) {
   constexpr int D = 128, G = 4;
   __shared__ double qv[G][D];
   __shared__ __attribute__((aligned(16))) float xf[G][D], sf[G][D];
@@ -1711,6 +1708,7 @@ __global__ __launch_bounds__(kPrepThreads) void mfma_prep_kernel(const float* __
       for (int h = 0; h < G; ++h) {
         xf[h][o] = (float)ax[h];
         sf[h][o] = (float)as[h];
+        if (POLAR) qx_out[(qrow0 + h) * D + o] = (float)ax[h];   // the decode's pair tables
       }
   }
   __syncthreads();
@@ -1813,32 +1811,13 @@ __global__ __launch_bounds__(kPrepThreads) void mfma_prep_kernel(const float* __
   //    2 - p of the sketch (weight 2^(8 (2 - p))); part 3: zero.
   // one 16-byte chunk per wave (no divergence): waves 0 .. NC - 1 the code chunks, the next two
   // the QJL chunks, the next one the scales, each for lane L = its own lane
-  constexpr int NC = POLAR ? 8 : 4;
+  constexpr int NC = POLAR ? 0 : 4;
   const int L = threadIdx.x & 63, role = threadIdx.x >> 6;
   if (role > NC + 2) return;
   const int n = L & 15, kg = L >> 4, hB = n >> 2, part = n & 3;
   u32x4* gdst = reinterpret_cast<u32x4*>(
       bop + ((int64_t)group * 64 + L) * (POLAR ? kPolarLaneWords : 32));
-  if (POLAR && role < NC) {
-    const int j = role, chain = j >> 2, jj = j & 3;
-    const float sc = ldexpf(1.0f, -(int)s_pe[hB]);      // exact: a power of two
-    u32x4 words;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const float x = xf[hB][32 * kg + 8 * jj + 2 * w + h2] * sc;
-        const _Float16 hi = (_Float16)x;
-        const uint32_t v = part == 0 ? (uint32_t)__builtin_bit_cast(uint16_t, hi)
-                           : (part == 1 && chain == 0) ? (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(x - (float)hi))
-                                                       : 0u;
-        word |= v << (16 * h2);
-      }
-      words[w] = word;
-    }
-    gdst[j] = words;
-  } else if (role < NC) {
+  if (role < NC) {
     // byte b of a packed limb word: 0 = l2, 1 = l1, 2 = l0, 3 = zero
     const int j = role;
     const uint32_t* kl = klimb + hB * LS + 33 * kg;
@@ -2013,19 +1992,20 @@ __device__ __forceinline__ void merge_group(const float* __restrict__ pi_t, cons
 
 constexpr int kMfmaThreads = 256;
 
-// POLAR: keys are polar codes (4-bit level-1, 2-bit higher angles, head_dim 128).  Lane
-// (token n, K slice kg) rebuilds the unit vector u of its token on coordinates
-// [32 kg, 32 kg + 32) (the subtree of level-5 node kg): the scale of the subtree root from its
-// two ancestors, levels 5..3 by cos / sin multiplies, then levels 2 and 1 together from the
-// tables TA[c2][c1] = cos psi (cos, sin) theta and TB = sin psi (cos, sin) theta.  16 u (the
-// factor keeps the low half in the normal fp16 range) = u_hi + u_lo, both fp16 rounded toward
-// zero, is the B operand of eight fp16 products with the query parts (q'_hi, q'_lo), so
-// part 0 + part 1 = <q', 16 u> to about 2^-20 of sum_i |q'_i u_i|.
+// POLAR: keys are polar codes (4-bit level-1, 2-bit higher angles, head_dim 128).  With the
+// unit vector u = R_p (cos theta_p, sin theta_p) on level-1 pair p (R_p the product of the
+// cos / sin factors of p's ancestors), <q_x, u> = sum_p R_p T[p][c_p] for the per-query pair
+// table T[p][c] = q_x,2p cos theta_c + q_x,2p+1 sin theta_c (the workgroup builds it for its four
+// heads in LDS from q_x).  Lane (token n, K slice kg) forms R_p top-down for its 16 pairs
+// [16 kg, 16 kg + 16) and sums R_p T[p][c_p] for all four heads in float32; the four K slices'
+// sums meet by two shuffle rounds in the lane of head kg.
 template <int BK, bool QJL, bool GATHER, bool LOGITS, bool POLAR = false>
 __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs A) {
   constexpr int D = 128, G = 4, NW = kMfmaThreads / 64;
-  // polar tables: TA [4][16], TB [4][16], cos / sin of levels 3..7 [5][4]
-  __shared__ float2 ptab[POLAR ? 2 * 64 + 5 * 4 : 1];
+  // polar: cos / sin of levels 2..7 [6][4]; the four heads' pair tables [64 pairs][16 codes]
+  __shared__ float2 ptab[POLAR ? 6 * 4 : 1];
+  __shared__ __attribute__((aligned(16))) float4 ptq[POLAR ? 64 * 16 : 1];
+  __shared__ float pqx[POLAR ? G : 1][POLAR ? D : 1];
   // value code -> bf16 (hi, lo) pair of its level / sqrt(d): 16 words in 16 distinct banks, so lookups
   // never conflict (equal codes are broadcast)
   __shared__ uint32_t vtab[16];
@@ -2047,13 +2027,21 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
   if (threadIdx.x < 16) vtab[threadIdx.x] = bf16_pair(A.val_levels[threadIdx.x] * A.inv_sqrt_d);
   if (threadIdx.x < 4) wzero[threadIdx.x] = 0u;
   if constexpr (POLAR) {
-    if (threadIdx.x < 128) {
-      const int tb = threadIdx.x >> 6, c2 = (threadIdx.x >> 4) & 3, c1 = threadIdx.x & 15;
-      const float f = A.pcs[2 * (16 + c2) + tb];          // cos psi (TA) or sin psi (TB), level 2
-      ptab[threadIdx.x] = make_float2(f * A.pcs[2 * c1], f * A.pcs[2 * c1 + 1]);
-    } else if (threadIdx.x < 148) {
-      const int i = threadIdx.x - 128, l = i >> 2, c = i & 3;   // level 3 + l
-      ptab[threadIdx.x] = make_float2(A.pcs[2 * ((2 + l) * 16 + c)], A.pcs[2 * ((2 + l) * 16 + c) + 1]);
+    if (threadIdx.x < 24) {
+      const int l = threadIdx.x >> 2, c = threadIdx.x & 3;      // level 2 + l
+      ptab[threadIdx.x] = make_float2(A.pcs[2 * ((1 + l) * 16 + c)], A.pcs[2 * ((1 + l) * 16 + c) + 1]);
+    }
+    for (int e = threadIdx.x; e < G * D; e += kMfmaThreads) pqx[e / D][e % D] = A.qx[qrow0 * D + e];
+    __syncthreads();
+    for (int e = threadIdx.x; e < 64 * 16; e += kMfmaThreads) {
+      const int p = e >> 4, c = e & 15;
+      const float ct = A.pcs[2 * c], st = A.pcs[2 * c + 1];   // level-1 angle c
+      float4 t;
+      t.x = fmaf(pqx[0][2 * p + 1], st, pqx[0][2 * p] * ct);
+      t.y = fmaf(pqx[1][2 * p + 1], st, pqx[1][2 * p] * ct);
+      t.z = fmaf(pqx[2][2 * p + 1], st, pqx[2][2 * p] * ct);
+      t.w = fmaf(pqx[3][2 * p + 1], st, pqx[3][2 * p] * ct);
+      ptq[e] = t;
     }
   }
 
@@ -2073,9 +2061,8 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
   // part of head kg for token n: the lane owns score (token n, head kg), and each lane loads
   // only its own token's fields (key group kg, sketch word kg, value quarter kg, norms).
   const int n = lane & 15, kg = lane >> 4;
-  constexpr int NCK = POLAR ? 8 : 4;                         // key operand chunks
+  constexpr int NCK = POLAR ? 0 : 4;                         // key operand chunks
   i32x4 Aq[POLAR ? 1 : 4], Aj[2];
-  f16x8 Ap[POLAR ? 8 : 1];
   float bk16, bk8, bq, oq, kpol;
   {
     const u32x4* bp = reinterpret_cast<const u32x4*>(
@@ -2083,10 +2070,7 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
     u32x4 w[NCK + 3];
 #pragma unroll
     for (int i = 0; i < NCK + 3; ++i) w[i] = bp[i];
-    if constexpr (POLAR) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) Ap[j] = __builtin_bit_cast(f16x8, w[j]);
-    } else {
+    if constexpr (!POLAR) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) Aq[j] = __builtin_bit_cast(i32x4, w[j]);
     }
@@ -2098,8 +2082,8 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
     const float bk = __uint_as_float(w[NCK + 2][0]);
     bk16 = 65536.0f * bk * ks;
     bk8 = 256.0f * bk * ks;
-    // polar: r <q_x, u> = r 2^e <q', 16 u> / 16, u of unit norm (the first scale word is 2^e)
-    kpol = A.scale * kLog2e * bk * 0.0625f;
+    // polar: the logit is r_k <q_x, u> (u of unit norm) times the scale
+    kpol = A.scale * kLog2e;
     bq = __uint_as_float(w[NCK + 2][1]) * qs;
     oq = __uint_as_float(w[NCK + 2][2]) * qs;
   }
@@ -2182,12 +2166,12 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
 
     float l2;
     if constexpr (POLAR) {
-      // ---- key scores from the rebuilt unit vector (bf16 hi / lo products) ----
+      // ---- key scores: sum_p R_p T[p][c_p] over the lane's 16 level-1 pairs, all four heads ----
       const uint32_t u3 = cur.kw[5], u2 = cur.kw[4], uw2 = kg < 2 ? cur.kw[2] : cur.kw[3];
-      const float2* csl = ptab + 128;                                  // levels 3..7
+      const float2* csl = ptab + 4;                                    // levels 3..7
       const float2 t7 = csl[16 + ((u3 >> 28) & 3u)];
       const float2 t6 = csl[12 + ((u3 >> (24 + 2 * (kg >> 1))) & 3u)];
-      const float sroot = 16.0f * ((kg >> 1) ? t7.y : t7.x) * ((kg & 1) ? t6.y : t6.x);
+      const float sroot = ((kg >> 1) ? t7.y : t7.x) * ((kg & 1) ? t6.y : t6.x);
       const float2 t5 = csl[8 + ((u3 >> (16 + 2 * kg)) & 3u)];
       float s4[2] = {sroot * t5.x, sroot * t5.y}, s3[4], s2[8];
 #pragma unroll
@@ -2202,30 +2186,34 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
         s2[2 * i] = s3[i] * t.x;
         s2[2 * i + 1] = s3[i] * t.y;
       }
-      f32x4 Ck = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      // level-1 codes pre-scaled to float4 offsets within a pair's 16-entry table: byte k of
+      // lo / hi = code of pair 2 (4 w + k) / 2 (4 w + k) + 1 times 16 bytes
+      const float4* tq = ptq + 256 * kg;                               // pairs 16 kg ..
+      float dot[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        u32x4 bh, bl;
+      for (int wq = 0; wq < 2; ++wq) {
+        uint32_t lo = (cur.kw[wq] << 4) & 0xF0F0F0F0u, hi = cur.kw[wq] & 0xF0F0F0F0u;
+        asm volatile("" : "+v"(lo));
+        asm volatile("" : "+v"(hi));
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {                 // level-2 node 2 jj + k2
-          const int k = 2 * jj + k2;
-          const uint32_t c2 = (uw2 >> (16 * (kg & 1) + 2 * k)) & 3u;
-          const uint32_t ca = (cur.kw[k >> 2] >> (8 * (k & 3))) & 15u;      // level-1 pair 2k
-          const uint32_t cb = (cur.kw[k >> 2] >> (8 * (k & 3) + 4)) & 15u;  // level-1 pair 2k + 1
-          const float2 ta = ptab[c2 * 16 + ca], tb = ptab[64 + c2 * 16 + cb];
-          const float v[4] = {s2[k] * ta.x, s2[k] * ta.y, s2[k] * tb.x, s2[k] * tb.y};
-#pragma unroll
-          for (int pr = 0; pr < 2; ++pr) {
-            // hi = fp16 pair rounded toward zero; lo = the exact fp32 remainders, again as a pair
-            const h16x2 hp = __builtin_amdgcn_cvt_pkrtz(v[2 * pr], v[2 * pr + 1]);
-            const h16x2 lp = __builtin_amdgcn_cvt_pkrtz(v[2 * pr] - (float)hp[0], v[2 * pr + 1] - (float)hp[1]);
-            bh[2 * k2 + pr] = __builtin_bit_cast(uint32_t, hp);
-            bl[2 * k2 + pr] = __builtin_bit_cast(uint32_t, lp);
-          }
+        for (int k2 = 0; k2 < 4; ++k2) {
+          const int k = 4 * wq + k2;                                   // level-2 node
+          const float2 l2 = ptab[(uw2 >> (16 * (kg & 1) + 2 * k)) & 3u];
+          const float ra = s2[k] * l2.x, rb = s2[k] * l2.y;
+          const uint8_t* tb = reinterpret_cast<const uint8_t*>(tq + 32 * k);
+          const float4 ta = *reinterpret_cast<const float4*>(tb + ((lo >> (8 * k2)) & 0xFFu));
+          const float4 tc = *reinterpret_cast<const float4*>(tb + 256 + ((hi >> (8 * k2)) & 0xFFu));
+          dot[0] = fmaf(rb, tc.x, fmaf(ra, ta.x, dot[0]));
+          dot[1] = fmaf(rb, tc.y, fmaf(ra, ta.y, dot[1]));
+          dot[2] = fmaf(rb, tc.z, fmaf(ra, ta.z, dot[2]));
+          dot[3] = fmaf(rb, tc.w, fmaf(ra, ta.w, dot[3]));
         }
-        Ck = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ap[jj], __builtin_bit_cast(f16x8, bh), Ck, 0, 0, 0);
-        Ck = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ap[4 + jj], __builtin_bit_cast(f16x8, bl), Ck, 0, 0, 0);
       }
+      // the token's four K slices (lanes n + 16 kg') meet in the lane of head kg
+      const bool upper = kg >> 1, odd = kg & 1;
+      const float b0 = (upper ? dot[2] : dot[0]) + __shfl_xor(upper ? dot[0] : dot[2], 32);
+      const float b1 = (upper ? dot[3] : dot[1]) + __shfl_xor(upper ? dot[1] : dot[3], 32);
+      const float qu = (odd ? b1 : b0) + __shfl_xor(odd ? b0 : b1, 16);
       i32x4 Cq = i32x4{0, 0, 0, 0};
       if (QJL) {
 #pragma unroll
@@ -2236,7 +2224,7 @@ __global__ __launch_bounds__(kMfmaThreads, 3) void decode_mfma_kernel(DecodeArgs
           Cq = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aj[j >> 1], q, Cq, 0, 0, 0);
         }
       }
-      l2 = cur.nk * (Ck[0] + Ck[1]) * kpol;
+      l2 = cur.nk * qu * kpol;
       if (QJL) l2 = fmaf(cur.nrho, fmaf((float)((Cq[0] << 16) + (Cq[1] << 8) + Cq[2]), bq, oq), l2);
     } else {
     // ---- key scores (exact int32), token operands from the level tables ----
@@ -2828,21 +2816,21 @@ bool plan_decode(const Consts& c, int batch, int q_heads, int kv_heads, int64_t 
 }
 
 static void launch_mfma_prep(const Consts& c, const DevConsts& dc, const void* q, tq_dtype q_dt,
-                             int batch, int q_heads, int kv_heads, uint32_t* bop, hipStream_t st) {
+                             int batch, int q_heads, int kv_heads, uint32_t* bop, float* qx, hipStream_t st) {
   const dim3 grid((unsigned)(batch * kv_heads));
   const bool qjl = c.m > 0;
   if (c.polar && qjl)
-    hipLaunchKernelGGL((mfma_prep_kernel<2, true, false, true>), grid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
+    hipLaunchKernelGGL((mfma_prep_kernel<2, true, false, true>), grid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop, qx);
   else if (c.polar)
-    hipLaunchKernelGGL((mfma_prep_kernel<2, false, false, true>), grid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
+    hipLaunchKernelGGL((mfma_prep_kernel<2, false, false, true>), grid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop, qx);
   else if (c.kb == 3 && qjl)
-    hipLaunchKernelGGL((mfma_prep_kernel<3, true, false>), grid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
+    hipLaunchKernelGGL((mfma_prep_kernel<3, true, false>), grid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop, qx);
   else if (c.kb == 3)
-    hipLaunchKernelGGL((mfma_prep_kernel<3, false, false>), grid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
+    hipLaunchKernelGGL((mfma_prep_kernel<3, false, false>), grid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop, qx);
   else if (qjl)
-    hipLaunchKernelGGL((mfma_prep_kernel<2, true, false>), grid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
+    hipLaunchKernelGGL((mfma_prep_kernel<2, true, false>), grid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop, qx);
   else
-    hipLaunchKernelGGL((mfma_prep_kernel<2, false, false>), grid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
+    hipLaunchKernelGGL((mfma_prep_kernel<2, false, false>), grid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop, qx);
 }
 
 template <int BK, bool QJL, bool POLAR = false>
@@ -2913,7 +2901,7 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
   const bool mfma = plan.mfma && capacity < (int64_t(1) << 24) &&
                     capacity * (int64_t)c.rec_bytes < (int64_t(1) << 31);
   if (mfma)
-    launch_mfma_prep(c, dc, q, q_dt, batch, q_heads, kv_heads, bop, stream);
+    launch_mfma_prep(c, dc, q, q_dt, batch, q_heads, kv_heads, bop, qx, stream);
   else
     hipLaunchKernelGGL(query_prep_kernel, dim3(rows), dim3(kQueryPrepThreads), 0, stream, dc.pi, dc.s, c.d, c.m, q,
                        q_dt, qx, qs);
@@ -5367,13 +5355,13 @@ hipError_t launch_scan(const Consts& c, const DevConsts& dc, const ScanPlan& pla
     const bool qjl = c.m > 0;
     // q viewed as [units][n_queries] rows: "heads" of the prep = queries per unit, groups per unit
     if (c.kb == 3 && qjl)
-      hipLaunchKernelGGL((mfma_prep_kernel<3, true, true>), pgrid, dim3(kPrepThreads), 0, stream, dc.pi, dc.s_pi, q, q_dt, n_queries, plan.n_groups, c.key_fix3, qop);
+      hipLaunchKernelGGL((mfma_prep_kernel<3, true, true>), pgrid, dim3(kPrepThreads), 0, stream, dc.pi, dc.s_pi, q, q_dt, n_queries, plan.n_groups, c.key_fix3, qop, nullptr);
     else if (c.kb == 3)
-      hipLaunchKernelGGL((mfma_prep_kernel<3, false, true>), pgrid, dim3(kPrepThreads), 0, stream, dc.pi, dc.s_pi, q, q_dt, n_queries, plan.n_groups, c.key_fix3, qop);
+      hipLaunchKernelGGL((mfma_prep_kernel<3, false, true>), pgrid, dim3(kPrepThreads), 0, stream, dc.pi, dc.s_pi, q, q_dt, n_queries, plan.n_groups, c.key_fix3, qop, nullptr);
     else if (qjl)
-      hipLaunchKernelGGL((mfma_prep_kernel<2, true, true>), pgrid, dim3(kPrepThreads), 0, stream, dc.pi, dc.s_pi, q, q_dt, n_queries, plan.n_groups, c.key_fix3, qop);
+      hipLaunchKernelGGL((mfma_prep_kernel<2, true, true>), pgrid, dim3(kPrepThreads), 0, stream, dc.pi, dc.s_pi, q, q_dt, n_queries, plan.n_groups, c.key_fix3, qop, nullptr);
     else
-      hipLaunchKernelGGL((mfma_prep_kernel<2, false, true>), pgrid, dim3(kPrepThreads), 0, stream, dc.pi, dc.s_pi, q, q_dt, n_queries, plan.n_groups, c.key_fix3, qop);
+      hipLaunchKernelGGL((mfma_prep_kernel<2, false, true>), pgrid, dim3(kPrepThreads), 0, stream, dc.pi, dc.s_pi, q, q_dt, n_queries, plan.n_groups, c.key_fix3, qop, nullptr);
     ScanMfmaArgs a;
     a.qop = reinterpret_cast<const u32x4*>(qop);
     a.records = static_cast<const uint8_t*>(records);
