@@ -5499,6 +5499,7 @@ struct MonarchArgs {
   const float* pi;        // [d][d]
   const float* pi_t;      // [d][d] transposed
   const float* s;         // [m][d]
+  const float* s_t;       // [d][m] transposed
   const void* q;
   tq_dtype q_dt;
   const void* k_new;
@@ -5597,6 +5598,47 @@ __device__ void pack_record(const Consts& c, const uint32_t* ck, const uint32_t*
   for (int i = c.norm_off + 12; i < c.rec_bytes; ++i) rec[i] = 0;
 }
 
+// Word w of the record pack_record writes, from the same codes, bits and norms: one thread
+// per word (b-bit streams with b dividing 32 hold whole codes per word; 3-bit fields are whole
+// 32-code groups at the head_dims this serves, 64 and 128).
+__device__ uint32_t record_word(const Consts& c, const uint32_t* ck, const uint32_t* bits, const uint32_t* cv,
+                                float rk, float rho, float rv, int w) {
+  auto stream_word = [](const uint32_t* codes, int n, int nbits, int idx) -> uint32_t {
+    const int per = 32 / nbits, first = idx * per;
+    uint32_t word = 0;
+    for (int i = 0; i < per && first + i < n; ++i) word |= codes[first + i] << (nbits * i);
+    return word;
+  };
+  auto group3_word = [](const uint32_t* codes, int idx) -> uint32_t {
+    const int k = idx % 3;
+    const uint32_t* cg = codes + 32 * (idx / 3);
+    uint32_t word = 0;
+    for (int j = 8 * k; j < 8 * k + 8; ++j) word |= cg[j] << (8 * (j & 3) + 3 * ((j >> 2) & 1));
+    for (int kk = 0; kk < 4; ++kk) {
+      const uint32_t t6 = cg[24 + kk] | (cg[28 + kk] << 3);     // codes 24 + kk and 28 + kk
+      word |= ((t6 >> (2 * k)) & 3u) << (8 * kk + 6);
+    }
+    return word;
+  };
+  const int off = 4 * w;
+  if (off < c.kbytes) {
+    if (c.polar) {
+      const int l1w = c.l1_bytes / 4;
+      return w < l1w ? stream_word(ck, c.d / 2, c.pb1, w) : stream_word(ck + c.d / 2, c.d / 2 - 1, c.pbh, w - l1w);
+    }
+    return c.kb == 3 ? group3_word(ck, w) : stream_word(ck, c.d, c.kb, w);
+  }
+  if (off < c.kbytes + c.sbytes) return stream_word(bits, c.m, 1, w - c.kbytes / 4);
+  if (off < c.kbytes + c.sbytes + c.vbytes) {
+    const int vw = w - (c.kbytes + c.sbytes) / 4;
+    return c.vb == 3 ? group3_word(cv, vw) : stream_word(cv, c.d, c.vb, vw);
+  }
+  if (off == c.norm_off) return __float_as_uint(rk);
+  if (off == c.norm_off + 4) return __float_as_uint(rho);
+  if (off == c.norm_off + 8) return __float_as_uint(rv);
+  return 0u;
+}
+
 template <int D>
 __global__ __launch_bounds__(1024) void monarch_prep_kernel(MonarchArgs M) {
   // lanes split a token's coordinates 8 at a time (LPK lanes per token), as the merge does
@@ -5687,27 +5729,47 @@ __global__ __launch_bounds__(1024) void monarch_promote_kernel(MonarchArgs M) {
   __syncthreads();
   int32_t* hits = M.hits + (int64_t)b * M.cold_cap;
   if (M.promote_steps > 0) {
-    for (int t0 = 0; t0 < n_cold; t0 += blockDim.x) {
-      const int t = t0 + threadIdx.x;
-      bool prom = false;
-      if (t < n_cold) {
-        float w = 0.0f;
-        const float* lg = M.logits + (int64_t)b * Hq * M.logit_stride + t;
-        for (int h0 = 0; h0 < Hq; h0 += 32) {
-          float v[32];
+    // two consecutive tokens per thread (2,048 per pass): every logit and count of a pass is
+    // loaded before any is used, so a pass costs one memory round trip
+    for (int t0 = 0; t0 < n_cold; t0 += 2 * blockDim.x) {
+      const int ta = t0 + 2 * threadIdx.x;
+      bool prom[2] = {false, false};
+      // the largest weight over the gated heads: exp of the largest logit - lse
+      float mx[2] = {-INFINITY, -INFINITY};
+      int hv[2];
 #pragma unroll
-          for (int u = 0; u < 32; ++u) v[u] = lg[(int64_t)min(h0 + u, Hq - 1) * M.logit_stride];   // 32 loads in flight
+      for (int k = 0; k < 2; ++k) hv[k] = hits[min(ta + k, max(n_cold - 1, 0))];
+      const float* lg0 = M.logits + (int64_t)b * Hq * M.logit_stride + min(ta, max(n_cold - 1, 0));
+      const int64_t d1 = min(ta + 1, max(n_cold - 1, 0)) - min(ta, max(n_cold - 1, 0));
+      for (int h0 = 0; h0 < Hq; h0 += 32) {
+        float v[2][32];
+        const float* lg = lg0 + (int64_t)h0 * M.logit_stride;
 #pragma unroll
-          for (int u = 0; u < 32; ++u)
-            if (h0 + u < Hq && s_gate[h0 + u]) w = fmaxf(w, __expf(v[u] - s_lse[h0 + u]));
+        for (int u = 0; u < 32; ++u) {
+          const int64_t ro = (int64_t)min(u, Hq - 1 - h0) * M.logit_stride;
+          v[0][u] = lg[ro];
+          v[1][u] = lg[ro + d1];
         }
-        const int hc = w >= M.promote_weight ? hits[t] + 1 : 0;
-        prom = hc >= M.promote_steps;
-        hits[t] = prom ? 0 : hc;
+#pragma unroll
+        for (int u = 0; u < 32; ++u)
+          if (h0 + u < Hq && s_gate[h0 + u]) {
+            mx[0] = fmaxf(mx[0], v[0][u] - s_lse[h0 + u]);
+            mx[1] = fmaxf(mx[1], v[1][u] - s_lse[h0 + u]);
+          }
+      }
+      const float w[2] = {mx[0] == -INFINITY ? 0.0f : __expf(mx[0]), mx[1] == -INFINITY ? 0.0f : __expf(mx[1])};
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        if (ta + k < n_cold) {
+          const int hc = w[k] >= M.promote_weight ? hv[k] + 1 : 0;
+          prom[k] = hc >= M.promote_steps;
+          hits[ta + k] = prom[k] ? 0 : hc;
+        }
       }
       int tot;
-      const int pos = block_exclusive_sum<1024>(prom ? 1 : 0, wsum, &tot);
-      if (prom && s_np + pos < kMonarchMaxPromote) plist[s_np + pos] = t;
+      const int pos = block_exclusive_sum<1024>((prom[0] ? 1 : 0) + (prom[1] ? 1 : 0), wsum, &tot);
+      if (prom[0] && s_np + pos < kMonarchMaxPromote) plist[s_np + pos] = ta;
+      if (prom[1] && s_np + pos + (prom[0] ? 1 : 0) < kMonarchMaxPromote) plist[s_np + pos + (prom[0] ? 1 : 0)] = ta + 1;
       __syncthreads();
       if (threadIdx.x == 0) s_np = min(s_np + tot, kMonarchMaxPromote);
       __syncthreads();
@@ -5749,11 +5811,12 @@ __global__ __launch_bounds__(1024) void monarch_promote_kernel(MonarchArgs M) {
       slot %= M.hot_cap;
       for (int i = threadIdx.x; i < 2 * D; i += blockDim.x) {
         const int which = i / D, o = i % D;
+        // row o of Pi^T read as column o of Pi (contiguous across the lanes' o)
         double acc = 0.0;
-        for (int j0 = 0; j0 < D; j0 += 32) {      // 32 loads of the row of Pi^T in flight
+        for (int j0 = 0; j0 < D; j0 += 32) {      // 32 loads in flight
           float pv[32];
 #pragma unroll
-          for (int u = 0; u < 32; ++u) pv[u] = M.pi_t[o * D + j0 + u];
+          for (int u = 0; u < 32; ++u) pv[u] = M.pi[(j0 + u) * D + o];
 #pragma unroll
           for (int u = 0; u < 32; ++u) acc = fma((double)pv[u], lev[which][j0 + u], acc);
         }
@@ -5840,14 +5903,17 @@ __global__ __launch_bounds__(512) void monarch_evict_kernel(MonarchArgs M) {
     for (int t = threadIdx.x; t < H * 2 * D; t += blockDim.x) {
       const int h = t / (2 * D), w = (t / D) & 1, o = t % D;
       const double* xv = vin + (h * 2 + w) * D;
-      double acc = 0.0;
-      for (int j0 = 0; j0 < D; j0 += 32) {        // 32 loads of the row of Pi in flight
-        float pv[32];
+      // row o of Pi read as column o of Pi^T: for each j the lanes (consecutive o) read one
+      // contiguous run; four partial sums keep the dependency chains short
+      double a4[4] = {0.0, 0.0, 0.0, 0.0};
+      for (int j0 = 0; j0 < D; j0 += 64) {        // 64 loads in flight
+        float pv[64];
 #pragma unroll
-        for (int u = 0; u < 32; ++u) pv[u] = M.pi[o * D + j0 + u];
+        for (int u = 0; u < 64; ++u) pv[u] = M.pi_t[(j0 + u) * D + o];
 #pragma unroll
-        for (int u = 0; u < 32; ++u) acc = fma((double)pv[u], xv[j0 + u], acc);
+        for (int u = 0; u < 64; ++u) a4[u & 3] = fma((double)pv[u], xv[j0 + u], a4[u & 3]);
       }
+      const double acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
       xr[t] = acc;
       const double r = nrm[h][w];
       const double scale = r > 0.0 ? c.sqrt_d / r : 0.0;
@@ -5909,21 +5975,26 @@ __global__ __launch_bounds__(512) void monarch_evict_kernel(MonarchArgs M) {
     // QJL signs of S e
     for (int t = threadIdx.x; t < H * c.m; t += blockDim.x) {
       const int h = t / c.m, j = t % c.m;
-      double acc = 0.0;
-      for (int k0 = 0; k0 < D; k0 += 32) {        // 32 loads of the row of S in flight
-        float sv[32];
+      double a4[4] = {0.0, 0.0, 0.0, 0.0};
+      for (int k0 = 0; k0 < D; k0 += 64) {        // row j of S as column j of S^T, 64 loads in flight
+        float sv[64];
 #pragma unroll
-        for (int u = 0; u < 32; ++u) sv[u] = M.s[j * D + k0 + u];
+        for (int u = 0; u < 64; ++u) sv[u] = M.s_t[(k0 + u) * c.m + j];
 #pragma unroll
-        for (int u = 0; u < 32; ++u) acc = fma((double)sv[u], er[h * D + k0 + u], acc);
+        for (int u = 0; u < 64; ++u) a4[u & 3] = fma((double)sv[u], er[h * D + k0 + u], a4[u & 3]);
       }
+      const double acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
       bits[t] = (float)acc >= 0.0f ? 1u : 0u;
     }
     __syncthreads();
-    for (int h = threadIdx.x; h < H; h += blockDim.x) {
+    // the records, one thread per (head, 32-bit word)
+    const int nw = c.rec_bytes / 4;
+    for (int t = threadIdx.x; t < H * nw; t += blockDim.x) {
+      const int h = t / nw, w = t % nw;
       const int64_t unit = (int64_t)b * H + h;
-      pack_record(c, codes + h * 2 * D, bits + h * c.m, codes + h * 2 * D + D, (float)nrm[h][0],
-                  (float)nrm[h][2], (float)nrm[h][1], M.records + (unit * M.cold_cap + c0 + i) * c.rec_bytes);
+      reinterpret_cast<uint32_t*>(M.records + (unit * M.cold_cap + c0 + i) * c.rec_bytes)[w] =
+          record_word(c, codes + h * 2 * D, bits + h * c.m, codes + h * 2 * D + D, (float)nrm[h][0],
+                      (float)nrm[h][2], (float)nrm[h][1], w);
     }
     __syncthreads();
   }
@@ -5966,6 +6037,7 @@ hipError_t launch_monarch_step(const Consts& c, const DevConsts& dc, const Monar
   M.pi = dc.pi;
   M.pi_t = dc.pi_t;
   M.s = dc.s;
+  M.s_t = dc.s_t;
   M.q = s.q;
   M.q_dt = s.q_dt;
   M.k_new = s.k_new;
