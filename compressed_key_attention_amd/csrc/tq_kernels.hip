@@ -1586,6 +1586,12 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __fp16 h16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// A 16-byte store marked non-temporal: output written once and not read back by the kernel
+// (the bulk scans' score matrices), so it streams out instead of displacing cached inputs.
+__device__ __forceinline__ void nt_store4(float* dst, f32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst));
+}
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -5060,7 +5066,7 @@ __global__ __launch_bounds__(256, 2) void scan_mfma16_kernel(Scan16Args A) {
       const float4 v = *reinterpret_cast<const float4*>(&so[row][col]);
       float* o = A.scores + ((int64_t)unit * A.n_queries + qq) * A.n_tokens + tok;
       if (vec && tok + 3 < A.n_tokens) {
-        *reinterpret_cast<float4*>(o) = v;
+        nt_store4(o, f32x4{v.x, v.y, v.z, v.w});
       } else {
         if (tok < A.n_tokens) o[0] = v.x;
         if (tok + 1 < A.n_tokens) o[1] = v.y;
@@ -5293,8 +5299,7 @@ __global__ __launch_bounds__(kScanThreads, 2) void scan_mfma_kernel(ScanMfmaArgs
         float* orow = A.scores + ((int64_t)unit * A.n_queries + qb * kScanQB + 16 * qt + row) * A.n_tokens + t0 + col;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
-          *reinterpret_cast<float4*>(orow + (int64_t)8 * i * A.n_tokens) =
-              *reinterpret_cast<const float4*>(stg + (8 * i + row) * kScanStgRow + col);
+          nt_store4(orow + (int64_t)8 * i * A.n_tokens, *reinterpret_cast<const f32x4*>(stg + (8 * i + row) * kScanStgRow + col));
       }
     };
     if constexpr (decltype(full_tag)::value) {

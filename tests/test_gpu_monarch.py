@@ -34,7 +34,8 @@ def _close(gpu, ref, what):
     (64, 64, "float32", 6.0, 0, 3, 4), (128, 0, "float16", 6.0, 0, 3, 4),
     (128, 128, "bfloat16", 6.0, 2, 4, 4), (64, 64, "float16", math.inf, 2, 4, 4),
     (64, 32, "float32", 6.0, 4, 4, 4), (128, 0, "float16", 6.0, 1, 4, 4),
-    (64, 64, "float16", math.inf, 0, 1, 1), (128, 128, "bfloat16", 6.0, 0, 1, 4)])
+    (64, 64, "float16", math.inf, 0, 1, 1), (128, 128, "bfloat16", 6.0, 0, 1, 4),
+    (64, 64, "float16", 6.0, 0, 2, 2)])
 def test_hot_cold_steps_match_the_oracle(d, m, dtype, gate, ub, kb, vb):
     """ub > 0: polar key codes (4-bit level-1 angles, ub bits per higher angle), the Monarch
     page's polar cold tier: eviction runs the polar transform, promotion rebuilds r_k u.
