@@ -1868,6 +1868,145 @@ __global__ __launch_bounds__(kPrepThreads) void mfma_prep_kernel(const float* __
   }
 }
 
+// Per (sequence, KV head, query head of the group) preparation for the matrix-core decode with
+// scalar key codes: the same operands as mfma_prep_kernel<BK, QJL, false>, one head per block so
+// that four times as many blocks each carry a quarter of the work (q_x = Pi q and q_s = (S Pi) q
+// in float64 rounded once to float32, the head's fixed-point scales, its int8 limbs, then the
+// operand chunks of its 16 lanes (row n = 4 h .. 4 h + 3) and the scale chunk of the 16 lanes of
+// K slice h).
+template <int BK, bool QJL>
+__global__ __launch_bounds__(kPrepThreads) void mfma_prep_head_kernel(const float* __restrict__ pi,
+                                                                      const float* __restrict__ s_pi,
+                                                                      const void* q, tq_dtype q_dt, int q_heads,
+                                                                      int kv_heads, float fk, uint32_t* bop) {
+  constexpr int D = 128, G = 4, LS = D + D / 32;
+  __shared__ double qv[D];
+  __shared__ float xf[D], sf[D];
+  __shared__ float s_fq, s_fs;
+  __shared__ int s_ssum;
+  __shared__ uint32_t klimb[LS], jlimb[QJL ? LS : 1];
+  const int group = blockIdx.x >> 2, h = blockIdx.x & 3, b = group / kv_heads, hkv = group % kv_heads;
+  const int64_t qrow = (int64_t)b * q_heads + (int64_t)hkv * G + h;
+  // thread (row o, slice ks): coordinates 32 jj + 4 ks .. + 3 of row o of Pi and of S Pi, so
+  // that the eight lanes of a row read whole 128-byte lines
+  const int o = threadIdx.x >> 3, ks = threadIdx.x & 7;
+  float4 wp[4], ws[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    wp[jj] = *reinterpret_cast<const float4*>(pi + o * D + 32 * jj + 4 * ks);
+    if (QJL) ws[jj] = *reinterpret_cast<const float4*>(s_pi + o * D + 32 * jj + 4 * ks);
+  }
+  if (threadIdx.x < D) qv[threadIdx.x] = (double)load_elem(q, q_dt, qrow * D + threadIdx.x);
+  __syncthreads();
+  {
+    double ax = 0.0, as = 0.0;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const double* vv = qv + 32 * jj + 4 * ks;
+      ax = fma((double)wp[jj].x, vv[0], ax);
+      ax = fma((double)wp[jj].y, vv[1], ax);
+      ax = fma((double)wp[jj].z, vv[2], ax);
+      ax = fma((double)wp[jj].w, vv[3], ax);
+      if (QJL) {
+        as = fma((double)ws[jj].x, vv[0], as);
+        as = fma((double)ws[jj].y, vv[1], as);
+        as = fma((double)ws[jj].z, vv[2], as);
+        as = fma((double)ws[jj].w, vv[3], as);
+      }
+    }
+#pragma unroll
+    for (int msk = 1; msk < 8; msk <<= 1) {
+      ax += __shfl_xor(ax, msk);
+      if (QJL) as += __shfl_xor(as, msk);
+    }
+    if (ks == 0) {
+      xf[o] = (float)ax;
+      sf[o] = (float)as;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    // fixed-point scales (three int8 limbs against the largest |entry|) and the sum of the
+    // sketch's fixed-point values
+    const int l = threadIdx.x;
+    float mx = fmaxf(fabsf(xf[l]), fabsf(xf[l + 64]));
+    float ms = QJL ? fmaxf(fabsf(sf[l]), fabsf(sf[l + 64])) : 0.0f;
+#pragma unroll
+    for (int msk = 32; msk > 0; msk >>= 1) {
+      mx = fmaxf(mx, __shfl_xor(mx, msk));
+      ms = fmaxf(ms, __shfl_xor(ms, msk));
+    }
+    constexpr float kFix3 = 8323072.0f;   // 127 * 65536: the three-limb range
+    const float fq = mx > 0.0f ? kFix3 / mx : 1.0f, fs = ms > 0.0f ? kFix3 / ms : 1.0f;
+    int ss = QJL ? (int)rintf(sf[l] * fs) + (int)rintf(sf[l + 64] * fs) : 0;
+#pragma unroll
+    for (int msk = 32; msk > 0; msk >>= 1) ss += __shfl_xor(ss, msk);
+    if (l == 0) {
+      s_fq = fq;
+      s_fs = fs;
+      s_ssum = ss;
+    }
+  }
+  __syncthreads();
+  // the three int8 limbs of every fixed-point query and sketch coordinate, packed as bytes
+  // (l2, l1, l0, 0); coordinate i at i + i / 32 (the 4 K-slice addresses of a read fall on
+  // distinct banks).  A sketch coordinate c carries its in-place bit weight s = c % 8.
+  if (threadIdx.x < 2 * D) {
+    const int i = threadIdx.x & (D - 1), at = i + (i >> 5);
+    int l2, l1, l0;
+    if (threadIdx.x < D) {
+      int8_limbs3((int)rintf(xf[i] * s_fq), l2, l1, l0);
+      klimb[at] = (uint32_t)(l2 & 0xFF) | (uint32_t)(l1 & 0xFF) << 8 | (uint32_t)(l0 & 0xFF) << 16;
+    } else if (QJL) {
+      const int s = i & 7;
+      const float sv = sf[i] * s_fs;
+      int8_limbs3(s == 7 ? -(int)rintf(sv * 0.0078125f) : (int)rintf(sv * (1.0f / (float)(1 << s))), l2, l1, l0);
+      jlimb[at] = (uint32_t)(l2 & 0xFF) | (uint32_t)(l1 & 0xFF) << 8 | (uint32_t)(l0 & 0xFF) << 16;
+    }
+  }
+  __syncthreads();
+  // 16 threads per 16-byte chunk: roles 0..3 the code chunks and 4, 5 the QJL chunks of lanes
+  // (row n = 4 h + part, K slice kg); role 6 the scale chunk of lanes (row n, K slice h)
+  const int role = threadIdx.x >> 4, idx = threadIdx.x & 15;
+  if (role > 6) return;
+  const int part = idx & 3, kg = role < 6 ? idx >> 2 : h, n = role < 6 ? 4 * h + part : idx;
+  u32x4* gdst = reinterpret_cast<u32x4*>(bop + ((int64_t)group * 64 + n + 16 * kg) * 32);
+  if (role < 4) {
+    // byte bi of a packed limb word: 0 = l2, 1 = l1, 2 = l0, 3 = zero.  High level limb slots
+    // (w < 2): part p takes query limb 2 - p; low slots: limb 3 - p
+    const uint32_t* kl = klimb + 33 * kg;
+    u32x4 words;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const bool hi_slot = w < 2;
+      const int bi = part == 0 ? (hi_slot ? 0 : 3) : part == 1 ? (hi_slot ? 1 : 0) : part == 2 ? (hi_slot ? 2 : 1) : 3;
+      uint32_t word = 0;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) word |= ((kl[sel_coord<BK>(2 * role + (w & 1), kk)] >> (8 * bi)) & 0xFFu) << (8 * kk);
+      words[w] = word;
+    }
+    gdst[role] = words;
+  } else if (role < 6) {
+    // the token side holds bit s = 4 j + w of each sketch byte in place; part p < 3 takes
+    // limb 2 - p, i.e. byte p of the packed word
+    const int j = role - 4;
+    const uint32_t* jl = jlimb + 33 * kg;
+    u32x4 words;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t word = 0;
+      if (QJL)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) word |= ((jl[8 * k + 4 * j + w] >> (8 * part)) & 0xFFu) << (8 * k);
+      words[w] = word;
+    }
+    gdst[role] = words;
+  } else {
+    const float bq = QJL ? 2.0f / s_fs : 0.0f, oq = QJL ? -(float)s_ssum / s_fs : 0.0f;
+    gdst[6] = u32x4{__float_as_uint(1.0f / (s_fq * fk)), __float_as_uint(bq), __float_as_uint(oq), 0u};
+  }
+}
+
 // Merge without an exact segment, one block per (sequence, KV head): the GG query heads of the
 // group share one read of Pi^T (D / 2 entries per thread, applied to all GG vectors).
 // 256 threads; rows row0 .. row0 + GG - 1 of part [rows][nch][D + 2] = (m, l, o_x[D]) in, out
@@ -1890,6 +2029,8 @@ __device__ __forceinline__ void merge_group(const float* __restrict__ pi_t, cons
       w[r][jj] = *reinterpret_cast<const float4*>(pi_t + (int64_t)(orow + RS * r) * D + 32 * jj + 4 * ks);
   // rotated-domain output of head h, coordinate i
   constexpr int PER = (GG * D + 255) / 256;   // elements per thread
+  constexpr int SPLIT = GG * D <= 128 ? 256 / (GG * D) : 1;   // threads per element (many chunks)
+  __shared__ float spl[SPLIT][SPLIT > 1 ? GG * D : 1], spM[SPLIT][GG], spL[SPLIT][GG];
   if (nch <= 8) {
     // one memory round trip: every chunk's (m, l, o_i) of this thread's elements at once
     float mc[PER][8], lc[PER][8], ov[PER][8];
@@ -1926,6 +2067,56 @@ __device__ __forceinline__ void merge_group(const float* __restrict__ pi_t, cons
       if (i == 0) {
         sM[h] = M;
         sL[h] = L;
+      }
+    }
+  } else if (SPLIT > 1 && nch <= 16 * SPLIT) {
+    // SPLIT threads per element, each over 16 strided chunks in one memory round trip (a chunk
+    // with m = -inf weighs 0), then the SPLIT partial sums combined through LDS
+    const int e = (int)threadIdx.x % (GG * D), sp = (int)threadIdx.x / (GG * D), h = e / D, i = e % D;
+    const float* pr = part + (row0 + h) * nch * stride;
+    float mc[16], lc[16], ov[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int c = sp + SPLIT * u, cc = min(c, nch - 1);
+      mc[u] = c < nch ? pr[(int64_t)cc * stride] : kNegInf;
+      lc[u] = pr[(int64_t)cc * stride + 1];
+      ov[u] = pr[(int64_t)cc * stride + 2 + i];
+    }
+    float M = kNegInf;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) M = fmaxf(M, mc[u]);
+    float L = 0.0f, acc = 0.0f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const float wgt = mc[u] == kNegInf ? 0.0f : __expf(mc[u] - M);
+        acc = fmaf(ov[u], wgt, acc);
+        L = fmaf(lc[u], wgt, L);
+      }
+    }
+    spl[sp][e] = acc;
+    if (i == 0) {
+      spM[sp][h] = M;
+      spL[sp][h] = L;
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < GG * D) {
+      float Mt = kNegInf;
+#pragma unroll
+      for (int s2 = 0; s2 < SPLIT; ++s2) Mt = fmaxf(Mt, spM[s2][h]);
+      float Lt = 0.0f, at = 0.0f;
+      if (Mt != kNegInf) {
+#pragma unroll
+        for (int s2 = 0; s2 < SPLIT; ++s2) {
+          const float wgt = spM[s2][h] == kNegInf ? 0.0f : __expf(spM[s2][h] - Mt);
+          at = fmaf(spl[s2][e], wgt, at);
+          Lt = fmaf(spL[s2][h], wgt, Lt);
+        }
+      }
+      ox[h][i] = at;
+      if (i == 0) {
+        sM[h] = Mt;
+        sL[h] = Lt;
       }
     }
   } else {
@@ -2823,20 +3014,20 @@ bool plan_decode(const Consts& c, int batch, int q_heads, int kv_heads, int64_t 
 
 static void launch_mfma_prep(const Consts& c, const DevConsts& dc, const void* q, tq_dtype q_dt,
                              int batch, int q_heads, int kv_heads, uint32_t* bop, float* qx, hipStream_t st) {
-  const dim3 grid((unsigned)(batch * kv_heads));
+  const dim3 grid((unsigned)(batch * kv_heads)), hgrid((unsigned)(batch * kv_heads * 4));
   const bool qjl = c.m > 0;
   if (c.polar && qjl)
     hipLaunchKernelGGL((mfma_prep_kernel<2, true, false, true>), grid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop, qx);
   else if (c.polar)
     hipLaunchKernelGGL((mfma_prep_kernel<2, false, false, true>), grid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop, qx);
   else if (c.kb == 3 && qjl)
-    hipLaunchKernelGGL((mfma_prep_kernel<3, true, false>), grid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop, qx);
+    hipLaunchKernelGGL((mfma_prep_head_kernel<3, true>), hgrid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
   else if (c.kb == 3)
-    hipLaunchKernelGGL((mfma_prep_kernel<3, false, false>), grid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop, qx);
+    hipLaunchKernelGGL((mfma_prep_head_kernel<3, false>), hgrid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
   else if (qjl)
-    hipLaunchKernelGGL((mfma_prep_kernel<2, true, false>), grid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop, qx);
+    hipLaunchKernelGGL((mfma_prep_head_kernel<2, true>), hgrid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
   else
-    hipLaunchKernelGGL((mfma_prep_kernel<2, false, false>), grid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop, qx);
+    hipLaunchKernelGGL((mfma_prep_head_kernel<2, false>), hgrid, dim3(kPrepThreads), 0, st, dc.pi, dc.s_pi, q, q_dt, q_heads, kv_heads, c.key_fix, bop);
 }
 
 template <int BK, bool QJL, bool POLAR = false>
@@ -3005,11 +3196,13 @@ static hipError_t launch_merge(const Consts& c, const MergeArgs& mg, int batch, 
     if (c.d == 128) hipLaunchKernelGGL((decode_merge_kernel<128, kMergeThreadsHot>), mgrid, dim3(kMergeThreadsHot), 0, stream, mg);
     else hipLaunchKernelGGL((decode_merge_kernel<64, kMergeThreadsHot>), mgrid, dim3(kMergeThreadsHot), 0, stream, mg);
   } else if (mg.G == 4 || mg.G == 2) {
-    const dim3 ggrid(kv_heads, batch);
-    if (c.d == 128 && mg.G == 4) hipLaunchKernelGGL((decode_merge_group_kernel<128, 4>), ggrid, dim3(256), 0, stream, mg);
-    else if (c.d == 128) hipLaunchKernelGGL((decode_merge_group_kernel<128, 2>), ggrid, dim3(256), 0, stream, mg);
-    else if (mg.G == 4) hipLaunchKernelGGL((decode_merge_group_kernel<64, 4>), ggrid, dim3(256), 0, stream, mg);
-    else hipLaunchKernelGGL((decode_merge_group_kernel<64, 2>), ggrid, dim3(256), 0, stream, mg);
+    // one block per query head: more blocks, each with a quarter (half) of the group's work
+    if (c.d == 128) hipLaunchKernelGGL((decode_merge_group_kernel<128, 1>), mgrid, dim3(256), 0, stream, mg);
+    else hipLaunchKernelGGL((decode_merge_group_kernel<64, 1>), mgrid, dim3(256), 0, stream, mg);
+  } else if (mg.G == 1 && !mg.gate && mg.n_chunks <= 16 * 256 / c.d) {
+    // one query head per KV head: the per-head merge, chunk partials split over the block
+    if (c.d == 128) hipLaunchKernelGGL((decode_merge_group_kernel<128, 1>), mgrid, dim3(256), 0, stream, mg);
+    else hipLaunchKernelGGL((decode_merge_group_kernel<64, 1>), mgrid, dim3(256), 0, stream, mg);
   } else {
     if (c.d == 128) hipLaunchKernelGGL((decode_merge_kernel<128, kMergeThreads>), mgrid, dim3(kMergeThreads), 0, stream, mg);
     else hipLaunchKernelGGL((decode_merge_kernel<64, kMergeThreads>), mgrid, dim3(kMergeThreads), 0, stream, mg);
@@ -3390,7 +3583,7 @@ __device__ __forceinline__ void select_lut_block(const void* q, tq_dtype q_dt, c
   const int64_t unit = (int64_t)b * heads + h;
   double* lut = reinterpret_cast<double*>(smem);           // [G][ng][16]
   int32_t* comb = reinterpret_cast<int32_t*>(lut + G * ng * 16);  // [ng][16]
-  __shared__ double mx[256];
+  __shared__ double mx[4];
   const float* cb = codebook + unit * ng * 64;
   for (int e = threadIdx.x; e < kSelBinsTotal; e += blockDim.x) hist_all[unit * kSelBinsTotal + e] = 0;
   double m = 0.0;
@@ -3403,13 +3596,14 @@ __device__ __forceinline__ void select_lut_block(const void* q, tq_dtype q_dt, c
     lut[e] = v;
     m = fmax(m, fabs(v));
   }
-  mx[threadIdx.x] = m;
+  // block max: wave shuffles, then one LDS word per wave
+#pragma unroll
+  for (int msk = 32; msk > 0; msk >>= 1) m = fmax(m, __shfl_xor(m, msk));
+  if ((threadIdx.x & 63) == 0) mx[threadIdx.x >> 6] = m;
   __syncthreads();
-  for (int s = blockDim.x / 2; s > 0; s >>= 1) {
-    if (threadIdx.x < s) mx[threadIdx.x] = fmax(mx[threadIdx.x], mx[threadIdx.x + s]);
-    __syncthreads();
-  }
-  const double a = (double)(G * ng) * mx[0];
+  double mall = mx[0];
+  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) mall = fmax(mall, mx[w]);
+  const double a = (double)(G * ng) * mall;
   int sexp = 0;
   if (a != 0.0) {
     int e;
