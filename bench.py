@@ -824,7 +824,8 @@ def main():
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; --gpus above 1 is not "
-                                   "supported (the decode shards with no exchange, see the design notes)"}))
+                                   "supported (sequences and KV heads would shard over GPUs with no "
+                                   "exchange, so one GPU's share is what is measured)"}))
         sys.exit(2)
 
     import torch

@@ -14,7 +14,7 @@ per-block normalisation).  The page's first step (random rotation) and second st
 (1-bit QJL on what stage 1 leaves) are unchanged; comments on the same page say the
 polar codebook survives in TurboQuant.
 
-Readings taken where the page leaves a step open (listed with the design notes too):
+Readings taken where the page leaves a step open:
 
 * P1  The polar transform acts on the rotated key y = Pi k, coordinates paired as
       (y_2i, y_2i+1).  Level 1: radius sqrt(a^2 + b^2), angle atan2(b, a) in (-pi, pi].

@@ -25,8 +25,8 @@ Every function follows the pages step by step, in their order:
 * Monarch v3 page, "Wie es funktioniert": recent tokens exact, older tokens compressed,
   both in one softmax.
 
-Where the pages leave a step open the reading taken is stated at the function (the same
-list is kept with the design notes of the repository).  Arithmetic is float64 unless a
+Where the pages leave a step open the reading taken is stated at the function.
+Arithmetic is float64 unless a
 step says otherwise; decisions that turn a float into an integer (a code, a sign bit, a
 sign-index bit) are taken in float32, the precision the GPU kernels take them in.
 
