@@ -4148,6 +4148,8 @@ struct SparseArgs {
 // candidates in the chunks before c.  Called by all kSmallThreads threads; the results are
 // valid in every thread on return.  Needs n_chunks ints of dynamic LDS (the exclusive prefix of
 // the chunks' candidate counts).
+constexpr int kCandCache = 512;   // threshold candidates kept in LDS
+
 __device__ void sparse_unit_threshold(const SparseArgs& S, int64_t unit, int c, int64_t n, int64_t kk,
                                       uint64_t* prefix_out, uint64_t* mask_out, int* base_out) {
   constexpr int NT = kSmallThreads;
@@ -4176,7 +4178,7 @@ __device__ void sparse_unit_threshold(const SparseArgs& S, int64_t unit, int c, 
   }
   __syncthreads();
   const uint2* cand = S.cand_all + unit * S.a.capacity;
-  auto cand_at = [&](int i) {
+  auto cand_global = [&](int i) {
     int lo = 0, hi = nch - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -4184,6 +4186,15 @@ __device__ void sparse_unit_threshold(const SparseArgs& S, int64_t unit, int c, 
     }
     return cand[(int64_t)lo * kSelChunk + (i - cpre[lo])];
   };
+  // the unit's candidates (the tokens in the k-th score's bin, ~100 at 131,072 tokens) are read
+  // from memory once into LDS when they fit; the radix passes and the final count then read LDS
+  __shared__ uint2 ccache[kCandCache];
+  const bool cached = nc <= kCandCache;
+  if (cached) {
+    for (int i = tid; i < nc; i += NT) ccache[i] = cand_global(i);
+    __syncthreads();
+  }
+  auto cand_at = [&](int i) { return cached ? ccache[i] : cand_global(i); };
   const SelectParams p0 = S.params[unit];
   uint64_t prefix = (uint64_t)p0.bin << (32 + kSelDigitShift);
   uint64_t mask = (uint64_t)(kSelBins - 1) << (32 + kSelDigitShift);
@@ -4249,18 +4260,16 @@ __device__ void sparse_unit_threshold(const SparseArgs& S, int64_t unit, int c, 
 // thread 0; read after the caller's next barrier).  Called by all kSmallThreads threads.
 __device__ __forceinline__ void sparse_chunk_list(const SparseArgs& S, int64_t unit, int c, int64_t n,
                                                   int64_t kk, uint16_t* list, int* wsum, int* s_nsel) {
-  uint64_t prefix = 0, mask = 0;
-  int base = 0;
-  sparse_unit_threshold(S, unit, c, n, kk, &prefix, &mask, &base);
   constexpr int kPer = kSelChunk / kSmallThreads;
   const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)c * kSelChunk;
   const int tb = tid * kPer;
-  uint32_t sel = 0;
+  // the chunk's scores are loaded before the threshold is formed, so that their latency overlaps
+  // the threshold's own reads
+  const int mm = (int)max<int64_t>(0, min((int64_t)kSelChunk, n - t0));
+  int32_t s[kPer];
   if (kk > 0 && t0 < n) {
-    const int mm = (int)min((int64_t)kSelChunk, n - t0);
     const int32_t* sc = S.scores + unit * S.a.capacity + t0;
-    int32_t s[kPer];
     if (tb + kPer <= mm) {
 #pragma unroll
       for (int j = 0; j < kPer; j += 4) {
@@ -4271,6 +4280,12 @@ __device__ __forceinline__ void sparse_chunk_list(const SparseArgs& S, int64_t u
 #pragma unroll
       for (int j = 0; j < kPer; ++j) s[j] = tb + j < mm ? sc[tb + j] : 0;
     }
+  }
+  uint64_t prefix = 0, mask = 0;
+  int base = 0;
+  sparse_unit_threshold(S, unit, c, n, kk, &prefix, &mask, &base);
+  uint32_t sel = 0;
+  if (kk > 0 && t0 < n) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int t = tb + j;
