@@ -276,6 +276,22 @@ def test_decode_group_sizes_and_empty_sequences():
     _decode_case(w2, [0, 299], hot_lens=[17, 0], scale=0.3)
 
 
+@pytest.mark.parametrize("base,hq,hkv,tokens", [
+    ("single_head_1k", 4, 1, 320), ("single_head_1k", 4, 1, 1100), ("single_head_1k", 4, 1, 2500),
+    ("single_head_1k", 2, 1, 1100), ("single_head_1k", 2, 1, 2500),
+    ("single_head_1k", 1, 1, 320), ("single_head_1k", 1, 1, 2047), ("single_head_1k", 1, 1, 2100),
+    ("tinyllama_layer", 2, 2, 3000), ("tinyllama_layer", 2, 2, 4500)])
+def test_decode_merge_paths_by_chunk_count(base, hq, hkv, tokens):
+    """The merge without an exact segment at chunk counts on each side of its paths: one block
+    per query head with every chunk in one round trip (at most 8 chunks), chunks split over the
+    block's threads (up to 16 * 256 / head_dim chunks), and the running-maximum pass beyond
+    (or the general merge for one query head per KV head); 64-token chunks at these sizes."""
+    b = W.WORKLOADS[base]
+    w = W.Workload(**{**W.small(b, tokens=tokens, batch=1).__dict__, "q_heads": hq, "kv_heads": hkv,
+                      "name": base})
+    _decode_case(w, [tokens])
+
+
 def test_decode_long_exact_segment():
     """Exact segments longer than the merge kernel keeps in LDS (logits recomputed past 2,048),
     float32 and bfloat16 hot tokens, head_dim 128, ragged hot lengths."""
