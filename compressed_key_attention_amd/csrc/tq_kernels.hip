@@ -3584,7 +3584,7 @@ __device__ __forceinline__ void select_lut_block(const void* q, tq_dtype q_dt, c
   const int64_t unit = (int64_t)b * heads + h;
   double* lut = reinterpret_cast<double*>(smem);           // [G][ng][16]
   int32_t* comb = reinterpret_cast<int32_t*>(lut + G * ng * 16);  // [ng][16]
-  __shared__ double mx[4];
+  __shared__ double mx[16];                                 // one per wave, up to 1,024 threads
   const float* cb = codebook + unit * ng * 64;
   for (int e = threadIdx.x; e < kSelBinsTotal; e += blockDim.x) hist_all[unit * kSelBinsTotal + e] = 0;
   double m = 0.0;
@@ -3629,7 +3629,7 @@ __global__ __launch_bounds__(256) void select_lut_kernel(const void* q, tq_dtype
 // The selection tables and the attention's query prep in one launch (sparse attention, whose
 // two first steps are independent one-block-per-unit / per-query jobs): blocks below
 // batch * heads build a unit's tables, the others prepare query row blockIdx.x - batch * heads.
-__global__ __launch_bounds__(256) void select_lut_prep_kernel(const void* q, tq_dtype q_dt, const float* codebook,
+__global__ __launch_bounds__(kQueryPrepThreads) void select_lut_prep_kernel(const void* q, tq_dtype q_dt, const float* codebook,
                                                               int d, int G, int q_heads, int heads, int units,
                                                               int32_t* lut_out, int32_t* hist_all, QueryPrep P) {
   if ((int)blockIdx.x < units)
@@ -4087,7 +4087,7 @@ hipError_t launch_select(const Consts& c, const SelectPlan& plan, const void* q,
   if (capacity > 0) {
     const size_t lds = (size_t)G * ng * 16 * 8 + (size_t)ng * 16 * 4;
     if (prep)
-      hipLaunchKernelGGL(select_lut_prep_kernel, dim3((unsigned)(batch * kv_heads + prep->rows)), dim3(256), lds,
+      hipLaunchKernelGGL(select_lut_prep_kernel, dim3((unsigned)(batch * kv_heads + prep->rows)), dim3(kQueryPrepThreads), lds,
                          stream, q, q_dt, codebook, c.d, G, q_heads, kv_heads, batch * kv_heads, lut, hist, *prep);
     else
       hipLaunchKernelGGL(select_lut_kernel, dim3(kv_heads, batch), dim3(256), lds, stream, q, q_dt, codebook,
