@@ -103,6 +103,9 @@ struct DecodeHooks {
   const int32_t* gate;       // [B][Hq]
   const int32_t* hot_start;  // [B]
   int hot_add;
+  // [B][capacity] float bits, zeroed: each open head's merge folds exp(logit - lse) of every
+  // cold token into the per-token maximum (NULL: not formed)
+  uint32_t* promo_w;
 };
 hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan& plan,
                          const void* q, tq_dtype q_dt, int batch, int q_heads, int kv_heads,
@@ -179,7 +182,7 @@ hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int
 struct MonarchPlan {
   DecodePlan decode;
   int64_t logit_stride;
-  size_t ws_decode, ws_gate, ws_lse, ws_logits, ws_counts, ws_total;
+  size_t ws_decode, ws_gate, ws_lse, ws_logits, ws_counts, ws_promo, ws_total;
 };
 struct MonarchStep {
   const void* q;

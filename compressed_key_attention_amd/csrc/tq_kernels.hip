@@ -2654,6 +2654,9 @@ struct MergeArgs {
   const int32_t* gate;        // [B][Hq] nonzero: the head's cold partials count (NULL: all do)
   int hot_add;                // tokens appended past hot_lens in this step (ring mode)
   int64_t hot_capacity, logit_hot_off, logit_stride;
+  uint32_t* promo_w;          // hot/cold step: per-token maximum of the open heads' weights (NULL: none)
+  const int32_t* promo_n;     // [B] cold tokens
+  int64_t promo_stride;       // cold capacity
   float* out;
   float* lse;
   float* logits;
@@ -2815,7 +2818,16 @@ __global__ __launch_bounds__(NT) void decode_merge_kernel(MergeArgs A) {
       }
     }
   }
-  if (threadIdx.x == 0 && A.lse) A.lse[row] = L > 0.0f ? M + logf(L) : kNegInf;
+  const float lse_r = L > 0.0f ? M + logf(L) : kNegInf;
+  if (threadIdx.x == 0 && A.lse) A.lse[row] = lse_r;
+  // hot/cold step: this head's weight exp(logit - lse) of every cold token, folded into the
+  // per-token maximum over the open heads (non-negative floats order as their bits)
+  if (A.promo_w && A.logits && n_chunks > 0) {
+    const int nc = (int)min((int64_t)A.promo_n[b], A.promo_stride);
+    const float* lg = A.logits + row * A.logit_stride;
+    uint32_t* pw = A.promo_w + (int64_t)b * A.promo_stride;
+    for (int t = threadIdx.x; t < nc; t += NT) atomicMax(pw + t, __float_as_uint(__expf(lg[t] - lse_r)));
+  }
 }
 
 // The merge for every other head_dim (d read at run time, up to 256): one workgroup per query
@@ -3172,6 +3184,9 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
   mg.hot_start = hooks ? hooks->hot_start : nullptr;
   mg.gate = hooks ? hooks->gate : nullptr;
   mg.hot_add = hooks ? hooks->hot_add : 0;
+  mg.promo_w = hooks ? hooks->promo_w : nullptr;
+  mg.promo_n = seq_lens;
+  mg.promo_stride = capacity;
   mg.hot_capacity = hot_capacity;
   mg.logit_hot_off = n_cold;
   mg.logit_stride = lstride;
@@ -3190,6 +3205,8 @@ hipError_t launch_decode(const Consts& c, const DevConsts& dc, const DecodePlan&
 // The merge of chunk partials (and the exact segment, if any) into out / lse.
 static hipError_t launch_merge(const Consts& c, const MergeArgs& mg, int batch, hipStream_t stream) {
   const int q_heads = mg.q_heads, kv_heads = mg.kv_heads;
+  // the hot/cold step's promotion weights are folded in by the merge with an exact segment
+  if (mg.promo_w && (!mg.hot_lens || (c.d != 64 && c.d != 128))) return hipErrorInvalidValue;
   const dim3 mgrid(q_heads, batch);
   if (c.d != 64 && c.d != 128) {
     hipLaunchKernelGGL(decode_merge_generic_kernel, mgrid, dim3(256), 0, stream, mg);
@@ -5738,6 +5755,7 @@ struct MonarchArgs {
   int32_t* promo_count;   // [B] (workspace)
   int32_t* cold_after;    // [B] (workspace)
   int32_t* gate_out;      // [B][Hq] copy of the gates for the caller (NULL: none)
+  uint32_t* promo_w;      // [B][cold_cap] per-token maximum weight over the open heads (float bits)
   int batch, q_heads, kv_heads, G, window, promote_steps;
   float cold_gate, promote_weight, scale;
 };
@@ -5865,6 +5883,10 @@ __global__ __launch_bounds__(1024) void monarch_prep_kernel(MonarchArgs M) {
   __shared__ float red[16][16];
   const int hkv = blockIdx.x, b = blockIdx.y, G = M.G;
   const int64_t unit = (int64_t)b * M.kv_heads + hkv;
+  if (M.promo_w && hkv == 0) {    // cleared before the step's merge folds the weights in
+    const int nc = (int)min((int64_t)M.cold_len[b], M.cold_cap);
+    for (int t = threadIdx.x; t < nc; t += blockDim.x) M.promo_w[(int64_t)b * M.cold_cap + t] = 0u;
+  }
   const int n = M.hot_len[b];
   const int64_t st = M.hot_start[b];
   int64_t slot = st + n;
@@ -5929,7 +5951,6 @@ __global__ __launch_bounds__(1024) void monarch_prep_kernel(MonarchArgs M) {
 
 template <int D>
 __global__ __launch_bounds__(1024) void monarch_promote_kernel(MonarchArgs M) {
-  __shared__ float s_lse[kMonarchMaxHeads];
   __shared__ int s_gate[kMonarchMaxHeads];
   __shared__ int plist[kMonarchMaxPromote];
   __shared__ int moves[kMonarchMaxPromote][2];
@@ -5939,7 +5960,6 @@ __global__ __launch_bounds__(1024) void monarch_promote_kernel(MonarchArgs M) {
   const int b = blockIdx.x, Hq = M.q_heads;
   const int n_cold = M.cold_len[b];
   for (int h = threadIdx.x; h < Hq; h += blockDim.x) {
-    s_lse[h] = M.lse[(int64_t)b * Hq + h];
     s_gate[h] = M.gate[(int64_t)b * Hq + h];
     if (M.gate_out) M.gate_out[(int64_t)b * Hq + h] = s_gate[h];
   }
@@ -5947,35 +5967,20 @@ __global__ __launch_bounds__(1024) void monarch_promote_kernel(MonarchArgs M) {
   __syncthreads();
   int32_t* hits = M.hits + (int64_t)b * M.cold_cap;
   if (M.promote_steps > 0) {
-    // two consecutive tokens per thread (2,048 per pass): every logit and count of a pass is
-    // loaded before any is used, so a pass costs one memory round trip
+    // two consecutive tokens per thread (2,048 per pass).  A token's weight, the largest
+    // exp(logit - lse) over the open heads, was folded into promo_w by the heads' merges (0 when
+    // no head is open)
+    const uint32_t* pw = M.promo_w + (int64_t)b * M.cold_cap;
     for (int t0 = 0; t0 < n_cold; t0 += 2 * blockDim.x) {
       const int ta = t0 + 2 * threadIdx.x;
       bool prom[2] = {false, false};
-      // the largest weight over the gated heads: exp of the largest logit - lse
-      float mx[2] = {-INFINITY, -INFINITY};
       int hv[2];
+      float w[2];
 #pragma unroll
-      for (int k = 0; k < 2; ++k) hv[k] = hits[min(ta + k, max(n_cold - 1, 0))];
-      const float* lg0 = M.logits + (int64_t)b * Hq * M.logit_stride + min(ta, max(n_cold - 1, 0));
-      const int64_t d1 = min(ta + 1, max(n_cold - 1, 0)) - min(ta, max(n_cold - 1, 0));
-      for (int h0 = 0; h0 < Hq; h0 += 32) {
-        float v[2][32];
-        const float* lg = lg0 + (int64_t)h0 * M.logit_stride;
-#pragma unroll
-        for (int u = 0; u < 32; ++u) {
-          const int64_t ro = (int64_t)min(u, Hq - 1 - h0) * M.logit_stride;
-          v[0][u] = lg[ro];
-          v[1][u] = lg[ro + d1];
-        }
-#pragma unroll
-        for (int u = 0; u < 32; ++u)
-          if (h0 + u < Hq && s_gate[h0 + u]) {
-            mx[0] = fmaxf(mx[0], v[0][u] - s_lse[h0 + u]);
-            mx[1] = fmaxf(mx[1], v[1][u] - s_lse[h0 + u]);
-          }
+      for (int k = 0; k < 2; ++k) {
+        hv[k] = hits[min(ta + k, max(n_cold - 1, 0))];
+        w[k] = __uint_as_float(pw[min(ta + k, max(n_cold - 1, 0))]);
       }
-      const float w[2] = {mx[0] == -INFINITY ? 0.0f : __expf(mx[0]), mx[1] == -INFINITY ? 0.0f : __expf(mx[1])};
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         if (ta + k < n_cold) {
@@ -6242,7 +6247,8 @@ MonarchPlan plan_monarch(const Consts& c, int batch, int q_heads, int kv_heads, 
   p.ws_lse = p.ws_gate + align256(rows * 4);
   p.ws_logits = p.ws_lse + align256(rows * 4);
   p.ws_counts = p.ws_logits + align256(rows * (size_t)p.logit_stride * 4);
-  p.ws_total = p.ws_counts + align256((size_t)std::max(batch, 1) * 8);
+  p.ws_promo = p.ws_counts + align256((size_t)std::max(batch, 1) * 8);
+  p.ws_total = p.ws_promo + align256((size_t)std::max(batch, 1) * (size_t)cold_cap * 4);
   return p;
 }
 
@@ -6279,6 +6285,7 @@ hipError_t launch_monarch_step(const Consts& c, const DevConsts& dc, const Monar
   M.logits = logits;
   M.lse = lse;
   M.promo_count = reinterpret_cast<int32_t*>(ws + plan.ws_counts);
+  M.promo_w = s.promote_steps > 0 ? reinterpret_cast<uint32_t*>(ws + plan.ws_promo) : nullptr;
   M.cold_after = M.promo_count + std::max(s.batch, 1);
   M.batch = s.batch;
   M.q_heads = s.q_heads;
@@ -6293,7 +6300,7 @@ hipError_t launch_monarch_step(const Consts& c, const DevConsts& dc, const Monar
   const dim3 g1(s.kv_heads, s.batch);
   if (c.d == 128) hipLaunchKernelGGL(monarch_prep_kernel<128>, g1, dim3(1024), 0, stream, M);
   else hipLaunchKernelGGL(monarch_prep_kernel<64>, g1, dim3(1024), 0, stream, M);
-  DecodeHooks hk{M.gate, s.hot_start, 1};
+  DecodeHooks hk{M.gate, s.hot_start, 1, M.promo_w};
   hipError_t e = launch_decode(c, dc, plan.decode, s.q, s.q_dt, s.batch, s.q_heads, s.kv_heads, s.records,
                                s.cold_cap, s.cold_len, s.hot_k, s.hot_v, s.hot_dt, s.hot_len, s.hot_cap,
                                nullptr, 0, M.scale, s.out, lse, logits, ws + plan.ws_decode, stream, ev, &hk);
