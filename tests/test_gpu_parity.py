@@ -292,6 +292,34 @@ def test_decode_merge_paths_by_chunk_count(base, hq, hkv, tokens):
     _decode_case(w, [tokens])
 
 
+def test_decode_cache_run_beyond_32_bit_offsets():
+    """A cache whose (sequence, KV head) runs exceed 2^31 bytes (15,000,000 slots of 144 bytes
+    per head, 4.3 GB of records): the host sends the matrix-core shape (head_dim 128, 4 query
+    heads per KV head) to the 64-bit-offset scan, and the second head's records, 2.16 GB into
+    the buffer, decode as the oracle says."""
+    base = W.WORKLOADS["llama8b_decode_32k"]
+    w = W.Workload(**{**W.small(base, tokens=1000, batch=1).__dict__, "q_heads": 8, "kv_heads": 2,
+                      "name": "llama8b_decode_32k"})
+    cap = 15_000_000
+    h = _handle(w)
+    assert cap * h.record_bytes >= 2 ** 31
+    K, V = W.make_kv(w, "cuda")
+    rec = h.new_cache(1, w.kv_heads, cap, "cuda")
+    h.compress_kv(K, V, rec)
+    q = W.make_queries(w, "cuda")
+    sl = torch.tensor([w.tokens], dtype=torch.int32, device="cuda")
+    out = torch.full((1, w.q_heads, w.head_dim), float("nan"), device="cuda")
+    lse = torch.full((1, w.q_heads), float("nan"), device="cuda")
+    h.decode_attention(q, rec, sl, out=out, lse=lse)
+    torch.cuda.synchronize()
+    small = rec[:, :, : w.tokens].cpu().numpy()
+    del rec
+    torch.cuda.empty_cache()
+    ref_out, ref_lse, _ = O.decode_attention(_codec(h), _np(q), small, [w.tokens])
+    _close(out.cpu().numpy(), ref_out, "out (15M-slot cache)")
+    _close(lse.cpu().numpy(), ref_lse, "lse (15M-slot cache)")
+
+
 def test_decode_long_exact_segment():
     """Exact segments longer than the merge kernel keeps in LDS (logits recomputed past 2,048),
     float32 and bfloat16 hot tokens, head_dim 128, ragged hot lengths."""
